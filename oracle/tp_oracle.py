@@ -1,0 +1,362 @@
+"""Plain, slow, obviously-correct float64 oracle for one rank's tensor-parallel shard.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  The GPU product
+path never calls it, imports nothing from it and shares no code with it.
+
+Everything here is numpy float64 (``numpy.matmul`` is the only library
+primitive used for the contraction).  Inputs that arrive as bf16/fp32 tensors
+are upcast to float64 *after* the shared generator has rounded them, so the
+oracle sees exactly the values the GPU sees.
+
+Sources (the web pages this method is described on):
+  [MLX]  "Tensor-parallel all-reduce count per transformer layer in MLX
+         shard_linear" - Facts list (ShardedToAllLinear adds its bias once,
+         after the sum).
+  [KL]   "Tensor Parallelism" (inference-engineering notes) - first paragraph
+         (column / row parallelism algebra), second paragraph (GQA per-rank
+         bookkeeping), fifth paragraph (KV heads bound the TP width).
+  [KS]   "Why Tensor Parallelism has to stay inside the scale-up domain" -
+         "What is Tensor Parallel" (h=2, d_ff=3 worked example),
+         "What happens if TP leaves the node" (6 x params x tokens).
+  [FFN]  "How does tensor parallelism split a transformer feed-forward block's
+         two matmuls across devices?" - "The shape of the block",
+         "Column split, then row split" (First matmul, column-parallel /
+         The nonlinearity is free / Second matmul, row-parallel /
+         One collective), "The backward pass", "Common failure".
+
+Readings where the pages are silent (also listed with the design notes):
+  * SwiGLU is silu(x W_gate) * (x W_up) with gate and up over the SAME owned
+    column range ([FFN] "The nonlinearity is free" allows "a gated variant
+    computed from the same slice"); silu(g) = g * sigmoid(g).
+  * GELU is the exact erf form 0.5 x (1 + erf(x / sqrt 2)); no tanh variant.
+  * ReLU'(0) = 0.
+  * Equal contiguous chunks only; an intermediate size not divisible by p is
+    rejected ([FFN] partitions 4d into N chunks of size 4d/N).
+  * Column-parallel bias: each shard adds its own slice; row-parallel bias:
+    added once after the sum ([MLX]).
+
+Every function below has a pin in ``tests/test_oracle_pins.py`` that checks it
+against something other than itself (the pages' worked example, exact rational
+brute force, algebraic invariants, finite differences, library special values).
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+F64 = np.float64
+ACTS = ("none", "relu", "gelu", "swiglu")
+
+
+def to64(a) -> np.ndarray:
+    """Upcast a torch tensor (any float dtype) or array to a float64 ndarray."""
+    if hasattr(a, "detach"):
+        a = a.detach().to("cpu").float().numpy()
+    return np.asarray(a, dtype=F64)
+
+
+# ---------------------------------------------------------------------------
+# Shard ownership.  [FFN] "Column split, then row split": the intermediate
+# dimension is cut into N equal chunks; device i owns columns i*n/N .. (i+1)*n/N
+# of the first matrix and exactly the matching rows of the second.
+# ---------------------------------------------------------------------------
+def shard_range(n_total: int, p: int, i: int) -> Tuple[int, int]:
+    """(begin, length) of shard ``i`` when ``n_total`` is cut into ``p`` equal chunks."""
+    if p <= 0 or not (0 <= i < p) or n_total < 0:
+        raise ValueError("bad shard request")
+    if n_total % p != 0:
+        raise ValueError(f"{n_total} is not divisible by p={p}")
+    length = n_total // p
+    return i * length, length
+
+
+def gqa_shard(n_q: int, n_kv: int, head_dim: int, p: int, i: int) -> Tuple[int, int, int, int]:
+    """Column ranges of rank ``i``'s query heads and KV heads.
+
+    [KL] second paragraph: with 64 Q heads, 8 KV heads, head dim 128 and p=8,
+    each rank owns 8 Q heads and 1 KV head, i.e. a 1024-wide Q slice and a
+    128-wide K and V slice.  [FFN] attention paragraph: heads are never split,
+    so both head counts must divide by p ([KL] fifth paragraph: 8 KV heads map
+    cleanly only for p <= 8).  Heads are taken contiguously, so Q head j groups
+    with KV head floor(j / (n_q / n_kv)) and both land on the same rank.
+    Returns (q_begin, q_len, kv_begin, kv_len) in columns."""
+    if n_q % p != 0 or n_kv % p != 0:
+        raise ValueError("head counts must be divisible by p (a head is never split)")
+    qh_b, qh_n = shard_range(n_q, p, i)
+    kh_b, kh_n = shard_range(n_kv, p, i)
+    return qh_b * head_dim, qh_n * head_dim, kh_b * head_dim, kh_n * head_dim
+
+
+def slice_cols(w: np.ndarray, begin: int, length: int) -> np.ndarray:
+    return np.ascontiguousarray(w[:, begin:begin + length])
+
+
+def slice_rows(w: np.ndarray, begin: int, length: int) -> np.ndarray:
+    return np.ascontiguousarray(w[begin:begin + length, :])
+
+
+# ---------------------------------------------------------------------------
+# Activations.  [FFN] "The nonlinearity is free": GELU, ReLU or a gated
+# variant, applied elementwise to the owned columns.
+# ---------------------------------------------------------------------------
+def sigmoid(g: np.ndarray) -> np.ndarray:
+    g = np.asarray(g, dtype=F64)
+    out = np.empty_like(g)
+    pos = g >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-g[pos]))
+    e = np.exp(g[~pos])
+    out[~pos] = e / (1.0 + e)
+    return out
+
+
+def relu(a: np.ndarray) -> np.ndarray:
+    return np.where(a > 0, a, 0.0)
+
+
+def relu_grad(a: np.ndarray) -> np.ndarray:
+    return np.where(a > 0, 1.0, 0.0)
+
+
+_erf = np.vectorize(math.erf, otypes=[F64])
+
+
+def gelu(a: np.ndarray) -> np.ndarray:
+    """Exact GELU: a * Phi(a) with Phi the standard normal CDF, via erf."""
+    a = np.asarray(a, dtype=F64)
+    return 0.5 * a * (1.0 + _erf(a / math.sqrt(2.0)))
+
+
+def gelu_grad(a: np.ndarray) -> np.ndarray:
+    """d/da [a Phi(a)] = Phi(a) + a phi(a)."""
+    a = np.asarray(a, dtype=F64)
+    cdf = 0.5 * (1.0 + _erf(a / math.sqrt(2.0)))
+    pdf = np.exp(-0.5 * a * a) / math.sqrt(2.0 * math.pi)
+    return cdf + a * pdf
+
+
+def silu(g: np.ndarray) -> np.ndarray:
+    return np.asarray(g, dtype=F64) * sigmoid(g)
+
+
+def silu_grad(g: np.ndarray) -> np.ndarray:
+    """d/dg [g s(g)] = s(g) + g s(g) (1 - s(g))."""
+    s = sigmoid(g)
+    return s + np.asarray(g, dtype=F64) * s * (1.0 - s)
+
+
+def act_apply(a: np.ndarray, act: str, up: Optional[np.ndarray] = None) -> np.ndarray:
+    if act == "none":
+        return np.asarray(a, dtype=F64)
+    if act == "relu":
+        return relu(a)
+    if act == "gelu":
+        return gelu(a)
+    if act == "swiglu":
+        if up is None:
+            raise ValueError("swiglu needs the up projection")
+        return silu(a) * up
+    raise ValueError(f"unknown act {act}")
+
+
+# ---------------------------------------------------------------------------
+# Linear layers.  [KL] first paragraph: Y = XW; column parallelism splits W
+# along its output dimension so device i computes Y_i = X W_i; row
+# parallelism splits W along its input dimension and X to match, so device i
+# computes the full-shape partial Z_i = X_i W_i and Y = sum_i Z_i.
+# ---------------------------------------------------------------------------
+def matmul(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    return np.matmul(np.asarray(a, dtype=F64), np.asarray(b, dtype=F64))
+
+
+def col_linear(x, w, w_up=None, bias=None, act: str = "none") -> np.ndarray:
+    """act(x W_i [+ b_i]); for swiglu: silu(x W_i) * (x W_up_i) (no bias).
+
+    [KL] first paragraph (Y_i = X W_i) and [FFN] "First matmul,
+    column-parallel" / "The nonlinearity is free" (act on owned columns)."""
+    a = matmul(x, w)
+    if act == "swiglu":
+        if bias is not None:
+            raise ValueError("bias is not defined for the gated variant")
+        return act_apply(a, act, matmul(x, w_up))
+    if bias is not None:
+        a = a + to64(bias)[None, :]
+    return act_apply(a, act)
+
+
+def row_linear_partial(x_i, w_i) -> np.ndarray:
+    """Z_i = X_i W_i: the full output shape, but only a partial sum.
+
+    [KL] first paragraph (row parallelism) and [FFN] "Second matmul,
+    row-parallel"; no bias here ([MLX]: the bias is added after the sum)."""
+    return matmul(x_i, w_i)
+
+
+def partial_sum(zs: Sequence[np.ndarray], bias=None) -> np.ndarray:
+    """Y = sum_i Z_i, then + bias once.
+
+    [KL] first paragraph (Y = sum_i Z_i, done by an all-reduce);
+    [FFN] "One collective"; [MLX] (ShardedToAllLinear adds the bias once,
+    after the sum)."""
+    y = np.zeros_like(to64(zs[0]))
+    for z in zs:
+        y = y + to64(z)
+    if bias is not None:
+        y = y + to64(bias)[None, :]
+    return y
+
+
+# ---------------------------------------------------------------------------
+# The feed-forward block.  [FFN] "The shape of the block": h = act(x W1),
+# y = h W2; "Column split, then row split": h_i = act(x W1_i),
+# y_i = h_i W2_i, y = sum_i y_i.
+# ---------------------------------------------------------------------------
+def mlp_full(x, w1, w_up, w2, act: str) -> np.ndarray:
+    """Unsharded block: act(x W1 [, x W_up]) W2."""
+    return matmul(col_linear(x, w1, w_up, None, act), w2)
+
+
+def mlp_shard_fwd(x, w1_i, w_up_i, w2_i, act: str) -> Tuple[np.ndarray, Dict[str, np.ndarray]]:
+    """One rank's forward: y_i = act(x W1_i [, x W_up_i]) W2_i.
+
+    Returns (y_i, saved) with the pre-activations the backward needs:
+    saved = {"g": x W1_i, "u": x W_up_i} for swiglu, {"a": x W1_i} otherwise."""
+    a = matmul(x, w1_i)
+    if act == "swiglu":
+        u = matmul(x, w_up_i)
+        h = silu(a) * u
+        saved = {"g": a, "u": u}
+    else:
+        h = act_apply(a, act)
+        saved = {"a": a}
+    return matmul(h, w2_i), saved
+
+
+def mlp_shard_bwd(x, w1_i, w_up_i, w2_i, dy, act: str,
+                  saved: Optional[Dict[str, np.ndarray]] = None) -> Dict[str, np.ndarray]:
+    """One rank's backward.
+
+    [FFN] "The backward pass": the gradient arriving at y is identical on
+    every device (the exit is an all-reduce forward, identity backward); each
+    device forms the gradients of its own W1/W2 slices with no exchange and a
+    partial gradient of x from its own column slice; those partials are summed
+    before leaving the block.  Chain rule for h_i = act(x W1_i) and
+    y_i = h_i W2_i:
+        dW2_i = h_i^T dy,   dh_i = dy W2_i^T,
+        dA = dh_i * act'(A)                        (relu / gelu)
+        dG = dh_i * U * silu'(G), dU = dh_i * silu(G)   (swiglu)
+        dW1_i = x^T dA (or x^T dG), dW_up_i = x^T dU,
+        dx_i = dA W1_i^T  (or dG W1_i^T + dU W_up_i^T).
+    The pre-activations are recomputed from x here unless given."""
+    x = to64(x)
+    dy = to64(dy)
+    if saved is None:
+        _, saved = mlp_shard_fwd(x, w1_i, w_up_i, w2_i, act)
+    out: Dict[str, np.ndarray] = {}
+    if act == "swiglu":
+        g, u = saved["g"], saved["u"]
+        h = silu(g) * u
+        dh = matmul(dy, to64(w2_i).T)
+        dg = dh * u * silu_grad(g)
+        du = dh * silu(g)
+        out["dw2"] = matmul(h.T, dy)
+        out["dw1"] = matmul(x.T, dg)
+        out["dw_up"] = matmul(x.T, du)
+        out["dx"] = matmul(dg, to64(w1_i).T) + matmul(du, to64(w_up_i).T)
+    else:
+        a = saved["a"]
+        h = act_apply(a, act)
+        dh = matmul(dy, to64(w2_i).T)
+        if act == "relu":
+            da = dh * relu_grad(a)
+        elif act == "gelu":
+            da = dh * gelu_grad(a)
+        elif act == "none":
+            da = dh
+        else:
+            raise ValueError(act)
+        out["dw2"] = matmul(h.T, dy)
+        out["dw1"] = matmul(x.T, da)
+        out["dx"] = matmul(da, to64(w1_i).T)
+    return out
+
+
+def mlp_full_bwd(x, w1, w_up, w2, dy, act: str) -> Dict[str, np.ndarray]:
+    """Unsharded backward (the same chain rule with p = 1)."""
+    return mlp_shard_bwd(x, w1, w_up, w2, dy, act)
+
+
+def shard_mlp_weights(w1, w_up, w2, p: int, i: int):
+    """Rank i's (W1_i, W_up_i, W2_i): columns of W1/W_up and the matching rows of W2."""
+    w1 = to64(w1)
+    w2 = to64(w2)
+    b, n = shard_range(w1.shape[1], p, i)
+    w1_i = slice_cols(w1, b, n)
+    w_up_i = slice_cols(to64(w_up), b, n) if w_up is not None else None
+    w2_i = slice_rows(w2, b, n)
+    return w1_i, w_up_i, w2_i
+
+
+# ---------------------------------------------------------------------------
+# GQA projections.  [KL] second paragraph: rank i's fused QKV projection is
+# the column slices [Q_i | K_i | V_i] of the unsharded projections; its
+# o_proj consumes the rank's 1024-wide attention output and contributes a
+# partial 8192-wide residual update that is then summed over ranks.
+# ---------------------------------------------------------------------------
+def gqa_local_qkv_weight(wq, wk, wv, n_q: int, n_kv: int, head_dim: int, p: int, i: int) -> np.ndarray:
+    qb, ql, kb, kl = gqa_shard(n_q, n_kv, head_dim, p, i)
+    return np.concatenate([slice_cols(to64(wq), qb, ql), slice_cols(to64(wk), kb, kl),
+                           slice_cols(to64(wv), kb, kl)], axis=1)
+
+
+def gqa_qkv_full(x, wq, wk, wv) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    return matmul(x, wq), matmul(x, wk), matmul(x, wv)
+
+
+# ---------------------------------------------------------------------------
+# Work accounting.  [KS] "What happens if TP leaves the node": training costs
+# about 6 x params x tokens; the forward matmuls are 2 x params x tokens.
+# ---------------------------------------------------------------------------
+def mlp_shard_params(d: int, ff_i: int, act: str) -> int:
+    return (3 if act == "swiglu" else 2) * d * ff_i
+
+
+def mlp_fwd_flops(T: int, d: int, ff_i: int, act: str) -> int:
+    return 2 * mlp_shard_params(d, ff_i, act) * T
+
+
+def mlp_bwd_flops(T: int, d: int, ff_i: int, act: str) -> int:
+    return 4 * mlp_shard_params(d, ff_i, act) * T
+
+
+# ---------------------------------------------------------------------------
+# Comparison metric (relative Frobenius error and max-abs error relative to
+# the reference's largest magnitude).
+# ---------------------------------------------------------------------------
+def compare(got, ref) -> Tuple[float, float]:
+    g = to64(got)
+    r = to64(ref)
+    if g.shape != r.shape:
+        raise ValueError(f"shape mismatch {g.shape} vs {r.shape}")
+    if r.size == 0:
+        return 0.0, 0.0
+    diff = g - r
+    nr = float(np.linalg.norm(r))
+    mr = float(np.max(np.abs(r)))
+    rel_frob = float(np.linalg.norm(diff)) / nr if nr > 0 else float(np.linalg.norm(diff))
+    rel_max = float(np.max(np.abs(diff))) / mr if mr > 0 else float(np.max(np.abs(diff)))
+    return rel_frob, rel_max
+
+
+BF16_TOL = (5e-3, 1e-2)   # rel Frobenius, max-abs / max|ref|
+F32_TOL = (1e-5, 1e-5)
+
+
+def within(got, ref, tol=BF16_TOL) -> Tuple[bool, float, float]:
+    rf, rm = compare(got, ref)
+    return (rf <= tol[0] and rm <= tol[1]), rf, rm
+
+
+__all__: List[str] = [n for n in dir() if not n.startswith("_")]

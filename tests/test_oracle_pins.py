@@ -1,0 +1,360 @@
+"""Pins for the fp64 oracle: each check ties the oracle to something other than itself.
+
+Sources cited by page title and section:
+  "Why Tensor Parallelism has to stay inside the scale-up domain" -
+      "What is Tensor Parallel" (worked example), "What happens if TP leaves
+      the node" (6 x params x tokens).
+  "Tensor Parallelism" (inference-engineering notes) - paragraph 1 (column /
+      row algebra), paragraph 2 (GQA bookkeeping), paragraph 5 (KV heads bound p).
+  "How does tensor parallelism split a transformer feed-forward block's two
+      matmuls across devices?" - "Column split, then row split",
+      "The backward pass", "Common failure".
+  "Tensor-parallel all-reduce count per transformer layer in MLX
+      shard_linear" - Facts (bias added once after the sum).
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.special
+import scipy.stats
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def load_golden(name):
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            k, v = line.split(":", 1)
+            rows = [[float(t) for t in r.split()] for r in v.split(";")]
+            out[k.strip()] = np.array(rows if len(rows) > 1 else rows[0], dtype=np.float64)
+    return out
+
+
+# --------------------------------------------------------------------------
+# The pages' worked example (h=2, d_ff=3, TP=3), exact.
+# --------------------------------------------------------------------------
+def test_worked_example_unsharded_exact():
+    g = load_golden("worked_example.txt")
+    x = g["x"][None, :]
+    for act in ("none", "relu"):
+        y = O.col_linear(x, g["A"], act=act)
+        assert np.array_equal(y[0], g["y"])
+        assert np.array_equal(O.mlp_full(x, g["A"], None, g["B"], act)[0], g["z"])
+
+
+def test_worked_example_tp3_shards_exact():
+    g = load_golden("worked_example.txt")
+    x = g["x"][None, :]
+    p = int(g["tp"][0])
+    partials = []
+    for i in range(p):
+        w1_i, _, w2_i = O.shard_mlp_weights(g["A"], None, g["B"], p, i)
+        assert w1_i.shape == (2, 1) and w2_i.shape == (1, 2)   # one column of A, one row of B
+        y_i, _ = O.mlp_shard_fwd(x, w1_i, None, w2_i, "relu")
+        # each shard's intermediate is exactly the page's y[i]
+        assert O.col_linear(x, w1_i, act="relu")[0, 0] == g["y"][i]
+        partials.append(y_i)
+    assert np.array_equal(O.partial_sum(partials)[0], g["z"])
+
+
+# --------------------------------------------------------------------------
+# Exact rational brute force on tiny integer inputs.
+# --------------------------------------------------------------------------
+def _brute_mlp_relu(x, w1, w2):
+    T, d = len(x), len(x[0])
+    ff = len(w1[0])
+    h = [[max(Fraction(0), sum((x[t][k] * w1[k][j] for k in range(d)), Fraction(0))) for j in range(ff)]
+         for t in range(T)]
+    return [[sum((h[t][j] * w2[j][c] for j in range(ff)), Fraction(0)) for c in range(d)] for t in range(T)]
+
+
+@pytest.mark.parametrize("p", [1, 2, 3, 6])
+def test_bruteforce_fraction_relu(p):
+    rng = np.random.default_rng(100 + p)
+    T, d, ff = 3, 4, 6
+    x = rng.integers(-3, 4, size=(T, d))
+    w1 = rng.integers(-3, 4, size=(d, ff))
+    w2 = rng.integers(-3, 4, size=(ff, d))
+    exact = _brute_mlp_relu([[Fraction(int(v)) for v in r] for r in x],
+                            [[Fraction(int(v)) for v in r] for r in w1],
+                            [[Fraction(int(v)) for v in r] for r in w2])
+    exact = np.array([[float(v) for v in r] for r in exact])
+    assert np.array_equal(O.mlp_full(x, w1, None, w2, "relu"), exact)
+    parts = []
+    for i in range(p):
+        a, _, c = O.shard_mlp_weights(w1, None, w2, p, i)
+        parts.append(O.mlp_shard_fwd(x, a, None, c, "relu")[0])
+    assert np.array_equal(O.partial_sum(parts), exact)
+
+
+def test_bruteforce_matmul_triple_loop():
+    rng = np.random.default_rng(7)
+    a = rng.standard_normal((5, 7))
+    b = rng.standard_normal((7, 3))
+    ref = np.zeros((5, 3))
+    for i in range(5):
+        for j in range(3):
+            s = 0.0
+            for k in range(7):
+                s += a[i, k] * b[k, j]
+            ref[i, j] = s
+    np.testing.assert_allclose(O.matmul(a, b), ref, rtol=1e-13, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# Sharding invariants (column concatenation, sum of row partials).
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("act", ["relu", "gelu", "swiglu", "none"])
+@pytest.mark.parametrize("p", [1, 2, 3, 4, 8])
+def test_sum_of_partials_equals_unsharded(act, p):
+    rng = np.random.default_rng(p * 10 + len(act))
+    T, d, ff = 5, 16, 48
+    x = rng.standard_normal((T, d))
+    w1 = rng.standard_normal((d, ff)) * 0.3
+    wup = rng.standard_normal((d, ff)) * 0.3 if act == "swiglu" else None
+    w2 = rng.standard_normal((ff, d)) * 0.3
+    full = O.mlp_full(x, w1, wup, w2, act)
+    parts, hs = [], []
+    for i in range(p):
+        a, u, c = O.shard_mlp_weights(w1, wup, w2, p, i)
+        parts.append(O.mlp_shard_fwd(x, a, u, c, act)[0])
+        hs.append(O.col_linear(x, a, u, None, act))
+    rf, rm = O.compare(O.partial_sum(parts), full)
+    assert rf < 1e-12 and rm < 1e-12
+    # the concatenation of the column shards is the unsharded intermediate
+    h_full = O.col_linear(x, w1, wup, None, act)
+    np.testing.assert_allclose(np.concatenate(hs, axis=1), h_full, rtol=0, atol=1e-12)
+
+
+def test_row_parallel_bias_added_once():
+    """A row-parallel linear with bias: sum of partials + bias once equals the
+    unsharded biased linear layer x W + b (the bias is not multiplied by p)."""
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((4, 12))
+    w = rng.standard_normal((12, 5))
+    b = rng.standard_normal(5)
+    p = 4
+    zs = []
+    for i in range(p):
+        s, n = O.shard_range(12, p, i)
+        zs.append(O.row_linear_partial(x[:, s:s + n], w[s:s + n, :]))
+    direct = np.array([[sum(x[t, k] * w[k, j] for k in range(12)) + b[j] for j in range(5)] for t in range(4)])
+    np.testing.assert_allclose(O.partial_sum(zs, b), direct, rtol=1e-12, atol=1e-12)
+
+
+def test_column_bias_slices():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((3, 8))
+    w = rng.standard_normal((8, 12))
+    b = rng.standard_normal(12)
+    full = O.col_linear(x, w, bias=b, act="gelu")
+    for i in range(3):
+        s, n = O.shard_range(12, 3, i)
+        np.testing.assert_allclose(O.col_linear(x, w[:, s:s + n], bias=b[s:s + n], act="gelu"),
+                                   full[:, s:s + n], rtol=1e-13, atol=1e-13)
+
+
+def test_row_then_column_needs_a_reduction_first():
+    """Common failure: splitting the first matmul by rows yields partial sums,
+    and the nonlinearity does not commute with the sum."""
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((6, 8))
+    w1 = rng.standard_normal((8, 10))
+    parts = []
+    for i in range(2):
+        s, n = O.shard_range(8, 2, i)
+        parts.append(O.relu(O.row_linear_partial(x[:, s:s + n], w1[s:s + n, :])))
+    wrong = parts[0] + parts[1]
+    right = O.relu(O.matmul(x, w1))
+    assert np.max(np.abs(wrong - right)) > 1e-3
+
+
+# --------------------------------------------------------------------------
+# Activations: special values and library routines.
+# --------------------------------------------------------------------------
+def test_activation_special_values():
+    assert O.relu(np.array([-1.0]))[0] == 0.0 and O.relu(np.array([2.5]))[0] == 2.5
+    assert O.gelu(np.array([0.0]))[0] == 0.0
+    assert O.silu(np.array([0.0]))[0] == 0.0
+    # Phi(1) and sigmoid(1) to double precision
+    assert abs(O.gelu(np.array([1.0]))[0] - 0.8413447460685429) < 1e-15
+    assert abs(O.silu(np.array([1.0]))[0] - 0.7310585786300049) < 1e-15
+    big = np.array([40.0, -40.0])
+    np.testing.assert_allclose(O.gelu(big), [40.0, 0.0], atol=1e-300)
+    np.testing.assert_allclose(O.silu(big), [40.0, -40.0 * math.exp(-40.0)], rtol=1e-12)
+
+
+def test_activations_match_library_routines():
+    xs = np.linspace(-8, 8, 1001)
+    np.testing.assert_allclose(O.gelu(xs), xs * scipy.stats.norm.cdf(xs), rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(O.silu(xs), xs * scipy.special.expit(xs), rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(O.sigmoid(xs), scipy.special.expit(xs), rtol=1e-14, atol=0)
+
+
+@pytest.mark.parametrize("name", ["relu", "gelu", "silu"])
+def test_activation_derivatives_finite_difference(name):
+    f = getattr(O, name)
+    fp = getattr(O, name + "_grad")
+    xs = np.linspace(-5, 5, 401)
+    xs = xs[np.abs(xs) > 1e-3]            # ReLU is not differentiable at 0
+    eps = 1e-6
+    fd = (f(xs + eps) - f(xs - eps)) / (2 * eps)
+    np.testing.assert_allclose(fp(xs), fd, rtol=1e-7, atol=1e-8)
+
+
+# --------------------------------------------------------------------------
+# Backward: central finite differences of L = sum(y * dy) on tiny shapes.
+# --------------------------------------------------------------------------
+def _fd_check(act, oracle_mod=O, seed=0):
+    rng = np.random.default_rng(seed)
+    T, d, ff = 3, 4, 6
+    x = rng.standard_normal((T, d))
+    w1 = rng.standard_normal((d, ff)) * 0.7
+    wup = rng.standard_normal((d, ff)) * 0.7 if act == "swiglu" else None
+    w2 = rng.standard_normal((ff, d)) * 0.7
+    dy = rng.standard_normal((T, d))
+
+    def loss(x_, w1_, wup_, w2_):
+        y, _ = O.mlp_shard_fwd(x_, w1_, wup_, w2_, act)
+        return float(np.sum(y * dy))
+
+    g = oracle_mod.mlp_shard_bwd(x, w1, wup, w2, dy, act)
+    eps = 1e-6
+    worst = 0.0
+    params = {"dx": x, "dw1": w1, "dw2": w2}
+    if wup is not None:
+        params["dw_up"] = wup
+    for key, arr in params.items():
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            old = arr[idx]
+            arr[idx] = old + eps
+            lp = loss(x, w1, wup, w2)
+            arr[idx] = old - eps
+            lm = loss(x, w1, wup, w2)
+            arr[idx] = old
+            num[idx] = (lp - lm) / (2 * eps)
+        worst = max(worst, float(np.max(np.abs(num - g[key])) / (np.max(np.abs(num)) + 1e-30)))
+    return worst
+
+
+@pytest.mark.parametrize("act", ["relu", "gelu", "swiglu", "none"])
+def test_backward_finite_difference(act):
+    assert _fd_check(act) < 1e-6
+
+
+def test_planted_mistake_in_backward_is_caught(monkeypatch):
+    """A dropped term in silu' (s instead of s + g s (1 - s)) must fail the FD pin."""
+    monkeypatch.setattr(O.tp_oracle, "silu_grad", lambda g: O.sigmoid(g))
+    assert _fd_check("swiglu") > 1e-3
+
+
+def test_planted_sign_error_in_gelu_grad_is_caught(monkeypatch):
+    real = O.tp_oracle.gelu_grad
+    monkeypatch.setattr(O.tp_oracle, "gelu_grad", lambda a: real(a) - 2 * a * np.exp(-0.5 * a * a) / math.sqrt(2 * math.pi))
+    assert _fd_check("gelu") > 1e-3
+
+
+@pytest.mark.parametrize("act", ["swiglu", "relu"])
+def test_weight_gradients_are_shard_local_and_dx_partials_sum(act):
+    """The backward pass: weight gradients need no exchange (each shard's
+    gradient is the slice of the unsharded one), and the partial input
+    gradients sum to the unsharded input gradient."""
+    rng = np.random.default_rng(21)
+    T, d, ff, p = 6, 8, 24, 4
+    x = rng.standard_normal((T, d))
+    w1 = rng.standard_normal((d, ff)) * 0.4
+    wup = rng.standard_normal((d, ff)) * 0.4 if act == "swiglu" else None
+    w2 = rng.standard_normal((ff, d)) * 0.4
+    dy = rng.standard_normal((T, d))
+    full = O.mlp_full_bwd(x, w1, wup, w2, dy, act)
+    dxs = []
+    for i in range(p):
+        s, n = O.shard_range(ff, p, i)
+        a, u, c = O.shard_mlp_weights(w1, wup, w2, p, i)
+        gi = O.mlp_shard_bwd(x, a, u, c, dy, act)
+        np.testing.assert_allclose(gi["dw1"], full["dw1"][:, s:s + n], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(gi["dw2"], full["dw2"][s:s + n, :], rtol=1e-12, atol=1e-12)
+        if act == "swiglu":
+            np.testing.assert_allclose(gi["dw_up"], full["dw_up"][:, s:s + n], rtol=1e-12, atol=1e-12)
+        dxs.append(gi["dx"])
+    np.testing.assert_allclose(O.partial_sum(dxs), full["dx"], rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# Shard ranges and GQA bookkeeping.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("n,p", [(256, 4), (28672, 8), (3, 3), (14336, 8), (0, 2)])
+def test_shard_ranges_partition(n, p):
+    covered = []
+    for i in range(p):
+        b, ln = O.shard_range(n, p, i)
+        assert ln == n // p
+        covered.extend(range(b, b + ln))
+    assert covered == list(range(n))
+
+
+def test_shard_range_rejects_uneven():
+    with pytest.raises(ValueError):
+        O.shard_range(10, 4, 0)
+
+
+def test_gqa_shard_matches_the_page_numbers():
+    """h=8192, 64 Q heads, 8 KV heads, head dim 128, p=8: each rank owns 8 Q
+    heads and 1 KV head; local Q is 8192 x 1024, local K and V 8192 x 128,
+    o_proj takes a 1024-wide input."""
+    for i in range(8):
+        qb, ql, kb, kl = O.gqa_shard(64, 8, 128, 8, i)
+        assert (qb, ql, kb, kl) == (1024 * i, 1024, 128 * i, 128)
+        # the rank's Q heads all group with its own KV head (contiguous grouping)
+        for qh in range(qb // 128, (qb + ql) // 128):
+            assert qh // (64 // 8) == kb // 128
+    rng = np.random.default_rng(0)
+    wq = rng.standard_normal((8192, 8192)).astype(np.float32)
+    wk = rng.standard_normal((8192, 1024)).astype(np.float32)
+    wv = rng.standard_normal((8192, 1024)).astype(np.float32)
+    assert O.gqa_local_qkv_weight(wq, wk, wv, 64, 8, 128, 8, 3).shape == (8192, 1024 + 128 + 128)
+    with pytest.raises(ValueError):          # 8 KV heads cannot map onto p = 16
+        O.gqa_shard(64, 8, 128, 16, 0)
+
+
+def test_gqa_local_qkv_is_slice_of_unsharded():
+    rng = np.random.default_rng(5)
+    h, nq, nkv, hd, p = 16, 8, 4, 2, 4
+    x = rng.standard_normal((3, h))
+    wq, wk, wv = (rng.standard_normal((h, n * hd)) for n in (nq, nkv, nkv))
+    q, k, v = O.gqa_qkv_full(x, wq, wk, wv)
+    for i in range(p):
+        qb, ql, kb, kl = O.gqa_shard(nq, nkv, hd, p, i)
+        loc = O.matmul(x, O.gqa_local_qkv_weight(wq, wk, wv, nq, nkv, hd, p, i))
+        np.testing.assert_allclose(loc, np.concatenate([q[:, qb:qb + ql], k[:, kb:kb + kl], v[:, kb:kb + kl]], 1),
+                                   rtol=1e-13, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# Work accounting: training ~ 6 x params x tokens.
+# --------------------------------------------------------------------------
+def test_flop_accounting():
+    T, d, ff_i = 4096, 8192, 3584
+    n = O.mlp_shard_params(d, ff_i, "swiglu")
+    assert O.mlp_fwd_flops(T, d, ff_i, "swiglu") + O.mlp_bwd_flops(T, d, ff_i, "swiglu") == 6 * n * T
+    assert O.mlp_fwd_flops(T, d, ff_i, "swiglu") == 721_554_505_728
+    assert O.mlp_bwd_flops(2048, 4096, 1792, "swiglu") == 180_388_626_432
+    # the page's training example: 6 x 70e9 x 4096 over 8 GPUs at 400 TFLOP/s ~ 0.5 s
+    assert abs(6 * 70e9 * 4096 / 8 / 400e12 - 0.5) < 0.05
+
+
+def test_compare_metric():
+    r = np.array([[3.0, -4.0]])
+    assert O.compare(r, r) == (0.0, 0.0)
+    rf, rm = O.compare(r * 1.01, r)
+    assert abs(rf - 0.01) < 1e-12 and abs(rm - 0.04 / 4.0) < 1e-12

@@ -1,0 +1,158 @@
+"""Seeded synthetic inputs shared by the oracle side and the GPU side.
+
+This module draws random tensors and nothing else: it holds none of the
+method's arithmetic (no matmul, no activation, no slicing into shards).
+Both the fp64 oracle and the HIP path receive exactly the tensors made here,
+so the two sides never exchange values with each other.
+
+Recipe (the same for every workload):
+  * a ``torch.Generator('cpu')`` seeded per workload and per tensor;
+  * ``torch.randn`` in float32, scaled by the stated standard deviation;
+  * for bf16 workloads, rounded to bfloat16 by torch (round-to-nearest-even).
+The oracle upcasts the *rounded* values to float64, so the comparison
+measures only the GPU's arithmetic, not the input rounding.
+
+Distributions follow the workloads the pages describe: activations ~N(0, 1),
+weights ~N(0, 0.02^2) (std 0.02, the usual initialisation scale).  Weights are
+stored (in, out) row-major, as the feed-forward description writes W1 of
+shape (d, 4d) and W2 of shape (4d, d).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, List, Optional
+
+import torch
+
+WEIGHT_STD = 0.02
+
+
+@dataclasses.dataclass(frozen=True)
+class MlpWorkload:
+    """A per-rank MLP shard workload (one rank's columns of W1/W_up, rows of W2)."""
+    name: str
+    T: int            # tokens in the micro-batch
+    d: int            # hidden size
+    ff: int           # unsharded intermediate size
+    p: int            # tensor-parallel width
+    act: str          # "relu" | "gelu" | "swiglu"
+    dtype: str        # "bf16" | "f32"
+    seed: int
+
+    @property
+    def ff_i(self) -> int:
+        return self.ff // self.p
+
+
+@dataclasses.dataclass(frozen=True)
+class GqaWorkload:
+    """Per-rank grouped-query-attention projections (fused local QKV, o_proj)."""
+    name: str
+    T: int
+    h: int
+    n_q: int
+    n_kv: int
+    head_dim: int
+    p: int
+    seed: int
+
+
+# The five workloads.  Sizes: tiny fp32 check; 70B-class SwiGLU MLP shard at
+# decode (T=64) and prefill (T=4096) for p=8; GQA projections of a 70B-class
+# model (h=8192, 64 Q heads, 8 KV heads, head_dim 128, p=8); SwiGLU backward
+# with d=4096, d_ff=14336, p=8, T=2048.
+TINY = MlpWorkload("tiny_fp32_relu_p4", T=4, d=64, ff=256, p=4, act="relu", dtype="f32", seed=0)
+DECODE = MlpWorkload("swiglu_mlp_decode_T64", T=64, d=8192, ff=28672, p=8, act="swiglu",
+                     dtype="bf16", seed=1)
+PREFILL = MlpWorkload("swiglu_mlp_prefill_T4096", T=4096, d=8192, ff=28672, p=8,
+                      act="swiglu", dtype="bf16", seed=2)
+GQA_PREFILL = GqaWorkload("gqa_proj_T4096", T=4096, h=8192, n_q=64, n_kv=8, head_dim=128, p=8, seed=3)
+GQA_DECODE = GqaWorkload("gqa_proj_T64", T=64, h=8192, n_q=64, n_kv=8, head_dim=128, p=8, seed=3)
+BACKWARD = MlpWorkload("swiglu_mlp_bwd_T2048", T=2048, d=4096, ff=14336, p=8, act="swiglu",
+                       dtype="bf16", seed=4)
+
+ALL = {w.name: w for w in (TINY, DECODE, PREFILL, GQA_PREFILL, GQA_DECODE, BACKWARD)}
+
+
+def _gen(seed: int, stream: int) -> torch.Generator:
+    g = torch.Generator(device="cpu")
+    # one independent stream per (workload seed, tensor id)
+    g.manual_seed(seed * 1_000_003 + stream)
+    return g
+
+
+def normal(shape, std: float, seed: int, stream: int, dtype: str = "bf16") -> torch.Tensor:
+    """fp32 N(0, std^2) draw, rounded to bf16 (RNE) unless dtype == 'f32'."""
+    t = torch.randn(*shape, generator=_gen(seed, stream), dtype=torch.float32)
+    if std != 1.0:
+        t.mul_(std)
+    if dtype == "bf16":
+        return t.to(torch.bfloat16)
+    if dtype == "f32":
+        return t
+    raise ValueError(f"unknown dtype {dtype}")
+
+
+# Tensor stream ids (fixed so every consumer draws the same values).
+S_X, S_W1, S_WUP, S_W2, S_DY = 1, 2, 3, 4, 5
+S_WQ, S_WK, S_WV, S_WO, S_ATTN = 11, 12, 13, 14, 15
+
+
+def mlp_unsharded(w: MlpWorkload, with_dy: bool = False, T: Optional[int] = None) -> Dict[str, torch.Tensor]:
+    """Unsharded x, W1 (d, ff), [W_up (d, ff)], W2 (ff, d) and optionally dy (T, d)."""
+    T = w.T if T is None else T
+    out = {
+        "x": normal((T, w.d), 1.0, w.seed, S_X, w.dtype),
+        "w1": normal((w.d, w.ff), WEIGHT_STD, w.seed, S_W1, w.dtype),
+        "w2": normal((w.ff, w.d), WEIGHT_STD, w.seed, S_W2, w.dtype),
+    }
+    if w.act == "swiglu":
+        out["w_up"] = normal((w.d, w.ff), WEIGHT_STD, w.seed, S_WUP, w.dtype)
+    if with_dy:
+        out["dy"] = normal((T, w.d), 1.0, w.seed, S_DY, w.dtype)
+    return out
+
+
+def mlp_rank_weights(w: MlpWorkload, rank: int, weight_seed: Optional[int] = None) -> Dict[str, torch.Tensor]:
+    """One rank's weights drawn directly at shard shape.
+
+    For the 70B-class shards the unsharded matrices would be 8192 x 28672; the
+    entries are i.i.d., so drawing rank ``rank``'s block directly has the same
+    distribution as slicing it out of an unsharded draw.  Decode and prefill
+    share these weights (``weight_seed`` defaults to the decode seed)."""
+    s = (DECODE.seed if weight_seed is None else weight_seed) * 64 + rank
+    out = {
+        "w1": normal((w.d, w.ff_i), WEIGHT_STD, s, S_W1, w.dtype),
+        "w2": normal((w.ff_i, w.d), WEIGHT_STD, s, S_W2, w.dtype),
+    }
+    if w.act == "swiglu":
+        out["w_up"] = normal((w.d, w.ff_i), WEIGHT_STD, s, S_WUP, w.dtype)
+    return out
+
+
+def mlp_input(w: MlpWorkload, T: Optional[int] = None) -> torch.Tensor:
+    T = w.T if T is None else T
+    return normal((T, w.d), 1.0, w.seed, S_X, w.dtype)
+
+
+def gqa_unsharded(w: GqaWorkload) -> Dict[str, torch.Tensor]:
+    """Unsharded Wq (h, n_q*hd), Wk, Wv (h, n_kv*hd), Wo (n_q*hd, h), x (T, h) and
+    the p ranks' attention outputs attn (T, n_q*hd) (rank i owns a 1024-wide slice)."""
+    qw = w.n_q * w.head_dim
+    kvw = w.n_kv * w.head_dim
+    return {
+        "x": normal((w.T, w.h), 1.0, w.seed + w.T, S_X),
+        "wq": normal((w.h, qw), WEIGHT_STD, w.seed, S_WQ),
+        "wk": normal((w.h, kvw), WEIGHT_STD, w.seed, S_WK),
+        "wv": normal((w.h, kvw), WEIGHT_STD, w.seed, S_WV),
+        "wo": normal((qw, w.h), WEIGHT_STD, w.seed, S_WO),
+        "attn": normal((w.T, qw), 1.0, w.seed + w.T, S_ATTN),
+    }
+
+
+def row_subset(T: int, n: int, seed: int) -> List[int]:
+    """Seeded, sorted subset of ``n`` distinct rows out of ``T`` (all rows if T <= n)."""
+    if T <= n:
+        return list(range(T))
+    g = _gen(seed, 99)
+    return sorted(torch.randperm(T, generator=g)[:n].tolist())
