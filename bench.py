@@ -1,0 +1,285 @@
+#!/usr/bin/env python3
+"""Benchmark: one tensor-parallel rank's SwiGLU MLP shard on one MI355X.
+
+A step is one rank's shard forward of a 70B-class SwiGLU MLP at decode size
+(T=64 tokens, d=8192, ff_i=28672/8=3584, bf16): the column-parallel gate/up
+GEMM with the SwiGLU epilogue fused, then the row-parallel down GEMM writing
+the full-shape partial y_i.  Inputs are resident in HBM before timing starts;
+three distinct weight sets (528 MB) rotate so the 256 MB Infinity Cache
+cannot serve them.  The headline value is algorithmic bytes (weights + x +
+y_i) per second.
+
+The same JSON line carries:
+  roofline      the dominant kernel (the fused gate/up GEMM) timed alone with
+                HIP events on its stream: algorithmic bytes / launch time vs 8 TB/s;
+  rows          the other hot-path rows: prefill shard (T=4096), GQA
+                projections (T=4096 and 64), the shard backward (T=2048,
+                d=4096, ff_i=1792) and the fp32 sum of partials;
+  cpu_baseline  the fp64 oracle computing the same decode step on the host.
+
+    python bench.py [--steps K] [--warmup W] [--rows all|none|prefill,gqa,bwd,sum]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "per-rank sharded MLP TFLOP/s (prefill) & GB/s (decode), % of MFMA/HBM peak"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def time_gpu(fn, steps: int, warmup: int) -> float:
+    """Average milliseconds per call of fn(i), timed with HIP events on the
+    current stream (the stream the library launches on)."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(s)
+    for i in range(steps):
+        fn(i)
+    end.record(s)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def gpu_normal(shape, std, seed, dev):
+    import torch
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    return (torch.randn(*shape, generator=g, device=dev, dtype=torch.float32) * std).to(torch.bfloat16)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--rows", default="all")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's shard only; --gpus {args.gpus} is not supported "
+              "(the per-rank work is independent of the group size; run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+    import workloads as W
+    import tensor_sharded_transformer_amd as tp
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    tp.load()
+
+    # ---------------- headline: decode shard step -------------------------------
+    wl = W.DECODE
+    T, d, ff_i = wl.T, wl.d, wl.ff_i
+    R = 3
+    log(f"bench: generating {R} weight sets for {wl.name} ...")
+    sets = []
+    for r in range(R):
+        wt = W.mlp_rank_weights(wl, r)
+        sets.append({k: v.to(dev) for k, v in wt.items()})
+        del wt
+    x = W.mlp_input(wl).to(dev)
+    y = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
+    ws = tp.new_workspace(tp.tp_mlp_shard_fwd_workspace(T, d, ff_i, tp.TP_BF16, "swiglu"), dev)
+
+    def step(i):
+        s = sets[i % R]
+        tp.tp_mlp_shard_fwd(x, s["w1"], s["w_up"], s["w2"], y, "swiglu", ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(args.steps):
+        step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    bytes_step = (3 * d * ff_i + 2 * T * d) * 2     # weights + x + y_i, bf16
+    value = bytes_step / (ms * 1e-3) / 1e9
+    log(f"bench: decode shard {ms * 1e3:.1f} us/step -> {value:.0f} GB/s ({value / HBM_PEAK_GBS:.1%} of HBM); "
+        f"wall {wall:.3f}s")
+
+    # ---------------- roofline: the fused gate/up GEMM alone ------------------------
+    h = torch.empty(T, ff_i, dtype=torch.bfloat16, device=dev)
+    ws_c = tp.new_workspace(tp.tp_col_linear_workspace(T, d, ff_i, tp.TP_BF16, "swiglu"), dev)
+
+    def gate_up(i):
+        s = sets[i % R]
+        tp.tp_col_linear(x, s["w1"], s["w_up"], None, h, "swiglu", ws_c)
+
+    k_ms = time_gpu(gate_up, args.steps, args.warmup)
+    k_bytes = (2 * d * ff_i + T * d + T * ff_i) * 2
+    k_gbs = k_bytes / (k_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "gemm_bf16_kernel<64,128,...,dual,EPI_SWIGLU> (fused gate/up GEMM + SwiGLU)",
+                "algorithmic_bytes": k_bytes, "avg_launch_us": round(k_ms * 1e3, 2)}
+    log(f"bench: gate/up GEMM {k_ms * 1e3:.1f} us -> {k_gbs:.0f} GB/s")
+    down_ms = None
+
+    rows = {}
+    want = set(["prefill", "gqa", "bwd", "sum"]) if args.rows == "all" else (
+        set() if args.rows == "none" else set(args.rows.split(",")))
+    steps_r = max(10, args.steps // 2)
+
+    if "sum" in want:
+        parts = [torch.randn(T, d, device=dev).to(torch.bfloat16) for _ in range(8)]
+        yf = torch.empty(T, d, dtype=torch.float32, device=dev)
+        t_ = time_gpu(lambda i: tp.tp_partial_sum(parts, None, yf), steps_r, 5)
+        b_ = (8 * T * d * 2 + T * d * 4)
+        rows["sum_partials_decode_p8"] = {"us": round(t_ * 1e3, 2), "GB/s": round(b_ / t_ / 1e6, 1)}
+        T5, d5 = W.BACKWARD.T, W.BACKWARD.d
+        parts = [torch.randn(T5, d5, device=dev).to(torch.bfloat16) for _ in range(8)]
+        yf = torch.empty(T5, d5, dtype=torch.float32, device=dev)
+        t_ = time_gpu(lambda i: tp.tp_partial_sum(parts, None, yf), steps_r, 5)
+        b_ = (8 * T5 * d5 * 2 + T5 * d5 * 4)
+        rows["sum_partials_dx_p8_T2048"] = {"us": round(t_ * 1e3, 2), "GB/s": round(b_ / t_ / 1e6, 1),
+                                            "frac_hbm": round(b_ / t_ / 1e6 / HBM_PEAK_GBS, 4)}
+        del parts
+
+    if "prefill" in want:
+        xp = W.mlp_input(W.PREFILL).to(dev)
+        Tp = W.PREFILL.T
+        yp = torch.empty(Tp, d, dtype=torch.bfloat16, device=dev)
+        wsp = tp.new_workspace(tp.tp_mlp_shard_fwd_workspace(Tp, d, ff_i, tp.TP_BF16, "swiglu"), dev)
+        s0 = sets[0]
+        t_ = time_gpu(lambda i: tp.tp_mlp_shard_fwd(xp, sets[i % R]["w1"], sets[i % R]["w_up"], sets[i % R]["w2"],
+                                                    yp, "swiglu", wsp), steps_r, 3)
+        fl = 3 * 2 * Tp * d * ff_i
+        rows["prefill_mlp_shard_T4096"] = {"us": round(t_ * 1e3, 1), "TFLOP/s": round(fl / t_ / 1e9, 1),
+                                           "frac_mfma": round(fl / t_ / 1e9 / BF16_PEAK_TFLOPS, 4)}
+        hp = torch.empty(Tp, ff_i, dtype=torch.bfloat16, device=dev)
+        t_ = time_gpu(lambda i: tp.tp_col_linear(xp, s0["w1"], s0["w_up"], None, hp, "swiglu"), steps_r, 3)
+        fl = 2 * 2 * Tp * d * ff_i
+        rows["prefill_gate_up_gemm"] = {"us": round(t_ * 1e3, 1), "TFLOP/s": round(fl / t_ / 1e9, 1),
+                                        "frac_mfma": round(fl / t_ / 1e9 / BF16_PEAK_TFLOPS, 4)}
+        t_ = time_gpu(lambda i: tp.tp_row_linear_partial(hp, s0["w2"], yp), steps_r, 3)
+        fl = 2 * Tp * d * ff_i
+        rows["prefill_down_gemm"] = {"us": round(t_ * 1e3, 1), "TFLOP/s": round(fl / t_ / 1e9, 1),
+                                     "frac_mfma": round(fl / t_ / 1e9 / BF16_PEAK_TFLOPS, 4)}
+        del xp, yp, wsp, hp
+
+    if "gqa" in want:
+        h_, q_, o_ = 8192, 1280, 1024
+        for Tg in (4096, 64):
+            nset = 1 if Tg > 64 else 32    # >= 512 MB of weights rotate at decode size
+            wqkv = gpu_normal((nset, h_, q_), 0.02, 11, dev)
+            wo = gpu_normal((nset, o_, h_), 0.02, 12, dev)
+            xg = gpu_normal((Tg, h_), 1.0, 13, dev)
+            ag = gpu_normal((Tg, o_), 1.0, 14, dev)
+            qkv = torch.empty(Tg, q_, dtype=torch.bfloat16, device=dev)
+            og = torch.empty(Tg, h_, dtype=torch.bfloat16, device=dev)
+            wsq = tp.new_workspace(tp.tp_col_linear_workspace(Tg, h_, q_, tp.TP_BF16, "none"), dev)
+            wso = tp.new_workspace(tp.tp_row_linear_partial_workspace(Tg, o_, h_, tp.TP_BF16), dev)
+            tq = time_gpu(lambda i: tp.tp_col_linear(xg, wqkv[i % nset], None, None, qkv, "none", wsq), steps_r, 3)
+            to = time_gpu(lambda i: tp.tp_row_linear_partial(ag, wo[i % nset], og, wso), steps_r, 3)
+            if Tg > 64:
+                fq, fo = 2 * Tg * h_ * q_, 2 * Tg * o_ * h_
+                rows[f"gqa_qkv_T{Tg}"] = {"us": round(tq * 1e3, 1), "TFLOP/s": round(fq / tq / 1e9, 1),
+                                          "frac_mfma": round(fq / tq / 1e9 / BF16_PEAK_TFLOPS, 4)}
+                rows[f"gqa_oproj_T{Tg}"] = {"us": round(to * 1e3, 1), "TFLOP/s": round(fo / to / 1e9, 1),
+                                            "frac_mfma": round(fo / to / 1e9 / BF16_PEAK_TFLOPS, 4)}
+            else:
+                bq = (h_ * q_ + Tg * h_ + Tg * q_) * 2
+                bo = (o_ * h_ + Tg * o_ + Tg * h_) * 2
+                rows[f"gqa_qkv_T{Tg}"] = {"us": round(tq * 1e3, 2), "GB/s": round(bq / tq / 1e6, 1),
+                                          "frac_hbm": round(bq / tq / 1e6 / HBM_PEAK_GBS, 4)}
+                rows[f"gqa_oproj_T{Tg}"] = {"us": round(to * 1e3, 2), "GB/s": round(bo / to / 1e6, 1),
+                                            "frac_hbm": round(bo / to / 1e6 / HBM_PEAK_GBS, 4)}
+            del wqkv, wo, xg, ag, qkv, og
+
+    if "bwd" in want:
+        wb = W.BACKWARD
+        Tb, db, fb = wb.T, wb.d, wb.ff_i
+        x5 = gpu_normal((Tb, db), 1.0, 21, dev)
+        dy5 = gpu_normal((Tb, db), 1.0, 22, dev)
+        w1 = gpu_normal((db, fb), 0.02, 23, dev)
+        wu = gpu_normal((db, fb), 0.02, 24, dev)
+        w2 = gpu_normal((fb, db), 0.02, 25, dev)
+        sv = torch.empty(Tb, 2 * fb, dtype=torch.bfloat16, device=dev)
+        y5 = torch.empty(Tb, db, dtype=torch.bfloat16, device=dev)
+        wsf = tp.new_workspace(tp.tp_mlp_shard_fwd_workspace(Tb, db, fb, tp.TP_BF16, "swiglu"), dev)
+        tp.tp_mlp_shard_fwd(x5, w1, wu, w2, y5, "swiglu", wsf, sv)
+        wsb = tp.new_workspace(tp.tp_mlp_shard_bwd_workspace(Tb, db, fb, tp.TP_BF16, "swiglu"), dev)
+        g1, gu, g2, gx = (torch.empty_like(t) for t in (w1, wu, w2, x5))
+        t_ = time_gpu(lambda i: tp.tp_mlp_shard_bwd(x5, w1, wu, w2, sv, dy5, g1, gu, g2, gx, "swiglu", wsb),
+                      steps_r, 3)
+        fl = 4 * 3 * db * fb * Tb
+        rows["bwd_mlp_shard_T2048"] = {"us": round(t_ * 1e3, 1), "TFLOP/s": round(fl / t_ / 1e9, 1),
+                                       "frac_mfma": round(fl / t_ / 1e9 / BF16_PEAK_TFLOPS, 4)}
+
+    # ---------------- CPU baseline: the fp64 oracle on the same decode step ------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        import numpy as np
+        import oracle as O
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [os.cpu_count()])
+        except Exception:
+            cores = os.cpu_count()
+        wt = W.mlp_rank_weights(wl, 0)
+        w64 = {k: O.to64(v) for k, v in wt.items()}
+        x64 = O.to64(W.mlp_input(wl))
+        reps, t_cpu = 0, 0.0
+        while t_cpu < args.cpu_seconds and reps < 50:
+            c0 = time.perf_counter()
+            O.mlp_shard_fwd(x64, w64["w1"], w64["w_up"], w64["w2"], "swiglu")
+            t_cpu += time.perf_counter() - c0
+            reps += 1
+        per = t_cpu / reps
+        cpu = {"value": round(bytes_step / per / 1e9, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
+               "sample": f"full decode shard step (T=64, d=8192, ff_i=3584, fp64 numpy) x {reps} reps, "
+                         f"{per:.3f} s/step",
+               "ms_per_step": round(per * 1e3, 2)}
+        log(f"bench: oracle {per * 1e3:.1f} ms/step on {cores} threads")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02^2) weights, bf16)",
+        "config": {"workload": wl.name, "T": T, "d": d, "ff_i": ff_i, "p": wl.p, "act": "swiglu",
+                   "weight_sets_rotated": R, "algorithmic_bytes_per_step": bytes_step,
+                   "frac_hbm_peak": round(value / HBM_PEAK_GBS, 4)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "rows": rows,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,195 @@
+/*
+ * tpshard.h - C ABI for one rank's share of a tensor-parallel transformer block
+ * on AMD MI355X (gfx950).
+ *
+ * The operations follow these pages:
+ *   [KL]  "Tensor Parallelism" (inference-engineering notes), first paragraph:
+ *         Y = XW; column parallelism splits W = [W_1 .. W_p] along its output
+ *         dimension, so device i computes Y_i = X W_i; row parallelism splits W
+ *         along its input dimension and X = [X_1 .. X_p] to match, so device i
+ *         computes the full-shape partial Z_i = X_i W_i and Y = sum_i Z_i.
+ *         Second paragraph: GQA bookkeeping (h=8192, 64 Q heads, 8 KV heads,
+ *         head dim 128, p=8: 8 Q heads and 1 KV head per rank).
+ *   [FFN] "How does tensor parallelism split a transformer feed-forward
+ *         block's two matmuls across devices?", sections "The shape of the
+ *         block", "Column split, then row split" (First matmul,
+ *         column-parallel / The nonlinearity is free / Second matmul,
+ *         row-parallel / One collective) and "The backward pass".
+ *   [MLX] "Tensor-parallel all-reduce count per transformer layer in MLX
+ *         shard_linear", Facts: the sharded-to-all linear multiplies by its
+ *         slice, sums across ranks, then adds the bias once.
+ *
+ * Conventions for every entry point
+ *   - Pointers marked (device) are device memory owned by the caller; the
+ *     library allocates nothing and keeps no state except a thread-local
+ *     error string.  Host pointers are marked (host).
+ *   - All matrices are dense, contiguous and row-major.  Weights are stored
+ *     (in, out): W1 is (d, n), W2 is (n, d), as the feed-forward page writes
+ *     W1 with shape (d, 4d).  This is NOT torch nn.Linear's (out, in).
+ *   - dtype TP_BF16: inputs bf16, fp32 accumulation, outputs rounded to bf16
+ *     with round-to-nearest-even unless an out_dtype says otherwise.
+ *     dtype TP_F32: fp32 everywhere.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and is asynchronous: no call synchronises the host.
+ *   - All argument checks run on the host before anything is launched, so a
+ *     rejected call has no side effect.  A launch failure returns TP_ERR_HIP
+ *     with the runtime's message in tp_last_error().
+ *   - T == 0 (no tokens) is a valid no-op returning TP_OK.
+ *   - Outputs may not alias inputs (except `h` in tp_act_inplace).
+ */
+#ifndef TPSHARD_H
+#define TPSHARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TPSHARD_ABI_VERSION 1
+
+typedef struct ihipStream_t* tp_stream; /* same type as hipStream_t */
+
+typedef enum {
+  TP_OK = 0,
+  TP_ERR_NULL = 1,        /* a required pointer is NULL                       */
+  TP_ERR_SHAPE = 2,       /* negative / overflowing size, uneven split, ...   */
+  TP_ERR_DTYPE = 3,       /* unknown or unsupported dtype combination         */
+  TP_ERR_ACT = 4,         /* unknown act, or up/w_up/bias inconsistent with it */
+  TP_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required       */
+  TP_ERR_UNSUPPORTED = 6, /* valid request this build does not implement      */
+  TP_ERR_HIP = 7          /* the HIP runtime reported an error                */
+} tp_status;
+
+typedef enum { TP_BF16 = 0, TP_F32 = 1 } tp_dtype;
+
+/* Activations on the owned columns ([FFN] "The nonlinearity is free"):
+ *   RELU   max(a, 0)                      (derivative at 0 taken as 0)
+ *   GELU   exact erf form 0.5 a (1 + erf(a / sqrt 2))
+ *   SWIGLU silu(g) * u with silu(g) = g / (1 + exp(-g)), g = x W_gate_i and
+ *          u = x W_up_i over the same owned column range. */
+typedef enum { TP_ACT_NONE = 0, TP_ACT_RELU = 1, TP_ACT_GELU = 2, TP_ACT_SWIGLU = 3 } tp_act;
+
+/* ---------------------------------------------------------------------------
+ * Column-parallel linear ([KL] Y_i = X W_i; [FFN] "First matmul,
+ * column-parallel" and "The nonlinearity is free").
+ *   y = act(x . w + bias)                     for NONE / RELU / GELU
+ *   y = silu(x . w) * (x . w_up)              for SWIGLU
+ * x (T, K) (device), w and w_up (K, N_i) (device), bias (N_i) or NULL
+ * (device; this shard's slice of the column bias; must be NULL for SWIGLU),
+ * y (T, N_i) (device).  Errors: TP_ERR_NULL, TP_ERR_SHAPE (negative sizes),
+ * TP_ERR_ACT (w_up given iff SWIGLU violated, or bias with SWIGLU),
+ * TP_ERR_DTYPE, TP_ERR_HIP. */
+tp_status tp_col_linear(const void* x, const void* w, const void* w_up, const void* bias, void* y,
+                        void* ws, size_t ws_bytes, int64_t T, int64_t K, int64_t N_i, tp_dtype dtype,
+                        tp_act act, tp_stream stream);
+
+/* Optional workspace (bytes) for tp_col_linear: with it, decode-sized calls
+ * split K over more workgroups; ws may be NULL (then ws_bytes is ignored and
+ * the call runs unsplit).  A non-NULL ws smaller than this is TP_ERR_WORKSPACE.
+ * Same zero-fill rule as tp_mlp_shard_fwd_workspace.  Returns 0 when no
+ * workspace would be used. */
+size_t tp_col_linear_workspace(int64_t T, int64_t K, int64_t N_i, tp_dtype dtype, tp_act act);
+
+/* Activation applied in place to owned columns ([FFN] "The nonlinearity is
+ * free").  h (T, N_i) (device) is overwritten with act(h); for SWIGLU h holds
+ * the gate pre-activation and up (T, N_i) (device) the up pre-activation,
+ * and h <- silu(h) * up.  NONE is a no-op.  `up` must be non-NULL iff SWIGLU
+ * (TP_ERR_ACT otherwise). */
+tp_status tp_act_inplace(void* h, const void* up, int64_t T, int64_t N_i, tp_dtype dtype,
+                         tp_act act, tp_stream stream);
+
+/* Row-parallel linear producing the full-shape partial ([KL] Z_i = X_i W_i;
+ * [FFN] "Second matmul, row-parallel").  x_i (T, K_i), w_i (K_i, N), z_i
+ * (T, N), all device.  Never adds a bias ([MLX]: the bias goes after the sum,
+ * see tp_partial_sum).  in_dtype bf16 allows out_dtype bf16 or f32; in_dtype
+ * f32 requires out_dtype f32.  ws/ws_bytes optional (see
+ * tp_row_linear_partial_workspace). */
+tp_status tp_row_linear_partial(const void* x_i, const void* w_i, void* z_i, void* ws,
+                                size_t ws_bytes, int64_t T, int64_t K_i, int64_t N,
+                                tp_dtype in_dtype, tp_dtype out_dtype, tp_stream stream);
+
+/* Optional workspace (bytes) for tp_row_linear_partial; same rules as
+ * tp_col_linear_workspace. */
+size_t tp_row_linear_partial_workspace(int64_t T, int64_t K_i, int64_t N, tp_dtype in_dtype);
+
+/* Workspace (bytes) tp_mlp_shard_fwd needs for these sizes.  Always > 0 for
+ * T > 0.  The workspace must be zero-filled before its FIRST use (e.g. with
+ * tp_workspace_init); every call leaves its counter region zeroed again, so a
+ * workspace can be reused by later calls on the same stream.  Calls that run
+ * concurrently must not share a workspace. */
+size_t tp_mlp_shard_fwd_workspace(int64_t T, int64_t d, int64_t ff_i, tp_dtype dtype, tp_act act);
+
+/* One rank's feed-forward shard ([FFN] "Column split, then row split"):
+ *   y_i = act(x . w1_i [, x . w_up_i]) . w2_i
+ * x (T, d), w1_i and w_up_i (d, ff_i), w2_i (ff_i, d), y_i (T, d): the
+ * full-shape partial that the group's all-reduce would sum.  w_up_i must be
+ * non-NULL iff SWIGLU.  The intermediate h_i (T, ff_i) is kept in the
+ * workspace in `dtype` (bf16 for TP_BF16).  saved (device, nullable)
+ * receives the pre-activations the backward needs: (T, 2*ff_i) as
+ * [G_i | U_i] per row for SWIGLU, (T, ff_i) A_i otherwise, in `dtype`.
+ * out_dtype: TP_BF16 or TP_F32 for dtype bf16, TP_F32 for dtype f32.
+ * ws (device) of ws_bytes >= tp_mlp_shard_fwd_workspace(...). */
+tp_status tp_mlp_shard_fwd(const void* x, const void* w1_i, const void* w_up_i, const void* w2_i,
+                           void* y_i, void* saved, void* ws, size_t ws_bytes, int64_t T, int64_t d,
+                           int64_t ff_i, tp_dtype dtype, tp_dtype out_dtype, tp_act act,
+                           tp_stream stream);
+
+/* Workspace (bytes) tp_mlp_shard_bwd needs (same zero-fill rule as forward). */
+size_t tp_mlp_shard_bwd_workspace(int64_t T, int64_t d, int64_t ff_i, tp_dtype dtype, tp_act act);
+
+/* One rank's backward ([FFN] "The backward pass"): dy (T, d) is the same on
+ * every rank; the shard produces its own weight gradients (no exchange) and a
+ * partial input gradient dx_i (T, d) that the group sums.
+ *   dW2_i = h_i^T dy,  dh_i = dy W2_i^T,
+ *   SWIGLU: dG = dh_i * U * silu'(G), dU = dh_i * silu(G),
+ *           dW1_i = x^T dG, dW_up_i = x^T dU, dx_i = dG W1_i^T + dU W_up_i^T
+ *   RELU/GELU/NONE: dA = dh_i * act'(A), dW1_i = x^T dA, dx_i = dA W1_i^T
+ * saved (device) must be what tp_mlp_shard_fwd wrote for the same x and
+ * weights; h_i is recomputed from it.  dw1_i, dw_up_i (d, ff_i), dw2_i
+ * (ff_i, d), dx_i (T, d), all device, in `dtype`.  dw_up_i and w_up_i
+ * non-NULL iff SWIGLU.  ws as for the forward. */
+tp_status tp_mlp_shard_bwd(const void* x, const void* w1_i, const void* w_up_i, const void* w2_i,
+                           const void* saved, const void* dy, void* dw1_i, void* dw_up_i,
+                           void* dw2_i, void* dx_i, void* ws, size_t ws_bytes, int64_t T,
+                           int64_t d, int64_t ff_i, tp_dtype dtype, tp_act act, tp_stream stream);
+
+/* Sum of the p full-shape partials, then the bias once ([KL] Y = sum_i Z_i;
+ * [FFN] "One collective"; [MLX] bias after the sum).  This is the one-GPU
+ * stand-in for the group's all-reduce.  z (host array of p device pointers),
+ * each (T, N) in in_dtype; bias (N) in in_dtype or NULL (device); y (T, N)
+ * in out_dtype (device).  Accumulation is fp32 (fp32 also for f32 inputs),
+ * in ascending i, so the result is deterministic.  1 <= p <= 64. */
+tp_status tp_partial_sum(const void* const* z, int p, const void* bias, void* y, int64_t T,
+                         int64_t N, tp_dtype in_dtype, tp_dtype out_dtype, tp_stream stream);
+
+/* Zero-fills `bytes` of device memory ws on `stream` with a kernel (no
+ * memset node, so it is safe to capture in a graph). */
+tp_status tp_workspace_init(void* ws, size_t bytes, tp_stream stream);
+
+/* ---- host helpers (no GPU needed) ------------------------------------- */
+
+/* Shard i of n_total cut into p equal contiguous chunks ([FFN] "Column split,
+ * then row split": device i owns columns i*n/p .. (i+1)*n/p of W1 and the
+ * matching rows of W2).  TP_ERR_SHAPE if n_total % p != 0, p <= 0, i out of
+ * range or n_total < 0; TP_ERR_NULL if an output pointer is NULL (host). */
+tp_status tp_shard_range(int64_t n_total, int p, int i, int64_t* begin, int64_t* len);
+
+/* Rank i's GQA column ranges ([KL] second paragraph; [FFN] attention
+ * paragraph: a head is never split, so both head counts must divide by p).
+ * Heads are assigned contiguously, so Q head j shares KV head
+ * j / (n_q_heads / n_kv_heads) and both live on the same rank.  Outputs
+ * (host) are column offsets/lengths into the unsharded Q and K/V
+ * projections.  TP_ERR_SHAPE if a head count is not divisible by p. */
+tp_status tp_gqa_shard(int n_q_heads, int n_kv_heads, int head_dim, int p, int i,
+                       int64_t* q_begin, int64_t* q_len, int64_t* kv_begin, int64_t* kv_len);
+
+const char* tp_status_string(tp_status s);
+const char* tp_last_error(void);
+int tp_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TPSHARD_H */

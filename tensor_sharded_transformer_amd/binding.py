@@ -1,0 +1,228 @@
+"""Thin ctypes binding over libtpshard.so (the C ABI in include/tpshard.h).
+
+Argument marshalling only: every function below checks that the torch tensors
+it is given have the shapes/dtypes the C entry point documents, passes their
+device pointers and the current HIP stream, and raises ``TpError`` on a
+non-zero status.  All arithmetic happens in the library's HIP kernels; there
+is no fallback path: if the library is not built, loading it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+from . import build as _build
+
+TP_BF16, TP_F32 = 0, 1
+ACT = {"none": 0, "relu": 1, "gelu": 2, "swiglu": 3}
+STATUS = {0: "TP_OK", 1: "TP_ERR_NULL", 2: "TP_ERR_SHAPE", 3: "TP_ERR_DTYPE", 4: "TP_ERR_ACT",
+          5: "TP_ERR_WORKSPACE", 6: "TP_ERR_UNSUPPORTED", 7: "TP_ERR_HIP"}
+
+
+class TpError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+c_p = ctypes.c_void_p
+c_i64 = ctypes.c_int64
+c_int = ctypes.c_int
+c_sz = ctypes.c_size_t
+
+# name -> (restype, argtypes); mirrors include/tpshard.h
+SIGNATURES = {
+    "tp_col_linear": (c_int, [c_p, c_p, c_p, c_p, c_p, c_p, c_sz, c_i64, c_i64, c_i64, c_int, c_int, c_p]),
+    "tp_col_linear_workspace": (c_sz, [c_i64, c_i64, c_i64, c_int, c_int]),
+    "tp_act_inplace": (c_int, [c_p, c_p, c_i64, c_i64, c_int, c_int, c_p]),
+    "tp_row_linear_partial": (c_int, [c_p, c_p, c_p, c_p, c_sz, c_i64, c_i64, c_i64, c_int, c_int, c_p]),
+    "tp_row_linear_partial_workspace": (c_sz, [c_i64, c_i64, c_i64, c_int]),
+    "tp_mlp_shard_fwd_workspace": (c_sz, [c_i64, c_i64, c_i64, c_int, c_int]),
+    "tp_mlp_shard_fwd": (c_int, [c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_sz, c_i64, c_i64, c_i64, c_int, c_int, c_int,
+                                 c_p]),
+    "tp_mlp_shard_bwd_workspace": (c_sz, [c_i64, c_i64, c_i64, c_int, c_int]),
+    "tp_mlp_shard_bwd": (c_int, [c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_sz, c_i64, c_i64, c_i64,
+                                 c_int, c_int, c_p]),
+    "tp_partial_sum": (c_int, [ctypes.POINTER(c_p), c_int, c_p, c_p, c_i64, c_i64, c_int, c_int, c_p]),
+    "tp_workspace_init": (c_int, [c_p, c_sz, c_p]),
+    "tp_shard_range": (c_int, [c_i64, c_int, c_int, ctypes.POINTER(c_i64), ctypes.POINTER(c_i64)]),
+    "tp_gqa_shard": (c_int, [c_int, c_int, c_int, c_int, c_int, ctypes.POINTER(c_i64), ctypes.POINTER(c_i64),
+                             ctypes.POINTER(c_i64), ctypes.POINTER(c_i64)]),
+    "tp_status_string": (ctypes.c_char_p, [c_int]),
+    "tp_last_error": (ctypes.c_char_p, []),
+    "tp_abi_version": (c_int, []),
+}
+
+
+def lib_path() -> str:
+    return _build.LIB
+
+
+def load() -> ctypes.CDLL:
+    """Loads the built library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it first (python -m tensor_sharded_transformer_amd.build)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise TpError(status, load().tp_last_error().decode())
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return TP_BF16
+    if t.dtype == torch.float32:
+        return TP_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _shape(t: torch.Tensor, shape, name: str) -> None:
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+# ---- workspaces ---------------------------------------------------------------
+def new_workspace(nbytes: int, device=None) -> Optional[torch.Tensor]:
+    """A zero-filled byte buffer (the library keeps its counter region zero)."""
+    if nbytes == 0:
+        return None
+    return torch.zeros(int(nbytes), dtype=torch.uint8, device=device or "cuda")
+
+
+# ---- host helpers ----------------------------------------------------------------
+def tp_shard_range(n_total: int, p: int, i: int):
+    b, ln = c_i64(), c_i64()
+    _check(load().tp_shard_range(n_total, p, i, ctypes.byref(b), ctypes.byref(ln)))
+    return b.value, ln.value
+
+
+def tp_gqa_shard(n_q: int, n_kv: int, head_dim: int, p: int, i: int):
+    out = [c_i64() for _ in range(4)]
+    _check(load().tp_gqa_shard(n_q, n_kv, head_dim, p, i, *[ctypes.byref(o) for o in out]))
+    return tuple(o.value for o in out)
+
+
+def tp_abi_version() -> int:
+    return load().tp_abi_version()
+
+
+# ---- device entry points ----------------------------------------------------------
+def tp_col_linear(x, w, w_up, bias, y, act: str = "none", ws: Optional[torch.Tensor] = None):
+    T, K = x.shape
+    N = w.shape[1]
+    _shape(w, (K, N), "w")
+    _shape(y, (T, N), "y")
+    if w_up is not None:
+        _shape(w_up, (K, N), "w_up")
+    ws_bytes = 0 if ws is None else ws.numel()
+    _check(load().tp_col_linear(_ptr(x), _ptr(w), _ptr(w_up), _ptr(bias), _ptr(y), _ptr(ws), ws_bytes, T, K, N,
+                                _dt(x), ACT[act], _stream()))
+    return y
+
+
+def tp_col_linear_workspace(T: int, K: int, N_i: int, dtype: int, act: str) -> int:
+    return load().tp_col_linear_workspace(T, K, N_i, dtype, ACT[act])
+
+
+def tp_act_inplace(h, up, act: str):
+    T, N = h.shape
+    if up is not None:
+        _shape(up, (T, N), "up")
+    _check(load().tp_act_inplace(_ptr(h), _ptr(up), T, N, _dt(h), ACT[act], _stream()))
+    return h
+
+
+def tp_row_linear_partial(x_i, w_i, z_i, ws: Optional[torch.Tensor] = None):
+    T, K = x_i.shape
+    N = w_i.shape[1]
+    _shape(w_i, (K, N), "w_i")
+    _shape(z_i, (T, N), "z_i")
+    ws_bytes = 0 if ws is None else ws.numel()
+    _check(load().tp_row_linear_partial(_ptr(x_i), _ptr(w_i), _ptr(z_i), _ptr(ws), ws_bytes, T, K, N, _dt(x_i),
+                                        _dt(z_i), _stream()))
+    return z_i
+
+
+def tp_row_linear_partial_workspace(T: int, K_i: int, N: int, dtype: int) -> int:
+    return load().tp_row_linear_partial_workspace(T, K_i, N, dtype)
+
+
+def tp_mlp_shard_fwd_workspace(T: int, d: int, ff_i: int, dtype: int, act: str) -> int:
+    return load().tp_mlp_shard_fwd_workspace(T, d, ff_i, dtype, ACT[act])
+
+
+def tp_mlp_shard_fwd(x, w1_i, w_up_i, w2_i, y_i, act: str, ws: torch.Tensor, saved=None):
+    T, d = x.shape
+    ff_i = w1_i.shape[1]
+    _shape(w1_i, (d, ff_i), "w1_i")
+    _shape(w2_i, (ff_i, d), "w2_i")
+    _shape(y_i, (T, d), "y_i")
+    if w_up_i is not None:
+        _shape(w_up_i, (d, ff_i), "w_up_i")
+    if saved is not None:
+        _shape(saved, (T, (2 if act == "swiglu" else 1) * ff_i), "saved")
+    _check(load().tp_mlp_shard_fwd(_ptr(x), _ptr(w1_i), _ptr(w_up_i), _ptr(w2_i), _ptr(y_i), _ptr(saved), _ptr(ws),
+                                   ws.numel() if ws is not None else 0, T, d, ff_i, _dt(x), _dt(y_i), ACT[act],
+                                   _stream()))
+    return y_i
+
+
+def tp_mlp_shard_bwd_workspace(T: int, d: int, ff_i: int, dtype: int, act: str) -> int:
+    return load().tp_mlp_shard_bwd_workspace(T, d, ff_i, dtype, ACT[act])
+
+
+def tp_mlp_shard_bwd(x, w1_i, w_up_i, w2_i, saved, dy, dw1_i, dw_up_i, dw2_i, dx_i, act: str, ws: torch.Tensor):
+    T, d = x.shape
+    ff_i = w1_i.shape[1]
+    for t, shp, nm in ((dy, (T, d), "dy"), (dw1_i, (d, ff_i), "dw1_i"), (dw2_i, (ff_i, d), "dw2_i"),
+                       (dx_i, (T, d), "dx_i"), (w2_i, (ff_i, d), "w2_i")):
+        _shape(t, shp, nm)
+    if dw_up_i is not None:
+        _shape(dw_up_i, (d, ff_i), "dw_up_i")
+    _check(load().tp_mlp_shard_bwd(_ptr(x), _ptr(w1_i), _ptr(w_up_i), _ptr(w2_i), _ptr(saved), _ptr(dy),
+                                   _ptr(dw1_i), _ptr(dw_up_i), _ptr(dw2_i), _ptr(dx_i), _ptr(ws),
+                                   ws.numel() if ws is not None else 0, T, d, ff_i, _dt(x), ACT[act], _stream()))
+
+
+def tp_partial_sum(zs: Sequence[torch.Tensor], bias, y):
+    T, N = y.shape
+    for z in zs:
+        _shape(z, (T, N), "z")
+    arr = (c_p * len(zs))(*[_ptr(z) for z in zs])
+    _check(load().tp_partial_sum(arr, len(zs), _ptr(bias), _ptr(y), T, N, _dt(zs[0]), _dt(y), _stream()))
+    return y
+
+
+def tp_workspace_init(ws: torch.Tensor):
+    _check(load().tp_workspace_init(_ptr(ws), ws.numel(), _stream()))

@@ -1,0 +1,533 @@
+// C ABI of the tpshard library: argument checks on the host, workspace
+// layout, and dispatch to the HIP kernels.  Every check happens before the
+// first launch, so a rejected call has no side effect.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/tpshard.h"
+#include "tp_kernels.h"
+
+using tpk::GemmKind;
+using tpk::GemmParams;
+using tpk::GemmPlan;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+tp_status fail(tp_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+tp_status fail(tp_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+tp_status hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return TP_OK;
+  return fail(TP_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxDim = 0x7fffffff;  // kernels index rows/cols with int
+
+bool dim_ok(int64_t v) { return v >= 0 && v <= kMaxDim; }
+
+bool valid_dtype(int d) { return d == TP_BF16 || d == TP_F32; }
+bool valid_act(int a) { return a >= TP_ACT_NONE && a <= TP_ACT_SWIGLU; }
+size_t esize(int d) { return d == TP_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// product of element counts must stay addressable
+bool prod_ok(int64_t a, int64_t b) { return a == 0 || b <= INT64_MAX / 8 / a; }
+
+GemmParams base_params() {
+  GemmParams p;
+  std::memset(&p, 0, sizeof p);
+  p.splitk = 1;
+  return p;
+}
+
+// Workspace layout shared by the forward and backward entry points:
+//   [ buffers ... ][ split-K counters (zero between calls) ][ split-K partials ]
+struct SplitNeeds {
+  size_t part_bytes = 0;
+  size_t n_tiles = 0;
+  void add(const GemmPlan& plan, int M, int N, bool dual) {
+    size_t pb, nt;
+    tpk::gemm_split_sizes(plan, M, N, dual, &pb, &nt);
+    if (pb > part_bytes) part_bytes = pb;
+    if (nt > n_tiles) n_tiles = nt;
+  }
+  size_t counter_bytes() const { return tpk::align_up(n_tiles * sizeof(int), 256); }
+};
+
+void attach_split(GemmParams& p, const GemmPlan& plan, char* counters, char* partials) {
+  p.splitk = plan.splitk;
+  p.counters = plan.splitk > 1 ? reinterpret_cast<int*>(counters) : nullptr;
+  p.partials = plan.splitk > 1 ? reinterpret_cast<float*>(partials) : nullptr;
+}
+
+GemmPlan plan_for(int dtype, int M, int N, int K, bool dual, bool allow_split) {
+  GemmPlan plan = tpk::plan_gemm(M, N, K, dual);
+  if (dtype != TP_BF16 || !allow_split) plan.splitk = 1;
+  return plan;
+}
+
+hipError_t run_gemm(int dtype, const GemmParams& p, const GemmPlan& plan, GemmKind kind, bool out_f32,
+                    hipStream_t s) {
+  if (dtype == TP_F32) return tpk::gemm_f32(p, kind, s);
+  return tpk::gemm_bf16(p, plan, kind, out_f32, s);
+}
+
+// ---- forward shard layout ----------------------------------------------------
+struct FwdLayout {
+  GemmPlan p1, p2;
+  size_t h_bytes = 0, cnt_off = 0, part_off = 0, total = 0;
+};
+
+FwdLayout fwd_layout(int64_t T, int64_t d, int64_t ff_i, int dtype, int act) {
+  FwdLayout L;
+  const bool dual = act == TP_ACT_SWIGLU;
+  L.p1 = plan_for(dtype, (int)T, (int)ff_i, (int)d, dual, true);
+  L.p2 = plan_for(dtype, (int)T, (int)d, (int)ff_i, false, true);
+  SplitNeeds sn;
+  sn.add(L.p1, (int)T, (int)ff_i, dual);
+  sn.add(L.p2, (int)T, (int)d, false);
+  L.h_bytes = tpk::align_up((size_t)T * ff_i * esize(dtype), 256);
+  L.cnt_off = L.h_bytes;
+  L.part_off = L.cnt_off + sn.counter_bytes();
+  L.total = L.part_off + tpk::align_up(sn.part_bytes, 256);
+  return L;
+}
+
+struct BwdLayout {
+  GemmPlan pa, pb, pc, pd;
+  size_t dgu_bytes = 0, h_off = 0, cnt_off = 0, part_off = 0, total = 0;
+};
+
+BwdLayout bwd_layout(int64_t T, int64_t d, int64_t ff_i, int dtype, int act) {
+  BwdLayout L;
+  const bool sw = act == TP_ACT_SWIGLU;
+  L.pa = plan_for(dtype, (int)T, (int)ff_i, (int)d, false, true);   // dh
+  L.pb = plan_for(dtype, (int)ff_i, (int)d, (int)T, false, true);   // dW2
+  L.pc = plan_for(dtype, (int)d, (int)ff_i, (int)T, sw, true);      // dW1 (+dWup)
+  L.pd = plan_for(dtype, (int)T, (int)d, (int)((sw ? 2 : 1) * ff_i), false, true);  // dx
+  SplitNeeds sn;
+  sn.add(L.pa, (int)T, (int)ff_i, false);
+  sn.add(L.pb, (int)ff_i, (int)d, false);
+  sn.add(L.pc, (int)d, (int)ff_i, sw);
+  sn.add(L.pd, (int)T, (int)d, false);
+  L.dgu_bytes = tpk::align_up((size_t)T * ff_i * (sw ? 2 : 1) * esize(dtype), 256);
+  L.h_off = L.dgu_bytes;
+  L.cnt_off = L.h_off + tpk::align_up((size_t)T * ff_i * esize(dtype), 256);
+  L.part_off = L.cnt_off + sn.counter_bytes();
+  L.total = L.part_off + tpk::align_up(sn.part_bytes, 256);
+  return L;
+}
+
+// Optional workspace of a single GEMM entry point: [counters][partials].
+struct SingleWs {
+  GemmPlan plan;
+  size_t cnt_bytes = 0, total = 0;
+  // With no workspace the call runs unsplit; a too-small one is an error.
+  tp_status bind(GemmParams& p, void* ws, size_t ws_bytes, const char* who) {
+    if (!ws || plan.splitk <= 1) {
+      plan.splitk = 1;
+      attach_split(p, plan, nullptr, nullptr);
+      return TP_OK;
+    }
+    if (ws_bytes < total) return fail(TP_ERR_WORKSPACE, "%s: workspace of %zu bytes < %zu needed", who, ws_bytes, total);
+    char* base = reinterpret_cast<char*>(ws);
+    attach_split(p, plan, base, base + cnt_bytes);
+    return TP_OK;
+  }
+};
+
+SingleWs single_ws(int dtype, int M, int N, int K, bool dual) {
+  SingleWs W;
+  W.plan = plan_for(dtype, M, N, K, dual, true);
+  SplitNeeds sn;
+  sn.add(W.plan, M, N, dual);
+  if (W.plan.splitk > 1) {
+    W.cnt_bytes = sn.counter_bytes();
+    W.total = W.cnt_bytes + tpk::align_up(sn.part_bytes, 256);
+  }
+  return W;
+}
+
+tp_status check_common(int dtype, int act) {
+  if (!valid_dtype(dtype)) return fail(TP_ERR_DTYPE, "unknown dtype %d", dtype);
+  if (!valid_act(act)) return fail(TP_ERR_ACT, "unknown act %d", act);
+  return TP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tp_status_string(tp_status s) {
+  switch (s) {
+    case TP_OK: return "ok";
+    case TP_ERR_NULL: return "null pointer";
+    case TP_ERR_SHAPE: return "invalid shape";
+    case TP_ERR_DTYPE: return "invalid dtype";
+    case TP_ERR_ACT: return "invalid activation arguments";
+    case TP_ERR_WORKSPACE: return "workspace too small";
+    case TP_ERR_UNSUPPORTED: return "unsupported";
+    case TP_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* tp_last_error(void) { return g_last_error.c_str(); }
+
+int tp_abi_version(void) { return TPSHARD_ABI_VERSION; }
+
+tp_status tp_shard_range(int64_t n_total, int p, int i, int64_t* begin, int64_t* len) {
+  if (!begin || !len) return fail(TP_ERR_NULL, "tp_shard_range: null output pointer");
+  if (p <= 0 || i < 0 || i >= p || n_total < 0)
+    return fail(TP_ERR_SHAPE, "tp_shard_range: need p > 0, 0 <= i < p, n_total >= 0 (got n=%lld p=%d i=%d)",
+                (long long)n_total, p, i);
+  if (n_total % p != 0)
+    return fail(TP_ERR_SHAPE, "tp_shard_range: %lld is not divisible into %d equal shards", (long long)n_total, p);
+  *len = n_total / p;
+  *begin = (int64_t)i * (*len);
+  return TP_OK;
+}
+
+tp_status tp_gqa_shard(int n_q_heads, int n_kv_heads, int head_dim, int p, int i, int64_t* q_begin, int64_t* q_len,
+                       int64_t* kv_begin, int64_t* kv_len) {
+  if (!q_begin || !q_len || !kv_begin || !kv_len) return fail(TP_ERR_NULL, "tp_gqa_shard: null output pointer");
+  if (n_q_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0 || p <= 0 || i < 0 || i >= p)
+    return fail(TP_ERR_SHAPE, "tp_gqa_shard: sizes must be positive and 0 <= i < p");
+  if (n_q_heads % n_kv_heads != 0)
+    return fail(TP_ERR_SHAPE, "tp_gqa_shard: %d query heads do not group evenly over %d KV heads", n_q_heads,
+                n_kv_heads);
+  if (n_q_heads % p != 0 || n_kv_heads % p != 0)
+    return fail(TP_ERR_SHAPE, "tp_gqa_shard: head counts (%d Q, %d KV) must divide by p=%d (a head is never split)",
+                n_q_heads, n_kv_heads, p);
+  const int64_t qh = n_q_heads / p, kh = n_kv_heads / p;
+  *q_begin = (int64_t)i * qh * head_dim;
+  *q_len = qh * head_dim;
+  *kv_begin = (int64_t)i * kh * head_dim;
+  *kv_len = kh * head_dim;
+  return TP_OK;
+}
+
+tp_status tp_workspace_init(void* ws, size_t bytes, tp_stream stream) {
+  if (bytes == 0) return TP_OK;
+  if (!ws) return fail(TP_ERR_NULL, "tp_workspace_init: null workspace");
+  return hip_status(tpk::zero_fill(ws, bytes, reinterpret_cast<hipStream_t>(stream)), "tp_workspace_init");
+}
+
+// ---- column-parallel linear ---------------------------------------------------
+size_t tp_col_linear_workspace(int64_t T, int64_t K, int64_t N_i, tp_dtype dtype, tp_act act) {
+  if (!valid_dtype(dtype) || !valid_act(act) || !dim_ok(T) || !dim_ok(K) || !dim_ok(N_i) || T == 0) return 0;
+  return single_ws(dtype, (int)T, (int)N_i, (int)K, act == TP_ACT_SWIGLU).total;
+}
+
+tp_status tp_col_linear(const void* x, const void* w, const void* w_up, const void* bias, void* y, void* ws,
+                        size_t ws_bytes, int64_t T, int64_t K, int64_t N_i, tp_dtype dtype, tp_act act,
+                        tp_stream stream) {
+  tp_status st = check_common(dtype, act);
+  if (st != TP_OK) return st;
+  if (!dim_ok(T) || !dim_ok(K) || !dim_ok(N_i) || !prod_ok(T, K) || !prod_ok(K, N_i) || !prod_ok(T, N_i))
+    return fail(TP_ERR_SHAPE, "tp_col_linear: sizes out of range (T=%lld K=%lld N_i=%lld)", (long long)T,
+                (long long)K, (long long)N_i);
+  const bool sw = act == TP_ACT_SWIGLU;
+  if (sw && !w_up) return fail(TP_ERR_ACT, "tp_col_linear: SWIGLU needs w_up");
+  if (!sw && w_up) return fail(TP_ERR_ACT, "tp_col_linear: w_up is only used by SWIGLU");
+  if (sw && bias) return fail(TP_ERR_ACT, "tp_col_linear: a bias is not defined for SWIGLU");
+  if (T == 0 || N_i == 0) return TP_OK;
+  if (!x || !w || !y) return fail(TP_ERR_NULL, "tp_col_linear: null x, w or y");
+  GemmParams p = base_params();
+  p.A0 = x;
+  p.lda = K;
+  p.B0 = w;
+  p.B1 = sw ? w_up : nullptr;
+  p.ldb = N_i;
+  p.K0 = (int)K;
+  p.M = (int)T;
+  p.N = (int)N_i;
+  p.C = y;
+  p.ldc = N_i;
+  p.bias = bias;
+  p.act = act;
+  p.vecA = aligned16(x) && K % 8 == 0;
+  p.vecB = aligned16(w) && (!sw || aligned16(w_up)) && N_i % 8 == 0;
+  SingleWs W = single_ws(dtype, (int)T, (int)N_i, (int)K, sw);
+  tp_status ws_st = W.bind(p, ws, ws_bytes, "tp_col_linear");
+  if (ws_st != TP_OK) return ws_st;
+  return hip_status(run_gemm(dtype, p, W.plan, sw ? tpk::GK_FWD_SWIGLU : tpk::GK_FWD_ACT, false,
+                             reinterpret_cast<hipStream_t>(stream)),
+                    "tp_col_linear");
+}
+
+tp_status tp_act_inplace(void* h, const void* up, int64_t T, int64_t N_i, tp_dtype dtype, tp_act act,
+                         tp_stream stream) {
+  tp_status st = check_common(dtype, act);
+  if (st != TP_OK) return st;
+  if (!dim_ok(T) || !dim_ok(N_i) || !prod_ok(T, N_i))
+    return fail(TP_ERR_SHAPE, "tp_act_inplace: sizes out of range");
+  const bool sw = act == TP_ACT_SWIGLU;
+  if (sw && !up) return fail(TP_ERR_ACT, "tp_act_inplace: SWIGLU needs up");
+  if (!sw && up) return fail(TP_ERR_ACT, "tp_act_inplace: up is only used by SWIGLU");
+  if (T == 0 || N_i == 0 || act == TP_ACT_NONE) return TP_OK;
+  if (!h) return fail(TP_ERR_NULL, "tp_act_inplace: null h");
+  return hip_status(tpk::act_inplace(h, up, T * N_i, dtype == TP_BF16, act, reinterpret_cast<hipStream_t>(stream)),
+                    "tp_act_inplace");
+}
+
+// ---- row-parallel partial ------------------------------------------------------
+size_t tp_row_linear_partial_workspace(int64_t T, int64_t K_i, int64_t N, tp_dtype in_dtype) {
+  if (!valid_dtype(in_dtype) || !dim_ok(T) || !dim_ok(K_i) || !dim_ok(N) || T == 0) return 0;
+  return single_ws(in_dtype, (int)T, (int)N, (int)K_i, false).total;
+}
+
+tp_status tp_row_linear_partial(const void* x_i, const void* w_i, void* z_i, void* ws, size_t ws_bytes, int64_t T,
+                                int64_t K_i, int64_t N, tp_dtype in_dtype, tp_dtype out_dtype, tp_stream stream) {
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+    return fail(TP_ERR_DTYPE, "tp_row_linear_partial: unknown dtype");
+  if (in_dtype == TP_F32 && out_dtype != TP_F32)
+    return fail(TP_ERR_DTYPE, "tp_row_linear_partial: f32 inputs need an f32 output");
+  if (!dim_ok(T) || !dim_ok(K_i) || !dim_ok(N) || !prod_ok(T, K_i) || !prod_ok(K_i, N) || !prod_ok(T, N))
+    return fail(TP_ERR_SHAPE, "tp_row_linear_partial: sizes out of range");
+  if (T == 0 || N == 0) return TP_OK;
+  if (!x_i || !w_i || !z_i) return fail(TP_ERR_NULL, "tp_row_linear_partial: null x_i, w_i or z_i");
+  GemmParams p = base_params();
+  p.A0 = x_i;
+  p.lda = K_i;
+  p.B0 = w_i;
+  p.ldb = N;
+  p.K0 = (int)K_i;
+  p.M = (int)T;
+  p.N = (int)N;
+  p.C = z_i;
+  p.ldc = N;
+  p.vecA = aligned16(x_i) && K_i % 8 == 0;
+  p.vecB = aligned16(w_i) && N % 8 == 0;
+  SingleWs W = single_ws(in_dtype, (int)T, (int)N, (int)K_i, false);
+  tp_status ws_st = W.bind(p, ws, ws_bytes, "tp_row_linear_partial");
+  if (ws_st != TP_OK) return ws_st;
+  return hip_status(run_gemm(in_dtype, p, W.plan, tpk::GK_FWD_STORE, out_dtype == TP_F32,
+                             reinterpret_cast<hipStream_t>(stream)),
+                    "tp_row_linear_partial");
+}
+
+// ---- sum of partials -------------------------------------------------------------
+tp_status tp_partial_sum(const void* const* z, int p, const void* bias, void* y, int64_t T, int64_t N,
+                         tp_dtype in_dtype, tp_dtype out_dtype, tp_stream stream) {
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return fail(TP_ERR_DTYPE, "tp_partial_sum: unknown dtype");
+  if (p < 1 || p > 64) return fail(TP_ERR_SHAPE, "tp_partial_sum: need 1 <= p <= 64 (got %d)", p);
+  if (!dim_ok(T) || !dim_ok(N) || !prod_ok(T, N)) return fail(TP_ERR_SHAPE, "tp_partial_sum: sizes out of range");
+  if (T == 0 || N == 0) return TP_OK;
+  if (!z || !y) return fail(TP_ERR_NULL, "tp_partial_sum: null z or y");
+  for (int i = 0; i < p; ++i)
+    if (!z[i]) return fail(TP_ERR_NULL, "tp_partial_sum: z[%d] is null", i);
+  return hip_status(tpk::partial_sum(z, p, bias, y, T, N, in_dtype == TP_BF16, out_dtype == TP_BF16,
+                                     reinterpret_cast<hipStream_t>(stream)),
+                    "tp_partial_sum");
+}
+
+// ---- MLP shard forward ------------------------------------------------------------
+size_t tp_mlp_shard_fwd_workspace(int64_t T, int64_t d, int64_t ff_i, tp_dtype dtype, tp_act act) {
+  if (!valid_dtype(dtype) || !valid_act(act) || !dim_ok(T) || !dim_ok(d) || !dim_ok(ff_i)) return 0;
+  if (T == 0) return 0;
+  return fwd_layout(T, d, ff_i, dtype, act).total;
+}
+
+tp_status tp_mlp_shard_fwd(const void* x, const void* w1_i, const void* w_up_i, const void* w2_i, void* y_i,
+                           void* saved, void* ws, size_t ws_bytes, int64_t T, int64_t d, int64_t ff_i, tp_dtype dtype,
+                           tp_dtype out_dtype, tp_act act, tp_stream stream) {
+  tp_status st = check_common(dtype, act);
+  if (st != TP_OK) return st;
+  if (!valid_dtype(out_dtype) || (dtype == TP_F32 && out_dtype != TP_F32))
+    return fail(TP_ERR_DTYPE, "tp_mlp_shard_fwd: out_dtype must be f32 for f32 inputs, bf16 or f32 otherwise");
+  if (!dim_ok(T) || !dim_ok(d) || !dim_ok(ff_i) || !prod_ok(T, d) || !prod_ok(d, ff_i) || !prod_ok(T, 2 * ff_i))
+    return fail(TP_ERR_SHAPE, "tp_mlp_shard_fwd: sizes out of range");
+  const bool sw = act == TP_ACT_SWIGLU;
+  if (sw != (w_up_i != nullptr)) return fail(TP_ERR_ACT, "tp_mlp_shard_fwd: w_up_i must be given iff SWIGLU");
+  if (T == 0) return TP_OK;
+  if (!x || !w1_i || !w2_i || !y_i) return fail(TP_ERR_NULL, "tp_mlp_shard_fwd: null x, w1_i, w2_i or y_i");
+  const FwdLayout L = fwd_layout(T, d, ff_i, dtype, act);
+  if (!ws) return fail(TP_ERR_WORKSPACE, "tp_mlp_shard_fwd: workspace required (%zu bytes)", L.total);
+  if (ws_bytes < L.total)
+    return fail(TP_ERR_WORKSPACE, "tp_mlp_shard_fwd: workspace of %zu bytes < %zu needed", ws_bytes, L.total);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* base = reinterpret_cast<char*>(ws);
+  void* h = base;
+  const bool bf = dtype == TP_BF16;
+
+  GemmParams p1 = base_params();
+  p1.A0 = x;
+  p1.lda = d;
+  p1.B0 = w1_i;
+  p1.B1 = w_up_i;
+  p1.ldb = ff_i;
+  p1.K0 = (int)d;
+  p1.M = (int)T;
+  p1.N = (int)ff_i;
+  p1.C = h;
+  p1.ldc = ff_i;
+  p1.act = act;
+  if (saved) {
+    p1.C2 = saved;
+    p1.C3 = sw ? reinterpret_cast<char*>(saved) + ff_i * esize(dtype) : nullptr;
+    p1.ldc2 = sw ? 2 * ff_i : ff_i;
+  }
+  p1.vecA = aligned16(x) && d % 8 == 0;
+  p1.vecB = aligned16(w1_i) && (!sw || aligned16(w_up_i)) && ff_i % 8 == 0;
+  attach_split(p1, L.p1, base + L.cnt_off, base + L.part_off);
+  hipError_t e = run_gemm(dtype, p1, L.p1, sw ? tpk::GK_FWD_SWIGLU : tpk::GK_FWD_ACT, false, s);
+  if (e != hipSuccess) return hip_status(e, "tp_mlp_shard_fwd (column GEMM)");
+  (void)bf;
+
+  GemmParams p2 = base_params();
+  p2.A0 = h;
+  p2.lda = ff_i;
+  p2.B0 = w2_i;
+  p2.ldb = d;
+  p2.K0 = (int)ff_i;
+  p2.M = (int)T;
+  p2.N = (int)d;
+  p2.C = y_i;
+  p2.ldc = d;
+  p2.vecA = ff_i % 8 == 0;
+  p2.vecB = aligned16(w2_i) && d % 8 == 0;
+  attach_split(p2, L.p2, base + L.cnt_off, base + L.part_off);
+  e = run_gemm(dtype, p2, L.p2, tpk::GK_FWD_STORE, out_dtype == TP_F32, s);
+  return hip_status(e, "tp_mlp_shard_fwd (row GEMM)");
+}
+
+// ---- MLP shard backward --------------------------------------------------------------
+size_t tp_mlp_shard_bwd_workspace(int64_t T, int64_t d, int64_t ff_i, tp_dtype dtype, tp_act act) {
+  if (!valid_dtype(dtype) || !valid_act(act) || !dim_ok(T) || !dim_ok(d) || !dim_ok(ff_i)) return 0;
+  if (T == 0) return 0;
+  return bwd_layout(T, d, ff_i, dtype, act).total;
+}
+
+tp_status tp_mlp_shard_bwd(const void* x, const void* w1_i, const void* w_up_i, const void* w2_i, const void* saved,
+                           const void* dy, void* dw1_i, void* dw_up_i, void* dw2_i, void* dx_i, void* ws,
+                           size_t ws_bytes, int64_t T, int64_t d, int64_t ff_i, tp_dtype dtype, tp_act act,
+                           tp_stream stream) {
+  tp_status st = check_common(dtype, act);
+  if (st != TP_OK) return st;
+  if (!dim_ok(T) || !dim_ok(d) || !dim_ok(ff_i) || !prod_ok(T, d) || !prod_ok(d, ff_i) || !prod_ok(T, 2 * ff_i))
+    return fail(TP_ERR_SHAPE, "tp_mlp_shard_bwd: sizes out of range");
+  const bool sw = act == TP_ACT_SWIGLU;
+  if (sw != (w_up_i != nullptr) || sw != (dw_up_i != nullptr))
+    return fail(TP_ERR_ACT, "tp_mlp_shard_bwd: w_up_i and dw_up_i must be given iff SWIGLU");
+  if (!x || !w1_i || !w2_i || !saved || !dy || !dw1_i || !dw2_i || !dx_i)
+    return fail(TP_ERR_NULL, "tp_mlp_shard_bwd: null input or output pointer");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const size_t es = esize(dtype);
+  if (T == 0) {
+    // no tokens: the weight gradients are zero, dx_i is empty
+    hipError_t e = tpk::zero_fill(dw1_i, (size_t)d * ff_i * es, s);
+    if (e == hipSuccess && sw) e = tpk::zero_fill(dw_up_i, (size_t)d * ff_i * es, s);
+    if (e == hipSuccess) e = tpk::zero_fill(dw2_i, (size_t)d * ff_i * es, s);
+    return hip_status(e, "tp_mlp_shard_bwd (T=0)");
+  }
+  const BwdLayout L = bwd_layout(T, d, ff_i, dtype, act);
+  if (!ws) return fail(TP_ERR_WORKSPACE, "tp_mlp_shard_bwd: workspace required (%zu bytes)", L.total);
+  if (ws_bytes < L.total)
+    return fail(TP_ERR_WORKSPACE, "tp_mlp_shard_bwd: workspace of %zu bytes < %zu needed", ws_bytes, L.total);
+  char* base = reinterpret_cast<char*>(ws);
+  char* dgu = base;                 // (T, 2 ff_i) [dG | dU] for SWIGLU, (T, ff_i) dA otherwise
+  char* h = base + L.h_off;         // (T, ff_i) recomputed activation
+  char* cnt = base + L.cnt_off;
+  char* part = base + L.part_off;
+  const int64_t ldg = sw ? 2 * ff_i : ff_i;
+
+  // (a) dh = dy W2^T, epilogue -> dG/dU (or dA) and h
+  GemmParams pa = base_params();
+  pa.A0 = dy;
+  pa.lda = d;
+  pa.B0 = w2_i;  // B(k = hidden j, n = f) = w2_i[f * d + j]
+  pa.ldb = d;
+  pa.K0 = (int)d;
+  pa.M = (int)T;
+  pa.N = (int)ff_i;
+  pa.C = dgu;
+  pa.ldc = ldg;
+  pa.C2 = sw ? dgu + ff_i * es : nullptr;
+  pa.ldc2 = ldg;
+  pa.C3 = h;
+  pa.ldc3 = ff_i;
+  pa.S0 = saved;
+  pa.S1 = sw ? reinterpret_cast<const char*>(saved) + ff_i * es : nullptr;
+  pa.lds = ldg;
+  pa.act = act;
+  pa.vecA = aligned16(dy) && d % 8 == 0;
+  pa.vecB = aligned16(w2_i) && d % 8 == 0;
+  attach_split(pa, L.pa, cnt, part);
+  hipError_t e = run_gemm(dtype, pa, L.pa, sw ? tpk::GK_BWD_DH_SWIGLU : tpk::GK_BWD_DH_ACT, false, s);
+  if (e != hipSuccess) return hip_status(e, "tp_mlp_shard_bwd (dh GEMM)");
+
+  // (b) dW2 = h^T dy
+  GemmParams pb = base_params();
+  pb.A0 = h;  // A(m = f, k = t) = h[t * ff_i + f]
+  pb.lda = ff_i;
+  pb.B0 = dy;  // B(k = t, n = j) = dy[t * d + j]
+  pb.ldb = d;
+  pb.K0 = (int)T;
+  pb.M = (int)ff_i;
+  pb.N = (int)d;
+  pb.C = dw2_i;
+  pb.ldc = d;
+  pb.vecA = ff_i % 8 == 0;
+  pb.vecB = aligned16(dy) && d % 8 == 0;
+  attach_split(pb, L.pb, cnt, part);
+  e = run_gemm(dtype, pb, L.pb, tpk::GK_BWD_DW, false, s);
+  if (e != hipSuccess) return hip_status(e, "tp_mlp_shard_bwd (dW2 GEMM)");
+
+  // (c) dW1 = x^T dG (and dWup = x^T dU)
+  GemmParams pc = base_params();
+  pc.A0 = x;  // A(m = j, k = t) = x[t * d + j]
+  pc.lda = d;
+  pc.B0 = dgu;  // B(k = t, n = f) = dG[t * ldg + f]
+  pc.B1 = sw ? dgu + ff_i * es : nullptr;
+  pc.ldb = ldg;
+  pc.K0 = (int)T;
+  pc.M = (int)d;
+  pc.N = (int)ff_i;
+  pc.C = dw1_i;
+  pc.ldc = ff_i;
+  pc.C2 = dw_up_i;
+  pc.ldc2 = ff_i;
+  pc.vecA = aligned16(x) && d % 8 == 0;
+  pc.vecB = ff_i % 8 == 0;
+  attach_split(pc, L.pc, cnt, part);
+  e = run_gemm(dtype, pc, L.pc, sw ? tpk::GK_BWD_DW_DUAL : tpk::GK_BWD_DW, false, s);
+  if (e != hipSuccess) return hip_status(e, "tp_mlp_shard_bwd (dW1 GEMM)");
+
+  // (d) dx_i = dG W1^T (+ dU Wup^T): two K segments
+  GemmParams pd = base_params();
+  pd.A0 = dgu;  // A(m = t, k = f) = dG[t * ldg + f]
+  pd.A1 = sw ? dgu + ff_i * es : nullptr;
+  pd.lda = ldg;
+  pd.B0 = w1_i;  // B(k = f, n = j) = w1_i[j * ff_i + f]
+  pd.B1 = w_up_i;
+  pd.ldb = ff_i;
+  pd.K0 = (int)ff_i;
+  pd.K1 = sw ? (int)ff_i : 0;
+  pd.M = (int)T;
+  pd.N = (int)d;
+  pd.C = dx_i;
+  pd.ldc = d;
+  pd.vecA = ff_i % 8 == 0;
+  pd.vecB = aligned16(w1_i) && (!sw || aligned16(w_up_i)) && ff_i % 8 == 0;
+  attach_split(pd, L.pd, cnt, part);
+  e = run_gemm(dtype, pd, L.pd, tpk::GK_BWD_DX, false, s);
+  return hip_status(e, "tp_mlp_shard_bwd (dx GEMM)");
+}
+
+}  // extern "C"

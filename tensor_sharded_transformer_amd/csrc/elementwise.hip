@@ -1,0 +1,194 @@
+// Elementwise kernels: activation on owned columns, the sum of the p
+// full-shape partials, and a workspace zero-fill.
+//
+// Activation: "How does tensor parallelism split a transformer feed-forward
+// block's two matmuls across devices?", "The nonlinearity is free" (an
+// elementwise function of each owned column, no communication).
+// Sum of partials: "Tensor Parallelism" notes, first paragraph (Y = sum_i Z_i,
+// an all-reduce in a real group) and the MLX shard_linear facts (the bias is
+// added once, after the sum).
+//
+// All three are HBM-bound streams: each thread moves 16-byte vectors, the grid
+// is sized to a few waves of workgroups per CU and loops grid-stride.
+#include "tp_kernels.h"
+#include "tp_device.h"
+
+namespace tpk {
+
+static int stream_grid(int64_t units, int block) {
+  int64_t g = (units + block - 1) / block;
+  const int64_t cap = 256 * 16;  // 256 CUs x 16 workgroups: enough bytes in flight
+  if (g > cap) g = cap;
+  if (g < 1) g = 1;
+  return (int)g;
+}
+
+// ---- activation in place ----------------------------------------------------
+__global__ __launch_bounds__(256) void act_bf16_kernel(uint16_t* h, const uint16_t* up, int64_t n, int act, int vec) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t nv = vec ? n / 8 : 0;
+  for (int64_t v = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; v < nv; v += stride) {
+    uint4 hv = reinterpret_cast<const uint4*>(h)[v];
+    uint4 uv = make_uint4(0, 0, 0, 0);
+    if (act == ACT_SWIGLU) uv = reinterpret_cast<const uint4*>(up)[v];
+    uint32_t* hw = reinterpret_cast<uint32_t*>(&hv);
+    const uint32_t* uw = reinterpret_cast<const uint32_t*>(&uv);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float a0 = bf2f((uint16_t)(hw[q] & 0xffffu)), a1 = bf2f((uint16_t)(hw[q] >> 16));
+      if (act == ACT_SWIGLU) {
+        const float u0 = bf2f((uint16_t)(uw[q] & 0xffffu)), u1 = bf2f((uint16_t)(uw[q] >> 16));
+        a0 = a0 * sigmoidf_(a0) * u0;
+        a1 = a1 * sigmoidf_(a1) * u1;
+      } else {
+        a0 = act_fwd(act, a0);
+        a1 = act_fwd(act, a1);
+      }
+      hw[q] = (uint32_t)f2bf(a0) | ((uint32_t)f2bf(a1) << 16);
+    }
+    reinterpret_cast<uint4*>(h)[v] = hv;
+  }
+  // scalar tail (or everything when not 16-byte aligned)
+  for (int64_t e = nv * 8 + blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n; e += stride) {
+    float a = bf2f(h[e]);
+    if (act == ACT_SWIGLU) a = a * sigmoidf_(a) * bf2f(up[e]);
+    else a = act_fwd(act, a);
+    h[e] = f2bf(a);
+  }
+}
+
+__global__ __launch_bounds__(256) void act_f32_kernel(float* h, const float* up, int64_t n, int act) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n; e += stride) {
+    float a = h[e];
+    if (act == ACT_SWIGLU) a = a * sigmoidf_(a) * up[e];
+    else a = act_fwd(act, a);
+    h[e] = a;
+  }
+}
+
+hipError_t act_inplace(void* h, const void* up, int64_t n, bool bf16, int act, hipStream_t s) {
+  if (n == 0 || act == ACT_NONE) return hipSuccess;
+  if (bf16) {
+    const int vec = ((uintptr_t)h % 16 == 0) && (up == nullptr || (uintptr_t)up % 16 == 0);
+    hipLaunchKernelGGL(act_bf16_kernel, dim3(stream_grid(vec ? (n + 7) / 8 : n, 256)), dim3(256), 0, s,
+                       (uint16_t*)h, (const uint16_t*)up, n, act, vec);
+  } else {
+    hipLaunchKernelGGL(act_f32_kernel, dim3(stream_grid(n, 256)), dim3(256), 0, s, (float*)h, (const float*)up, n,
+                       act);
+  }
+  return hipGetLastError();
+}
+
+// ---- sum of partials ----------------------------------------------------------
+constexpr int MAX_P = 64;
+struct SumArgs {
+  const void* z[MAX_P];
+};
+
+template <bool IN_BF16, bool OUT_BF16>
+__global__ __launch_bounds__(256) void partial_sum_kernel(const SumArgs a, int p, const void* bias, void* y,
+                                                          int64_t T, int64_t N, int vec) {
+  const int64_t n = T * N;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  // 8 elements per thread per step when every row start is 16-byte aligned
+  // for bf16 (32 bytes for f32 in two 16-byte halves).
+  if (vec) {
+    const int64_t nv = n / 8;
+    for (int64_t v = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; v < nv; v += stride) {
+      float acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+      for (int i = 0; i < p; ++i) {
+        if constexpr (IN_BF16) {
+          const uint4 w = reinterpret_cast<const uint4*>(a.z[i])[v];
+          const uint32_t* ww = reinterpret_cast<const uint32_t*>(&w);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[2 * q] += bf2f((uint16_t)(ww[q] & 0xffffu));
+            acc[2 * q + 1] += bf2f((uint16_t)(ww[q] >> 16));
+          }
+        } else {
+          const float4 w0 = reinterpret_cast<const float4*>(a.z[i])[2 * v];
+          const float4 w1 = reinterpret_cast<const float4*>(a.z[i])[2 * v + 1];
+          acc[0] += w0.x; acc[1] += w0.y; acc[2] += w0.z; acc[3] += w0.w;
+          acc[4] += w1.x; acc[5] += w1.y; acc[6] += w1.z; acc[7] += w1.w;
+        }
+      }
+      if (bias) {
+        const int64_t col = (v * 8) % N;  // N % 8 == 0 on this path
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if constexpr (IN_BF16) acc[e] += bf2f(reinterpret_cast<const uint16_t*>(bias)[col + e]);
+          else acc[e] += reinterpret_cast<const float*>(bias)[col + e];
+        }
+      }
+      if constexpr (OUT_BF16) {
+        uint4 o;
+        o.x = (uint32_t)f2bf(acc[0]) | ((uint32_t)f2bf(acc[1]) << 16);
+        o.y = (uint32_t)f2bf(acc[2]) | ((uint32_t)f2bf(acc[3]) << 16);
+        o.z = (uint32_t)f2bf(acc[4]) | ((uint32_t)f2bf(acc[5]) << 16);
+        o.w = (uint32_t)f2bf(acc[6]) | ((uint32_t)f2bf(acc[7]) << 16);
+        reinterpret_cast<uint4*>(y)[v] = o;
+      } else {
+        reinterpret_cast<float4*>(y)[2 * v] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        reinterpret_cast<float4*>(y)[2 * v + 1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+      }
+    }
+    return;
+  }
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n; e += stride) {
+    float acc = 0.f;
+    for (int i = 0; i < p; ++i) {
+      if constexpr (IN_BF16) acc += bf2f(reinterpret_cast<const uint16_t*>(a.z[i])[e]);
+      else acc += reinterpret_cast<const float*>(a.z[i])[e];
+    }
+    if (bias) {
+      if constexpr (IN_BF16) acc += bf2f(reinterpret_cast<const uint16_t*>(bias)[e % N]);
+      else acc += reinterpret_cast<const float*>(bias)[e % N];
+    }
+    if constexpr (OUT_BF16) reinterpret_cast<uint16_t*>(y)[e] = f2bf(acc);
+    else reinterpret_cast<float*>(y)[e] = acc;
+  }
+}
+
+hipError_t partial_sum(const void* const* z, int p, const void* bias, void* y, int64_t T, int64_t N, bool in_bf16,
+                       bool out_bf16, hipStream_t s) {
+  if (T == 0 || N == 0) return hipSuccess;
+  SumArgs a{};
+  bool aligned = ((uintptr_t)y % 16 == 0) && (N % 8 == 0);
+  for (int i = 0; i < p; ++i) {
+    a.z[i] = z[i];
+    aligned = aligned && ((uintptr_t)z[i] % 16 == 0);
+  }
+  const int vec = aligned ? 1 : 0;
+  const int grid = stream_grid(vec ? (T * N) / 8 : T * N, 256);
+  if (in_bf16 && out_bf16)
+    hipLaunchKernelGGL((partial_sum_kernel<true, true>), dim3(grid), dim3(256), 0, s, a, p, bias, y, T, N, vec);
+  else if (in_bf16)
+    hipLaunchKernelGGL((partial_sum_kernel<true, false>), dim3(grid), dim3(256), 0, s, a, p, bias, y, T, N, vec);
+  else if (out_bf16)
+    hipLaunchKernelGGL((partial_sum_kernel<false, true>), dim3(grid), dim3(256), 0, s, a, p, bias, y, T, N, vec);
+  else
+    hipLaunchKernelGGL((partial_sum_kernel<false, false>), dim3(grid), dim3(256), 0, s, a, p, bias, y, T, N, vec);
+  return hipGetLastError();
+}
+
+// ---- zero fill --------------------------------------------------------------------
+__global__ __launch_bounds__(256) void zero_kernel(char* p, size_t bytes, int vec) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  const size_t nv = vec ? bytes / 16 : 0;
+  for (size_t v = blockIdx.x * (size_t)blockDim.x + threadIdx.x; v < nv; v += stride)
+    reinterpret_cast<uint4*>(p)[v] = make_uint4(0, 0, 0, 0);
+  for (size_t e = nv * 16 + blockIdx.x * (size_t)blockDim.x + threadIdx.x; e < bytes; e += stride) p[e] = 0;
+}
+
+hipError_t zero_fill(void* ws, size_t bytes, hipStream_t s) {
+  if (bytes == 0) return hipSuccess;
+  const int vec = ((uintptr_t)ws % 16 == 0) ? 1 : 0;
+  const int64_t units = vec ? (int64_t)(bytes / 16) + 1 : (int64_t)bytes;
+  hipLaunchKernelGGL(zero_kernel, dim3(stream_grid(units, 256)), dim3(256), 0, s, (char*)ws, bytes, vec);
+  return hipGetLastError();
+}
+
+}  // namespace tpk

@@ -1,0 +1,138 @@
+// Device-side helpers shared by the tpshard kernels (gfx950 / CDNA4, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tpk {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Epilogue kinds of the GEMM kernels.
+enum Epi : int {
+  EPI_STORE = 0,       // C = acc
+  EPI_ACT = 1,         // a = acc (+ bias); C2 <- a (optional); C = act(a)
+  EPI_SWIGLU = 2,      // dual: C2 <- g, C3 <- u (optional); C = silu(g) * u
+  EPI_DUAL_STORE = 3,  // dual: C = acc0, C2 = acc1
+  EPI_SWIGLU_BWD = 4,  // acc = dh; g = S0, u = S1: C = dh*u*silu'(g), C2 = dh*silu(g), C3 = silu(g)*u
+  EPI_ACT_BWD = 5,     // acc = dh; a = S0: C = dh*act'(a), C3 = act(a)
+};
+
+enum ActKind : int { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU = 2, ACT_SWIGLU = 3 };
+
+// fp32 -> bf16 with round-to-nearest-even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+// Activations in fp32 (exact erf GELU; silu(g) = g * sigmoid(g)).
+__device__ __forceinline__ float sigmoidf_(float g) { return 1.0f / (1.0f + expf(-g)); }
+__device__ __forceinline__ float act_fwd(int act, float a) {
+  if (act == ACT_RELU) return a > 0.0f ? a : 0.0f;
+  if (act == ACT_GELU) return 0.5f * a * (1.0f + erff(a * 0.70710678118654752f));
+  return a;
+}
+__device__ __forceinline__ float act_grad(int act, float a) {
+  if (act == ACT_RELU) return a > 0.0f ? 1.0f : 0.0f;
+  if (act == ACT_GELU) {
+    const float cdf = 0.5f * (1.0f + erff(a * 0.70710678118654752f));
+    const float pdf = 0.39894228040143268f * expf(-0.5f * a * a);
+    return cdf + a * pdf;
+  }
+  return 1.0f;
+}
+
+// Parameters shared by the bf16 MFMA GEMM and the fp32 GEMM.
+//   C[m, n] = sum_k A(m, k) B(k, n)
+// A(m, k) is A[m*lda + k] when A is k-contiguous, else A[k*lda + m].
+// B(k, n) is B[n*ldb + k] when B is k-contiguous, else B[k*ldb + n].
+// Two K segments (seg 0 then seg 1) let dx = dG W1^T + dU Wup^T run as one
+// GEMM; in dual mode B0 and B1 are two B matrices over the same K that give
+// two accumulators per output element (gate and up).
+struct GemmParams {
+  const void* A0;
+  const void* A1;
+  const void* B0;
+  const void* B1;
+  int64_t lda, ldb;
+  int K0, K1;
+  int M, N;            // output rows / columns (columns of ONE B in dual mode)
+  void* C;
+  void* C2;
+  void* C3;
+  int64_t ldc, ldc2, ldc3;
+  const void* S0;
+  const void* S1;
+  int64_t lds;
+  const void* bias;    // per-column bias (EPI_ACT only), may be null
+  int act;
+  int vecA, vecB;      // 16-byte vector loads allowed for A / B
+  int splitk;          // number of K splits (>= 1)
+  float* partials;     // split-K fp32 partial tiles
+  int* counters;       // split-K arrival counters (zero on entry, left zero)
+};
+
+// Element stores / loads of the output and side tensors.
+template <typename T>
+__device__ __forceinline__ void st(void* base, int64_t ld, int m, int n, float v);
+template <>
+__device__ __forceinline__ void st<uint16_t>(void* base, int64_t ld, int m, int n, float v) {
+  reinterpret_cast<uint16_t*>(base)[(int64_t)m * ld + n] = f2bf(v);
+}
+template <>
+__device__ __forceinline__ void st<float>(void* base, int64_t ld, int m, int n, float v) {
+  reinterpret_cast<float*>(base)[(int64_t)m * ld + n] = v;
+}
+template <typename T>
+__device__ __forceinline__ float ld_in(const void* base, int64_t ld, int m, int n);
+template <>
+__device__ __forceinline__ float ld_in<uint16_t>(const void* base, int64_t ld, int m, int n) {
+  return bf2f(reinterpret_cast<const uint16_t*>(base)[(int64_t)m * ld + n]);
+}
+template <>
+__device__ __forceinline__ float ld_in<float>(const void* base, int64_t ld, int m, int n) {
+  return reinterpret_cast<const float*>(base)[(int64_t)m * ld + n];
+}
+
+// The epilogue for one output element.  OutT is the type of C (and of the
+// C2/C3 side outputs and S0/S1 side inputs, except EPI_STORE's f32 output of
+// bf16 inputs, which only writes C).
+template <int EPI, typename OutT, typename SideT>
+__device__ __forceinline__ void epilogue_elem(const GemmParams& p, int m, int n, float v0, float v1) {
+  if constexpr (EPI == EPI_STORE) {
+    st<OutT>(p.C, p.ldc, m, n, v0);
+  } else if constexpr (EPI == EPI_ACT) {
+    float a = v0;
+    if (p.bias) a += ld_in<SideT>(p.bias, 0, 0, n);
+    if (p.C2) st<SideT>(p.C2, p.ldc2, m, n, a);
+    st<OutT>(p.C, p.ldc, m, n, act_fwd(p.act, a));
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    if (p.C2) {
+      st<SideT>(p.C2, p.ldc2, m, n, v0);
+      st<SideT>(p.C3, p.ldc2, m, n, v1);
+    }
+    st<OutT>(p.C, p.ldc, m, n, v0 * sigmoidf_(v0) * v1);
+  } else if constexpr (EPI == EPI_DUAL_STORE) {
+    st<OutT>(p.C, p.ldc, m, n, v0);
+    st<OutT>(p.C2, p.ldc2, m, n, v1);
+  } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+    const float g = ld_in<SideT>(p.S0, p.lds, m, n);
+    const float u = ld_in<SideT>(p.S1, p.lds, m, n);
+    const float s = sigmoidf_(g);
+    const float sg = g * s;
+    st<OutT>(p.C, p.ldc, m, n, v0 * u * (s + sg * (1.0f - s)));
+    st<OutT>(p.C2, p.ldc2, m, n, v0 * sg);
+    st<OutT>(p.C3, p.ldc3, m, n, sg * u);
+  } else if constexpr (EPI == EPI_ACT_BWD) {
+    const float a = ld_in<SideT>(p.S0, p.lds, m, n);
+    st<OutT>(p.C, p.ldc, m, n, v0 * act_grad(p.act, a));
+    st<OutT>(p.C3, p.ldc3, m, n, act_fwd(p.act, a));
+  }
+}
+
+}  // namespace tpk

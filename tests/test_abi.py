@@ -1,0 +1,153 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol,
+its host helpers agree with the oracle, and every invalid-argument path
+returns its status code before anything is launched (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle as O
+import tensor_sharded_transformer_amd as tp
+from tensor_sharded_transformer_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tpshard.h")
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+OK, NULL, SHAPE, DTYPE, ACTE, WS = 0, 1, 2, 3, 4, 5
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.lib_path()):
+        pytest.skip("libtpshard.so not built")
+    return B.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(tp_[a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("tp_col_linear", "tp_act_inplace", "tp_row_linear_partial", "tp_mlp_shard_fwd", "tp_mlp_shard_bwd",
+              "tp_partial_sum", "tp_shard_range", "tp_gqa_shard"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(B.SIGNATURES)
+
+
+def test_abi_version(lib):
+    assert tp.tp_abi_version() == 1
+
+
+@pytest.mark.parametrize("n,p", [(256, 4), (28672, 8), (3, 3), (14336, 8), (1280, 1)])
+def test_shard_range_matches_oracle(lib, n, p):
+    for i in range(p):
+        assert tp.tp_shard_range(n, p, i) == O.shard_range(n, p, i)
+
+
+def test_shard_range_errors(lib):
+    b, ln = ctypes.c_int64(), ctypes.c_int64()
+    assert lib.tp_shard_range(10, 4, 0, ctypes.byref(b), ctypes.byref(ln)) == SHAPE
+    assert lib.tp_shard_range(8, 0, 0, ctypes.byref(b), ctypes.byref(ln)) == SHAPE
+    assert lib.tp_shard_range(8, 2, 2, ctypes.byref(b), ctypes.byref(ln)) == SHAPE
+    assert lib.tp_shard_range(-8, 2, 0, ctypes.byref(b), ctypes.byref(ln)) == SHAPE
+    assert lib.tp_shard_range(8, 2, 0, None, ctypes.byref(ln)) == NULL
+    assert "divisible" in lib.tp_last_error().decode() or lib.tp_last_error()
+
+
+def test_gqa_shard_matches_page_and_oracle(lib):
+    for i in range(8):
+        assert tp.tp_gqa_shard(64, 8, 128, 8, i) == O.gqa_shard(64, 8, 128, 8, i) == (1024 * i, 1024, 128 * i, 128)
+    with pytest.raises(tp.TpError) as e:
+        tp.tp_gqa_shard(64, 8, 128, 16, 0)   # 8 KV heads cannot be split over 16 ranks
+    assert e.value.status == SHAPE
+
+
+def test_col_linear_validation(lib):
+    f = lib.tp_col_linear
+    # bad dtype / act
+    assert f(FAKE, FAKE, None, None, FAKE, None, 0, 4, 8, 8, 7, 0, None) == DTYPE
+    assert f(FAKE, FAKE, None, None, FAKE, None, 0, 4, 8, 8, 0, 9, None) == ACTE
+    # SWIGLU needs w_up; others must not have it; no bias with SWIGLU
+    assert f(FAKE, FAKE, None, None, FAKE, None, 0, 4, 8, 8, 0, 3, None) == ACTE
+    assert f(FAKE, FAKE, FAKE, None, FAKE, None, 0, 4, 8, 8, 0, 1, None) == ACTE
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 4, 8, 8, 0, 3, None) == ACTE
+    # negative sizes
+    assert f(FAKE, FAKE, None, None, FAKE, None, 0, -1, 8, 8, 0, 1, None) == SHAPE
+    # null operands
+    assert f(None, FAKE, None, None, FAKE, None, 0, 4, 8, 8, 0, 1, None) == NULL
+    assert f(FAKE, FAKE, None, None, None, None, 0, 4, 8, 8, 0, 1, None) == NULL
+    # T == 0 is a no-op, even with null pointers
+    assert f(None, None, None, None, None, None, 0, 0, 8, 8, 0, 1, None) == OK
+
+
+def test_col_linear_workspace_too_small(lib):
+    need = lib.tp_col_linear_workspace(64, 8192, 3584, 0, 3)
+    assert need > 0   # decode-sized calls split K
+    assert lib.tp_col_linear(FAKE, FAKE, FAKE, None, FAKE, FAKE, need - 1, 64, 8192, 3584, 0, 3, None) == WS
+    assert lib.tp_col_linear_workspace(4096, 8192, 3584, 0, 3) == 0   # large T: no split
+
+
+def test_act_inplace_validation(lib):
+    f = lib.tp_act_inplace
+    assert f(FAKE, None, 4, 8, 0, 3, None) == ACTE        # SWIGLU without up
+    assert f(FAKE, FAKE, 4, 8, 0, 2, None) == ACTE        # up with GELU
+    assert f(None, None, 4, 8, 0, 1, None) == NULL
+    assert f(FAKE, None, 4, 8, 5, 1, None) == DTYPE
+    assert f(None, None, 4, 8, 0, 0, None) == OK          # NONE: no-op
+
+
+def test_row_linear_validation(lib):
+    f = lib.tp_row_linear_partial
+    assert f(FAKE, FAKE, FAKE, None, 0, 4, 8, 8, 1, 0, None) == DTYPE   # f32 in, bf16 out
+    assert f(FAKE, None, FAKE, None, 0, 4, 8, 8, 0, 0, None) == NULL
+    assert f(FAKE, FAKE, FAKE, None, 0, 4, -8, 8, 0, 0, None) == SHAPE
+    assert f(None, None, None, None, 0, 0, 8, 8, 0, 0, None) == OK
+
+
+def test_mlp_fwd_validation(lib):
+    f = lib.tp_mlp_shard_fwd
+    need = lib.tp_mlp_shard_fwd_workspace(64, 8192, 3584, 0, 3)
+    assert need >= 64 * 3584 * 2
+    args = (64, 8192, 3584, 0, 0, 3, None)
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, need - 1, *args) == WS
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, *args) == WS
+    assert f(FAKE, FAKE, None, FAKE, FAKE, None, FAKE, need, *args) == ACTE    # SWIGLU needs w_up
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, need, 64, 8192, 3584, 0, 0, 1, None) == ACTE
+    assert f(FAKE, FAKE, None, FAKE, FAKE, None, FAKE, need, 64, 8192, 3584, 1, 0, 1, None) == DTYPE  # f32 -> bf16
+    assert f(None, FAKE, FAKE, FAKE, FAKE, None, FAKE, need, *args) == NULL
+    assert f(None, None, FAKE, None, None, None, None, 0, 0, 8192, 3584, 0, 0, 3, None) == OK  # T == 0
+
+
+def test_mlp_bwd_validation(lib):
+    f = lib.tp_mlp_shard_bwd
+    need = lib.tp_mlp_shard_bwd_workspace(2048, 4096, 1792, 0, 3)
+    assert need >= 2048 * 1792 * 2 * 3
+    sz = (2048, 4096, 1792, 0, 3, None)
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, *sz) == WS
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, need, *sz) == ACTE  # dw_up missing
+    assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need, *sz) == NULL  # saved missing
+
+
+def test_partial_sum_validation(lib):
+    f = lib.tp_partial_sum
+    arr = (ctypes.c_void_p * 2)(0x1000, None)
+    assert f(arr, 2, None, FAKE, 4, 8, 0, 1, None) == NULL          # z[1] null
+    assert f(arr, 0, None, FAKE, 4, 8, 0, 1, None) == SHAPE
+    assert f(arr, 65, None, FAKE, 4, 8, 0, 1, None) == SHAPE
+    assert f(arr, 1, None, FAKE, 4, 8, 3, 1, None) == DTYPE
+    assert f(arr, 2, None, FAKE, 0, 8, 0, 1, None) == OK             # T == 0
+
+
+def test_status_strings(lib):
+    for s in range(8):
+        assert lib.tp_status_string(s)

@@ -1,0 +1,352 @@
+"""GPU parity: every entry point of the C ABI against the fp64 oracle on the
+same seeded inputs.
+
+Bars: bf16 inputs with fp32 accumulation -> relative Frobenius error <= 5e-3
+and max |err| <= 1e-2 * max |ref|; fp32 throughout -> both <= 1e-5; the
+integer worked example -> bit-exact.  Large workloads are checked on a
+seeded 64-row subset (rows are independent for the forward and for dx);
+weight gradients reduce over all tokens, so they are checked in full.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+import tensor_sharded_transformer_amd as tp
+
+from test_oracle_pins import load_golden
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = (5e-3, 1e-2)
+F32_TOL = (1e-5, 1e-5)
+
+
+def cuda(t):
+    return t.contiguous().to("cuda")
+
+
+def assert_close(got, ref, tol, what=""):
+    ok, rf, rm = O.within(got, ref, tol)
+    assert ok, f"{what}: rel_frob={rf:.3e} rel_max={rm:.3e} (tol {tol})"
+
+
+def dt_of(t):
+    return tp.TP_BF16 if t.dtype == torch.bfloat16 else tp.TP_F32
+
+
+def fwd(x, w1, wup, w2, act, out_dtype=None, saved=False):
+    T, d = x.shape
+    ff_i = w1.shape[1]
+    ws = tp.new_workspace(tp.tp_mlp_shard_fwd_workspace(T, d, ff_i, dt_of(x), act))
+    y = torch.empty(T, d, dtype=out_dtype or x.dtype, device="cuda")
+    sv = None
+    if saved:
+        sv = torch.empty(T, (2 if act == "swiglu" else 1) * ff_i, dtype=x.dtype, device="cuda")
+    tp.tp_mlp_shard_fwd(x, w1, wup, w2, y, act, ws, sv)
+    return y, sv
+
+
+def bwd(x, w1, wup, w2, saved, dy, act):
+    T, d = x.shape
+    ff_i = w1.shape[1]
+    ws = tp.new_workspace(tp.tp_mlp_shard_bwd_workspace(T, d, ff_i, dt_of(x), act))
+    dw1 = torch.empty_like(w1)
+    dwup = torch.empty_like(wup) if wup is not None else None
+    dw2 = torch.empty_like(w2)
+    dx = torch.empty_like(x)
+    tp.tp_mlp_shard_bwd(x, w1, wup, w2, saved, dy, dw1, dwup, dw2, dx, act, ws)
+    return dw1, dwup, dw2, dx
+
+
+def shard(w1, wup, w2, p, i):
+    """Host-side slicing of the unsharded weights with the library's own ranges."""
+    b, n = tp.tp_shard_range(w1.shape[1], p, i)
+    return (w1[:, b:b + n].contiguous(), None if wup is None else wup[:, b:b + n].contiguous(),
+            w2[b:b + n, :].contiguous())
+
+
+# ---------------------------------------------------------------------------
+# The pages' worked example, bit-exact on the GPU.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_worked_example_exact(dtype):
+    g = load_golden("worked_example.txt")
+    x = cuda(torch.tensor(g["x"][None, :], dtype=dtype))
+    A = torch.tensor(g["A"], dtype=dtype)
+    Bm = torch.tensor(g["B"], dtype=dtype)
+    p = int(g["tp"][0])
+    parts = []
+    for i in range(p):
+        w1_i, _, w2_i = shard(A, None, Bm, p, i)
+        w1_i, w2_i = cuda(w1_i), cuda(w2_i)
+        h = torch.empty(1, 1, dtype=dtype, device="cuda")
+        tp.tp_col_linear(x, w1_i, None, None, h, "relu")
+        y_i, _ = fwd(x, w1_i, None, w2_i, "relu", out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert h.item() == g["y"][i]
+        parts.append(y_i)
+    z = torch.empty(1, 2, dtype=torch.float32, device="cuda")
+    tp.tp_partial_sum(parts, None, z)
+    assert z.cpu().numpy().tolist() == [g["z"].tolist()]
+
+
+# ---------------------------------------------------------------------------
+# Identity operand: the product must reproduce the other operand exactly
+# (checks tile staging, the MFMA output mapping and the edge masks).
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T,N", [(64, 200), (300, 520), (1000, 1032)])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_identity_times_w_is_w(T, N, dtype):
+    x = cuda(torch.eye(T, dtype=dtype))
+    w = W.normal((T, N), 1.0, 42, T + N, "f32").to(dtype)
+    z = torch.empty(T, N, dtype=torch.float32, device="cuda")
+    tp.tp_row_linear_partial(x, cuda(w), z)
+    torch.cuda.synchronize()
+    assert torch.equal(z.cpu(), w.float())
+
+
+# ---------------------------------------------------------------------------
+# Tiny fp32 MLP, p = 4 (x 4x64, W1 64x256, W2 256x64, ReLU).
+# ---------------------------------------------------------------------------
+def test_tiny_fp32_p4():
+    w = W.TINY
+    t = W.mlp_unsharded(w)
+    x = cuda(t["x"])
+    parts = []
+    for i in range(w.p):
+        w1_i, _, w2_i = shard(t["w1"], None, t["w2"], w.p, i)
+        y_i, _ = fwd(x, cuda(w1_i), None, cuda(w2_i), w.act)
+        o1, _, o2 = O.shard_mlp_weights(t["w1"], None, t["w2"], w.p, i)
+        ref_i, _ = O.mlp_shard_fwd(O.to64(t["x"]), o1, None, o2, w.act)
+        assert_close(y_i, ref_i, F32_TOL, f"shard {i}")
+        parts.append(y_i)
+    y = torch.empty(w.T, w.d, dtype=torch.float32, device="cuda")
+    tp.tp_partial_sum(parts, None, y)
+    ref = O.mlp_full(O.to64(t["x"]), O.to64(t["w1"]), None, O.to64(t["w2"]), w.act)
+    assert_close(y, ref, F32_TOL, "sum of partials vs unsharded")
+
+
+# ---------------------------------------------------------------------------
+# Ragged shapes (nothing a multiple of the tile sizes), every activation.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("act", ["relu", "gelu", "swiglu", "none"])
+@pytest.mark.parametrize("T,d,ff,p", [(5, 72, 120, 3), (77, 200, 168, 3), (300, 1000, 784, 2)])
+def test_ragged_forward_and_sum(act, T, d, ff, p):
+    w = W.MlpWorkload("ragged", T=T, d=d, ff=ff, p=p, act=act, dtype="bf16", seed=T + d)
+    t = W.mlp_unsharded(w)
+    x = cuda(t["x"])
+    x64 = O.to64(t["x"])
+    parts = []
+    for i in range(p):
+        w1_i, wup_i, w2_i = shard(t["w1"], t.get("w_up"), t["w2"], p, i)
+        y_i, sv = fwd(x, cuda(w1_i), None if wup_i is None else cuda(wup_i), cuda(w2_i), act,
+                      out_dtype=torch.float32, saved=True)
+        o1, ou, o2 = O.shard_mlp_weights(t["w1"], t.get("w_up"), t["w2"], p, i)
+        ref_i, ref_sv = O.mlp_shard_fwd(x64, o1, ou, o2, act)
+        assert_close(y_i, ref_i, BF16_TOL, f"y_{i}")
+        if act == "swiglu":
+            ff_i = w1_i.shape[1]
+            assert_close(sv[:, :ff_i], ref_sv["g"], BF16_TOL, "saved G")
+            assert_close(sv[:, ff_i:], ref_sv["u"], BF16_TOL, "saved U")
+        else:
+            assert_close(sv, ref_sv["a"], BF16_TOL, "saved A")
+        # the pieces separately: column GEMM + act, then row partial
+        h = torch.empty(T, w1_i.shape[1], dtype=torch.bfloat16, device="cuda")
+        tp.tp_col_linear(x, cuda(w1_i), None if wup_i is None else cuda(wup_i), None, h, act)
+        assert_close(h, O.col_linear(x64, o1, ou, None, act), BF16_TOL, "h_i")
+        # row partial on its own seeded input (never a GPU output fed to the oracle)
+        h_in = W.normal((T, w1_i.shape[1]), 1.0, w.seed, 50 + i)
+        z = torch.empty(T, d, dtype=torch.float32, device="cuda")
+        tp.tp_row_linear_partial(cuda(h_in), cuda(w2_i), z)
+        assert_close(z, O.row_linear_partial(O.to64(h_in), o2), BF16_TOL, "row partial")
+        parts.append(y_i)
+    y = torch.empty(T, d, dtype=torch.float32, device="cuda")
+    tp.tp_partial_sum(parts, None, y)
+    ref = O.mlp_full(x64, O.to64(t["w1"]), None if "w_up" not in t else O.to64(t["w_up"]), O.to64(t["w2"]), act)
+    assert_close(y, ref, BF16_TOL, "sum of partials vs unsharded")
+
+
+def test_act_inplace_matches_oracle():
+    for act in ("relu", "gelu", "swiglu"):
+        h = W.normal((37, 99), 2.0, 5, 1)
+        up = W.normal((37, 99), 1.0, 5, 2) if act == "swiglu" else None
+        hd = cuda(h)
+        tp.tp_act_inplace(hd, None if up is None else cuda(up), act)
+        ref = O.act_apply(O.to64(h), act, None if up is None else O.to64(up))
+        assert_close(hd, ref, BF16_TOL, act)
+        # fp32 variant
+        hf = cuda(h.float())
+        tp.tp_act_inplace(hf, None if up is None else cuda(up.float()), act)
+        assert_close(hf, ref, (2e-6, 2e-6), act + " f32")
+
+
+def test_col_linear_with_bias_is_a_slice():
+    x = W.normal((50, 96), 1.0, 9, 1)
+    w = W.normal((96, 240), 0.1, 9, 2)
+    b = W.normal((240,), 1.0, 9, 3)
+    full = O.col_linear(O.to64(x), O.to64(w), bias=O.to64(b), act="gelu")
+    for i in range(3):
+        s, n = tp.tp_shard_range(240, 3, i)
+        y = torch.empty(50, n, dtype=torch.bfloat16, device="cuda")
+        tp.tp_col_linear(cuda(x), cuda(w[:, s:s + n]), None, cuda(b[s:s + n]), y, "gelu")
+        assert_close(y, full[:, s:s + n], BF16_TOL, f"shard {i}")
+
+
+def test_partial_sum_bias_once_and_dtypes():
+    zs = [W.normal((33, 80), 1.0, 11, i) for i in range(5)]
+    bias = W.normal((80,), 1.0, 11, 9)
+    ref = O.partial_sum([O.to64(z) for z in zs], O.to64(bias))
+    for out in (torch.float32, torch.bfloat16):
+        y = torch.empty(33, 80, dtype=out, device="cuda")
+        tp.tp_partial_sum([cuda(z) for z in zs], cuda(bias), y)
+        assert_close(y, ref, F32_TOL if out == torch.float32 else BF16_TOL, str(out))
+    # fp32 inputs, odd sizes (scalar path)
+    zf = [W.normal((7, 13), 1.0, 12, i, "f32") for i in range(3)]
+    y = torch.empty(7, 13, dtype=torch.float32, device="cuda")
+    tp.tp_partial_sum([cuda(z) for z in zf], None, y)
+    assert_close(y, O.partial_sum([O.to64(z) for z in zf]), F32_TOL, "f32 ragged")
+
+
+def test_zero_tokens_is_a_noop():
+    x = torch.empty(0, 64, dtype=torch.bfloat16, device="cuda")
+    w1 = torch.zeros(64, 32, dtype=torch.bfloat16, device="cuda")
+    w2 = torch.zeros(32, 64, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty(0, 64, dtype=torch.bfloat16, device="cuda")
+    tp.tp_mlp_shard_fwd(x, w1, None, w2, y, "relu", None)
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# Large single GEMM through the 256x256 tiles with ragged edges.
+# ---------------------------------------------------------------------------
+def test_large_ragged_row_partial():
+    T, K, N = 2000, 264, 8100
+    x = W.normal((T, K), 1.0, 21, 1)
+    w = W.normal((K, N), 0.02, 21, 2)
+    z = torch.empty(T, N, dtype=torch.bfloat16, device="cuda")
+    tp.tp_row_linear_partial(cuda(x), cuda(w), z)
+    rows = W.row_subset(T, 64, 21)
+    assert_close(z[rows], O.matmul(O.to64(x[rows]), O.to64(w)), BF16_TOL, "rows")
+
+
+# ---------------------------------------------------------------------------
+# The 70B-class SwiGLU shard at decode (T=64, split-K path) and prefill.
+# ---------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def rank0_weights():
+    return W.mlp_rank_weights(W.DECODE, 0)
+
+
+def test_decode_T64_shard(rank0_weights):
+    w = W.DECODE
+    x = W.mlp_input(w)
+    wt = rank0_weights
+    y, sv = fwd(cuda(x), cuda(wt["w1"]), cuda(wt["w_up"]), cuda(wt["w2"]), "swiglu", saved=True)
+    ref, rsv = O.mlp_shard_fwd(O.to64(x), O.to64(wt["w1"]), O.to64(wt["w_up"]), O.to64(wt["w2"]), "swiglu")
+    assert_close(y, ref, BF16_TOL, "y_0 decode")
+    assert_close(sv[:, :w.ff_i], rsv["g"], BF16_TOL, "G")
+    # determinism: the split-K reduction order is fixed
+    y2, _ = fwd(cuda(x), cuda(wt["w1"]), cuda(wt["w_up"]), cuda(wt["w2"]), "swiglu")
+    assert torch.equal(y, y2)
+
+
+def test_prefill_T4096_shard(rank0_weights):
+    w = W.PREFILL
+    x = W.mlp_input(w)
+    wt = rank0_weights
+    y, _ = fwd(cuda(x), cuda(wt["w1"]), cuda(wt["w_up"]), cuda(wt["w2"]), "swiglu")
+    rows = W.row_subset(w.T, 64, w.seed)
+    ref, _ = O.mlp_shard_fwd(O.to64(x[rows]), O.to64(wt["w1"]), O.to64(wt["w_up"]), O.to64(wt["w2"]), "swiglu")
+    assert_close(y[rows], ref, BF16_TOL, "y_0 prefill rows")
+    y2, _ = fwd(cuda(x), cuda(wt["w1"]), cuda(wt["w_up"]), cuda(wt["w2"]), "swiglu")
+    assert torch.equal(y, y2)
+
+
+# ---------------------------------------------------------------------------
+# GQA projections (h=8192, 64 Q heads, 8 KV heads, head_dim 128, p=8).
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("wl", [W.GQA_DECODE, W.GQA_PREFILL], ids=lambda w: w.name)
+def test_gqa_projections(wl):
+    t = W.gqa_unsharded(wl)
+    rows = W.row_subset(wl.T, 64, wl.seed)
+    x = cuda(t["x"])
+    x64 = O.to64(t["x"][rows])
+    parts = []
+    for i in range(wl.p):
+        qb, ql, kb, kl = tp.tp_gqa_shard(wl.n_q, wl.n_kv, wl.head_dim, wl.p, i)
+        wqkv = torch.cat([t["wq"][:, qb:qb + ql], t["wk"][:, kb:kb + kl], t["wv"][:, kb:kb + kl]], 1).contiguous()
+        assert wqkv.shape == (8192, 1280)
+        if i in (0, wl.p - 1):
+            ws = tp.new_workspace(tp.tp_col_linear_workspace(wl.T, wl.h, 1280, tp.TP_BF16, "none"))
+            qkv = torch.empty(wl.T, 1280, dtype=torch.bfloat16, device="cuda")
+            tp.tp_col_linear(x, cuda(wqkv), None, None, qkv, "none", ws)
+            ref = O.matmul(x64, O.gqa_local_qkv_weight(t["wq"], t["wk"], t["wv"], wl.n_q, wl.n_kv, wl.head_dim,
+                                                       wl.p, i))
+            assert_close(qkv[rows], ref, BF16_TOL, f"qkv rank {i}")
+        a_i = cuda(t["attn"][:, qb:qb + ql])
+        wo_i = cuda(t["wo"][qb:qb + ql, :])
+        ws = tp.new_workspace(tp.tp_row_linear_partial_workspace(wl.T, ql, wl.h, tp.TP_BF16))
+        o_i = torch.empty(wl.T, wl.h, dtype=torch.bfloat16, device="cuda")
+        tp.tp_row_linear_partial(a_i, wo_i, o_i, ws)
+        parts.append(o_i)
+    y = torch.empty(wl.T, wl.h, dtype=torch.float32, device="cuda")
+    tp.tp_partial_sum(parts, None, y)
+    ref = O.matmul(O.to64(t["attn"][rows]), O.to64(t["wo"]))
+    assert_close(y[rows], ref, BF16_TOL, "sum of o_proj partials")
+    ref0 = O.matmul(O.to64(t["attn"][rows][:, :1024]), O.to64(t["wo"][:1024]))
+    assert_close(parts[0][rows], ref0, BF16_TOL, "o_proj partial rank 0")
+
+
+# ---------------------------------------------------------------------------
+# Backward.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("act", ["swiglu", "relu", "gelu", "none"])
+def test_backward_small_ragged(act):
+    w = W.MlpWorkload("bwd_small", T=70, d=136, ff=168, p=3, act=act, dtype="bf16", seed=31)
+    t = W.mlp_unsharded(w, with_dy=True)
+    x, dy = cuda(t["x"]), cuda(t["dy"])
+    dxs = []
+    for i in range(w.p):
+        w1_i, wup_i, w2_i = (None if v is None else cuda(v) for v in shard(t["w1"], t.get("w_up"), t["w2"], w.p, i))
+        _, sv = fwd(x, w1_i, wup_i, w2_i, act, saved=True)
+        dw1, dwup, dw2, dx = bwd(x, w1_i, wup_i, w2_i, sv, dy, act)
+        o1, ou, o2 = O.shard_mlp_weights(t["w1"], t.get("w_up"), t["w2"], w.p, i)
+        ref = O.mlp_shard_bwd(O.to64(t["x"]), o1, ou, o2, O.to64(t["dy"]), act)
+        assert_close(dw1, ref["dw1"], BF16_TOL, "dW1")
+        assert_close(dw2, ref["dw2"], BF16_TOL, "dW2")
+        if act == "swiglu":
+            assert_close(dwup, ref["dw_up"], BF16_TOL, "dWup")
+        assert_close(dx, ref["dx"], BF16_TOL, "dx_i")
+        dxs.append(dx)
+    y = torch.empty_like(x, dtype=torch.float32)
+    tp.tp_partial_sum(dxs, None, y)
+    full = O.mlp_full_bwd(O.to64(t["x"]), O.to64(t["w1"]), None if "w_up" not in t else O.to64(t["w_up"]),
+                          O.to64(t["w2"]), O.to64(t["dy"]), act)
+    assert_close(y, full["dx"], BF16_TOL, "sum of dx partials")
+
+
+def test_backward_T2048_all_shards():
+    w = W.BACKWARD
+    t = W.mlp_unsharded(w, with_dy=True)
+    x, dy = cuda(t["x"]), cuda(t["dy"])
+    rows = W.row_subset(w.T, 64, w.seed)
+    x64, dy64 = O.to64(t["x"]), O.to64(t["dy"])
+    dxs = []
+    for i in range(w.p):
+        w1_i, wup_i, w2_i = (cuda(v) for v in shard(t["w1"], t["w_up"], t["w2"], w.p, i))
+        _, sv = fwd(x, w1_i, wup_i, w2_i, "swiglu", saved=True)
+        dw1, dwup, dw2, dx = bwd(x, w1_i, wup_i, w2_i, sv, dy, "swiglu")
+        if i in (0, w.p - 1):
+            o1, ou, o2 = O.shard_mlp_weights(t["w1"], t["w_up"], t["w2"], w.p, i)
+            ref = O.mlp_shard_bwd(x64, o1, ou, o2, dy64, "swiglu")
+            assert_close(dw1, ref["dw1"], BF16_TOL, f"dW1_{i}")
+            assert_close(dwup, ref["dw_up"], BF16_TOL, f"dWup_{i}")
+            assert_close(dw2, ref["dw2"], BF16_TOL, f"dW2_{i}")
+            assert_close(dx[rows], ref["dx"][rows], BF16_TOL, f"dx_{i}")
+        dxs.append(dx)
+    y = torch.empty(w.T, w.d, dtype=torch.float32, device="cuda")
+    tp.tp_partial_sum(dxs, None, y)
+    full = O.mlp_shard_bwd(x64[rows], O.to64(t["w1"]), O.to64(t["w_up"]), O.to64(t["w2"]), dy64[rows], "swiglu")
+    assert_close(y[rows], full["dx"], BF16_TOL, "sum of the 8 dx partials vs unsharded dx")
