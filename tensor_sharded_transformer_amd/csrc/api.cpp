@@ -75,10 +75,8 @@ void attach_split(GemmParams& p, const GemmPlan& plan, char* counters, char* par
   p.partials = plan.splitk > 1 ? reinterpret_cast<float*>(partials) : nullptr;
 }
 
-GemmPlan plan_for(int dtype, int M, int N, int K, bool dual, bool allow_split) {
-  GemmPlan plan = tpk::plan_gemm(M, N, K, dual);
-  if (dtype != TP_BF16 || !allow_split) plan.splitk = 1;
-  return plan;
+GemmPlan plan_for(int dtype, int M, int N, int K, bool dual, bool allow_split, bool fwd_layout, bool vec_ok) {
+  return tpk::plan_gemm(M, N, K, dual, fwd_layout, vec_ok, allow_split && dtype == TP_BF16);
 }
 
 hipError_t run_gemm(int dtype, const GemmParams& p, const GemmPlan& plan, GemmKind kind, bool out_f32,
@@ -93,11 +91,12 @@ struct FwdLayout {
   size_t h_bytes = 0, cnt_off = 0, part_off = 0, total = 0;
 };
 
-FwdLayout fwd_layout(int64_t T, int64_t d, int64_t ff_i, int dtype, int act) {
+// vec: every operand allows 16-byte vector loads (aligned, rows multiple of 8).
+FwdLayout fwd_layout(int64_t T, int64_t d, int64_t ff_i, int dtype, int act, bool vec) {
   FwdLayout L;
   const bool dual = act == TP_ACT_SWIGLU;
-  L.p1 = plan_for(dtype, (int)T, (int)ff_i, (int)d, dual, true);
-  L.p2 = plan_for(dtype, (int)T, (int)d, (int)ff_i, false, true);
+  L.p1 = plan_for(dtype, (int)T, (int)ff_i, (int)d, dual, true, true, vec);
+  L.p2 = plan_for(dtype, (int)T, (int)d, (int)ff_i, false, true, true, vec);
   SplitNeeds sn;
   sn.add(L.p1, (int)T, (int)ff_i, dual);
   sn.add(L.p2, (int)T, (int)d, false);
@@ -116,10 +115,10 @@ struct BwdLayout {
 BwdLayout bwd_layout(int64_t T, int64_t d, int64_t ff_i, int dtype, int act) {
   BwdLayout L;
   const bool sw = act == TP_ACT_SWIGLU;
-  L.pa = plan_for(dtype, (int)T, (int)ff_i, (int)d, false, true);   // dh
-  L.pb = plan_for(dtype, (int)ff_i, (int)d, (int)T, false, true);   // dW2
-  L.pc = plan_for(dtype, (int)d, (int)ff_i, (int)T, sw, true);      // dW1 (+dWup)
-  L.pd = plan_for(dtype, (int)T, (int)d, (int)((sw ? 2 : 1) * ff_i), false, true);  // dx
+  L.pa = plan_for(dtype, (int)T, (int)ff_i, (int)d, false, true, false, false);   // dh
+  L.pb = plan_for(dtype, (int)ff_i, (int)d, (int)T, false, true, false, false);   // dW2
+  L.pc = plan_for(dtype, (int)d, (int)ff_i, (int)T, sw, true, false, false);      // dW1 (+dWup)
+  L.pd = plan_for(dtype, (int)T, (int)d, (int)((sw ? 2 : 1) * ff_i), false, true, false, false);  // dx
   SplitNeeds sn;
   sn.add(L.pa, (int)T, (int)ff_i, false);
   sn.add(L.pb, (int)ff_i, (int)d, false);
@@ -136,11 +135,14 @@ BwdLayout bwd_layout(int64_t T, int64_t d, int64_t ff_i, int dtype, int act) {
 // Optional workspace of a single GEMM entry point: [counters][partials].
 struct SingleWs {
   GemmPlan plan;
+  bool dual = false;
   size_t cnt_bytes = 0, total = 0;
-  // With no workspace the call runs unsplit; a too-small one is an error.
+  // With no workspace the call runs unsplit (re-planned for that); a
+  // too-small workspace is an error.
   tp_status bind(GemmParams& p, void* ws, size_t ws_bytes, const char* who) {
     if (!ws || plan.splitk <= 1) {
-      plan.splitk = 1;
+      if (plan.splitk > 1) plan = tpk::plan_gemm(p.M, p.N, p.K0, dual, true,
+                                                 p.vecA && p.vecB, false);
       attach_split(p, plan, nullptr, nullptr);
       return TP_OK;
     }
@@ -151,9 +153,10 @@ struct SingleWs {
   }
 };
 
-SingleWs single_ws(int dtype, int M, int N, int K, bool dual) {
+SingleWs single_ws(int dtype, int M, int N, int K, bool dual, bool vec) {
   SingleWs W;
-  W.plan = plan_for(dtype, M, N, K, dual, true);
+  W.dual = dual;
+  W.plan = plan_for(dtype, M, N, K, dual, true, true, vec);
   SplitNeeds sn;
   sn.add(W.plan, M, N, dual);
   if (W.plan.splitk > 1) {
@@ -231,7 +234,11 @@ tp_status tp_workspace_init(void* ws, size_t bytes, tp_stream stream) {
 // ---- column-parallel linear ---------------------------------------------------
 size_t tp_col_linear_workspace(int64_t T, int64_t K, int64_t N_i, tp_dtype dtype, tp_act act) {
   if (!valid_dtype(dtype) || !valid_act(act) || !dim_ok(T) || !dim_ok(K) || !dim_ok(N_i) || T == 0) return 0;
-  return single_ws(dtype, (int)T, (int)N_i, (int)K, act == TP_ACT_SWIGLU).total;
+  // the kernel choice depends on operand alignment: report the larger need
+  const bool sw = act == TP_ACT_SWIGLU;
+  const size_t a = single_ws(dtype, (int)T, (int)N_i, (int)K, sw, true).total;
+  const size_t b = single_ws(dtype, (int)T, (int)N_i, (int)K, sw, false).total;
+  return a > b ? a : b;
 }
 
 tp_status tp_col_linear(const void* x, const void* w, const void* w_up, const void* bias, void* y, void* ws,
@@ -263,7 +270,7 @@ tp_status tp_col_linear(const void* x, const void* w, const void* w_up, const vo
   p.act = act;
   p.vecA = aligned16(x) && K % 8 == 0;
   p.vecB = aligned16(w) && (!sw || aligned16(w_up)) && N_i % 8 == 0;
-  SingleWs W = single_ws(dtype, (int)T, (int)N_i, (int)K, sw);
+  SingleWs W = single_ws(dtype, (int)T, (int)N_i, (int)K, sw, p.vecA && p.vecB);
   tp_status ws_st = W.bind(p, ws, ws_bytes, "tp_col_linear");
   if (ws_st != TP_OK) return ws_st;
   return hip_status(run_gemm(dtype, p, W.plan, sw ? tpk::GK_FWD_SWIGLU : tpk::GK_FWD_ACT, false,
@@ -289,7 +296,9 @@ tp_status tp_act_inplace(void* h, const void* up, int64_t T, int64_t N_i, tp_dty
 // ---- row-parallel partial ------------------------------------------------------
 size_t tp_row_linear_partial_workspace(int64_t T, int64_t K_i, int64_t N, tp_dtype in_dtype) {
   if (!valid_dtype(in_dtype) || !dim_ok(T) || !dim_ok(K_i) || !dim_ok(N) || T == 0) return 0;
-  return single_ws(in_dtype, (int)T, (int)N, (int)K_i, false).total;
+  const size_t a = single_ws(in_dtype, (int)T, (int)N, (int)K_i, false, true).total;
+  const size_t b = single_ws(in_dtype, (int)T, (int)N, (int)K_i, false, false).total;
+  return a > b ? a : b;
 }
 
 tp_status tp_row_linear_partial(const void* x_i, const void* w_i, void* z_i, void* ws, size_t ws_bytes, int64_t T,
@@ -314,7 +323,7 @@ tp_status tp_row_linear_partial(const void* x_i, const void* w_i, void* z_i, voi
   p.ldc = N;
   p.vecA = aligned16(x_i) && K_i % 8 == 0;
   p.vecB = aligned16(w_i) && N % 8 == 0;
-  SingleWs W = single_ws(in_dtype, (int)T, (int)N, (int)K_i, false);
+  SingleWs W = single_ws(in_dtype, (int)T, (int)N, (int)K_i, false, p.vecA && p.vecB);
   tp_status ws_st = W.bind(p, ws, ws_bytes, "tp_row_linear_partial");
   if (ws_st != TP_OK) return ws_st;
   return hip_status(run_gemm(in_dtype, p, W.plan, tpk::GK_FWD_STORE, out_dtype == TP_F32,
@@ -341,7 +350,9 @@ tp_status tp_partial_sum(const void* const* z, int p, const void* bias, void* y,
 size_t tp_mlp_shard_fwd_workspace(int64_t T, int64_t d, int64_t ff_i, tp_dtype dtype, tp_act act) {
   if (!valid_dtype(dtype) || !valid_act(act) || !dim_ok(T) || !dim_ok(d) || !dim_ok(ff_i)) return 0;
   if (T == 0) return 0;
-  return fwd_layout(T, d, ff_i, dtype, act).total;
+  const size_t a = fwd_layout(T, d, ff_i, dtype, act, true).total;
+  const size_t b = fwd_layout(T, d, ff_i, dtype, act, false).total;
+  return a > b ? a : b;
 }
 
 tp_status tp_mlp_shard_fwd(const void* x, const void* w1_i, const void* w_up_i, const void* w2_i, void* y_i,
@@ -357,7 +368,9 @@ tp_status tp_mlp_shard_fwd(const void* x, const void* w1_i, const void* w_up_i, 
   if (sw != (w_up_i != nullptr)) return fail(TP_ERR_ACT, "tp_mlp_shard_fwd: w_up_i must be given iff SWIGLU");
   if (T == 0) return TP_OK;
   if (!x || !w1_i || !w2_i || !y_i) return fail(TP_ERR_NULL, "tp_mlp_shard_fwd: null x, w1_i, w2_i or y_i");
-  const FwdLayout L = fwd_layout(T, d, ff_i, dtype, act);
+  const bool vec = aligned16(x) && aligned16(w1_i) && (!sw || aligned16(w_up_i)) && aligned16(w2_i) &&
+                   d % 8 == 0 && ff_i % 8 == 0;
+  const FwdLayout L = fwd_layout(T, d, ff_i, dtype, act, vec);
   if (!ws) return fail(TP_ERR_WORKSPACE, "tp_mlp_shard_fwd: workspace required (%zu bytes)", L.total);
   if (ws_bytes < L.total)
     return fail(TP_ERR_WORKSPACE, "tp_mlp_shard_fwd: workspace of %zu bytes < %zu needed", ws_bytes, L.total);

@@ -151,16 +151,6 @@ struct TileRC {
 template <int R, int NT, bool KC, bool DUAL>
 using Tile = typename std::conditional<KC, TileKC<R, NT, DUAL>, TileRC<R, NT, DUAL>>::type;
 
-// Renumber workgroups so that each XCD gets a contiguous range of ids.
-__device__ __forceinline__ int xcd_remap(int bid, int nblk) {
-  if (nblk < 8) return bid;
-  const int xcd = bid & 7;
-  const int idx = bid >> 3;
-  const int per = nblk >> 3;
-  const int rem = nblk & 7;
-  return xcd * per + (xcd < rem ? xcd : rem) + idx;
-}
-
 template <int BM, int BN, int WGM, int WGN, bool AKC, bool BKC, bool DUAL, int EPI, typename OutT>
 __global__ __launch_bounds__(WGM* WGN * 64) void gemm_bf16_kernel(const GemmParams p) {
   constexpr int NT = WGM * WGN * 64;
@@ -276,47 +266,59 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_bf16_kernel(const GemmPara
   }
 
   // ---- split-K: publish, and let the last arriving split finish ----------
+  // Partials are written and read with relaxed agent-scope atomics, which are
+  // coherent across the XCDs' separate L2s without flushing them; a
+  // vmcnt(0) wait orders the stores before the arrival ticket, and the reads
+  // happen only after the ticket says every split has arrived.
   if (p.splitk > 1) {
-    constexpr int NV = TM * TN * 4;  // float4 per lane
-    float4* mine = reinterpret_cast<float4*>(p.partials) + ((int64_t)t * p.splitk + split) * NV * NT;
+    constexpr int NE = TM * TN * 16;  // floats per lane
+    float* mine = p.partials + ((int64_t)t * p.splitk + split) * NE * NT;
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          mine[((i * TN + j) * 4 + q) * NT + tid] =
-              make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-    __threadfence();
+        for (int r = 0; r < 16; ++r)
+          __hip_atomic_store(&mine[((i * TN + j) * 16 + r) * NT + tid], acc[i][j][r], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this lane's stores are complete
     __syncthreads();
     if (tid == 0) {
-      const int prev = atomicAdd(&p.counters[t], 1);
+      const int prev = __hip_atomic_fetch_add(&p.counters[t], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       s_last = (prev == p.splitk - 1);
     }
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
-    const float4* all = reinterpret_cast<const float4*>(p.partials) + (int64_t)t * p.splitk * NV * NT;
+    const float* all = p.partials + (int64_t)t * p.splitk * NE * NT;
+    // Sum the splits in ascending order; each split's values for one row of
+    // accumulator tiles are loaded together so the loads overlap.
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TM; ++i) {
+      f32x16 tot[TN];
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
-          for (int s = 0; s < p.splitk; ++s) {
-            float4 v;
-            if (s == split) {
-              v = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-            } else {
-              v = all[((int64_t)s * NV + (i * TN + j) * 4 + q) * NT + tid];
-            }
-            sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
-          }
-          acc[i][j][4 * q] = sum.x; acc[i][j][4 * q + 1] = sum.y;
-          acc[i][j][4 * q + 2] = sum.z; acc[i][j][4 * q + 3] = sum.w;
+        for (int r = 0; r < 16; ++r) tot[j][r] = 0.0f;
+      for (int s = 0; s < p.splitk; ++s) {
+        if (s == split) {
+#pragma unroll
+          for (int j = 0; j < TN; ++j) tot[j] += acc[i][j];
+        } else {
+          f32x16 v[TN];
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              v[j][r] = __hip_atomic_load(&all[((int64_t)s * NE + (i * TN + j) * 16 + r) * NT + tid], __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+          for (int j = 0; j < TN; ++j) tot[j] += v[j];
         }
-    if (tid == 0) atomicExch(&p.counters[t], 0);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = tot[j];
+    }
+    if (tid == 0) __hip_atomic_store(&p.counters[t], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // ---- epilogue -----------------------------------------------------------
@@ -380,31 +382,42 @@ static hipError_t launch_shape(GemmParams p, const GemmPlan& plan, hipStream_t s
   }
 }
 
-// Tile shape and K-split for an (M, N, K) problem on 256 CUs.
-GemmPlan plan_gemm(int M, int N, int K, bool dual) {
+// Kernel, tile shape and K-split for an (M, N, K) problem on 256 CUs.
+GemmPlan plan_gemm(int M, int N, int K, bool dual, bool fwd_layout, bool vec_ok, bool allow_split) {
   GemmPlan plan;
-  const int ncols = dual ? 2 * N : N;  // combined columns
+  constexpr int CUS = 256;
+  const int ksteps = (K + 15) / 16;
+  const bool stream_fits = allow_split || stream_lds_bytes(M, ksteps, dual) <= (size_t)STREAM_LDS_MAX;
+  if (M <= STREAM_MAX_M && fwd_layout && vec_ok && N >= 8 && stream_fits) {
+    // Decode-sized forward GEMM: weight streaming.  Split K across
+    // workgroups (a power of two) until about one workgroup per CU while
+    // keeping at least 16 k-steps of 16 per split, then further if the
+    // split's activation slice would not fit in LDS.
+    plan.kernel = KERNEL_STREAM;
+    const int strips = (N + STREAM_WCOLS - 1) / STREAM_WCOLS;
+    const int nsteps = (K + 15) / 16;
+    int split = 1;
+    const int min_steps = STREAM_MODE == 2 ? 8 * STREAM_KW : 16;  // per split
+    while (strips * split * 2 <= STREAM_TARGET_WGS && nsteps / (split * 2) >= min_steps) split *= 2;
+    while (stream_lds_bytes(M, (nsteps + split - 1) / split, dual) > (size_t)STREAM_LDS_MAX) split *= 2;
+    plan.splitk = allow_split ? split : 1;
+    return plan;
+  }
   auto tiles_for = [&](int bm, int bn) {
     const int bnh = dual ? bn / 2 : bn;
     return ((M + bm - 1) / bm) * ((N + bnh - 1) / bnh);
   };
-  (void)ncols;
+  plan.kernel = KERNEL_TILED;
   if (M <= 128) {
-    // Decode-sized: stream the weights once, split K so enough workgroups are
-    // in flight to keep HBM busy.
     plan.tile = TILE_64x128;
     const int tiles = tiles_for(64, 128);
     const int nk = (K + BK - 1) / BK;
     int split = 1;
-    while (tiles * split < 512 && split * 2 <= nk && split < 16) split *= 2;
-    plan.splitk = split;
+    while (tiles * split < CUS && split * 2 <= nk && split < 8) split *= 2;
+    plan.splitk = allow_split ? split : 1;
     return plan;
   }
-  if (tiles_for(256, 256) >= 256) {
-    plan.tile = TILE_256x256;
-  } else {
-    plan.tile = TILE_128x128;
-  }
+  plan.tile = tiles_for(256, 256) >= CUS ? TILE_256x256 : TILE_128x128;
   plan.splitk = 1;
   return plan;
 }
@@ -413,6 +426,14 @@ void gemm_split_sizes(const GemmPlan& plan, int M, int N, bool dual, size_t* par
   *part_bytes = 0;
   *n_tiles = 0;
   if (plan.splitk <= 1) return;
+  if (plan.kernel == KERNEL_STREAM) {
+    const size_t tiles = (size_t)(N + STREAM_WCOLS - 1) / STREAM_WCOLS * STREAM_TILES_PER_WG;
+    const int mt = M <= 32 ? 1 : (M <= 64 ? 2 : 4);
+    const size_t per = (size_t)mt * (dual ? 2 : 1) * STREAM_NW * 16 * 64;  // floats per column-group tile
+    *part_bytes = tiles * plan.splitk * per * sizeof(float);
+    *n_tiles = tiles;
+    return;
+  }
   int bm = 64, bn = 128;
   if (plan.tile == TILE_256x256) { bm = 256; bn = 256; }
   if (plan.tile == TILE_128x128) { bm = 128; bn = 128; }
@@ -423,6 +444,7 @@ void gemm_split_sizes(const GemmPlan& plan, int M, int N, bool dual, size_t* par
 }
 
 hipError_t gemm_bf16(const GemmParams& p, const GemmPlan& plan, GemmKind kind, bool out_f32, hipStream_t s) {
+  if (plan.kernel == KERNEL_STREAM) return gemm_stream(p, plan, kind, out_f32, s);
   switch (kind) {
     case GK_FWD_STORE:
       return out_f32 ? launch_shape<true, false, false, EPI_STORE, float>(p, plan, s)

@@ -77,6 +77,34 @@ struct GemmParams {
   int* counters;       // split-K arrival counters (zero on entry, left zero)
 };
 
+// Renumber workgroups so that each XCD gets a contiguous range of ids.
+__device__ __forceinline__ int xcd_remap(int bid, int nblk) {
+  if (nblk < 8) return bid;
+  const int xcd = bid & 7;
+  const int idx = bid >> 3;
+  const int per = nblk >> 3;
+  const int rem = nblk & 7;
+  return xcd * per + (xcd < rem ? xcd : rem) + idx;
+}
+
+// ---- split-K exchange ------------------------------------------------------
+// Partial tiles move through the workspace with 16-byte buffer operations
+// carrying the agent-scope coherence bit (sc1): they are coherent across the
+// XCDs' separate L2 caches without flushing or invalidating them.  The
+// buffer's byte bound makes out-of-range reads return 0.
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+constexpr int CPOL_SC1 = 16;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t splitk_rsrc(const float* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ void splitk_store(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4v v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, CPOL_SC1);
+}
+__device__ __forceinline__ f32x4v splitk_load(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CPOL_SC1);
+}
+
 // Element stores / loads of the output and side tensors.
 template <typename T>
 __device__ __forceinline__ void st(void* base, int64_t ld, int m, int n, float v);

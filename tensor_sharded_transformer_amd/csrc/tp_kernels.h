@@ -6,13 +6,54 @@
 
 #include "tp_device.h"
 
+// Build-time tuning of the weight-streaming kernel: k-steps of weight loads
+// in flight per wave, 32-column fragments per wave, waves (column groups) per
+// workgroup.
+#ifndef TP_STREAM_DEPTH
+#define TP_STREAM_DEPTH 3
+#endif
+#ifndef TP_STREAM_NW
+#define TP_STREAM_NW 1
+#endif
+#ifndef TP_STREAM_CW
+#define TP_STREAM_CW 4
+#endif
+#ifndef TP_STREAM_TARGET_WGS
+#define TP_STREAM_TARGET_WGS 256
+#endif
+// 1: the waves of a workgroup own adjacent column groups over one K range,
+//    with that range's activations staged once in LDS;
+// 2: the waves of a workgroup split the K range of one column group.
+#ifndef TP_STREAM_MODE
+#define TP_STREAM_MODE 1
+#endif
+#ifndef TP_STREAM_KW
+#define TP_STREAM_KW 8
+#endif
+
 namespace tpk {
+
+constexpr int STREAM_NW = TP_STREAM_NW;
+constexpr int STREAM_CW = TP_STREAM_CW;
+constexpr int STREAM_MODE = TP_STREAM_MODE;
+constexpr int STREAM_KW = TP_STREAM_KW;
+constexpr int STREAM_WCOLS = 32 * STREAM_NW * (STREAM_MODE == 2 ? 1 : STREAM_CW);  // output columns per workgroup
+constexpr int STREAM_TILES_PER_WG = STREAM_MODE == 2 ? 1 : STREAM_CW;             // split-K tiles per workgroup
+constexpr int STREAM_LDS_MAX = 160 * 1024;                // gfx950 LDS per workgroup
+constexpr int STREAM_MAX_M = 64;                          // tokens the streaming kernel serves
+constexpr int STREAM_TARGET_WGS = TP_STREAM_TARGET_WGS;   // K is split until about this many workgroups
+
+// LDS bytes the streaming kernel needs for M rows and a K range of `ksteps`
+// 16-value steps.
+size_t stream_lds_bytes(int M, int ksteps, bool dual);
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 enum TileShape : int { TILE_256x256 = 0, TILE_128x128 = 1, TILE_64x128 = 2 };
+enum KernelKind : int { KERNEL_TILED = 0, KERNEL_STREAM = 1 };
 
 struct GemmPlan {
+  int kernel = KERNEL_TILED;
   int tile = TILE_128x128;
   int splitk = 1;
 };
@@ -29,11 +70,16 @@ enum GemmKind : int {
   GK_BWD_DX = 7,          // A k-contig (two segments), B k-contig (two segments)
 };
 
-GemmPlan plan_gemm(int M, int N, int K, bool dual);
+// fwd_layout: A k-contiguous and B (K, N) n-contiguous (the forward GEMMs),
+// the only layout the weight-streaming kernel serves; vec_ok: both operands
+// allow 16-byte loads (its other precondition); allow_split: a workspace for
+// split-K partials is available.
+GemmPlan plan_gemm(int M, int N, int K, bool dual, bool fwd_layout, bool vec_ok, bool allow_split);
 // Split-K scratch for a plan: fp32 partial tiles (bytes) and one arrival
 // counter per output tile.
 void gemm_split_sizes(const GemmPlan& plan, int M, int N, bool dual, size_t* part_bytes, size_t* n_tiles);
 hipError_t gemm_bf16(const GemmParams& p, const GemmPlan& plan, GemmKind kind, bool out_f32, hipStream_t s);
+hipError_t gemm_stream(const GemmParams& p, const GemmPlan& plan, GemmKind kind, bool out_f32, hipStream_t s);
 
 // fp32 (SIMT) GEMM with the same parameter block and epilogues.
 hipError_t gemm_f32(const GemmParams& p, GemmKind kind, hipStream_t s);
