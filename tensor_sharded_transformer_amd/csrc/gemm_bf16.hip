@@ -30,6 +30,8 @@
 //    register order; the last split to arrive (agent-scope ticket) sums all
 //    splits in ascending order, so the result does not depend on timing, then
 //    runs the epilogue and re-zeroes the ticket.
+#include <type_traits>
+
 #include "tp_kernels.h"
 #include "tp_device.h"
 
@@ -40,26 +42,31 @@ constexpr int BK = 64;
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 __device__ __forceinline__ int lds_off(int row, int chunk) { return row * 128 + ((chunk ^ swz(row)) << 4); }
 
-// 8 consecutive bf16 starting at src[idx..idx+8), masked to `valid` elements.
-__device__ __forceinline__ uint4 load8_masked(const uint16_t* src, int valid) {
-  uint32_t w[4] = {0u, 0u, 0u, 0u};
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// 8 consecutive bf16 starting at src, masked to `valid` elements.
+__device__ __forceinline__ u32x4 load8_masked(const uint16_t* src, int valid) {
+  u32x4 w = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     if (e < valid) w[e >> 1] |= ((uint32_t)src[e]) << ((e & 1) * 16);
   }
-  return make_uint4(w[0], w[1], w[2], w[3]);
+  return w;
 }
 
 // A tile of R rows x BK k-values read from a k-contiguous matrix src[row*ld + k].
-// In dual mode rows [0, R/2) come from src0 and [R/2, R) from src1.
+// In dual mode rows [0, R/2) come from src0 and [R/2, R) from src1.  The
+// unmasked form is used for tiles that lie entirely inside the matrix with
+// 16-byte aligned rows; the masked form zero-fills past the edges.
 template <int R, int NT, bool DUAL>
 struct TileKC {
   static constexpr int TOTAL = R * (BK / 8);
   static constexpr int PER = (TOTAL + NT - 1) / NT;
-  uint4 v[PER];
+  u32x4 v[PER];
 
-  __device__ __forceinline__ void load(const uint16_t* src0, const uint16_t* src1, int64_t ld, int r0,
-                                       int rows, int k0, int klen, bool vec, int tid) {
+  template <bool MASKED>
+  __device__ __forceinline__ void load(const uint16_t* src0, const uint16_t* src1, int64_t ld, int r0, int rows,
+                                       int k0, int klen, bool vec, int tid) {
 #pragma unroll
     for (int c = 0; c < PER; ++c) {
       const int id = tid + c * NT;
@@ -70,12 +77,14 @@ struct TileKC {
       if (DUAL && row >= R / 2) { src = src1; row -= R / 2; }
       const int gr = r0 + row;
       const int gk = k0 + kc * 8;
-      if (gr < rows && gk < klen) {
+      if constexpr (!MASKED) {
+        v[c] = *reinterpret_cast<const u32x4*>(src + (int64_t)gr * ld + gk);
+      } else if (gr < rows && gk < klen) {
         const uint16_t* ptr = src + (int64_t)gr * ld + gk;
-        if (vec && gk + 8 <= klen) v[c] = *reinterpret_cast<const uint4*>(ptr);
+        if (vec && gk + 8 <= klen) v[c] = *reinterpret_cast<const u32x4*>(ptr);
         else v[c] = load8_masked(ptr, klen - gk);
       } else {
-        v[c] = make_uint4(0u, 0u, 0u, 0u);
+        v[c] = u32x4{0u, 0u, 0u, 0u};
       }
     }
   }
@@ -84,7 +93,7 @@ struct TileKC {
     for (int c = 0; c < PER; ++c) {
       const int id = tid + c * NT;
       if (TOTAL % NT != 0 && id >= TOTAL) break;
-      *reinterpret_cast<uint4*>(lds + lds_off(id >> 3, id & 7)) = v[c];
+      *reinterpret_cast<u32x4*>(lds + lds_off(id >> 3, id & 7)) = v[c];
     }
   }
 };
@@ -96,10 +105,11 @@ struct TileRC {
   static constexpr int RB = R / 8;
   static constexpr int TOTAL = RB * (BK / 8);
   static constexpr int PER = (TOTAL + NT - 1) / NT;
-  uint4 v[PER][8];
+  u32x4 v[PER][8];
 
-  __device__ __forceinline__ void load(const uint16_t* src0, const uint16_t* src1, int64_t ld, int r0,
-                                       int rows, int k0, int klen, bool vec, int tid) {
+  template <bool MASKED>
+  __device__ __forceinline__ void load(const uint16_t* src0, const uint16_t* src1, int64_t ld, int r0, int rows,
+                                       int k0, int klen, bool vec, int tid) {
 #pragma unroll
     for (int c = 0; c < PER; ++c) {
       const int id = tid + c * NT;
@@ -113,12 +123,14 @@ struct TileRC {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int gk = k0 + kb * 8 + j;
-        if (gk < klen && valid_r > 0) {
+        if constexpr (!MASKED) {
+          v[c][j] = *reinterpret_cast<const u32x4*>(src + (int64_t)gk * ld + gr);
+        } else if (gk < klen && valid_r > 0) {
           const uint16_t* ptr = src + (int64_t)gk * ld + gr;
-          if (vec && valid_r >= 8) v[c][j] = *reinterpret_cast<const uint4*>(ptr);
+          if (vec && valid_r >= 8) v[c][j] = *reinterpret_cast<const u32x4*>(ptr);
           else v[c][j] = load8_masked(ptr, valid_r);
         } else {
-          v[c][j] = make_uint4(0u, 0u, 0u, 0u);
+          v[c][j] = u32x4{0u, 0u, 0u, 0u};
         }
       }
     }
@@ -132,17 +144,16 @@ struct TileRC {
       const int kb = id / RB;
       // v[c][j] holds k = 8kb + j, rows 8rb .. 8rb+7 (two rows per dword).
       // Output row i needs k = 8kb .. 8kb+7 at row 8rb + i.
-      const uint32_t* w = reinterpret_cast<const uint32_t*>(&v[c][0]);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int q = i >> 1;
         const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-        uint4 o;
-        o.x = __builtin_amdgcn_perm(w[1 * 4 + q], w[0 * 4 + q], sel);
-        o.y = __builtin_amdgcn_perm(w[3 * 4 + q], w[2 * 4 + q], sel);
-        o.z = __builtin_amdgcn_perm(w[5 * 4 + q], w[4 * 4 + q], sel);
-        o.w = __builtin_amdgcn_perm(w[7 * 4 + q], w[6 * 4 + q], sel);
-        *reinterpret_cast<uint4*>(lds + lds_off(rb * 8 + i, kb)) = o;
+        u32x4 o;
+        o[0] = __builtin_amdgcn_perm(v[c][1][q], v[c][0][q], sel);
+        o[1] = __builtin_amdgcn_perm(v[c][3][q], v[c][2][q], sel);
+        o[2] = __builtin_amdgcn_perm(v[c][5][q], v[c][4][q], sel);
+        o[3] = __builtin_amdgcn_perm(v[c][7][q], v[c][6][q], sel);
+        *reinterpret_cast<u32x4*>(lds + lds_off(rb * 8 + i, kb)) = o;
       }
     }
   }
@@ -163,7 +174,6 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_bf16_kernel(const GemmPara
   static_assert(!DUAL || (TN % 2 == 0), "dual mode needs gate and up fragments per wave");
   constexpr int STAGE = (BM + BN) * BK * 2;  // bytes per LDS stage
   __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
-  __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -198,17 +208,6 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_bf16_kernel(const GemmPara
   Tile<BM, NT, AKC, false> ta;
   Tile<BN, NT, BKC, DUAL> tb;
 
-  auto load_tiles = [&](int kt) {
-    const bool s1 = kt >= nk0;
-    const int k0 = (s1 ? kt - nk0 : kt) * BK;
-    const int klen = s1 ? p.K1 : p.K0;
-    const uint16_t* a = reinterpret_cast<const uint16_t*>(s1 ? p.A1 : p.A0);
-    const uint16_t* b0 = reinterpret_cast<const uint16_t*>(s1 ? p.B1 : p.B0);
-    const uint16_t* b1 = reinterpret_cast<const uint16_t*>(p.B1);
-    ta.load(a, a, p.lda, m0, p.M, k0, klen, p.vecA, tid);
-    tb.load(b0, b1, p.ldb, n0, p.N, k0, klen, p.vecB, tid);
-  };
-
   f32x16 acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -227,98 +226,67 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_bf16_kernel(const GemmPara
     }
   };
 
-  if (kt_begin < kt_end) {
-    load_tiles(kt_begin);
-    ta.store(smem, tid);
-    tb.store(smem + BM * BK * 2, tid);
-  }
-  __syncthreads();
-
-  for (int kt = kt_begin; kt < kt_end; ++kt) {
-    const int cur = (kt - kt_begin) & 1;
-    const bool more = kt + 1 < kt_end;
-    if (more) load_tiles(kt + 1);
-    const char* la = smem + cur * STAGE;
-    const char* lb = la + BM * BK * 2;
+  // The K loop, compiled twice: without any masking for tiles that lie
+  // entirely inside the operands (the common case), and with edge masking.
+  auto kloop = [&](auto masked_tag) {
+    constexpr bool MK = decltype(masked_tag)::value;
+    auto load_tiles = [&](int kt) {
+      const bool s1 = kt >= nk0;
+      const int k0 = (s1 ? kt - nk0 : kt) * BK;
+      const int klen = s1 ? p.K1 : p.K0;
+      const uint16_t* a = reinterpret_cast<const uint16_t*>(s1 ? p.A1 : p.A0);
+      const uint16_t* b0 = reinterpret_cast<const uint16_t*>(s1 ? p.B1 : p.B0);
+      const uint16_t* b1 = reinterpret_cast<const uint16_t*>(p.B1);
+      ta.template load<MK>(a, a, p.lda, m0, p.M, k0, klen, p.vecA, tid);
+      tb.template load<MK>(b0, b1, p.ldb, n0, p.N, k0, klen, p.vecB, tid);
+    };
+    if (kt_begin < kt_end) {
+      load_tiles(kt_begin);
+      ta.store(smem, tid);
+      tb.store(smem + BM * BK * 2, tid);
+    }
+    __syncthreads();
+    for (int kt = kt_begin; kt < kt_end; ++kt) {
+      const int cur = (kt - kt_begin) & 1;
+      const bool more = kt + 1 < kt_end;
+      if (more) load_tiles(kt + 1);
+      const char* la = smem + cur * STAGE;
+      const char* lb = la + BM * BK * 2;
 #pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      const int chunk = 2 * s + (lane >> 5);
-      bf16x8 af[TM];
-      bf16x8 bfr[TN];
+      for (int s = 0; s < BK / 16; ++s) {
+        const int chunk = 2 * s + (lane >> 5);
+        bf16x8 af[TM];
+        bf16x8 bfr[TN];
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(la + lds_off(wm * WM + i * 32 + (lane & 31), chunk));
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(lb + lds_off(brow(j) + (lane & 31), chunk));
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
+        for (int i = 0; i < TM; ++i)
+          af[i] = *reinterpret_cast<const bf16x8*>(la + lds_off(wm * WM + i * 32 + (lane & 31), chunk));
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (more) {
-      char* nxt = smem + (cur ^ 1) * STAGE;
-      ta.store(nxt, tid);
-      tb.store(nxt + BM * BK * 2, tid);
-    }
-    __syncthreads();
-  }
-
-  // ---- split-K: publish, and let the last arriving split finish ----------
-  // Partials are written and read with relaxed agent-scope atomics, which are
-  // coherent across the XCDs' separate L2s without flushing them; a
-  // vmcnt(0) wait orders the stores before the arrival ticket, and the reads
-  // happen only after the ticket says every split has arrived.
-  if (p.splitk > 1) {
-    constexpr int NE = TM * TN * 16;  // floats per lane
-    float* mine = p.partials + ((int64_t)t * p.splitk + split) * NE * NT;
+          bfr[j] = *reinterpret_cast<const bf16x8*>(lb + lds_off(brow(j) + (lane & 31), chunk));
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          __hip_atomic_store(&mine[((i * TN + j) * 16 + r) * NT + tid], acc[i][j][r], __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this lane's stores are complete
-    __syncthreads();
-    if (tid == 0) {
-      const int prev = __hip_atomic_fetch_add(&p.counters[t], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_last = (prev == p.splitk - 1);
-    }
-    __syncthreads();
-    if (!s_last) return;
-    const float* all = p.partials + (int64_t)t * p.splitk * NE * NT;
-    // Sum the splits in ascending order; each split's values for one row of
-    // accumulator tiles are loaded together so the loads overlap.
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      f32x16 tot[TN];
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) tot[j][r] = 0.0f;
-      for (int s = 0; s < p.splitk; ++s) {
-        if (s == split) {
-#pragma unroll
-          for (int j = 0; j < TN; ++j) tot[j] += acc[i][j];
-        } else {
-          f32x16 v[TN];
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
           for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              v[j][r] = __hip_atomic_load(&all[((int64_t)s * NE + (i * TN + j) * 16 + r) * NT + tid], __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-          for (int j = 0; j < TN; ++j) tot[j] += v[j];
-        }
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
       }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = tot[j];
+      if (more) {
+        char* nxt = smem + (cur ^ 1) * STAGE;
+        ta.store(nxt, tid);
+        tb.store(nxt + BM * BK * 2, tid);
+      }
+      __syncthreads();
     }
-    if (tid == 0) __hip_atomic_store(&p.counters[t], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  const bool interior = p.vecA && p.vecB && m0 + BM <= p.M && n0 + BNH <= p.N && p.K0 % BK == 0 && p.K1 % BK == 0;
+  if (interior) kloop(std::false_type{});
+  else kloop(std::true_type{});
+
+  // ---- split-K (only the small-M tile splits K) ----------------------------
+  // Each wave's accumulators are one exchange tile; see splitk_exchange.
+  if constexpr (BM <= 64) {
+    if (p.splitk > 1) {
+      if (!splitk_exchange<TM * TN>(p, t * (NT / 64) + wave, split, lane, &acc[0][0])) return;
+    }
   }
 
   // ---- epilogue -----------------------------------------------------------
@@ -434,13 +402,12 @@ void gemm_split_sizes(const GemmPlan& plan, int M, int N, bool dual, size_t* par
     *n_tiles = tiles;
     return;
   }
-  int bm = 64, bn = 128;
-  if (plan.tile == TILE_256x256) { bm = 256; bn = 256; }
-  if (plan.tile == TILE_128x128) { bm = 128; bn = 128; }
+  // only the 64x128 tile (4 waves) splits K; one exchange tile per wave
+  const int bm = 64, bn = 128, waves = 4;
   const int bnh = dual ? bn / 2 : bn;
   const size_t tiles = (size_t)((M + bm - 1) / bm) * ((N + bnh - 1) / bnh);
   *part_bytes = tiles * plan.splitk * (size_t)bm * bn * sizeof(float);
-  *n_tiles = tiles;
+  *n_tiles = tiles * waves;
 }
 
 hipError_t gemm_bf16(const GemmParams& p, const GemmPlan& plan, GemmKind kind, bool out_f32, hipStream_t s) {

@@ -105,6 +105,61 @@ __device__ __forceinline__ f32x4v splitk_load(__amdgpu_buffer_rsrc_t r, uint32_t
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CPOL_SC1);
 }
 
+// Split-K exchange for one wave's tile of NACC accumulators (tile t of the
+// launch, split `split`): publish this split's partial, take an arrival
+// ticket, and if this was the last split to arrive, replace acc by the sum of
+// all splits in split order and re-zero the ticket.  Returns false for the
+// splits that are not last (they have nothing left to do).  Layout per tile:
+// [split][acc][quarter][lane][4 floats], so every store and load is 1 KB
+// contiguous per wave.
+template <int NACC>
+__device__ __forceinline__ bool splitk_exchange(const GemmParams& p, int t, int split, int lane, f32x16* acc) {
+  constexpr uint32_t SPLIT_BYTES = NACC * 16 * 64 * 4;
+  const float* base = p.partials + (int64_t)t * p.splitk * NACC * 16 * 64;
+  const __amdgpu_buffer_rsrc_t r = splitk_rsrc(base, SPLIT_BYTES * (uint32_t)p.splitk);
+#pragma unroll
+  for (int a = 0; a < NACC; ++a)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4v v = {acc[a][4 * q], acc[a][4 * q + 1], acc[a][4 * q + 2], acc[a][4 * q + 3]};
+      splitk_store(r, split * SPLIT_BYTES + ((a * 4 + q) * 64 + lane) * 16, v);
+    }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this lane's partial stores are complete
+  __builtin_amdgcn_wave_barrier();
+  int prev = 0;
+  if (lane == 0) prev = __hip_atomic_fetch_add(&p.counters[t], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  prev = __shfl(prev, 0);
+  if (prev != p.splitk - 1) return false;
+  // Every split has arrived: for each accumulator, load all splits' values
+  // (8 at a time, issued together) and add them in split order.
+  constexpr int SB = 8;
+#pragma unroll
+  for (int a = 0; a < NACC; ++a) {
+    f32x16 sum;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sum[e] = 0.0f;
+    for (int s0 = 0; s0 < p.splitk; s0 += SB) {
+      f32x4v v[SB][4];
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[sb][q] = splitk_load(r, (s0 + sb) * SPLIT_BYTES + ((a * 4 + q) * 64 + lane) * 16);
+#pragma unroll
+      for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          sum[4 * q] += v[sb][q][0];
+          sum[4 * q + 1] += v[sb][q][1];
+          sum[4 * q + 2] += v[sb][q][2];
+          sum[4 * q + 3] += v[sb][q][3];
+        }
+    }
+    acc[a] = sum;
+  }
+  if (lane == 0) __hip_atomic_store(&p.counters[t], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+
 // Element stores / loads of the output and side tensors.
 template <typename T>
 __device__ __forceinline__ void st(void* base, int64_t ld, int m, int n, float v);
