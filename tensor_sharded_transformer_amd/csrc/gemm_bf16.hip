@@ -240,41 +240,53 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_bf16_kernel(const GemmPara
       ta.template load<MK>(a, a, p.lda, m0, p.M, k0, klen, p.vecA, tid);
       tb.template load<MK>(b0, b1, p.ldb, n0, p.N, k0, klen, p.vecB, tid);
     };
+    // MFMA operands are double-buffered in registers: the LDS reads of
+    // substep s+1 are issued before the MFMAs of substep s, and the next K
+    // tile (fetched from global memory at the top of the step) is written to
+    // the other LDS stage halfway through the step.
+    bf16x8 af[2][TM];
+    bf16x8 bfr[2][TN];
+    auto read_frags = [&](const char* la, int s, int buf) {
+      const char* lb = la + BM * BK * 2;
+      const int chunk = 2 * s + (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        af[buf][i] = *reinterpret_cast<const bf16x8*>(la + lds_off(wm * WM + i * 32 + (lane & 31), chunk));
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        bfr[buf][j] = *reinterpret_cast<const bf16x8*>(lb + lds_off(brow(j) + (lane & 31), chunk));
+    };
+    auto mma = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][i], bfr[buf][j], acc[i][j], 0, 0, 0);
+    };
     if (kt_begin < kt_end) {
       load_tiles(kt_begin);
       ta.store(smem, tid);
       tb.store(smem + BM * BK * 2, tid);
     }
     __syncthreads();
+    if (kt_begin < kt_end) read_frags(smem, 0, 0);
     for (int kt = kt_begin; kt < kt_end; ++kt) {
       const int cur = (kt - kt_begin) & 1;
       const bool more = kt + 1 < kt_end;
-      if (more) load_tiles(kt + 1);
       const char* la = smem + cur * STAGE;
-      const char* lb = la + BM * BK * 2;
+      char* nxt = smem + (cur ^ 1) * STAGE;
+      if (more) load_tiles(kt + 1);
 #pragma unroll
       for (int s = 0; s < BK / 16; ++s) {
-        const int chunk = 2 * s + (lane >> 5);
-        bf16x8 af[TM];
-        bf16x8 bfr[TN];
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-          af[i] = *reinterpret_cast<const bf16x8*>(la + lds_off(wm * WM + i * 32 + (lane & 31), chunk));
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          bfr[j] = *reinterpret_cast<const bf16x8*>(lb + lds_off(brow(j) + (lane & 31), chunk));
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-      }
-      if (more) {
-        char* nxt = smem + (cur ^ 1) * STAGE;
-        ta.store(nxt, tid);
-        tb.store(nxt + BM * BK * 2, tid);
+        if (s + 1 < BK / 16) read_frags(la, s + 1, (s + 1) & 1);
+        mma(s & 1);
+        if (s == 1 && more) {
+          ta.store(nxt, tid);
+          tb.store(nxt + BM * BK * 2, tid);
+        }
       }
       __syncthreads();
+      if (more) read_frags(nxt, 0, 0);
     }
   };
   const bool interior = p.vecA && p.vecB && m0 + BM <= p.M && n0 + BNH <= p.N && p.K0 % BK == 0 && p.K1 % BK == 0;
