@@ -17,7 +17,11 @@ The same JSON line carries:
                 d=4096, ff_i=1792) and the fp32 sum of partials;
   cpu_baseline  the fp64 oracle computing the same decode step on the host.
 
-    python bench.py [--steps K] [--warmup W] [--rows all|none|prefill,gqa,bwd,sum]
+    python bench.py [--steps K] [--warmup W] [--rows all|none|prefill,gqa,bwd,sum,calib]
+
+--rows calib adds a plain device-to-device copy of 117,440,512 bytes (five
+launches), the known-size kernel that scales the FETCH_SIZE / WRITE_SIZE
+counters of the same profiling run.
 """
 from __future__ import annotations
 
@@ -33,6 +37,13 @@ sys.path.insert(0, ROOT)
 METRIC = "per-rank sharded MLP TFLOP/s (prefill) & GB/s (decode), % of MFMA/HBM peak"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+
+
+# HBM bytes per launch of the fused gate/up decode kernel from rocprofv3 PMC
+# (FETCH_SIZE + WRITE_SIZE, each scaled by what the same counter reads for a
+# plain copy of known size: run with --rows calib); None once the kernel has
+# changed since the counters were taken.
+TRAFFIC_GATE_UP = 148_796_376
 
 
 def log(*a):
@@ -134,16 +145,23 @@ def main() -> int:
     k_bytes = (2 * d * ff_i + T * d + T * ff_i) * 2
     k_gbs = k_bytes / (k_ms * 1e-3) / 1e9
     roofline = {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": "gemm_bf16_kernel<64,128,...,dual,EPI_SWIGLU> (fused gate/up GEMM + SwiGLU)",
+                "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": TRAFFIC_GATE_UP,
+                "kernel": "gemm_stream_kernel (dual, SwiGLU epilogue): fused gate/up weight-streaming GEMM",
                 "algorithmic_bytes": k_bytes, "avg_launch_us": round(k_ms * 1e3, 2)}
     log(f"bench: gate/up GEMM {k_ms * 1e3:.1f} us -> {k_gbs:.0f} GB/s")
-    down_ms = None
 
     rows = {}
     want = set(["prefill", "gqa", "bwd", "sum"]) if args.rows == "all" else (
         set() if args.rows == "none" else set(args.rows.split(",")))
     steps_r = max(10, args.steps // 2)
+
+    if "calib" in want:
+        src = torch.ones(8192, 7168, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        t_ = time_gpu(lambda i: dst.copy_(src), 5, 0)
+        rows["calib_copy_117440512B"] = {"us": round(t_ * 1e3, 2),
+                                         "GB/s_rd+wr": round(2 * src.numel() * 2 / t_ / 1e6, 1)}
+        del src, dst
 
     if "sum" in want:
         parts = [torch.randn(T, d, device=dev).to(torch.bfloat16) for _ in range(8)]
@@ -245,7 +263,7 @@ def main() -> int:
         w64 = {k: O.to64(v) for k, v in wt.items()}
         x64 = O.to64(W.mlp_input(wl))
         reps, t_cpu = 0, 0.0
-        while t_cpu < args.cpu_seconds and reps < 50:
+        while t_cpu < args.cpu_seconds and reps < 100000:
             c0 = time.perf_counter()
             O.mlp_shard_fwd(x64, w64["w1"], w64["w_up"], w64["w2"], "swiglu")
             t_cpu += time.perf_counter() - c0
