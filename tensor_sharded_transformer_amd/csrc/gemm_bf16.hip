@@ -424,6 +424,7 @@ void gemm_split_sizes(const GemmPlan& plan, int M, int N, bool dual, size_t* par
 
 hipError_t gemm_bf16(const GemmParams& p, const GemmPlan& plan, GemmKind kind, bool out_f32, hipStream_t s) {
   if (plan.kernel == KERNEL_STREAM) return gemm_stream(p, plan, kind, out_f32, s);
+  if (TP_TILE_PIPE && gemm_tile_supported(p, plan, kind)) return gemm_tile(p, plan, kind, out_f32, s);
   switch (kind) {
     case GK_FWD_STORE:
       return out_f32 ? launch_shape<true, false, false, EPI_STORE, float>(p, plan, s)

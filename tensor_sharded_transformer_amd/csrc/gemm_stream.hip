@@ -121,16 +121,6 @@ __device__ __forceinline__ bf16x8 read_b_frag(const char* tile, int lane) {
 
 }  // namespace
 
-// Calls f(integral_constant<int, I>) for I = 0 .. N-1, so array indices in
-// f are compile-time constants (keeps the prefetch ring in registers).
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<I + 1, N>(f);
-  }
-}
-
 // K range of split `split` in whole 16-value steps.
 __device__ __forceinline__ void split_range(int K, int splitk, int split, int* s_begin, int* s_end) {
   const int nsteps = (K + 15) / 16;

@@ -1,0 +1,424 @@
+// bf16 MFMA GEMM for gfx950 (CDNA4) with a deep global-load pipeline: the
+// prefill-sized column-parallel and row-parallel matmuls of one
+// tensor-parallel rank and the shard backward's GEMMs.
+//
+// What is computed (see "Tensor Parallelism" notes, first paragraph, and
+// "How does tensor parallelism split a transformer feed-forward block's two
+// matmuls across devices?", "Column split, then row split"):
+//   C[m, n] = epilogue( sum_k A(m, k) B(k, n) )   with fp32 accumulation.
+//
+// Design (one workgroup of 4 waves = one BM x BN output tile):
+//  * v_mfma_f32_32x32x16_bf16; each wave owns a (BM/2) x (BN/2) block of
+//    32x32 accumulator tiles.
+//  * K advances in tiles of 64.  The 16-byte buffer loads of tile kt+RS land
+//    in a ring of RS register slots while tile kt feeds the MFMAs; tile kt+1
+//    moves from its register slot to the other half of a double-buffered LDS
+//    tile halfway through step kt.  Loads therefore have about RS steps of
+//    MFMA work to arrive, and the compiler sees every load and wait.
+//  * Operands keep their memory layout in LDS.  A k-contiguous operand is a
+//    [rows][64] tile (128 B rows) read as MFMA fragments with ds_read_b128; an
+//    m- or n-contiguous operand (the (in, out) weights, the transposed
+//    operands of the weight gradients) is a [64][cols] tile in sub-tiles of at
+//    most 128 columns, read with ds_read_b64_tr_b16, which transposes 16-bit
+//    elements on the way out of LDS.  Both layouts XOR-swizzle 16-byte chunks
+//    so the fragment reads are free of bank conflicts; the swizzle is applied
+//    on the global side of the load (each lane fetches the chunk that belongs
+//    at its fixed LDS slot, and the LDS writes are linear).
+//  * Edges: each lane's buffer offset is replaced by an out-of-range value
+//    when its 16-byte chunk lies outside the matrix, and the buffer unit then
+//    returns zeros.  No separate masked loop.
+//  * Workgroup ids are renumbered so each XCD works on a contiguous, M-grouped
+//    range of tiles and shares operand panels in its own L2.
+#include <type_traits>
+
+#include "tp_kernels.h"
+#include "tp_device.h"
+
+namespace tpk {
+namespace {
+
+constexpr int TBK = 64;                 // k per LDS stage
+constexpr int NSUB = TBK / 16;          // MFMA k-substeps per stage
+constexpr uint32_t OOB = 0x80000000u;   // buffer offset past the record bound
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_at(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFFF, 0x00020000);
+}
+
+// Chunk swizzle of a k-contiguous [rows][64] tile (eight 16-byte chunks per
+// row): conflict-free ds_read_b128 of 32 consecutive rows, one chunk each,
+// and conflict-free 16-byte writes of whole rows.
+__device__ __forceinline__ int kc_swz(int row) { return (row ^ (row >> 3)) & 7; }
+// Chunk swizzle of a [64][SW] sub-tile (SW = 128: 16 chunks per row,
+// SW = 64: 8): conflict-free ds_read_b64_tr_b16 of four k-rows x 32 columns.
+template <int SW>
+__device__ __forceinline__ int mn_swz(int krow) {
+  if constexpr (SW == 128) return ((krow & 1) * 10) ^ ((krow & 2) * 2);
+  else return 2 * (krow & 3);
+}
+
+// Scheduling recipe for one block: NM MFMAs, each followed by its share of
+// NR LDS reads, NW LDS writes and NV global loads, so the wave issues memory
+// instructions while the matrix core works instead of in bursts between MFMAs.
+template <int NM, int NR, int NW, int NV>
+__device__ __forceinline__ void interleave() {
+  static_for<0, NM>([&](auto ic) __attribute__((always_inline)) {
+    constexpr int i = decltype(ic)::value;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    constexpr int r = (i + 1) * NR / NM - i * NR / NM;
+    constexpr int w = (i + 1) * NW / NM - i * NW / NM;
+    constexpr int v = (i + 1) * NV / NM - i * NV / NM;
+    if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);  // DS read
+    if constexpr (w > 0) __builtin_amdgcn_sched_group_barrier(0x200, w, 0);  // DS write
+    if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x020, v, 0);  // VMEM read
+  });
+}
+
+// One operand's tile of R rows (k-contiguous) or R columns (m/n-contiguous)
+// by 64 k-values.  Each of the 256 threads issues R/32 16-byte loads per
+// stage; load c of thread tid fills LDS slot c*256 + tid.  Every wave-wide
+// load lies inside one source matrix, so its buffer descriptor is uniform.
+template <int R, bool KC, bool DUAL>
+struct OpTile {
+  static constexpr int NL = R / 32;                          // loads per thread per stage
+  static constexpr int BYTES = R * TBK * 2;                  // LDS bytes per stage
+  static constexpr int SW = KC ? 0 : (DUAL ? (R / 2 < 128 ? R / 2 : 128) : (R < 128 ? R : 128));
+  static_assert(KC || SW == 64 || SW == 128, "sub-tile width");
+  static_assert(R % 64 == 0, "tile extent");
+  static constexpr int SUB_SLOTS = KC ? 0 : TBK * SW / 8;    // 16-byte slots per sub-tile
+
+  uint32_t voff[NL];  // byte offset from the (source, k-tile) base
+  int kidx[NL];       // k position checked against the k-tile's valid length (INT_MAX: masked)
+
+  // Which source matrix (0 / 1) load c reads: the second half of a dual tile.
+  static constexpr int src_of(int c) {
+    if constexpr (!DUAL) return 0;
+    else if constexpr (KC) return c * 256 >= 4 * R ? 1 : 0;
+    else return ((c * 256) / SUB_SLOTS) >= (R / SW) / 2 ? 1 : 0;
+  }
+
+  // r0: first row (KC) or column (MN) of the tile in each source;
+  // extent: rows (KC) or columns (MN) of each source; ld in elements.
+  __device__ __forceinline__ void setup(int tid, int r0, int extent, int64_t ld) {
+#pragma unroll
+    for (int c = 0; c < NL; ++c) {
+      const int slot = c * 256 + tid;
+      if constexpr (KC) {
+        int row = slot >> 3;
+        if (DUAL && row >= R / 2) row -= R / 2;
+        const int chunk = (slot & 7) ^ kc_swz(slot >> 3);
+        voff[c] = (uint32_t)(row * ld * 2 + chunk * 16);
+        kidx[c] = r0 + row < extent ? chunk * 8 : INT_MAX;
+      } else {
+        const int st = slot / SUB_SLOTS;                // sub-tile
+        const int within = slot % SUB_SLOTS;
+        const int krow = within / (SW / 8);
+        const int chunk = (within % (SW / 8)) ^ mn_swz<SW>(krow);
+        const int col = (DUAL ? st % ((R / SW) / 2) : st) * SW + chunk * 8;
+        voff[c] = (uint32_t)(krow * ld * 2 + col * 2);
+        kidx[c] = r0 + col < extent ? krow : INT_MAX;
+      }
+    }
+  }
+
+  // Load one k-tile into registers.  base0/base1: the sources at (tile
+  // origin, k-tile start); kvalid: k-values of the k-tile inside the matrix.
+  __device__ __forceinline__ void load(u32x4* regs, const void* base0, const void* base1, int kvalid) const {
+    const __amdgpu_buffer_rsrc_t r0 = rsrc_at(base0);
+    const __amdgpu_buffer_rsrc_t r1 = rsrc_at(base1);
+#pragma unroll
+    for (int c = 0; c < NL; ++c) {
+      const uint32_t off = kidx[c] < kvalid ? voff[c] : OOB;
+      regs[c] = __builtin_amdgcn_raw_buffer_load_b128(src_of(c) ? r1 : r0, off, 0, 0);
+    }
+  }
+  __device__ __forceinline__ static void store(const u32x4* regs, char* lds, int tid) {
+#pragma unroll
+    for (int c = 0; c < NL; ++c) *reinterpret_cast<u32x4*>(lds + (c * 256 + tid) * 16) = regs[c];
+  }
+};
+
+// Lane-constant part of the LDS byte offset of an MFMA fragment whose 32
+// rows (KC) or columns (MN) start at `first` inside the operand tile.
+// KC: o0 = row start, o1 = the lane's chunk for substep 0 (substep s reads
+// chunk o1 ^ 2s).  MN: o0 = the offset for substep 0.
+template <int R, bool KC, bool DUAL>
+__device__ __forceinline__ void frag_offsets(int first, int lane, int* o0, int* o1) {
+  if constexpr (KC) {
+    const int row = first + (lane & 31);
+    *o0 = row * (TBK * 2);
+    *o1 = (lane >> 5) ^ kc_swz(row);
+  } else {
+    constexpr int SW = OpTile<R, KC, DUAL>::SW;
+    const int g = lane >> 4, i = lane & 15;
+    const int col = first + (g & 1) * 16 + 4 * (i & 3);
+    const int st = col / SW, cc = col % SW;
+    const int krow = (g >> 1) * 8 + (i >> 2);        // plus 16*substep + 4*read
+    *o0 = st * (TBK * SW * 2) + krow * (SW * 2) + (((cc >> 3) ^ mn_swz<SW>(krow)) << 4) + (cc & 7) * 2;
+    *o1 = *o0;
+  }
+}
+
+template <int R, bool KC, bool DUAL>
+__device__ __forceinline__ bf16x8 read_frag(const char* tile, int o0, int o1, int s) {
+  if constexpr (KC) {
+    return *reinterpret_cast<const bf16x8*>(tile + o0 + ((o1 ^ (2 * s)) << 4));
+  } else {
+    constexpr int SW = OpTile<R, KC, DUAL>::SW;
+    const char* p = tile + o0 + s * 16 * (SW * 2);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * SW * 2));
+    const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v);
+  }
+}
+
+template <int BM, int BN, int RS, bool AKC, bool BKC, bool DUAL, int EPI, typename OutT>
+__global__ __launch_bounds__(256) void gemm_tile_kernel(const GemmParams p) {
+  constexpr int WM = BM / 2, WN = BN / 2;
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr int BNH = DUAL ? BN / 2 : BN;  // output columns per tile
+  static_assert(!DUAL || (TN % 2 == 0), "dual mode needs gate and up fragments per wave");
+  using TA = OpTile<BM, AKC, false>;
+  using TB = OpTile<BN, BKC, DUAL>;
+  constexpr int STAGE = TA::BYTES + TB::BYTES;
+  static_assert(RS >= 1 && RS <= 4, "register ring depth");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1;
+  const int wn = wave & 1;
+
+  // ---- tile assignment (XCD-contiguous, M-grouped) -------------------------
+  const int tiles_m = (p.M + BM - 1) / BM;
+  const int tiles_n = (p.N + BNH - 1) / BNH;
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  constexpr int GROUP = 8;
+  const int per_group = GROUP * tiles_n;
+  const int g = t / per_group;
+  const int first_m = g * GROUP;
+  const int gsz = min(tiles_m - first_m, GROUP);
+  const int tin = t - g * per_group;
+  const int m0 = (first_m + tin % gsz) * BM;
+  const int n0 = (tin / gsz) * BNH;
+
+  const int nk0 = (p.K0 + TBK - 1) / TBK;
+  const int nk = nk0 + (p.K1 + TBK - 1) / TBK;
+
+  TA ta;
+  TB tb;
+  ta.setup(tid, m0, p.M, p.lda);
+  tb.setup(tid, n0, p.N, p.ldb);
+
+  // Register ring: slot r holds the A and B loads of one k-tile.
+  u32x4 ra[RS][TA::NL];
+  u32x4 rb[RS][TB::NL];
+  // Tiles past the end are issued too, fully masked (no memory access), so
+  // every step issues the same loads and the compiler's wait counts stay exact.
+  auto load = [&](int kt, u32x4* a_regs, u32x4* b_regs) {
+    const bool s1 = kt >= nk0;
+    const int k0 = (s1 ? kt - nk0 : kt) * TBK;
+    const int kvalid = kt >= nk ? 0 : (s1 ? p.K1 : p.K0) - k0;
+    const uint16_t* a = reinterpret_cast<const uint16_t*>(s1 ? p.A1 : p.A0);
+    const uint16_t* b0 = reinterpret_cast<const uint16_t*>(s1 ? p.B1 : p.B0);
+    const uint16_t* b1 = reinterpret_cast<const uint16_t*>(p.B1);
+    // tile origin + k-tile start in each source
+    const int64_t ao = kvalid <= 0 ? 0 : (AKC ? (int64_t)m0 * p.lda + k0 : (int64_t)k0 * p.lda + m0);
+    const int64_t bo = kvalid <= 0 ? 0 : (BKC ? (int64_t)n0 * p.ldb + k0 : (int64_t)k0 * p.ldb + n0);
+    ta.load(a_regs, a + ao, a + ao, kvalid);
+    tb.load(b_regs, b0 + bo, b1 + bo, kvalid);
+  };
+  auto store = [&](const u32x4* a_regs, const u32x4* b_regs, char* st) {
+    TA::store(a_regs, st, tid);
+    TB::store(b_regs, st + TA::BYTES, tid);
+  };
+
+  // Fragment offsets (lane-constant) inside a stage.
+  int ao0[TM], ao1[TM], bo0[TN], bo1[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) frag_offsets<BM, AKC, false>(wm * WM + i * 32, lane, &ao0[i], &ao1[i]);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    int first;
+    if constexpr (DUAL) {
+      constexpr int TNH = TN / 2;
+      first = (j < TNH ? 0 : BN / 2) + wn * (WN / 2) + (j % TNH) * 32;
+    } else {
+      first = wn * WN + j * 32;
+    }
+    frag_offsets<BN, BKC, DUAL>(first, lane, &bo0[j], &bo1[j]);
+  }
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  bf16x8 af[2][TM];
+  bf16x8 bf[2][TN];
+  auto read_frags = [&](const char* stage, int s, int buf) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) af[buf][i] = read_frag<BM, AKC, false>(stage, ao0[i], ao1[i], s);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) bf[buf][j] = read_frag<BN, BKC, DUAL>(stage + TA::BYTES, bo0[j], bo1[j], s);
+  };
+  auto mma = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][i], bf[buf][j], acc[i][j], 0, 0, 0);
+  };
+
+  // ---- main loop -------------------------------------------------------------
+  // A step consumes one k-tile in four blocks of 16 MFMAs (one 16-deep
+  // k-substep each).  Each block's MFMAs use fragments read during the
+  // previous block, and the LDS reads of the next substep are interleaved
+  // with them; block 2 also writes tile kt+1 from its register slot to the
+  // other LDS half, block 3 also issues the global loads of tile kt+1+RS.
+  // Block 0 runs the previous tile's last substep, so the only barrier of a
+  // step comes after all of its LDS reads.
+  //   tile t: loaded into register slot t % RS in step t-1-RS (prologue:
+  //   tiles 0 .. RS), written to LDS half t % 2 in step t-1, read in step t.
+  // Steps past the end see zero-filled tiles (their loads are fully masked),
+  // so the loop is branch-free and the wait counts stay exact.
+  static_for<0, RS>([&](auto ic) __attribute__((always_inline)) {
+    constexpr int i = decltype(ic)::value;
+    load(i, ra[i], rb[i]);
+  });
+  store(ra[0], rb[0], smem);
+  load(RS, ra[0], rb[0]);
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) af[1][i][e] = (__bf16)0.0f;
+#pragma unroll
+  for (int j = 0; j < TN; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) bf[1][j][e] = (__bf16)0.0f;
+  __syncthreads();
+  constexpr int UNROLL = RS % 2 == 0 ? RS : 2 * RS;
+  constexpr int NMF = TM * TN;                            // MFMAs per block
+  constexpr int NRD = TM * (AKC ? 1 : 2) + TN * (BKC ? 1 : 2);  // LDS reads per block
+  constexpr int NWR = TA::NL + TB::NL;                    // LDS writes / global loads per step
+  const int nk_pad = (nk + UNROLL - 1) / UNROLL * UNROLL;
+  for (int kt0 = 0; kt0 < nk_pad; kt0 += UNROLL) {
+    static_for<0, UNROLL>([&](auto uc) __attribute__((always_inline)) {
+      constexpr int u = decltype(uc)::value;
+      const int kt = kt0 + u;
+      const char* cur = smem + (u % 2) * STAGE;
+      char* nxt = smem + ((u + 1) % 2) * STAGE;
+      constexpr int slot_next = (u + 1) % RS;  // holds tile kt+1
+      read_frags(cur, 0, 0);
+      mma(1);
+      interleave<NMF, NRD, 0, 0>();
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(cur, 1, 1);
+      mma(0);
+      interleave<NMF, NRD, 0, 0>();
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(cur, 2, 0);
+      mma(1);
+      store(ra[slot_next], rb[slot_next], nxt);
+      interleave<NMF, NRD, NWR, 0>();
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags(cur, 3, 1);
+      mma(0);
+      load(kt + 1 + RS, ra[slot_next], rb[slot_next]);
+      interleave<NMF, NRD, 0, NWR>();
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+    });
+  }
+  mma(1);
+
+  // ---- epilogue --------------------------------------------------------------
+  // Accumulator register r of tile (i, j) is row 8(r/4) + 4(lane/32) + r%4,
+  // column lane%32 of that 32x32 tile.  Fully unrolled so every accumulator
+  // index is a compile-time constant.
+  const int mrow = m0 + wm * WM + 4 * (lane >> 5);
+  constexpr int TNO = DUAL ? TN / 2 : TN;  // output fragments per wave row
+  static_for<0, TM>([&](auto ic) __attribute__((always_inline)) {
+    constexpr int i = decltype(ic)::value;
+    static_for<0, TNO>([&](auto jc) __attribute__((always_inline)) {
+      constexpr int j = decltype(jc)::value;
+      const int n = n0 + wn * (DUAL ? WN / 2 : WN) + j * 32 + (lane & 31);
+      if (n < p.N) {
+        static_for<0, 16>([&](auto rc) __attribute__((always_inline)) {
+          constexpr int r = decltype(rc)::value;
+          const int m = mrow + i * 32 + 8 * (r >> 2) + (r & 3);
+          if (m < p.M) {
+            if constexpr (DUAL) epilogue_elem<EPI, OutT, uint16_t>(p, m, n, acc[i][j][r], acc[i][j + TNO][r]);
+            else epilogue_elem<EPI, OutT, uint16_t>(p, m, n, acc[i][j][r], 0.0f);
+          }
+        });
+      }
+    });
+  });
+}
+
+template <int BM, int BN, int RS, bool AKC, bool BKC, bool DUAL, int EPI, typename OutT>
+hipError_t launch_tile(const GemmParams& p, hipStream_t s) {
+  constexpr int BNH = DUAL ? BN / 2 : BN;
+  const int grid = ((p.M + BM - 1) / BM) * ((p.N + BNH - 1) / BNH);
+  hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, RS, AKC, BKC, DUAL, EPI, OutT>), dim3(grid), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+template <bool AKC, bool BKC, bool DUAL, int EPI, typename OutT>
+hipError_t launch_tile_shape(const GemmParams& p, int tile, hipStream_t s) {
+  switch (tile) {
+    case TILE_256x256: return launch_tile<256, 256, TP_TILE_RS_256, AKC, BKC, DUAL, EPI, OutT>(p, s);
+    case TILE_128x128: return launch_tile<128, 128, TP_TILE_RS_128, AKC, BKC, DUAL, EPI, OutT>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+bool aligned16(const void* q) { return q == nullptr || ((uintptr_t)q & 15) == 0; }
+
+}  // namespace
+
+// The pipelined kernel needs every 16-byte chunk it loads to be aligned
+// and either wholly inside or wholly outside the matrix.
+bool gemm_tile_supported(const GemmParams& p, const GemmPlan& plan, GemmKind kind) {
+  if (plan.kernel != KERNEL_TILED || plan.splitk != 1) return false;
+  if (plan.tile != TILE_256x256 && plan.tile != TILE_128x128) return false;
+  if (!p.vecA || !p.vecB) return false;
+  if (p.lda % 8 || p.ldb % 8 || p.K0 % 8 || p.K1 % 8) return false;
+  if (p.lda > (1 << 21) || p.ldb > (1 << 21)) return false;  // per-lane offsets stay below 2^31
+  if (!aligned16(p.A0) || !aligned16(p.A1) || !aligned16(p.B0) || !aligned16(p.B1)) return false;
+  const bool akc = !(kind == GK_BWD_DW || kind == GK_BWD_DW_DUAL);
+  const bool bkc = kind == GK_BWD_DH_SWIGLU || kind == GK_BWD_DH_ACT || kind == GK_BWD_DX;
+  if (!akc && p.M % 8) return false;
+  if (!bkc && p.N % 8) return false;
+  return true;
+}
+
+hipError_t gemm_tile(const GemmParams& p, const GemmPlan& plan, GemmKind kind, bool out_f32, hipStream_t s) {
+  const int t = plan.tile;
+  switch (kind) {
+    case GK_FWD_STORE:
+      return out_f32 ? launch_tile_shape<true, false, false, EPI_STORE, float>(p, t, s)
+                     : launch_tile_shape<true, false, false, EPI_STORE, uint16_t>(p, t, s);
+    case GK_FWD_ACT: return launch_tile_shape<true, false, false, EPI_ACT, uint16_t>(p, t, s);
+    case GK_FWD_SWIGLU: return launch_tile_shape<true, false, true, EPI_SWIGLU, uint16_t>(p, t, s);
+    case GK_BWD_DH_SWIGLU: return launch_tile_shape<true, true, false, EPI_SWIGLU_BWD, uint16_t>(p, t, s);
+    case GK_BWD_DH_ACT: return launch_tile_shape<true, true, false, EPI_ACT_BWD, uint16_t>(p, t, s);
+    case GK_BWD_DW: return launch_tile_shape<false, false, false, EPI_STORE, uint16_t>(p, t, s);
+    case GK_BWD_DW_DUAL: return launch_tile_shape<false, false, true, EPI_DUAL_STORE, uint16_t>(p, t, s);
+    case GK_BWD_DX: return launch_tile_shape<true, true, false, EPI_STORE, uint16_t>(p, t, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace tpk

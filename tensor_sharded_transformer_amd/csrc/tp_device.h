@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace tpk {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -76,6 +78,16 @@ struct GemmParams {
   float* partials;     // split-K fp32 partial tiles
   int* counters;       // split-K arrival counters (zero on entry, left zero)
 };
+
+// Calls f(integral_constant<int, I>) for I = 0 .. N-1, so array indices in
+// f are compile-time constants (keeps the prefetch ring in registers).
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
 
 // Renumber workgroups so that each XCD gets a contiguous range of ids.
 __device__ __forceinline__ int xcd_remap(int bid, int nblk) {

@@ -31,6 +31,19 @@
 #define TP_STREAM_KW 8
 #endif
 
+// Pipelined tiled kernel: k-tiles of loads in flight (register ring depth)
+// for the 256x256 and 128x128 tiles; TP_TILE_PIPE=0 keeps the older
+// two-stage kernel for those tiles.
+#ifndef TP_TILE_RS_256
+#define TP_TILE_RS_256 1
+#endif
+#ifndef TP_TILE_RS_128
+#define TP_TILE_RS_128 2
+#endif
+#ifndef TP_TILE_PIPE
+#define TP_TILE_PIPE 1
+#endif
+
 namespace tpk {
 
 constexpr int STREAM_NW = TP_STREAM_NW;
@@ -80,6 +93,9 @@ GemmPlan plan_gemm(int M, int N, int K, bool dual, bool fwd_layout, bool vec_ok,
 void gemm_split_sizes(const GemmPlan& plan, int M, int N, bool dual, size_t* part_bytes, size_t* n_tiles);
 hipError_t gemm_bf16(const GemmParams& p, const GemmPlan& plan, GemmKind kind, bool out_f32, hipStream_t s);
 hipError_t gemm_stream(const GemmParams& p, const GemmPlan& plan, GemmKind kind, bool out_f32, hipStream_t s);
+// The pipelined tiled kernel, for plans and operands it supports.
+bool gemm_tile_supported(const GemmParams& p, const GemmPlan& plan, GemmKind kind);
+hipError_t gemm_tile(const GemmParams& p, const GemmPlan& plan, GemmKind kind, bool out_f32, hipStream_t s);
 
 // fp32 (SIMT) GEMM with the same parameter block and epilogues.
 hipError_t gemm_f32(const GemmParams& p, GemmKind kind, hipStream_t s);
