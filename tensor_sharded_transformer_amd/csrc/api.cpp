@@ -55,24 +55,33 @@ GemmParams base_params() {
   return p;
 }
 
-// Workspace layout shared by the forward and backward entry points:
+// Workspace layout shared by the entry points:
 //   [ buffers ... ][ split-K counters (zero between calls) ][ split-K partials ]
+//   [ packed activations of the decode kernel ]
 struct SplitNeeds {
   size_t part_bytes = 0;
   size_t n_tiles = 0;
-  void add(const GemmPlan& plan, int M, int N, bool dual) {
-    size_t pb, nt;
-    tpk::gemm_split_sizes(plan, M, N, dual, &pb, &nt);
+  size_t pack_bytes = 0;
+  void add(const GemmPlan& plan, int M, int N, int K, bool dual) {
+    size_t pb, nt, pk;
+    tpk::gemm_split_sizes(plan, M, N, K, dual, &pb, &nt, &pk);
     if (pb > part_bytes) part_bytes = pb;
     if (nt > n_tiles) n_tiles = nt;
+    if (pk > pack_bytes) pack_bytes = pk;
   }
   size_t counter_bytes() const { return tpk::align_up(n_tiles * sizeof(int), 256); }
+  size_t partial_bytes() const { return tpk::align_up(part_bytes, 256); }
+  size_t packed_bytes() const { return tpk::align_up(pack_bytes, 256); }
 };
 
-void attach_split(GemmParams& p, const GemmPlan& plan, char* counters, char* partials) {
+// Does this plan use workspace (split-K scratch or packed activations)?
+bool needs_ws(const GemmPlan& plan) { return plan.splitk > 1 || plan.kernel == tpk::KERNEL_DECODE; }
+
+void attach_split(GemmParams& p, const GemmPlan& plan, char* counters, char* partials, char* pack) {
   p.splitk = plan.splitk;
   p.counters = plan.splitk > 1 ? reinterpret_cast<int*>(counters) : nullptr;
   p.partials = plan.splitk > 1 ? reinterpret_cast<float*>(partials) : nullptr;
+  p.apk = plan.kernel == tpk::KERNEL_DECODE ? pack : nullptr;
 }
 
 GemmPlan plan_for(int dtype, int M, int N, int K, bool dual, bool allow_split, bool fwd_layout, bool vec_ok) {
@@ -88,7 +97,8 @@ hipError_t run_gemm(int dtype, const GemmParams& p, const GemmPlan& plan, GemmKi
 // ---- forward shard layout ----------------------------------------------------
 struct FwdLayout {
   GemmPlan p1, p2;
-  size_t h_bytes = 0, cnt_off = 0, part_off = 0, total = 0;
+  size_t h_bytes = 0, cnt_off = 0, part_off = 0, pack_off = 0, pack2_off = 0, total = 0;
+  bool fuse_pack = false;  // the column GEMM writes h straight into the row GEMM's packed A
 };
 
 // vec: every operand allows 16-byte vector loads (aligned, rows multiple of 8).
@@ -97,19 +107,26 @@ FwdLayout fwd_layout(int64_t T, int64_t d, int64_t ff_i, int dtype, int act, boo
   const bool dual = act == TP_ACT_SWIGLU;
   L.p1 = plan_for(dtype, (int)T, (int)ff_i, (int)d, dual, true, true, vec);
   L.p2 = plan_for(dtype, (int)T, (int)d, (int)ff_i, false, true, true, vec);
-  SplitNeeds sn;
-  sn.add(L.p1, (int)T, (int)ff_i, dual);
-  sn.add(L.p2, (int)T, (int)d, false);
+  SplitNeeds s1, s2, sn;
+  s1.add(L.p1, (int)T, (int)ff_i, (int)d, dual);
+  s2.add(L.p2, (int)T, (int)d, (int)ff_i, false);
+  sn.add(L.p1, (int)T, (int)ff_i, (int)d, dual);
+  sn.add(L.p2, (int)T, (int)d, (int)ff_i, false);
   L.h_bytes = tpk::align_up((size_t)T * ff_i * esize(dtype), 256);
   L.cnt_off = L.h_bytes;
   L.part_off = L.cnt_off + sn.counter_bytes();
-  L.total = L.part_off + tpk::align_up(sn.part_bytes, 256);
+  L.pack_off = L.part_off + sn.partial_bytes();
+  L.pack2_off = L.pack_off + s1.packed_bytes();
+  L.total = L.pack2_off + s2.packed_bytes();
+  // h goes straight into the packed A of the row GEMM when both GEMMs use
+  // the decode kernel and h has no partial 16-wide k step (whose pad must be 0).
+  L.fuse_pack = L.p1.kernel == tpk::KERNEL_DECODE && L.p2.kernel == tpk::KERNEL_DECODE && ff_i % 16 == 0;
   return L;
 }
 
 struct BwdLayout {
   GemmPlan pa, pb, pc, pd;
-  size_t dgu_bytes = 0, h_off = 0, cnt_off = 0, part_off = 0, total = 0;
+  size_t dgu_bytes = 0, h_off = 0, cnt_off = 0, part_off = 0, pack_off = 0, total = 0;
 };
 
 BwdLayout bwd_layout(int64_t T, int64_t d, int64_t ff_i, int dtype, int act) {
@@ -120,35 +137,35 @@ BwdLayout bwd_layout(int64_t T, int64_t d, int64_t ff_i, int dtype, int act) {
   L.pc = plan_for(dtype, (int)d, (int)ff_i, (int)T, sw, true, false, false);      // dW1 (+dWup)
   L.pd = plan_for(dtype, (int)T, (int)d, (int)((sw ? 2 : 1) * ff_i), false, true, false, false);  // dx
   SplitNeeds sn;
-  sn.add(L.pa, (int)T, (int)ff_i, false);
-  sn.add(L.pb, (int)ff_i, (int)d, false);
-  sn.add(L.pc, (int)d, (int)ff_i, sw);
-  sn.add(L.pd, (int)T, (int)d, false);
+  sn.add(L.pa, (int)T, (int)ff_i, (int)d, false);
+  sn.add(L.pb, (int)ff_i, (int)d, (int)T, false);
+  sn.add(L.pc, (int)d, (int)ff_i, (int)T, sw);
+  sn.add(L.pd, (int)T, (int)d, (int)((sw ? 2 : 1) * ff_i), false);
   L.dgu_bytes = tpk::align_up((size_t)T * ff_i * (sw ? 2 : 1) * esize(dtype), 256);
   L.h_off = L.dgu_bytes;
   L.cnt_off = L.h_off + tpk::align_up((size_t)T * ff_i * esize(dtype), 256);
   L.part_off = L.cnt_off + sn.counter_bytes();
-  L.total = L.part_off + tpk::align_up(sn.part_bytes, 256);
+  L.pack_off = L.part_off + sn.partial_bytes();
+  L.total = L.pack_off + sn.packed_bytes();
   return L;
 }
 
-// Optional workspace of a single GEMM entry point: [counters][partials].
+// Optional workspace of a single GEMM entry point: [counters][partials][packed A].
 struct SingleWs {
   GemmPlan plan;
   bool dual = false;
-  size_t cnt_bytes = 0, total = 0;
-  // With no workspace the call runs unsplit (re-planned for that); a
-  // too-small workspace is an error.
+  size_t cnt_bytes = 0, part_bytes = 0, total = 0;
+  // With no workspace the call runs unsplit without packed activations
+  // (re-planned for that); a too-small workspace is an error.
   tp_status bind(GemmParams& p, void* ws, size_t ws_bytes, const char* who) {
-    if (!ws || plan.splitk <= 1) {
-      if (plan.splitk > 1) plan = tpk::plan_gemm(p.M, p.N, p.K0, dual, true,
-                                                 p.vecA && p.vecB, false);
-      attach_split(p, plan, nullptr, nullptr);
+    if (!ws || !needs_ws(plan)) {
+      if (needs_ws(plan)) plan = tpk::plan_gemm(p.M, p.N, p.K0, dual, true, p.vecA && p.vecB, false);
+      attach_split(p, plan, nullptr, nullptr, nullptr);
       return TP_OK;
     }
     if (ws_bytes < total) return fail(TP_ERR_WORKSPACE, "%s: workspace of %zu bytes < %zu needed", who, ws_bytes, total);
     char* base = reinterpret_cast<char*>(ws);
-    attach_split(p, plan, base, base + cnt_bytes);
+    attach_split(p, plan, base, base + cnt_bytes, base + cnt_bytes + part_bytes);
     return TP_OK;
   }
 };
@@ -158,10 +175,11 @@ SingleWs single_ws(int dtype, int M, int N, int K, bool dual, bool vec) {
   W.dual = dual;
   W.plan = plan_for(dtype, M, N, K, dual, true, true, vec);
   SplitNeeds sn;
-  sn.add(W.plan, M, N, dual);
-  if (W.plan.splitk > 1) {
-    W.cnt_bytes = sn.counter_bytes();
-    W.total = W.cnt_bytes + tpk::align_up(sn.part_bytes, 256);
+  sn.add(W.plan, M, N, K, dual);
+  if (needs_ws(W.plan)) {
+    W.cnt_bytes = sn.n_tiles ? sn.counter_bytes() : 0;
+    W.part_bytes = sn.partial_bytes();
+    W.total = W.cnt_bytes + W.part_bytes + sn.packed_bytes();
   }
   return W;
 }
@@ -398,7 +416,11 @@ tp_status tp_mlp_shard_fwd(const void* x, const void* w1_i, const void* w_up_i, 
   }
   p1.vecA = aligned16(x) && d % 8 == 0;
   p1.vecB = aligned16(w1_i) && (!sw || aligned16(w_up_i)) && ff_i % 8 == 0;
-  attach_split(p1, L.p1, base + L.cnt_off, base + L.part_off);
+  attach_split(p1, L.p1, base + L.cnt_off, base + L.part_off, base + L.pack_off);
+  if (L.fuse_pack) {
+    p1.cpk = base + L.pack2_off;
+    p1.cpk_mt = T <= 32 ? 1 : 2;
+  }
   hipError_t e = run_gemm(dtype, p1, L.p1, sw ? tpk::GK_FWD_SWIGLU : tpk::GK_FWD_ACT, false, s);
   if (e != hipSuccess) return hip_status(e, "tp_mlp_shard_fwd (column GEMM)");
   (void)bf;
@@ -415,7 +437,8 @@ tp_status tp_mlp_shard_fwd(const void* x, const void* w1_i, const void* w_up_i, 
   p2.ldc = d;
   p2.vecA = ff_i % 8 == 0;
   p2.vecB = aligned16(w2_i) && d % 8 == 0;
-  attach_split(p2, L.p2, base + L.cnt_off, base + L.part_off);
+  attach_split(p2, L.p2, base + L.cnt_off, base + L.part_off, base + L.pack2_off);
+  p2.apk_ready = L.fuse_pack ? 1 : 0;
   e = run_gemm(dtype, p2, L.p2, tpk::GK_FWD_STORE, out_dtype == TP_F32, s);
   return hip_status(e, "tp_mlp_shard_fwd (row GEMM)");
 }
@@ -481,7 +504,7 @@ tp_status tp_mlp_shard_bwd(const void* x, const void* w1_i, const void* w_up_i, 
   pa.act = act;
   pa.vecA = aligned16(dy) && d % 8 == 0;
   pa.vecB = aligned16(w2_i) && d % 8 == 0;
-  attach_split(pa, L.pa, cnt, part);
+  attach_split(pa, L.pa, cnt, part, base + L.pack_off);
   hipError_t e = run_gemm(dtype, pa, L.pa, sw ? tpk::GK_BWD_DH_SWIGLU : tpk::GK_BWD_DH_ACT, false, s);
   if (e != hipSuccess) return hip_status(e, "tp_mlp_shard_bwd (dh GEMM)");
 
@@ -498,7 +521,7 @@ tp_status tp_mlp_shard_bwd(const void* x, const void* w1_i, const void* w_up_i, 
   pb.ldc = d;
   pb.vecA = ff_i % 8 == 0;
   pb.vecB = aligned16(dy) && d % 8 == 0;
-  attach_split(pb, L.pb, cnt, part);
+  attach_split(pb, L.pb, cnt, part, base + L.pack_off);
   e = run_gemm(dtype, pb, L.pb, tpk::GK_BWD_DW, false, s);
   if (e != hipSuccess) return hip_status(e, "tp_mlp_shard_bwd (dW2 GEMM)");
 
@@ -518,7 +541,7 @@ tp_status tp_mlp_shard_bwd(const void* x, const void* w1_i, const void* w_up_i, 
   pc.ldc2 = ff_i;
   pc.vecA = aligned16(x) && d % 8 == 0;
   pc.vecB = ff_i % 8 == 0;
-  attach_split(pc, L.pc, cnt, part);
+  attach_split(pc, L.pc, cnt, part, base + L.pack_off);
   e = run_gemm(dtype, pc, L.pc, sw ? tpk::GK_BWD_DW_DUAL : tpk::GK_BWD_DW, false, s);
   if (e != hipSuccess) return hip_status(e, "tp_mlp_shard_bwd (dW1 GEMM)");
 
@@ -538,7 +561,7 @@ tp_status tp_mlp_shard_bwd(const void* x, const void* w1_i, const void* w_up_i, 
   pd.ldc = d;
   pd.vecA = ff_i % 8 == 0;
   pd.vecB = aligned16(w1_i) && (!sw || aligned16(w_up_i)) && ff_i % 8 == 0;
-  attach_split(pd, L.pd, cnt, part);
+  attach_split(pd, L.pd, cnt, part, base + L.pack_off);
   e = run_gemm(dtype, pd, L.pd, tpk::GK_BWD_DX, false, s);
   return hip_status(e, "tp_mlp_shard_bwd (dx GEMM)");
 }

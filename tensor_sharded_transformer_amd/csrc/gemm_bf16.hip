@@ -366,19 +366,29 @@ static hipError_t launch_shape(GemmParams p, const GemmPlan& plan, hipStream_t s
 GemmPlan plan_gemm(int M, int N, int K, bool dual, bool fwd_layout, bool vec_ok, bool allow_split) {
   GemmPlan plan;
   constexpr int CUS = 256;
-  const int ksteps = (K + 15) / 16;
-  const bool stream_fits = allow_split || stream_lds_bytes(M, ksteps, dual) <= (size_t)STREAM_LDS_MAX;
-  if (M <= STREAM_MAX_M && fwd_layout && vec_ok && N >= 8 && stream_fits) {
-    // Decode-sized forward GEMM: weight streaming.  Split K across
+  const int nsteps = (K + 15) / 16;
+  const bool decode_shape = M <= STREAM_MAX_M && fwd_layout && vec_ok && N >= 8;
+  if (decode_shape && TP_DECODE && allow_split) {
+    // Decode-sized forward GEMM with a workspace: packed-activation weight
+    // streaming.  Split K across workgroups (a power of two) until about one
+    // workgroup per CU, keeping at least 8 k-steps per wave.
+    plan.kernel = KERNEL_DECODE;
+    const int strips = (N + DECODE_WCOLS - 1) / DECODE_WCOLS;
+    int split = 1;
+    while (strips * split * 2 <= CUS && nsteps / (split * 2) >= DECODE_KW * 8) split *= 2;
+    plan.splitk = split;
+    return plan;
+  }
+  const bool stream_fits = allow_split || stream_lds_bytes(M, nsteps, dual) <= (size_t)STREAM_LDS_MAX;
+  if (decode_shape && stream_fits) {
+    // Weight streaming with the activation slice in LDS.  Split K across
     // workgroups (a power of two) until about one workgroup per CU while
     // keeping at least 16 k-steps of 16 per split, then further if the
     // split's activation slice would not fit in LDS.
     plan.kernel = KERNEL_STREAM;
     const int strips = (N + STREAM_WCOLS - 1) / STREAM_WCOLS;
-    const int nsteps = (K + 15) / 16;
     int split = 1;
-    const int min_steps = STREAM_MODE == 2 ? 8 * STREAM_KW : 16;  // per split
-    while (strips * split * 2 <= STREAM_TARGET_WGS && nsteps / (split * 2) >= min_steps) split *= 2;
+    while (strips * split * 2 <= STREAM_TARGET_WGS && nsteps / (split * 2) >= 16) split *= 2;
     while (stream_lds_bytes(M, (nsteps + split - 1) / split, dual) > (size_t)STREAM_LDS_MAX) split *= 2;
     plan.splitk = allow_split ? split : 1;
     return plan;
@@ -402,9 +412,19 @@ GemmPlan plan_gemm(int M, int N, int K, bool dual, bool fwd_layout, bool vec_ok,
   return plan;
 }
 
-void gemm_split_sizes(const GemmPlan& plan, int M, int N, bool dual, size_t* part_bytes, size_t* n_tiles) {
+void gemm_split_sizes(const GemmPlan& plan, int M, int N, int K, bool dual, size_t* part_bytes, size_t* n_tiles,
+                      size_t* pack_bytes) {
   *part_bytes = 0;
   *n_tiles = 0;
+  *pack_bytes = 0;
+  if (plan.kernel == KERNEL_DECODE) {
+    *pack_bytes = decode_pack_bytes(M, K);
+    if (plan.splitk <= 1) return;
+    const size_t tiles = decode_tiles(M, N);
+    *part_bytes = tiles * plan.splitk * (dual ? 2 : 1) * 16 * 64 * sizeof(float);
+    *n_tiles = tiles;
+    return;
+  }
   if (plan.splitk <= 1) return;
   if (plan.kernel == KERNEL_STREAM) {
     const size_t tiles = (size_t)(N + STREAM_WCOLS - 1) / STREAM_WCOLS * STREAM_TILES_PER_WG;
@@ -424,6 +444,7 @@ void gemm_split_sizes(const GemmPlan& plan, int M, int N, bool dual, size_t* par
 
 hipError_t gemm_bf16(const GemmParams& p, const GemmPlan& plan, GemmKind kind, bool out_f32, hipStream_t s) {
   if (plan.kernel == KERNEL_STREAM) return gemm_stream(p, plan, kind, out_f32, s);
+  if (plan.kernel == KERNEL_DECODE) return gemm_decode(p, plan, kind, out_f32, s);
   if (TP_TILE_PIPE && gemm_tile_supported(p, plan, kind)) return gemm_tile(p, plan, kind, out_f32, s);
   switch (kind) {
     case GK_FWD_STORE:

@@ -1,0 +1,248 @@
+// Weight-streaming bf16 GEMM for decode-sized token counts (M <= 64), with the
+// activations pre-packed in MFMA fragment order.
+//
+// At decode size one rank's matmul reads every weight byte once and does
+// only 2*M flops per weight element, so its time is the time to stream the
+// (in, out) weight shard from HBM ("Tensor Parallelism" notes, fourth
+// paragraph: a decode token costs weight bytes / HBM bandwidth).  Design:
+//
+//  * A first pass rewrites x (M x K, row-major) so that the A operand of one
+//    32x32x16 MFMA (32 rows x 16 k) is 1 KB of contiguous memory in lane
+//    order; the streaming kernel then reads each A fragment with one fully
+//    coalesced 16-byte load per lane, straight from L2 (x is small and every
+//    workgroup re-reads it), and needs no activation copy in LDS.
+//  * A workgroup owns NW*32 output columns (gate and up columns together in
+//    dual mode, NW*64 contiguous bytes of every weight row) and one K range;
+//    its KW waves stream disjoint K sub-ranges of that range, each with DEPTH
+//    k-steps of weight and activation loads in flight and no barrier.  K is
+//    split across workgroups only until there is about one workgroup per CU,
+//    which keeps the cross-workgroup partials small.
+//  * Weights are n-contiguous while the MFMA wants 8 consecutive k of one
+//    column per lane: each wave copies each 16-row slab into a private LDS
+//    tile and reads the operand back with ds_read_b64_tr_b16.
+//  * The waves' accumulators meet in LDS; each wave then owns one output
+//    fragment (gate and up together), sums it over the waves in wave order,
+//    and takes it through the split-K exchange (last-arriving workgroup adds
+//    the splits in split order), so results are bitwise reproducible.
+#include <type_traits>
+
+#include "tp_kernels.h"
+#include "tp_device.h"
+#include "stream_frag.h"
+
+namespace tpk {
+
+namespace {
+
+constexpr int KW = DECODE_KW;
+constexpr int NW = DECODE_NW;
+constexpr int DEPTH = TP_DECODE_DEPTH;
+
+// Packed A: fragment (step s, m-tile i) is 64 lanes x 16 bytes at
+// ((s * MT + i) * 64 + lane) * 16; lane l holds row 32i + l%32, k values
+// 16s + 8(l/32) .. +7.  Rows >= M and k >= K are zero.
+template <int MT>
+__global__ __launch_bounds__(256) void pack_a_kernel(const uint16_t* __restrict__ x, int64_t lda, int M, int K,
+                                                     int nsteps, u32x4* __restrict__ out) {
+  const int gid = blockIdx.x * 256 + threadIdx.x;
+  if (gid >= nsteps * MT * 64) return;
+  const int lane = gid & 63;
+  const int f = gid >> 6;
+  const int i = f % MT;
+  const int s = f / MT;
+  const int m = i * 32 + (lane & 31);
+  const int k = s * 16 + (lane >> 5) * 8;
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (m < M && k < K) v = *reinterpret_cast<const u32x4*>(x + (int64_t)m * lda + k);
+  out[gid] = v;
+}
+
+template <int MT, bool DUAL>
+constexpr int decode_lds_bytes() {
+  constexpr int NF = DUAL ? 2 * NW : NW;
+  return KW * NF * tile_bytes<NW>() + KW * MT * NF * 16 * 64 * 4;
+}
+
+template <int MT, bool DUAL, int EPI, typename OutT>
+__global__ __launch_bounds__(KW * 64) void gemm_decode_kernel(const GemmParams p) {
+  constexpr int NF = DUAL ? 2 * NW : NW;  // fragments per wave (gate then up)
+  constexpr int NACC = MT * NF;
+  constexpr int GCOLS = NW * 32;
+  constexpr int TB = tile_bytes<NW>();
+  constexpr int UNITS = MT * NW;           // output fragments of the workgroup
+  __shared__ __attribute__((aligned(16))) char smem[decode_lds_bytes<MT, DUAL>()];
+  char* wt = smem;                                             // [KW][NF][TB] weight tiles
+  float* red = reinterpret_cast<float*>(smem + KW * NF * TB);  // [KW][NACC][16][64]
+
+  // Every parameter the kernel reads, loaded in one batch up front: each
+  // dependent round trip to the argument buffer costs about a microsecond.
+  __asm__ volatile("" ::"s"(p.B0), "s"(p.B1), "s"(p.apk), "s"(p.ldb), "s"(p.N), "s"(p.K0), "s"(p.M),
+                   "s"(p.splitk), "s"(p.partials), "s"(p.counters), "s"(p.C), "s"(p.ldc), "s"(p.cpk),
+                   "s"(p.cpk_mt));
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nstrips = (p.N + GCOLS - 1) / GCOLS;
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int split = id / nstrips;
+  const int strip = id - split * nstrips;
+  const int n0 = strip * GCOLS;
+
+  int s_begin, s_end;
+  split_range(p.K0, p.splitk, split, &s_begin, &s_end);
+  const int w_begin = s_begin + (s_end - s_begin) * wave / KW;
+  const int w_end = s_begin + (s_end - s_begin) * (wave + 1) / KW;
+  const int full_end = min(w_end, p.K0 / 16);  // steps whose weight rows all lie inside K
+
+  f32x16 acc[MT][NF];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NF; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const u32x4* apk = reinterpret_cast<const u32x4*>(p.apk);
+  auto load_a = [&](u32x4 (&a)[MT], int step) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i) a[i] = apk[(step * MT + i) * 64 + lane];
+  };
+  char* my = wt + wave * NF * TB;
+  auto mma = [&](const WFrag<NF>& f, const u32x4 (&a)[MT]) {
+#pragma unroll
+    for (int mat = 0; mat < (DUAL ? 2 : 1); ++mat)
+#pragma unroll
+      for (int u = 0; u < NW; ++u) *reinterpret_cast<u32x4*>(my + w_lds_off<NW>(mat, u, lane)) = f.b[mat * NW + u];
+    bf16x8 bv[NF];
+#pragma unroll
+    for (int j = 0; j < NF; ++j) bv[j] = read_b_frag(my + j * TB, lane);
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const bf16x8 av = __builtin_bit_cast(bf16x8, a[i]);
+#pragma unroll
+      for (int j = 0; j < NF; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // Each wave walks its steps from a rotated start, so the workgroups of a
+  // launch do not all read the same weight rows at the same time (with
+  // power-of-two row strides that lockstep concentrates on few DRAM banks).
+  const int nw = full_end - w_begin;
+  if (nw > 0) {
+    const int rot = (strip * 7 + wave * 3) % nw;
+    auto phys = [&](int it) {
+      const int q = min(it, nw - 1) + rot;
+      return w_begin + (q >= nw ? q - nw : q);
+    };
+    WFrag<NF> fr[DEPTH];
+    u32x4 fa[DEPTH][MT];
+    static_for<0, DEPTH>([&](auto d) {
+      const int st = phys(d);
+      load_w<NW, DUAL, false>(fr[d], p, st, n0, lane);
+      load_a(fa[d], st);
+    });
+    for (int it = 0; it < nw; it += DEPTH) {
+      static_for<0, DEPTH>([&](auto d) {
+        if (it + (int)d < nw) mma(fr[d], fa[d]);
+        const int st = phys(it + DEPTH + (int)d);
+        load_w<NW, DUAL, false>(fr[d], p, st, n0, lane);
+        load_a(fa[d], st);
+      });
+    }
+  }
+  if (w_end > full_end && w_end > w_begin) {  // the partial last k-step of K (packed A is zero past K)
+    WFrag<NF> ft;
+    u32x4 at[MT];
+    load_w<NW, DUAL, true>(ft, p, w_end - 1, n0, lane);
+    load_a(at, w_end - 1);
+    mma(ft, at);
+  }
+
+  // ---- the waves meet in LDS; wave u owns output fragment u ----------------------
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < NF; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red[(((wave * NACC) + i * NF + j) * 16 + r) * 64 + lane] = acc[i][j][r];
+  __syncthreads();
+  if (wave >= UNITS) return;
+  const int ui = wave / NW;  // m-tile
+  const int uj = wave % NW;  // column fragment
+  constexpr int NOUT = DUAL ? 2 : 1;
+  f32x16 out[NOUT];
+#pragma unroll
+  for (int o = 0; o < NOUT; ++o) {
+    const int a = ui * NF + uj + o * NW;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) out[o][r] = 0.0f;
+#pragma unroll
+    for (int w = 0; w < KW; ++w)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) out[o][r] += red[(((w * NACC) + a) * 16 + r) * 64 + lane];
+  }
+
+  // ---- split-K across workgroups: each output fragment is its own tile -----
+  if (p.splitk > 1) {
+    if (!splitk_exchange<NOUT>(p, strip * UNITS + wave, split, lane, out)) return;
+  }
+
+  // ---- epilogue ----------------------------------------------------------------
+  const int n = n0 + uj * 32 + (lane & 31);
+  if (n >= p.N) return;
+  const int mrow = ui * 32 + 4 * (lane >> 5);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int m = mrow + 8 * (r >> 2) + (r & 3);
+    if (m < p.M) epilogue_elem<EPI, OutT, uint16_t>(p, m, n, out[0][r], DUAL ? out[NOUT - 1][r] : 0.0f);
+  }
+}
+
+template <int MT, bool DUAL, int EPI, typename OutT>
+hipError_t launch_decode_mt(const GemmParams& p, const GemmPlan& plan, hipStream_t s) {
+  if (!p.apk_ready) {
+    const int nsteps = (p.K0 + 15) / 16;
+    const int npk = nsteps * MT * 64;
+    hipLaunchKernelGGL(pack_a_kernel<MT>, dim3((npk + 255) / 256), dim3(256), 0, s,
+                       reinterpret_cast<const uint16_t*>(p.A0), p.lda, p.M, p.K0, nsteps,
+                       reinterpret_cast<u32x4*>(p.apk));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int nstrips = (p.N + DECODE_WCOLS - 1) / DECODE_WCOLS;
+  hipLaunchKernelGGL((gemm_decode_kernel<MT, DUAL, EPI, OutT>), dim3(nstrips * plan.splitk), dim3(KW * 64), 0, s, p);
+  return hipGetLastError();
+}
+
+template <bool DUAL, int EPI, typename OutT>
+hipError_t launch_decode(const GemmParams& p, const GemmPlan& plan, hipStream_t s) {
+  if (!p.apk) return hipErrorInvalidValue;
+  if (p.M <= 32) return launch_decode_mt<1, DUAL, EPI, OutT>(p, plan, s);
+  if (p.M <= STREAM_MAX_M) return launch_decode_mt<2, DUAL, EPI, OutT>(p, plan, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+size_t decode_pack_bytes(int M, int K) {
+  const int mt = M <= 32 ? 1 : 2;
+  return (size_t)((K + 15) / 16) * mt * 64 * 16;
+}
+
+// Split-K exchange tiles of a decode launch: one per output fragment.
+size_t decode_tiles(int M, int N) {
+  const int mt = M <= 32 ? 1 : 2;
+  return (size_t)((N + DECODE_WCOLS - 1) / DECODE_WCOLS) * mt * DECODE_NW;
+}
+
+hipError_t gemm_decode(const GemmParams& p, const GemmPlan& plan, GemmKind kind, bool out_f32, hipStream_t s) {
+  switch (kind) {
+    case GK_FWD_STORE:
+      return out_f32 ? launch_decode<false, EPI_STORE, float>(p, plan, s)
+                     : launch_decode<false, EPI_STORE, uint16_t>(p, plan, s);
+    case GK_FWD_ACT: return launch_decode<false, EPI_ACT, uint16_t>(p, plan, s);
+    case GK_FWD_SWIGLU: return launch_decode<true, EPI_SWIGLU, uint16_t>(p, plan, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace tpk

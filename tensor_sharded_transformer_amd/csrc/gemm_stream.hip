@@ -33,100 +33,9 @@
 
 #include "tp_kernels.h"
 #include "tp_device.h"
+#include "stream_frag.h"
 
 namespace tpk {
-
-namespace {
-
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-// One k-step (16 values of k) of weight operands for one wave, as loaded
-// from global memory: per matrix, NW instructions of 1 KB, instruction u
-// covering rows u*16/NW .. (u+1)*16/NW - 1 and all NW*32 columns, so every
-// instruction reads NW*64 contiguous bytes of each of its rows.
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-
-template <int NF>
-struct WFrag {
-  u32x4 b[NF];
-};
-
-// LDS tile of one 32-column fragment: [16 rows][32 columns] bf16 (64-byte
-// rows), padded so the NW tiles a row of lanes writes to land on different
-// banks.
-template <int NW>
-constexpr int tile_bytes() { return NW == 1 ? 1024 : 1152; }
-
-// Weight loads of one k-step.  The kernel runs only when the weights allow
-// 16-byte loads (rows 16-byte aligned, N a multiple of 8); columns beyond N
-// are clamped to the last valid 8-column chunk, whose products only reach
-// outputs the epilogue never stores.  In the TAIL step rows at or beyond K
-// read as zero.
-template <int NW, bool DUAL, bool TAIL>
-__device__ __forceinline__ void load_w(WFrag<DUAL ? 2 * NW : NW>& fr, const GemmParams& p, int step, int n0,
-                                       int lane) {
-  constexpr int RPI = 16 / NW;     // rows per instruction
-  constexpr int CPR = NW * 4;      // 16-byte chunks per row
-  const int c = lane % CPR;
-  const int n = min(n0 + c * 8, p.N - 8);
-#pragma unroll
-  for (int mat = 0; mat < (DUAL ? 2 : 1); ++mat) {
-    const uint16_t* B = reinterpret_cast<const uint16_t*>(mat ? p.B1 : p.B0);
-#pragma unroll
-    for (int u = 0; u < NW; ++u) {
-      const int kb = step * 16 + u * RPI + lane / CPR;
-      if (!TAIL || kb < p.K0) fr.b[mat * NW + u] = *reinterpret_cast<const u32x4*>(B + (int64_t)kb * p.ldb + n);
-      else fr.b[mat * NW + u] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-}
-
-// LDS position of this lane's 16 bytes of instruction u of matrix `mat`.
-template <int NW>
-__device__ __forceinline__ int w_lds_off(int mat, int u, int lane) {
-  constexpr int RPI = 16 / NW, CPR = NW * 4;
-  const int c = lane % CPR;
-  const int row = u * RPI + lane / CPR;
-  return (mat * NW + c / 4) * tile_bytes<NW>() + row * 64 + (c % 4) * 16;
-}
-
-// Activation fragment of the TAIL step straight from global memory, with
-// k-values at or beyond K read as zero (rows beyond M clamped).
-__device__ __forceinline__ u32x4 load_a_tail(const GemmParams& p, int mt, int step, int lane) {
-  const int m = min(mt * 32 + (lane & 31), p.M - 1);
-  const int ka = step * 16 + (lane >> 5) * 8;
-  const uint16_t* ptr = reinterpret_cast<const uint16_t*>(p.A0) + (int64_t)m * p.lda + ka;
-  uint32_t w[4] = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int e = 0; e < 8; ++e)
-    if (ka + e < p.K0) w[e >> 1] |= ((uint32_t)ptr[e]) << ((e & 1) * 16);
-  return u32x4{w[0], w[1], w[2], w[3]};
-}
-
-// ds_read_b64_tr_b16 over a [16 rows][32 columns] bf16 tile (64-byte rows):
-// in each group of 16 lanes, lane 4j+q names row r0+j, columns c0+4q..c0+4q+3,
-// and lane i receives rows r0..r0+3 of column c0+i.  Two reads give the MFMA
-// B operand: lane l gets rows 8(l/32)..8(l/32)+7 of column l%32.
-__device__ __forceinline__ bf16x8 read_b_frag(const char* tile, int lane) {
-  const int g = lane >> 4, s = lane & 15;
-  const int c0 = (g & 1) * 16, r0 = (g >> 1) * 8;
-  const int off = (r0 + (s >> 2)) * 64 + (c0 + (s & 3) * 4) * 2;
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + off));
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + off + 4 * 64));
-  typedef short i16x8 __attribute__((ext_vector_type(8)));
-  const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, v);
-}
-
-}  // namespace
-
-// K range of split `split` in whole 16-value steps.
-__device__ __forceinline__ void split_range(int K, int splitk, int split, int* s_begin, int* s_end) {
-  const int nsteps = (K + 15) / 16;
-  *s_begin = (int)(((int64_t)nsteps * split) / splitk);
-  *s_end = (int)(((int64_t)nsteps * (split + 1)) / splitk);
-}
 
 template <int MT, int NW, bool DUAL, int DEPTH, int CW, int EPI, typename OutT>
 __global__ __launch_bounds__(CW * 64) void gemm_stream_kernel(const GemmParams p) {
@@ -247,157 +156,17 @@ __global__ __launch_bounds__(CW * 64) void gemm_stream_kernel(const GemmParams p
     }
 }
 
-// Variant with the K range split across the waves of a workgroup instead of
-// across workgroups: the KW waves of a workgroup share one column group, each
-// streams its own K sub-range, reading its A operands straight from global
-// memory (x is small and stays in L2), and the waves' accumulators are summed
-// through LDS in a fixed tree order.  Only a few K splits across workgroups
-// remain, so the cross-workgroup fixup is short.
-template <int MT, int NW, bool DUAL, int DEPTH, int KW, int EPI, typename OutT>
-__global__ __launch_bounds__(KW * 64) void gemm_stream_kw_kernel(const GemmParams p) {
-  constexpr int NF = DUAL ? 2 * NW : NW;
-  constexpr int NACC = MT * NF;
-  constexpr int GCOLS = NW * 32;
-  constexpr int TB = tile_bytes<NW>();
-  static_assert((KW & (KW - 1)) == 0, "KW must be a power of two");
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  char* wt = smem;                                        // [KW][NF][TB] weight tiles
-  float* red = reinterpret_cast<float*>(smem + KW * NF * TB);  // [KW/2][NACC*16][64]
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int nstrips = (p.N + GCOLS - 1) / GCOLS;
-  const int id = xcd_remap(blockIdx.x, gridDim.x);
-  const int split = id / nstrips;
-  const int strip = id - split * nstrips;
-  const int n0 = strip * GCOLS;
-
-  int s_begin, s_end;
-  split_range(p.K0, p.splitk, split, &s_begin, &s_end);
-  const int w_begin = s_begin + (s_end - s_begin) * wave / KW;
-  const int w_end = s_begin + (s_end - s_begin) * (wave + 1) / KW;
-  const int full_end = min(w_end, p.K0 / 16);
-
-  f32x16 acc[MT][NF];
-#pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int j = 0; j < NF; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  const uint16_t* A = reinterpret_cast<const uint16_t*>(p.A0);
-  auto load_a = [&](u32x4 (&a)[MT], int step) {
-#pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      const int m = min(i * 32 + (lane & 31), p.M - 1);
-      a[i] = *reinterpret_cast<const u32x4*>(A + (int64_t)m * p.lda + step * 16 + (lane >> 5) * 8);
-    }
-  };
-  char* my = wt + wave * NF * TB;
-  auto mma = [&](const WFrag<NF>& f, const u32x4 (&a)[MT]) {
-#pragma unroll
-    for (int mat = 0; mat < (DUAL ? 2 : 1); ++mat)
-#pragma unroll
-      for (int u = 0; u < NW; ++u) *reinterpret_cast<u32x4*>(my + w_lds_off<NW>(mat, u, lane)) = f.b[mat * NW + u];
-    bf16x8 bv[NF];
-#pragma unroll
-    for (int j = 0; j < NF; ++j) bv[j] = read_b_frag(my + j * TB, lane);
-#pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      const bf16x8 av = __builtin_bit_cast(bf16x8, a[i]);
-#pragma unroll
-      for (int j = 0; j < NF; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv[j], acc[i][j], 0, 0, 0);
-    }
-  };
-
-  if (w_begin < full_end) {
-    WFrag<NF> fr[DEPTH];
-    u32x4 fa[DEPTH][MT];
-    static_for<0, DEPTH>([&](auto d) {
-      const int st = min(w_begin + (int)d, full_end - 1);
-      load_w<NW, DUAL, false>(fr[d], p, st, n0, lane);
-      load_a(fa[d], st);
-    });
-    for (int s = w_begin; s < full_end; s += DEPTH) {
-      static_for<0, DEPTH>([&](auto d) {
-        if (s + (int)d < full_end) mma(fr[d], fa[d]);
-        const int st = min(s + DEPTH + (int)d, full_end - 1);
-        load_w<NW, DUAL, false>(fr[d], p, st, n0, lane);
-        load_a(fa[d], st);
-      });
-    }
-  }
-  if (w_end > full_end && w_end > w_begin) {  // the partial last k-step of K
-    WFrag<NF> ft;
-    u32x4 at[MT];
-    load_w<NW, DUAL, true>(ft, p, w_end - 1, n0, lane);
-#pragma unroll
-    for (int i = 0; i < MT; ++i) at[i] = load_a_tail(p, i, w_end - 1, lane);
-    mma(ft, at);
-  }
-
-  // ---- tree sum of the KW waves through LDS (fixed order) --------------------
-#pragma unroll
-  for (int half = KW / 2; half >= 1; half /= 2) {
-    if (wave >= half && wave < 2 * half) {
-      float* dst = red + (wave - half) * NACC * 16 * 64;
-#pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int j = 0; j < NF; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) dst[((i * NF + j) * 16 + r) * 64 + lane] = acc[i][j][r];
-    }
-    __syncthreads();
-    if (wave < half) {
-      const float* src = red + wave * NACC * 16 * 64;
-#pragma unroll
-      for (int i = 0; i < MT; ++i)
-#pragma unroll
-        for (int j = 0; j < NF; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[i][j][r] += src[((i * NF + j) * 16 + r) * 64 + lane];
-    }
-    __syncthreads();
-  }
-  if (wave != 0) return;
-
-  // ---- split-K across workgroups (wave 0 only; no block barriers below) ------
-  if (p.splitk > 1) {
-    if (!splitk_exchange<MT * NF>(p, strip, split, lane, &acc[0][0])) return;
-  }
-
-  // ---- epilogue --------------------------------------------------------------
-  const int mrow = 4 * (lane >> 5);
-#pragma unroll
-  for (int i = 0; i < MT; ++i)
-#pragma unroll
-    for (int j = 0; j < NW; ++j) {
-      const int n = n0 + j * 32 + (lane & 31);
-      if (n >= p.N) continue;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = i * 32 + mrow + 8 * (r >> 2) + (r & 3);
-        if (m < p.M) epilogue_elem<EPI, OutT, uint16_t>(p, m, n, acc[i][j][r], DUAL ? acc[i][j + NW][r] : 0.0f);
-      }
-    }
-}
-
 // LDS bytes the streaming kernel needs for an M-row, K-range-of-`ksteps` launch.
 size_t stream_lds_bytes(int M, int ksteps, bool dual) {
   const int mt = M <= 32 ? 1 : 2;
   const int nf = (dual ? 2 : 1) * STREAM_NW;
-  if (STREAM_MODE == 2)
-    return (size_t)STREAM_KW * nf * tile_bytes<STREAM_NW>() + (size_t)(STREAM_KW / 2) * mt * nf * 16 * 64 * 4;
   return (size_t)STREAM_CW * nf * tile_bytes<STREAM_NW>() + (size_t)mt * 32 * (ksteps * 32 + 16);
 }
 
 template <int MT, bool DUAL, int EPI, typename OutT>
 static hipError_t launch_stream_mt(const GemmParams& p, const GemmPlan& plan, hipStream_t s) {
-  auto kern = STREAM_MODE == 2 ? gemm_stream_kw_kernel<MT, STREAM_NW, DUAL, TP_STREAM_DEPTH, STREAM_KW, EPI, OutT>
-                               : gemm_stream_kernel<MT, STREAM_NW, DUAL, TP_STREAM_DEPTH, STREAM_CW, EPI, OutT>;
-  const int threads = 64 * (STREAM_MODE == 2 ? STREAM_KW : STREAM_CW);
+  auto kern = gemm_stream_kernel<MT, STREAM_NW, DUAL, TP_STREAM_DEPTH, STREAM_CW, EPI, OutT>;
+  const int threads = 64 * STREAM_CW;
   const int nstrips = (p.N + STREAM_WCOLS - 1) / STREAM_WCOLS;
   const int nsteps = (p.K0 + 15) / 16;
   const int max_steps = (nsteps + plan.splitk - 1) / plan.splitk;  // longest split

@@ -38,7 +38,6 @@ namespace tpk {
 namespace {
 
 constexpr int TBK = 64;                 // k per LDS stage
-constexpr int NSUB = TBK / 16;          // MFMA k-substeps per stage
 constexpr uint32_t OOB = 0x80000000u;   // buffer offset past the record bound
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));

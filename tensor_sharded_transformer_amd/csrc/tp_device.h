@@ -77,6 +77,10 @@ struct GemmParams {
   int splitk;          // number of K splits (>= 1)
   float* partials;     // split-K fp32 partial tiles
   int* counters;       // split-K arrival counters (zero on entry, left zero)
+  void* apk;           // decode kernel: A in MFMA fragment order (workspace)
+  int apk_ready;       // decode kernel: apk already holds A (skip the packing pass)
+  void* cpk;           // if set: the bf16 output goes here, in the packed A
+  int cpk_mt;          //   layout of a decode GEMM with cpk_mt 32-row tiles, instead of to C
 };
 
 // Calls f(integral_constant<int, I>) for I = 0 .. N-1, so array indices in
@@ -142,32 +146,37 @@ __device__ __forceinline__ bool splitk_exchange(const GemmParams& p, int t, int 
   if (lane == 0) prev = __hip_atomic_fetch_add(&p.counters[t], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   prev = __shfl(prev, 0);
   if (prev != p.splitk - 1) return false;
-  // Every split has arrived: for each accumulator, load all splits' values
-  // (8 at a time, issued together) and add them in split order.
-  constexpr int SB = 8;
+  // Every split has arrived: load the splits' values in batches of SB splits
+  // (all accumulators of a batch issued together, about 32 loads per lane)
+  // and add them in split order.
+  constexpr int SB = NACC >= 8 ? 1 : 8 / NACC;
+  f32x16 sum[NACC];
 #pragma unroll
-  for (int a = 0; a < NACC; ++a) {
-    f32x16 sum;
+  for (int a = 0; a < NACC; ++a)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) sum[e] = 0.0f;
-    for (int s0 = 0; s0 < p.splitk; s0 += SB) {
-      f32x4v v[SB][4];
+    for (int e = 0; e < 16; ++e) sum[a][e] = 0.0f;
+  for (int s0 = 0; s0 < p.splitk; s0 += SB) {
+    f32x4v v[SB][NACC][4];
 #pragma unroll
-      for (int sb = 0; sb < SB; ++sb)
+    for (int sb = 0; sb < SB; ++sb)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) v[sb][q] = splitk_load(r, (s0 + sb) * SPLIT_BYTES + ((a * 4 + q) * 64 + lane) * 16);
+      for (int a = 0; a < NACC; ++a)
 #pragma unroll
-      for (int sb = 0; sb < SB; ++sb)
+        for (int q = 0; q < 4; ++q) v[sb][a][q] = splitk_load(r, (s0 + sb) * SPLIT_BYTES + ((a * 4 + q) * 64 + lane) * 16);
+#pragma unroll
+    for (int sb = 0; sb < SB; ++sb)
+#pragma unroll
+      for (int a = 0; a < NACC; ++a)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          sum[4 * q] += v[sb][q][0];
-          sum[4 * q + 1] += v[sb][q][1];
-          sum[4 * q + 2] += v[sb][q][2];
-          sum[4 * q + 3] += v[sb][q][3];
+          sum[a][4 * q] += v[sb][a][q][0];
+          sum[a][4 * q + 1] += v[sb][a][q][1];
+          sum[a][4 * q + 2] += v[sb][a][q][2];
+          sum[a][4 * q + 3] += v[sb][a][q][3];
         }
-    }
-    acc[a] = sum;
   }
+#pragma unroll
+  for (int a = 0; a < NACC; ++a) acc[a] = sum[a];
   if (lane == 0) __hip_atomic_store(&p.counters[t], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return true;
 }
@@ -194,6 +203,17 @@ __device__ __forceinline__ float ld_in<float>(const void* base, int64_t ld, int 
   return reinterpret_cast<const float*>(base)[(int64_t)m * ld + n];
 }
 
+// The main (bf16) output of the activation epilogues: row-major C, or the
+// packed fragment layout of the next decode GEMM's A operand (k = n).
+__device__ __forceinline__ void st_main(const GemmParams& p, int m, int n, float v) {
+  if (p.cpk) {
+    const int64_t chunk = ((int64_t)(n >> 4) * p.cpk_mt + (m >> 5)) * 64 + (m & 31) + ((n >> 3) & 1) * 32;
+    reinterpret_cast<uint16_t*>(p.cpk)[chunk * 8 + (n & 7)] = f2bf(v);
+  } else {
+    st<uint16_t>(p.C, p.ldc, m, n, v);
+  }
+}
+
 // The epilogue for one output element.  OutT is the type of C (and of the
 // C2/C3 side outputs and S0/S1 side inputs, except EPI_STORE's f32 output of
 // bf16 inputs, which only writes C).
@@ -205,13 +225,15 @@ __device__ __forceinline__ void epilogue_elem(const GemmParams& p, int m, int n,
     float a = v0;
     if (p.bias) a += ld_in<SideT>(p.bias, 0, 0, n);
     if (p.C2) st<SideT>(p.C2, p.ldc2, m, n, a);
-    st<OutT>(p.C, p.ldc, m, n, act_fwd(p.act, a));
+    if constexpr (std::is_same<OutT, uint16_t>::value) st_main(p, m, n, act_fwd(p.act, a));
+    else st<OutT>(p.C, p.ldc, m, n, act_fwd(p.act, a));
   } else if constexpr (EPI == EPI_SWIGLU) {
     if (p.C2) {
       st<SideT>(p.C2, p.ldc2, m, n, v0);
       st<SideT>(p.C3, p.ldc2, m, n, v1);
     }
-    st<OutT>(p.C, p.ldc, m, n, v0 * sigmoidf_(v0) * v1);
+    if constexpr (std::is_same<OutT, uint16_t>::value) st_main(p, m, n, v0 * sigmoidf_(v0) * v1);
+    else st<OutT>(p.C, p.ldc, m, n, v0 * sigmoidf_(v0) * v1);
   } else if constexpr (EPI == EPI_DUAL_STORE) {
     st<OutT>(p.C, p.ldc, m, n, v0);
     st<OutT>(p.C2, p.ldc2, m, n, v1);

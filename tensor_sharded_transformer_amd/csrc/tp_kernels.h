@@ -21,14 +21,20 @@
 #ifndef TP_STREAM_TARGET_WGS
 #define TP_STREAM_TARGET_WGS 256
 #endif
-// 1: the waves of a workgroup own adjacent column groups over one K range,
-//    with that range's activations staged once in LDS;
-// 2: the waves of a workgroup split the K range of one column group.
-#ifndef TP_STREAM_MODE
-#define TP_STREAM_MODE 1
+// Packed-activation decode kernel: waves per workgroup (each streams its own
+// K sub-range), 32-column fragments per weight matrix and workgroup, k-steps
+// of loads in flight per wave; TP_DECODE=0 keeps the LDS-slice kernel.
+#ifndef TP_DECODE
+#define TP_DECODE 1
 #endif
-#ifndef TP_STREAM_KW
-#define TP_STREAM_KW 8
+#ifndef TP_DECODE_KW
+#define TP_DECODE_KW 4
+#endif
+#ifndef TP_DECODE_NW
+#define TP_DECODE_NW 2
+#endif
+#ifndef TP_DECODE_DEPTH
+#define TP_DECODE_DEPTH 4
 #endif
 
 // Pipelined tiled kernel: k-tiles of loads in flight (register ring depth)
@@ -48,10 +54,11 @@ namespace tpk {
 
 constexpr int STREAM_NW = TP_STREAM_NW;
 constexpr int STREAM_CW = TP_STREAM_CW;
-constexpr int STREAM_MODE = TP_STREAM_MODE;
-constexpr int STREAM_KW = TP_STREAM_KW;
-constexpr int STREAM_WCOLS = 32 * STREAM_NW * (STREAM_MODE == 2 ? 1 : STREAM_CW);  // output columns per workgroup
-constexpr int STREAM_TILES_PER_WG = STREAM_MODE == 2 ? 1 : STREAM_CW;             // split-K tiles per workgroup
+constexpr int STREAM_WCOLS = 32 * STREAM_NW * STREAM_CW;  // output columns per workgroup
+constexpr int STREAM_TILES_PER_WG = STREAM_CW;            // split-K tiles per workgroup
+constexpr int DECODE_KW = TP_DECODE_KW;
+constexpr int DECODE_NW = TP_DECODE_NW;
+constexpr int DECODE_WCOLS = 32 * DECODE_NW;              // output columns per workgroup
 constexpr int STREAM_LDS_MAX = 160 * 1024;                // gfx950 LDS per workgroup
 constexpr int STREAM_MAX_M = 64;                          // tokens the streaming kernel serves
 constexpr int STREAM_TARGET_WGS = TP_STREAM_TARGET_WGS;   // K is split until about this many workgroups
@@ -63,7 +70,7 @@ size_t stream_lds_bytes(int M, int ksteps, bool dual);
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 enum TileShape : int { TILE_256x256 = 0, TILE_128x128 = 1, TILE_64x128 = 2 };
-enum KernelKind : int { KERNEL_TILED = 0, KERNEL_STREAM = 1 };
+enum KernelKind : int { KERNEL_TILED = 0, KERNEL_STREAM = 1, KERNEL_DECODE = 2 };
 
 struct GemmPlan {
   int kernel = KERNEL_TILED;
@@ -88,11 +95,18 @@ enum GemmKind : int {
 // allow 16-byte loads (its other precondition); allow_split: a workspace for
 // split-K partials is available.
 GemmPlan plan_gemm(int M, int N, int K, bool dual, bool fwd_layout, bool vec_ok, bool allow_split);
-// Split-K scratch for a plan: fp32 partial tiles (bytes) and one arrival
-// counter per output tile.
-void gemm_split_sizes(const GemmPlan& plan, int M, int N, bool dual, size_t* part_bytes, size_t* n_tiles);
+// Workspace a plan needs: split-K fp32 partial tiles (bytes), one arrival
+// counter per exchange tile, and the packed activation fragments of the
+// decode kernel (bytes).
+void gemm_split_sizes(const GemmPlan& plan, int M, int N, int K, bool dual, size_t* part_bytes, size_t* n_tiles,
+                      size_t* pack_bytes);
 hipError_t gemm_bf16(const GemmParams& p, const GemmPlan& plan, GemmKind kind, bool out_f32, hipStream_t s);
 hipError_t gemm_stream(const GemmParams& p, const GemmPlan& plan, GemmKind kind, bool out_f32, hipStream_t s);
+// Decode kernel (packs p.A0 into p.apk first), its packed-A bytes and its
+// split-K exchange tiles.
+size_t decode_pack_bytes(int M, int K);
+size_t decode_tiles(int M, int N);
+hipError_t gemm_decode(const GemmParams& p, const GemmPlan& plan, GemmKind kind, bool out_f32, hipStream_t s);
 // The pipelined tiled kernel, for plans and operands it supports.
 bool gemm_tile_supported(const GemmParams& p, const GemmPlan& plan, GemmKind kind);
 hipError_t gemm_tile(const GemmParams& p, const GemmPlan& plan, GemmKind kind, bool out_f32, hipStream_t s);

@@ -120,7 +120,8 @@ def test_mlp_fwd_validation(lib):
     need = lib.tp_mlp_shard_fwd_workspace(64, 8192, 3584, 0, 3)
     assert need >= 64 * 3584 * 2
     args = (64, 8192, 3584, 0, 0, 3, None)
-    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, need - 1, *args) == WS
+    # the query is the maximum over operand alignments; half of it is too small for every plan
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, need // 2, *args) == WS
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 0, *args) == WS
     assert f(FAKE, FAKE, None, FAKE, FAKE, None, FAKE, need, *args) == ACTE    # SWIGLU needs w_up
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, need, 64, 8192, 3584, 0, 0, 1, None) == ACTE
