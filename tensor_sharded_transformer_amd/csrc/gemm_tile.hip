@@ -10,23 +10,27 @@
 // Design (one workgroup of 4 waves = one BM x BN output tile):
 //  * v_mfma_f32_32x32x16_bf16; each wave owns a (BM/2) x (BN/2) block of
 //    32x32 accumulator tiles.
-//  * K advances in tiles of 64.  The 16-byte buffer loads of tile kt+RS land
-//    in a ring of RS register slots while tile kt feeds the MFMAs; tile kt+1
-//    moves from its register slot to the other half of a double-buffered LDS
-//    tile halfway through step kt.  Loads therefore have about RS steps of
-//    MFMA work to arrive, and the compiler sees every load and wait.
+//  * K advances in tiles of 32.  Operand tiles go from global memory straight
+//    into LDS (buffer_load_dwordx4 ... lds, no staging registers) through a
+//    ring of STAGES separate LDS arrays; the loads of tile kt+STAGES-1 are
+//    issued while tile kt feeds the MFMAs.  Because each stage is its own LDS
+//    object, the compiler orders a fragment read only after the loads into
+//    that stage, not after every load in flight.
 //  * Operands keep their memory layout in LDS.  A k-contiguous operand is a
-//    [rows][64] tile (128 B rows) read as MFMA fragments with ds_read_b128; an
-//    m- or n-contiguous operand (the (in, out) weights, the transposed
-//    operands of the weight gradients) is a [64][cols] tile in sub-tiles of at
+//    [rows][32] tile (64-byte rows) read as MFMA fragments with ds_read_b128;
+//    an m- or n-contiguous operand (the (in, out) weights, the transposed
+//    operands of the weight gradients) is a [32][cols] tile in sub-tiles of at
 //    most 128 columns, read with ds_read_b64_tr_b16, which transposes 16-bit
 //    elements on the way out of LDS.  Both layouts XOR-swizzle 16-byte chunks
-//    so the fragment reads are free of bank conflicts; the swizzle is applied
-//    on the global side of the load (each lane fetches the chunk that belongs
-//    at its fixed LDS slot, and the LDS writes are linear).
+//    (measured conflict-free on gfx950); the swizzle is applied on the global
+//    side of the load: each lane fetches the chunk that belongs at its fixed
+//    LDS slot.
 //  * Edges: each lane's buffer offset is replaced by an out-of-range value
-//    when its 16-byte chunk lies outside the matrix, and the buffer unit then
-//    returns zeros.  No separate masked loop.
+//    when its 16-byte chunk lies outside the matrix; the buffer unit then
+//    writes zeros to LDS.  No separate masked loop.
+//  * One barrier per k-tile.  The MFMAs of a tile's last substep run after
+//    that barrier, interleaved with the next tile's first fragment reads, and
+//    every MFMA block is interleaved with the LDS reads of the next block.
 //  * Workgroup ids are renumbered so each XCD works on a contiguous, M-grouped
 //    range of tiles and shares operand panels in its own L2.
 #include <type_traits>
@@ -37,23 +41,23 @@
 namespace tpk {
 namespace {
 
-constexpr int TBK = 64;                 // k per LDS stage
+constexpr int TBK = 32;                 // k per LDS stage
 constexpr uint32_t OOB = 0x80000000u;   // buffer offset past the record bound
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_at(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFFF, 0x00020000);
 }
 
-// Chunk swizzle of a k-contiguous [rows][64] tile (eight 16-byte chunks per
-// row): conflict-free ds_read_b128 of 32 consecutive rows, one chunk each,
-// and conflict-free 16-byte writes of whole rows.
-__device__ __forceinline__ int kc_swz(int row) { return (row ^ (row >> 3)) & 7; }
-// Chunk swizzle of a [64][SW] sub-tile (SW = 128: 16 chunks per row,
+// Chunk swizzle of a k-contiguous [rows][32] tile (four 16-byte chunks per
+// row): conflict-free ds_read_b128 of 32 consecutive rows, one chunk each.
+__device__ __forceinline__ int kc_swz(int row) { return ((row >> 2) ^ (row >> 3)) & 3; }
+// Chunk swizzle of a [32][SW] sub-tile (SW = 128: 16 chunks per row,
 // SW = 64: 8): conflict-free ds_read_b64_tr_b16 of four k-rows x 32 columns.
 template <int SW>
 __device__ __forceinline__ int mn_swz(int krow) {
@@ -79,12 +83,12 @@ __device__ __forceinline__ void interleave() {
 }
 
 // One operand's tile of R rows (k-contiguous) or R columns (m/n-contiguous)
-// by 64 k-values.  Each of the 256 threads issues R/32 16-byte loads per
+// by 32 k-values.  Each of the 256 threads issues R/64 16-byte loads per
 // stage; load c of thread tid fills LDS slot c*256 + tid.  Every wave-wide
 // load lies inside one source matrix, so its buffer descriptor is uniform.
 template <int R, bool KC, bool DUAL>
 struct OpTile {
-  static constexpr int NL = R / 32;                          // loads per thread per stage
+  static constexpr int NL = R / 64;                          // loads per thread per stage
   static constexpr int BYTES = R * TBK * 2;                  // LDS bytes per stage
   static constexpr int SW = KC ? 0 : (DUAL ? (R / 2 < 128 ? R / 2 : 128) : (R < 128 ? R : 128));
   static_assert(KC || SW == 64 || SW == 128, "sub-tile width");
@@ -97,7 +101,7 @@ struct OpTile {
   // Which source matrix (0 / 1) load c reads: the second half of a dual tile.
   static constexpr int src_of(int c) {
     if constexpr (!DUAL) return 0;
-    else if constexpr (KC) return c * 256 >= 4 * R ? 1 : 0;
+    else if constexpr (KC) return c * 256 >= 2 * R ? 1 : 0;
     else return ((c * 256) / SUB_SLOTS) >= (R / SW) / 2 ? 1 : 0;
   }
 
@@ -108,9 +112,9 @@ struct OpTile {
     for (int c = 0; c < NL; ++c) {
       const int slot = c * 256 + tid;
       if constexpr (KC) {
-        int row = slot >> 3;
+        int row = slot >> 2;
         if (DUAL && row >= R / 2) row -= R / 2;
-        const int chunk = (slot & 7) ^ kc_swz(slot >> 3);
+        const int chunk = (slot & 3) ^ kc_swz(slot >> 2);
         voff[c] = (uint32_t)(row * ld * 2 + chunk * 16);
         kidx[c] = r0 + row < extent ? chunk * 8 : INT_MAX;
       } else {
@@ -125,20 +129,19 @@ struct OpTile {
     }
   }
 
-  // Load one k-tile into registers.  base0/base1: the sources at (tile
-  // origin, k-tile start); kvalid: k-values of the k-tile inside the matrix.
-  __device__ __forceinline__ void load(u32x4* regs, const void* base0, const void* base1, int kvalid) const {
+  // Issue one k-tile's loads straight into LDS.  base0/base1: the sources
+  // at (tile origin, k-tile start); kvalid: k-values of the k-tile inside the
+  // matrix (<= 0: every load masked); lds: this operand's tile in the stage.
+  __device__ __forceinline__ void issue(const void* base0, const void* base1, int kvalid, char* lds,
+                                        int wave) const {
     const __amdgpu_buffer_rsrc_t r0 = rsrc_at(base0);
     const __amdgpu_buffer_rsrc_t r1 = rsrc_at(base1);
 #pragma unroll
     for (int c = 0; c < NL; ++c) {
       const uint32_t off = kidx[c] < kvalid ? voff[c] : OOB;
-      regs[c] = __builtin_amdgcn_raw_buffer_load_b128(src_of(c) ? r1 : r0, off, 0, 0);
+      lds_void* dst = (lds_void*)(lds + (c * 256 + wave * 64) * 16);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(src_of(c) ? r1 : r0, dst, 16, off, 0, 0, 0);
     }
-  }
-  __device__ __forceinline__ static void store(const u32x4* regs, char* lds, int tid) {
-#pragma unroll
-    for (int c = 0; c < NL; ++c) *reinterpret_cast<u32x4*>(lds + (c * 256 + tid) * 16) = regs[c];
   }
 };
 
@@ -177,17 +180,53 @@ __device__ __forceinline__ bf16x8 read_frag(const char* tile, int o0, int o1, in
   }
 }
 
-template <int BM, int BN, int RS, bool AKC, bool BKC, bool DUAL, int EPI, typename OutT>
+// s_waitcnt vmcnt(N), other counters untouched, then s_barrier.  Written as
+// one asm statement with a memory clobber so no LDS access moves across it;
+// the wait covers this wave's own LDS-bound loads, the barrier everyone's.
+template <int N>
+__device__ __forceinline__ void wait_loads_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  if constexpr (N == 0) __asm__ volatile("s_waitcnt vmcnt(0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 8) __asm__ volatile("s_waitcnt vmcnt(8)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 16) __asm__ volatile("s_waitcnt vmcnt(16)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 24) __asm__ volatile("s_waitcnt vmcnt(24)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 4) __asm__ volatile("s_waitcnt vmcnt(4)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 12) __asm__ volatile("s_waitcnt vmcnt(12)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else static_assert(N == 0, "add the vmcnt value here");
+}
+
+template <int BM, int BN, bool AKC, bool BKC, bool DUAL>
+struct TileCfg {
+  using TA = OpTile<BM, AKC, false>;
+  using TB = OpTile<BN, BKC, DUAL>;
+  static constexpr int STAGE = TA::BYTES + TB::BYTES;
+  static constexpr int LPS = TA::NL + TB::NL;  // loads per thread per stage
+};
+
+template <int BM, int BN, int STAGES, bool AKC, bool BKC, bool DUAL, int EPI, typename OutT>
 __global__ __launch_bounds__(256) void gemm_tile_kernel(const GemmParams p) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int BNH = DUAL ? BN / 2 : BN;  // output columns per tile
   static_assert(!DUAL || (TN % 2 == 0), "dual mode needs gate and up fragments per wave");
-  using TA = OpTile<BM, AKC, false>;
-  using TB = OpTile<BN, BKC, DUAL>;
-  constexpr int STAGE = TA::BYTES + TB::BYTES;
-  static_assert(RS >= 1 && RS <= 4, "register ring depth");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  using Cfg = TileCfg<BM, BN, AKC, BKC, DUAL>;
+  using TA = typename Cfg::TA;
+  using TB = typename Cfg::TB;
+  constexpr int STAGE = Cfg::STAGE;
+  constexpr int LPS = Cfg::LPS;
+  static_assert(STAGES == 4, "the ring is four LDS arrays");
+  // One LDS object per stage (see the header comment).
+  __shared__ __attribute__((aligned(1024))) char st0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1[STAGE];
+  __shared__ __attribute__((aligned(1024))) char st2[STAGE];
+  __shared__ __attribute__((aligned(1024))) char st3[STAGE];
+  auto stage = [&](auto ic) -> char* {
+    constexpr int i = decltype(ic)::value % 4;
+    if constexpr (i == 0) return st0;
+    else if constexpr (i == 1) return st1;
+    else if constexpr (i == 2) return st2;
+    else return st3;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -216,27 +255,20 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(const GemmParams p) {
   ta.setup(tid, m0, p.M, p.lda);
   tb.setup(tid, n0, p.N, p.ldb);
 
-  // Register ring: slot r holds the A and B loads of one k-tile.
-  u32x4 ra[RS][TA::NL];
-  u32x4 rb[RS][TB::NL];
-  // Tiles past the end are issued too, fully masked (no memory access), so
-  // every step issues the same loads and the compiler's wait counts stay exact.
-  auto load = [&](int kt, u32x4* a_regs, u32x4* b_regs) {
+  // Issue the LDS-bound loads of k-tile kt into stage array st.  Tiles past
+  // the end are issued too, fully masked (no memory access, zeros in LDS), so
+  // every step issues the same number of loads and the wait counts are exact.
+  auto issue = [&](int kt, char* st) {
     const bool s1 = kt >= nk0;
     const int k0 = (s1 ? kt - nk0 : kt) * TBK;
     const int kvalid = kt >= nk ? 0 : (s1 ? p.K1 : p.K0) - k0;
     const uint16_t* a = reinterpret_cast<const uint16_t*>(s1 ? p.A1 : p.A0);
     const uint16_t* b0 = reinterpret_cast<const uint16_t*>(s1 ? p.B1 : p.B0);
     const uint16_t* b1 = reinterpret_cast<const uint16_t*>(p.B1);
-    // tile origin + k-tile start in each source
     const int64_t ao = kvalid <= 0 ? 0 : (AKC ? (int64_t)m0 * p.lda + k0 : (int64_t)k0 * p.lda + m0);
     const int64_t bo = kvalid <= 0 ? 0 : (BKC ? (int64_t)n0 * p.ldb + k0 : (int64_t)k0 * p.ldb + n0);
-    ta.load(a_regs, a + ao, a + ao, kvalid);
-    tb.load(b_regs, b0 + bo, b1 + bo, kvalid);
-  };
-  auto store = [&](const u32x4* a_regs, const u32x4* b_regs, char* st) {
-    TA::store(a_regs, st, tid);
-    TB::store(b_regs, st + TA::BYTES, tid);
+    ta.issue(a + ao, a + ao, kvalid, st, wave);
+    tb.issue(b0 + bo, b1 + bo, kvalid, st + TA::BYTES, wave);
   };
 
   // Fragment offsets (lane-constant) inside a stage.
@@ -265,11 +297,11 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(const GemmParams p) {
 
   bf16x8 af[2][TM];
   bf16x8 bf[2][TN];
-  auto read_frags = [&](const char* stage, int s, int buf) {
+  auto read_frags = [&](const char* st, int s, int buf) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i) af[buf][i] = read_frag<BM, AKC, false>(stage, ao0[i], ao1[i], s);
+    for (int i = 0; i < TM; ++i) af[buf][i] = read_frag<BM, AKC, false>(st, ao0[i], ao1[i], s);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) bf[buf][j] = read_frag<BN, BKC, DUAL>(stage + TA::BYTES, bo0[j], bo1[j], s);
+    for (int j = 0; j < TN; ++j) bf[buf][j] = read_frag<BN, BKC, DUAL>(st + TA::BYTES, bo0[j], bo1[j], s);
   };
   auto mma = [&](int buf) {
 #pragma unroll
@@ -280,23 +312,16 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(const GemmParams p) {
   };
 
   // ---- main loop -------------------------------------------------------------
-  // A step consumes one k-tile in four blocks of 16 MFMAs (one 16-deep
-  // k-substep each).  Each block's MFMAs use fragments read during the
-  // previous block, and the LDS reads of the next substep are interleaved
-  // with them; block 2 also writes tile kt+1 from its register slot to the
-  // other LDS half, block 3 also issues the global loads of tile kt+1+RS.
-  // Block 0 runs the previous tile's last substep, so the only barrier of a
-  // step comes after all of its LDS reads.
-  //   tile t: loaded into register slot t % RS in step t-1-RS (prologue:
-  //   tiles 0 .. RS), written to LDS half t % 2 in step t-1, read in step t.
-  // Steps past the end see zero-filled tiles (their loads are fully masked),
-  // so the loop is branch-free and the wait counts stay exact.
-  static_for<0, RS>([&](auto ic) __attribute__((always_inline)) {
+  // Tile t lives in stage t % 4.  Step kt: issue tile kt+3 into the stage tile
+  // kt-1 used (every wave finished reading it before the barrier that ended
+  // step kt-1); block 0 = MFMAs of tile kt-1's second substep + fragment reads
+  // of tile kt's first; block 1 = MFMAs of tile kt's first substep + reads of
+  // its second; then wait for this wave's loads of tile kt+1 and barrier.
+  // The loop is unrolled by 4 so every stage array is a constant.
+  static_for<0, STAGES - 1>([&](auto ic) __attribute__((always_inline)) {
     constexpr int i = decltype(ic)::value;
-    load(i, ra[i], rb[i]);
+    issue(i, stage(ic));
   });
-  store(ra[0], rb[0], smem);
-  load(RS, ra[0], rb[0]);
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -305,38 +330,25 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(const GemmParams p) {
   for (int j = 0; j < TN; ++j)
 #pragma unroll
     for (int e = 0; e < 8; ++e) bf[1][j][e] = (__bf16)0.0f;
-  __syncthreads();
-  constexpr int UNROLL = RS % 2 == 0 ? RS : 2 * RS;
-  constexpr int NMF = TM * TN;                            // MFMAs per block
+  wait_loads_barrier<(STAGES - 2) * LPS>();
+  constexpr int NMF = TM * TN;                                  // MFMAs per block
   constexpr int NRD = TM * (AKC ? 1 : 2) + TN * (BKC ? 1 : 2);  // LDS reads per block
-  constexpr int NWR = TA::NL + TB::NL;                    // LDS writes / global loads per step
-  const int nk_pad = (nk + UNROLL - 1) / UNROLL * UNROLL;
-  for (int kt0 = 0; kt0 < nk_pad; kt0 += UNROLL) {
-    static_for<0, UNROLL>([&](auto uc) __attribute__((always_inline)) {
+  const int nk_pad = (nk + STAGES - 1) / STAGES * STAGES;
+  for (int kt0 = 0; kt0 < nk_pad; kt0 += STAGES) {
+    static_for<0, STAGES>([&](auto uc) __attribute__((always_inline)) {
       constexpr int u = decltype(uc)::value;
       const int kt = kt0 + u;
-      const char* cur = smem + (u % 2) * STAGE;
-      char* nxt = smem + ((u + 1) % 2) * STAGE;
-      constexpr int slot_next = (u + 1) % RS;  // holds tile kt+1
+      const char* cur = stage(uc);
+      issue(kt + STAGES - 1, stage(std::integral_constant<int, u + STAGES - 1>{}));
       read_frags(cur, 0, 0);
       mma(1);
-      interleave<NMF, NRD, 0, 0>();
+      interleave<NMF, NRD, 0, LPS>();
       __builtin_amdgcn_sched_barrier(0);
       read_frags(cur, 1, 1);
       mma(0);
       interleave<NMF, NRD, 0, 0>();
       __builtin_amdgcn_sched_barrier(0);
-      read_frags(cur, 2, 0);
-      mma(1);
-      store(ra[slot_next], rb[slot_next], nxt);
-      interleave<NMF, NRD, NWR, 0>();
-      __builtin_amdgcn_sched_barrier(0);
-      read_frags(cur, 3, 1);
-      mma(0);
-      load(kt + 1 + RS, ra[slot_next], rb[slot_next]);
-      interleave<NMF, NRD, 0, NWR>();
-      __builtin_amdgcn_sched_barrier(0);
-      __syncthreads();
+      wait_loads_barrier<(STAGES - 2) * LPS>();
     });
   }
   mma(1);
@@ -366,19 +378,19 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(const GemmParams p) {
   });
 }
 
-template <int BM, int BN, int RS, bool AKC, bool BKC, bool DUAL, int EPI, typename OutT>
+template <int BM, int BN, int STAGES, bool AKC, bool BKC, bool DUAL, int EPI, typename OutT>
 hipError_t launch_tile(const GemmParams& p, hipStream_t s) {
   constexpr int BNH = DUAL ? BN / 2 : BN;
   const int grid = ((p.M + BM - 1) / BM) * ((p.N + BNH - 1) / BNH);
-  hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, RS, AKC, BKC, DUAL, EPI, OutT>), dim3(grid), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, STAGES, AKC, BKC, DUAL, EPI, OutT>), dim3(grid), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
 template <bool AKC, bool BKC, bool DUAL, int EPI, typename OutT>
 hipError_t launch_tile_shape(const GemmParams& p, int tile, hipStream_t s) {
   switch (tile) {
-    case TILE_256x256: return launch_tile<256, 256, TP_TILE_RS_256, AKC, BKC, DUAL, EPI, OutT>(p, s);
-    case TILE_128x128: return launch_tile<128, 128, TP_TILE_RS_128, AKC, BKC, DUAL, EPI, OutT>(p, s);
+    case TILE_256x256: return launch_tile<256, 256, 4, AKC, BKC, DUAL, EPI, OutT>(p, s);
+    case TILE_128x128: return launch_tile<128, 128, 4, AKC, BKC, DUAL, EPI, OutT>(p, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -37,15 +37,9 @@
 #define TP_DECODE_DEPTH 4
 #endif
 
-// Pipelined tiled kernel: k-tiles of loads in flight (register ring depth)
-// for the 256x256 and 128x128 tiles; TP_TILE_PIPE=0 keeps the older
-// two-stage kernel for those tiles.
-#ifndef TP_TILE_RS_256
-#define TP_TILE_RS_256 1
-#endif
-#ifndef TP_TILE_RS_128
-#define TP_TILE_RS_128 2
-#endif
+// Pipelined tiled kernel (LDS-bound loads, four-stage ring) for the 256x256
+// and 128x128 tiles; TP_TILE_PIPE=0 keeps the register-staged two-stage
+// kernel for those tiles.
 #ifndef TP_TILE_PIPE
 #define TP_TILE_PIPE 1
 #endif
