@@ -41,7 +41,9 @@
 namespace tpk {
 namespace {
 
-constexpr int TBK = 32;                 // k per LDS stage
+constexpr int TBK = TP_TILE_BK;         // k per LDS stage (32 or 64)
+constexpr int NSUB = TBK / 16;          // MFMA k-substeps per stage
+constexpr int KC_CHUNKS = TBK / 8;      // 16-byte chunks per k-contiguous row
 constexpr uint32_t OOB = 0x80000000u;   // buffer offset past the record bound
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -54,9 +56,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_at(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFFF, 0x00020000);
 }
 
-// Chunk swizzle of a k-contiguous [rows][32] tile (four 16-byte chunks per
-// row): conflict-free ds_read_b128 of 32 consecutive rows, one chunk each.
-__device__ __forceinline__ int kc_swz(int row) { return ((row >> 2) ^ (row >> 3)) & 3; }
+// Chunk swizzle of a k-contiguous [rows][TBK] tile: conflict-free
+// ds_read_b128 of 32 consecutive rows, one chunk each (both measured on
+// gfx950: 64-byte rows need the row bits 2-3, 128-byte rows bits 0-2 and 3).
+__device__ __forceinline__ int kc_swz(int row) {
+  if constexpr (TBK == 32) return ((row >> 2) ^ (row >> 3)) & 3;
+  else return (row ^ (row >> 3)) & 7;
+}
 // Chunk swizzle of a [32][SW] sub-tile (SW = 128: 16 chunks per row,
 // SW = 64: 8): conflict-free ds_read_b64_tr_b16 of four k-rows x 32 columns.
 template <int SW>
@@ -88,7 +94,7 @@ __device__ __forceinline__ void interleave() {
 // load lies inside one source matrix, so its buffer descriptor is uniform.
 template <int R, bool KC, bool DUAL>
 struct OpTile {
-  static constexpr int NL = R / 64;                          // loads per thread per stage
+  static constexpr int NL = R * TBK / 2048;                  // loads per thread per stage
   static constexpr int BYTES = R * TBK * 2;                  // LDS bytes per stage
   static constexpr int SW = KC ? 0 : (DUAL ? (R / 2 < 128 ? R / 2 : 128) : (R < 128 ? R : 128));
   static_assert(KC || SW == 64 || SW == 128, "sub-tile width");
@@ -101,7 +107,7 @@ struct OpTile {
   // Which source matrix (0 / 1) load c reads: the second half of a dual tile.
   static constexpr int src_of(int c) {
     if constexpr (!DUAL) return 0;
-    else if constexpr (KC) return c * 256 >= 2 * R ? 1 : 0;
+    else if constexpr (KC) return c * 256 >= (R / 2) * KC_CHUNKS ? 1 : 0;
     else return ((c * 256) / SUB_SLOTS) >= (R / SW) / 2 ? 1 : 0;
   }
 
@@ -112,9 +118,9 @@ struct OpTile {
     for (int c = 0; c < NL; ++c) {
       const int slot = c * 256 + tid;
       if constexpr (KC) {
-        int row = slot >> 2;
+        int row = slot / KC_CHUNKS;
         if (DUAL && row >= R / 2) row -= R / 2;
-        const int chunk = (slot & 3) ^ kc_swz(slot >> 2);
+        const int chunk = (slot % KC_CHUNKS) ^ kc_swz(slot / KC_CHUNKS);
         voff[c] = (uint32_t)(row * ld * 2 + chunk * 16);
         kidx[c] = r0 + row < extent ? chunk * 8 : INT_MAX;
       } else {
@@ -192,6 +198,8 @@ __device__ __forceinline__ void wait_loads_barrier() {
   else if constexpr (N == 24) __asm__ volatile("s_waitcnt vmcnt(24)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   else if constexpr (N == 4) __asm__ volatile("s_waitcnt vmcnt(4)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   else if constexpr (N == 12) __asm__ volatile("s_waitcnt vmcnt(12)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 32) __asm__ volatile("s_waitcnt vmcnt(32)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 48) __asm__ volatile("s_waitcnt vmcnt(48)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   else static_assert(N == 0, "add the vmcnt value here");
 }
 
@@ -214,18 +222,21 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(const GemmParams p) {
   using TB = typename Cfg::TB;
   constexpr int STAGE = Cfg::STAGE;
   constexpr int LPS = Cfg::LPS;
-  static_assert(STAGES == 4, "the ring is four LDS arrays");
+  static_assert(STAGES >= 2 && STAGES <= 5, "the ring is two to five LDS arrays");
+  static_assert(NSUB % 2 == 0, "fragment buffers alternate per substep");
   // One LDS object per stage (see the header comment).
   __shared__ __attribute__((aligned(1024))) char st0[STAGE];
   __shared__ __attribute__((aligned(1024))) char st1[STAGE];
   __shared__ __attribute__((aligned(1024))) char st2[STAGE];
-  __shared__ __attribute__((aligned(1024))) char st3[STAGE];
+  __shared__ __attribute__((aligned(1024))) char st3[STAGES > 3 ? STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) char st4[STAGES > 4 ? STAGE : 16];
   auto stage = [&](auto ic) -> char* {
-    constexpr int i = decltype(ic)::value % 4;
+    constexpr int i = decltype(ic)::value % STAGES;
     if constexpr (i == 0) return st0;
     else if constexpr (i == 1) return st1;
     else if constexpr (i == 2) return st2;
-    else return st3;
+    else if constexpr (i == 3) return st3;
+    else return st4;
   };
 
   const int tid = threadIdx.x;
@@ -312,12 +323,12 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(const GemmParams p) {
   };
 
   // ---- main loop -------------------------------------------------------------
-  // Tile t lives in stage t % 4.  Step kt: issue tile kt+3 into the stage tile
+  // Tile t lives in stage t % STAGES.  Step kt: issue tile kt+STAGES-1 into the stage tile
   // kt-1 used (every wave finished reading it before the barrier that ended
   // step kt-1); block 0 = MFMAs of tile kt-1's second substep + fragment reads
   // of tile kt's first; block 1 = MFMAs of tile kt's first substep + reads of
   // its second; then wait for this wave's loads of tile kt+1 and barrier.
-  // The loop is unrolled by 4 so every stage array is a constant.
+  // The loop is unrolled by STAGES so every stage array is a constant.
   static_for<0, STAGES - 1>([&](auto ic) __attribute__((always_inline)) {
     constexpr int i = decltype(ic)::value;
     issue(i, stage(ic));
@@ -340,14 +351,15 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(const GemmParams p) {
       const int kt = kt0 + u;
       const char* cur = stage(uc);
       issue(kt + STAGES - 1, stage(std::integral_constant<int, u + STAGES - 1>{}));
-      read_frags(cur, 0, 0);
-      mma(1);
-      interleave<NMF, NRD, 0, LPS>();
-      __builtin_amdgcn_sched_barrier(0);
-      read_frags(cur, 1, 1);
-      mma(0);
-      interleave<NMF, NRD, 0, 0>();
-      __builtin_amdgcn_sched_barrier(0);
+      // block b: MFMAs of the substep before b (block 0: the previous tile's
+      // last one) while the fragments of substep b are read.
+      static_for<0, NSUB>([&](auto bc) __attribute__((always_inline)) {
+        constexpr int b = decltype(bc)::value;
+        read_frags(cur, b, b & 1);
+        mma((b + 1) & 1);
+        interleave<NMF, NRD, 0, b == 0 ? LPS : 0>();
+        __builtin_amdgcn_sched_barrier(0);
+      });
       wait_loads_barrier<(STAGES - 2) * LPS>();
     });
   }
@@ -389,8 +401,8 @@ hipError_t launch_tile(const GemmParams& p, hipStream_t s) {
 template <bool AKC, bool BKC, bool DUAL, int EPI, typename OutT>
 hipError_t launch_tile_shape(const GemmParams& p, int tile, hipStream_t s) {
   switch (tile) {
-    case TILE_256x256: return launch_tile<256, 256, 4, AKC, BKC, DUAL, EPI, OutT>(p, s);
-    case TILE_128x128: return launch_tile<128, 128, 4, AKC, BKC, DUAL, EPI, OutT>(p, s);
+    case TILE_256x256: return launch_tile<256, 256, TP_TILE_STAGES_256, AKC, BKC, DUAL, EPI, OutT>(p, s);
+    case TILE_128x128: return launch_tile<128, 128, TP_TILE_STAGES_128, AKC, BKC, DUAL, EPI, OutT>(p, s);
     default: return hipErrorInvalidValue;
   }
 }

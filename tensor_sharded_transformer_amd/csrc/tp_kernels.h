@@ -40,6 +40,15 @@
 // Pipelined tiled kernel (LDS-bound loads, four-stage ring) for the 256x256
 // and 128x128 tiles; TP_TILE_PIPE=0 keeps the register-staged two-stage
 // kernel for those tiles.
+#ifndef TP_TILE_BK
+#define TP_TILE_BK 64
+#endif
+#ifndef TP_TILE_STAGES_256
+#define TP_TILE_STAGES_256 2
+#endif
+#ifndef TP_TILE_STAGES_128
+#define TP_TILE_STAGES_128 2
+#endif
 #ifndef TP_TILE_PIPE
 #define TP_TILE_PIPE 1
 #endif
