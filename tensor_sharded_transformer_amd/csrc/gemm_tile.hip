@@ -371,6 +371,49 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(const GemmParams p) {
   // index is a compile-time constant.
   const int mrow = m0 + wm * WM + 4 * (lane >> 5);
   constexpr int TNO = DUAL ? TN / 2 : TN;  // output fragments per wave row
+
+  // Common case (a bf16 output with nothing else to write): each 32x32 tile
+  // goes through a per-wave LDS patch so the global stores are 16 bytes per
+  // lane along rows (two per tile) instead of 16 two-byte stores.
+  if constexpr (std::is_same<OutT, uint16_t>::value && (EPI == EPI_STORE || EPI == EPI_ACT || EPI == EPI_SWIGLU)) {
+    if (!p.C2 && !p.cpk && p.N % 8 == 0 && p.ldc % 8 == 0 && ((uintptr_t)p.C & 15) == 0) {
+      wait_loads_barrier<0>();                // every stage is idle (masked tail loads included)
+      constexpr int PITCH = 80;               // bytes per patch row: 64 + 16 of padding
+      char* patch = st0 + wave * 32 * PITCH;
+      static_for<0, TM>([&](auto ic) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
+        static_for<0, TNO>([&](auto jc) __attribute__((always_inline)) {
+          constexpr int j = decltype(jc)::value;
+          const int ncol = n0 + wn * (DUAL ? WN / 2 : WN) + j * 32;
+          const int n = ncol + (lane & 31);
+          float bias = 0.0f;
+          if constexpr (EPI == EPI_ACT) {
+            if (p.bias && n < p.N) bias = bf2f(reinterpret_cast<const uint16_t*>(p.bias)[n]);
+          }
+          static_for<0, 16>([&](auto rc) __attribute__((always_inline)) {
+            constexpr int r = decltype(rc)::value;
+            float v;
+            if constexpr (EPI == EPI_STORE) v = acc[i][j][r];
+            else if constexpr (EPI == EPI_ACT) v = act_fwd(p.act, acc[i][j][r] + bias);
+            else v = acc[i][j][r] * sigmoidf_(acc[i][j][r]) * acc[i][j + TNO][r];
+            const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            *reinterpret_cast<uint16_t*>(patch + row * PITCH + (lane & 31) * 2) = f2bf(v);
+          });
+          // one wave's LDS operations complete in order: the reads see the writes
+          static_for<0, 2>([&](auto qc) __attribute__((always_inline)) {
+            constexpr int q = decltype(qc)::value;
+            const int row = q * 16 + (lane >> 2);
+            const int cc = (lane & 3) * 8;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(patch + row * PITCH + cc * 2);
+            const int m = m0 + wm * WM + i * 32 + row;
+            if (m < p.M && ncol + cc < p.N)
+              *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.C) + (int64_t)m * p.ldc + ncol + cc) = v;
+          });
+        });
+      });
+      return;
+    }
+  }
   static_for<0, TM>([&](auto ic) __attribute__((always_inline)) {
     constexpr int i = decltype(ic)::value;
     static_for<0, TNO>([&](auto jc) __attribute__((always_inline)) {
