@@ -187,6 +187,47 @@ __global__ __launch_bounds__(KW * 64) void gemm_decode_kernel(const GemmParams p
   }
 
   // ---- epilogue ----------------------------------------------------------------
+  // Common case (a bf16 output and nothing else to write): the 32x32 tile
+  // goes through this wave's LDS weight tile (idle now) so the global stores
+  // are 16 bytes per lane (two per tile), row-major or packed.
+  if constexpr (std::is_same<OutT, uint16_t>::value && (EPI == EPI_STORE || EPI == EPI_ACT || EPI == EPI_SWIGLU)) {
+    if (!p.C2 && p.N % 8 == 0 && (p.cpk || (p.ldc % 8 == 0 && ((uintptr_t)p.C & 15) == 0))) {
+      constexpr int PITCH = 64;
+      static_assert(32 * PITCH <= NF * TB, "patch fits in the wave's weight tiles");
+      const int ncol = n0 + uj * 32;
+      const int nl = ncol + (lane & 31);
+      float bias = 0.0f;
+      if constexpr (EPI == EPI_ACT) {
+        if (p.bias && nl < p.N) bias = bf2f(reinterpret_cast<const uint16_t*>(p.bias)[nl]);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float v;
+        if constexpr (EPI == EPI_STORE) v = out[0][r];
+        else if constexpr (EPI == EPI_ACT) v = act_fwd(p.act, out[0][r] + bias);
+        else v = out[0][r] * sigmoidf_(out[0][r]) * out[NOUT - 1][r];
+        const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        *reinterpret_cast<uint16_t*>(my + row * PITCH + (lane & 31) * 2) = f2bf(v);
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int row = q * 16 + (lane >> 2);
+        const int cc = (lane & 3) * 8;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(my + row * PITCH + cc * 2);
+        const int m = ui * 32 + row;
+        const int nn = ncol + cc;
+        if (m < p.M && nn < p.N) {
+          if (p.cpk) {
+            const int64_t chunk = ((int64_t)(nn >> 4) * p.cpk_mt + (m >> 5)) * 64 + (m & 31) + ((nn >> 3) & 1) * 32;
+            reinterpret_cast<u32x4*>(p.cpk)[chunk] = v;
+          } else {
+            *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.C) + (int64_t)m * p.ldc + nn) = v;
+          }
+        }
+      }
+      return;
+    }
+  }
   const int n = n0 + uj * 32 + (lane & 31);
   if (n >= p.N) return;
   const int mrow = ui * 32 + 4 * (lane >> 5);
