@@ -395,7 +395,6 @@ tp_status tp_mlp_shard_fwd(const void* x, const void* w1_i, const void* w_up_i, 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* base = reinterpret_cast<char*>(ws);
   void* h = base;
-  const bool bf = dtype == TP_BF16;
 
   GemmParams p1 = base_params();
   p1.A0 = x;
@@ -421,9 +420,6 @@ tp_status tp_mlp_shard_fwd(const void* x, const void* w1_i, const void* w_up_i, 
     p1.cpk = base + L.pack2_off;
     p1.cpk_mt = T <= 32 ? 1 : 2;
   }
-  hipError_t e = run_gemm(dtype, p1, L.p1, sw ? tpk::GK_FWD_SWIGLU : tpk::GK_FWD_ACT, false, s);
-  if (e != hipSuccess) return hip_status(e, "tp_mlp_shard_fwd (column GEMM)");
-  (void)bf;
 
   GemmParams p2 = base_params();
   p2.A0 = h;
@@ -439,6 +435,9 @@ tp_status tp_mlp_shard_fwd(const void* x, const void* w1_i, const void* w_up_i, 
   p2.vecB = aligned16(w2_i) && d % 8 == 0;
   attach_split(p2, L.p2, base + L.cnt_off, base + L.part_off, base + L.pack2_off);
   p2.apk_ready = L.fuse_pack ? 1 : 0;
+
+  hipError_t e = run_gemm(dtype, p1, L.p1, sw ? tpk::GK_FWD_SWIGLU : tpk::GK_FWD_ACT, false, s);
+  if (e != hipSuccess) return hip_status(e, "tp_mlp_shard_fwd (column GEMM)");
   e = run_gemm(dtype, p2, L.p2, tpk::GK_FWD_STORE, out_dtype == TP_F32, s);
   return hip_status(e, "tp_mlp_shard_fwd (row GEMM)");
 }

@@ -421,7 +421,8 @@ void gemm_split_sizes(const GemmPlan& plan, int M, int N, int K, bool dual, size
     *pack_bytes = decode_pack_bytes(M, K);
     if (plan.splitk <= 1) return;
     const size_t tiles = decode_tiles(M, N);
-    *part_bytes = tiles * plan.splitk * (dual ? 2 : 1) * 16 * 64 * sizeof(float);
+    // split slots per tile: the plan's splits plus the slow-class strips' extra ones
+    *part_bytes = tiles * (plan.splitk + TP_DECODE_SLOW_EXTRA) * (dual ? 2 : 1) * 16 * 64 * sizeof(float);
     *n_tiles = tiles;
     return;
   }

@@ -63,101 +63,100 @@ constexpr int decode_lds_bytes() {
   return KW * NF * tile_bytes<NW>() + KW * MT * NF * 16 * 64 * 4;
 }
 
-template <int MT, bool DUAL, int EPI, typename OutT>
-__global__ __launch_bounds__(KW * 64) void gemm_decode_kernel(const GemmParams p) {
-  constexpr int NF = DUAL ? 2 * NW : NW;  // fragments per wave (gate then up)
-  constexpr int NACC = MT * NF;
-  constexpr int GCOLS = NW * 32;
+// One k-step of A (MT fragments) from the packed array.
+template <int MT>
+__device__ __forceinline__ void load_a(const u32x4* apk, int step, int lane, u32x4 (&a)[MT]) {
+#pragma unroll
+  for (int i = 0; i < MT; ++i) a[i] = apk[(step * MT + i) * 64 + lane];
+}
+
+// One k-step of MFMAs: the wave's weight slab goes through its private LDS
+// tiles (written row-major, read back transposed) into the B operands.
+template <int MT, bool DUAL>
+__device__ __forceinline__ void mma_step(char* my, int lane, const WFrag<DUAL ? 2 * NW : NW>& f,
+                                         const u32x4 (&a)[MT], f32x16 (&acc)[MT][DUAL ? 2 * NW : NW]) {
+  constexpr int NF = DUAL ? 2 * NW : NW;
   constexpr int TB = tile_bytes<NW>();
-  constexpr int UNITS = MT * NW;           // output fragments of the workgroup
-  __shared__ __attribute__((aligned(16))) char smem[decode_lds_bytes<MT, DUAL>()];
-  char* wt = smem;                                             // [KW][NF][TB] weight tiles
-  float* red = reinterpret_cast<float*>(smem + KW * NF * TB);  // [KW][NACC][16][64]
-
-  // Every parameter the kernel reads, loaded in one batch up front: each
-  // dependent round trip to the argument buffer costs about a microsecond.
-  __asm__ volatile("" ::"s"(p.B0), "s"(p.B1), "s"(p.apk), "s"(p.ldb), "s"(p.N), "s"(p.K0), "s"(p.M),
-                   "s"(p.splitk), "s"(p.partials), "s"(p.counters), "s"(p.C), "s"(p.ldc), "s"(p.cpk),
-                   "s"(p.cpk_mt));
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int nstrips = (p.N + GCOLS - 1) / GCOLS;
-  const int id = xcd_remap(blockIdx.x, gridDim.x);
-  const int split = id / nstrips;
-  const int strip = id - split * nstrips;
-  const int n0 = strip * GCOLS;
-
-  int s_begin, s_end;
-  split_range(p.K0, p.splitk, split, &s_begin, &s_end);
-  const int w_begin = s_begin + (s_end - s_begin) * wave / KW;
-  const int w_end = s_begin + (s_end - s_begin) * (wave + 1) / KW;
-  const int full_end = min(w_end, p.K0 / 16);  // steps whose weight rows all lie inside K
-
-  f32x16 acc[MT][NF];
 #pragma unroll
-  for (int i = 0; i < MT; ++i)
+  for (int mat = 0; mat < (DUAL ? 2 : 1); ++mat)
 #pragma unroll
-    for (int j = 0; j < NF; ++j)
+    for (int u = 0; u < NW; ++u) *reinterpret_cast<u32x4*>(my + w_lds_off<NW>(mat, u, lane)) = f.b[mat * NW + u];
+  bf16x8 bv[NF];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  for (int j = 0; j < NF; ++j) bv[j] = read_b_frag(my + j * TB, lane);
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    const bf16x8 av = __builtin_bit_cast(bf16x8, a[i]);
+#pragma unroll
+    for (int j = 0; j < NF; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv[j], acc[i][j], 0, 0, 0);
+  }
+}
 
+// The last, partial k-step of K (packed A is zero past K; weight rows past K
+// read as zero).
+template <int MT, bool DUAL>
+__device__ __forceinline__ void tail_step(const GemmParams& p, int n0, int step, int lane, char* my,
+                                          f32x16 (&acc)[MT][DUAL ? 2 * NW : NW]) {
+  WFrag<DUAL ? 2 * NW : NW> ft;
+  u32x4 at[MT];
+  load_w<NW, DUAL, true>(ft, p, step, n0, lane);
+  load_a<MT>(reinterpret_cast<const u32x4*>(p.apk), step, lane, at);
+  mma_step<MT, DUAL>(my, lane, ft, at, acc);
+}
+
+// Main loop of one wave over k-steps [w_begin, w_end): a ring of DEPTH steps
+// of weight and activation loads in flight.  The weights of the first DEPTH
+// steps are requested before `ready()` returns (it may wait for the packed
+// activations to be published); the activations only after.
+//
+// Each wave walks its steps from a rotated start, so the workgroups of a
+// launch do not all read the same weight rows at the same time (with
+// power-of-two row strides that lockstep concentrates on few DRAM banks).
+template <int MT, bool DUAL, typename Ready>
+__device__ __forceinline__ void ring_loop(const GemmParams& p, int n0, int w_begin, int w_end, int rot_seed, int lane,
+                                          char* my, f32x16 (&acc)[MT][DUAL ? 2 * NW : NW], Ready&& ready) {
+  constexpr int NF = DUAL ? 2 * NW : NW;
   const u32x4* apk = reinterpret_cast<const u32x4*>(p.apk);
-  auto load_a = [&](u32x4 (&a)[MT], int step) {
-#pragma unroll
-    for (int i = 0; i < MT; ++i) a[i] = apk[(step * MT + i) * 64 + lane];
-  };
-  char* my = wt + wave * NF * TB;
-  auto mma = [&](const WFrag<NF>& f, const u32x4 (&a)[MT]) {
-#pragma unroll
-    for (int mat = 0; mat < (DUAL ? 2 : 1); ++mat)
-#pragma unroll
-      for (int u = 0; u < NW; ++u) *reinterpret_cast<u32x4*>(my + w_lds_off<NW>(mat, u, lane)) = f.b[mat * NW + u];
-    bf16x8 bv[NF];
-#pragma unroll
-    for (int j = 0; j < NF; ++j) bv[j] = read_b_frag(my + j * TB, lane);
-#pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      const bf16x8 av = __builtin_bit_cast(bf16x8, a[i]);
-#pragma unroll
-      for (int j = 0; j < NF; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv[j], acc[i][j], 0, 0, 0);
-    }
-  };
-
-  // Each wave walks its steps from a rotated start, so the workgroups of a
-  // launch do not all read the same weight rows at the same time (with
-  // power-of-two row strides that lockstep concentrates on few DRAM banks).
+  const int full_end = min(w_end, p.K0 / 16);  // steps whose weight rows all lie inside K
   const int nw = full_end - w_begin;
   if (nw > 0) {
-    const int rot = (strip * 7 + wave * 3) % nw;
+    const int rot = rot_seed % nw;
     auto phys = [&](int it) {
       const int q = min(it, nw - 1) + rot;
       return w_begin + (q >= nw ? q - nw : q);
     };
     WFrag<NF> fr[DEPTH];
     u32x4 fa[DEPTH][MT];
-    static_for<0, DEPTH>([&](auto d) {
-      const int st = phys(d);
-      load_w<NW, DUAL, false>(fr[d], p, st, n0, lane);
-      load_a(fa[d], st);
-    });
+    static_for<0, DEPTH>([&](auto d) { load_w<NW, DUAL, false>(fr[d], p, phys(d), n0, lane); });
+    ready();
+    static_for<0, DEPTH>([&](auto d) { load_a<MT>(apk, phys(d), lane, fa[d]); });
     for (int it = 0; it < nw; it += DEPTH) {
       static_for<0, DEPTH>([&](auto d) {
-        if (it + (int)d < nw) mma(fr[d], fa[d]);
+        if (it + (int)d < nw) mma_step<MT, DUAL>(my, lane, fr[d], fa[d], acc);
         const int st = phys(it + DEPTH + (int)d);
         load_w<NW, DUAL, false>(fr[d], p, st, n0, lane);
-        load_a(fa[d], st);
+        load_a<MT>(apk, st, lane, fa[d]);
       });
     }
+  } else {
+    ready();
   }
-  if (w_end > full_end && w_end > w_begin) {  // the partial last k-step of K (packed A is zero past K)
-    WFrag<NF> ft;
-    u32x4 at[MT];
-    load_w<NW, DUAL, true>(ft, p, w_end - 1, n0, lane);
-    load_a(at, w_end - 1);
-    mma(ft, at);
-  }
+  if (w_end > full_end && w_end > w_begin) tail_step<MT, DUAL>(p, n0, w_end - 1, lane, my, acc);
+}
 
-  // ---- the waves meet in LDS; wave u owns output fragment u ----------------------
+// After a workgroup's main loops: the waves' accumulators meet in LDS, wave u
+// owns output fragment u (gate and up together) and sums it over the waves
+// in wave order, takes it through the split-K exchange (the last-arriving
+// split adds the splits in split order, so results are bitwise
+// reproducible) and stores it.
+template <int MT, bool DUAL, int EPI, typename OutT>
+__device__ __forceinline__ void decode_finish(const GemmParams& p, int strip, int split, int nsplit, int lane, int wave,
+                                              char* my, float* red, f32x16 (&acc)[MT][DUAL ? 2 * NW : NW]) {
+  constexpr int NF = DUAL ? 2 * NW : NW;
+  constexpr int NACC = MT * NF;
+  constexpr int UNITS = MT * NW;
+  constexpr int TB = tile_bytes<NW>();
+  const int n0 = strip * (NW * 32);
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -181,12 +180,10 @@ __global__ __launch_bounds__(KW * 64) void gemm_decode_kernel(const GemmParams p
       for (int r = 0; r < 16; ++r) out[o][r] += red[(((w * NACC) + a) * 16 + r) * 64 + lane];
   }
 
-  // ---- split-K across workgroups: each output fragment is its own tile -----
-  if (p.splitk > 1) {
-    if (!splitk_exchange<NOUT>(p, strip * UNITS + wave, split, lane, out)) return;
+  if (nsplit > 1) {
+    if (!splitk_exchange<NOUT>(p, strip * UNITS + wave, split, nsplit, lane, out)) return;
   }
 
-  // ---- epilogue ----------------------------------------------------------------
   // Common case (a bf16 output and nothing else to write): the 32x32 tile
   // goes through this wave's LDS weight tile (idle now) so the global stores
   // are 16 bytes per lane (two per tile), row-major or packed.
@@ -238,6 +235,90 @@ __global__ __launch_bounds__(KW * 64) void gemm_decode_kernel(const GemmParams p
   }
 }
 
+template <int MT, bool DUAL>
+__device__ __forceinline__ void zero_acc(f32x16 (&acc)[MT][DUAL ? 2 * NW : NW]) {
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+#pragma unroll
+    for (int j = 0; j < (DUAL ? 2 * NW : NW); ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+}
+
+// The k-steps of wave `wave` in split `split` of `nsplit`.
+__device__ __forceinline__ void wave_range(const GemmParams& p, int nsplit, int split, int wave, int* w_begin,
+                                           int* w_end) {
+  int s_begin, s_end;
+  split_range(p.K0, nsplit, split, &s_begin, &s_end);
+  *w_begin = s_begin + (s_end - s_begin) * wave / KW;
+  *w_end = s_begin + (s_end - s_begin) * (wave + 1) / KW;
+}
+
+// Workgroup tile i of a decode GEMM: split_base K splits of every column
+// strip (each XCD gets a contiguous block of those), then the extra splits of
+// the slow-class strips.
+__device__ __forceinline__ void decode_tile(const GemmParams& p, int nstrips, int i, int* strip, int* split,
+                                            int* nsplit) {
+  const int base_tiles = nstrips * p.split_base;
+  if (i < base_tiles) {
+    const int id = xcd_remap(i, base_tiles);
+    *split = id / nstrips;
+    *strip = id - *split * nstrips;
+  } else {
+    const int e = i - base_tiles;
+    *strip = p.slow_first + 8 * (e / p.slow_extra);
+    *split = p.split_base + e % p.slow_extra;
+  }
+  *nsplit = p.split_base + (p.slow_extra > 0 && (*strip & 7) == p.slow_first ? p.slow_extra : 0);
+}
+
+template <int MT, bool DUAL, int EPI, typename OutT>
+__global__ __launch_bounds__(KW * 64) void gemm_decode_kernel(const GemmParams p) {
+  constexpr int NF = DUAL ? 2 * NW : NW;
+  constexpr int TB = tile_bytes<NW>();
+  __shared__ __attribute__((aligned(16))) char smem[decode_lds_bytes<MT, DUAL>()];
+  // Every parameter the kernel reads, loaded in one batch up front: each
+  // dependent round trip to the argument buffer costs about a microsecond.
+  __asm__ volatile("" ::"s"(p.B0), "s"(p.B1), "s"(p.apk), "s"(p.ldb), "s"(p.N), "s"(p.K0), "s"(p.M),
+                   "s"(p.splitk), "s"(p.partials), "s"(p.counters), "s"(p.C), "s"(p.ldc), "s"(p.cpk),
+                   "s"(p.cpk_mt), "s"(p.split_base), "s"(p.slow_first), "s"(p.slow_extra));
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nstrips = (p.N + NW * 32 - 1) / (NW * 32);
+  int strip, split, nsplit;
+  decode_tile(p, nstrips, blockIdx.x, &strip, &split, &nsplit);
+  int w_begin, w_end;
+  wave_range(p, nsplit, split, wave, &w_begin, &w_end);
+  char* my = smem + wave * NF * TB;
+  float* red = reinterpret_cast<float*>(smem + KW * NF * TB);
+  f32x16 acc[MT][NF];
+  zero_acc<MT, DUAL>(acc);
+  ring_loop<MT, DUAL>(p, strip * NW * 32, w_begin, w_end, strip * 7 + wave * 3, lane, my, acc, [] {});
+  decode_finish<MT, DUAL, EPI, OutT>(p, strip, split, nsplit, lane, wave, my, red, acc);
+}
+
+// Column strips whose weight bytes have address bits 7..9 equal to 3 stream
+// about 30% slower than the others on this chip (measured per wave, for the
+// (d, 3584) gate/up and (3584, d) down shards alike): with split-K on, they
+// get extra K splits.  Fills split_base/slow_first/slow_extra/splitk and
+// returns the number of workgroups.
+constexpr uintptr_t SLOW_CLASS = 3;
+
+int decode_split(GemmParams& p, const GemmPlan& plan) {
+  const int nstrips = (p.N + DECODE_WCOLS - 1) / DECODE_WCOLS;
+  const uintptr_t b0 = reinterpret_cast<uintptr_t>(p.B0), b1 = p.B1 ? reinterpret_cast<uintptr_t>(p.B1) : b0;
+  p.split_base = plan.splitk;
+  p.slow_first = (int)((SLOW_CLASS - (b0 >> 7)) & 7);
+  const int nslow = p.slow_first < nstrips ? (nstrips - p.slow_first + 7) / 8 : 0;
+  // only while the grid stays within one workgroup per CU, and for splits of
+  // at most 4 (finer splits already keep the slow strips' tiles short)
+  const bool extra = plan.splitk > 1 && plan.splitk <= 4 && ((b0 ^ b1) >> 7 & 7) == 0 && nslow > 0 &&
+                     nstrips * plan.splitk + nslow * TP_DECODE_SLOW_EXTRA <= 256;
+  p.slow_extra = extra ? TP_DECODE_SLOW_EXTRA : 0;
+  p.splitk = plan.splitk + p.slow_extra;
+  return nstrips * plan.splitk + (extra ? nslow * p.slow_extra : 0);
+}
+
 template <int MT, bool DUAL, int EPI, typename OutT>
 hipError_t launch_decode_mt(const GemmParams& p, const GemmPlan& plan, hipStream_t s) {
   if (!p.apk_ready) {
@@ -249,8 +330,9 @@ hipError_t launch_decode_mt(const GemmParams& p, const GemmPlan& plan, hipStream
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int nstrips = (p.N + DECODE_WCOLS - 1) / DECODE_WCOLS;
-  hipLaunchKernelGGL((gemm_decode_kernel<MT, DUAL, EPI, OutT>), dim3(nstrips * plan.splitk), dim3(KW * 64), 0, s, p);
+  GemmParams pd = p;
+  const int nwg = decode_split(pd, plan);
+  hipLaunchKernelGGL((gemm_decode_kernel<MT, DUAL, EPI, OutT>), dim3(nwg), dim3(KW * 64), 0, s, pd);
   return hipGetLastError();
 }
 

@@ -81,6 +81,9 @@ struct GemmParams {
   int apk_ready;       // decode kernel: apk already holds A (skip the packing pass)
   void* cpk;           // if set: the bf16 output goes here, in the packed A
   int cpk_mt;          //   layout of a decode GEMM with cpk_mt 32-row tiles, instead of to C
+  int split_base;      // decode kernel: K splits of a column strip (splitk = split slots per tile) ...
+  int slow_first;      //   ... except strips slow_first + 8j (weight bytes of the slow address class),
+  int slow_extra;      //   which get slow_extra more
 };
 
 // Calls f(integral_constant<int, I>) for I = 0 .. N-1, so array indices in
@@ -128,11 +131,14 @@ __device__ __forceinline__ f32x4v splitk_load(__amdgpu_buffer_rsrc_t r, uint32_t
 // splits that are not last (they have nothing left to do).  Layout per tile:
 // [split][acc][quarter][lane][4 floats], so every store and load is 1 KB
 // contiguous per wave.
+// A tile may have fewer splits (nsplit) than the p.splitk slots it is laid
+// out with.
 template <int NACC>
-__device__ __forceinline__ bool splitk_exchange(const GemmParams& p, int t, int split, int lane, f32x16* acc) {
+__device__ __forceinline__ bool splitk_exchange(const GemmParams& p, int t, int split, int nsplit, int lane,
+                                                f32x16* acc) {
   constexpr uint32_t SPLIT_BYTES = NACC * 16 * 64 * 4;
   const float* base = p.partials + (int64_t)t * p.splitk * NACC * 16 * 64;
-  const __amdgpu_buffer_rsrc_t r = splitk_rsrc(base, SPLIT_BYTES * (uint32_t)p.splitk);
+  const __amdgpu_buffer_rsrc_t r = splitk_rsrc(base, SPLIT_BYTES * (uint32_t)nsplit);
 #pragma unroll
   for (int a = 0; a < NACC; ++a)
 #pragma unroll
@@ -145,7 +151,7 @@ __device__ __forceinline__ bool splitk_exchange(const GemmParams& p, int t, int 
   int prev = 0;
   if (lane == 0) prev = __hip_atomic_fetch_add(&p.counters[t], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   prev = __shfl(prev, 0);
-  if (prev != p.splitk - 1) return false;
+  if (prev != nsplit - 1) return false;
   // Every split has arrived: load the splits' values in batches of SB splits
   // (all accumulators of a batch issued together, about 32 loads per lane)
   // and add them in split order.
@@ -155,7 +161,7 @@ __device__ __forceinline__ bool splitk_exchange(const GemmParams& p, int t, int 
   for (int a = 0; a < NACC; ++a)
 #pragma unroll
     for (int e = 0; e < 16; ++e) sum[a][e] = 0.0f;
-  for (int s0 = 0; s0 < p.splitk; s0 += SB) {
+  for (int s0 = 0; s0 < nsplit; s0 += SB) {
     f32x4v v[SB][NACC][4];
 #pragma unroll
     for (int sb = 0; sb < SB; ++sb)
@@ -179,6 +185,10 @@ __device__ __forceinline__ bool splitk_exchange(const GemmParams& p, int t, int 
   for (int a = 0; a < NACC; ++a) acc[a] = sum[a];
   if (lane == 0) __hip_atomic_store(&p.counters[t], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return true;
+}
+template <int NACC>
+__device__ __forceinline__ bool splitk_exchange(const GemmParams& p, int t, int split, int lane, f32x16* acc) {
+  return splitk_exchange<NACC>(p, t, split, p.splitk, lane, acc);
 }
 
 // Element stores / loads of the output and side tensors.

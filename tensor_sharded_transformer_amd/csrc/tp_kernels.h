@@ -36,6 +36,11 @@
 #ifndef TP_DECODE_DEPTH
 #define TP_DECODE_DEPTH 4
 #endif
+// Extra K splits for the decode kernel's column strips of the slow
+// weight-address class (when split-K is on).
+#ifndef TP_DECODE_SLOW_EXTRA
+#define TP_DECODE_SLOW_EXTRA 4
+#endif
 
 // Pipelined tiled kernel (LDS-bound loads, four-stage ring) for the 256x256
 // and 128x128 tiles; TP_TILE_PIPE=0 keeps the register-staged two-stage

@@ -252,6 +252,54 @@ def test_decode_T64_shard(rank0_weights):
     assert torch.equal(y, y2)
 
 
+# ---------------------------------------------------------------------------
+# Decode-size forward (weight-streaming kernels, h written straight into the
+# row GEMM's packed activations): ragged T and d, every activation, both
+# output types.  Asking for the saved activations takes the per-element
+# epilogue instead of the staged one; the sums are the same, so the two agree
+# bit for bit.  Two calls in a row on one workspace with different x check
+# that nothing stale is read and that the counters are left zero.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("act", ["swiglu", "relu", "gelu", "none"])
+@pytest.mark.parametrize("T,d,ff_i", [(1, 1024, 512), (40, 1000, 384), (64, 2056, 1024)])
+def test_decode_step(act, T, d, ff_i):
+    seed = 7 * T + d + ff_i
+    w1 = W.normal((d, ff_i), 0.05, seed, 1)
+    wup = W.normal((d, ff_i), 0.05, seed, 2) if act == "swiglu" else None
+    w2 = W.normal((ff_i, d), 0.05, seed, 3)
+    xs = [W.normal((T, d), 1.0, seed, 4 + r) for r in range(2)]
+    dw1, dwup, dw2 = cuda(w1), None if wup is None else cuda(wup), cuda(w2)
+    o1, ou, o2 = O.to64(w1), None if wup is None else O.to64(wup), O.to64(w2)
+    ws = tp.new_workspace(tp.tp_mlp_shard_fwd_workspace(T, d, ff_i, tp.TP_BF16, act))
+    for out in (torch.bfloat16, torch.float32):
+        for r, x in enumerate(xs):
+            ref, _ = O.mlp_shard_fwd(O.to64(x), o1, ou, o2, act)
+            y = torch.empty(T, d, dtype=out, device="cuda")
+            tp.tp_mlp_shard_fwd(cuda(x), dw1, dwup, dw2, y, act, ws)
+            assert_close(y, ref, BF16_TOL, f"call {r}, out {out}")
+            y2, _ = fwd(cuda(x), dw1, dwup, dw2, act, out_dtype=out, saved=True)
+            assert torch.equal(y, y2), "staged and per-element epilogues differ"
+
+
+def test_decode_step_repeats(rank0_weights):
+    """The 70B-class decode shard, many back-to-back steps on one workspace
+    (each relies on the previous one having re-zeroed the split-K counters)."""
+    w = W.DECODE
+    x = W.mlp_input(w)
+    wt = rank0_weights
+    args = [cuda(wt["w1"]), cuda(wt["w_up"]), cuda(wt["w2"])]
+    ws = tp.new_workspace(tp.tp_mlp_shard_fwd_workspace(w.T, w.d, w.ff_i, tp.TP_BF16, "swiglu"))
+    xd = cuda(x)
+    ys = [torch.empty(w.T, w.d, dtype=torch.bfloat16, device="cuda") for _ in range(20)]
+    for y in ys:
+        tp.tp_mlp_shard_fwd(xd, *args, y, "swiglu", ws)
+    torch.cuda.synchronize()
+    ref, _ = O.mlp_shard_fwd(O.to64(x), O.to64(wt["w1"]), O.to64(wt["w_up"]), O.to64(wt["w2"]), "swiglu")
+    assert_close(ys[-1], ref, BF16_TOL, "last of 20")
+    for y in ys[:-1]:
+        assert torch.equal(y, ys[-1])
+
+
 def test_prefill_T4096_shard(rank0_weights):
     w = W.PREFILL
     x = W.mlp_input(w)
