@@ -7,8 +7,8 @@
 // matmuls across devices?", "Column split, then row split"):
 //   C[m, n] = epilogue( sum_k A(m, k) B(k, n) )   with fp32 accumulation.
 //
-// Design (one workgroup of 4 waves = one BM x BN output tile):
-//  * v_mfma_f32_32x32x16_bf16; each wave owns a (BM/2) x (BN/2) block of
+// Design (one workgroup of WGM x WGN waves = one BM x BN output tile):
+//  * v_mfma_f32_32x32x16_bf16; each wave owns a (BM/WGM) x (BN/WGN) block of
 //    32x32 accumulator tiles.
 //  * K advances in tiles of 32.  Operand tiles go from global memory straight
 //    into LDS (buffer_load_dwordx4 ... lds, no staging registers) through a
@@ -89,12 +89,13 @@ __device__ __forceinline__ void interleave() {
 }
 
 // One operand's tile of R rows (k-contiguous) or R columns (m/n-contiguous)
-// by 32 k-values.  Each of the 256 threads issues R/64 16-byte loads per
-// stage; load c of thread tid fills LDS slot c*256 + tid.  Every wave-wide
+// by TBK k-values.  Each of the NT threads issues NL 16-byte loads per
+// stage; load c of thread tid fills LDS slot c*NT + tid.  Every wave-wide
 // load lies inside one source matrix, so its buffer descriptor is uniform.
-template <int R, bool KC, bool DUAL>
+template <int R, bool KC, bool DUAL, int NT>
 struct OpTile {
-  static constexpr int NL = R * TBK / 2048;                  // loads per thread per stage
+  static constexpr int NL = R * TBK / (8 * NT);              // loads per thread per stage
+  static_assert(R * TBK % (8 * NT) == 0, "whole loads per thread");
   static constexpr int BYTES = R * TBK * 2;                  // LDS bytes per stage
   static constexpr int SW = KC ? 0 : (DUAL ? (R / 2 < 128 ? R / 2 : 128) : (R < 128 ? R : 128));
   static_assert(KC || SW == 64 || SW == 128, "sub-tile width");
@@ -107,8 +108,8 @@ struct OpTile {
   // Which source matrix (0 / 1) load c reads: the second half of a dual tile.
   static constexpr int src_of(int c) {
     if constexpr (!DUAL) return 0;
-    else if constexpr (KC) return c * 256 >= (R / 2) * KC_CHUNKS ? 1 : 0;
-    else return ((c * 256) / SUB_SLOTS) >= (R / SW) / 2 ? 1 : 0;
+    else if constexpr (KC) return c * NT >= (R / 2) * KC_CHUNKS ? 1 : 0;
+    else return ((c * NT) / SUB_SLOTS) >= (R / SW) / 2 ? 1 : 0;
   }
 
   // r0: first row (KC) or column (MN) of the tile in each source;
@@ -116,7 +117,7 @@ struct OpTile {
   __device__ __forceinline__ void setup(int tid, int r0, int extent, int64_t ld) {
 #pragma unroll
     for (int c = 0; c < NL; ++c) {
-      const int slot = c * 256 + tid;
+      const int slot = c * NT + tid;
       if constexpr (KC) {
         int row = slot / KC_CHUNKS;
         if (DUAL && row >= R / 2) row -= R / 2;
@@ -145,7 +146,7 @@ struct OpTile {
 #pragma unroll
     for (int c = 0; c < NL; ++c) {
       const uint32_t off = kidx[c] < kvalid ? voff[c] : OOB;
-      lds_void* dst = (lds_void*)(lds + (c * 256 + wave * 64) * 16);
+      lds_void* dst = (lds_void*)(lds + (c * NT + wave * 64) * 16);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(src_of(c) ? r1 : r0, dst, 16, off, 0, 0, 0);
     }
   }
@@ -162,7 +163,7 @@ __device__ __forceinline__ void frag_offsets(int first, int lane, int* o0, int* 
     *o0 = row * (TBK * 2);
     *o1 = (lane >> 5) ^ kc_swz(row);
   } else {
-    constexpr int SW = OpTile<R, KC, DUAL>::SW;
+    constexpr int SW = OpTile<R, KC, DUAL, 256>::SW;
     const int g = lane >> 4, i = lane & 15;
     const int col = first + (g & 1) * 16 + 4 * (i & 3);
     const int st = col / SW, cc = col % SW;
@@ -177,7 +178,7 @@ __device__ __forceinline__ bf16x8 read_frag(const char* tile, int o0, int o1, in
   if constexpr (KC) {
     return *reinterpret_cast<const bf16x8*>(tile + o0 + ((o1 ^ (2 * s)) << 4));
   } else {
-    constexpr int SW = OpTile<R, KC, DUAL>::SW;
+    constexpr int SW = OpTile<R, KC, DUAL, 256>::SW;
     const char* p = tile + o0 + s * 16 * (SW * 2);
     const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
     const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * SW * 2));
@@ -203,21 +204,25 @@ __device__ __forceinline__ void wait_loads_barrier() {
   else static_assert(N == 0, "add the vmcnt value here");
 }
 
-template <int BM, int BN, bool AKC, bool BKC, bool DUAL>
+template <int BM, int BN, bool AKC, bool BKC, bool DUAL, int NT>
 struct TileCfg {
-  using TA = OpTile<BM, AKC, false>;
-  using TB = OpTile<BN, BKC, DUAL>;
+  using TA = OpTile<BM, AKC, false, NT>;
+  using TB = OpTile<BN, BKC, DUAL, NT>;
   static constexpr int STAGE = TA::BYTES + TB::BYTES;
   static constexpr int LPS = TA::NL + TB::NL;  // loads per thread per stage
 };
 
-template <int BM, int BN, int STAGES, bool AKC, bool BKC, bool DUAL, int EPI, typename OutT>
-__global__ __launch_bounds__(256) void gemm_tile_kernel(const GemmParams p) {
-  constexpr int WM = BM / 2, WN = BN / 2;
+// WGM x WGN waves; wave (wm, wn) owns rows [wm*BM/WGM, +BM/WGM) and
+// columns [wn*BN/WGN, +BN/WGN) of the tile (per source in dual mode).
+template <int BM, int BN, int WGM, int WGN, int STAGES, bool AKC, bool BKC, bool DUAL, int EPI, typename OutT>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(const GemmParams p) {
+  constexpr int NT = 64 * WGM * WGN;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
   constexpr int TM = WM / 32, TN = WN / 32;
   constexpr int BNH = DUAL ? BN / 2 : BN;  // output columns per tile
+  static_assert(TM >= 1 && TN >= 1, "at least one 32x32 fragment per wave");
   static_assert(!DUAL || (TN % 2 == 0), "dual mode needs gate and up fragments per wave");
-  using Cfg = TileCfg<BM, BN, AKC, BKC, DUAL>;
+  using Cfg = TileCfg<BM, BN, AKC, BKC, DUAL, NT>;
   using TA = typename Cfg::TA;
   using TB = typename Cfg::TB;
   constexpr int STAGE = Cfg::STAGE;
@@ -242,14 +247,14 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(const GemmParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
+  const int wm = wave / WGN;
+  const int wn = wave % WGN;
 
   // ---- tile assignment (XCD-contiguous, M-grouped) -------------------------
   const int tiles_m = (p.M + BM - 1) / BM;
   const int tiles_n = (p.N + BNH - 1) / BNH;
   const int t = xcd_remap(blockIdx.x, gridDim.x);
-  constexpr int GROUP = 8;
+  constexpr int GROUP = TP_TILE_GROUP;
   const int per_group = GROUP * tiles_n;
   const int g = t / per_group;
   const int first_m = g * GROUP;
@@ -379,6 +384,7 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(const GemmParams p) {
     if (!p.C2 && !p.cpk && p.N % 8 == 0 && p.ldc % 8 == 0 && ((uintptr_t)p.C & 15) == 0) {
       wait_loads_barrier<0>();                // every stage is idle (masked tail loads included)
       constexpr int PITCH = 80;               // bytes per patch row: 64 + 16 of padding
+      static_assert(NT / 64 * 32 * PITCH <= STAGE, "patches fit in stage 0");
       char* patch = st0 + wave * 32 * PITCH;
       static_for<0, TM>([&](auto ic) __attribute__((always_inline)) {
         constexpr int i = decltype(ic)::value;
@@ -433,19 +439,21 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(const GemmParams p) {
   });
 }
 
-template <int BM, int BN, int STAGES, bool AKC, bool BKC, bool DUAL, int EPI, typename OutT>
+template <int BM, int BN, int WGM, int WGN, int STAGES, bool AKC, bool BKC, bool DUAL, int EPI, typename OutT>
 hipError_t launch_tile(const GemmParams& p, hipStream_t s) {
   constexpr int BNH = DUAL ? BN / 2 : BN;
   const int grid = ((p.M + BM - 1) / BM) * ((p.N + BNH - 1) / BNH);
-  hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, STAGES, AKC, BKC, DUAL, EPI, OutT>), dim3(grid), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WGM, WGN, STAGES, AKC, BKC, DUAL, EPI, OutT>), dim3(grid),
+                     dim3(64 * WGM * WGN), 0, s, p);
   return hipGetLastError();
 }
 
 template <bool AKC, bool BKC, bool DUAL, int EPI, typename OutT>
 hipError_t launch_tile_shape(const GemmParams& p, int tile, hipStream_t s) {
   switch (tile) {
-    case TILE_256x256: return launch_tile<256, 256, TP_TILE_STAGES_256, AKC, BKC, DUAL, EPI, OutT>(p, s);
-    case TILE_128x128: return launch_tile<128, 128, TP_TILE_STAGES_128, AKC, BKC, DUAL, EPI, OutT>(p, s);
+    case TILE_256x256:
+      return launch_tile<256, 256, TP_TILE_WGM_256, TP_TILE_WGN_256, TP_TILE_STAGES_256, AKC, BKC, DUAL, EPI, OutT>(p, s);
+    case TILE_128x128: return launch_tile<128, 128, 2, 2, TP_TILE_STAGES_128, AKC, BKC, DUAL, EPI, OutT>(p, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -57,6 +57,17 @@
 #ifndef TP_TILE_PIPE
 #define TP_TILE_PIPE 1
 #endif
+// Wave grid of the 256x256 tile (waves along M x along N).
+#ifndef TP_TILE_WGM_256
+#define TP_TILE_WGM_256 2
+#endif
+#ifndef TP_TILE_WGN_256
+#define TP_TILE_WGN_256 4
+#endif
+// M tiles per group of the tiled kernel's tile order (operand panel reuse in L2).
+#ifndef TP_TILE_GROUP
+#define TP_TILE_GROUP 8
+#endif
 
 namespace tpk {
 
