@@ -300,6 +300,37 @@ def test_decode_step_repeats(rank0_weights):
         assert torch.equal(y, ys[-1])
 
 
+def test_decode_step_graph_replay():
+    """The decode step captured as a HIP graph: several replays, with other
+    eager calls and synchronisations between them, each bit-identical to the
+    eager step (the step issues no memset; its split-K counters re-zero
+    themselves)."""
+    T, d, ff_i = 64, 2048, 1024
+    w1, wup, w2 = (cuda(W.normal(s, 0.05, 31, k)) for k, s in ((1, (d, ff_i)), (2, (d, ff_i)), (3, (ff_i, d))))
+    x = cuda(W.normal((T, d), 1.0, 31, 4))
+    x_other = cuda(W.normal((T, d), 1.0, 31, 5))
+    ws = tp.new_workspace(tp.tp_mlp_shard_fwd_workspace(T, d, ff_i, tp.TP_BF16, "swiglu"))
+    ws_other = tp.new_workspace(tp.tp_mlp_shard_fwd_workspace(T, d, ff_i, tp.TP_BF16, "swiglu"))
+    y = torch.empty(T, d, dtype=torch.bfloat16, device="cuda")
+    y_other = torch.empty_like(y)
+    tp.tp_mlp_shard_fwd(x, w1, wup, w2, y, "swiglu", ws)
+    torch.cuda.synchronize()
+    y_eager = y.clone()
+    ref, _ = O.mlp_shard_fwd(O.to64(x.cpu()), O.to64(w1.cpu()), O.to64(wup.cpu()), O.to64(w2.cpu()), "swiglu")
+    assert_close(y_eager, ref, BF16_TOL, "eager")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        tp.tp_mlp_shard_fwd(x, w1, wup, w2, y, "swiglu", ws)
+    for r in range(4):
+        y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager), f"replay {r}"
+        tp.tp_mlp_shard_fwd(x_other, w1, wup, w2, y_other, "swiglu", ws_other)
+        tp.tp_mlp_shard_fwd(x_other, w1, wup, w2, y_other, "swiglu", ws)   # the graph's workspace, eagerly
+        torch.cuda.synchronize()
+
+
 def test_prefill_T4096_shard(rank0_weights):
     w = W.PREFILL
     x = W.mlp_input(w)
