@@ -453,7 +453,8 @@ hipError_t launch_tile_shape(const GemmParams& p, int tile, hipStream_t s) {
   switch (tile) {
     case TILE_256x256:
       return launch_tile<256, 256, TP_TILE_WGM_256, TP_TILE_WGN_256, TP_TILE_STAGES_256, AKC, BKC, DUAL, EPI, OutT>(p, s);
-    case TILE_128x128: return launch_tile<128, 128, 2, 2, TP_TILE_STAGES_128, AKC, BKC, DUAL, EPI, OutT>(p, s);
+    case TILE_128x128:
+      return launch_tile<128, 128, TP_TILE_WGM_128, TP_TILE_WGN_128, TP_TILE_STAGES_128, AKC, BKC, DUAL, EPI, OutT>(p, s);
     default: return hipErrorInvalidValue;
   }
 }

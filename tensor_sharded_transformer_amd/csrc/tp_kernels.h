@@ -64,6 +64,13 @@
 #ifndef TP_TILE_WGN_256
 #define TP_TILE_WGN_256 4
 #endif
+// Wave grid of the 128x128 tile.
+#ifndef TP_TILE_WGM_128
+#define TP_TILE_WGM_128 2
+#endif
+#ifndef TP_TILE_WGN_128
+#define TP_TILE_WGN_128 2
+#endif
 // M tiles per group of the tiled kernel's tile order (operand panel reuse in L2).
 #ifndef TP_TILE_GROUP
 #define TP_TILE_GROUP 8

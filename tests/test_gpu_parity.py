@@ -300,6 +300,37 @@ def test_decode_step_repeats(rank0_weights):
         assert torch.equal(y, ys[-1])
 
 
+@pytest.mark.parametrize("shift_gate,shift_up", [(0, 0), (128, 128), (640, 640), (384, 0), (896, 256)])
+def test_decode_weight_address_classes(shift_gate, shift_up):
+    """Decode GEMMs whose weight bytes start at different 128-byte offsets:
+    the extra K splits land on other column strips (or are off when gate and
+    up disagree); every case matches the oracle, and two calls agree bit for
+    bit."""
+    T, d, ff_i = 64, 2048, 1024
+    w1 = W.normal((d, ff_i), 0.05, 41, 1)
+    wup = W.normal((d, ff_i), 0.05, 41, 2)
+    x = W.normal((T, d), 1.0, 41, 3)
+
+    def at_offset(w, shift):
+        # the weight rows start `shift` bytes into a larger buffer (row stride unchanged)
+        n = w.numel() + 4096
+        buf = torch.zeros(n, dtype=torch.bfloat16, device="cuda")
+        view = buf[shift // 2: shift // 2 + w.numel()].view(w.shape)
+        view.copy_(cuda(w))
+        return view
+
+    g, u = at_offset(w1, shift_gate), at_offset(wup, shift_up)
+    assert (g.data_ptr() - u.data_ptr()) % 128 == (shift_gate - shift_up) % 128
+    ws = tp.new_workspace(tp.tp_col_linear_workspace(T, d, ff_i, tp.TP_BF16, "swiglu"))
+    h = torch.empty(T, ff_i, dtype=torch.bfloat16, device="cuda")
+    tp.tp_col_linear(cuda(x), g, u, None, h, "swiglu", ws)
+    ref = O.col_linear(O.to64(x), O.to64(w1), O.to64(wup), None, "swiglu")
+    assert_close(h, ref, BF16_TOL, f"gate +{shift_gate} B, up +{shift_up} B")
+    h2 = torch.empty_like(h)
+    tp.tp_col_linear(cuda(x), g, u, None, h2, "swiglu", ws)
+    assert torch.equal(h, h2)
+
+
 def test_decode_step_graph_replay():
     """The decode step captured as a HIP graph: several replays, with other
     eager calls and synchronisations between them, each bit-identical to the
