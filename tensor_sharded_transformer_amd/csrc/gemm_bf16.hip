@@ -407,7 +407,13 @@ GemmPlan plan_gemm(int M, int N, int K, bool dual, bool fwd_layout, bool vec_ok,
     plan.splitk = allow_split ? split : 1;
     return plan;
   }
-  plan.tile = tiles_for(256, 256) >= CUS ? TILE_256x256 : TILE_128x128;
+  // Tile size by estimated time: rounds of 256 CUs times the time of one tile.
+  // A 256x256 tile (8 waves) has 4x the work of a 128x128 one (4 waves) and
+  // runs at ~1.24 vs ~1.0 PFLOP/s, so it takes ~3.2x as long.
+  const int r256 = (tiles_for(256, 256) + CUS - 1) / CUS;
+  const int r128 = (tiles_for(128, 128) + CUS - 1) / CUS;
+  plan.tile = TP_TILE_COST ? (r256 * 32 < r128 * 10 ? TILE_256x256 : TILE_128x128)
+                           : (tiles_for(256, 256) >= CUS ? TILE_256x256 : TILE_128x128);
   plan.splitk = 1;
   return plan;
 }

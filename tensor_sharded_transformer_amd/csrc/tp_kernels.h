@@ -71,6 +71,11 @@
 #ifndef TP_TILE_WGN_128
 #define TP_TILE_WGN_128 2
 #endif
+// Tiled kernel: choose the tile size by estimated time (0: 256x256 whenever
+// it gives a full round).
+#ifndef TP_TILE_COST
+#define TP_TILE_COST 1
+#endif
 // M tiles per group of the tiled kernel's tile order (operand panel reuse in L2).
 #ifndef TP_TILE_GROUP
 #define TP_TILE_GROUP 8
