@@ -14,7 +14,9 @@ The same JSON line carries:
                 HIP events on its stream: algorithmic bytes / launch time vs 8 TB/s;
   rows          the other hot-path rows: prefill shard (T=4096), GQA
                 projections (T=4096 and 64), the shard backward (T=2048,
-                d=4096, ff_i=1792) and the fp32 sum of partials;
+                d=4096, ff_i=1792), the fp32 sum of partials and the
+                sequence-parallel boundary (a rank's rows of the sum +
+                residual, then RMSNorm);
   cpu_baseline  the fp64 oracle computing the same decode step on the host.
 
     python bench.py [--steps K] [--warmup W] [--rows all|none|prefill,gqa,bwd,sum,calib]
@@ -189,6 +191,19 @@ def main() -> int:
         rows["sum_partials_dx_p8_T2048"] = {"us": round(t_ * 1e3, 2), "GB/s": round(b_ / t_ / 1e6, 1),
                                             "frac_hbm": round(b_ / t_ / 1e6 / HBM_PEAK_GBS, 4)}
         del parts
+        # sequence-parallel boundary at prefill size: rank 3's 512 rows of 8 partials
+        # (4096 x 8192 bf16) + residual, then RMSNorm
+        Ts, ps = W.PREFILL.T, 8
+        parts = [torch.randn(Ts, d, device=dev).to(torch.bfloat16) for _ in range(ps)]
+        res = torch.randn(Ts // ps, d, device=dev).to(torch.bfloat16)
+        nw = torch.randn(d, device=dev).to(torch.bfloat16)
+        r_out = torch.empty_like(res)
+        yn = torch.empty_like(res)
+        t_ = time_gpu(lambda i: tp.tp_rs_residual_rmsnorm(parts, 3, None, res, nw, 1e-5, r_out, yn), steps_r, 5)
+        b_ = (ps * (Ts // ps) * d + 3 * (Ts // ps) * d + d) * 2
+        rows["sp_rs_residual_rmsnorm_T4096_p8"] = {"us": round(t_ * 1e3, 2), "GB/s": round(b_ / t_ / 1e6, 1),
+                                                   "frac_hbm": round(b_ / t_ / 1e6 / HBM_PEAK_GBS, 4)}
+        del parts, res, r_out, yn
 
     if "prefill" in want:
         xp = W.mlp_input(W.PREFILL).to(dev)

@@ -164,6 +164,26 @@ tp_status tp_mlp_shard_bwd(const void* x, const void* w1_i, const void* w_up_i, 
 tp_status tp_partial_sum(const void* const* z, int p, const void* bias, void* y, int64_t T,
                          int64_t N, tp_dtype in_dtype, tp_dtype out_dtype, tp_stream stream);
 
+/* Sequence-parallel boundary, one rank's share: with sequence parallelism the
+ * block's all-reduce becomes a reduce-scatter + all-gather ([KL] "With
+ * Sequence Parallelism ... each AllReduce becomes a ReduceScatter +
+ * AllGather"), and the summed output feeds the residual add and the following
+ * normalization ([FFN] "One collective").  Rank `rank` owns rows
+ * [rank*T/p, (rank+1)*T/p) of the T x N partials; for each owned row r (row
+ * R = rank*T/p + r of the partials):
+ *   s[r]            = residual_in[r] + sum_i z[i][R] (ascending i) + bias     (fp32)
+ *   residual_out[r] = s[r]
+ *   y[r]            = s[r] / sqrt(mean_j s[r][j]^2 + eps) * norm_w           (RMSNorm)
+ * The norm is taken over the fp32 sum (before residual_out is rounded).
+ * z: host array of p device pointers, each (T, N) in in_dtype; bias (N) in
+ * in_dtype or NULL; residual_in, residual_out, y: (T/p, N) in out_dtype;
+ * norm_w (N) in out_dtype (all device).  1 <= p <= 64, 0 <= rank < p,
+ * T % p == 0 (equal shares), N <= 32768, eps >= 0.  residual_out may alias
+ * residual_in; y may not alias anything. */
+tp_status tp_rs_residual_rmsnorm(const void* const* z, int p, int rank, const void* bias, const void* residual_in,
+                                 const void* norm_w, float eps, void* residual_out, void* y, int64_t T, int64_t N,
+                                 tp_dtype in_dtype, tp_dtype out_dtype, tp_stream stream);
+
 /* Zero-fills `bytes` of device memory ws on `stream` with a kernel (no
  * memset node, so it is safe to capture in a graph). */
 tp_status tp_workspace_init(void* ws, size_t bytes, tp_stream stream);

@@ -35,6 +35,8 @@ Readings where the pages are silent (also listed with the design notes):
     rejected ([FFN] partitions 4d into N chunks of size 4d/N).
   * Column-parallel bias: each shard adds its own slice; row-parallel bias:
     added once after the sum ([MLX]).
+  * The normalization after the block's sum is RMSNorm with a learned scale
+    and a caller-given epsilon, taken over the fp32/float64 sum.
 
 Every function below has a pin in ``tests/test_oracle_pins.py`` that checks it
 against something other than itself (the pages' worked example, exact rational
@@ -206,6 +208,30 @@ def partial_sum(zs: Sequence[np.ndarray], bias=None) -> np.ndarray:
     if bias is not None:
         y = y + to64(bias)[None, :]
     return y
+
+
+def rs_residual_rmsnorm(zs: Sequence[np.ndarray], rank: int, residual, norm_w, eps: float, bias=None):
+    """One rank's share of the sequence-parallel block boundary.
+
+    [KL] sequence-parallelism paragraph (with sequence parallelism each
+    all-reduce becomes a reduce-scatter + all-gather: rank `rank` ends up
+    with the sum over its T/p contiguous rows only) and [FFN] "One
+    collective" (the summed output goes to the residual add and the
+    following normalization).  The normalization is read as RMSNorm with a
+    learned scale (the pages name a Llama-style block but not the norm):
+    y = s / sqrt(mean(s^2) + eps) * norm_w, over the summed row s.
+    Returns (s, y) for the rank's rows; the partials are summed in order,
+    then the bias (once), then the residual is added."""
+    p = len(zs)
+    T = zs[0].shape[0]
+    if T % p != 0:
+        raise ValueError(f"{T} rows do not split into {p} equal shares")
+    rows = T // p
+    r0 = rank * rows
+    part = [to64(z)[r0:r0 + rows] for z in zs]
+    s = partial_sum(part, bias) + to64(residual)
+    y = s / np.sqrt(np.mean(s * s, axis=1, keepdims=True) + eps) * to64(norm_w)[None, :]
+    return s, y
 
 
 # ---------------------------------------------------------------------------

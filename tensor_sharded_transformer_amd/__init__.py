@@ -23,6 +23,7 @@ from .binding import (  # noqa: F401
     tp_partial_sum,
     tp_row_linear_partial,
     tp_row_linear_partial_workspace,
+    tp_rs_residual_rmsnorm,
     tp_shard_range,
     tp_workspace_init,
 )

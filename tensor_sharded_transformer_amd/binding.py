@@ -49,6 +49,8 @@ SIGNATURES = {
     "tp_mlp_shard_bwd": (c_int, [c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_sz, c_i64, c_i64, c_i64,
                                  c_int, c_int, c_p]),
     "tp_partial_sum": (c_int, [ctypes.POINTER(c_p), c_int, c_p, c_p, c_i64, c_i64, c_int, c_int, c_p]),
+    "tp_rs_residual_rmsnorm": (c_int, [ctypes.POINTER(c_p), c_int, c_int, c_p, c_p, c_p, ctypes.c_float, c_p, c_p,
+                                       c_i64, c_i64, c_int, c_int, c_p]),
     "tp_workspace_init": (c_int, [c_p, c_sz, c_p]),
     "tp_shard_range": (c_int, [c_i64, c_int, c_int, ctypes.POINTER(c_i64), ctypes.POINTER(c_i64)]),
     "tp_gqa_shard": (c_int, [c_int, c_int, c_int, c_int, c_int, ctypes.POINTER(c_i64), ctypes.POINTER(c_i64),
@@ -221,6 +223,25 @@ def tp_partial_sum(zs: Sequence[torch.Tensor], bias, y):
         _shape(z, (T, N), "z")
     arr = (c_p * len(zs))(*[_ptr(z) for z in zs])
     _check(load().tp_partial_sum(arr, len(zs), _ptr(bias), _ptr(y), T, N, _dt(zs[0]), _dt(y), _stream()))
+    return y
+
+
+def tp_rs_residual_rmsnorm(zs: Sequence[torch.Tensor], rank: int, bias, residual_in, norm_w, eps: float,
+                           residual_out, y):
+    """Rank `rank`'s rows of sum(zs) (+ bias) + residual_in -> residual_out, and
+    their RMSNorm (scale norm_w, epsilon eps) -> y."""
+    p = len(zs)
+    T, N = zs[0].shape
+    for z in zs:
+        _shape(z, (T, N), "z")
+    rows = T // p if p else 0
+    _shape(residual_in, (rows, N), "residual_in")
+    _shape(residual_out, (rows, N), "residual_out")
+    _shape(y, (rows, N), "y")
+    _shape(norm_w, (N,), "norm_w")
+    arr = (c_p * p)(*[_ptr(z) for z in zs])
+    _check(load().tp_rs_residual_rmsnorm(arr, p, rank, _ptr(bias), _ptr(residual_in), _ptr(norm_w), eps,
+                                         _ptr(residual_out), _ptr(y), T, N, _dt(zs[0]), _dt(y), _stream()))
     return y
 
 

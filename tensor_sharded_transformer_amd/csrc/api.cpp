@@ -364,6 +364,33 @@ tp_status tp_partial_sum(const void* const* z, int p, const void* bias, void* y,
                     "tp_partial_sum");
 }
 
+// ---- sequence-parallel boundary ---------------------------------------------------------
+tp_status tp_rs_residual_rmsnorm(const void* const* z, int p, int rank, const void* bias, const void* residual_in,
+                                 const void* norm_w, float eps, void* residual_out, void* y, int64_t T, int64_t N,
+                                 tp_dtype in_dtype, tp_dtype out_dtype, tp_stream stream) {
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype))
+    return fail(TP_ERR_DTYPE, "tp_rs_residual_rmsnorm: unknown dtype");
+  if (p < 1 || p > 64) return fail(TP_ERR_SHAPE, "tp_rs_residual_rmsnorm: need 1 <= p <= 64 (got %d)", p);
+  if (rank < 0 || rank >= p) return fail(TP_ERR_SHAPE, "tp_rs_residual_rmsnorm: rank %d outside [0, %d)", rank, p);
+  if (!dim_ok(T) || !dim_ok(N) || !prod_ok(T, N)) return fail(TP_ERR_SHAPE, "tp_rs_residual_rmsnorm: sizes out of range");
+  if (T % p != 0)
+    return fail(TP_ERR_SHAPE, "tp_rs_residual_rmsnorm: T=%lld is not divisible into %d equal row shares",
+                (long long)T, p);
+  if (N > tpk::RS_NORM_MAX_N)
+    return fail(TP_ERR_UNSUPPORTED, "tp_rs_residual_rmsnorm: N=%lld > %lld", (long long)N,
+                (long long)tpk::RS_NORM_MAX_N);
+  if (!(eps >= 0.0f)) return fail(TP_ERR_SHAPE, "tp_rs_residual_rmsnorm: eps must be >= 0");
+  if (T == 0 || N == 0) return TP_OK;
+  if (!z || !residual_in || !norm_w || !residual_out || !y)
+    return fail(TP_ERR_NULL, "tp_rs_residual_rmsnorm: null z, residual_in, norm_w, residual_out or y");
+  for (int i = 0; i < p; ++i)
+    if (!z[i]) return fail(TP_ERR_NULL, "tp_rs_residual_rmsnorm: z[%d] is null", i);
+  return hip_status(tpk::rs_residual_rmsnorm(z, p, rank, bias, residual_in, norm_w, eps, residual_out, y, T, N,
+                                             in_dtype == TP_BF16, out_dtype == TP_BF16,
+                                             reinterpret_cast<hipStream_t>(stream)),
+                    "tp_rs_residual_rmsnorm");
+}
+
 // ---- MLP shard forward ------------------------------------------------------------
 size_t tp_mlp_shard_fwd_workspace(int64_t T, int64_t d, int64_t ff_i, tp_dtype dtype, tp_act act) {
   if (!valid_dtype(dtype) || !valid_act(act) || !dim_ok(T) || !dim_ok(d) || !dim_ok(ff_i)) return 0;

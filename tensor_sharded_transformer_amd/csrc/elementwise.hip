@@ -10,6 +10,9 @@
 //
 // All three are HBM-bound streams: each thread moves 16-byte vectors, the grid
 // is sized to a few waves of workgroups per CU and loops grid-stride.
+#include <algorithm>
+#include <type_traits>
+
 #include "tp_kernels.h"
 #include "tp_device.h"
 
@@ -171,6 +174,166 @@ hipError_t partial_sum(const void* const* z, int p, const void* bias, void* y, i
     hipLaunchKernelGGL((partial_sum_kernel<false, true>), dim3(grid), dim3(256), 0, s, a, p, bias, y, T, N, vec);
   else
     hipLaunchKernelGGL((partial_sum_kernel<false, false>), dim3(grid), dim3(256), 0, s, a, p, bias, y, T, N, vec);
+  return hipGetLastError();
+}
+
+// ---- sequence-parallel boundary: reduce-scatter share + residual add + RMSNorm -------
+// One workgroup per owned row, sized to the row (up to 1024 threads, one
+// 8-column group each) so all of a row's loads are in flight together.  Pass 1 sums the p partials (ascending i), the
+// bias and the residual in fp32, keeps the row in LDS, writes residual_out and
+// accumulates the sum of squares; the block reduces it; pass 2 scales the LDS
+// row by 1/sqrt(mean + eps) and norm_w.  8 columns per thread per step (16-byte
+// loads) when every row start is 16-byte aligned, else one.
+template <typename InT, typename OutT>
+__device__ __forceinline__ float ld1(const void* p, int64_t i) {
+  if constexpr (std::is_same<InT, uint16_t>::value) return bf2f(reinterpret_cast<const uint16_t*>(p)[i]);
+  else return reinterpret_cast<const float*>(p)[i];
+}
+template <typename T>
+__device__ __forceinline__ void st1(void* p, int64_t i, float v) {
+  if constexpr (std::is_same<T, uint16_t>::value) reinterpret_cast<uint16_t*>(p)[i] = f2bf(v);
+  else reinterpret_cast<float*>(p)[i] = v;
+}
+// 8 consecutive values from a 16-byte aligned address (bf16: one 16-byte load; f32: two)
+template <typename T>
+__device__ __forceinline__ void ld8(const void* p, int64_t i, float (&v)[8]) {
+  if constexpr (std::is_same<T, uint16_t>::value) {
+    const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p) + i);
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = bf2f((uint16_t)(ww[q] & 0xffffu));
+      v[2 * q + 1] = bf2f((uint16_t)(ww[q] >> 16));
+    }
+  } else {
+    const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p) + i);
+    const float4 b = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(p) + i + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+template <typename T>
+__device__ __forceinline__ void st8(void* p, int64_t i, const float (&v)[8]) {
+  if constexpr (std::is_same<T, uint16_t>::value) {
+    uint4 o;
+    o.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+    o.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+    o.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
+    o.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p) + i) = o;
+  } else {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(p) + i) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(p) + i + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
+template <typename InT, typename OutT>
+__global__ __launch_bounds__(1024) void rs_norm_kernel(const SumArgs a, int p, int64_t row0, const void* bias,
+                                                      const void* res_in, const void* norm_w, float eps,
+                                                      void* res_out, void* y, int64_t N, int vec) {
+  extern __shared__ float srow[];  // the row's fp32 sums
+  __shared__ float wsum[16];
+  const int nt = blockDim.x;
+  const int64_t r = blockIdx.x;    // owned row
+  const int64_t zrow = (row0 + r) * N, orow = r * N;
+  float ss = 0.f;
+  if (vec) {
+    for (int64_t c = threadIdx.x * 8; c < N; c += nt * 8) {
+      float s[8], t[8];
+      ld8<OutT>(res_in, orow + c, s);
+      for (int i = 0; i < p; ++i) {
+        ld8<InT>(a.z[i], zrow + c, t);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e] += t[e];
+      }
+      if (bias) {
+        ld8<InT>(bias, c, t);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e] += t[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        srow[c + e] = s[e];
+        ss += s[e] * s[e];
+      }
+      st8<OutT>(res_out, orow + c, s);
+    }
+  } else {
+    for (int64_t c = threadIdx.x; c < N; c += nt) {
+      float s = ld1<OutT, OutT>(res_in, orow + c);
+      for (int i = 0; i < p; ++i) s += ld1<InT, InT>(a.z[i], zrow + c);
+      if (bias) s += ld1<InT, InT>(bias, c);
+      srow[c] = s;
+      ss += s * s;
+      st1<OutT>(res_out, orow + c, s);
+    }
+  }
+  // block sum of squares: wave shuffles, then the four wave totals in wave order
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = ss;
+  __syncthreads();  // also orders the srow writes before pass 2
+  float tot = 0.f;
+  for (int w = 0; w < nt / 64; ++w) tot += wsum[w];  // in wave order
+  const float inv = 1.0f / sqrtf(tot / (float)N + eps);
+  if (vec) {
+    for (int64_t c = threadIdx.x * 8; c < N; c += nt * 8) {
+      float w[8], o[8];
+      ld8<OutT>(norm_w, c, w);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = srow[c + e] * inv * w[e];
+      st8<OutT>(y, orow + c, o);
+    }
+  } else {
+    for (int64_t c = threadIdx.x; c < N; c += nt) st1<OutT>(y, orow + c, srow[c] * inv * ld1<OutT, OutT>(norm_w, c));
+  }
+}
+
+hipError_t rs_residual_rmsnorm(const void* const* z, int p, int rank, const void* bias, const void* residual_in,
+                               const void* norm_w, float eps, void* residual_out, void* y, int64_t T, int64_t N,
+                               bool in_bf16, bool out_bf16, hipStream_t s) {
+  const int64_t rows = T / p;
+  if (rows == 0 || N == 0) return hipSuccess;
+  SumArgs a{};
+  bool aligned = N % 8 == 0;
+  for (int i = 0; i < p; ++i) {
+    a.z[i] = z[i];
+    aligned = aligned && (uintptr_t)z[i] % 16 == 0;
+  }
+  for (const void* q : {residual_in, norm_w, (const void*)residual_out, (const void*)y, bias})
+    aligned = aligned && (q == nullptr || (uintptr_t)q % 16 == 0);
+  const int vec = aligned ? 1 : 0;
+  const size_t lds = (size_t)N * sizeof(float);
+  const int64_t groups = vec ? (N + 7) / 8 : N;  // work items of a row
+  const int nt = (int)std::min<int64_t>(1024, std::max<int64_t>(64, (groups + 63) / 64 * 64));
+  const int64_t row0 = (int64_t)rank * rows;
+  if (lds > 48 * 1024) {  // more dynamic LDS than the default limit: raise it for this kernel
+    hipError_t e = hipSuccess;
+    if (in_bf16 && out_bf16)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(rs_norm_kernel<uint16_t, uint16_t>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    else if (in_bf16)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(rs_norm_kernel<uint16_t, float>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    else if (out_bf16)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(rs_norm_kernel<float, uint16_t>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    else
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(rs_norm_kernel<float, float>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  if (in_bf16 && out_bf16)
+    hipLaunchKernelGGL((rs_norm_kernel<uint16_t, uint16_t>), dim3(rows), dim3(nt), lds, s, a, p, row0, bias,
+                       residual_in, norm_w, eps, residual_out, y, N, vec);
+  else if (in_bf16)
+    hipLaunchKernelGGL((rs_norm_kernel<uint16_t, float>), dim3(rows), dim3(nt), lds, s, a, p, row0, bias,
+                       residual_in, norm_w, eps, residual_out, y, N, vec);
+  else if (out_bf16)
+    hipLaunchKernelGGL((rs_norm_kernel<float, uint16_t>), dim3(rows), dim3(nt), lds, s, a, p, row0, bias,
+                       residual_in, norm_w, eps, residual_out, y, N, vec);
+  else
+    hipLaunchKernelGGL((rs_norm_kernel<float, float>), dim3(rows), dim3(nt), lds, s, a, p, row0, bias, residual_in,
+                       norm_w, eps, residual_out, y, N, vec);
   return hipGetLastError();
 }
 

@@ -149,6 +149,12 @@ hipError_t gemm_f32(const GemmParams& p, GemmKind kind, hipStream_t s);
 hipError_t act_inplace(void* h, const void* up, int64_t n_elems, bool bf16, int act, hipStream_t s);
 hipError_t partial_sum(const void* const* z, int p, const void* bias, void* y, int64_t T, int64_t N,
                        bool in_bf16, bool out_bf16, hipStream_t s);
+// Rows [rank*T/p, +T/p) of sum_i z[i] (+ bias) + residual -> residual_out, and
+// their RMSNorm (scale norm_w) -> y.  N <= RS_NORM_MAX_N.
+constexpr int64_t RS_NORM_MAX_N = 32768;
+hipError_t rs_residual_rmsnorm(const void* const* z, int p, int rank, const void* bias, const void* residual_in,
+                               const void* norm_w, float eps, void* residual_out, void* y, int64_t T, int64_t N,
+                               bool in_bf16, bool out_bf16, hipStream_t s);
 hipError_t zero_fill(void* ws, size_t bytes, hipStream_t s);
 
 }  // namespace tpk

@@ -150,6 +150,23 @@ def test_partial_sum_validation(lib):
     assert f(arr, 2, None, FAKE, 0, 8, 0, 1, None) == OK             # T == 0
 
 
+def test_rs_residual_rmsnorm_validation(lib):
+    f = lib.tp_rs_residual_rmsnorm
+    arr = (ctypes.c_void_p * 2)(0x1000, 0x2000)
+    args = (None, FAKE, FAKE, ctypes.c_float(1e-5), FAKE, FAKE)
+    assert f(arr, 2, 0, *args, 8, 64, 7, 0, None) == DTYPE
+    assert f(arr, 0, 0, *args, 8, 64, 0, 0, None) == SHAPE          # p = 0
+    assert f(arr, 2, 2, *args, 8, 64, 0, 0, None) == SHAPE          # rank out of range
+    assert f(arr, 2, -1, *args, 8, 64, 0, 0, None) == SHAPE
+    assert f(arr, 2, 0, *args, 7, 64, 0, 0, None) == SHAPE          # 7 rows, 2 shares
+    assert f(arr, 2, 0, *args, 8, 40000, 0, 0, None) == 6           # N above the row limit: unsupported
+    assert f(arr, 2, 0, None, FAKE, FAKE, ctypes.c_float(-1.0), FAKE, FAKE, 8, 64, 0, 0, None) == SHAPE
+    assert f(arr, 2, 0, None, None, FAKE, ctypes.c_float(0.0), FAKE, FAKE, 8, 64, 0, 0, None) == NULL
+    bad = (ctypes.c_void_p * 2)(0x1000, None)
+    assert f(bad, 2, 0, *args, 8, 64, 0, 0, None) == NULL            # z[1] null
+    assert f(arr, 2, 0, *args, 0, 64, 0, 0, None) == OK              # T == 0
+
+
 def test_status_strings(lib):
     for s in range(8):
         assert lib.tp_status_string(s)

@@ -209,6 +209,45 @@ def test_partial_sum_bias_once_and_dtypes():
     assert_close(y, O.partial_sum([O.to64(z) for z in zf]), F32_TOL, "f32 ragged")
 
 
+# ---------------------------------------------------------------------------
+# Sequence-parallel boundary: a rank's rows of the partials' sum + residual,
+# then RMSNorm (ragged N takes the scalar path; the last case is the prefill
+# size, T=4096, N=8192, p=8).
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("p,T,N,in_dt,out_dt,with_bias", [
+    (1, 3, 1000, "bf16", "bf16", False),
+    (3, 12, 1000, "bf16", "f32", True),
+    (4, 8, 4100, "f32", "f32", False),
+    (2, 6, 77, "bf16", "bf16", True),
+    (8, 4096, 8192, "bf16", "bf16", False),
+])
+def test_rs_residual_rmsnorm(p, T, N, in_dt, out_dt, with_bias):
+    seed = p * 1000 + N
+    zs = [W.normal((T, N), 1.0, seed, i, in_dt) for i in range(p)]
+    bias = W.normal((N,), 1.0, seed, 90, in_dt) if with_bias else None
+    norm_w = W.normal((N,), 1.0, seed, 91, out_dt)
+    eps = 1e-5
+    dz = [cuda(z) for z in zs]
+    odt = torch.bfloat16 if out_dt == "bf16" else torch.float32
+    tol = BF16_TOL if out_dt == "bf16" else F32_TOL
+    ranks = range(p) if T * N < 10 ** 6 else (5,)
+    for rank in ranks:
+        res = W.normal((T // p, N), 1.0, seed, 100 + rank, out_dt)
+        r_out = torch.empty(T // p, N, dtype=odt, device="cuda")
+        y = torch.empty(T // p, N, dtype=odt, device="cuda")
+        tp.tp_rs_residual_rmsnorm(dz, rank, None if bias is None else cuda(bias), cuda(res), cuda(norm_w), eps,
+                                  r_out, y)
+        ref_s, ref_y = O.rs_residual_rmsnorm([O.to64(z) for z in zs], rank, O.to64(res), O.to64(norm_w), eps,
+                                             None if bias is None else O.to64(bias))
+        assert_close(r_out, ref_s, tol, f"residual, rank {rank}")
+        assert_close(y, ref_y, tol, f"normalized, rank {rank}")
+        # the residual may be updated in place
+        r_io = cuda(res)
+        y2 = torch.empty_like(y)
+        tp.tp_rs_residual_rmsnorm(dz, rank, None if bias is None else cuda(bias), r_io, cuda(norm_w), eps, r_io, y2)
+        assert torch.equal(r_io, r_out) and torch.equal(y2, y)
+
+
 def test_zero_tokens_is_a_noop():
     x = torch.empty(0, 64, dtype=torch.bfloat16, device="cuda")
     w1 = torch.zeros(64, 32, dtype=torch.bfloat16, device="cuda")

@@ -358,3 +358,59 @@ def test_compare_metric():
     assert O.compare(r, r) == (0.0, 0.0)
     rf, rm = O.compare(r * 1.01, r)
     assert abs(rf - 0.01) < 1e-12 and abs(rm - 0.04 / 4.0) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# Sequence-parallel boundary: the rank's rows of sum + residual, then RMSNorm.
+# ---------------------------------------------------------------------------
+def test_rs_norm_hand_values():
+    # one rank owns row 1 of 2; s = [2, -2] -> mean(s^2) = 4; eps = 5 -> sqrt(9) = 3
+    z0 = np.array([[9.0, 9.0], [1.5, -0.5]])
+    z1 = np.array([[9.0, 9.0], [0.5, -1.5]])
+    res = np.array([[0.0, 0.0]])
+    w = np.array([3.0, 0.75])
+    s, y = O.rs_residual_rmsnorm([z0, z1], 1, res, w, 5.0)
+    assert s.tolist() == [[2.0, -2.0]]
+    assert np.allclose(y, [[2.0 / 3.0 * 3.0, -2.0 / 3.0 * 0.75]], rtol=0, atol=1e-15)
+    # bias once after the partials, then the residual
+    s, _ = O.rs_residual_rmsnorm([z0, z1], 0, np.array([[1.0, 2.0]]), w, 0.0, bias=np.array([0.25, 0.5]))
+    assert s.tolist() == [[19.25, 20.5]]
+
+
+def test_rs_norm_constant_rows_and_scale_invariance():
+    rng = np.random.default_rng(5)
+    T, N, p = 12, 7, 3
+    c = rng.normal(size=(T, 1))
+    zs = [np.repeat(c / p, N, axis=1) for _ in range(p)]
+    w = rng.normal(size=N)
+    for rank in range(p):
+        res = np.zeros((T // p, N))
+        s, y = O.rs_residual_rmsnorm(zs, rank, res, w, 0.0)
+        # a constant row normalizes to its sign
+        assert np.allclose(y, np.sign(c[rank * 4:(rank + 1) * 4]) * w[None, :], rtol=1e-12, atol=1e-12)
+    # eps = 0: positive scaling of everything leaves y unchanged; y / w has unit RMS
+    zs = [rng.normal(size=(T, N)) for _ in range(p)]
+    res = rng.normal(size=(T // p, N))
+    _, y1 = O.rs_residual_rmsnorm(zs, 2, res, w, 0.0)
+    _, y2 = O.rs_residual_rmsnorm([3.5 * z for z in zs], 2, 3.5 * res, w, 0.0)
+    assert np.allclose(y1, y2, rtol=1e-12, atol=1e-12)
+    assert np.allclose(np.mean((y1 / w[None, :]) ** 2, axis=1), 1.0, rtol=1e-12)
+
+
+def test_rs_norm_shares_tile_the_unsharded_sum():
+    # element by element with plain loops: the p ranks' shares, stacked, are the
+    # full residual add (reduce-scatter of the all-reduce's result)
+    rng = np.random.default_rng(6)
+    T, N, p = 6, 5, 3
+    zs = [rng.normal(size=(T, N)) for _ in range(p)]
+    res = rng.normal(size=(T, N))
+    w = np.ones(N)
+    got = np.vstack([O.rs_residual_rmsnorm(zs, r, res[r * 2:(r + 1) * 2], w, 1e-6)[0] for r in range(p)])
+    for t in range(T):
+        for n in range(N):
+            want = res[t, n]
+            for z in zs:
+                want += z[t, n]
+            assert abs(got[t, n] - want) < 1e-12
+    with pytest.raises(ValueError):  # 5 rows do not split into 3 equal shares
+        O.rs_residual_rmsnorm([z[:5] for z in zs], 0, res[:1], w, 0.0)
