@@ -35,6 +35,9 @@ Readings where the pages are silent (also listed with the design notes):
     rejected ([FFN] partitions 4d into N chunks of size 4d/N).
   * Column-parallel bias: each shard adds its own slice; row-parallel bias:
     added once after the sum ([MLX]).
+  * The backward of the attention projections is the backward of two
+    linear shards: QKV column-parallel (partial dx), o_proj row-parallel
+    (replicated dy, local dx); no bias gradients.
   * The normalization after the block's sum is RMSNorm with a learned scale
     and a caller-given epsilon, taken over the fp32/float64 sum.
 
@@ -339,6 +342,24 @@ def gqa_local_qkv_weight(wq, wk, wv, n_q: int, n_kv: int, head_dim: int, p: int,
 
 def gqa_qkv_full(x, wq, wk, wv) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     return matmul(x, wq), matmul(x, wk), matmul(x, wv)
+
+
+def linear_shard_bwd(x, w, dy) -> Dict[str, np.ndarray]:
+    """Backward of one rank's shard of a linear layer y = x W.
+
+    Chain rule for y = x W: dW = x^T dy, dx = dy W^T.  What the two outputs
+    mean depends on how the layer is sharded ([FFN] "The backward pass";
+    [KL] second paragraph for the attention projections):
+      * column-parallel (the fused QKV projection): x is the replicated input,
+        W = W_i its column slice and dy the rank's own output gradient; dW_i
+        needs no exchange, dx_i is a partial that the group sums;
+      * row-parallel (o_proj): x = X_i is the rank's own input slice and dy is
+        identical on every rank (all-reduce forward, identity backward); dW_i
+        and dX_i are both final, with no exchange."""
+    x = to64(x)
+    w = to64(w)
+    dy = to64(dy)
+    return {"dw": matmul(x.T, dy), "dx": matmul(dy, w.T)}
 
 
 # ---------------------------------------------------------------------------

@@ -341,6 +341,83 @@ def test_gqa_local_qkv_is_slice_of_unsharded():
 
 
 # --------------------------------------------------------------------------
+# Backward of the attention projections: a column-parallel QKV shard and a
+# row-parallel o_proj shard ("The backward pass"; "Tensor Parallelism"
+# paragraph 2).
+# --------------------------------------------------------------------------
+def _linear_fd_check(fn, T=3, K=4, N=4, seed=31):
+    """Worst relative error of fn's (dW, dx) against central differences of
+    L(x, W) = sum((x W) * dy), whose gradients are the backward's outputs."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, K))
+    w = rng.standard_normal((K, N))
+    dy = rng.standard_normal((T, N))
+    g = fn(x, w, dy)
+
+    def loss(x_, w_):
+        return float(np.sum((x_ @ w_) * dy))
+
+    worst = 0.0
+    for key, arr in (("dx", x), ("dw", w)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            old = arr[idx]
+            arr[idx] = old + 1e-3
+            lp = loss(x, w)
+            arr[idx] = old - 1e-3
+            lm = loss(x, w)
+            arr[idx] = old
+            num[idx] = (lp - lm) / 2e-3
+        worst = max(worst, float(np.max(np.abs(num - g[key])) / np.max(np.abs(num))))
+    return worst
+
+
+def test_linear_backward_finite_difference():
+    assert _linear_fd_check(O.linear_shard_bwd) < 1e-9
+    assert _linear_fd_check(O.linear_shard_bwd, T=5, K=2, N=7) < 1e-9
+
+
+def test_linear_backward_planted_transpose_is_caught():
+    """dx = dy W instead of dy W^T (shapes agree when W is square) must fail."""
+    wrong = lambda x, w, dy: {"dw": O.matmul(x.T, dy), "dx": O.matmul(dy, w)}
+    assert _linear_fd_check(wrong) > 1e-2
+
+
+def test_attention_projection_backward_shards():
+    """QKV column-parallel: each rank's dW_qkv_i is its [Q_i | K_i | V_i]
+    column slice of the unsharded weight gradient and the dx_i partials sum
+    to the unsharded dx.  o_proj row-parallel: with dy replicated, dW_o_i is
+    the rank's row slice of the unsharded gradient and dX_i the rank's
+    column slice of the unsharded input gradient."""
+    rng = np.random.default_rng(41)
+    T, h, nq, nkv, hd, p = 5, 16, 8, 4, 2, 4
+    x = rng.standard_normal((T, h))
+    wq, wk, wv = (rng.standard_normal((h, n * hd)) for n in (nq, nkv, nkv))
+    dq, dk, dv = (rng.standard_normal((T, n * hd)) for n in (nq, nkv, nkv))
+    full = {n: O.linear_shard_bwd(x, w_, g_) for n, w_, g_ in (("q", wq, dq), ("k", wk, dk), ("v", wv, dv))}
+    dx_full = full["q"]["dx"] + full["k"]["dx"] + full["v"]["dx"]
+    attn = rng.standard_normal((T, nq * hd))
+    wo = rng.standard_normal((nq * hd, h))
+    dy = rng.standard_normal((T, h))
+    ofull = O.linear_shard_bwd(attn, wo, dy)
+    dxs = []
+    for i in range(p):
+        qb, ql, kb, kl = O.gqa_shard(nq, nkv, hd, p, i)
+        w_i = O.gqa_local_qkv_weight(wq, wk, wv, nq, nkv, hd, p, i)
+        d_i = np.concatenate([dq[:, qb:qb + ql], dk[:, kb:kb + kl], dv[:, kb:kb + kl]], 1)
+        gi = O.linear_shard_bwd(x, w_i, d_i)
+        np.testing.assert_allclose(gi["dw"], np.concatenate([full["q"]["dw"][:, qb:qb + ql],
+                                                             full["k"]["dw"][:, kb:kb + kl],
+                                                             full["v"]["dw"][:, kb:kb + kl]], 1),
+                                   rtol=1e-12, atol=1e-12)
+        dxs.append(gi["dx"])
+        go = O.linear_shard_bwd(attn[:, qb:qb + ql], O.slice_rows(wo, qb, ql), dy)
+        np.testing.assert_allclose(go["dw"], ofull["dw"][qb:qb + ql], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(go["dx"], ofull["dx"][:, qb:qb + ql], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(O.partial_sum(dxs), dx_full, rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
 # Work accounting: training ~ 6 x params x tokens.
 # --------------------------------------------------------------------------
 def test_flop_accounting():
