@@ -277,6 +277,31 @@ def main() -> int:
         rows["bwd_mlp_shard_T2048"] = {"us": round(t_ * 1e3, 1), "TFLOP/s": round(fl / t_ / 1e9, 1),
                                        "frac_mfma": round(fl / t_ / 1e9 / BF16_PEAK_TFLOPS, 4)}
 
+    if "bwd" in want:
+        # backward of one rank's attention projections (70B-class GQA, T=4096):
+        # QKV column-parallel (dW_qkv_i, dx_i partial) and o_proj row-parallel
+        # (dW_o_i, dX_i), four GEMMs of 2*T*h*(1280 or 1024) each
+        Ta, ha, qa, oa = 4096, 8192, 1280, 1024
+        xa = gpu_normal((Ta, ha), 1.0, 31, dev)
+        wqa = gpu_normal((ha, qa), 0.02, 32, dev)
+        dqa = gpu_normal((Ta, qa), 1.0, 33, dev)
+        aa = gpu_normal((Ta, oa), 1.0, 34, dev)
+        woa = gpu_normal((oa, ha), 0.02, 35, dev)
+        dya = gpu_normal((Ta, ha), 1.0, 36, dev)
+        gq, gxa, go, gaa = (torch.empty_like(t) for t in (wqa, xa, woa, aa))
+        wsa = tp.new_workspace(max(tp.tp_linear_shard_bwd_workspace(Ta, ha, qa, tp.TP_BF16),
+                                   tp.tp_linear_shard_bwd_workspace(Ta, oa, ha, tp.TP_BF16)), dev)
+
+        def attn_bwd(i):
+            tp.tp_linear_shard_bwd(xa, wqa, dqa, gq, gxa, wsa)
+            tp.tp_linear_shard_bwd(aa, woa, dya, go, gaa, wsa)
+
+        t_ = time_gpu(attn_bwd, steps_r, 3)
+        fl = 4 * Ta * ha * (qa + oa)
+        rows["bwd_attn_proj_shard_T4096"] = {"us": round(t_ * 1e3, 1), "TFLOP/s": round(fl / t_ / 1e9, 1),
+                                             "frac_mfma": round(fl / t_ / 1e9 / BF16_PEAK_TFLOPS, 4)}
+        del xa, wqa, dqa, aa, woa, dya, gq, gxa, go, gaa, wsa
+
     # ---------------- CPU baseline: the fp64 oracle on the same decode step ------------
     cpu = None
     if not args.no_cpu_baseline:

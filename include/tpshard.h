@@ -155,6 +155,28 @@ tp_status tp_mlp_shard_bwd(const void* x, const void* w1_i, const void* w_up_i, 
                            void* dw2_i, void* dx_i, void* ws, size_t ws_bytes, int64_t T,
                            int64_t d, int64_t ff_i, tp_dtype dtype, tp_act act, tp_stream stream);
 
+/* Backward of one rank's shard of a linear layer y = x w ([FFN] "The backward
+ * pass"; [KL] second paragraph: Q, K, V column-parallel by heads, o_proj
+ * row-parallel).  With dy the gradient at y:
+ *   dw = x^T dy   (K, N),   dx = dy w^T   (T, K).
+ * Column-parallel shard (the fused QKV projection): x is the replicated
+ * input, w = [Wq_i | Wk_i | Wv_i] and dy the rank's own output gradient; dw
+ * is final (no exchange) and dx a partial for tp_partial_sum.  Row-parallel
+ * shard (o_proj): x = the rank's attention output X_i, w = its row slice and
+ * dy the gradient every rank holds; dw and dx are both final.
+ * x (T, K), w (K, N), dy (T, N), dw (K, N), dx (T, K): device, row-major, in
+ * `dtype`; bf16 operands accumulate in fp32 and are stored with RNE.  dw or
+ * dx may be NULL to skip it (not both); x is read only for dw, w only for
+ * dx; a pointer to an empty array may be NULL.  No bias gradient.  ws (device) of ws_bytes >=
+ * tp_linear_shard_bwd_workspace(...) (0: none needed, ws may be NULL),
+ * under the same zero-fill and reuse rules as tp_mlp_shard_fwd's workspace.
+ * T == 0 zero-fills dw.  Errors: TP_ERR_NULL, TP_ERR_SHAPE, TP_ERR_DTYPE,
+ * TP_ERR_WORKSPACE, TP_ERR_HIP. */
+size_t tp_linear_shard_bwd_workspace(int64_t T, int64_t K, int64_t N, tp_dtype dtype);
+tp_status tp_linear_shard_bwd(const void* x, const void* w, const void* dy, void* dw, void* dx,
+                              void* ws, size_t ws_bytes, int64_t T, int64_t K, int64_t N,
+                              tp_dtype dtype, tp_stream stream);
+
 /* Sum of the p full-shape partials, then the bias once ([KL] Y = sum_i Z_i;
  * [FFN] "One collective"; [MLX] bias after the sum).  This is the one-GPU
  * stand-in for the group's all-reduce.  z (host array of p device pointers),

@@ -16,6 +16,8 @@ from .binding import (  # noqa: F401
     tp_col_linear,
     tp_col_linear_workspace,
     tp_gqa_shard,
+    tp_linear_shard_bwd,
+    tp_linear_shard_bwd_workspace,
     tp_mlp_shard_bwd,
     tp_mlp_shard_bwd_workspace,
     tp_mlp_shard_fwd,

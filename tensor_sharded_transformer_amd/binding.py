@@ -48,6 +48,8 @@ SIGNATURES = {
     "tp_mlp_shard_bwd_workspace": (c_sz, [c_i64, c_i64, c_i64, c_int, c_int]),
     "tp_mlp_shard_bwd": (c_int, [c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_sz, c_i64, c_i64, c_i64,
                                  c_int, c_int, c_p]),
+    "tp_linear_shard_bwd_workspace": (c_sz, [c_i64, c_i64, c_i64, c_int]),
+    "tp_linear_shard_bwd": (c_int, [c_p, c_p, c_p, c_p, c_p, c_p, c_sz, c_i64, c_i64, c_i64, c_int, c_p]),
     "tp_partial_sum": (c_int, [ctypes.POINTER(c_p), c_int, c_p, c_p, c_i64, c_i64, c_int, c_int, c_p]),
     "tp_rs_residual_rmsnorm": (c_int, [ctypes.POINTER(c_p), c_int, c_int, c_p, c_p, c_p, ctypes.c_float, c_p, c_p,
                                        c_i64, c_i64, c_int, c_int, c_p]),
@@ -215,6 +217,26 @@ def tp_mlp_shard_bwd(x, w1_i, w_up_i, w2_i, saved, dy, dw1_i, dw_up_i, dw2_i, dx
     _check(load().tp_mlp_shard_bwd(_ptr(x), _ptr(w1_i), _ptr(w_up_i), _ptr(w2_i), _ptr(saved), _ptr(dy),
                                    _ptr(dw1_i), _ptr(dw_up_i), _ptr(dw2_i), _ptr(dx_i), _ptr(ws),
                                    ws.numel() if ws is not None else 0, T, d, ff_i, _dt(x), ACT[act], _stream()))
+
+
+def tp_linear_shard_bwd_workspace(T: int, K: int, N: int, dtype: int) -> int:
+    return load().tp_linear_shard_bwd_workspace(T, K, N, dtype)
+
+
+def tp_linear_shard_bwd(x, w, dy, dw, dx, ws: Optional[torch.Tensor] = None):
+    """dw = x^T dy and dx = dy w^T for one rank's shard of y = x w (either
+    output may be None to skip it)."""
+    K, N = (w if w is not None else dw).shape
+    T = dy.shape[0]
+    _shape(dy, (T, N), "dy")
+    if x is not None:
+        _shape(x, (T, K), "x")
+    if dw is not None:
+        _shape(dw, (K, N), "dw")
+    if dx is not None:
+        _shape(dx, (T, K), "dx")
+    _check(load().tp_linear_shard_bwd(_ptr(x), _ptr(w), _ptr(dy), _ptr(dw), _ptr(dx), _ptr(ws),
+                                      ws.numel() if ws is not None else 0, T, K, N, _dt(dy), _stream()))
 
 
 def tp_partial_sum(zs: Sequence[torch.Tensor], bias, y):

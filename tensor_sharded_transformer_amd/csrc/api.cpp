@@ -150,6 +150,27 @@ BwdLayout bwd_layout(int64_t T, int64_t d, int64_t ff_i, int dtype, int act) {
   return L;
 }
 
+// ---- backward of one linear shard ---------------------------------------------
+struct LinBwdLayout {
+  GemmPlan pw, px;
+  size_t cnt_off = 0, part_off = 0, pack_off = 0, total = 0;
+};
+
+LinBwdLayout lin_bwd_layout(int64_t T, int64_t K, int64_t N, int dtype) {
+  LinBwdLayout L;
+  L.pw = plan_for(dtype, (int)K, (int)N, (int)T, false, true, false, false);  // dW = x^T dy
+  L.px = plan_for(dtype, (int)T, (int)K, (int)N, false, true, false, false);  // dx = dy W^T
+  SplitNeeds sn;
+  sn.add(L.pw, (int)K, (int)N, (int)T, false);
+  sn.add(L.px, (int)T, (int)K, (int)N, false);
+  if (!needs_ws(L.pw) && !needs_ws(L.px)) return L;
+  L.cnt_off = 0;
+  L.part_off = sn.counter_bytes();
+  L.pack_off = L.part_off + sn.partial_bytes();
+  L.total = L.pack_off + sn.packed_bytes();
+  return L;
+}
+
 // Optional workspace of a single GEMM entry point: [counters][partials][packed A].
 struct SingleWs {
   GemmPlan plan;
@@ -590,6 +611,77 @@ tp_status tp_mlp_shard_bwd(const void* x, const void* w1_i, const void* w_up_i, 
   attach_split(pd, L.pd, cnt, part, base + L.pack_off);
   e = run_gemm(dtype, pd, L.pd, tpk::GK_BWD_DX, false, s);
   return hip_status(e, "tp_mlp_shard_bwd (dx GEMM)");
+}
+
+size_t tp_linear_shard_bwd_workspace(int64_t T, int64_t K, int64_t N, tp_dtype dtype) {
+  if (!valid_dtype(dtype) || !dim_ok(T) || !dim_ok(K) || !dim_ok(N) || T == 0) return 0;
+  return lin_bwd_layout(T, K, N, dtype).total;
+}
+
+tp_status tp_linear_shard_bwd(const void* x, const void* w, const void* dy, void* dw, void* dx, void* ws,
+                              size_t ws_bytes, int64_t T, int64_t K, int64_t N, tp_dtype dtype, tp_stream stream) {
+  if (!valid_dtype(dtype)) return fail(TP_ERR_DTYPE, "tp_linear_shard_bwd: unknown dtype %d", dtype);
+  if (!dim_ok(T) || !dim_ok(K) || !dim_ok(N) || !prod_ok(T, K) || !prod_ok(K, N) || !prod_ok(T, N))
+    return fail(TP_ERR_SHAPE, "tp_linear_shard_bwd: sizes out of range");
+  // a pointer to an empty array may be NULL
+  if (!dw && !dx && (K * N > 0 || T * K > 0))
+    return fail(TP_ERR_NULL, "tp_linear_shard_bwd: neither dw nor dx requested");
+  if ((!dy && T * N > 0 && (dw || dx)) || (dw && !x && T * K > 0) || (dx && !w && K * N > 0))
+    return fail(TP_ERR_NULL, "tp_linear_shard_bwd: null input pointer");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const size_t es = esize(dtype);
+  if (T == 0) {
+    // no tokens: the weight gradient is zero, dx is empty
+    return hip_status(dw ? tpk::zero_fill(dw, (size_t)K * N * es, s) : hipSuccess, "tp_linear_shard_bwd (T=0)");
+  }
+  if (K == 0) return TP_OK;
+  if (N == 0)  // an empty contraction: dx is zero, dW is empty
+    return hip_status(dx ? tpk::zero_fill(dx, (size_t)T * K * es, s) : hipSuccess, "tp_linear_shard_bwd (N=0)");
+  const LinBwdLayout L = lin_bwd_layout(T, K, N, dtype);
+  if (L.total && !ws) return fail(TP_ERR_WORKSPACE, "tp_linear_shard_bwd: workspace required (%zu bytes)", L.total);
+  if (ws_bytes < L.total)
+    return fail(TP_ERR_WORKSPACE, "tp_linear_shard_bwd: workspace of %zu bytes < %zu needed", ws_bytes, L.total);
+  char* base = reinterpret_cast<char*>(ws);
+  char* cnt = L.total ? base + L.cnt_off : nullptr;
+  char* part = L.total ? base + L.part_off : nullptr;
+  char* pack = L.total ? base + L.pack_off : nullptr;
+  hipError_t e = hipSuccess;
+  if (dw) {
+    // dW = x^T dy: A(m = k, k = t) = x[t * K + k], B(k = t, n) = dy[t * N + n]
+    GemmParams pw = base_params();
+    pw.A0 = x;
+    pw.lda = K;
+    pw.B0 = dy;
+    pw.ldb = N;
+    pw.K0 = (int)T;
+    pw.M = (int)K;
+    pw.N = (int)N;
+    pw.C = dw;
+    pw.ldc = N;
+    pw.vecA = aligned16(x) && K % 8 == 0;
+    pw.vecB = aligned16(dy) && N % 8 == 0;
+    attach_split(pw, L.pw, cnt, part, pack);
+    e = run_gemm(dtype, pw, L.pw, tpk::GK_BWD_DW, false, s);
+    if (e != hipSuccess) return hip_status(e, "tp_linear_shard_bwd (dW GEMM)");
+  }
+  if (dx) {
+    // dx = dy W^T: A(m = t, k = n) = dy[t * N + n], B(k = n, n' = k) = w[k * N + n]
+    GemmParams px = base_params();
+    px.A0 = dy;
+    px.lda = N;
+    px.B0 = w;
+    px.ldb = N;
+    px.K0 = (int)N;
+    px.M = (int)T;
+    px.N = (int)K;
+    px.C = dx;
+    px.ldc = K;
+    px.vecA = aligned16(dy) && N % 8 == 0;
+    px.vecB = aligned16(w) && N % 8 == 0;
+    attach_split(px, L.px, cnt, part, pack);
+    e = run_gemm(dtype, px, L.px, tpk::GK_BWD_DX, false, s);
+  }
+  return hip_status(e, "tp_linear_shard_bwd (dx GEMM)");
 }
 
 }  // extern "C"

@@ -167,6 +167,23 @@ def test_rs_residual_rmsnorm_validation(lib):
     assert f(arr, 2, 0, *args, 0, 64, 0, 0, None) == OK              # T == 0
 
 
+def test_linear_shard_bwd_validation(lib):
+    f = lib.tp_linear_shard_bwd
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 8, 16, 32, 5, None) == DTYPE
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, -1, 16, 32, 0, None) == SHAPE
+    assert f(FAKE, FAKE, FAKE, None, None, None, 0, 8, 16, 32, 0, None) == NULL      # nothing requested
+    assert f(None, FAKE, FAKE, FAKE, None, None, 0, 8, 16, 32, 0, None) == NULL      # dw without x
+    assert f(FAKE, None, FAKE, None, FAKE, None, 0, 8, 16, 32, 0, None) == NULL      # dx without w
+    assert f(FAKE, FAKE, None, FAKE, FAKE, None, 0, 8, 16, 32, 0, None) == NULL      # no dy
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 8, 0, 32, 0, None) == OK         # K == 0: nothing to do
+    assert f(FAKE, FAKE, FAKE, None, FAKE, None, 0, 0, 16, 32, 0, None) == OK        # T == 0, no dw
+    assert lib.tp_linear_shard_bwd_workspace(0, 8192, 1280, 0) == 0
+    need = lib.tp_linear_shard_bwd_workspace(64, 8192, 1280, 0)   # split-K at T = 64
+    assert need > 0
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 64, 8192, 1280, 0, None) == WS
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, 64, 8192, 1280, 0, None) == WS
+
+
 def test_status_strings(lib):
     for s in range(8):
         assert lib.tp_status_string(s)

@@ -499,3 +499,84 @@ def test_backward_T2048_all_shards():
     tp.tp_partial_sum(dxs, None, y)
     full = O.mlp_shard_bwd(x64[rows], O.to64(t["w1"]), O.to64(t["w_up"]), O.to64(t["w2"]), dy64[rows], "swiglu")
     assert_close(y[rows], full["dx"], BF16_TOL, "sum of the 8 dx partials vs unsharded dx")
+
+
+# ---------------------------------------------------------------------------
+# Backward of the attention projections (linear shards).
+# ---------------------------------------------------------------------------
+def lin_bwd(x, w, dy, want_dw=True, want_dx=True):
+    T, K = (dy.shape[0], w.shape[0]) if w is not None else (dy.shape[0], x.shape[1])
+    N = dy.shape[1]
+    ws = tp.new_workspace(tp.tp_linear_shard_bwd_workspace(T, K, N, dt_of(dy)))
+    dw = torch.full((K, N), 7.0, dtype=dy.dtype, device="cuda") if want_dw else None
+    dx = torch.full((T, K), 7.0, dtype=dy.dtype, device="cuda") if want_dx else None
+    tp.tp_linear_shard_bwd(x, w, dy, dw, dx, ws)
+    return dw, dx
+
+
+@pytest.mark.parametrize("T,K,N", [(77, 200, 131), (300, 1000, 264), (5, 72, 1280), (640, 1024, 520)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_linear_shard_bwd_ragged(T, K, N, dtype):
+    x = W.normal((T, K), 1.0, 61, 1, dtype)
+    w = W.normal((K, N), 0.02, 61, 2, dtype)
+    dy = W.normal((T, N), 1.0, 61, 3, dtype)
+    dw, dx = lin_bwd(cuda(x), cuda(w), cuda(dy))
+    ref = O.linear_shard_bwd(x, w, dy)
+    tol = BF16_TOL if dtype == "bf16" else F32_TOL
+    assert_close(dw, ref["dw"], tol, "dW")
+    assert_close(dx, ref["dx"], tol, "dx")
+    # one output at a time gives the same values
+    dw1, none_x = lin_bwd(cuda(x), None, cuda(dy), want_dx=False)
+    none_w, dx1 = lin_bwd(None, cuda(w), cuda(dy), want_dw=False)
+    assert none_x is None and none_w is None
+    assert torch.equal(dw1, dw) and torch.equal(dx1, dx)
+
+
+def test_linear_shard_bwd_empty():
+    dy = torch.zeros(0, 64, dtype=torch.bfloat16, device="cuda")
+    x = torch.zeros(0, 32, dtype=torch.bfloat16, device="cuda")
+    w = torch.ones(32, 64, dtype=torch.bfloat16, device="cuda")
+    dw, dx = lin_bwd(x, w, dy)
+    assert dx.shape == (0, 32) and bool((dw == 0).all())          # T = 0: zero weight gradient
+    dy = torch.ones(16, 0, dtype=torch.bfloat16, device="cuda")
+    x = torch.ones(16, 32, dtype=torch.bfloat16, device="cuda")
+    w = torch.ones(32, 0, dtype=torch.bfloat16, device="cuda")
+    dw, dx = lin_bwd(x, w, dy)
+    assert dw.shape == (32, 0) and bool((dx == 0).all())          # N = 0: zero input gradient
+
+
+@pytest.mark.parametrize("T", [4096, 64])
+def test_attention_projection_backward(T):
+    """The 70B-class GQA projections' backward on every rank: QKV
+    column-parallel (dW_qkv_i in full for ranks 0 and 7, the 8 dx partials
+    summed against the unsharded dx) and o_proj row-parallel (dW_o_i in full,
+    dX_i on sampled rows)."""
+    wl = W.GQA_BWD
+    t = W.gqa_unsharded(wl)
+    g = W.gqa_grads(wl, T)
+    x_all = t["x"][:T]
+    attn = t["attn"][:T]
+    rows = W.row_subset(T, 64, wl.seed)
+    x = cuda(x_all)
+    dy = cuda(g["dy"])
+    x64, dy64 = O.to64(x_all), O.to64(g["dy"])
+    dxs = []
+    for i in range(wl.p):
+        qb, ql, kb, kl = tp.tp_gqa_shard(wl.n_q, wl.n_kv, wl.head_dim, wl.p, i)
+        wqkv = torch.cat([t["wq"][:, qb:qb + ql], t["wk"][:, kb:kb + kl], t["wv"][:, kb:kb + kl]], 1)
+        dqkv = torch.cat([g["dq"][:, qb:qb + ql], g["dk"][:, kb:kb + kl], g["dv"][:, kb:kb + kl]], 1)
+        dw, dx = lin_bwd(x, cuda(wqkv), cuda(dqkv))
+        dxs.append(dx)
+        a_i, wo_i = attn[:, qb:qb + ql], t["wo"][qb:qb + ql, :]
+        dwo, da = lin_bwd(cuda(a_i), cuda(wo_i), dy)
+        if i in (0, wl.p - 1):
+            ref = O.linear_shard_bwd(x64, wqkv, dqkv)
+            assert_close(dw, ref["dw"], BF16_TOL, f"dW_qkv rank {i}")
+            assert_close(dx[rows], ref["dx"][rows], BF16_TOL, f"dx partial rank {i}")
+            ref = O.linear_shard_bwd(a_i, wo_i, dy64)
+            assert_close(dwo, ref["dw"], BF16_TOL, f"dW_o rank {i}")
+            assert_close(da[rows], ref["dx"][rows], BF16_TOL, f"dX rank {i}")
+    y = torch.empty(T, wl.h, dtype=torch.float32, device="cuda")
+    tp.tp_partial_sum(dxs, None, y)
+    full = sum(O.linear_shard_bwd(x64[rows], t[w_], g[d_][rows])["dx"] for w_, d_ in (("wq", "dq"), ("wk", "dk"), ("wv", "dv")))
+    assert_close(y[rows], full, BF16_TOL, "sum of the 8 QKV dx partials vs unsharded dx")

@@ -68,10 +68,11 @@ PREFILL = MlpWorkload("swiglu_mlp_prefill_T4096", T=4096, d=8192, ff=28672, p=8,
                       act="swiglu", dtype="bf16", seed=2)
 GQA_PREFILL = GqaWorkload("gqa_proj_T4096", T=4096, h=8192, n_q=64, n_kv=8, head_dim=128, p=8, seed=3)
 GQA_DECODE = GqaWorkload("gqa_proj_T64", T=64, h=8192, n_q=64, n_kv=8, head_dim=128, p=8, seed=3)
+GQA_BWD = GqaWorkload("gqa_proj_bwd_T4096", T=4096, h=8192, n_q=64, n_kv=8, head_dim=128, p=8, seed=5)
 BACKWARD = MlpWorkload("swiglu_mlp_bwd_T2048", T=2048, d=4096, ff=14336, p=8, act="swiglu",
                        dtype="bf16", seed=4)
 
-ALL = {w.name: w for w in (TINY, DECODE, PREFILL, GQA_PREFILL, GQA_DECODE, BACKWARD)}
+ALL = {w.name: w for w in (TINY, DECODE, PREFILL, GQA_PREFILL, GQA_DECODE, GQA_BWD, BACKWARD)}
 
 
 def _gen(seed: int, stream: int) -> torch.Generator:
@@ -96,6 +97,7 @@ def normal(shape, std: float, seed: int, stream: int, dtype: str = "bf16") -> to
 # Tensor stream ids (fixed so every consumer draws the same values).
 S_X, S_W1, S_WUP, S_W2, S_DY = 1, 2, 3, 4, 5
 S_WQ, S_WK, S_WV, S_WO, S_ATTN = 11, 12, 13, 14, 15
+S_DQ, S_DK, S_DV = 16, 17, 18
 
 
 def mlp_unsharded(w: MlpWorkload, with_dy: bool = False, T: Optional[int] = None) -> Dict[str, torch.Tensor]:
@@ -147,6 +149,20 @@ def gqa_unsharded(w: GqaWorkload) -> Dict[str, torch.Tensor]:
         "wv": normal((w.h, kvw), WEIGHT_STD, w.seed, S_WV),
         "wo": normal((qw, w.h), WEIGHT_STD, w.seed, S_WO),
         "attn": normal((w.T, qw), 1.0, w.seed + w.T, S_ATTN),
+    }
+
+
+def gqa_grads(w: GqaWorkload, T: Optional[int] = None) -> Dict[str, torch.Tensor]:
+    """Gradients arriving at the projections' outputs: unsharded dQ (T, n_q*hd),
+    dK, dV (T, n_kv*hd) and the o_proj output gradient dy (T, h)."""
+    T = w.T if T is None else T
+    qw = w.n_q * w.head_dim
+    kvw = w.n_kv * w.head_dim
+    return {
+        "dq": normal((T, qw), 1.0, w.seed, S_DQ),
+        "dk": normal((T, kvw), 1.0, w.seed, S_DK),
+        "dv": normal((T, kvw), 1.0, w.seed, S_DV),
+        "dy": normal((T, w.h), 1.0, w.seed, S_DY),
     }
 
 
