@@ -38,6 +38,8 @@ Readings where the pages are silent (also listed with the design notes):
   * The backward of the attention projections is the backward of two
     linear shards: QKV column-parallel (partial dx), o_proj row-parallel
     (replicated dy, local dx); no bias gradients.
+  * Local attention is scaled dot-product softmax attention, optionally
+    causal, with query head j reading KV head j // (n_q / n_kv).
   * The normalization after the block's sum is RMSNorm with a learned scale
     and a caller-given epsilon, taken over the fp32/float64 sum.
 
@@ -360,6 +362,54 @@ def linear_shard_bwd(x, w, dy) -> Dict[str, np.ndarray]:
     w = to64(w)
     dy = to64(dy)
     return {"dw": matmul(x.T, dy), "dx": matmul(dy, w.T)}
+
+
+def gqa_attention(qkv, n_q: int, n_kv: int, head_dim: int, causal: bool, scale: float) -> np.ndarray:
+    """Attention over one rank's local heads, between the fused QKV projection
+    and o_proj.
+
+    [KL] second paragraph: with grouped-query attention each rank owns n_q
+    query heads and n_kv KV heads and computes attention locally over them;
+    [FFN] attention paragraph: heads are independent, so this needs no
+    communication.  The pages do not write the attention itself; it is read
+    as scaled dot-product softmax attention (the tiling of "QK softmax V" that
+    [KL]'s FlashAttention paragraph refers to): for query head j, served by KV
+    head j // (n_q / n_kv),
+        S = scale * Q_j K^T,  S[t, u] = -inf for u > t when causal,
+        P = softmax over u (each row), O_j = P V.
+    qkv is (T, (n_q + 2 n_kv) * head_dim) with each row [Q heads | K heads |
+    V heads]; the result is (T, n_q * head_dim), heads side by side (the
+    layout o_proj consumes)."""
+    a = to64(qkv)
+    T = a.shape[0]
+    if n_q % n_kv != 0:
+        raise ValueError("query heads must be a multiple of KV heads")
+    if a.shape[1] != (n_q + 2 * n_kv) * head_dim:
+        raise ValueError("qkv width does not match the head counts")
+    group = n_q // n_kv
+    out = np.zeros((T, n_q * head_dim), dtype=F64)
+    k0 = n_q * head_dim
+    v0 = k0 + n_kv * head_dim
+    for j in range(n_q):
+        g = j // group
+        q = a[:, j * head_dim:(j + 1) * head_dim]
+        k = a[:, k0 + g * head_dim:k0 + (g + 1) * head_dim]
+        v = a[:, v0 + g * head_dim:v0 + (g + 1) * head_dim]
+        s = scale * matmul(q, k.T)
+        if causal:
+            s = np.where(np.tril(np.ones((T, T), dtype=bool)), s, -np.inf)
+        if T:
+            s = s - np.max(s, axis=1, keepdims=True)
+        e = np.exp(s)
+        pm = e / np.sum(e, axis=1, keepdims=True)
+        out[:, j * head_dim:(j + 1) * head_dim] = matmul(pm, v)
+    return out
+
+
+def attention_flops(T: int, n_q: int, head_dim: int, causal: bool) -> int:
+    """Multiply-adds x 2 of Q K^T and P V over the (unmasked) score matrix."""
+    pairs = T * (T + 1) // 2 if causal else T * T
+    return 4 * pairs * head_dim * n_q
 
 
 # ---------------------------------------------------------------------------

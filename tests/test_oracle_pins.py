@@ -418,6 +418,95 @@ def test_attention_projection_backward_shards():
 
 
 # --------------------------------------------------------------------------
+# Local attention over the rank's heads ("Tensor Parallelism" paragraph 2;
+# "How does tensor parallelism split..." attention paragraph).
+# --------------------------------------------------------------------------
+def _qkv(q, k, v):
+    return np.concatenate([q, k, v], axis=1)
+
+
+def test_attention_hand_values():
+    """One head of width 1: q = [1, 2], k = [0, ln 3], v = [4, 8].  Row 0
+    weighs the keys 1/4 and 3/4 (non-causal) and sees only key 0 (causal);
+    row 1 has logits 0 and 2 ln 3, weights 1/10 and 9/10."""
+    q = np.array([[1.0], [2.0]])
+    k = np.array([[0.0], [math.log(3.0)]])
+    v = np.array([[4.0], [8.0]])
+    full = O.gqa_attention(_qkv(q, k, v), 1, 1, 1, False, 1.0)
+    np.testing.assert_allclose(full[:, 0], [0.25 * 4 + 0.75 * 8, 0.1 * 4 + 0.9 * 8], rtol=1e-14)
+    causal = O.gqa_attention(_qkv(q, k, v), 1, 1, 1, True, 1.0)
+    np.testing.assert_allclose(causal[:, 0], [4.0, 0.1 * 4 + 0.9 * 8], rtol=1e-14)
+
+
+def test_attention_uniform_keys_give_prefix_means():
+    """Equal keys make every weight equal: the output is the mean of the
+    visible values (all of them, or the prefix 0..t when causal)."""
+    rng = np.random.default_rng(51)
+    T, hd = 9, 4
+    q = rng.standard_normal((T, hd))
+    k = np.tile(rng.standard_normal((1, hd)), (T, 1))
+    v = rng.standard_normal((T, hd))
+    full = O.gqa_attention(_qkv(q, k, v), 1, 1, hd, False, 0.7)
+    np.testing.assert_allclose(full, np.tile(v.mean(0), (T, 1)), rtol=1e-12, atol=1e-12)
+    causal = O.gqa_attention(_qkv(q, k, v), 1, 1, hd, True, 0.7)
+    prefix = np.cumsum(v, 0) / np.arange(1, T + 1)[:, None]
+    np.testing.assert_allclose(causal, prefix, rtol=1e-12, atol=1e-12)
+
+
+def test_attention_invariances():
+    """Permuting keys with their values leaves non-causal attention unchanged;
+    adding one vector to every key shifts each row's logits by a constant and
+    changes nothing, causal or not; a very large scale selects the value of
+    the highest-scoring key."""
+    rng = np.random.default_rng(52)
+    T, hd = 7, 3
+    q, k, v = (rng.standard_normal((T, hd)) for _ in range(3))
+    base = O.gqa_attention(_qkv(q, k, v), 1, 1, hd, False, 0.5)
+    perm = rng.permutation(T)
+    np.testing.assert_allclose(O.gqa_attention(_qkv(q, k[perm], v[perm]), 1, 1, hd, False, 0.5), base,
+                               rtol=1e-12, atol=1e-12)
+    c = rng.standard_normal((1, hd))
+    for causal in (False, True):
+        ref = O.gqa_attention(_qkv(q, k, v), 1, 1, hd, causal, 0.5)
+        np.testing.assert_allclose(O.gqa_attention(_qkv(q, k + c, v), 1, 1, hd, causal, 0.5), ref,
+                                   rtol=1e-12, atol=1e-12)
+    hard = O.gqa_attention(_qkv(q, k, v), 1, 1, hd, False, 1e4)
+    np.testing.assert_allclose(hard, v[np.argmax(q @ k.T, axis=1)], rtol=1e-9, atol=1e-9)
+
+
+def test_attention_matches_library_softmax():
+    rng = np.random.default_rng(53)
+    T, hd = 6, 5
+    q, k, v = (rng.standard_normal((T, hd)) for _ in range(3))
+    w = scipy.special.softmax(0.3 * (q @ k.T) + np.triu(np.full((T, T), -np.inf), 1), axis=1)
+    np.testing.assert_allclose(O.gqa_attention(_qkv(q, k, v), 1, 1, hd, True, 0.3), w @ v, rtol=1e-12, atol=1e-12)
+
+
+def test_gqa_attention_equals_mha_with_shared_kv():
+    """Grouped-query attention with 4 query heads over 2 KV heads equals
+    multi-head attention with each KV head repeated for its group of query
+    heads (query heads 0, 1 read KV head 0; heads 2, 3 read KV head 1)."""
+    rng = np.random.default_rng(54)
+    T, hd = 5, 2
+    q = rng.standard_normal((T, 4 * hd))
+    k = rng.standard_normal((T, 2 * hd))
+    v = rng.standard_normal((T, 2 * hd))
+    rep = lambda a: np.concatenate([a[:, :hd], a[:, :hd], a[:, hd:], a[:, hd:]], 1)
+    got = O.gqa_attention(_qkv(q, k, v), 4, 2, hd, True, 0.8)
+    mha = O.gqa_attention(_qkv(q, rep(k), rep(v)), 4, 4, hd, True, 0.8)
+    np.testing.assert_allclose(got, mha, rtol=1e-13, atol=1e-13)
+    for j in range(4):       # and each head on its own
+        one = O.gqa_attention(_qkv(q[:, j * hd:(j + 1) * hd], k[:, (j // 2) * hd:(j // 2 + 1) * hd],
+                                   v[:, (j // 2) * hd:(j // 2 + 1) * hd]), 1, 1, hd, True, 0.8)
+        np.testing.assert_allclose(got[:, j * hd:(j + 1) * hd], one, rtol=1e-13, atol=1e-13)
+
+
+def test_attention_flops():
+    assert O.attention_flops(4096, 8, 128, False) == 4 * 4096 * 4096 * 128 * 8
+    assert O.attention_flops(3, 1, 1, True) == 4 * 6
+
+
+# --------------------------------------------------------------------------
 # Work accounting: training ~ 6 x params x tokens.
 # --------------------------------------------------------------------------
 def test_flop_accounting():
