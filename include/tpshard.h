@@ -177,6 +177,25 @@ tp_status tp_linear_shard_bwd(const void* x, const void* w, const void* dy, void
                               void* ws, size_t ws_bytes, int64_t T, int64_t K, int64_t N,
                               tp_dtype dtype, tp_stream stream);
 
+/* Attention over one rank's local heads, between the fused QKV projection and
+ * o_proj ([KL] second paragraph: each rank owns whole query and KV heads and
+ * computes attention locally; [FFN] attention paragraph: heads are
+ * independent; [KL] FlashAttention paragraph: Q K^T, softmax and V tiled so
+ * the scores stay on chip).  For query head j, with KV head
+ * g = j / (n_q / n_kv):
+ *   O_j = softmax_rows(scale * Q_j K_g^T  [keys > query dropped if causal]) V_g
+ * qkv (T, (n_q + 2 n_kv) * head_dim) bf16, row t = [Q heads | K heads |
+ * V heads] (the output of tp_col_linear with w = [Wq_i | Wk_i | Wv_i]);
+ * out (T, n_q * head_dim) bf16, heads side by side (the input of o_proj).
+ * Both device, 16-byte aligned.  One sequence of T tokens.  fp32 scores and
+ * softmax, bf16 probabilities into the P V product, fp32 accumulation, bf16
+ * output (RNE).  Errors: TP_ERR_SHAPE (sizes, n_q not a multiple of n_kv,
+ * causal not 0/1, scale not finite and > 0), TP_ERR_UNSUPPORTED (head_dim
+ * other than 128, unaligned pointers), TP_ERR_NULL, TP_ERR_HIP.  T == 0 is a
+ * no-op. */
+tp_status tp_gqa_attention_fwd(const void* qkv, void* out, int64_t T, int n_q, int n_kv, int head_dim,
+                               int causal, float scale, tp_stream stream);
+
 /* Sum of the p full-shape partials, then the bias once ([KL] Y = sum_i Z_i;
  * [FFN] "One collective"; [MLX] bias after the sum).  This is the one-GPU
  * stand-in for the group's all-reduce.  z (host array of p device pointers),

@@ -364,7 +364,8 @@ def linear_shard_bwd(x, w, dy) -> Dict[str, np.ndarray]:
     return {"dw": matmul(x.T, dy), "dx": matmul(dy, w.T)}
 
 
-def gqa_attention(qkv, n_q: int, n_kv: int, head_dim: int, causal: bool, scale: float) -> np.ndarray:
+def gqa_attention(qkv, n_q: int, n_kv: int, head_dim: int, causal: bool, scale: float,
+                  rows: Optional[Sequence[int]] = None) -> np.ndarray:
     """Attention over one rank's local heads, between the fused QKV projection
     and o_proj.
 
@@ -379,7 +380,8 @@ def gqa_attention(qkv, n_q: int, n_kv: int, head_dim: int, causal: bool, scale: 
         P = softmax over u (each row), O_j = P V.
     qkv is (T, (n_q + 2 n_kv) * head_dim) with each row [Q heads | K heads |
     V heads]; the result is (T, n_q * head_dim), heads side by side (the
-    layout o_proj consumes)."""
+    layout o_proj consumes).  ``rows`` restricts the queries (each output row
+    depends only on its own query), giving (len(rows), n_q * head_dim)."""
     a = to64(qkv)
     T = a.shape[0]
     if n_q % n_kv != 0:
@@ -387,17 +389,18 @@ def gqa_attention(qkv, n_q: int, n_kv: int, head_dim: int, causal: bool, scale: 
     if a.shape[1] != (n_q + 2 * n_kv) * head_dim:
         raise ValueError("qkv width does not match the head counts")
     group = n_q // n_kv
-    out = np.zeros((T, n_q * head_dim), dtype=F64)
+    qrows = np.arange(T) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.zeros((len(qrows), n_q * head_dim), dtype=F64)
     k0 = n_q * head_dim
     v0 = k0 + n_kv * head_dim
     for j in range(n_q):
         g = j // group
-        q = a[:, j * head_dim:(j + 1) * head_dim]
+        q = a[qrows, j * head_dim:(j + 1) * head_dim]
         k = a[:, k0 + g * head_dim:k0 + (g + 1) * head_dim]
         v = a[:, v0 + g * head_dim:v0 + (g + 1) * head_dim]
         s = scale * matmul(q, k.T)
         if causal:
-            s = np.where(np.tril(np.ones((T, T), dtype=bool)), s, -np.inf)
+            s = np.where(np.arange(T)[None, :] <= qrows[:, None], s, -np.inf)
         if T:
             s = s - np.max(s, axis=1, keepdims=True)
         e = np.exp(s)

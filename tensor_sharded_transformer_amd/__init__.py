@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     tp_act_inplace,
     tp_col_linear,
     tp_col_linear_workspace,
+    tp_gqa_attention_fwd,
     tp_gqa_shard,
     tp_linear_shard_bwd,
     tp_linear_shard_bwd_workspace,

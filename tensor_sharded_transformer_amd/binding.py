@@ -50,6 +50,7 @@ SIGNATURES = {
                                  c_int, c_int, c_p]),
     "tp_linear_shard_bwd_workspace": (c_sz, [c_i64, c_i64, c_i64, c_int]),
     "tp_linear_shard_bwd": (c_int, [c_p, c_p, c_p, c_p, c_p, c_p, c_sz, c_i64, c_i64, c_i64, c_int, c_p]),
+    "tp_gqa_attention_fwd": (c_int, [c_p, c_p, c_i64, c_int, c_int, c_int, c_int, ctypes.c_float, c_p]),
     "tp_partial_sum": (c_int, [ctypes.POINTER(c_p), c_int, c_p, c_p, c_i64, c_i64, c_int, c_int, c_p]),
     "tp_rs_residual_rmsnorm": (c_int, [ctypes.POINTER(c_p), c_int, c_int, c_p, c_p, c_p, ctypes.c_float, c_p, c_p,
                                        c_i64, c_i64, c_int, c_int, c_p]),
@@ -237,6 +238,17 @@ def tp_linear_shard_bwd(x, w, dy, dw, dx, ws: Optional[torch.Tensor] = None):
         _shape(dx, (T, K), "dx")
     _check(load().tp_linear_shard_bwd(_ptr(x), _ptr(w), _ptr(dy), _ptr(dw), _ptr(dx), _ptr(ws),
                                       ws.numel() if ws is not None else 0, T, K, N, _dt(dy), _stream()))
+
+
+def tp_gqa_attention_fwd(qkv, out, n_q: int, n_kv: int, head_dim: int, causal: bool, scale: float):
+    """Attention over a rank's local heads: qkv (T, (n_q + 2 n_kv) head_dim)
+    rows [Q | K | V] -> out (T, n_q head_dim)."""
+    T = qkv.shape[0]
+    _shape(qkv, (T, (n_q + 2 * n_kv) * head_dim), "qkv")
+    _shape(out, (T, n_q * head_dim), "out")
+    _check(load().tp_gqa_attention_fwd(_ptr(qkv), _ptr(out), T, n_q, n_kv, head_dim, int(bool(causal)), scale,
+                                       _stream()))
+    return out
 
 
 def tp_partial_sum(zs: Sequence[torch.Tensor], bias, y):

@@ -684,4 +684,24 @@ tp_status tp_linear_shard_bwd(const void* x, const void* w, const void* dy, void
   return hip_status(e, "tp_linear_shard_bwd (dx GEMM)");
 }
 
+tp_status tp_gqa_attention_fwd(const void* qkv, void* out, int64_t T, int n_q, int n_kv, int head_dim, int causal,
+                               float scale, tp_stream stream) {
+  if (!dim_ok(T) || n_q < 1 || n_kv < 1 || n_q % n_kv != 0 || head_dim < 1)
+    return fail(TP_ERR_SHAPE, "tp_gqa_attention_fwd: bad sizes (T=%lld, n_q=%d, n_kv=%d, head_dim=%d)", (long long)T,
+                n_q, n_kv, head_dim);
+  if (causal != 0 && causal != 1) return fail(TP_ERR_SHAPE, "tp_gqa_attention_fwd: causal must be 0 or 1");
+  if (!(scale > 0.0f) || scale > 3.0e38f) return fail(TP_ERR_SHAPE, "tp_gqa_attention_fwd: scale must be finite and > 0");
+  if (head_dim != tpk::attention_head_dim())
+    return fail(TP_ERR_UNSUPPORTED, "tp_gqa_attention_fwd: head_dim %d (only %d is built)", head_dim,
+                tpk::attention_head_dim());
+  const int64_t width = (int64_t)(n_q + 2 * n_kv) * head_dim;
+  if (width > kMaxDim || !prod_ok(T, width)) return fail(TP_ERR_SHAPE, "tp_gqa_attention_fwd: sizes out of range");
+  if (T == 0) return TP_OK;
+  if (!qkv || !out) return fail(TP_ERR_NULL, "tp_gqa_attention_fwd: null qkv or out");
+  if (!aligned16(qkv) || !aligned16(out))
+    return fail(TP_ERR_UNSUPPORTED, "tp_gqa_attention_fwd: qkv and out must be 16-byte aligned");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return hip_status(tpk::gqa_attention_fwd(qkv, out, (int)T, n_q, n_kv, causal == 1, scale, s), "tp_gqa_attention_fwd");
+}
+
 }  // extern "C"

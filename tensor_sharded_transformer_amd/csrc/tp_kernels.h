@@ -157,4 +157,11 @@ hipError_t rs_residual_rmsnorm(const void* const* z, int p, int rank, const void
                                bool in_bf16, bool out_bf16, hipStream_t s);
 hipError_t zero_fill(void* ws, size_t bytes, hipStream_t s);
 
+// Local grouped-query attention over a rank's heads: qkv (T, (n_q + 2 n_kv)
+// * 128) bf16 rows [Q | K | V], out (T, n_q * 128) bf16; both 16-byte
+// aligned.  head_dim is fixed at attention_head_dim().
+int attention_head_dim();
+hipError_t gqa_attention_fwd(const void* qkv, void* out, int T, int n_q, int n_kv, bool causal, float scale,
+                             hipStream_t s);
+
 }  // namespace tpk

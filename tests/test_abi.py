@@ -184,6 +184,21 @@ def test_linear_shard_bwd_validation(lib):
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, 64, 8192, 1280, 0, None) == WS
 
 
+def test_gqa_attention_validation(lib):
+    f = lib.tp_gqa_attention_fwd
+    sc = ctypes.c_float(0.088)
+    assert f(FAKE, FAKE, -1, 8, 1, 128, 1, sc, None) == SHAPE
+    assert f(FAKE, FAKE, 64, 8, 3, 128, 1, sc, None) == SHAPE          # 8 query heads over 3 KV heads
+    assert f(FAKE, FAKE, 64, 0, 1, 128, 1, sc, None) == SHAPE
+    assert f(FAKE, FAKE, 64, 8, 1, 128, 2, sc, None) == SHAPE          # causal flag not 0/1
+    assert f(FAKE, FAKE, 64, 8, 1, 128, 1, ctypes.c_float(0.0), None) == SHAPE
+    assert f(FAKE, FAKE, 64, 8, 1, 128, 1, ctypes.c_float(float("nan")), None) == SHAPE
+    assert f(FAKE, FAKE, 64, 8, 1, 64, 1, sc, None) == 6               # head_dim 64: not built
+    assert f(None, FAKE, 64, 8, 1, 128, 1, sc, None) == NULL
+    assert f(ctypes.c_void_p(0x1008), FAKE, 64, 8, 1, 128, 1, sc, None) == 6   # unaligned
+    assert f(None, None, 0, 8, 1, 128, 1, sc, None) == OK              # T == 0
+
+
 def test_status_strings(lib):
     for s in range(8):
         assert lib.tp_status_string(s)

@@ -580,3 +580,71 @@ def test_attention_projection_backward(T):
     tp.tp_partial_sum(dxs, None, y)
     full = sum(O.linear_shard_bwd(x64[rows], t[w_], g[d_][rows])["dx"] for w_, d_ in (("wq", "dq"), ("wk", "dk"), ("wv", "dv")))
     assert_close(y[rows], full, BF16_TOL, "sum of the 8 QKV dx partials vs unsharded dx")
+
+
+# ---------------------------------------------------------------------------
+# Local grouped-query attention.
+# ---------------------------------------------------------------------------
+def attn(qkv, n_q, n_kv, causal, scale):
+    out = torch.full((qkv.shape[0], n_q * 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    return tp.tp_gqa_attention_fwd(qkv, out, n_q, n_kv, 128, causal, scale)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("T,n_q,n_kv,std", [(1, 8, 1, 1.0), (5, 8, 1, 1.0), (77, 8, 1, 1.81), (200, 4, 2, 1.0),
+                                            (300, 2, 2, 3.0), (129, 8, 1, 1.81), (640, 8, 1, 1.81)])
+def test_attention_ragged(causal, T, n_q, n_kv, std):
+    qkv = W.normal((T, (n_q + 2 * n_kv) * 128), std, 71 + T, 1)
+    scale = 128 ** -0.5
+    got = attn(cuda(qkv), n_q, n_kv, causal, scale)
+    ref = O.gqa_attention(qkv, n_q, n_kv, 128, causal, scale)
+    assert_close(got, ref, BF16_TOL, f"attention T={T} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_attention_T4096_rank_heads(causal):
+    """A 70B-class rank's 8 query heads over its 1 KV head at T=4096, on 64
+    sampled query rows (each row depends only on its own query)."""
+    wl = W.GQA_ATTN
+    qkv = W.attention_qkv(wl)
+    n_q, n_kv = wl.n_q // wl.p, wl.n_kv // wl.p
+    scale = wl.head_dim ** -0.5
+    got = attn(cuda(qkv), n_q, n_kv, causal, scale)
+    rows = sorted(set(W.row_subset(wl.T, 62, wl.seed) + [0, wl.T - 1]))
+    ref = O.gqa_attention(qkv, n_q, n_kv, wl.head_dim, causal, scale, rows=rows)
+    assert_close(got[rows], ref, BF16_TOL, "attention rows")
+    again = attn(cuda(qkv), n_q, n_kv, causal, scale)
+    assert torch.equal(got, again)          # deterministic
+
+
+def test_attention_between_the_projections():
+    """QKV projection -> local attention -> o_proj partial on one rank, chained
+    through the C ABI, against the fp64 oracle chain on sampled rows.
+
+    The chain stores qkv in bf16 between the launches; the oracle keeps it in
+    fp64.  Rounding qkv alone moves the fp64 attention output by a relative
+    Frobenius error of 4.8e-3 (max 7.3e-3) at these inputs (scores with a
+    standard deviation near 3 amplify it), so the chained stages get that
+    budget on top of one kernel's 5e-3 / 1e-2."""
+    wl = W.GQA_PREFILL
+    T = 512
+    t = W.gqa_unsharded(wl)
+    i = 2
+    qb, ql, kb, kl = tp.tp_gqa_shard(wl.n_q, wl.n_kv, wl.head_dim, wl.p, i)
+    wqkv = torch.cat([t["wq"][:, qb:qb + ql], t["wk"][:, kb:kb + kl], t["wv"][:, kb:kb + kl]], 1).contiguous()
+    x = t["x"][:T].contiguous()
+    qkv = torch.empty(T, 1280, dtype=torch.bfloat16, device="cuda")
+    ws = tp.new_workspace(tp.tp_col_linear_workspace(T, wl.h, 1280, tp.TP_BF16, "none"))
+    tp.tp_col_linear(cuda(x), cuda(wqkv), None, None, qkv, "none", ws)
+    a = attn(qkv, 8, 1, True, 128 ** -0.5)
+    wo_i = cuda(t["wo"][qb:qb + ql, :])
+    z = torch.empty(T, wl.h, dtype=torch.bfloat16, device="cuda")
+    ws = tp.new_workspace(tp.tp_row_linear_partial_workspace(T, ql, wl.h, tp.TP_BF16))
+    tp.tp_row_linear_partial(a, wo_i, z, ws)
+    rows = W.row_subset(T, 32, 7)
+    qkv64 = O.matmul(O.to64(x), O.gqa_local_qkv_weight(t["wq"], t["wk"], t["wv"], wl.n_q, wl.n_kv, wl.head_dim,
+                                                       wl.p, i))
+    a64 = O.gqa_attention(qkv64, 8, 1, 128, True, 128 ** -0.5, rows=rows)
+    chain_tol = (BF16_TOL[0] + 4.8e-3, BF16_TOL[1] + 7.3e-3)
+    assert_close(a[rows], a64, chain_tol, "attention on the projected qkv")
+    assert_close(z[rows], O.row_linear_partial(a64, O.to64(t["wo"][qb:qb + ql, :])), chain_tol, "o_proj partial")

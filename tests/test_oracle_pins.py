@@ -501,6 +501,17 @@ def test_gqa_attention_equals_mha_with_shared_kv():
         np.testing.assert_allclose(got[:, j * hd:(j + 1) * hd], one, rtol=1e-13, atol=1e-13)
 
 
+def test_attention_row_subset_equals_full():
+    rng = np.random.default_rng(55)
+    T, hd = 11, 3
+    qkv = rng.standard_normal((T, (2 + 2) * hd))
+    rows = [0, 4, 10]
+    for causal in (False, True):
+        full = O.gqa_attention(qkv, 2, 1, hd, causal, 0.6)
+        np.testing.assert_allclose(O.gqa_attention(qkv, 2, 1, hd, causal, 0.6, rows=rows), full[rows],
+                                   rtol=1e-13, atol=1e-13)
+
+
 def test_attention_flops():
     assert O.attention_flops(4096, 8, 128, False) == 4 * 4096 * 4096 * 128 * 8
     assert O.attention_flops(3, 1, 1, True) == 4 * 6

@@ -68,11 +68,12 @@ PREFILL = MlpWorkload("swiglu_mlp_prefill_T4096", T=4096, d=8192, ff=28672, p=8,
                       act="swiglu", dtype="bf16", seed=2)
 GQA_PREFILL = GqaWorkload("gqa_proj_T4096", T=4096, h=8192, n_q=64, n_kv=8, head_dim=128, p=8, seed=3)
 GQA_DECODE = GqaWorkload("gqa_proj_T64", T=64, h=8192, n_q=64, n_kv=8, head_dim=128, p=8, seed=3)
+GQA_ATTN = GqaWorkload("gqa_attention_T4096", T=4096, h=8192, n_q=64, n_kv=8, head_dim=128, p=8, seed=6)
 GQA_BWD = GqaWorkload("gqa_proj_bwd_T4096", T=4096, h=8192, n_q=64, n_kv=8, head_dim=128, p=8, seed=5)
 BACKWARD = MlpWorkload("swiglu_mlp_bwd_T2048", T=2048, d=4096, ff=14336, p=8, act="swiglu",
                        dtype="bf16", seed=4)
 
-ALL = {w.name: w for w in (TINY, DECODE, PREFILL, GQA_PREFILL, GQA_DECODE, GQA_BWD, BACKWARD)}
+ALL = {w.name: w for w in (TINY, DECODE, PREFILL, GQA_PREFILL, GQA_DECODE, GQA_ATTN, GQA_BWD, BACKWARD)}
 
 
 def _gen(seed: int, stream: int) -> torch.Generator:
@@ -98,6 +99,7 @@ def normal(shape, std: float, seed: int, stream: int, dtype: str = "bf16") -> to
 S_X, S_W1, S_WUP, S_W2, S_DY = 1, 2, 3, 4, 5
 S_WQ, S_WK, S_WV, S_WO, S_ATTN = 11, 12, 13, 14, 15
 S_DQ, S_DK, S_DV = 16, 17, 18
+S_QKV = 19
 
 
 def mlp_unsharded(w: MlpWorkload, with_dy: bool = False, T: Optional[int] = None) -> Dict[str, torch.Tensor]:
@@ -164,6 +166,16 @@ def gqa_grads(w: GqaWorkload, T: Optional[int] = None) -> Dict[str, torch.Tensor
         "dv": normal((T, kvw), 1.0, w.seed, S_DV),
         "dy": normal((T, w.h), 1.0, w.seed, S_DY),
     }
+
+
+def attention_qkv(w: GqaWorkload, T: Optional[int] = None) -> torch.Tensor:
+    """One rank's fused projection output (T, (n_q/p + 2 n_kv/p) * head_dim):
+    rows [Q heads | K heads | V heads].  Drawn directly with the spread a
+    projection of N(0, 1) activations through N(0, 0.02^2) weights has
+    (std 0.02 * sqrt(h)), so the scaled scores have a realistic spread."""
+    T = w.T if T is None else T
+    width = (w.n_q // w.p + 2 * (w.n_kv // w.p)) * w.head_dim
+    return normal((T, width), WEIGHT_STD * w.h ** 0.5, w.seed, S_QKV)
 
 
 def row_subset(T: int, n: int, seed: int) -> List[int]:
