@@ -165,7 +165,7 @@ def main() -> int:
     log(f"bench: gate/up GEMM {k_ms * 1e3:.1f} us -> {k_gbs:.0f} GB/s")
 
     rows = {}
-    want = set(["prefill", "gqa", "bwd", "sum"]) if args.rows == "all" else (
+    want = set(["prefill", "gqa", "attn", "bwd", "sum"]) if args.rows == "all" else (
         set() if args.rows == "none" else set(args.rows.split(",")))
     steps_r = max(10, args.steps // 2)
 
@@ -256,6 +256,21 @@ def main() -> int:
                 rows[f"gqa_oproj_T{Tg}"] = {"us": round(to * 1e3, 2), "GB/s": round(bo / to / 1e6, 1),
                                             "frac_hbm": round(bo / to / 1e6 / HBM_PEAK_GBS, 4)}
             del wqkv, wo, xg, ag, qkv, og
+
+    if "attn" in want:
+        # local attention over one rank's 8 query heads and 1 KV head (70B-class GQA), T=4096
+        wa = W.GQA_ATTN
+        na_q, na_kv, hd_ = wa.n_q // wa.p, wa.n_kv // wa.p, wa.head_dim
+        qkva = gpu_normal((wa.T, (na_q + 2 * na_kv) * hd_), 1.81, 41, dev)
+        outa = torch.empty(wa.T, na_q * hd_, dtype=torch.bfloat16, device=dev)
+        for causal in (True, False):
+            t_ = time_gpu(lambda i: tp.tp_gqa_attention_fwd(qkva, outa, na_q, na_kv, hd_, causal, hd_ ** -0.5),
+                          steps_r, 3)
+            fl = 4 * (wa.T * (wa.T + 1) // 2 if causal else wa.T * wa.T) * hd_ * na_q
+            rows[f"attention_{'causal' if causal else 'full'}_T4096_8q1kv"] = {
+                "us": round(t_ * 1e3, 1), "TFLOP/s": round(fl / t_ / 1e9, 1),
+                "frac_mfma": round(fl / t_ / 1e9 / BF16_PEAK_TFLOPS, 4)}
+        del qkva, outa
 
     if "bwd" in want:
         wb = W.BACKWARD
