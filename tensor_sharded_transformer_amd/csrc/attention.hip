@@ -100,8 +100,9 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(const uint16_t* __restrict
                                                       int ldo, int T, int n_q, int group, int nqb, float c2) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, h = lane >> 5;
-  const int wave = (tid >> 6) & 3;          // query group inside the half
-  const int half = tid >> 8;                // which half of the key tiles
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, in a scalar register
+  const int wave = wv & 3;                  // query group inside the half
+  const int half = wv >> 2;                 // which half of the key tiles
   const int htid = tid & (HT - 1);
   const int bid = blockIdx.x;
   const int qb = nqb - 1 - bid / n_q;       // most key tiles first
@@ -151,7 +152,7 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(const uint16_t* __restrict
     const __amdgpu_buffer_rsrc_t rv = rsrc_at(qkv + (size_t)row0 * ld + vcol);
 #pragma unroll
     for (int c = 0; c < CHUNKS; ++c) {
-      const int slot0 = c * HT + (tid & ~63 & (HT - 1));   // this wave's first slot
+      const int slot0 = c * HT + wave * 64;   // this wave's first slot
       const bool krow_ok = row0 + krow_of[c] < T;
       const int vr = (c * HT + htid) >> 4;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)(stage + slot0 * 16), 16, krow_ok ? koff_g[c] : OOB, 0, 0, 0);
@@ -198,30 +199,31 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(const uint16_t* __restrict
         sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[kt], 0, 0, 0);
       }
     }
-    // scores in base-2 units; mask keys past the diagonal or the sequence
-    const bool need_mask = (CAUSAL && key0 + BKEY - 1 > qw) || key0 + BKEY > T;
+    // mask keys past the diagonal or the end of the sequence (raw scores)
+    if (__builtin_expect((CAUSAL && key0 + BKEY - 1 > qw) || key0 + BKEY > T, 0)) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 32 * kt + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (key >= T || (CAUSAL && key > myq)) sacc[kt][r] = -INFINITY;
+        }
+    }
     float mloc = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = sacc[kt][r] * c2;
-        if (need_mask) {
-          const int key = key0 + 32 * kt + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (key >= T || (CAUSAL && key > myq)) v = -INFINITY;
-        }
-        sacc[kt][r] = v;
-        mloc = fmaxf(mloc, v);
-      }
+      for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[kt][r]);
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc);
+    // running max in base-2 units (c2 = scale * log2 e > 0 keeps the order)
+    const float m_new = fmaxf(m_run, mloc * c2);
     const float m_use = m_new == -INFINITY ? 0.0f : m_new;
     float lsum = 0.0f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(sacc[kt][r] - m_use);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][r], c2, -m_use));
         sacc[kt][r] = p;
         lsum += p;
       }
