@@ -206,10 +206,12 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(const uint16_t* __restrict
   auto tile = [&](const char* kt_lds, int kb) __attribute__((always_inline)) {
     const char* vt_lds = kt_lds + C::K_BYTES;
     const int key0 = kb * BKEY;
-    // S^T = K Q^T for the tile's 32-key pieces
-    f32x16 sacc[C::NKT];
+    // S^T = K Q^T for the tile's 32-key pieces; with a single piece the two
+    // head-dim halves accumulate in separate chains (two MFMAs in flight)
+    constexpr int NCH = C::NKT == 1 ? 2 : 1;
+    f32x16 sacc[C::NKT * NCH];
 #pragma unroll
-    for (int kt = 0; kt < C::NKT; ++kt) sacc[kt] = f32x16{};
+    for (int kt = 0; kt < C::NKT * NCH; ++kt) sacc[kt] = f32x16{};
 #pragma unroll
     for (int s = 0; s < HD / 16; ++s) {
       const int dh = s >> 2, ss = s & 3;
@@ -217,9 +219,11 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(const uint16_t* __restrict
       for (int kt = 0; kt < C::NKT; ++kt) {
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kt_lds + dh * (C::K_BYTES / 2) + koff[kt] +
                                                           (((2 * ss + h) ^ ksw[kt]) << 4));
-        sacc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[kt], 0, 0, 0);
+        const int a = NCH == 2 ? dh : kt;
+        sacc[a] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sacc[a], 0, 0, 0);
       }
     }
+    if constexpr (NCH == 2) sacc[0] += sacc[1];
     // mask keys past the diagonal or the end of the sequence (raw scores)
     if (__builtin_expect((CAUSAL && key0 + BKEY - 1 > qw) || key0 + BKEY > T, 0)) {
 #pragma unroll
@@ -239,15 +243,16 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(const uint16_t* __restrict
     // running max in base-2 units (c2 = scale * log2 e > 0 keeps the order)
     const float m_new = fmaxf(m_run, mloc * c2);
     const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-    float lsum = 0.0f;
+    float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // four short add chains instead of one long one
 #pragma unroll
     for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][r], c2, -m_use));
         sacc[kt][r] = p;
-        lsum += p;
+        ls[r & 3] += p;
       }
+    const float lsum = (ls[0] + ls[1]) + (ls[2] + ls[3]);
     if (__any(m_new > m_run)) {  // some running max grew: rescale
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
       l_run *= alpha;
