@@ -617,6 +617,19 @@ def test_attention_T4096_rank_heads(causal):
     assert torch.equal(got, again)          # deterministic
 
 
+@pytest.mark.parametrize("T,n_q,n_kv,causal", [(4000, 8, 1, True), (4000, 8, 1, False), (1000, 8, 2, True),
+                                                (2113, 4, 4, False)])
+def test_attention_ragged_long(T, n_q, n_kv, causal):
+    """Lengths that leave partial key tiles and uneven key ranges across the
+    workgroup's groups, on 48 sampled query rows plus the first and last."""
+    qkv = W.normal((T, (n_q + 2 * n_kv) * 128), 1.81, 90 + T, 1)
+    scale = 128 ** -0.5
+    got = attn(cuda(qkv), n_q, n_kv, causal, scale)
+    rows = sorted(set(W.row_subset(T, 48, T) + [0, T - 1]))
+    ref = O.gqa_attention(qkv, n_q, n_kv, 128, causal, scale, rows=rows)
+    assert_close(got[rows], ref, BF16_TOL, f"attention T={T}")
+
+
 def test_attention_between_the_projections():
     """QKV projection -> local attention -> o_proj partial on one rank, chained
     through the C ABI, against the fp64 oracle chain on sampled rows.
