@@ -117,8 +117,12 @@ size_t tp_row_linear_partial_workspace(int64_t T, int64_t K_i, int64_t N, tp_dty
 /* Workspace (bytes) tp_mlp_shard_fwd needs for these sizes.  Always > 0 for
  * T > 0.  The workspace must be zero-filled before its FIRST use (e.g. with
  * tp_workspace_init); every call leaves its counter region zeroed again, so a
- * workspace can be reused by later calls on the same stream.  Calls that run
- * concurrently must not share a workspace. */
+ * workspace can be reused by later calls on the same stream, of any entry
+ * point and shape: the split-K arrival counters always sit in a region at the
+ * start of the workspace (at least 64 KiB) that no call writes anything else
+ * to, which holds for every call needing at most 16384 counters (all shapes
+ * up to 2^18 output columns).  Calls that run concurrently must not share a
+ * workspace. */
 size_t tp_mlp_shard_fwd_workspace(int64_t T, int64_t d, int64_t ff_i, tp_dtype dtype, tp_act act);
 
 /* One rank's feed-forward shard ([FFN] "Column split, then row split"):
@@ -195,6 +199,33 @@ tp_status tp_linear_shard_bwd(const void* x, const void* w, const void* dy, void
  * no-op. */
 tp_status tp_gqa_attention_fwd(const void* qkv, void* out, int64_t T, int n_q, int n_kv, int head_dim,
                                int causal, float scale, tp_stream stream);
+
+/* Sharded linears with fp8 weights, for decode-sized token counts (the
+ * quantized form of the column- and row-parallel linear that [MLX] mentions
+ * as the "quantized equivalent" of the sharded linear).  Weights are OCP
+ * e4m3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; 0x7F /
+ * 0xFF are NaN), (K, N) row-major, one byte each, with one fp32 scale per
+ * output column: W[k, n] = e4m3(wq[k, n]) * scale[n].  Activations stay
+ * bf16; products accumulate in fp32 and the scale multiplies each column's
+ * sum (exactly the product with the dequantized weights, up to rounding).
+ *   tp_col_linear_fp8:          y = act(x W + bias), or
+ *                               silu(x W) * (x W_up) for SWIGLU (wq_up and
+ *                               scale_up given iff SWIGLU; no bias then)
+ *   tp_row_linear_partial_fp8:  z_i = x_i W_i (no bias), out_dtype bf16/f32
+ * x (T, K) bf16, 16-byte aligned with K % 8 == 0; wq (K, N), 16-byte
+ * aligned with N % 16 == 0; scale (N) fp32; y / z_i (T, N).  All device.
+ * 1 <= T <= 64 (TP_ERR_UNSUPPORTED above; T == 0 is a no-op).  ws (device)
+ * of ws_bytes >= tp_linear_fp8_workspace(T, K, N, act), required, under the
+ * zero-fill and reuse rules of tp_mlp_shard_fwd's workspace.  Errors:
+ * TP_ERR_NULL, TP_ERR_SHAPE, TP_ERR_ACT, TP_ERR_DTYPE, TP_ERR_WORKSPACE,
+ * TP_ERR_UNSUPPORTED, TP_ERR_HIP. */
+size_t tp_linear_fp8_workspace(int64_t T, int64_t K, int64_t N, tp_act act);
+tp_status tp_col_linear_fp8(const void* x, const void* wq, const float* scale, const void* wq_up,
+                            const float* scale_up, const void* bias, void* y, void* ws, size_t ws_bytes,
+                            int64_t T, int64_t K, int64_t N_i, tp_act act, tp_stream stream);
+tp_status tp_row_linear_partial_fp8(const void* x_i, const void* wq_i, const float* scale_i, void* z_i,
+                                    void* ws, size_t ws_bytes, int64_t T, int64_t K_i, int64_t N,
+                                    tp_dtype out_dtype, tp_stream stream);
 
 /* Sum of the p full-shape partials, then the bias once ([KL] Y = sum_i Z_i;
  * [FFN] "One collective"; [MLX] bias after the sum).  This is the one-GPU

@@ -40,6 +40,8 @@ Readings where the pages are silent (also listed with the design notes):
     (replicated dy, local dx); no bias gradients.
   * Local attention is scaled dot-product softmax attention, optionally
     causal, with query head j reading KV head j // (n_q / n_kv).
+  * The "quantized equivalent" of a sharded linear is read as fp8 weights:
+    OCP E4M3 codes with one fp32 scale per output column, bf16 activations.
   * The normalization after the block's sum is RMSNorm with a learned scale
     and a caller-given epsilon, taken over the fp32/float64 sum.
 
@@ -175,7 +177,7 @@ def act_apply(a: np.ndarray, act: str, up: Optional[np.ndarray] = None) -> np.nd
 # computes the full-shape partial Z_i = X_i W_i and Y = sum_i Z_i.
 # ---------------------------------------------------------------------------
 def matmul(a: np.ndarray, b: np.ndarray) -> np.ndarray:
-    return np.matmul(np.asarray(a, dtype=F64), np.asarray(b, dtype=F64))
+    return np.matmul(to64(a), to64(b))
 
 
 def col_linear(x, w, w_up=None, bias=None, act: str = "none") -> np.ndarray:
@@ -199,6 +201,40 @@ def row_linear_partial(x_i, w_i) -> np.ndarray:
     [KL] first paragraph (row parallelism) and [FFN] "Second matmul,
     row-parallel"; no bias here ([MLX]: the bias is added after the sum)."""
     return matmul(x_i, w_i)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Values of OCP FP8 E4M3 codes (the "quantized" weights): bit 7 sign,
+    bits 6-3 exponent e with bias 7, bits 2-0 mantissa m.
+        e = 0:       (-1)^s * m/8 * 2^(1-7)       (subnormal, m = 0 is zero)
+        0 < e < 15:  (-1)^s * (1 + m/8) * 2^(e-7)
+        e = 15:      as above, except m = 7 is NaN (no infinities; max 448)
+    Written out from the format's definition (the pages only mention a
+    "quantized equivalent" of the sharded linear)."""
+    c = np.asarray(codes.cpu().numpy() if hasattr(codes, "cpu") else codes).astype(np.int64) & 0xFF
+    sign = np.where(c >> 7, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(F64)
+    val = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.power(2.0, e.astype(F64) - 7.0))
+    val = np.where((e == 15) & ((c & 7) == 7), np.nan, val)
+    return sign * val
+
+
+def dequant_e4m3(codes, scale) -> np.ndarray:
+    """W[k, n] = e4m3(codes[k, n]) * scale[n] (one scale per output column)."""
+    return e4m3_decode(codes) * to64(scale)[None, :]
+
+
+def col_linear_fp8(x, wq, scale, wq_up=None, scale_up=None, bias=None, act: str = "none") -> np.ndarray:
+    """The column-parallel linear of col_linear with fp8 weights."""
+    w = dequant_e4m3(wq, scale)
+    w_up = dequant_e4m3(wq_up, scale_up) if wq_up is not None else None
+    return col_linear(x, w, w_up, bias, act)
+
+
+def row_linear_partial_fp8(x_i, wq_i, scale_i) -> np.ndarray:
+    """The row-parallel partial of row_linear_partial with fp8 weights."""
+    return row_linear_partial(x_i, dequant_e4m3(wq_i, scale_i))
 
 
 def partial_sum(zs: Sequence[np.ndarray], bias=None) -> np.ndarray:

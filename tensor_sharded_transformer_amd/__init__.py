@@ -14,10 +14,12 @@ from .binding import (  # noqa: F401
     tp_abi_version,
     tp_act_inplace,
     tp_col_linear,
+    tp_col_linear_fp8,
     tp_col_linear_workspace,
     tp_gqa_attention_fwd,
     tp_gqa_shard,
     tp_linear_shard_bwd,
+    tp_linear_fp8_workspace,
     tp_linear_shard_bwd_workspace,
     tp_mlp_shard_bwd,
     tp_mlp_shard_bwd_workspace,
@@ -25,6 +27,7 @@ from .binding import (  # noqa: F401
     tp_mlp_shard_fwd_workspace,
     tp_partial_sum,
     tp_row_linear_partial,
+    tp_row_linear_partial_fp8,
     tp_row_linear_partial_workspace,
     tp_rs_residual_rmsnorm,
     tp_shard_range,

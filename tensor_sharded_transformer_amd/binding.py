@@ -51,6 +51,9 @@ SIGNATURES = {
     "tp_linear_shard_bwd_workspace": (c_sz, [c_i64, c_i64, c_i64, c_int]),
     "tp_linear_shard_bwd": (c_int, [c_p, c_p, c_p, c_p, c_p, c_p, c_sz, c_i64, c_i64, c_i64, c_int, c_p]),
     "tp_gqa_attention_fwd": (c_int, [c_p, c_p, c_i64, c_int, c_int, c_int, c_int, ctypes.c_float, c_p]),
+    "tp_linear_fp8_workspace": (c_sz, [c_i64, c_i64, c_i64, c_int]),
+    "tp_col_linear_fp8": (c_int, [c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_sz, c_i64, c_i64, c_i64, c_int, c_p]),
+    "tp_row_linear_partial_fp8": (c_int, [c_p, c_p, c_p, c_p, c_p, c_sz, c_i64, c_i64, c_i64, c_int, c_p]),
     "tp_partial_sum": (c_int, [ctypes.POINTER(c_p), c_int, c_p, c_p, c_i64, c_i64, c_int, c_int, c_p]),
     "tp_rs_residual_rmsnorm": (c_int, [ctypes.POINTER(c_p), c_int, c_int, c_p, c_p, c_p, ctypes.c_float, c_p, c_p,
                                        c_i64, c_i64, c_int, c_int, c_p]),
@@ -249,6 +252,44 @@ def tp_gqa_attention_fwd(qkv, out, n_q: int, n_kv: int, head_dim: int, causal: b
     _check(load().tp_gqa_attention_fwd(_ptr(qkv), _ptr(out), T, n_q, n_kv, head_dim, int(bool(causal)), scale,
                                        _stream()))
     return out
+
+
+def _fp8_codes(t: torch.Tensor, name: str) -> None:
+    if t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+        raise ValueError(f"{name} must hold e4m3 codes (uint8 or float8_e4m3fn)")
+
+
+def tp_linear_fp8_workspace(T: int, K: int, N: int, act: str = "none") -> int:
+    return load().tp_linear_fp8_workspace(T, K, N, ACT[act])
+
+
+def tp_col_linear_fp8(x, wq, scale, wq_up, scale_up, bias, y, act: str, ws: torch.Tensor):
+    """y = act(x (e4m3(wq) * scale) [+ bias]); SWIGLU: silu(x W) * (x W_up)."""
+    T, K = x.shape
+    N = wq.shape[1]
+    _fp8_codes(wq, "wq")
+    _shape(wq, (K, N), "wq")
+    _shape(scale, (N,), "scale")
+    _shape(y, (T, N), "y")
+    if wq_up is not None:
+        _fp8_codes(wq_up, "wq_up")
+        _shape(wq_up, (K, N), "wq_up")
+    _check(load().tp_col_linear_fp8(_ptr(x), _ptr(wq), _ptr(scale), _ptr(wq_up), _ptr(scale_up), _ptr(bias), _ptr(y),
+                                    _ptr(ws), ws.numel() if ws is not None else 0, T, K, N, ACT[act], _stream()))
+    return y
+
+
+def tp_row_linear_partial_fp8(x_i, wq_i, scale_i, z_i, ws: torch.Tensor):
+    """z_i = x_i (e4m3(wq_i) * scale_i), the full-shape partial."""
+    T, K = x_i.shape
+    N = wq_i.shape[1]
+    _fp8_codes(wq_i, "wq_i")
+    _shape(wq_i, (K, N), "wq_i")
+    _shape(scale_i, (N,), "scale_i")
+    _shape(z_i, (T, N), "z_i")
+    _check(load().tp_row_linear_partial_fp8(_ptr(x_i), _ptr(wq_i), _ptr(scale_i), _ptr(z_i), _ptr(ws),
+                                            ws.numel() if ws is not None else 0, T, K, N, _dt(z_i), _stream()))
+    return z_i
 
 
 def tp_partial_sum(zs: Sequence[torch.Tensor], bias, y):

@@ -56,8 +56,13 @@ GemmParams base_params() {
 }
 
 // Workspace layout shared by the entry points:
-//   [ buffers ... ][ split-K counters (zero between calls) ][ split-K partials ]
+//   [ split-K counters (zero between calls) ][ buffers ... ][ split-K partials ]
 //   [ packed activations of the decode kernel ]
+// The counter region always starts at offset 0 and spans at least
+// CNT_RESERVE bytes, and no entry point writes anything else there, so one
+// workspace can serve any sequence of calls (of any entry point and shape)
+// as long as no call needs more than CNT_RESERVE / 4 arrival counters.
+constexpr size_t CNT_RESERVE = 64 * 1024;
 struct SplitNeeds {
   size_t part_bytes = 0;
   size_t n_tiles = 0;
@@ -69,7 +74,10 @@ struct SplitNeeds {
     if (nt > n_tiles) n_tiles = nt;
     if (pk > pack_bytes) pack_bytes = pk;
   }
-  size_t counter_bytes() const { return tpk::align_up(n_tiles * sizeof(int), 256); }
+  size_t counter_bytes() const {
+    const size_t b = tpk::align_up(n_tiles * sizeof(int), 256);
+    return b > CNT_RESERVE ? b : CNT_RESERVE;
+  }
   size_t partial_bytes() const { return tpk::align_up(part_bytes, 256); }
   size_t packed_bytes() const { return tpk::align_up(pack_bytes, 256); }
 };
@@ -97,7 +105,7 @@ hipError_t run_gemm(int dtype, const GemmParams& p, const GemmPlan& plan, GemmKi
 // ---- forward shard layout ----------------------------------------------------
 struct FwdLayout {
   GemmPlan p1, p2;
-  size_t h_bytes = 0, cnt_off = 0, part_off = 0, pack_off = 0, pack2_off = 0, total = 0;
+  size_t h_bytes = 0, h_off = 0, cnt_off = 0, part_off = 0, pack_off = 0, pack2_off = 0, total = 0;
   bool fuse_pack = false;  // the column GEMM writes h straight into the row GEMM's packed A
 };
 
@@ -113,8 +121,9 @@ FwdLayout fwd_layout(int64_t T, int64_t d, int64_t ff_i, int dtype, int act, boo
   sn.add(L.p1, (int)T, (int)ff_i, (int)d, dual);
   sn.add(L.p2, (int)T, (int)d, (int)ff_i, false);
   L.h_bytes = tpk::align_up((size_t)T * ff_i * esize(dtype), 256);
-  L.cnt_off = L.h_bytes;
-  L.part_off = L.cnt_off + sn.counter_bytes();
+  L.cnt_off = 0;
+  L.h_off = sn.counter_bytes();
+  L.part_off = L.h_off + L.h_bytes;
   L.pack_off = L.part_off + sn.partial_bytes();
   L.pack2_off = L.pack_off + s1.packed_bytes();
   L.total = L.pack2_off + s2.packed_bytes();
@@ -126,7 +135,7 @@ FwdLayout fwd_layout(int64_t T, int64_t d, int64_t ff_i, int dtype, int act, boo
 
 struct BwdLayout {
   GemmPlan pa, pb, pc, pd;
-  size_t dgu_bytes = 0, h_off = 0, cnt_off = 0, part_off = 0, pack_off = 0, total = 0;
+  size_t dgu_bytes = 0, dgu_off = 0, h_off = 0, cnt_off = 0, part_off = 0, pack_off = 0, total = 0;
 };
 
 BwdLayout bwd_layout(int64_t T, int64_t d, int64_t ff_i, int dtype, int act) {
@@ -142,9 +151,10 @@ BwdLayout bwd_layout(int64_t T, int64_t d, int64_t ff_i, int dtype, int act) {
   sn.add(L.pc, (int)d, (int)ff_i, (int)T, sw);
   sn.add(L.pd, (int)T, (int)d, (int)((sw ? 2 : 1) * ff_i), false);
   L.dgu_bytes = tpk::align_up((size_t)T * ff_i * (sw ? 2 : 1) * esize(dtype), 256);
-  L.h_off = L.dgu_bytes;
-  L.cnt_off = L.h_off + tpk::align_up((size_t)T * ff_i * esize(dtype), 256);
-  L.part_off = L.cnt_off + sn.counter_bytes();
+  L.cnt_off = 0;
+  L.dgu_off = sn.counter_bytes();
+  L.h_off = L.dgu_off + L.dgu_bytes;
+  L.part_off = L.h_off + tpk::align_up((size_t)T * ff_i * esize(dtype), 256);
   L.pack_off = L.part_off + sn.partial_bytes();
   L.total = L.pack_off + sn.packed_bytes();
   return L;
@@ -198,7 +208,7 @@ SingleWs single_ws(int dtype, int M, int N, int K, bool dual, bool vec) {
   SplitNeeds sn;
   sn.add(W.plan, M, N, K, dual);
   if (needs_ws(W.plan)) {
-    W.cnt_bytes = sn.n_tiles ? sn.counter_bytes() : 0;
+    W.cnt_bytes = sn.counter_bytes();
     W.part_bytes = sn.partial_bytes();
     W.total = W.cnt_bytes + W.part_bytes + sn.packed_bytes();
   }
@@ -209,6 +219,45 @@ tp_status check_common(int dtype, int act) {
   if (!valid_dtype(dtype)) return fail(TP_ERR_DTYPE, "unknown dtype %d", dtype);
   if (!valid_act(act)) return fail(TP_ERR_ACT, "unknown act %d", act);
   return TP_OK;
+}
+
+// Shared checks and launch of the fp8-weight decode GEMM.
+tp_status linear_fp8(const char* who, const void* x, const void* wq, const float* scale, const void* wq_up,
+                     const float* scale_up, const void* bias, void* y, void* ws, size_t ws_bytes, int64_t T, int64_t K,
+                     int64_t N, int act, bool out_f32, GemmKind kind, hipStream_t s) {
+  if (!dim_ok(T) || !dim_ok(K) || !dim_ok(N) || !prod_ok(K, N))
+    return fail(TP_ERR_SHAPE, "%s: sizes out of range", who);
+  if (T > tpk::STREAM_MAX_M)
+    return fail(TP_ERR_UNSUPPORTED, "%s: T=%lld (fp8 weights are built for decode sizes, T <= %d)", who,
+                (long long)T, tpk::STREAM_MAX_M);
+  if (T == 0 || N == 0) return TP_OK;
+  if (!x || !wq || !scale || !y || (kind == tpk::GK_FWD_SWIGLU && (!wq_up || !scale_up)))
+    return fail(TP_ERR_NULL, "%s: null input or output pointer", who);
+  if (N % 16 || K % 8 || !aligned16(x) || !aligned16(wq) || (wq_up && !aligned16(wq_up)))
+    return fail(TP_ERR_UNSUPPORTED, "%s: needs N %% 16 == 0, K %% 8 == 0 and 16-byte aligned x and weights", who);
+  GemmParams p = base_params();
+  p.A0 = x;
+  p.lda = K;
+  p.B0 = wq;
+  p.B1 = kind == tpk::GK_FWD_SWIGLU ? wq_up : nullptr;
+  p.ldb = N;
+  p.K0 = (int)K;
+  p.M = (int)T;
+  p.N = (int)N;
+  p.C = y;
+  p.ldc = N;
+  p.bias = bias;
+  p.act = act;
+  p.vecA = p.vecB = 1;
+  p.b_fp8 = 1;
+  p.bscale0 = scale;
+  p.bscale1 = kind == tpk::GK_FWD_SWIGLU ? scale_up : nullptr;
+  SingleWs W = single_ws(TP_BF16, (int)T, (int)N, (int)K, kind == tpk::GK_FWD_SWIGLU, true);
+  if (W.plan.kernel != tpk::KERNEL_DECODE) return fail(TP_ERR_UNSUPPORTED, "%s: no fp8 kernel for this shape", who);
+  if (!ws) return fail(TP_ERR_WORKSPACE, "%s: workspace required (%zu bytes)", who, W.total);
+  tp_status ws_st = W.bind(p, ws, ws_bytes, who);
+  if (ws_st != TP_OK) return ws_st;
+  return hip_status(tpk::gemm_bf16(p, W.plan, kind, out_f32, s), who);
 }
 
 }  // namespace
@@ -370,6 +419,33 @@ tp_status tp_row_linear_partial(const void* x_i, const void* w_i, void* z_i, voi
                     "tp_row_linear_partial");
 }
 
+// ---- fp8-weight linears (decode sizes) --------------------------------------------
+size_t tp_linear_fp8_workspace(int64_t T, int64_t K, int64_t N, tp_act act) {
+  if (!valid_act(act) || T < 1 || T > tpk::STREAM_MAX_M || !dim_ok(K) || !dim_ok(N)) return 0;
+  return single_ws(TP_BF16, (int)T, (int)N, (int)K, act == TP_ACT_SWIGLU, true).total;
+}
+
+
+tp_status tp_col_linear_fp8(const void* x, const void* wq, const float* scale, const void* wq_up,
+                            const float* scale_up, const void* bias, void* y, void* ws, size_t ws_bytes, int64_t T,
+                            int64_t K, int64_t N_i, tp_act act, tp_stream stream) {
+  if (!valid_act(act)) return fail(TP_ERR_ACT, "tp_col_linear_fp8: unknown act %d", act);
+  const bool sw = act == TP_ACT_SWIGLU;
+  if (sw != (wq_up != nullptr) || sw != (scale_up != nullptr))
+    return fail(TP_ERR_ACT, "tp_col_linear_fp8: wq_up and scale_up must be given iff SWIGLU");
+  if (sw && bias) return fail(TP_ERR_ACT, "tp_col_linear_fp8: a bias is not defined for SWIGLU");
+  return linear_fp8("tp_col_linear_fp8", x, wq, scale, wq_up, scale_up, bias, y, ws, ws_bytes, T, K, N_i, act, false,
+                    sw ? tpk::GK_FWD_SWIGLU : tpk::GK_FWD_ACT, reinterpret_cast<hipStream_t>(stream));
+}
+
+tp_status tp_row_linear_partial_fp8(const void* x_i, const void* wq_i, const float* scale_i, void* z_i, void* ws,
+                                    size_t ws_bytes, int64_t T, int64_t K_i, int64_t N, tp_dtype out_dtype,
+                                    tp_stream stream) {
+  if (!valid_dtype(out_dtype)) return fail(TP_ERR_DTYPE, "tp_row_linear_partial_fp8: unknown dtype");
+  return linear_fp8("tp_row_linear_partial_fp8", x_i, wq_i, scale_i, nullptr, nullptr, nullptr, z_i, ws, ws_bytes, T,
+                    K_i, N, TP_ACT_NONE, out_dtype == TP_F32, tpk::GK_FWD_STORE, reinterpret_cast<hipStream_t>(stream));
+}
+
 // ---- sum of partials -------------------------------------------------------------
 tp_status tp_partial_sum(const void* const* z, int p, const void* bias, void* y, int64_t T, int64_t N,
                          tp_dtype in_dtype, tp_dtype out_dtype, tp_stream stream) {
@@ -442,7 +518,7 @@ tp_status tp_mlp_shard_fwd(const void* x, const void* w1_i, const void* w_up_i, 
     return fail(TP_ERR_WORKSPACE, "tp_mlp_shard_fwd: workspace of %zu bytes < %zu needed", ws_bytes, L.total);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* base = reinterpret_cast<char*>(ws);
-  void* h = base;
+  void* h = base + L.h_off;
 
   GemmParams p1 = base_params();
   p1.A0 = x;
@@ -524,7 +600,7 @@ tp_status tp_mlp_shard_bwd(const void* x, const void* w1_i, const void* w_up_i, 
   if (ws_bytes < L.total)
     return fail(TP_ERR_WORKSPACE, "tp_mlp_shard_bwd: workspace of %zu bytes < %zu needed", ws_bytes, L.total);
   char* base = reinterpret_cast<char*>(ws);
-  char* dgu = base;                 // (T, 2 ff_i) [dG | dU] for SWIGLU, (T, ff_i) dA otherwise
+  char* dgu = base + L.dgu_off;     // (T, 2 ff_i) [dG | dU] for SWIGLU, (T, ff_i) dA otherwise
   char* h = base + L.h_off;         // (T, ff_i) recomputed activation
   char* cnt = base + L.cnt_off;
   char* part = base + L.part_off;

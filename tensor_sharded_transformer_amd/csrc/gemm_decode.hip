@@ -20,6 +20,10 @@
 //  * Weights are n-contiguous while the MFMA wants 8 consecutive k of one
 //    column per lane: each wave copies each 16-row slab into a private LDS
 //    tile and reads the operand back with ds_read_b64_tr_b16.
+//  * fp8 weights (OCP e4m3 codes with per-column scales) travel the same
+//    way at half the bytes: a k-step of one matrix is one 16-byte load per
+//    lane, decoded to bf16 in registers (exact) just before the LDS copy;
+//    the scales multiply the summed tile before the epilogue.
 //  * The waves' accumulators meet in LDS; each wave then owns one output
 //    fragment (gate and up together), sums it over the waves in wave order,
 //    and takes it through the split-K exchange (last-arriving workgroup adds
@@ -70,17 +74,41 @@ __device__ __forceinline__ void load_a(const u32x4* apk, int step, int lane, u32
   for (int i = 0; i < MT; ++i) a[i] = apk[(step * MT + i) * 64 + lane];
 }
 
+// Registers of one k-step of weights: NW 16-byte chunks per matrix (bf16),
+// one (fp8 codes).
+template <bool DUAL, bool F8>
+using WRegs = WFrag<F8 ? (DUAL ? 2 : 1) : (DUAL ? 2 * NW : NW)>;
+
 // One k-step of MFMAs: the wave's weight slab goes through its private LDS
-// tiles (written row-major, read back transposed) into the B operands.
-template <int MT, bool DUAL>
-__device__ __forceinline__ void mma_step(char* my, int lane, const WFrag<DUAL ? 2 * NW : NW>& f,
-                                         const u32x4 (&a)[MT], f32x16 (&acc)[MT][DUAL ? 2 * NW : NW]) {
+// tiles (written row-major, read back transposed) into the B operands; fp8
+// codes are decoded to bf16 on the way in.
+template <int MT, bool DUAL, bool F8>
+__device__ __forceinline__ void mma_step(char* my, int lane, const WRegs<DUAL, F8>& f, const u32x4 (&a)[MT],
+                                         f32x16 (&acc)[MT][DUAL ? 2 * NW : NW]) {
   constexpr int NF = DUAL ? 2 * NW : NW;
   constexpr int TB = tile_bytes<NW>();
+  if constexpr (F8) {
+    static_assert(NW == 2, "fp8 k-step layout assumes 64-column strips");
+    // lane: row lane/4, columns 16 (lane%4) .. +15 = bf16 chunks 2 (lane%4) and 2 (lane%4) + 1
+    const int row = lane >> 2, c0 = (lane & 3) * 2;
 #pragma unroll
-  for (int mat = 0; mat < (DUAL ? 2 : 1); ++mat)
+    for (int mat = 0; mat < (DUAL ? 2 : 1); ++mat) {
+      uint32_t w[8];
 #pragma unroll
-    for (int u = 0; u < NW; ++u) *reinterpret_cast<u32x4*>(my + w_lds_off<NW>(mat, u, lane)) = f.b[mat * NW + u];
+      for (int q = 0; q < 4; ++q) fp8x4_to_bf16x4(f.b[mat][q], &w[2 * q], &w[2 * q + 1]);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int c = c0 + h;
+        *reinterpret_cast<u32x4*>(my + (mat * NW + c / 4) * TB + row * 64 + (c % 4) * 16) =
+            u32x4{w[4 * h], w[4 * h + 1], w[4 * h + 2], w[4 * h + 3]};
+      }
+    }
+  } else {
+#pragma unroll
+    for (int mat = 0; mat < (DUAL ? 2 : 1); ++mat)
+#pragma unroll
+      for (int u = 0; u < NW; ++u) *reinterpret_cast<u32x4*>(my + w_lds_off<NW>(mat, u, lane)) = f.b[mat * NW + u];
+  }
   bf16x8 bv[NF];
 #pragma unroll
   for (int j = 0; j < NF; ++j) bv[j] = read_b_frag(my + j * TB, lane);
@@ -94,14 +122,20 @@ __device__ __forceinline__ void mma_step(char* my, int lane, const WFrag<DUAL ? 
 
 // The last, partial k-step of K (packed A is zero past K; weight rows past K
 // read as zero).
-template <int MT, bool DUAL>
+template <bool DUAL, bool F8, bool TAIL>
+__device__ __forceinline__ void load_wregs(WRegs<DUAL, F8>& f, const GemmParams& p, int step, int n0, int lane) {
+  if constexpr (F8) load_w8<DUAL, TAIL>(f, p, step, n0, lane);
+  else load_w<NW, DUAL, TAIL>(f, p, step, n0, lane);
+}
+
+template <int MT, bool DUAL, bool F8>
 __device__ __forceinline__ void tail_step(const GemmParams& p, int n0, int step, int lane, char* my,
                                           f32x16 (&acc)[MT][DUAL ? 2 * NW : NW]) {
-  WFrag<DUAL ? 2 * NW : NW> ft;
+  WRegs<DUAL, F8> ft;
   u32x4 at[MT];
-  load_w<NW, DUAL, true>(ft, p, step, n0, lane);
+  load_wregs<DUAL, F8, true>(ft, p, step, n0, lane);
   load_a<MT>(reinterpret_cast<const u32x4*>(p.apk), step, lane, at);
-  mma_step<MT, DUAL>(my, lane, ft, at, acc);
+  mma_step<MT, DUAL, F8>(my, lane, ft, at, acc);
 }
 
 // Main loop of one wave over k-steps [w_begin, w_end): a ring of DEPTH steps
@@ -112,7 +146,7 @@ __device__ __forceinline__ void tail_step(const GemmParams& p, int n0, int step,
 // Each wave walks its steps from a rotated start, so the workgroups of a
 // launch do not all read the same weight rows at the same time (with
 // power-of-two row strides that lockstep concentrates on few DRAM banks).
-template <int MT, bool DUAL, typename Ready>
+template <int MT, bool DUAL, bool F8, typename Ready>
 __device__ __forceinline__ void ring_loop(const GemmParams& p, int n0, int w_begin, int w_end, int rot_seed, int lane,
                                           char* my, f32x16 (&acc)[MT][DUAL ? 2 * NW : NW], Ready&& ready) {
   constexpr int NF = DUAL ? 2 * NW : NW;
@@ -125,23 +159,23 @@ __device__ __forceinline__ void ring_loop(const GemmParams& p, int n0, int w_beg
       const int q = min(it, nw - 1) + rot;
       return w_begin + (q >= nw ? q - nw : q);
     };
-    WFrag<NF> fr[DEPTH];
+    WRegs<DUAL, F8> fr[DEPTH];
     u32x4 fa[DEPTH][MT];
-    static_for<0, DEPTH>([&](auto d) { load_w<NW, DUAL, false>(fr[d], p, phys(d), n0, lane); });
+    static_for<0, DEPTH>([&](auto d) { load_wregs<DUAL, F8, false>(fr[d], p, phys(d), n0, lane); });
     ready();
     static_for<0, DEPTH>([&](auto d) { load_a<MT>(apk, phys(d), lane, fa[d]); });
     for (int it = 0; it < nw; it += DEPTH) {
       static_for<0, DEPTH>([&](auto d) {
-        if (it + (int)d < nw) mma_step<MT, DUAL>(my, lane, fr[d], fa[d], acc);
+        if (it + (int)d < nw) mma_step<MT, DUAL, F8>(my, lane, fr[d], fa[d], acc);
         const int st = phys(it + DEPTH + (int)d);
-        load_w<NW, DUAL, false>(fr[d], p, st, n0, lane);
+        load_wregs<DUAL, F8, false>(fr[d], p, st, n0, lane);
         load_a<MT>(apk, st, lane, fa[d]);
       });
     }
   } else {
     ready();
   }
-  if (w_end > full_end && w_end > w_begin) tail_step<MT, DUAL>(p, n0, w_end - 1, lane, my, acc);
+  if (w_end > full_end && w_end > w_begin) tail_step<MT, DUAL, F8>(p, n0, w_end - 1, lane, my, acc);
 }
 
 // After a workgroup's main loops: the waves' accumulators meet in LDS, wave u
@@ -149,7 +183,7 @@ __device__ __forceinline__ void ring_loop(const GemmParams& p, int n0, int w_beg
 // in wave order, takes it through the split-K exchange (the last-arriving
 // split adds the splits in split order, so results are bitwise
 // reproducible) and stores it.
-template <int MT, bool DUAL, int EPI, typename OutT>
+template <int MT, bool DUAL, bool F8, int EPI, typename OutT>
 __device__ __forceinline__ void decode_finish(const GemmParams& p, int strip, int split, int nsplit, int lane, int wave,
                                               char* my, float* red, f32x16 (&acc)[MT][DUAL ? 2 * NW : NW]) {
   constexpr int NF = DUAL ? 2 * NW : NW;
@@ -182,6 +216,16 @@ __device__ __forceinline__ void decode_finish(const GemmParams& p, int strip, in
 
   if (nsplit > 1) {
     if (!splitk_exchange<NOUT>(p, strip * UNITS + wave, split, nsplit, lane, out)) return;
+  }
+  if constexpr (F8) {  // per-column scales of the fp8 weights (lane % 32 is the tile column)
+    const int nc = min(n0 + uj * 32 + (lane & 31), p.N - 1);
+    const float s0 = p.bscale0[nc];
+    const float s1 = DUAL ? p.bscale1[nc] : 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      out[0][r] *= s0;
+      if constexpr (DUAL) out[NOUT - 1][r] *= s1;
+    }
   }
 
   // Common case (a bf16 output and nothing else to write): the 32x32 tile
@@ -272,7 +316,7 @@ __device__ __forceinline__ void decode_tile(const GemmParams& p, int nstrips, in
   *nsplit = p.split_base + (p.slow_extra > 0 && (*strip & 7) == p.slow_first ? p.slow_extra : 0);
 }
 
-template <int MT, bool DUAL, int EPI, typename OutT>
+template <int MT, bool DUAL, bool F8, int EPI, typename OutT>
 __global__ __launch_bounds__(KW * 64) void gemm_decode_kernel(const GemmParams p) {
   constexpr int NF = DUAL ? 2 * NW : NW;
   constexpr int TB = tile_bytes<NW>();
@@ -293,8 +337,8 @@ __global__ __launch_bounds__(KW * 64) void gemm_decode_kernel(const GemmParams p
   float* red = reinterpret_cast<float*>(smem + KW * NF * TB);
   f32x16 acc[MT][NF];
   zero_acc<MT, DUAL>(acc);
-  ring_loop<MT, DUAL>(p, strip * NW * 32, w_begin, w_end, strip * 7 + wave * 3, lane, my, acc, [] {});
-  decode_finish<MT, DUAL, EPI, OutT>(p, strip, split, nsplit, lane, wave, my, red, acc);
+  ring_loop<MT, DUAL, F8>(p, strip * NW * 32, w_begin, w_end, strip * 7 + wave * 3, lane, my, acc, [] {});
+  decode_finish<MT, DUAL, F8, EPI, OutT>(p, strip, split, nsplit, lane, wave, my, red, acc);
 }
 
 // Column strips whose weight bytes have address bits 7..9 equal to 3 stream
@@ -312,7 +356,7 @@ int decode_split(GemmParams& p, const GemmPlan& plan) {
   const int nslow = p.slow_first < nstrips ? (nstrips - p.slow_first + 7) / 8 : 0;
   // only while the grid stays within one workgroup per CU, and for splits of
   // at most 4 (finer splits already keep the slow strips' tiles short)
-  const bool extra = plan.splitk > 1 && plan.splitk <= 4 && ((b0 ^ b1) >> 7 & 7) == 0 && nslow > 0 &&
+  const bool extra = !p.b_fp8 && plan.splitk > 1 && plan.splitk <= 4 && ((b0 ^ b1) >> 7 & 7) == 0 && nslow > 0 &&
                      nstrips * plan.splitk + nslow * TP_DECODE_SLOW_EXTRA <= 256;
   p.slow_extra = extra ? TP_DECODE_SLOW_EXTRA : 0;
   p.splitk = plan.splitk + p.slow_extra;
@@ -332,7 +376,10 @@ hipError_t launch_decode_mt(const GemmParams& p, const GemmPlan& plan, hipStream
   }
   GemmParams pd = p;
   const int nwg = decode_split(pd, plan);
-  hipLaunchKernelGGL((gemm_decode_kernel<MT, DUAL, EPI, OutT>), dim3(nwg), dim3(KW * 64), 0, s, pd);
+  if (p.b_fp8)
+    hipLaunchKernelGGL((gemm_decode_kernel<MT, DUAL, true, EPI, OutT>), dim3(nwg), dim3(KW * 64), 0, s, pd);
+  else
+    hipLaunchKernelGGL((gemm_decode_kernel<MT, DUAL, false, EPI, OutT>), dim3(nwg), dim3(KW * 64), 0, s, pd);
   return hipGetLastError();
 }
 

@@ -51,6 +51,32 @@ __device__ __forceinline__ void load_w(WFrag<DUAL ? 2 * NW : NW>& fr, const Gemm
   }
 }
 
+// fp8 weights (one byte per value, NW == 2): one k-step of one matrix is a
+// single 1 KB instruction, lane l reading row l/4, columns 16 (l%4) .. +15 of
+// the strip.  Raw codes stay in registers until the k-step is consumed.
+template <bool DUAL, bool TAIL>
+__device__ __forceinline__ void load_w8(WFrag<DUAL ? 2 : 1>& fr, const GemmParams& p, int step, int n0, int lane) {
+  const int n = min(n0 + (lane & 3) * 16, p.N - 16);
+  const int kb = step * 16 + (lane >> 2);
+#pragma unroll
+  for (int mat = 0; mat < (DUAL ? 2 : 1); ++mat) {
+    const uint8_t* B = reinterpret_cast<const uint8_t*>(mat ? p.B1 : p.B0);
+    if (!TAIL || kb < p.K0) fr.b[mat] = *reinterpret_cast<const u32x4*>(B + (int64_t)kb * p.ldb + n);
+    else fr.b[mat] = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// Four fp8 (e4m3) codes -> four bf16 values (exact: every e4m3 value is a
+// bf16 value), in two 32-bit words, low code first.
+__device__ __forceinline__ void fp8x4_to_bf16x4(uint32_t w, uint32_t* lo, uint32_t* hi) {
+  typedef float f32x2_ __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_ __attribute__((ext_vector_type(2)));
+  const f32x2_ a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const f32x2_ b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  *lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(a, bf16x2_));
+  *hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(b, bf16x2_));
+}
+
 // LDS position of this lane's 16 bytes of instruction u of matrix `mat`.
 template <int NW>
 __device__ __forceinline__ int w_lds_off(int mat, int u, int lane) {

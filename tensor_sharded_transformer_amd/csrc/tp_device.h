@@ -84,6 +84,9 @@ struct GemmParams {
   int split_base;      // decode kernel: K splits of a column strip (splitk = split slots per tile) ...
   int slow_first;      //   ... except strips slow_first + 8j (weight bytes of the slow address class),
   int slow_extra;      //   which get slow_extra more
+  int b_fp8;           // decode kernel: B0/B1 hold fp8 (OCP e4m3) codes, ldb in elements (= bytes) ...
+  const float* bscale0;  //   ... with per-column scales applied to the sums (B0)
+  const float* bscale1;  //   (B1)
 };
 
 // Calls f(integral_constant<int, I>) for I = 0 .. N-1, so array indices in

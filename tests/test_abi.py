@@ -199,6 +199,25 @@ def test_gqa_attention_validation(lib):
     assert f(None, None, 0, 8, 1, 128, 1, sc, None) == OK              # T == 0
 
 
+def test_linear_fp8_validation(lib):
+    f = lib.tp_col_linear_fp8
+    ws = lib.tp_linear_fp8_workspace(64, 1024, 256, 0)
+    assert ws > 0 and lib.tp_linear_fp8_workspace(65, 1024, 256, 0) == 0
+    args = (FAKE, ctypes.c_size_t(ws), 64, 1024, 256)
+    assert f(FAKE, FAKE, FAKE, None, None, None, FAKE, *args, 9, None) == ACTE          # unknown act
+    assert f(FAKE, FAKE, FAKE, None, None, None, FAKE, *args, 3, None) == ACTE          # SWIGLU without wq_up
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, *args, 3, None) == ACTE          # bias with SWIGLU
+    assert f(FAKE, FAKE, None, None, None, None, FAKE, *args, 0, None) == NULL          # no scale
+    assert f(FAKE, FAKE, FAKE, None, None, None, FAKE, FAKE, ws, 65, 1024, 256, 0, None) == 6   # T > 64
+    assert f(FAKE, FAKE, FAKE, None, None, None, FAKE, FAKE, ws, 64, 1024, 264, 0, None) == 6   # N % 16
+    assert f(FAKE, FAKE, FAKE, None, None, None, FAKE, None, 0, 64, 1024, 256, 0, None) == WS
+    assert f(FAKE, FAKE, FAKE, None, None, None, FAKE, FAKE, ws - 1, 64, 1024, 256, 0, None) == WS
+    assert f(None, None, None, None, None, None, None, None, 0, 0, 1024, 256, 0, None) == OK   # T == 0
+    g = lib.tp_row_linear_partial_fp8
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, ws, 64, 1024, 256, 7, None) == DTYPE
+    assert g(FAKE, FAKE, None, FAKE, FAKE, ws, 64, 1024, 256, 0, None) == NULL
+
+
 def test_status_strings(lib):
     for s in range(8):
         assert lib.tp_status_string(s)

@@ -661,3 +661,91 @@ def test_attention_between_the_projections():
     chain_tol = (BF16_TOL[0] + 4.8e-3, BF16_TOL[1] + 7.3e-3)
     assert_close(a[rows], a64, chain_tol, "attention on the projected qkv")
     assert_close(z[rows], O.row_linear_partial(a64, O.to64(t["wo"][qb:qb + ql, :])), chain_tol, "o_proj partial")
+
+
+# ---------------------------------------------------------------------------
+# fp8 (E4M3) weights at decode sizes.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T,K,N", [(1, 1000, 256), (40, 4096, 1040), (64, 1000, 3584), (33, 2056, 512)])
+@pytest.mark.parametrize("act", ["none", "relu", "gelu", "swiglu"])
+def test_fp8_col_linear(T, K, N, act):
+    x = W.normal((T, K), 1.0, 81, 1)
+    q = W.e4m3_codes((K, N), 81, 2)
+    if N == 256:   # every finite code, both signs and the subnormals, somewhere in the matrix
+        allc = torch.tensor([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=torch.uint8)
+        q[:2] = allc.repeat(4)[: 2 * N].view(2, N)
+    sc = W.column_scales(N, 81, 3)
+    qu = W.e4m3_codes((K, N), 81, 4) if act == "swiglu" else None
+    su = W.column_scales(N, 81, 5) if act == "swiglu" else None
+    bias = W.normal((N,), 0.1, 81, 6) if act in ("relu", "gelu") else None
+    y = torch.full((T, N), 7.0, dtype=torch.bfloat16, device="cuda")
+    ws = tp.new_workspace(tp.tp_linear_fp8_workspace(T, K, N, act))
+    tp.tp_col_linear_fp8(cuda(x), cuda(q), cuda(sc), None if qu is None else cuda(qu), None if su is None else cuda(su),
+                         None if bias is None else cuda(bias), y, act, ws)
+    ref = O.col_linear_fp8(x, q, sc, qu, su, bias, act)
+    assert_close(y, ref, BF16_TOL, f"fp8 col linear {act}")
+
+
+@pytest.mark.parametrize("out_dt", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("T,K,N", [(64, 3584, 8192), (7, 1000, 1024)])
+def test_fp8_row_linear_partial(T, K, N, out_dt):
+    x = W.normal((T, K), 1.0, 82, 1)
+    q = W.e4m3_codes((K, N), 82, 2)
+    sc = W.column_scales(N, 82, 3)
+    z = torch.full((T, N), 7.0, dtype=out_dt, device="cuda")
+    ws = tp.new_workspace(tp.tp_linear_fp8_workspace(T, K, N, "none"))
+    tp.tp_row_linear_partial_fp8(cuda(x), cuda(q), cuda(sc), z, ws)
+    assert_close(z, O.row_linear_partial_fp8(x, q, sc), BF16_TOL, "fp8 row partial")
+    again = torch.empty_like(z)
+    tp.tp_row_linear_partial_fp8(cuda(x), cuda(q), cuda(sc), again, ws)
+    assert torch.equal(z, again)
+
+
+def test_fp8_decode_shard_T64():
+    """The 70B-class SwiGLU shard at decode size with fp8 weights: gate/up
+    column-parallel then down row-parallel, all 64 rows against the fp64
+    chain."""
+    T, d, ff_i = 64, 8192, 3584
+    x = W.normal((T, d), 1.0, 83, 1)
+    qg, qu, qd = W.e4m3_codes((d, ff_i), 83, 2), W.e4m3_codes((d, ff_i), 83, 3), W.e4m3_codes((ff_i, d), 83, 4)
+    sg, su, sd = W.column_scales(ff_i, 83, 5), W.column_scales(ff_i, 83, 6), W.column_scales(d, 83, 7)
+    h = torch.empty(T, ff_i, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty(T, d, dtype=torch.bfloat16, device="cuda")
+    ws = tp.new_workspace(max(tp.tp_linear_fp8_workspace(T, d, ff_i, "swiglu"),
+                              tp.tp_linear_fp8_workspace(T, ff_i, d, "none")))
+    tp.tp_col_linear_fp8(cuda(x), cuda(qg), cuda(sg), cuda(qu), cuda(su), None, h, "swiglu", ws)
+    tp.tp_row_linear_partial_fp8(h, cuda(qd), cuda(sd), y, ws)
+    h64 = O.col_linear_fp8(x, qg, sg, qu, su, None, "swiglu")
+    assert_close(h, h64, BF16_TOL, "fp8 gate/up + SwiGLU")
+    assert_close(y, O.row_linear_partial_fp8(h64, qd, sd), BF16_TOL, "fp8 shard output")
+
+
+def test_one_workspace_serves_every_entry_point():
+    """One zero-initialised workspace reused across entry points and shapes in
+    sequence gives bitwise the results each call gives with a fresh one (the
+    split-K counters stay in their reserved, zero region)."""
+    T, d, ff_i = 64, 2048, 512
+    x = cuda(W.normal((T, d), 1.0, 91, 1))
+    w1, wu, w2 = (cuda(W.normal(sh, 0.02, 91, k)) for k, sh in ((2, (d, ff_i)), (3, (d, ff_i)), (4, (ff_i, d))))
+    q, sc = cuda(W.e4m3_codes((ff_i, d), 91, 5)), cuda(W.column_scales(d, 91, 6))
+    a = cuda(W.normal((T, 1024), 1.0, 91, 7))
+    wo = cuda(W.normal((1024, 4096), 0.02, 91, 8))
+    calls = {
+        "mlp": (lambda ws: tp.tp_mlp_shard_fwd(x, w1, wu, w2, torch.empty(T, d, dtype=torch.bfloat16, device="cuda"),
+                                               "swiglu", ws),
+                tp.tp_mlp_shard_fwd_workspace(T, d, ff_i, tp.TP_BF16, "swiglu")),
+        "col": (lambda ws: tp.tp_col_linear(x, w1, wu, None, torch.empty(T, ff_i, dtype=torch.bfloat16,
+                                                                         device="cuda"), "swiglu", ws),
+                tp.tp_col_linear_workspace(T, d, ff_i, tp.TP_BF16, "swiglu")),
+        "row": (lambda ws: tp.tp_row_linear_partial(a, wo, torch.empty(T, 4096, dtype=torch.bfloat16, device="cuda"),
+                                                    ws),
+                tp.tp_row_linear_partial_workspace(T, 1024, 4096, tp.TP_BF16)),
+        "fp8": (lambda ws: tp.tp_row_linear_partial_fp8(x[:, :ff_i].contiguous(), q, sc,
+                                                        torch.empty(T, d, dtype=torch.bfloat16, device="cuda"), ws),
+                tp.tp_linear_fp8_workspace(T, ff_i, d, "none")),
+    }
+    fresh = {k: f(tp.new_workspace(n)) for k, (f, n) in calls.items()}
+    shared = tp.new_workspace(max(n for _, n in calls.values()))
+    for order in (["mlp", "col", "row", "fp8"], ["fp8", "row", "col", "mlp"], ["col", "mlp", "fp8", "row"]):
+        for k in order:
+            assert torch.equal(calls[k][0](shared), fresh[k]), f"{k} after {order}"

@@ -518,6 +518,48 @@ def test_attention_flops():
 
 
 # --------------------------------------------------------------------------
+# fp8 (OCP E4M3) weights of the quantized sharded linear.
+# --------------------------------------------------------------------------
+def test_e4m3_hand_values():
+    got = O.e4m3_decode(np.array([0x38, 0x7E, 0x01, 0x08, 0x07, 0x80, 0xB8, 0x40, 0x3C, 0x7F, 0xFF]))
+    want = [1.0, 448.0, 2.0 ** -9, 2.0 ** -6, 7 * 2.0 ** -9, -0.0, -1.0, 2.0, 1.5]
+    np.testing.assert_array_equal(got[:9], want)
+    assert np.signbit(got[5]) and np.isnan(got[9]) and np.isnan(got[10])
+
+
+def test_e4m3_matches_library_for_every_code():
+    """Every code against torch's float8_e4m3fn conversion (a library routine
+    the oracle does not use)."""
+    import torch
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float32).numpy().astype(np.float64)
+    got = O.e4m3_decode(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan) and nan.sum() == 2
+    np.testing.assert_array_equal(got[~nan], ref[~nan])
+
+
+def test_fp8_linear_column_scales():
+    """A per-column scale multiplies that output column (linear case), and the
+    fp8 linear with unit scales is the plain linear of the decoded weights
+    summed term by term (exact on small integers)."""
+    rng = np.random.default_rng(61)
+    x = rng.integers(-3, 4, size=(3, 5)).astype(np.float64)
+    q = rng.integers(0, 256, size=(5, 4))
+    q[q == 0x7F] = 0x38
+    q[q == 0xFF] = 0xB8
+    ones = np.ones(4)
+    s = np.array([0.5, 2.0, 0.25, 8.0])
+    base = O.row_linear_partial_fp8(x, q, ones)
+    np.testing.assert_allclose(O.row_linear_partial_fp8(x, q, s), base * s[None, :], rtol=1e-15)
+    vals = O.e4m3_decode(q)
+    brute = np.array([[sum(x[t, k] * vals[k, n] for k in range(5)) for n in range(4)] for t in range(3)])
+    np.testing.assert_allclose(base, brute, rtol=1e-13, atol=1e-13)
+    y = O.col_linear_fp8(x, q, s, q, s, None, "swiglu")
+    np.testing.assert_allclose(y, O.silu(base * s) * (base * s), rtol=1e-13, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
 # Work accounting: training ~ 6 x params x tokens.
 # --------------------------------------------------------------------------
 def test_flop_accounting():

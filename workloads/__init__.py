@@ -178,6 +178,21 @@ def attention_qkv(w: GqaWorkload, T: Optional[int] = None) -> torch.Tensor:
     return normal((T, width), WEIGHT_STD * w.h ** 0.5, w.seed, S_QKV)
 
 
+def e4m3_codes(shape, seed: int, stream: int) -> torch.Tensor:
+    """fp8 weight codes (uint8, OCP E4M3): an N(0, 64^2) fp32 draw rounded to
+    the nearest e4m3 value by torch (saturating at +-448), so the codes span
+    normal and subnormal values of both signs."""
+    t = torch.randn(*shape, generator=_gen(seed, stream), dtype=torch.float32).mul_(64.0)
+    return t.clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+def column_scales(n: int, seed: int, stream: int) -> torch.Tensor:
+    """Per-column fp32 weight scales, uniform in [0.5, 1.5) * 0.02 / 64, so the
+    scaled weights have about the spread of the bf16 workloads' weights."""
+    u = torch.rand(n, generator=_gen(seed, stream), dtype=torch.float32)
+    return (0.5 + u) * (WEIGHT_STD / 64.0)
+
+
 def row_subset(T: int, n: int, seed: int) -> List[int]:
     """Seeded, sorted subset of ``n`` distinct rows out of ``T`` (all rows if T <= n)."""
     if T <= n:
