@@ -165,7 +165,7 @@ def main() -> int:
     log(f"bench: gate/up GEMM {k_ms * 1e3:.1f} us -> {k_gbs:.0f} GB/s")
 
     rows = {}
-    want = set(["prefill", "gqa", "attn", "bwd", "sum"]) if args.rows == "all" else (
+    want = set(["prefill", "gqa", "attn", "bwd", "fp8", "sum"]) if args.rows == "all" else (
         set() if args.rows == "none" else set(args.rows.split(",")))
     steps_r = max(10, args.steps // 2)
 
@@ -176,6 +176,35 @@ def main() -> int:
         rows["calib_copy_117440512B"] = {"us": round(t_ * 1e3, 2),
                                          "GB/s_rd+wr": round(2 * src.numel() * 2 / t_ / 1e6, 1)}
         del src, dst
+
+    if "fp8" in want:
+        # the decode shard step with fp8 (E4M3) weights and per-column scales:
+        # gate/up column-parallel GEMM + SwiGLU, then the down row-parallel partial
+        R8 = 4   # 4 x 88 MB of weights rotate, more than the 256 MB Infinity Cache holds
+        g8 = torch.Generator(device=dev)
+        sets8 = []
+        for r in range(R8):
+            g8.manual_seed(100 + r)
+            codes = lambda shp: (torch.randn(*shp, generator=g8, device=dev) * 64.0).clamp_(-448, 448).to(
+                torch.float8_e4m3fn).view(torch.uint8)
+            sc = lambda n: (0.5 + torch.rand(n, generator=g8, device=dev)) * (0.02 / 64.0)
+            sets8.append((codes((d, ff_i)), sc(ff_i), codes((d, ff_i)), sc(ff_i), codes((ff_i, d)), sc(d)))
+        h8 = torch.empty(T, ff_i, dtype=torch.bfloat16, device=dev)
+        y8 = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
+        ws8 = tp.new_workspace(max(tp.tp_linear_fp8_workspace(T, d, ff_i, "swiglu"),
+                                   tp.tp_linear_fp8_workspace(T, ff_i, d, "none")), dev)
+
+        def step8(i):
+            qg, sg, qu, su, qd, sd = sets8[i % R8]
+            tp.tp_col_linear_fp8(x, qg, sg, qu, su, None, h8, "swiglu", ws8)
+            tp.tp_row_linear_partial_fp8(h8, qd, sd, y8, ws8)
+
+        t_ = time_gpu(step8, steps_r, 3)
+        b8 = 3 * d * ff_i + (2 * ff_i + d) * 4 + 2 * T * d * 2
+        rows["decode_fp8_weights_shard_T64"] = {"us": round(t_ * 1e3, 2), "GB/s": round(b8 / t_ / 1e6, 1),
+                                                "frac_hbm": round(b8 / t_ / 1e6 / HBM_PEAK_GBS, 4),
+                                                "algorithmic_bytes": b8}
+        del sets8, h8, y8, ws8
 
     if "sum" in want:
         parts = [torch.randn(T, d, device=dev).to(torch.bfloat16) for _ in range(8)]

@@ -151,6 +151,7 @@ __device__ __forceinline__ void ring_loop(const GemmParams& p, int n0, int w_beg
                                           char* my, f32x16 (&acc)[MT][DUAL ? 2 * NW : NW], Ready&& ready) {
   constexpr int NF = DUAL ? 2 * NW : NW;
   const u32x4* apk = reinterpret_cast<const u32x4*>(p.apk);
+  constexpr int RD = DEPTH;  // (fp8: 8 steps in flight measured no faster than 4)
   const int full_end = min(w_end, p.K0 / 16);  // steps whose weight rows all lie inside K
   const int nw = full_end - w_begin;
   if (nw > 0) {
@@ -159,15 +160,15 @@ __device__ __forceinline__ void ring_loop(const GemmParams& p, int n0, int w_beg
       const int q = min(it, nw - 1) + rot;
       return w_begin + (q >= nw ? q - nw : q);
     };
-    WRegs<DUAL, F8> fr[DEPTH];
-    u32x4 fa[DEPTH][MT];
-    static_for<0, DEPTH>([&](auto d) { load_wregs<DUAL, F8, false>(fr[d], p, phys(d), n0, lane); });
+    WRegs<DUAL, F8> fr[RD];
+    u32x4 fa[RD][MT];
+    static_for<0, RD>([&](auto d) { load_wregs<DUAL, F8, false>(fr[d], p, phys(d), n0, lane); });
     ready();
-    static_for<0, DEPTH>([&](auto d) { load_a<MT>(apk, phys(d), lane, fa[d]); });
-    for (int it = 0; it < nw; it += DEPTH) {
-      static_for<0, DEPTH>([&](auto d) {
+    static_for<0, RD>([&](auto d) { load_a<MT>(apk, phys(d), lane, fa[d]); });
+    for (int it = 0; it < nw; it += RD) {
+      static_for<0, RD>([&](auto d) {
         if (it + (int)d < nw) mma_step<MT, DUAL, F8>(my, lane, fr[d], fa[d], acc);
-        const int st = phys(it + DEPTH + (int)d);
+        const int st = phys(it + RD + (int)d);
         load_wregs<DUAL, F8, false>(fr[d], p, st, n0, lane);
         load_a<MT>(apk, st, lane, fa[d]);
       });
