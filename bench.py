@@ -188,7 +188,10 @@ def main() -> int:
             codes = lambda shp: (torch.randn(*shp, generator=g8, device=dev) * 64.0).clamp_(-448, 448).to(
                 torch.float8_e4m3fn).view(torch.uint8)
             sc = lambda n: (0.5 + torch.rand(n, generator=g8, device=dev)) * (0.02 / 64.0)
-            sets8.append((codes((d, ff_i)), sc(ff_i), codes((d, ff_i)), sc(ff_i), codes((ff_i, d)), sc(d)))
+            def strips(q):   # the strip-major order the fp8 linears read
+                return tp.tp_fp8_pack_strips(q, torch.empty_like(q))
+            sets8.append((strips(codes((d, ff_i))), sc(ff_i), strips(codes((d, ff_i))), sc(ff_i),
+                          strips(codes((ff_i, d))), sc(d)))
         h8 = torch.empty(T, ff_i, dtype=torch.bfloat16, device=dev)
         y8 = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
         ws8 = tp.new_workspace(max(tp.tp_linear_fp8_workspace(T, d, ff_i, "swiglu"),

@@ -204,22 +204,31 @@ tp_status tp_gqa_attention_fwd(const void* qkv, void* out, int64_t T, int n_q, i
  * quantized form of the column- and row-parallel linear that [MLX] mentions
  * as the "quantized equivalent" of the sharded linear).  Weights are OCP
  * e4m3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; 0x7F /
- * 0xFF are NaN), (K, N) row-major, one byte each, with one fp32 scale per
- * output column: W[k, n] = e4m3(wq[k, n]) * scale[n].  Activations stay
+ * 0xFF are NaN), one byte each, with one fp32 scale per output column:
+ * W[k, n] = e4m3(code(k, n)) * scale[n].  The codes are stored 64-column
+ * strip-major (as tp_fp8_pack_strips writes them): code (k, n) at byte
+ * (n / 64) * 64 K + 64 k + n % 64, so each strip streams as one contiguous
+ * run.  Activations stay
  * bf16; products accumulate in fp32 and the scale multiplies each column's
  * sum (exactly the product with the dequantized weights, up to rounding).
  *   tp_col_linear_fp8:          y = act(x W + bias), or
  *                               silu(x W) * (x W_up) for SWIGLU (wq_up and
  *                               scale_up given iff SWIGLU; no bias then)
  *   tp_row_linear_partial_fp8:  z_i = x_i W_i (no bias), out_dtype bf16/f32
- * x (T, K) bf16, 16-byte aligned with K % 8 == 0; wq (K, N), 16-byte
- * aligned with N % 16 == 0; scale (N) fp32; y / z_i (T, N).  All device.
+ * x (T, K) bf16, 16-byte aligned with K % 8 == 0; wq (K x N codes,
+ * strip-major), 16-byte aligned with N % 64 == 0; scale (N) fp32; y / z_i
+ * (T, N).  All device.
  * 1 <= T <= 64 (TP_ERR_UNSUPPORTED above; T == 0 is a no-op).  ws (device)
  * of ws_bytes >= tp_linear_fp8_workspace(T, K, N, act), required, under the
  * zero-fill and reuse rules of tp_mlp_shard_fwd's workspace.  Errors:
  * TP_ERR_NULL, TP_ERR_SHAPE, TP_ERR_ACT, TP_ERR_DTYPE, TP_ERR_WORKSPACE,
  * TP_ERR_UNSUPPORTED, TP_ERR_HIP. */
 size_t tp_linear_fp8_workspace(int64_t T, int64_t K, int64_t N, tp_act act);
+/* Rearranges fp8 codes from (K, N) row-major (src) into the 64-column
+ * strip-major order the fp8 linears read (dst), once per weight matrix.  Both
+ * device, 16-byte aligned, not aliasing; N % 64 == 0 (TP_ERR_SHAPE).
+ * A pure byte permutation. */
+tp_status tp_fp8_pack_strips(const void* src, void* dst, int64_t K, int64_t N, tp_stream stream);
 tp_status tp_col_linear_fp8(const void* x, const void* wq, const float* scale, const void* wq_up,
                             const float* scale_up, const void* bias, void* y, void* ws, size_t ws_bytes,
                             int64_t T, int64_t K, int64_t N_i, tp_act act, tp_stream stream);

@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     tp_col_linear,
     tp_col_linear_fp8,
     tp_col_linear_workspace,
+    tp_fp8_pack_strips,
     tp_gqa_attention_fwd,
     tp_gqa_shard,
     tp_linear_shard_bwd,

@@ -52,6 +52,7 @@ SIGNATURES = {
     "tp_linear_shard_bwd": (c_int, [c_p, c_p, c_p, c_p, c_p, c_p, c_sz, c_i64, c_i64, c_i64, c_int, c_p]),
     "tp_gqa_attention_fwd": (c_int, [c_p, c_p, c_i64, c_int, c_int, c_int, c_int, ctypes.c_float, c_p]),
     "tp_linear_fp8_workspace": (c_sz, [c_i64, c_i64, c_i64, c_int]),
+    "tp_fp8_pack_strips": (c_int, [c_p, c_p, c_i64, c_i64, c_p]),
     "tp_col_linear_fp8": (c_int, [c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_sz, c_i64, c_i64, c_i64, c_int, c_p]),
     "tp_row_linear_partial_fp8": (c_int, [c_p, c_p, c_p, c_p, c_p, c_sz, c_i64, c_i64, c_i64, c_int, c_p]),
     "tp_partial_sum": (c_int, [ctypes.POINTER(c_p), c_int, c_p, c_p, c_i64, c_i64, c_int, c_int, c_p]),
@@ -263,8 +264,21 @@ def tp_linear_fp8_workspace(T: int, K: int, N: int, act: str = "none") -> int:
     return load().tp_linear_fp8_workspace(T, K, N, ACT[act])
 
 
+def tp_fp8_pack_strips(src, dst):
+    """(K, N) row-major fp8 codes -> the 64-column strip-major order (dst, K*N bytes)."""
+    K, N = src.shape
+    _fp8_codes(src, "src")
+    _fp8_codes(dst, "dst")
+    if dst.numel() != K * N:
+        raise ValueError("dst must hold K*N codes")
+    _check(load().tp_fp8_pack_strips(_ptr(src), _ptr(dst), K, N, _stream()))
+    return dst
+
+
 def tp_col_linear_fp8(x, wq, scale, wq_up, scale_up, bias, y, act: str, ws: torch.Tensor):
-    """y = act(x (e4m3(wq) * scale) [+ bias]); SWIGLU: silu(x W) * (x W_up)."""
+    """y = act(x (e4m3(wq) * scale) [+ bias]); SWIGLU: silu(x W) * (x W_up).
+    wq / wq_up: (K, N)-shaped buffers holding the codes strip-major (see
+    tp_fp8_pack_strips)."""
     T, K = x.shape
     N = wq.shape[1]
     _fp8_codes(wq, "wq")
@@ -280,7 +294,7 @@ def tp_col_linear_fp8(x, wq, scale, wq_up, scale_up, bias, y, act: str, ws: torc
 
 
 def tp_row_linear_partial_fp8(x_i, wq_i, scale_i, z_i, ws: torch.Tensor):
-    """z_i = x_i (e4m3(wq_i) * scale_i), the full-shape partial."""
+    """z_i = x_i (e4m3(wq_i) * scale_i), the full-shape partial (wq_i strip-major)."""
     T, K = x_i.shape
     N = wq_i.shape[1]
     _fp8_codes(wq_i, "wq_i")

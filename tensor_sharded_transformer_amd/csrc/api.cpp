@@ -233,8 +233,8 @@ tp_status linear_fp8(const char* who, const void* x, const void* wq, const float
   if (T == 0 || N == 0) return TP_OK;
   if (!x || !wq || !scale || !y || (kind == tpk::GK_FWD_SWIGLU && (!wq_up || !scale_up)))
     return fail(TP_ERR_NULL, "%s: null input or output pointer", who);
-  if (N % 16 || K % 8 || !aligned16(x) || !aligned16(wq) || (wq_up && !aligned16(wq_up)))
-    return fail(TP_ERR_UNSUPPORTED, "%s: needs N %% 16 == 0, K %% 8 == 0 and 16-byte aligned x and weights", who);
+  if (N % 64 || K % 8 || !aligned16(x) || !aligned16(wq) || (wq_up && !aligned16(wq_up)))
+    return fail(TP_ERR_UNSUPPORTED, "%s: needs N %% 64 == 0, K %% 8 == 0 and 16-byte aligned x and weights", who);
   GemmParams p = base_params();
   p.A0 = x;
   p.lda = K;
@@ -444,6 +444,16 @@ tp_status tp_row_linear_partial_fp8(const void* x_i, const void* wq_i, const flo
   if (!valid_dtype(out_dtype)) return fail(TP_ERR_DTYPE, "tp_row_linear_partial_fp8: unknown dtype");
   return linear_fp8("tp_row_linear_partial_fp8", x_i, wq_i, scale_i, nullptr, nullptr, nullptr, z_i, ws, ws_bytes, T,
                     K_i, N, TP_ACT_NONE, out_dtype == TP_F32, tpk::GK_FWD_STORE, reinterpret_cast<hipStream_t>(stream));
+}
+
+tp_status tp_fp8_pack_strips(const void* src, void* dst, int64_t K, int64_t N, tp_stream stream) {
+  if (!dim_ok(K) || !dim_ok(N) || !prod_ok(K, N)) return fail(TP_ERR_SHAPE, "tp_fp8_pack_strips: sizes out of range");
+  if (N % 64) return fail(TP_ERR_SHAPE, "tp_fp8_pack_strips: N=%lld is not a multiple of 64", (long long)N);
+  if (K == 0 || N == 0) return TP_OK;
+  if (!src || !dst) return fail(TP_ERR_NULL, "tp_fp8_pack_strips: null src or dst");
+  if (src == dst) return fail(TP_ERR_SHAPE, "tp_fp8_pack_strips: src and dst must not alias");
+  if (!aligned16(src) || !aligned16(dst)) return fail(TP_ERR_UNSUPPORTED, "tp_fp8_pack_strips: unaligned pointers");
+  return hip_status(tpk::pack_fp8_strips(src, dst, K, N, reinterpret_cast<hipStream_t>(stream)), "tp_fp8_pack_strips");
 }
 
 // ---- sum of partials -------------------------------------------------------------

@@ -354,4 +354,25 @@ hipError_t zero_fill(void* ws, size_t bytes, hipStream_t s) {
   return hipGetLastError();
 }
 
+// fp8 weight codes (K, N) row-major -> 64-column strip-major: one thread per
+// 16-byte piece of a strip row.
+__global__ __launch_bounds__(256) void pack_strips_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                                          int64_t K, int64_t N) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // piece index in destination order
+  const int64_t pieces = K * (N / 16);
+  if (i >= pieces) return;
+  const int64_t strip = i / (K * 4), rem = i % (K * 4);
+  const int64_t k = rem / 4, q = rem % 4;
+  const uint4 v = *reinterpret_cast<const uint4*>(src + k * N + strip * 64 + q * 16);
+  *reinterpret_cast<uint4*>(dst + i * 16) = v;
+}
+
+hipError_t pack_fp8_strips(const void* src, void* dst, int64_t K, int64_t N, hipStream_t s) {
+  const int64_t pieces = K * (N / 16);
+  if (pieces == 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_strips_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, s,
+                     reinterpret_cast<const uint8_t*>(src), reinterpret_cast<uint8_t*>(dst), K, N);
+  return hipGetLastError();
+}
+
 }  // namespace tpk

@@ -51,17 +51,20 @@ __device__ __forceinline__ void load_w(WFrag<DUAL ? 2 * NW : NW>& fr, const Gemm
   }
 }
 
-// fp8 weights (one byte per value, NW == 2): one k-step of one matrix is a
-// single 1 KB instruction, lane l reading row l/4, columns 16 (l%4) .. +15 of
-// the strip.  Raw codes stay in registers until the k-step is consumed.
+// fp8 weights (one byte per value, NW == 2) in 64-column strip-major order:
+// value (k, n) at byte (n / 64) * 64 K + 64 k + n % 64, so a strip's rows are
+// one contiguous run and every cache line feeds a single workgroup.  One
+// k-step of one matrix is a single 1 KB instruction: lane l reads row l/4,
+// columns 16 (l%4) .. +15 of the strip.  Raw codes stay in registers until
+// the k-step is consumed.
 template <bool DUAL, bool TAIL>
 __device__ __forceinline__ void load_w8(WFrag<DUAL ? 2 : 1>& fr, const GemmParams& p, int step, int n0, int lane) {
-  const int n = min(n0 + (lane & 3) * 16, p.N - 16);
   const int kb = step * 16 + (lane >> 2);
+  const int64_t off = (int64_t)(n0 >> 6) * 64 * p.K0 + (int64_t)kb * 64 + (lane & 3) * 16;
 #pragma unroll
   for (int mat = 0; mat < (DUAL ? 2 : 1); ++mat) {
     const uint8_t* B = reinterpret_cast<const uint8_t*>(mat ? p.B1 : p.B0);
-    if (!TAIL || kb < p.K0) fr.b[mat] = *reinterpret_cast<const u32x4*>(B + (int64_t)kb * p.ldb + n);
+    if (!TAIL || kb < p.K0) fr.b[mat] = *reinterpret_cast<const u32x4*>(B + off);
     else fr.b[mat] = u32x4{0u, 0u, 0u, 0u};
   }
 }

@@ -156,6 +156,8 @@ hipError_t rs_residual_rmsnorm(const void* const* z, int p, int rank, const void
                                const void* norm_w, float eps, void* residual_out, void* y, int64_t T, int64_t N,
                                bool in_bf16, bool out_bf16, hipStream_t s);
 hipError_t zero_fill(void* ws, size_t bytes, hipStream_t s);
+// fp8 codes (K, N) row-major -> 64-column strip-major (N % 64 == 0, both 16-byte aligned).
+hipError_t pack_fp8_strips(const void* src, void* dst, int64_t K, int64_t N, hipStream_t s);
 
 // Local grouped-query attention over a rank's heads: qkv (T, (n_q + 2 n_kv)
 // * 128) bf16 rows [Q | K | V], out (T, n_q * 128) bf16; both 16-byte

@@ -209,13 +209,18 @@ def test_linear_fp8_validation(lib):
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, *args, 3, None) == ACTE          # bias with SWIGLU
     assert f(FAKE, FAKE, None, None, None, None, FAKE, *args, 0, None) == NULL          # no scale
     assert f(FAKE, FAKE, FAKE, None, None, None, FAKE, FAKE, ws, 65, 1024, 256, 0, None) == 6   # T > 64
-    assert f(FAKE, FAKE, FAKE, None, None, None, FAKE, FAKE, ws, 64, 1024, 264, 0, None) == 6   # N % 16
+    assert f(FAKE, FAKE, FAKE, None, None, None, FAKE, FAKE, ws, 64, 1024, 272, 0, None) == 6   # N % 64
     assert f(FAKE, FAKE, FAKE, None, None, None, FAKE, None, 0, 64, 1024, 256, 0, None) == WS
     assert f(FAKE, FAKE, FAKE, None, None, None, FAKE, FAKE, ws - 1, 64, 1024, 256, 0, None) == WS
     assert f(None, None, None, None, None, None, None, None, 0, 0, 1024, 256, 0, None) == OK   # T == 0
     g = lib.tp_row_linear_partial_fp8
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, ws, 64, 1024, 256, 7, None) == DTYPE
     assert g(FAKE, FAKE, None, FAKE, FAKE, ws, 64, 1024, 256, 0, None) == NULL
+    pk = lib.tp_fp8_pack_strips
+    assert pk(FAKE, ctypes.c_void_p(0x2000), 16, 100, None) == SHAPE     # N % 64
+    assert pk(FAKE, FAKE, 16, 128, None) == SHAPE                         # aliasing
+    assert pk(None, FAKE, 16, 128, None) == NULL
+    assert pk(None, None, 0, 128, None) == OK
 
 
 def test_status_strings(lib):

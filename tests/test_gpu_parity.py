@@ -666,7 +666,20 @@ def test_attention_between_the_projections():
 # ---------------------------------------------------------------------------
 # fp8 (E4M3) weights at decode sizes.
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("T,K,N", [(1, 1000, 256), (40, 4096, 1040), (64, 1000, 3584), (33, 2056, 512)])
+def packed(q):
+    """Device copy of (K, N) row-major codes in the strip-major order."""
+    dst = torch.empty(q.shape, dtype=torch.uint8, device="cuda")
+    return tp.tp_fp8_pack_strips(cuda(q), dst)
+
+
+@pytest.mark.parametrize("K,N", [(1, 64), (5, 128), (1000, 3584), (33, 1088)])
+def test_fp8_pack_strips_is_the_strip_permutation(K, N):
+    q = torch.randint(0, 256, (K, N), dtype=torch.uint8)
+    want = q.reshape(K, N // 64, 64).permute(1, 0, 2).contiguous().reshape(K, N)
+    assert torch.equal(packed(q).cpu(), want)
+
+
+@pytest.mark.parametrize("T,K,N", [(1, 1000, 256), (40, 4096, 1088), (64, 1000, 3584), (33, 2056, 512)])
 @pytest.mark.parametrize("act", ["none", "relu", "gelu", "swiglu"])
 def test_fp8_col_linear(T, K, N, act):
     x = W.normal((T, K), 1.0, 81, 1)
@@ -680,8 +693,8 @@ def test_fp8_col_linear(T, K, N, act):
     bias = W.normal((N,), 0.1, 81, 6) if act in ("relu", "gelu") else None
     y = torch.full((T, N), 7.0, dtype=torch.bfloat16, device="cuda")
     ws = tp.new_workspace(tp.tp_linear_fp8_workspace(T, K, N, act))
-    tp.tp_col_linear_fp8(cuda(x), cuda(q), cuda(sc), None if qu is None else cuda(qu), None if su is None else cuda(su),
-                         None if bias is None else cuda(bias), y, act, ws)
+    tp.tp_col_linear_fp8(cuda(x), packed(q), cuda(sc), None if qu is None else packed(qu),
+                         None if su is None else cuda(su), None if bias is None else cuda(bias), y, act, ws)
     ref = O.col_linear_fp8(x, q, sc, qu, su, bias, act)
     assert_close(y, ref, BF16_TOL, f"fp8 col linear {act}")
 
@@ -694,10 +707,11 @@ def test_fp8_row_linear_partial(T, K, N, out_dt):
     sc = W.column_scales(N, 82, 3)
     z = torch.full((T, N), 7.0, dtype=out_dt, device="cuda")
     ws = tp.new_workspace(tp.tp_linear_fp8_workspace(T, K, N, "none"))
-    tp.tp_row_linear_partial_fp8(cuda(x), cuda(q), cuda(sc), z, ws)
+    qp = packed(q)
+    tp.tp_row_linear_partial_fp8(cuda(x), qp, cuda(sc), z, ws)
     assert_close(z, O.row_linear_partial_fp8(x, q, sc), BF16_TOL, "fp8 row partial")
     again = torch.empty_like(z)
-    tp.tp_row_linear_partial_fp8(cuda(x), cuda(q), cuda(sc), again, ws)
+    tp.tp_row_linear_partial_fp8(cuda(x), qp, cuda(sc), again, ws)
     assert torch.equal(z, again)
 
 
@@ -713,8 +727,8 @@ def test_fp8_decode_shard_T64():
     y = torch.empty(T, d, dtype=torch.bfloat16, device="cuda")
     ws = tp.new_workspace(max(tp.tp_linear_fp8_workspace(T, d, ff_i, "swiglu"),
                               tp.tp_linear_fp8_workspace(T, ff_i, d, "none")))
-    tp.tp_col_linear_fp8(cuda(x), cuda(qg), cuda(sg), cuda(qu), cuda(su), None, h, "swiglu", ws)
-    tp.tp_row_linear_partial_fp8(h, cuda(qd), cuda(sd), y, ws)
+    tp.tp_col_linear_fp8(cuda(x), packed(qg), cuda(sg), packed(qu), cuda(su), None, h, "swiglu", ws)
+    tp.tp_row_linear_partial_fp8(h, packed(qd), cuda(sd), y, ws)
     h64 = O.col_linear_fp8(x, qg, sg, qu, su, None, "swiglu")
     assert_close(h, h64, BF16_TOL, "fp8 gate/up + SwiGLU")
     assert_close(y, O.row_linear_partial_fp8(h64, qd, sd), BF16_TOL, "fp8 shard output")
@@ -727,7 +741,7 @@ def test_one_workspace_serves_every_entry_point():
     T, d, ff_i = 64, 2048, 512
     x = cuda(W.normal((T, d), 1.0, 91, 1))
     w1, wu, w2 = (cuda(W.normal(sh, 0.02, 91, k)) for k, sh in ((2, (d, ff_i)), (3, (d, ff_i)), (4, (ff_i, d))))
-    q, sc = cuda(W.e4m3_codes((ff_i, d), 91, 5)), cuda(W.column_scales(d, 91, 6))
+    q, sc = packed(W.e4m3_codes((ff_i, d), 91, 5)), cuda(W.column_scales(d, 91, 6))
     a = cuda(W.normal((T, 1024), 1.0, 91, 7))
     wo = cuda(W.normal((1024, 4096), 0.02, 91, 8))
     calls = {
