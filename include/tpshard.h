@@ -58,7 +58,7 @@ typedef enum {
   TP_ERR_DTYPE = 3,       /* unknown or unsupported dtype combination         */
   TP_ERR_ACT = 4,         /* unknown act, or up/w_up/bias inconsistent with it */
   TP_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required       */
-  TP_ERR_UNSUPPORTED = 6, /* valid request this build does not implement      */
+  TP_ERR_UNSUPPORTED = 6, /* valid request the library does not implement    */
   TP_ERR_HIP = 7          /* the HIP runtime reported an error                */
 } tp_status;
 
