@@ -192,22 +192,19 @@ def main() -> int:
                 return tp.tp_fp8_pack_strips(q, torch.empty_like(q))
             sets8.append((strips(codes((d, ff_i))), sc(ff_i), strips(codes((d, ff_i))), sc(ff_i),
                           strips(codes((ff_i, d))), sc(d)))
-        h8 = torch.empty(T, ff_i, dtype=torch.bfloat16, device=dev)
         y8 = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
-        ws8 = tp.new_workspace(max(tp.tp_linear_fp8_workspace(T, d, ff_i, "swiglu"),
-                                   tp.tp_linear_fp8_workspace(T, ff_i, d, "none")), dev)
+        ws8 = tp.new_workspace(tp.tp_mlp_shard_fwd_fp8_workspace(T, d, ff_i, "swiglu"), dev)
 
         def step8(i):
             qg, sg, qu, su, qd, sd = sets8[i % R8]
-            tp.tp_col_linear_fp8(x, qg, sg, qu, su, None, h8, "swiglu", ws8)
-            tp.tp_row_linear_partial_fp8(h8, qd, sd, y8, ws8)
+            tp.tp_mlp_shard_fwd_fp8(x, qg, sg, qu, su, qd, sd, y8, "swiglu", ws8)
 
         t_ = time_gpu(step8, steps_r, 3)
         b8 = 3 * d * ff_i + (2 * ff_i + d) * 4 + 2 * T * d * 2
         rows["decode_fp8_weights_shard_T64"] = {"us": round(t_ * 1e3, 2), "GB/s": round(b8 / t_ / 1e6, 1),
                                                 "frac_hbm": round(b8 / t_ / 1e6 / HBM_PEAK_GBS, 4),
                                                 "algorithmic_bytes": b8}
-        del sets8, h8, y8, ws8
+        del sets8, y8, ws8
 
     if "sum" in want:
         parts = [torch.randn(T, d, device=dev).to(torch.bfloat16) for _ in range(8)]

@@ -224,6 +224,21 @@ tp_status tp_gqa_attention_fwd(const void* qkv, void* out, int64_t T, int n_q, i
  * TP_ERR_NULL, TP_ERR_SHAPE, TP_ERR_ACT, TP_ERR_DTYPE, TP_ERR_WORKSPACE,
  * TP_ERR_UNSUPPORTED, TP_ERR_HIP. */
 size_t tp_linear_fp8_workspace(int64_t T, int64_t K, int64_t N, tp_act act);
+/* One rank's feed-forward shard at decode size with fp8 weights (the same
+ * block as tp_mlp_shard_fwd, [FFN] "Column split, then row split", with the
+ * weights of the fp8 linears above, strip-major): y_i = act(x W1_i [, x
+ * W_up_i]) W2_i with W = e4m3(codes) * per-column scale.  h_i stays in the
+ * workspace (bf16, written by the column GEMM straight in the row GEMM's
+ * packed activation order).  x (T, d) bf16; wq1_i, wq_up_i (d x ff_i codes),
+ * wq2_i (ff_i x d codes); s1_i, s_up_i (ff_i), s2_i (d) fp32; y_i (T, d) in
+ * out_dtype.  1 <= T <= 64, d and ff_i multiples of 64, 16-byte aligned
+ * pointers (TP_ERR_UNSUPPORTED otherwise).  ws of ws_bytes >=
+ * tp_mlp_shard_fwd_fp8_workspace(...), same rules as tp_mlp_shard_fwd's. */
+size_t tp_mlp_shard_fwd_fp8_workspace(int64_t T, int64_t d, int64_t ff_i, tp_act act);
+tp_status tp_mlp_shard_fwd_fp8(const void* x, const void* wq1_i, const float* s1_i, const void* wq_up_i,
+                               const float* s_up_i, const void* wq2_i, const float* s2_i, void* y_i,
+                               void* ws, size_t ws_bytes, int64_t T, int64_t d, int64_t ff_i,
+                               tp_dtype out_dtype, tp_act act, tp_stream stream);
 /* Rearranges fp8 codes from (K, N) row-major (src) into the 64-column
  * strip-major order the fp8 linears read (dst), once per weight matrix.  Both
  * device, 16-byte aligned, not aliasing; N % 64 == 0 (TP_ERR_SHAPE).

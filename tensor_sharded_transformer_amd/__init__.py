@@ -25,6 +25,8 @@ from .binding import (  # noqa: F401
     tp_mlp_shard_bwd,
     tp_mlp_shard_bwd_workspace,
     tp_mlp_shard_fwd,
+    tp_mlp_shard_fwd_fp8,
+    tp_mlp_shard_fwd_fp8_workspace,
     tp_mlp_shard_fwd_workspace,
     tp_partial_sum,
     tp_row_linear_partial,

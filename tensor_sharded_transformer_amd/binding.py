@@ -53,6 +53,9 @@ SIGNATURES = {
     "tp_gqa_attention_fwd": (c_int, [c_p, c_p, c_i64, c_int, c_int, c_int, c_int, ctypes.c_float, c_p]),
     "tp_linear_fp8_workspace": (c_sz, [c_i64, c_i64, c_i64, c_int]),
     "tp_fp8_pack_strips": (c_int, [c_p, c_p, c_i64, c_i64, c_p]),
+    "tp_mlp_shard_fwd_fp8_workspace": (c_sz, [c_i64, c_i64, c_i64, c_int]),
+    "tp_mlp_shard_fwd_fp8": (c_int, [c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_sz, c_i64, c_i64, c_i64, c_int,
+                                     c_int, c_p]),
     "tp_col_linear_fp8": (c_int, [c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_sz, c_i64, c_i64, c_i64, c_int, c_p]),
     "tp_row_linear_partial_fp8": (c_int, [c_p, c_p, c_p, c_p, c_p, c_sz, c_i64, c_i64, c_i64, c_int, c_p]),
     "tp_partial_sum": (c_int, [ctypes.POINTER(c_p), c_int, c_p, c_p, c_i64, c_i64, c_int, c_int, c_p]),
@@ -273,6 +276,30 @@ def tp_fp8_pack_strips(src, dst):
         raise ValueError("dst must hold K*N codes")
     _check(load().tp_fp8_pack_strips(_ptr(src), _ptr(dst), K, N, _stream()))
     return dst
+
+
+def tp_mlp_shard_fwd_fp8_workspace(T: int, d: int, ff_i: int, act: str) -> int:
+    return load().tp_mlp_shard_fwd_fp8_workspace(T, d, ff_i, ACT[act])
+
+
+def tp_mlp_shard_fwd_fp8(x, wq1_i, s1_i, wq_up_i, s_up_i, wq2_i, s2_i, y_i, act: str, ws: torch.Tensor):
+    """Decode-size shard forward with strip-major fp8 weights and per-column scales."""
+    T, d = x.shape
+    ff_i = wq1_i.shape[1]
+    for t, nm in ((wq1_i, "wq1_i"), (wq2_i, "wq2_i")):
+        _fp8_codes(t, nm)
+    _shape(wq1_i, (d, ff_i), "wq1_i")
+    _shape(wq2_i, (ff_i, d), "wq2_i")
+    _shape(s1_i, (ff_i,), "s1_i")
+    _shape(s2_i, (d,), "s2_i")
+    _shape(y_i, (T, d), "y_i")
+    if wq_up_i is not None:
+        _fp8_codes(wq_up_i, "wq_up_i")
+        _shape(wq_up_i, (d, ff_i), "wq_up_i")
+    _check(load().tp_mlp_shard_fwd_fp8(_ptr(x), _ptr(wq1_i), _ptr(s1_i), _ptr(wq_up_i), _ptr(s_up_i), _ptr(wq2_i),
+                                       _ptr(s2_i), _ptr(y_i), _ptr(ws), ws.numel() if ws is not None else 0, T, d,
+                                       ff_i, _dt(y_i), ACT[act], _stream()))
+    return y_i
 
 
 def tp_col_linear_fp8(x, wq, scale, wq_up, scale_up, bias, y, act: str, ws: torch.Tensor):

@@ -446,6 +446,82 @@ tp_status tp_row_linear_partial_fp8(const void* x_i, const void* wq_i, const flo
                     K_i, N, TP_ACT_NONE, out_dtype == TP_F32, tpk::GK_FWD_STORE, reinterpret_cast<hipStream_t>(stream));
 }
 
+size_t tp_mlp_shard_fwd_fp8_workspace(int64_t T, int64_t d, int64_t ff_i, tp_act act) {
+  if (!valid_act(act) || T < 1 || T > tpk::STREAM_MAX_M || !dim_ok(d) || !dim_ok(ff_i)) return 0;
+  return fwd_layout(T, d, ff_i, TP_BF16, act, true).total;
+}
+
+tp_status tp_mlp_shard_fwd_fp8(const void* x, const void* wq1_i, const float* s1_i, const void* wq_up_i,
+                               const float* s_up_i, const void* wq2_i, const float* s2_i, void* y_i, void* ws,
+                               size_t ws_bytes, int64_t T, int64_t d, int64_t ff_i, tp_dtype out_dtype, tp_act act,
+                               tp_stream stream) {
+  if (!valid_act(act)) return fail(TP_ERR_ACT, "tp_mlp_shard_fwd_fp8: unknown act %d", act);
+  if (!valid_dtype(out_dtype)) return fail(TP_ERR_DTYPE, "tp_mlp_shard_fwd_fp8: unknown out_dtype");
+  if (!dim_ok(T) || !dim_ok(d) || !dim_ok(ff_i) || !prod_ok(d, ff_i))
+    return fail(TP_ERR_SHAPE, "tp_mlp_shard_fwd_fp8: sizes out of range");
+  const bool sw = act == TP_ACT_SWIGLU;
+  if (sw != (wq_up_i != nullptr) || sw != (s_up_i != nullptr))
+    return fail(TP_ERR_ACT, "tp_mlp_shard_fwd_fp8: wq_up_i and s_up_i must be given iff SWIGLU");
+  if (T > tpk::STREAM_MAX_M)
+    return fail(TP_ERR_UNSUPPORTED, "tp_mlp_shard_fwd_fp8: T=%lld (decode sizes, T <= %d)", (long long)T,
+                tpk::STREAM_MAX_M);
+  if (T == 0) return TP_OK;
+  if (!x || !wq1_i || !s1_i || !wq2_i || !s2_i || !y_i) return fail(TP_ERR_NULL, "tp_mlp_shard_fwd_fp8: null pointer");
+  if (d % 64 || ff_i % 64 || !aligned16(x) || !aligned16(wq1_i) || (sw && !aligned16(wq_up_i)) || !aligned16(wq2_i))
+    return fail(TP_ERR_UNSUPPORTED, "tp_mlp_shard_fwd_fp8: needs d, ff_i multiples of 64 and 16-byte aligned x, weights");
+  const FwdLayout L = fwd_layout(T, d, ff_i, TP_BF16, act, true);
+  if (L.p1.kernel != tpk::KERNEL_DECODE || L.p2.kernel != tpk::KERNEL_DECODE)
+    return fail(TP_ERR_UNSUPPORTED, "tp_mlp_shard_fwd_fp8: no fp8 kernel for this shape");
+  if (!ws) return fail(TP_ERR_WORKSPACE, "tp_mlp_shard_fwd_fp8: workspace required (%zu bytes)", L.total);
+  if (ws_bytes < L.total)
+    return fail(TP_ERR_WORKSPACE, "tp_mlp_shard_fwd_fp8: workspace of %zu bytes < %zu needed", ws_bytes, L.total);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* base = reinterpret_cast<char*>(ws);
+
+  // column GEMM: h = act(x W1) (or SwiGLU) written straight into the row
+  // GEMM's packed activation layout (ff_i is a multiple of 16 here)
+  GemmParams p1 = base_params();
+  p1.A0 = x;
+  p1.lda = d;
+  p1.B0 = wq1_i;
+  p1.B1 = wq_up_i;
+  p1.ldb = ff_i;
+  p1.K0 = (int)d;
+  p1.M = (int)T;
+  p1.N = (int)ff_i;
+  p1.C = base + L.h_off;
+  p1.ldc = ff_i;
+  p1.act = act;
+  p1.vecA = p1.vecB = 1;
+  p1.b_fp8 = 1;
+  p1.bscale0 = s1_i;
+  p1.bscale1 = s_up_i;
+  attach_split(p1, L.p1, base + L.cnt_off, base + L.part_off, base + L.pack_off);
+  p1.cpk = base + L.pack2_off;
+  p1.cpk_mt = T <= 32 ? 1 : 2;
+
+  GemmParams p2 = base_params();
+  p2.A0 = base + L.h_off;
+  p2.lda = ff_i;
+  p2.B0 = wq2_i;
+  p2.ldb = d;
+  p2.K0 = (int)ff_i;
+  p2.M = (int)T;
+  p2.N = (int)d;
+  p2.C = y_i;
+  p2.ldc = d;
+  p2.vecA = p2.vecB = 1;
+  p2.b_fp8 = 1;
+  p2.bscale0 = s2_i;
+  attach_split(p2, L.p2, base + L.cnt_off, base + L.part_off, base + L.pack2_off);
+  p2.apk_ready = 1;
+
+  hipError_t e = tpk::gemm_bf16(p1, L.p1, sw ? tpk::GK_FWD_SWIGLU : tpk::GK_FWD_ACT, false, s);
+  if (e != hipSuccess) return hip_status(e, "tp_mlp_shard_fwd_fp8 (column GEMM)");
+  e = tpk::gemm_bf16(p2, L.p2, tpk::GK_FWD_STORE, out_dtype == TP_F32, s);
+  return hip_status(e, "tp_mlp_shard_fwd_fp8 (row GEMM)");
+}
+
 tp_status tp_fp8_pack_strips(const void* src, void* dst, int64_t K, int64_t N, tp_stream stream) {
   if (!dim_ok(K) || !dim_ok(N) || !prod_ok(K, N)) return fail(TP_ERR_SHAPE, "tp_fp8_pack_strips: sizes out of range");
   if (N % 64) return fail(TP_ERR_SHAPE, "tp_fp8_pack_strips: N=%lld is not a multiple of 64", (long long)N);

@@ -216,6 +216,15 @@ def test_linear_fp8_validation(lib):
     g = lib.tp_row_linear_partial_fp8
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, ws, 64, 1024, 256, 7, None) == DTYPE
     assert g(FAKE, FAKE, None, FAKE, FAKE, ws, 64, 1024, 256, 0, None) == NULL
+    m = lib.tp_mlp_shard_fwd_fp8
+    mws = lib.tp_mlp_shard_fwd_fp8_workspace(64, 8192, 3584, 3)
+    assert mws > 0 and lib.tp_mlp_shard_fwd_fp8_workspace(65, 8192, 3584, 3) == 0
+    margs = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert m(*margs, ctypes.c_size_t(mws), 64, 8192, 3584, 0, 9, None) == ACTE
+    assert m(*margs, ctypes.c_size_t(mws), 65, 8192, 3584, 0, 3, None) == 6      # T > 64
+    assert m(*margs, ctypes.c_size_t(mws), 64, 8192, 3600, 0, 3, None) == 6      # ff_i % 64
+    assert m(*margs[:8], None, 0, 64, 8192, 3584, 0, 3, None) == WS
+    assert m(FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, mws, 64, 8192, 3584, 0, 3, None) == ACTE
     pk = lib.tp_fp8_pack_strips
     assert pk(FAKE, ctypes.c_void_p(0x2000), 16, 100, None) == SHAPE     # N % 64
     assert pk(FAKE, FAKE, 16, 128, None) == SHAPE                         # aliasing

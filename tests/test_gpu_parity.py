@@ -734,6 +734,31 @@ def test_fp8_decode_shard_T64():
     assert_close(y, O.row_linear_partial_fp8(h64, qd, sd), BF16_TOL, "fp8 shard output")
 
 
+@pytest.mark.parametrize("T,act", [(64, "swiglu"), (1, "swiglu"), (40, "gelu"), (33, "relu")])
+def test_fp8_mlp_shard_fwd(T, act):
+    """The fused fp8 shard (h handed to the row GEMM in packed form) against the
+    fp64 chain, and bitwise against the two separate fp8 linears."""
+    d, ff_i = 8192, 3584
+    x = W.normal((T, d), 1.0, 84, 1)
+    q1, qd = W.e4m3_codes((d, ff_i), 84, 2), W.e4m3_codes((ff_i, d), 84, 4)
+    qu = W.e4m3_codes((d, ff_i), 84, 3) if act == "swiglu" else None
+    s1, sd = W.column_scales(ff_i, 84, 5), W.column_scales(d, 84, 7)
+    su = W.column_scales(ff_i, 84, 6) if act == "swiglu" else None
+    p1, pu, p2 = packed(q1), None if qu is None else packed(qu), packed(qd)
+    c1, cu, c2 = cuda(s1), None if su is None else cuda(su), cuda(sd)
+    y = torch.empty(T, d, dtype=torch.bfloat16, device="cuda")
+    ws = tp.new_workspace(tp.tp_mlp_shard_fwd_fp8_workspace(T, d, ff_i, act))
+    tp.tp_mlp_shard_fwd_fp8(cuda(x), p1, c1, pu, cu, p2, c2, y, act, ws)
+    h64 = O.col_linear_fp8(x, q1, s1, qu, su, None, act)
+    assert_close(y, O.row_linear_partial_fp8(h64, qd, sd), BF16_TOL, f"fp8 shard {act}")
+    h = torch.empty(T, ff_i, dtype=torch.bfloat16, device="cuda")
+    y2 = torch.empty_like(y)
+    ws2 = tp.new_workspace(max(tp.tp_linear_fp8_workspace(T, d, ff_i, act), tp.tp_linear_fp8_workspace(T, ff_i, d)))
+    tp.tp_col_linear_fp8(cuda(x), p1, c1, pu, cu, None, h, act, ws2)
+    tp.tp_row_linear_partial_fp8(h, p2, c2, y2, ws2)
+    assert torch.equal(y, y2)
+
+
 def test_one_workspace_serves_every_entry_point():
     """One zero-initialised workspace reused across entry points and shapes in
     sequence gives bitwise the results each call gives with a fresh one (the
