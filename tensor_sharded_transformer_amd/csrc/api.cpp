@@ -3,6 +3,7 @@
 // first launch, so a rejected call has no side effect.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -852,7 +853,8 @@ tp_status tp_gqa_attention_fwd(const void* qkv, void* out, int64_t T, int n_q, i
     return fail(TP_ERR_SHAPE, "tp_gqa_attention_fwd: bad sizes (T=%lld, n_q=%d, n_kv=%d, head_dim=%d)", (long long)T,
                 n_q, n_kv, head_dim);
   if (causal != 0 && causal != 1) return fail(TP_ERR_SHAPE, "tp_gqa_attention_fwd: causal must be 0 or 1");
-  if (!(scale > 0.0f) || scale > 3.0e38f) return fail(TP_ERR_SHAPE, "tp_gqa_attention_fwd: scale must be finite and > 0");
+  if (!(scale > 0.0f) || !std::isfinite(scale))
+    return fail(TP_ERR_SHAPE, "tp_gqa_attention_fwd: scale must be finite and > 0");
   if (head_dim != tpk::attention_head_dim())
     return fail(TP_ERR_UNSUPPORTED, "tp_gqa_attention_fwd: head_dim %d (only %d is built)", head_dim,
                 tpk::attention_head_dim());

@@ -193,6 +193,7 @@ def test_gqa_attention_validation(lib):
     assert f(FAKE, FAKE, 64, 8, 1, 128, 2, sc, None) == SHAPE          # causal flag not 0/1
     assert f(FAKE, FAKE, 64, 8, 1, 128, 1, ctypes.c_float(0.0), None) == SHAPE
     assert f(FAKE, FAKE, 64, 8, 1, 128, 1, ctypes.c_float(float("nan")), None) == SHAPE
+    assert f(FAKE, FAKE, 64, 8, 1, 128, 1, ctypes.c_float(float("inf")), None) == SHAPE
     assert f(FAKE, FAKE, 64, 8, 1, 64, 1, sc, None) == 6               # head_dim 64: not built
     assert f(None, FAKE, 64, 8, 1, 128, 1, sc, None) == NULL
     assert f(ctypes.c_void_p(0x1008), FAKE, 64, 8, 1, 128, 1, sc, None) == 6   # unaligned
