@@ -78,7 +78,8 @@ typedef enum { TP_ACT_NONE = 0, TP_ACT_RELU = 1, TP_ACT_GELU = 2, TP_ACT_SWIGLU 
  *   y = silu(x . w) * (x . w_up)              for SWIGLU
  * x (T, K) (device), w and w_up (K, N_i) (device), bias (N_i) or NULL
  * (device; this shard's slice of the column bias; must be NULL for SWIGLU),
- * y (T, N_i) (device).  Errors: TP_ERR_NULL, TP_ERR_SHAPE (negative sizes),
+ * y (T, N_i) (device).  K == 0 gives act(bias) in every row (x and w may
+ * then be NULL).  Errors: TP_ERR_NULL, TP_ERR_SHAPE (negative sizes),
  * TP_ERR_ACT (w_up given iff SWIGLU violated, or bias with SWIGLU),
  * TP_ERR_DTYPE, TP_ERR_HIP. */
 tp_status tp_col_linear(const void* x, const void* w, const void* w_up, const void* bias, void* y,

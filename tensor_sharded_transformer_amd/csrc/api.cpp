@@ -232,7 +232,8 @@ tp_status linear_fp8(const char* who, const void* x, const void* wq, const float
     return fail(TP_ERR_UNSUPPORTED, "%s: T=%lld (fp8 weights are built for decode sizes, T <= %d)", who,
                 (long long)T, tpk::STREAM_MAX_M);
   if (T == 0 || N == 0) return TP_OK;
-  if (!x || !wq || !scale || !y || (kind == tpk::GK_FWD_SWIGLU && (!wq_up || !scale_up)))
+  if ((!x && K > 0) || (!wq && K > 0) || !scale || !y ||
+      (kind == tpk::GK_FWD_SWIGLU && ((!wq_up && K > 0) || !scale_up)))
     return fail(TP_ERR_NULL, "%s: null input or output pointer", who);
   if (N % 64 || K % 8 || !aligned16(x) || !aligned16(wq) || (wq_up && !aligned16(wq_up)))
     return fail(TP_ERR_UNSUPPORTED, "%s: needs N %% 64 == 0, K %% 8 == 0 and 16-byte aligned x and weights", who);
@@ -343,7 +344,9 @@ tp_status tp_col_linear(const void* x, const void* w, const void* w_up, const vo
   if (!sw && w_up) return fail(TP_ERR_ACT, "tp_col_linear: w_up is only used by SWIGLU");
   if (sw && bias) return fail(TP_ERR_ACT, "tp_col_linear: a bias is not defined for SWIGLU");
   if (T == 0 || N_i == 0) return TP_OK;
-  if (!x || !w || !y) return fail(TP_ERR_NULL, "tp_col_linear: null x, w or y");
+  // (an empty x or w, K == 0, may be NULL: the output is then act(bias))
+  if ((!x && K > 0) || (!w && K > 0) || !y)
+    return fail(TP_ERR_NULL, "tp_col_linear: null x, w or y");
   GemmParams p = base_params();
   p.A0 = x;
   p.lda = K;
@@ -399,7 +402,8 @@ tp_status tp_row_linear_partial(const void* x_i, const void* w_i, void* z_i, voi
   if (!dim_ok(T) || !dim_ok(K_i) || !dim_ok(N) || !prod_ok(T, K_i) || !prod_ok(K_i, N) || !prod_ok(T, N))
     return fail(TP_ERR_SHAPE, "tp_row_linear_partial: sizes out of range");
   if (T == 0 || N == 0) return TP_OK;
-  if (!x_i || !w_i || !z_i) return fail(TP_ERR_NULL, "tp_row_linear_partial: null x_i, w_i or z_i");
+  if ((!x_i && K_i > 0) || (!w_i && K_i > 0) || !z_i)
+    return fail(TP_ERR_NULL, "tp_row_linear_partial: null x_i, w_i or z_i");
   GemmParams p = base_params();
   p.A0 = x_i;
   p.lda = K_i;

@@ -366,7 +366,7 @@ int decode_split(GemmParams& p, const GemmPlan& plan) {
 
 template <int MT, bool DUAL, int EPI, typename OutT>
 hipError_t launch_decode_mt(const GemmParams& p, const GemmPlan& plan, hipStream_t s) {
-  if (!p.apk_ready) {
+  if (!p.apk_ready && p.K0 > 0) {  // (an empty contraction has nothing to pack)
     const int nsteps = (p.K0 + 15) / 16;
     const int npk = nsteps * MT * 64;
     hipLaunchKernelGGL(pack_a_kernel<MT>, dim3((npk + 255) / 256), dim3(256), 0, s,

@@ -788,3 +788,23 @@ def test_one_workspace_serves_every_entry_point():
     for order in (["mlp", "col", "row", "fp8"], ["fp8", "row", "col", "mlp"], ["col", "mlp", "fp8", "row"]):
         for k in order:
             assert torch.equal(calls[k][0](shared), fresh[k]), f"{k} after {order}"
+
+
+@pytest.mark.parametrize("T", [64, 300])
+def test_empty_contraction(T):
+    """K = 0: the column-parallel linear gives act(bias) in every row and the
+    row-parallel partial gives zeros (decode and tiled sizes, with and without
+    a workspace)."""
+    N = 256
+    x = torch.empty(T, 0, dtype=torch.bfloat16, device="cuda")
+    w = torch.empty(0, N, dtype=torch.bfloat16, device="cuda")
+    bias = cuda(W.normal((N,), 1.0, 95, 1))
+    for with_ws in (True, False):
+        ws = tp.new_workspace(tp.tp_col_linear_workspace(T, 0, N, tp.TP_BF16, "relu")) if with_ws else None
+        y = torch.full((T, N), 7.0, dtype=torch.bfloat16, device="cuda")
+        tp.tp_col_linear(x, w, None, bias, y, "relu", ws)
+        assert torch.equal(y, torch.relu(bias.float()).to(torch.bfloat16).expand(T, N))
+        ws = tp.new_workspace(tp.tp_row_linear_partial_workspace(T, 0, N, tp.TP_BF16)) if with_ws else None
+        z = torch.full((T, N), 7.0, dtype=torch.float32, device="cuda")
+        tp.tp_row_linear_partial(x, w, z, ws)
+        assert bool((z == 0).all())
