@@ -470,7 +470,12 @@ tp_status tp_mlp_shard_fwd_fp8(const void* x, const void* wq1_i, const float* s1
   if (T > tpk::STREAM_MAX_M)
     return fail(TP_ERR_UNSUPPORTED, "tp_mlp_shard_fwd_fp8: T=%lld (decode sizes, T <= %d)", (long long)T,
                 tpk::STREAM_MAX_M);
-  if (T == 0) return TP_OK;
+  if (T == 0 || d == 0) return TP_OK;
+  if (ff_i == 0) {  // empty intermediate: the partial is zero
+    if (!y_i) return fail(TP_ERR_NULL, "tp_mlp_shard_fwd_fp8: null y_i");
+    const size_t yb = (size_t)T * d * (out_dtype == TP_F32 ? 4 : 2);
+    return hip_status(tpk::zero_fill(y_i, yb, reinterpret_cast<hipStream_t>(stream)), "tp_mlp_shard_fwd_fp8 (ff_i=0)");
+  }
   if (!x || !wq1_i || !s1_i || !wq2_i || !s2_i || !y_i) return fail(TP_ERR_NULL, "tp_mlp_shard_fwd_fp8: null pointer");
   if (d % 64 || ff_i % 64 || !aligned16(x) || !aligned16(wq1_i) || (sw && !aligned16(wq_up_i)) || !aligned16(wq2_i))
     return fail(TP_ERR_UNSUPPORTED, "tp_mlp_shard_fwd_fp8: needs d, ff_i multiples of 64 and 16-byte aligned x, weights");
@@ -599,7 +604,12 @@ tp_status tp_mlp_shard_fwd(const void* x, const void* w1_i, const void* w_up_i, 
     return fail(TP_ERR_SHAPE, "tp_mlp_shard_fwd: sizes out of range");
   const bool sw = act == TP_ACT_SWIGLU;
   if (sw != (w_up_i != nullptr)) return fail(TP_ERR_ACT, "tp_mlp_shard_fwd: w_up_i must be given iff SWIGLU");
-  if (T == 0) return TP_OK;
+  if (T == 0 || d == 0) return TP_OK;
+  if (ff_i == 0) {  // empty intermediate: the partial is zero (and saved is empty)
+    if (!y_i) return fail(TP_ERR_NULL, "tp_mlp_shard_fwd: null y_i");
+    const size_t yb = (size_t)T * d * esize(out_dtype);
+    return hip_status(tpk::zero_fill(y_i, yb, reinterpret_cast<hipStream_t>(stream)), "tp_mlp_shard_fwd (ff_i=0)");
+  }
   if (!x || !w1_i || !w2_i || !y_i) return fail(TP_ERR_NULL, "tp_mlp_shard_fwd: null x, w1_i, w2_i or y_i");
   const bool vec = aligned16(x) && aligned16(w1_i) && (!sw || aligned16(w_up_i)) && aligned16(w2_i) &&
                    d % 8 == 0 && ff_i % 8 == 0;
@@ -675,10 +685,15 @@ tp_status tp_mlp_shard_bwd(const void* x, const void* w1_i, const void* w_up_i, 
   const bool sw = act == TP_ACT_SWIGLU;
   if (sw != (w_up_i != nullptr) || sw != (dw_up_i != nullptr))
     return fail(TP_ERR_ACT, "tp_mlp_shard_bwd: w_up_i and dw_up_i must be given iff SWIGLU");
-  if (!x || !w1_i || !w2_i || !saved || !dy || !dw1_i || !dw2_i || !dx_i)
-    return fail(TP_ERR_NULL, "tp_mlp_shard_bwd: null input or output pointer");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const size_t es = esize(dtype);
+  if (d == 0) return TP_OK;  // every gradient is empty
+  if (ff_i == 0) {           // empty intermediate: weight gradients empty, dx_i zero
+    if (!dx_i && T > 0) return fail(TP_ERR_NULL, "tp_mlp_shard_bwd: null dx_i");
+    return hip_status(T ? tpk::zero_fill(dx_i, (size_t)T * d * es, s) : hipSuccess, "tp_mlp_shard_bwd (ff_i=0)");
+  }
+  if (!w1_i || !w2_i || !dw1_i || !dw2_i || (T > 0 && (!x || !saved || !dy || !dx_i)))
+    return fail(TP_ERR_NULL, "tp_mlp_shard_bwd: null input or output pointer");
   if (T == 0) {
     // no tokens: the weight gradients are zero, dx_i is empty
     hipError_t e = tpk::zero_fill(dw1_i, (size_t)d * ff_i * es, s);

@@ -808,3 +808,30 @@ def test_empty_contraction(T):
         z = torch.full((T, N), 7.0, dtype=torch.float32, device="cuda")
         tp.tp_row_linear_partial(x, w, z, ws)
         assert bool((z == 0).all())
+
+
+def test_empty_intermediate_and_no_tokens():
+    """ff_i = 0: the shard's partial is zero and so is its dx_i; T = 0: the
+    weight gradients are zero."""
+    T, d = 16, 128
+    x = cuda(W.normal((T, d), 1.0, 96, 1))
+    e_w1 = torch.empty(d, 0, dtype=torch.bfloat16, device="cuda")
+    e_w2 = torch.empty(0, d, dtype=torch.bfloat16, device="cuda")
+    y = torch.full((T, d), 7.0, dtype=torch.bfloat16, device="cuda")
+    tp.tp_mlp_shard_fwd(x, e_w1, None, e_w2, y, "relu", None)
+    assert bool((y == 0).all())
+    dy = cuda(W.normal((T, d), 1.0, 96, 2))
+    dx = torch.full((T, d), 7.0, dtype=torch.bfloat16, device="cuda")
+    sv = torch.empty(T, 0, dtype=torch.bfloat16, device="cuda")
+    tp.tp_mlp_shard_bwd(x, e_w1, None, e_w2, sv, dy, torch.empty_like(e_w1), None, torch.empty_like(e_w2), dx,
+                        "relu", None)
+    assert bool((dx == 0).all())
+    w1 = cuda(W.normal((d, 64), 0.02, 96, 3))
+    w2 = cuda(W.normal((64, d), 0.02, 96, 4))
+    g1 = torch.full_like(w1, 7.0)
+    g2 = torch.full_like(w2, 7.0)
+    x0 = torch.empty(0, d, dtype=torch.bfloat16, device="cuda")
+    tp.tp_mlp_shard_bwd(x0, w1, None, w2, torch.empty(0, 64, dtype=torch.bfloat16, device="cuda"),
+                        torch.empty(0, d, dtype=torch.bfloat16, device="cuda"), g1, None, g2,
+                        torch.empty(0, d, dtype=torch.bfloat16, device="cuda"), "relu", None)
+    assert bool((g1 == 0).all()) and bool((g2 == 0).all())
