@@ -220,6 +220,9 @@ def test_partial_sum_bias_once_and_dtypes():
     (4, 8, 4100, "f32", "f32", False),
     (2, 6, 77, "bf16", "bf16", True),
     (8, 4096, 8192, "bf16", "bf16", False),
+    (2, 4, 32768, "bf16", "f32", True),        # the largest row the kernel takes (whole row in LDS)
+    (2, 4, 32768, "f32", "f32", False),
+    (1, 2, 32761, "bf16", "bf16", False),      # odd row length: the scalar path
 ])
 def test_rs_residual_rmsnorm(p, T, N, in_dt, out_dt, with_bias):
     seed = p * 1000 + N
@@ -618,7 +621,7 @@ def test_attention_T4096_rank_heads(causal):
 
 
 @pytest.mark.parametrize("T,n_q,n_kv,causal", [(4000, 8, 1, True), (4000, 8, 1, False), (1000, 8, 2, True),
-                                                (2113, 4, 4, False)])
+                                                (2113, 4, 4, False), (8192, 8, 1, True)])
 def test_attention_ragged_long(T, n_q, n_kv, causal):
     """Lengths that leave partial key tiles and uneven key ranges across the
     workgroup's groups, on 48 sampled query rows plus the first and last."""
