@@ -34,8 +34,10 @@
 //  * O^T = V^T P^T: V^T is the A operand read from LDS with
 //    ds_read_b64_tr_b16 (V keeps its key-major layout), P^T the B operand
 //    built from the exponentiated S^T accumulators (hardware bf16
-//    conversion); the two lanes of a query swap one 4-key group so the
-//    fragment's k order is the standard one.
+//    conversion); the two lanes of a query swap one 4-key group with
+//    v_permlane32_swap (no LDS traffic) so the fragment's k order is the
+//    standard one.  The row max and the final row sum combine the two lanes
+//    the same way.
 //  * Keys advance in tiles of BKEY through a two-stage ring per group (K and
 //    V, 256 bytes per key each), filled by buffer loads that write LDS directly;
 //    the next tile's loads are in flight while the current tile feeds the
@@ -75,6 +77,20 @@ __device__ __forceinline__ int vswz(int r) { return ((r & 1) * 10) ^ ((r & 2) * 
 
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// The two lanes of a query (l and l + 32) exchange halves with
+// v_permlane32_swap (VALU, no LDS traffic): it returns {x with the upper
+// half replaced by y's lower half, y with the lower half replaced by x's
+// upper half}.  half_max / half_sum combine a value over the lane pair
+// (both lanes get the same result, low lane's value first).
+__device__ __forceinline__ float half_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_at(const void* base) {
@@ -239,7 +255,7 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(const uint16_t* __restrict
     for (int kt = 0; kt < C::NKT; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sacc[kt][r]);
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    mloc = half_max(mloc);
     // running max in base-2 units (c2 = scale * log2 e > 0 keeps the order)
     const float m_new = fmaxf(m_run, mloc * c2);
     const float m_use = m_new == -INFINITY ? 0.0f : m_new;
@@ -268,9 +284,10 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(const uint16_t* __restrict
       // this lane: keys 4h..4h+3 (a) and 8+4h..8+4h+3 (b) of the substep
       const u32x2 a = {pack2(sacc[kt][r0 + 0], sacc[kt][r0 + 1]), pack2(sacc[kt][r0 + 2], sacc[kt][r0 + 3])};
       const u32x2 b = {pack2(sacc[kt][r0 + 4], sacc[kt][r0 + 5]), pack2(sacc[kt][r0 + 6], sacc[kt][r0 + 7])};
-      const u32x2 send = h ? a : b;
-      const u32x2 recv = {(unsigned)__shfl_xor((int)send[0], 32), (unsigned)__shfl_xor((int)send[1], 32)};
-      const u32x4 pf = h ? u32x4{recv[0], recv[1], b[0], b[1]} : u32x4{a[0], a[1], recv[0], recv[1]};
+      // low lane: {a, partner's a} = keys 0..7; high lane: {partner's b, b} = keys 8..15
+      const auto s0 = __builtin_amdgcn_permlane32_swap(a[0], b[0], false, false);
+      const auto s1 = __builtin_amdgcn_permlane32_swap(a[1], b[1], false, false);
+      const u32x4 pf = {s0[0], s1[0], s0[1], s1[1]};
       const bf16x8 pfrag = __builtin_bit_cast(bf16x8, pf);
 #pragma unroll
       for (int dt = 0; dt < HD / 32; ++dt) {
@@ -338,7 +355,7 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(const uint16_t* __restrict
 #pragma unroll
       for (int r = 0; r < 16; ++r) oacc[dt][r] += xo[(dt * 16 + r) * 64 + lane] * ag;
   }
-  const float inv = 1.0f / (l_lane + __shfl_xor(l_lane, 32));
+  const float inv = 1.0f / half_sum(l_lane);
   uint16_t* orow = out + (size_t)myq * ldo + head * HD;
 #pragma unroll
   for (int dt = 0; dt < HD / 32; ++dt)
