@@ -880,6 +880,8 @@ tp_status tp_gqa_attention_fwd(const void* qkv, void* out, int64_t T, int n_q, i
   const int64_t width = (int64_t)(n_q + 2 * n_kv) * head_dim;
   // a 64-row key tile of one row stride must stay within 32-bit buffer offsets
   if (width > (1 << 23) || !prod_ok(T, width)) return fail(TP_ERR_SHAPE, "tp_gqa_attention_fwd: sizes out of range");
+  if ((T + 63) / 64 * n_q > kMaxDim)  // one workgroup per (query block, head)
+    return fail(TP_ERR_SHAPE, "tp_gqa_attention_fwd: too many query blocks x heads for one launch");
   if (T == 0) return TP_OK;
   if (!qkv || !out) return fail(TP_ERR_NULL, "tp_gqa_attention_fwd: null qkv or out");
   if (!aligned16(qkv) || !aligned16(out))
