@@ -838,3 +838,43 @@ def test_empty_intermediate_and_no_tokens():
                         torch.empty(0, d, dtype=torch.bfloat16, device="cuda"), g1, None, g2,
                         torch.empty(0, d, dtype=torch.bfloat16, device="cuda"), "relu", None)
     assert bool((g1 == 0).all()) and bool((g2 == 0).all())
+
+
+def test_block_rows_graph_replay():
+    """Local attention, the fp8 decode shard and the sequence-parallel boundary
+    captured together in one HIP graph: several replays with eager calls in
+    between, each bit-identical to the eager results (none of them issues a
+    memset)."""
+    T, d, ff_i = 64, 2048, 512
+    qkv = cuda(W.normal((256, 1280), 1.81, 97, 1))
+    att = torch.empty(256, 1024, dtype=torch.bfloat16, device="cuda")
+    x = cuda(W.normal((T, d), 1.0, 97, 2))
+    q1, qu, q2 = (packed(W.e4m3_codes(sh, 97, k)) for k, sh in ((3, (d, ff_i)), (4, (d, ff_i)), (5, (ff_i, d))))
+    s1, su, s2 = cuda(W.column_scales(ff_i, 97, 6)), cuda(W.column_scales(ff_i, 97, 7)), cuda(W.column_scales(d, 97, 8))
+    y = torch.empty(T, d, dtype=torch.bfloat16, device="cuda")
+    ws = tp.new_workspace(tp.tp_mlp_shard_fwd_fp8_workspace(T, d, ff_i, "swiglu"))
+    zs = [cuda(W.normal((T, d), 1.0, 97, 10 + i)) for i in range(4)]
+    res, nw = cuda(W.normal((T // 4, d), 1.0, 97, 20)), cuda(W.normal((d,), 1.0, 97, 21))
+    r_out = torch.empty_like(res)
+    yn = torch.empty_like(res)
+
+    def run():
+        tp.tp_gqa_attention_fwd(qkv, att, 8, 1, 128, True, 128 ** -0.5)
+        tp.tp_mlp_shard_fwd_fp8(x, q1, s1, qu, su, q2, s2, y, "swiglu", ws)
+        tp.tp_rs_residual_rmsnorm(zs, 1, None, res, nw, 1e-5, r_out, yn)
+
+    run()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (att, y, r_out, yn)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for r in range(3):
+        for t in (att, y, r_out, yn):
+            t.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((att, y, r_out, yn), eager):
+            assert torch.equal(a, b), f"replay {r}"
+        run()   # eager calls on the same buffers and workspace between replays
+        torch.cuda.synchronize()
