@@ -38,6 +38,8 @@ Readings where the pages are silent (also listed with the design notes):
   * The backward of the attention projections is the backward of two
     linear shards: QKV column-parallel (partial dx), o_proj row-parallel
     (replicated dy, local dx); no bias gradients.
+  * MoE routing: softmax over the router logits, top-k (ties to the lower
+    index), the k probabilities renormalised; experts sharded in place.
   * Local attention is scaled dot-product softmax attention, optionally
     causal, with query head j reading KV head j // (n_q / n_kv).
   * The "quantized equivalent" of a sharded linear is read as fp8 weights:
@@ -398,6 +400,50 @@ def linear_shard_bwd(x, w, dy) -> Dict[str, np.ndarray]:
     w = to64(w)
     dy = to64(dy)
     return {"dw": matmul(x.T, dy), "dx": matmul(dy, w.T)}
+
+
+# ---------------------------------------------------------------------------
+# Mixture-of-experts block with experts sharded in place.  [MLX] Facts: the
+# MoE layers of DeepSeek V3 and Qwen3-MoE shard their routed experts in place
+# (each rank keeps a slice of every expert), leave the router replicated and
+# sum the block's output once.  The routing rule is not on the pages; it is
+# read as softmax over the router logits, the top-k experts per token (ties to
+# the lower index), with the k probabilities renormalised to sum to 1.
+# ---------------------------------------------------------------------------
+def moe_route(logits, k: int) -> Tuple[np.ndarray, np.ndarray]:
+    """(idx (T, k) int, gate (T, k)) from router logits (T, E): the k largest
+    softmax probabilities per row in descending order (equal logits: lower
+    expert index first), renormalised over the chosen k."""
+    lg = to64(logits)
+    T, E = lg.shape
+    if not 1 <= k <= E:
+        raise ValueError("k must be in 1..E")
+    idx = np.zeros((T, k), dtype=np.int64)
+    gate = np.zeros((T, k), dtype=F64)
+    for t in range(T):
+        order = sorted(range(E), key=lambda e: (-lg[t, e], e))[:k]
+        w = np.exp(lg[t, order] - lg[t, order[0]])
+        idx[t] = order
+        gate[t] = w / w.sum()
+    return idx, gate
+
+
+def moe_shard_fwd(x, idx, gate, w1, w_up, w2, act: str = "swiglu") -> np.ndarray:
+    """One rank's partial of the MoE block: for each token t,
+        y_i[t] = sum_j gate[t, j] * mlp_shard(x[t]; expert idx[t, j]'s slices)
+    with w1, w_up (E, d, ff_i) and w2 (E, ff_i, d) the rank's slices of every
+    expert (in-place sharding).  Summing y_i over ranks gives the block."""
+    x = to64(x)
+    idx = np.asarray(idx)
+    gate = to64(gate)
+    T, d = x.shape
+    y = np.zeros((T, d), dtype=F64)
+    for j in range(idx.shape[1]):
+        for e in np.unique(idx[:, j]):
+            rows = np.nonzero(idx[:, j] == e)[0]
+            h = col_linear(x[rows], w1[e], None if w_up is None else w_up[e], None, act)
+            y[rows] += gate[rows, j][:, None] * matmul(h, to64(w2[e]))
+    return y
 
 
 def gqa_attention(qkv, n_q: int, n_kv: int, head_dim: int, causal: bool, scale: float,

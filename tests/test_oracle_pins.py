@@ -560,6 +560,63 @@ def test_fp8_linear_column_scales():
 
 
 # --------------------------------------------------------------------------
+# Mixture of experts, experts sharded in place (MLX page, Facts).
+# --------------------------------------------------------------------------
+def test_moe_route_hand_values():
+    idx, gate = O.moe_route(np.array([[0.0, 1.0, 1.0, -1.0], [2.0, 0.0, 0.0, 0.0]]), 2)
+    np.testing.assert_array_equal(idx, [[1, 2], [0, 1]])            # equal logits: lower index first
+    np.testing.assert_allclose(gate, [[0.5, 0.5], [math.e ** 2 / (math.e ** 2 + 1), 1 / (math.e ** 2 + 1)]],
+                               rtol=1e-14)
+
+
+def test_moe_route_all_experts_is_the_softmax():
+    rng = np.random.default_rng(71)
+    lg = rng.standard_normal((5, 6))
+    idx, gate = O.moe_route(lg, 6)
+    sm = scipy.special.softmax(lg, axis=1)
+    np.testing.assert_array_equal(idx, np.argsort(-lg, axis=1, kind="stable"))
+    np.testing.assert_allclose(gate, np.take_along_axis(sm, idx, 1), rtol=1e-13)
+
+
+def _moe_weights(rng, E, d, ff):
+    return (rng.standard_normal((E, d, ff)) * 0.3, rng.standard_normal((E, d, ff)) * 0.3,
+            rng.standard_normal((E, ff, d)) * 0.3)
+
+
+def test_moe_identical_experts_reduce_to_the_dense_block():
+    """With every expert equal and gates summing to 1 the block is the plain
+    SwiGLU shard."""
+    rng = np.random.default_rng(72)
+    T, d, ff, E, k = 6, 8, 12, 5, 3
+    x = rng.standard_normal((T, d))
+    w1, wu, w2 = (np.repeat(a[:1], E, axis=0) for a in _moe_weights(rng, 1, d, ff))
+    idx, gate = O.moe_route(rng.standard_normal((T, E)), k)
+    dense, _ = O.mlp_shard_fwd(x, w1[0], wu[0], w2[0], "swiglu")
+    np.testing.assert_allclose(O.moe_shard_fwd(x, idx, gate, w1, wu, w2), dense, rtol=1e-12, atol=1e-12)
+
+
+def test_moe_in_place_shards_sum_to_the_block_and_match_a_token_loop():
+    rng = np.random.default_rng(73)
+    T, d, ff, E, k, p = 7, 8, 12, 4, 2, 3
+    x = rng.standard_normal((T, d))
+    w1, wu, w2 = _moe_weights(rng, E, d, ff)
+    idx, gate = O.moe_route(rng.standard_normal((T, E)), k)
+    full = O.moe_shard_fwd(x, idx, gate, w1, wu, w2)
+    loop = np.zeros((T, d))
+    for t in range(T):
+        for j in range(k):
+            e = idx[t, j]
+            g = x[t] @ w1[e]
+            loop[t] += gate[t, j] * ((g / (1 + np.exp(-g)) * (x[t] @ wu[e])) @ w2[e])
+    np.testing.assert_allclose(full, loop, rtol=1e-12, atol=1e-12)
+    parts = []
+    for i in range(p):
+        b, n = O.shard_range(ff, p, i)
+        parts.append(O.moe_shard_fwd(x, idx, gate, w1[:, :, b:b + n], wu[:, :, b:b + n], w2[:, b:b + n, :]))
+    np.testing.assert_allclose(O.partial_sum(parts), full, rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
 # Work accounting: training ~ 6 x params x tokens.
 # --------------------------------------------------------------------------
 def test_flop_accounting():
