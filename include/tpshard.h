@@ -240,6 +240,31 @@ tp_status tp_mlp_shard_fwd_fp8(const void* x, const void* wq1_i, const float* s1
                                const float* s_up_i, const void* wq2_i, const float* s2_i, void* y_i,
                                void* ws, size_t ws_bytes, int64_t T, int64_t d, int64_t ff_i,
                                tp_dtype out_dtype, tp_act act, tp_stream stream);
+/* Mixture-of-experts block with the routed experts sharded in place
+ * ([MLX] Facts: DeepSeek V3 and Qwen3-MoE shard their experts in place, keep
+ * the router replicated and sum the block output once).
+ * tp_moe_route: from router logits (T, E) fp32 (x times the replicated router
+ * weight, e.g. tp_row_linear_partial with an f32 output) to idx (T, k) int32
+ * and gate (T, k) fp32: the k largest logits per token in descending order
+ * (equal logits: lower expert index first), gates = softmax over the chosen
+ * k.  1 <= k <= min(E, 16), E <= 1024.
+ * tp_moe_shard_fwd: y_i[t] = sum_j gate[t, j] * silu(x[t] W1[e]) * (x[t] Wup[e])
+ * . W2[e] with e = idx[t, j]: this rank's partial (the group sums it).  x (T,
+ * d) bf16; w1, w_up (E, d, ff_i) and w2 (E, ff_i, d) bf16, the rank's slice
+ * of every expert, contiguous per expert; y_i (T, d) in out_dtype.  d and
+ * ff_i multiples of 8, 16-byte aligned pointers (TP_ERR_UNSUPPORTED
+ * otherwise).  Routed rows are grouped per expert on the device (no host
+ * round trip); ws (device) of ws_bytes >= tp_moe_shard_fwd_workspace(...),
+ * same rules as tp_mlp_shard_fwd's.  Results do not depend on the order in
+ * which the rows are grouped. */
+tp_status tp_moe_route(const float* logits, int64_t T, int E, int k, int32_t* idx, float* gate,
+                       tp_stream stream);
+size_t tp_moe_shard_fwd_workspace(int64_t T, int64_t d, int64_t ff_i, int E, int k);
+tp_status tp_moe_shard_fwd(const void* x, const int32_t* idx, const float* gate, const void* w1,
+                           const void* w_up, const void* w2, void* y_i, void* ws, size_t ws_bytes,
+                           int64_t T, int64_t d, int64_t ff_i, int E, int k, tp_dtype out_dtype,
+                           tp_stream stream);
+
 /* Rearranges fp8 codes from (K, N) row-major (src) into the 64-column
  * strip-major order the fp8 linears read (dst), once per weight matrix.  Both
  * device, 16-byte aligned, not aliasing; N % 64 == 0 (TP_ERR_SHAPE).

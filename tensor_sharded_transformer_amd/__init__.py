@@ -25,6 +25,9 @@ from .binding import (  # noqa: F401
     tp_mlp_shard_bwd,
     tp_mlp_shard_bwd_workspace,
     tp_mlp_shard_fwd,
+    tp_moe_route,
+    tp_moe_shard_fwd,
+    tp_moe_shard_fwd_workspace,
     tp_mlp_shard_fwd_fp8,
     tp_mlp_shard_fwd_fp8_workspace,
     tp_mlp_shard_fwd_workspace,

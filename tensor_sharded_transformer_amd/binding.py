@@ -53,6 +53,10 @@ SIGNATURES = {
     "tp_gqa_attention_fwd": (c_int, [c_p, c_p, c_i64, c_int, c_int, c_int, c_int, ctypes.c_float, c_p]),
     "tp_linear_fp8_workspace": (c_sz, [c_i64, c_i64, c_i64, c_int]),
     "tp_fp8_pack_strips": (c_int, [c_p, c_p, c_i64, c_i64, c_p]),
+    "tp_moe_route": (c_int, [c_p, c_i64, c_int, c_int, c_p, c_p, c_p]),
+    "tp_moe_shard_fwd_workspace": (c_sz, [c_i64, c_i64, c_i64, c_int, c_int]),
+    "tp_moe_shard_fwd": (c_int, [c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_sz, c_i64, c_i64, c_i64, c_int, c_int,
+                                 c_int, c_p]),
     "tp_mlp_shard_fwd_fp8_workspace": (c_sz, [c_i64, c_i64, c_i64, c_int]),
     "tp_mlp_shard_fwd_fp8": (c_int, [c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_sz, c_i64, c_i64, c_i64, c_int,
                                      c_int, c_p]),
@@ -299,6 +303,41 @@ def tp_mlp_shard_fwd_fp8(x, wq1_i, s1_i, wq_up_i, s_up_i, wq2_i, s2_i, y_i, act:
     _check(load().tp_mlp_shard_fwd_fp8(_ptr(x), _ptr(wq1_i), _ptr(s1_i), _ptr(wq_up_i), _ptr(s_up_i), _ptr(wq2_i),
                                        _ptr(s2_i), _ptr(y_i), _ptr(ws), ws.numel() if ws is not None else 0, T, d,
                                        ff_i, _dt(y_i), ACT[act], _stream()))
+    return y_i
+
+
+def tp_moe_route(logits, k: int, idx, gate):
+    """Top-k experts per token (idx int32 (T, k)) and their renormalised
+    softmax gates (fp32 (T, k)) from fp32 router logits (T, E)."""
+    T, E = logits.shape
+    if logits.dtype != torch.float32 or idx.dtype != torch.int32 or gate.dtype != torch.float32:
+        raise TypeError("logits and gate are float32, idx int32")
+    _shape(idx, (T, k), "idx")
+    _shape(gate, (T, k), "gate")
+    _check(load().tp_moe_route(_ptr(logits), T, E, k, _ptr(idx), _ptr(gate), _stream()))
+    return idx, gate
+
+
+def tp_moe_shard_fwd_workspace(T: int, d: int, ff_i: int, E: int, k: int) -> int:
+    return load().tp_moe_shard_fwd_workspace(T, d, ff_i, E, k)
+
+
+def tp_moe_shard_fwd(x, idx, gate, w1, w_up, w2, y_i, ws: torch.Tensor):
+    """This rank's partial of the MoE block (experts sharded in place)."""
+    T, d = x.shape
+    E, _, ff_i = w1.shape
+    k = idx.shape[1]
+    _shape(w1, (E, d, ff_i), "w1")
+    _shape(w_up, (E, d, ff_i), "w_up")
+    _shape(w2, (E, ff_i, d), "w2")
+    _shape(idx, (T, k), "idx")
+    _shape(gate, (T, k), "gate")
+    _shape(y_i, (T, d), "y_i")
+    if idx.dtype != torch.int32 or gate.dtype != torch.float32:
+        raise TypeError("idx must be int32 and gate float32")
+    _check(load().tp_moe_shard_fwd(_ptr(x), _ptr(idx), _ptr(gate), _ptr(w1), _ptr(w_up), _ptr(w2), _ptr(y_i),
+                                   _ptr(ws), ws.numel() if ws is not None else 0, T, d, ff_i, E, k, _dt(y_i),
+                                   _stream()))
     return y_i
 
 

@@ -262,6 +262,34 @@ tp_status linear_fp8(const char* who, const void* x, const void* wq, const float
   return hip_status(tpk::gemm_bf16(p, W.plan, kind, out_f32, s), who);
 }
 
+struct MoeLayout {
+  int64_t rows = 0, n_tiles = 0;
+  size_t counts = 0, offsets = 0, cursors = 0, tiles = 0, src = 0, pos = 0, xs = 0, hs = 0, zs = 0, total = 0;
+};
+MoeLayout moe_layout(int64_t T, int64_t d, int64_t ff_i, int E, int k) {
+  MoeLayout L;
+  const int64_t tile = tpk::MOE_TILE;
+  L.rows = ((T * k + tile - 1) / tile + E) * tile;  // every expert's group padded to whole tiles
+  L.n_tiles = L.rows / tile;
+  size_t o = CNT_RESERVE;                           // (the shared counter region stays untouched)
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += tpk::align_up(bytes, 256);
+    return at;
+  };
+  L.counts = take((size_t)E * 4);
+  L.offsets = take((size_t)(E + 1) * 4);
+  L.cursors = take((size_t)E * 4);
+  L.tiles = take((size_t)L.n_tiles * 4);
+  L.src = take((size_t)L.rows * 4);
+  L.pos = take((size_t)T * k * 4);
+  L.xs = take((size_t)L.rows * d * 2);
+  L.hs = take((size_t)L.rows * ff_i * 2);
+  L.zs = take((size_t)L.rows * d * 4);
+  L.total = o;
+  return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -530,6 +558,99 @@ tp_status tp_mlp_shard_fwd_fp8(const void* x, const void* wq1_i, const float* s1
   if (e != hipSuccess) return hip_status(e, "tp_mlp_shard_fwd_fp8 (column GEMM)");
   e = tpk::gemm_bf16(p2, L.p2, tpk::GK_FWD_STORE, out_dtype == TP_F32, s);
   return hip_status(e, "tp_mlp_shard_fwd_fp8 (row GEMM)");
+}
+
+// ---- mixture of experts (experts sharded in place) --------------------------------
+
+tp_status tp_moe_route(const float* logits, int64_t T, int E, int k, int32_t* idx, float* gate, tp_stream stream) {
+  if (!dim_ok(T) || E < 1 || E > tpk::MOE_MAX_E || k < 1 || k > tpk::MOE_MAX_K || k > E || !prod_ok(T, E))
+    return fail(TP_ERR_SHAPE, "tp_moe_route: need 1 <= k <= min(E, %d), 1 <= E <= %d", tpk::MOE_MAX_K, tpk::MOE_MAX_E);
+  if (T == 0) return TP_OK;
+  if (!logits || !idx || !gate) return fail(TP_ERR_NULL, "tp_moe_route: null pointer");
+  return hip_status(tpk::moe_route(logits, (int)T, E, k, idx, gate, reinterpret_cast<hipStream_t>(stream)),
+                    "tp_moe_route");
+}
+
+size_t tp_moe_shard_fwd_workspace(int64_t T, int64_t d, int64_t ff_i, int E, int k) {
+  if (!dim_ok(T) || !dim_ok(d) || !dim_ok(ff_i) || E < 1 || E > tpk::MOE_MAX_E || k < 1 || k > tpk::MOE_MAX_K ||
+      T == 0)
+    return 0;
+  return moe_layout(T, d, ff_i, E, k).total;
+}
+
+tp_status tp_moe_shard_fwd(const void* x, const int32_t* idx, const float* gate, const void* w1, const void* w_up,
+                           const void* w2, void* y_i, void* ws, size_t ws_bytes, int64_t T, int64_t d, int64_t ff_i,
+                           int E, int k, tp_dtype out_dtype, tp_stream stream) {
+  if (!valid_dtype(out_dtype)) return fail(TP_ERR_DTYPE, "tp_moe_shard_fwd: unknown out_dtype");
+  if (!dim_ok(T) || !dim_ok(d) || !dim_ok(ff_i) || E < 1 || E > tpk::MOE_MAX_E || k < 1 || k > tpk::MOE_MAX_K ||
+      k > E || !prod_ok(T * k, d) || !prod_ok((int64_t)E * d, ff_i))
+    return fail(TP_ERR_SHAPE, "tp_moe_shard_fwd: sizes out of range");
+  if (T == 0 || d == 0) return TP_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (ff_i == 0)
+    return hip_status(tpk::zero_fill(y_i, (size_t)T * d * esize(out_dtype), s), "tp_moe_shard_fwd (ff_i=0)");
+  if (!x || !idx || !gate || !w1 || !w_up || !w2 || !y_i) return fail(TP_ERR_NULL, "tp_moe_shard_fwd: null pointer");
+  if (d % 8 || ff_i % 8 || !aligned16(x) || !aligned16(w1) || !aligned16(w_up) || !aligned16(w2))
+    return fail(TP_ERR_UNSUPPORTED, "tp_moe_shard_fwd: needs d, ff_i multiples of 8 and 16-byte aligned x, weights");
+  const MoeLayout L = moe_layout(T, d, ff_i, E, k);
+  if (L.rows > kMaxDim / 8) return fail(TP_ERR_SHAPE, "tp_moe_shard_fwd: too many routed rows");
+  if (!ws) return fail(TP_ERR_WORKSPACE, "tp_moe_shard_fwd: workspace required (%zu bytes)", L.total);
+  if (ws_bytes < L.total)
+    return fail(TP_ERR_WORKSPACE, "tp_moe_shard_fwd: workspace of %zu bytes < %zu needed", ws_bytes, L.total);
+  char* base = reinterpret_cast<char*>(ws);
+  int* counts = reinterpret_cast<int*>(base + L.counts);
+  int* tiles = reinterpret_cast<int*>(base + L.tiles);
+  int* pos_of = reinterpret_cast<int*>(base + L.pos);
+  hipError_t e = tpk::moe_group(idx, (int)T, E, k, x, (int)d, (int)L.rows, (int)L.n_tiles, counts,
+                                reinterpret_cast<int*>(base + L.offsets), reinterpret_cast<int*>(base + L.cursors),
+                                tiles, reinterpret_cast<int*>(base + L.src), pos_of, base + L.xs, s);
+  if (e != hipSuccess) return hip_status(e, "tp_moe_shard_fwd (grouping)");
+
+  // grouped gate/up GEMM with the SwiGLU epilogue, 128-row tiles, one expert each
+  GemmPlan plan;
+  plan.kernel = tpk::KERNEL_TILED;
+  plan.tile = tpk::TILE_128x128;
+  plan.splitk = 1;
+  GemmParams p1 = base_params();
+  p1.A0 = base + L.xs;
+  p1.lda = d;
+  p1.B0 = w1;
+  p1.B1 = w_up;
+  p1.ldb = ff_i;
+  p1.K0 = (int)d;
+  p1.M = (int)L.rows;
+  p1.N = (int)ff_i;
+  p1.C = base + L.hs;
+  p1.ldc = ff_i;
+  p1.act = TP_ACT_SWIGLU;
+  p1.vecA = p1.vecB = 1;
+  p1.tile_expert = tiles;
+  p1.b_expert_stride = d * ff_i;
+  if (!tpk::gemm_tile_supported(p1, plan, tpk::GK_FWD_SWIGLU))
+    return fail(TP_ERR_UNSUPPORTED, "tp_moe_shard_fwd: no grouped kernel for these operands");
+  e = tpk::gemm_tile(p1, plan, tpk::GK_FWD_SWIGLU, false, s);
+  if (e != hipSuccess) return hip_status(e, "tp_moe_shard_fwd (gate/up GEMM)");
+  // grouped down GEMM to fp32 rows
+  GemmParams p2 = base_params();
+  p2.A0 = base + L.hs;
+  p2.lda = ff_i;
+  p2.B0 = w2;
+  p2.ldb = d;
+  p2.K0 = (int)ff_i;
+  p2.M = (int)L.rows;
+  p2.N = (int)d;
+  p2.C = base + L.zs;
+  p2.ldc = d;
+  p2.vecA = p2.vecB = 1;
+  p2.tile_expert = tiles;
+  p2.b_expert_stride = ff_i * d;
+  if (!tpk::gemm_tile_supported(p2, plan, tpk::GK_FWD_STORE))
+    return fail(TP_ERR_UNSUPPORTED, "tp_moe_shard_fwd: no grouped kernel for these operands");
+  e = tpk::gemm_tile(p2, plan, tpk::GK_FWD_STORE, true, s);
+  if (e != hipSuccess) return hip_status(e, "tp_moe_shard_fwd (down GEMM)");
+  return hip_status(tpk::moe_combine(reinterpret_cast<const float*>(base + L.zs), pos_of, gate, (int)T, k, (int)d, y_i,
+                                     out_dtype == TP_F32, s),
+                    "tp_moe_shard_fwd (combine)");
 }
 
 tp_status tp_fp8_pack_strips(const void* src, void* dst, int64_t K, int64_t N, tp_stream stream) {

@@ -266,6 +266,17 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(const GemmPar
   const int nk0 = (p.K0 + TBK - 1) / TBK;
   const int nk = nk0 + (p.K1 + TBK - 1) / TBK;
 
+  // grouped mode: this M tile's expert selects the weights (a tile with no
+  // routed rows has nothing to do; the whole workgroup leaves together)
+  const uint16_t* gB0 = reinterpret_cast<const uint16_t*>(p.B0);
+  const uint16_t* gB1 = reinterpret_cast<const uint16_t*>(p.B1);
+  if (p.tile_expert) {
+    const int ex = p.tile_expert[m0 / BM];
+    if (ex < 0) return;
+    gB0 += ex * p.b_expert_stride;
+    if (gB1) gB1 += ex * p.b_expert_stride;
+  }
+
   TA ta;
   TB tb;
   ta.setup(tid, m0, p.M, p.lda);
@@ -279,8 +290,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(const GemmPar
     const int k0 = (s1 ? kt - nk0 : kt) * TBK;
     const int kvalid = kt >= nk ? 0 : (s1 ? p.K1 : p.K0) - k0;
     const uint16_t* a = reinterpret_cast<const uint16_t*>(s1 ? p.A1 : p.A0);
-    const uint16_t* b0 = reinterpret_cast<const uint16_t*>(s1 ? p.B1 : p.B0);
-    const uint16_t* b1 = reinterpret_cast<const uint16_t*>(p.B1);
+    const uint16_t* b0 = s1 ? gB1 : gB0;
+    const uint16_t* b1 = gB1;
     const int64_t ao = kvalid <= 0 ? 0 : (AKC ? (int64_t)m0 * p.lda + k0 : (int64_t)k0 * p.lda + m0);
     const int64_t bo = kvalid <= 0 ? 0 : (BKC ? (int64_t)n0 * p.ldb + k0 : (int64_t)k0 * p.ldb + n0);
     ta.issue(a + ao, a + ao, kvalid, st, wave);

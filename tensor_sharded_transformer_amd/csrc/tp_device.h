@@ -87,6 +87,8 @@ struct GemmParams {
   int b_fp8;           // decode kernel: B0/B1 hold fp8 (OCP e4m3) codes, ldb in elements (= bytes) ...
   const float* bscale0;  //   ... with per-column scales applied to the sums (B0)
   const float* bscale1;  //   (B1)
+  const int* tile_expert;   // tiled kernel, grouped mode: expert of each BM-row tile (-1: no rows) ...
+  int64_t b_expert_stride;  //   ... whose B0/B1 start this many elements further per expert index
 };
 
 // Calls f(integral_constant<int, I>) for I = 0 .. N-1, so array indices in

@@ -159,6 +159,17 @@ hipError_t zero_fill(void* ws, size_t bytes, hipStream_t s);
 // fp8 codes (K, N) row-major -> 64-column strip-major (N % 64 == 0, both 16-byte aligned).
 hipError_t pack_fp8_strips(const void* src, void* dst, int64_t K, int64_t N, hipStream_t s);
 
+// Mixture of experts (experts sharded in place): routing, grouping of the
+// routed rows into 128-row tiles per expert, weighted combine.
+constexpr int MOE_MAX_E = 1024;
+constexpr int MOE_MAX_K = 16;
+constexpr int MOE_TILE = 128;
+hipError_t moe_route(const float* logits, int T, int E, int k, int* idx, float* gate, hipStream_t s);
+hipError_t moe_group(const int* idx, int T, int E, int k, const void* x, int d, int rows, int n_tiles, int* counts,
+                     int* offsets, int* cursors, int* tile_expert, int* src_row, int* pos_of, void* xs, hipStream_t s);
+hipError_t moe_combine(const float* zs, const int* pos_of, const float* gate, int T, int k, int d, void* y,
+                       bool out_f32, hipStream_t s);
+
 // Local grouped-query attention over a rank's heads: qkv (T, (n_q + 2 n_kv)
 // * 128) bf16 rows [Q | K | V], out (T, n_q * 128) bf16; both 16-byte
 // aligned.  head_dim is fixed at attention_head_dim().

@@ -233,6 +233,25 @@ def test_linear_fp8_validation(lib):
     assert pk(None, None, 0, 128, None) == OK
 
 
+def test_moe_validation(lib):
+    r = lib.tp_moe_route
+    assert r(FAKE, 8, 4, 5, FAKE, FAKE, None) == SHAPE        # k > E
+    assert r(FAKE, 8, 2000, 2, FAKE, FAKE, None) == SHAPE     # E > 1024
+    assert r(FAKE, 8, 16, 17, FAKE, FAKE, None) == SHAPE      # k > 16
+    assert r(None, 8, 16, 2, FAKE, FAKE, None) == NULL
+    assert r(None, 0, 16, 2, None, None, None) == OK
+    f = lib.tp_moe_shard_fwd
+    ws = lib.tp_moe_shard_fwd_workspace(64, 256, 96, 16, 4)
+    assert ws > 0
+    a = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert f(*a, FAKE, ctypes.c_size_t(ws), 64, 256, 96, 16, 4, 7, None) == DTYPE
+    assert f(*a, FAKE, ctypes.c_size_t(ws), 64, 256, 96, 16, 17, 0, None) == SHAPE
+    assert f(*a, FAKE, ctypes.c_size_t(ws), 64, 260, 96, 16, 4, 0, None) == 6       # d % 8
+    assert f(*a, None, 0, 64, 256, 96, 16, 4, 0, None) == WS
+    assert f(*a, FAKE, ctypes.c_size_t(ws - 1), 64, 256, 96, 16, 4, 0, None) == WS
+    assert f(None, None, None, None, None, None, None, None, 0, 0, 256, 96, 16, 4, 0, None) == OK
+
+
 def test_status_strings(lib):
     for s in range(8):
         assert lib.tp_status_string(s)

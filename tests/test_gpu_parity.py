@@ -878,3 +878,48 @@ def test_block_rows_graph_replay():
             assert torch.equal(a, b), f"replay {r}"
         run()   # eager calls on the same buffers and workspace between replays
         torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# Mixture of experts, experts sharded in place.
+# ---------------------------------------------------------------------------
+def moe_run(t, k, out_dt=torch.bfloat16):
+    T, d = t["x"].shape
+    E, _, ff_i = t["w1"].shape
+    idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    gate = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    tp.tp_moe_route(cuda(t["logits"]), k, idx, gate)
+    y = torch.full((T, d), 7.0, dtype=out_dt, device="cuda")
+    ws = tp.new_workspace(tp.tp_moe_shard_fwd_workspace(T, d, ff_i, E, k))
+    tp.tp_moe_shard_fwd(cuda(t["x"]), idx, gate, cuda(t["w1"]), cuda(t["w_up"]), cuda(t["w2"]), y, ws)
+    return idx, gate, y
+
+
+@pytest.mark.parametrize("T,d,ff_i,E,k", [(1, 64, 32, 4, 2), (77, 256, 96, 16, 4), (300, 512, 200, 8, 8),
+                                         (513, 128, 64, 64, 1)])
+def test_moe_small(T, d, ff_i, E, k):
+    wl = W.MoeWorkload("moe_small", T=T, d=d, ff=ff_i, E=E, k=k, p=1, seed=40 + T)
+    t = W.moe_rank_inputs(wl)
+    idx, gate, y = moe_run(t, k)
+    ridx, rgate = O.moe_route(t["logits"], k)
+    assert torch.equal(idx.cpu().long(), torch.from_numpy(ridx)), "routing decisions"
+    np.testing.assert_allclose(gate.cpu().numpy(), rgate, rtol=1e-5, atol=1e-6)
+    ref = O.moe_shard_fwd(t["x"], ridx, rgate, t["w1"], t["w_up"], t["w2"])
+    assert_close(y, ref, BF16_TOL, "moe block")
+    _, _, y2 = moe_run(t, k, torch.float32)
+    assert_close(y2, ref, BF16_TOL, "moe block, fp32 out")
+
+
+def test_moe_qwen3_class_rank_T4096():
+    """A Qwen3-MoE-class layer's rank share (128 experts, top-8, d=2048,
+    ff_i=96) at T=4096 on 64 sampled tokens, and run-to-run bitwise equal."""
+    wl = W.MOE_PREFILL
+    t = W.moe_rank_inputs(wl)
+    idx, gate, y = moe_run(t, wl.k)
+    rows = W.row_subset(wl.T, 64, wl.seed)
+    ridx, rgate = O.moe_route(t["logits"][rows], wl.k)
+    assert torch.equal(idx[rows].cpu().long(), torch.from_numpy(ridx))
+    ref = O.moe_shard_fwd(t["x"][rows], ridx, rgate, t["w1"], t["w_up"], t["w2"])
+    assert_close(y[rows], ref, BF16_TOL, "moe rank rows")
+    _, _, y_again = moe_run(t, wl.k)
+    assert torch.equal(y, y_again)

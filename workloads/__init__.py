@@ -193,6 +193,42 @@ def column_scales(n: int, seed: int, stream: int) -> torch.Tensor:
     return (0.5 + u) * (WEIGHT_STD / 64.0)
 
 
+@dataclasses.dataclass(frozen=True)
+class MoeWorkload:
+    """One rank's slice of an MoE block with experts sharded in place."""
+    name: str
+    T: int
+    d: int
+    ff: int        # one expert's intermediate size (unsharded)
+    E: int
+    k: int
+    p: int
+    seed: int
+
+    @property
+    def ff_i(self) -> int:
+        return self.ff // self.p
+
+
+# A Qwen3-MoE-class layer (hidden 2048, 128 routed experts, top-8, expert
+# intermediate 768) on p = 8 ranks, at prefill length.
+MOE_PREFILL = MoeWorkload("moe_qwen3_class_T4096", T=4096, d=2048, ff=768, E=128, k=8, p=8, seed=8)
+S_ROUTER, S_MW1, S_MWUP, S_MW2 = 30, 31, 32, 33
+
+
+def moe_rank_inputs(w: MoeWorkload, T: Optional[int] = None) -> Dict[str, torch.Tensor]:
+    """x (T, d), router logits (T, E) fp32 drawn directly (N(0, 1): the spread of
+    a router projection), and rank weights w1, w_up (E, d, ff_i), w2 (E, ff_i, d)."""
+    T = w.T if T is None else T
+    return {
+        "x": normal((T, w.d), 1.0, w.seed, S_X),
+        "logits": normal((T, w.E), 1.0, w.seed, S_ROUTER, "f32"),
+        "w1": normal((w.E, w.d, w.ff_i), WEIGHT_STD, w.seed, S_MW1),
+        "w_up": normal((w.E, w.d, w.ff_i), WEIGHT_STD, w.seed, S_MWUP),
+        "w2": normal((w.E, w.ff_i, w.d), WEIGHT_STD, w.seed, S_MW2),
+    }
+
+
 def row_subset(T: int, n: int, seed: int) -> List[int]:
     """Seeded, sorted subset of ``n`` distinct rows out of ``T`` (all rows if T <= n)."""
     if T <= n:
