@@ -165,7 +165,7 @@ def main() -> int:
     log(f"bench: gate/up GEMM {k_ms * 1e3:.1f} us -> {k_gbs:.0f} GB/s")
 
     rows = {}
-    want = set(["prefill", "gqa", "attn", "bwd", "fp8", "sum"]) if args.rows == "all" else (
+    want = set(["prefill", "gqa", "attn", "bwd", "fp8", "moe", "sum"]) if args.rows == "all" else (
         set() if args.rows == "none" else set(args.rows.split(",")))
     steps_r = max(10, args.steps // 2)
 
@@ -176,6 +176,31 @@ def main() -> int:
         rows["calib_copy_117440512B"] = {"us": round(t_ * 1e3, 2),
                                          "GB/s_rd+wr": round(2 * src.numel() * 2 / t_ / 1e6, 1)}
         del src, dst
+
+    if "moe" in want:
+        # one rank's share of a Qwen3-MoE-class layer (128 experts, top-8, hidden
+        # 2048, expert intermediate 768 / 8 ranks) at T=4096: routing, grouping,
+        # the two grouped GEMMs and the combine
+        wm = W.MOE_PREFILL
+        gm = torch.Generator(device=dev)
+        gm.manual_seed(51)
+        rn = lambda *shp, sd=1.0, dt=torch.bfloat16: (torch.randn(*shp, generator=gm, device=dev) * sd).to(dt)
+        xm, lm = rn(wm.T, wm.d), rn(wm.T, wm.E, dt=torch.float32)
+        w1m, wum, w2m = rn(wm.E, wm.d, wm.ff_i, sd=0.02), rn(wm.E, wm.d, wm.ff_i, sd=0.02), rn(wm.E, wm.ff_i, wm.d, sd=0.02)
+        idxm = torch.empty(wm.T, wm.k, dtype=torch.int32, device=dev)
+        gatem = torch.empty(wm.T, wm.k, dtype=torch.float32, device=dev)
+        ym = torch.empty(wm.T, wm.d, dtype=torch.bfloat16, device=dev)
+        wsm = tp.new_workspace(tp.tp_moe_shard_fwd_workspace(wm.T, wm.d, wm.ff_i, wm.E, wm.k), dev)
+
+        def moe_step(i):
+            tp.tp_moe_route(lm, wm.k, idxm, gatem)
+            tp.tp_moe_shard_fwd(xm, idxm, gatem, w1m, wum, w2m, ym, wsm)
+
+        t_ = time_gpu(moe_step, steps_r, 3)
+        fl = wm.T * wm.k * 6 * wm.d * wm.ff_i
+        rows["moe_qwen3_class_rank_T4096"] = {"us": round(t_ * 1e3, 1), "TFLOP/s": round(fl / t_ / 1e9, 1),
+                                              "frac_mfma": round(fl / t_ / 1e9 / BF16_PEAK_TFLOPS, 4)}
+        del xm, lm, w1m, wum, w2m, idxm, gatem, ym, wsm
 
     if "fp8" in want:
         # the decode shard step with fp8 (E4M3) weights and per-column scales:

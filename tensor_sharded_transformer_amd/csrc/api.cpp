@@ -264,6 +264,7 @@ tp_status linear_fp8(const char* who, const void* x, const void* wq, const float
 
 struct MoeLayout {
   int64_t rows = 0, n_tiles = 0;
+  bool gather = false;  // x too large for the GEMM's 32-bit row offsets: copy the routed rows first
   size_t counts = 0, offsets = 0, cursors = 0, tiles = 0, src = 0, pos = 0, xs = 0, hs = 0, zs = 0, total = 0;
 };
 MoeLayout moe_layout(int64_t T, int64_t d, int64_t ff_i, int E, int k) {
@@ -283,7 +284,8 @@ MoeLayout moe_layout(int64_t T, int64_t d, int64_t ff_i, int E, int k) {
   L.tiles = take((size_t)L.n_tiles * 4);
   L.src = take((size_t)L.rows * 4);
   L.pos = take((size_t)T * k * 4);
-  L.xs = take((size_t)L.rows * d * 2);
+  L.gather = T * d * 2 > INT32_MAX - 64;
+  L.xs = take(L.gather ? (size_t)L.rows * d * 2 : 0);
   L.hs = take((size_t)L.rows * ff_i * 2);
   L.zs = take((size_t)L.rows * d * 4);
   L.total = o;
@@ -601,18 +603,21 @@ tp_status tp_moe_shard_fwd(const void* x, const int32_t* idx, const float* gate,
   int* counts = reinterpret_cast<int*>(base + L.counts);
   int* tiles = reinterpret_cast<int*>(base + L.tiles);
   int* pos_of = reinterpret_cast<int*>(base + L.pos);
+  int* src = reinterpret_cast<int*>(base + L.src);
   hipError_t e = tpk::moe_group(idx, (int)T, E, k, x, (int)d, (int)L.rows, (int)L.n_tiles, counts,
                                 reinterpret_cast<int*>(base + L.offsets), reinterpret_cast<int*>(base + L.cursors),
-                                tiles, reinterpret_cast<int*>(base + L.src), pos_of, base + L.xs, s);
+                                tiles, src, pos_of, L.gather ? base + L.xs : nullptr, s);
   if (e != hipSuccess) return hip_status(e, "tp_moe_shard_fwd (grouping)");
 
-  // grouped gate/up GEMM with the SwiGLU epilogue, 128-row tiles, one expert each
+  // grouped gate/up GEMM with the SwiGLU epilogue, 128-row tiles, one expert
+  // each, reading the routed rows of x through the row table
   GemmPlan plan;
   plan.kernel = tpk::KERNEL_TILED;
   plan.tile = tpk::TILE_128x128;
   plan.splitk = 1;
   GemmParams p1 = base_params();
-  p1.A0 = base + L.xs;
+  p1.A0 = L.gather ? base + L.xs : x;
+  p1.a_rows = L.gather ? nullptr : src;
   p1.lda = d;
   p1.B0 = w1;
   p1.B1 = w_up;

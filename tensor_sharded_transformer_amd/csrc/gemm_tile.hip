@@ -136,6 +136,21 @@ struct OpTile {
     }
   }
 
+  // k-contiguous rows named by a table: row r of the tile reads source row
+  // rows[r0 + r] (offsets from the source's row 0; -1 masks the row).
+  __device__ __forceinline__ void setup_rows(int tid, int r0, int extent, int64_t ld, const int* rows) {
+    static_assert(KC && !DUAL, "row tables index k-contiguous single operands");
+#pragma unroll
+    for (int c = 0; c < NL; ++c) {
+      const int slot = c * NT + tid;
+      const int row = slot / KC_CHUNKS;
+      const int chunk = (slot % KC_CHUNKS) ^ kc_swz(row);
+      const int src = r0 + row < extent ? rows[r0 + row] : -1;
+      voff[c] = (uint32_t)(max(src, 0) * ld * 2 + chunk * 16);
+      kidx[c] = src >= 0 ? chunk * 8 : INT_MAX;
+    }
+  }
+
   // Issue one k-tile's loads straight into LDS.  base0/base1: the sources
   // at (tile origin, k-tile start); kvalid: k-values of the k-tile inside the
   // matrix (<= 0: every load masked); lds: this operand's tile in the stage.
@@ -279,7 +294,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(const GemmPar
 
   TA ta;
   TB tb;
-  ta.setup(tid, m0, p.M, p.lda);
+  if constexpr (AKC) {
+    if (p.a_rows) ta.setup_rows(tid, m0, p.M, p.lda, p.a_rows);
+    else ta.setup(tid, m0, p.M, p.lda);
+  } else {
+    ta.setup(tid, m0, p.M, p.lda);
+  }
   tb.setup(tid, n0, p.N, p.ldb);
 
   // Issue the LDS-bound loads of k-tile kt into stage array st.  Tiles past
@@ -292,7 +312,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(const GemmPar
     const uint16_t* a = reinterpret_cast<const uint16_t*>(s1 ? p.A1 : p.A0);
     const uint16_t* b0 = s1 ? gB1 : gB0;
     const uint16_t* b1 = gB1;
-    const int64_t ao = kvalid <= 0 ? 0 : (AKC ? (int64_t)m0 * p.lda + k0 : (int64_t)k0 * p.lda + m0);
+    const int64_t ao =
+        kvalid <= 0 ? 0 : (AKC ? (p.a_rows ? 0 : (int64_t)m0 * p.lda) + k0 : (int64_t)k0 * p.lda + m0);
     const int64_t bo = kvalid <= 0 ? 0 : (BKC ? (int64_t)n0 * p.ldb + k0 : (int64_t)k0 * p.ldb + n0);
     ta.issue(a + ao, a + ao, kvalid, st, wave);
     tb.issue(b0 + bo, b1 + bo, kvalid, st + TA::BYTES, wave);
@@ -486,6 +507,7 @@ bool gemm_tile_supported(const GemmParams& p, const GemmPlan& plan, GemmKind kin
   const bool akc = !(kind == GK_BWD_DW || kind == GK_BWD_DW_DUAL);
   const bool bkc = kind == GK_BWD_DH_SWIGLU || kind == GK_BWD_DH_ACT || kind == GK_BWD_DX;
   if (!akc && p.M % 8) return false;
+  if (p.a_rows && (!akc || p.A1 || p.K1)) return false;
   if (!bkc && p.N % 8) return false;
   return true;
 }

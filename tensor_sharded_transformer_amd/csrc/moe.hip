@@ -11,58 +11,82 @@
 //   y_i[t] = sum_j gate[t, j] * swiglu_shard(x[t]; expert idx[t, j]).
 //
 // Design:
-//  * Routing: one thread per token, k passes of an arg-max over the fp32
+//  * Routing: one wave per token, k passes of a wave arg-max over the fp32
 //    logits (k <= 16, E <= 1024), exponentials relative to the largest.
-//  * Grouping, without a host round trip: per-expert counts (atomics), one
+//  * Grouping, without a host round trip: per-expert counts (per-workgroup
+//    LDS histograms, one global atomic per workgroup and expert), one
 //    workgroup turns them into offsets with every expert's group padded to a
 //    whole 128-row tile and writes the tile -> expert table, then each routed
 //    (token, slot) takes a row in its expert's group.  Row order inside a
 //    group does not affect any value (every output row is its own dot
 //    products), so the atomics leave results bitwise reproducible.
-//  * The routed rows of x are gathered into the grouped order (padding rows
-//    zero), the grouped tiled GEMMs read each tile's expert weights from the
-//    table (gate/up with the SwiGLU epilogue, then down to fp32), and the
-//    combine adds each token's k rows in slot order with their gates.
+//  * The grouped tiled GEMMs read each tile's expert weights from the tile
+//    table (gate/up with the SwiGLU epilogue, then down to fp32 rows); the
+//    gate/up GEMM reads the routed rows of x through the row table (padding
+//    rows load as zeros; an x of 2 GiB or more is first gathered into the
+//    grouped order).  The combine adds each token's k rows in slot order
+//    with their gates.
 #include "tp_kernels.h"
 #include "tp_device.h"
 
 namespace tpk {
 namespace {
 
+// One wave per token: lane l holds logits l, l + 64, ... (a NaN logit ranks
+// as -inf); each of the k passes takes the wave's arg-max (larger value, then
+// lower index) and removes it.
 __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                         int* __restrict__ idx, float* __restrict__ gate) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
+  constexpr int PER = MOE_MAX_E / 64;
+  constexpr int NONE = 0x7fffffff;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float* lg = logits + (int64_t)t * E;
-  uint32_t taken[MOE_MAX_E / 32];
+  float v[PER];
+  uint32_t live = 0;  // bit q: value q of this lane is still a candidate
 #pragma unroll
-  for (int w = 0; w < MOE_MAX_E / 32; ++w) taken[w] = 0u;
-  int sel[MOE_MAX_K];
-  float val[MOE_MAX_K];
+  for (int q = 0; q < PER; ++q) {
+    const int e = lane + 64 * q;
+    const float x = e < E ? lg[e] : -INFINITY;
+    v[q] = x != x ? -INFINITY : x;
+    if (e < E) live |= 1u << q;
+  }
+  float my_val = -INFINITY;  // lane j keeps pass j's pick
+  int my_sel = 0;
   for (int j = 0; j < k; ++j) {
-    int best = -1;
-    float bv = 0.0f;
-    for (int e = 0; e < E; ++e) {
-      if (taken[e >> 5] >> (e & 31) & 1u) continue;
-      const float v = lg[e];
-      if (best < 0 || v > bv) {  // strict: equal logits keep the lower index
-        best = e;
-        bv = v;
+    float bv = -INFINITY;
+    int be = NONE;
+#pragma unroll
+    for (int q = 0; q < PER; ++q)  // indices rise with q: strict > keeps the lower on ties
+      if ((live >> q & 1u) && (be == NONE || v[q] > bv)) {
+        bv = v[q];
+        be = lane + 64 * q;
+      }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oe = __shfl_xor(be, off);
+      if (ov > bv || (ov == bv && oe < be)) {
+        bv = ov;
+        be = oe;
       }
     }
-    taken[best >> 5] |= 1u << (best & 31);
-    sel[j] = best;
-    val[j] = bv;
+    if (lane == j) {
+      my_val = bv;
+      my_sel = be;
+    }
+    if ((be & 63) == lane) live &= ~(1u << (be >> 6));
   }
-  float w[MOE_MAX_K];
-  float sum = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    w[j] = expf(val[j] - val[0]);
-    sum += w[j];
-  }
-  for (int j = 0; j < k; ++j) {
-    idx[(int64_t)t * k + j] = sel[j];
-    gate[(int64_t)t * k + j] = w[j] / sum;
+  // gates: exponentials relative to the largest pick, normalised over the k
+  const float top = __shfl(my_val, 0);
+  const float w = lane < k ? expf(my_val - top) : 0.0f;
+  float sum = w;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+  if (lane < k) {
+    idx[(int64_t)t * k + lane] = my_sel;
+    gate[(int64_t)t * k + lane] = w / sum;
   }
 }
 
@@ -70,10 +94,16 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict_
 // slot contributes nothing)
 __global__ __launch_bounds__(256) void moe_count_kernel(const int* __restrict__ idx, int n, int E,
                                                         int* __restrict__ counts) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  const int e = idx[i];
-  if (e >= 0 && e < E) atomicAdd(&counts[e], 1);
+  __shared__ int h[MOE_MAX_E];
+  for (int e = threadIdx.x; e < E; e += 256) h[e] = 0;
+  __syncthreads();
+  for (int i = blockIdx.x * 256 * 8 + threadIdx.x; i < min(n, (blockIdx.x + 1) * 256 * 8); i += 256) {
+    const int e = idx[i];
+    if (e >= 0 && e < E) atomicAdd(&h[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256)
+    if (h[e]) atomicAdd(&counts[e], h[e]);
 }
 
 // One workgroup: padded group offsets, tile -> expert table, cleared cursors
@@ -110,19 +140,37 @@ __global__ __launch_bounds__(1024) void moe_plan_kernel(const int* __restrict__ 
   for (int r = threadIdx.x; r < rows; r += blockDim.x) src_row[r] = -1;
 }
 
+// Each workgroup (2048 entries) counts its entries per expert in LDS,
+// reserves one block per expert with a single global atomic, then hands out
+// rows inside the block with LDS atomics.
 __global__ __launch_bounds__(256) void moe_scatter_kernel(const int* __restrict__ idx, int n, int k, int E,
                                                           const int* __restrict__ offsets, int* __restrict__ cursors,
                                                           int* __restrict__ src_row, int* __restrict__ pos_of) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  const int e = idx[i];
-  if (e < 0 || e >= E) {
-    pos_of[i] = -1;
-    return;
+  __shared__ int h[MOE_MAX_E];
+  __shared__ int base[MOE_MAX_E];
+  for (int e = threadIdx.x; e < E; e += 256) h[e] = 0;
+  __syncthreads();
+  const int lo = blockIdx.x * 256 * 8, hi = min(n, lo + 256 * 8);
+  for (int i = lo + threadIdx.x; i < hi; i += 256) {
+    const int e = idx[i];
+    if (e >= 0 && e < E) atomicAdd(&h[e], 1);
   }
-  const int pos = offsets[e] + atomicAdd(&cursors[e], 1);
-  src_row[pos] = i / k;
-  pos_of[i] = pos;
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 256) {
+    base[e] = h[e] ? offsets[e] + atomicAdd(&cursors[e], h[e]) : 0;
+    h[e] = 0;
+  }
+  __syncthreads();
+  for (int i = lo + threadIdx.x; i < hi; i += 256) {
+    const int e = idx[i];
+    if (e < 0 || e >= E) {
+      pos_of[i] = -1;
+      continue;
+    }
+    const int pos = base[e] + atomicAdd(&h[e], 1);
+    src_row[pos] = i / k;
+    pos_of[i] = pos;
+  }
 }
 
 // xs[r] = x[src_row[r]] (zero for padding rows); d % 8 == 0, 16-byte rows.
@@ -135,21 +183,35 @@ __global__ __launch_bounds__(256) void moe_gather_kernel(const uint4* __restrict
   xs[i] = s >= 0 ? x[(int64_t)s * d8 + c] : make_uint4(0u, 0u, 0u, 0u);
 }
 
-// y[t, c] = sum_j gate[t, j] * zs[pos_of[t, j], c] in slot order (fp32).
+// y[t, c] = sum_j gate[t, j] * zs[pos_of[t, j], c] in slot order (fp32);
+// four columns per thread (d % 8 == 0).
 template <typename OutT>
 __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ zs, const int* __restrict__ pos_of,
                                                           const float* __restrict__ gate, int T, int k, int d,
                                                           OutT* __restrict__ y) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= (int64_t)T * d) return;
-  const int t = (int)(i / d), c = (int)(i % d);
-  float s = 0.0f;
+  const int d4 = d / 4;
+  if (i >= (int64_t)T * d4) return;
+  const int t = (int)(i / d4), c = (int)(i % d4) * 4;
+  float4 s = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   for (int j = 0; j < k; ++j) {
     const int pos = pos_of[(int64_t)t * k + j];
-    if (pos >= 0) s += gate[(int64_t)t * k + j] * zs[(int64_t)pos * d + c];
+    if (pos < 0) continue;
+    const float g = gate[(int64_t)t * k + j];
+    const float4 z = *reinterpret_cast<const float4*>(zs + (int64_t)pos * d + c);
+    s.x += g * z.x;
+    s.y += g * z.y;
+    s.z += g * z.z;
+    s.w += g * z.w;
   }
-  if constexpr (std::is_same<OutT, float>::value) y[i] = s;
-  else y[i] = f2bf(s);
+  if constexpr (std::is_same<OutT, float>::value) {
+    *reinterpret_cast<float4*>(y + (int64_t)t * d + c) = s;
+  } else {
+    uint2 o;
+    o.x = (uint32_t)f2bf(s.x) | ((uint32_t)f2bf(s.y) << 16);
+    o.y = (uint32_t)f2bf(s.z) | ((uint32_t)f2bf(s.w) << 16);
+    *reinterpret_cast<uint2*>(y + (int64_t)t * d + c) = o;
+  }
 }
 
 unsigned blocks(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
@@ -158,7 +220,7 @@ unsigned blocks(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
 
 hipError_t moe_route(const float* logits, int T, int E, int k, int* idx, float* gate, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(moe_route_kernel, dim3(blocks(T, 256)), dim3(256), 0, s, logits, T, E, k, idx, gate);
+  hipLaunchKernelGGL(moe_route_kernel, dim3(blocks(T, 4)), dim3(256), 0, s, logits, T, E, k, idx, gate);
   return hipGetLastError();
 }
 
@@ -167,11 +229,12 @@ hipError_t moe_group(const int* idx, int T, int E, int k, const void* x, int d, 
   const int n = T * k;
   hipError_t e = zero_fill(counts, (size_t)E * sizeof(int), s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(moe_count_kernel, dim3(blocks(n, 256)), dim3(256), 0, s, idx, n, E, counts);
+  hipLaunchKernelGGL(moe_count_kernel, dim3(blocks(n, 256 * 8)), dim3(256), 0, s, idx, n, E, counts);
   hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(1024), 0, s, counts, E, offsets, cursors, tile_expert, n_tiles,
                      src_row, rows);
-  hipLaunchKernelGGL(moe_scatter_kernel, dim3(blocks(n, 256)), dim3(256), 0, s, idx, n, k, E, offsets, cursors,
+  hipLaunchKernelGGL(moe_scatter_kernel, dim3(blocks(n, 256 * 8)), dim3(256), 0, s, idx, n, k, E, offsets, cursors,
                      src_row, pos_of);
+  if (!xs) return hipGetLastError();  // the GEMM reads x through src_row
   const int64_t units = (int64_t)rows * (d / 8);
   hipLaunchKernelGGL(moe_gather_kernel, dim3(blocks(units, 256)), dim3(256), 0, s, reinterpret_cast<const uint4*>(x),
                      src_row, rows, d / 8, reinterpret_cast<uint4*>(xs));
@@ -180,7 +243,7 @@ hipError_t moe_group(const int* idx, int T, int E, int k, const void* x, int d, 
 
 hipError_t moe_combine(const float* zs, const int* pos_of, const float* gate, int T, int k, int d, void* y,
                        bool out_f32, hipStream_t s) {
-  const int64_t n = (int64_t)T * d;
+  const int64_t n = (int64_t)T * (d / 4);
   if (n == 0) return hipSuccess;
   if (out_f32)
     hipLaunchKernelGGL(moe_combine_kernel<float>, dim3(blocks(n, 256)), dim3(256), 0, s, zs, pos_of, gate, T, k, d,

@@ -89,6 +89,8 @@ struct GemmParams {
   const float* bscale1;  //   (B1)
   const int* tile_expert;   // tiled kernel, grouped mode: expert of each BM-row tile (-1: no rows) ...
   int64_t b_expert_stride;  //   ... whose B0/B1 start this many elements further per expert index
+  const int* a_rows;        // tiled kernel, k-contiguous A only: the A row of each output row (-1: a zero
+                            //   row), A0 pointing at row 0; A's bytes must stay below 2^31
 };
 
 // Calls f(integral_constant<int, I>) for I = 0 .. N-1, so array indices in

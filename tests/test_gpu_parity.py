@@ -923,3 +923,32 @@ def test_moe_qwen3_class_rank_T4096():
     assert_close(y[rows], ref, BF16_TOL, "moe rank rows")
     _, _, y_again = moe_run(t, wl.k)
     assert torch.equal(y, y_again)
+
+
+def test_moe_x_of_2gib_takes_the_gathered_path():
+    """x of exactly 2 GiB (65536 x 16384 bf16) is past the GEMM's 32-bit row
+    offsets, so the routed rows are first gathered into the grouped order;
+    checked on 32 sampled tokens."""
+    T, d, ff_i, E, k, seed = 65536, 16384, 8, 2, 1, 61
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    x = torch.empty(T, d, dtype=torch.bfloat16, device="cuda")
+    for i in range(0, T, 4096):
+        x[i:i + 4096] = torch.randn(4096, d, generator=g, device="cuda")
+    logits = W.normal((T, E), 1.0, seed, W.S_ROUTER, "f32")
+    w1 = W.normal((E, d, ff_i), W.WEIGHT_STD, seed, W.S_MW1)
+    w_up = W.normal((E, d, ff_i), W.WEIGHT_STD, seed, W.S_MWUP)
+    w2 = W.normal((E, ff_i, d), W.WEIGHT_STD, seed, W.S_MW2)
+    idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    gate = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    tp.tp_moe_route(cuda(logits), k, idx, gate)
+    y = torch.full((T, d), 7.0, dtype=torch.bfloat16, device="cuda")
+    ws = tp.new_workspace(tp.tp_moe_shard_fwd_workspace(T, d, ff_i, E, k))
+    tp.tp_moe_shard_fwd(x, idx, gate, cuda(w1), cuda(w_up), cuda(w2), y, ws)
+    rows = W.row_subset(T, 32, seed)
+    ridx, rgate = O.moe_route(logits[rows], k)
+    assert torch.equal(idx[rows].cpu().long(), torch.from_numpy(ridx))
+    ref = O.moe_shard_fwd(x[rows].cpu(), ridx, rgate, w1, w_up, w2)
+    assert_close(y[rows], ref, BF16_TOL, "moe rows, gathered x")
+    del ws, x
+    torch.cuda.empty_cache()
