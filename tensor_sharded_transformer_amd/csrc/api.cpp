@@ -265,7 +265,7 @@ tp_status linear_fp8(const char* who, const void* x, const void* wq, const float
 struct MoeLayout {
   int64_t rows = 0, n_tiles = 0;
   bool gather = false;  // x too large for the GEMM's 32-bit row offsets: copy the routed rows first
-  size_t counts = 0, offsets = 0, cursors = 0, tiles = 0, src = 0, pos = 0, xs = 0, hs = 0, zs = 0, total = 0;
+  size_t counts = 0, offsets = 0, cursors = 0, tiles = 0, src = 0, dst = 0, pos = 0, xs = 0, hs = 0, zs = 0, total = 0;
 };
 MoeLayout moe_layout(int64_t T, int64_t d, int64_t ff_i, int E, int k) {
   MoeLayout L;
@@ -283,11 +283,12 @@ MoeLayout moe_layout(int64_t T, int64_t d, int64_t ff_i, int E, int k) {
   L.cursors = take((size_t)E * 4);
   L.tiles = take((size_t)L.n_tiles * 4);
   L.src = take((size_t)L.rows * 4);
+  L.dst = take((size_t)L.rows * 4);
   L.pos = take((size_t)T * k * 4);
   L.gather = T * d * 2 > INT32_MAX - 64;
   L.xs = take(L.gather ? (size_t)L.rows * d * 2 : 0);
   L.hs = take((size_t)L.rows * ff_i * 2);
-  L.zs = take((size_t)L.rows * d * 4);
+  L.zs = take((size_t)T * k * d * 4);  // down-projection rows in (token, slot) order
   L.total = o;
   return L;
 }
@@ -604,9 +605,10 @@ tp_status tp_moe_shard_fwd(const void* x, const int32_t* idx, const float* gate,
   int* tiles = reinterpret_cast<int*>(base + L.tiles);
   int* pos_of = reinterpret_cast<int*>(base + L.pos);
   int* src = reinterpret_cast<int*>(base + L.src);
+  int* dst = reinterpret_cast<int*>(base + L.dst);
   hipError_t e = tpk::moe_group(idx, (int)T, E, k, x, (int)d, (int)L.rows, (int)L.n_tiles, counts,
                                 reinterpret_cast<int*>(base + L.offsets), reinterpret_cast<int*>(base + L.cursors),
-                                tiles, src, pos_of, L.gather ? base + L.xs : nullptr, s);
+                                tiles, src, dst, pos_of, L.gather ? base + L.xs : nullptr, s);
   if (e != hipSuccess) return hip_status(e, "tp_moe_shard_fwd (grouping)");
 
   // grouped gate/up GEMM with the SwiGLU epilogue, 128-row tiles, one expert
@@ -635,7 +637,7 @@ tp_status tp_moe_shard_fwd(const void* x, const int32_t* idx, const float* gate,
     return fail(TP_ERR_UNSUPPORTED, "tp_moe_shard_fwd: no grouped kernel for these operands");
   e = tpk::gemm_tile(p1, plan, tpk::GK_FWD_SWIGLU, false, s);
   if (e != hipSuccess) return hip_status(e, "tp_moe_shard_fwd (gate/up GEMM)");
-  // grouped down GEMM to fp32 rows
+  // grouped down GEMM to fp32 rows, each stored at its (token, slot) row
   GemmParams p2 = base_params();
   p2.A0 = base + L.hs;
   p2.lda = ff_i;
@@ -649,6 +651,7 @@ tp_status tp_moe_shard_fwd(const void* x, const int32_t* idx, const float* gate,
   p2.vecA = p2.vecB = 1;
   p2.tile_expert = tiles;
   p2.b_expert_stride = ff_i * d;
+  p2.c_rows = dst;
   if (!tpk::gemm_tile_supported(p2, plan, tpk::GK_FWD_STORE))
     return fail(TP_ERR_UNSUPPORTED, "tp_moe_shard_fwd: no grouped kernel for these operands");
   e = tpk::gemm_tile(p2, plan, tpk::GK_FWD_STORE, true, s);

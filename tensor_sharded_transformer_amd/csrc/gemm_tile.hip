@@ -413,7 +413,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(const GemmPar
   // goes through a per-wave LDS patch so the global stores are 16 bytes per
   // lane along rows (two per tile) instead of 16 two-byte stores.
   if constexpr (std::is_same<OutT, uint16_t>::value && (EPI == EPI_STORE || EPI == EPI_ACT || EPI == EPI_SWIGLU)) {
-    if (!p.C2 && !p.cpk && p.N % 8 == 0 && p.ldc % 8 == 0 && ((uintptr_t)p.C & 15) == 0) {
+    if (!p.C2 && !p.cpk && !p.c_rows && p.N % 8 == 0 && p.ldc % 8 == 0 && ((uintptr_t)p.C & 15) == 0) {
       wait_loads_barrier<0>();                // every stage is idle (masked tail loads included)
       constexpr int PITCH = 80;               // bytes per patch row: 64 + 16 of padding
       static_assert(NT / 64 * 32 * PITCH <= STAGE, "patches fit in stage 0");
@@ -452,6 +452,43 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(const GemmPar
       return;
     }
   }
+  // fp32 rows (partials): the same per-wave patch, 16-byte stores of 128-byte
+  // row pieces, rows optionally remapped through c_rows.
+  if constexpr (std::is_same<OutT, float>::value && EPI == EPI_STORE && !DUAL) {
+    if (!p.C2 && !p.cpk && p.N % 4 == 0 && p.ldc % 4 == 0 && ((uintptr_t)p.C & 15) == 0) {
+      wait_loads_barrier<0>();
+      constexpr int PITCH = 144;              // 128 + 16 bytes of padding
+      static_assert(NT / 64 * 32 * PITCH <= STAGE, "patches fit in stage 0");
+      char* patch = st0 + wave * 32 * PITCH;
+      static_for<0, TM>([&](auto ic) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
+        int crow[4];                          // destination rows of this lane's four stores
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int m = m0 + wm * WM + i * 32 + q * 8 + (lane >> 3);
+          crow[q] = m >= p.M ? -1 : (p.c_rows ? p.c_rows[m] : m);
+        }
+        static_for<0, TNO>([&](auto jc) __attribute__((always_inline)) {
+          constexpr int j = decltype(jc)::value;
+          const int ncol = n0 + wn * WN + j * 32;
+          static_for<0, 16>([&](auto rc) __attribute__((always_inline)) {
+            constexpr int r = decltype(rc)::value;
+            const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            *reinterpret_cast<float*>(patch + row * PITCH + (lane & 31) * 4) = acc[i][j][r];
+          });
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int row = q * 8 + (lane >> 3);
+            const int cc = (lane & 7) * 4;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(patch + row * PITCH + cc * 4);
+            if (crow[q] >= 0 && ncol + cc < p.N)
+              *reinterpret_cast<u32x4*>(reinterpret_cast<float*>(p.C) + (int64_t)crow[q] * p.ldc + ncol + cc) = v;
+          }
+        });
+      });
+      return;
+    }
+  }
   static_for<0, TM>([&](auto ic) __attribute__((always_inline)) {
     constexpr int i = decltype(ic)::value;
     static_for<0, TNO>([&](auto jc) __attribute__((always_inline)) {
@@ -461,9 +498,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(const GemmPar
         static_for<0, 16>([&](auto rc) __attribute__((always_inline)) {
           constexpr int r = decltype(rc)::value;
           const int m = mrow + i * 32 + 8 * (r >> 2) + (r & 3);
-          if (m < p.M) {
-            if constexpr (DUAL) epilogue_elem<EPI, OutT, uint16_t>(p, m, n, acc[i][j][r], acc[i][j + TNO][r]);
-            else epilogue_elem<EPI, OutT, uint16_t>(p, m, n, acc[i][j][r], 0.0f);
+          const int mo = m < p.M && p.c_rows ? p.c_rows[m] : m;
+          if (m < p.M && mo >= 0) {
+            if constexpr (DUAL) epilogue_elem<EPI, OutT, uint16_t>(p, mo, n, acc[i][j][r], acc[i][j + TNO][r]);
+            else epilogue_elem<EPI, OutT, uint16_t>(p, mo, n, acc[i][j][r], 0.0f);
           }
         });
       }
@@ -508,6 +546,7 @@ bool gemm_tile_supported(const GemmParams& p, const GemmPlan& plan, GemmKind kin
   const bool bkc = kind == GK_BWD_DH_SWIGLU || kind == GK_BWD_DH_ACT || kind == GK_BWD_DX;
   if (!akc && p.M % 8) return false;
   if (p.a_rows && (!akc || p.A1 || p.K1)) return false;
+  if (p.c_rows && (kind != GK_FWD_STORE || p.C2 || p.cpk)) return false;
   if (!bkc && p.N % 8) return false;
   return true;
 }

@@ -24,8 +24,9 @@
 //    table (gate/up with the SwiGLU epilogue, then down to fp32 rows); the
 //    gate/up GEMM reads the routed rows of x through the row table (padding
 //    rows load as zeros; an x of 2 GiB or more is first gathered into the
-//    grouped order).  The combine adds each token's k rows in slot order
-//    with their gates.
+//    grouped order), and the down GEMM stores each row at its (token, slot)
+//    position (padding rows are not stored).  The combine adds each token's
+//    k contiguous rows in slot order with their gates.
 #include "tp_kernels.h"
 #include "tp_device.h"
 
@@ -110,7 +111,8 @@ __global__ __launch_bounds__(256) void moe_count_kernel(const int* __restrict__ 
 // and padding rows marked empty.
 __global__ __launch_bounds__(1024) void moe_plan_kernel(const int* __restrict__ counts, int E, int* __restrict__ offsets,
                                                         int* __restrict__ cursors, int* __restrict__ tile_expert,
-                                                        int n_tiles, int* __restrict__ src_row, int rows) {
+                                                        int n_tiles, int* __restrict__ src_row,
+                                                        int* __restrict__ dst_slot, int rows) {
   __shared__ int s_off[MOE_MAX_E + 1];
   if (threadIdx.x == 0) {
     int o = 0;
@@ -137,7 +139,10 @@ __global__ __launch_bounds__(1024) void moe_plan_kernel(const int* __restrict__ 
     }
     tile_expert[tl] = ex;
   }
-  for (int r = threadIdx.x; r < rows; r += blockDim.x) src_row[r] = -1;
+  for (int r = threadIdx.x; r < rows; r += blockDim.x) {
+    src_row[r] = -1;
+    dst_slot[r] = -1;
+  }
 }
 
 // Each workgroup (2048 entries) counts its entries per expert in LDS,
@@ -145,7 +150,8 @@ __global__ __launch_bounds__(1024) void moe_plan_kernel(const int* __restrict__ 
 // rows inside the block with LDS atomics.
 __global__ __launch_bounds__(256) void moe_scatter_kernel(const int* __restrict__ idx, int n, int k, int E,
                                                           const int* __restrict__ offsets, int* __restrict__ cursors,
-                                                          int* __restrict__ src_row, int* __restrict__ pos_of) {
+                                                          int* __restrict__ src_row, int* __restrict__ dst_slot,
+                                                          int* __restrict__ pos_of) {
   __shared__ int h[MOE_MAX_E];
   __shared__ int base[MOE_MAX_E];
   for (int e = threadIdx.x; e < E; e += 256) h[e] = 0;
@@ -169,6 +175,7 @@ __global__ __launch_bounds__(256) void moe_scatter_kernel(const int* __restrict_
     }
     const int pos = base[e] + atomicAdd(&h[e], 1);
     src_row[pos] = i / k;
+    dst_slot[pos] = i;
     pos_of[i] = pos;
   }
 }
@@ -183,8 +190,9 @@ __global__ __launch_bounds__(256) void moe_gather_kernel(const uint4* __restrict
   xs[i] = s >= 0 ? x[(int64_t)s * d8 + c] : make_uint4(0u, 0u, 0u, 0u);
 }
 
-// y[t, c] = sum_j gate[t, j] * zs[pos_of[t, j], c] in slot order (fp32);
-// four columns per thread (d % 8 == 0).
+// y[t, c] = sum_j gate[t, j] * zs[t k + j, c] in slot order (fp32), over
+// the slots that were routed (pos_of >= 0); four columns per thread
+// (d % 8 == 0).
 template <typename OutT>
 __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ zs, const int* __restrict__ pos_of,
                                                           const float* __restrict__ gate, int T, int k, int d,
@@ -195,10 +203,9 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
   const int t = (int)(i / d4), c = (int)(i % d4) * 4;
   float4 s = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   for (int j = 0; j < k; ++j) {
-    const int pos = pos_of[(int64_t)t * k + j];
-    if (pos < 0) continue;
+    if (pos_of[(int64_t)t * k + j] < 0) continue;
     const float g = gate[(int64_t)t * k + j];
-    const float4 z = *reinterpret_cast<const float4*>(zs + (int64_t)pos * d + c);
+    const float4 z = *reinterpret_cast<const float4*>(zs + ((int64_t)t * k + j) * d + c);
     s.x += g * z.x;
     s.y += g * z.y;
     s.z += g * z.z;
@@ -225,15 +232,16 @@ hipError_t moe_route(const float* logits, int T, int E, int k, int* idx, float* 
 }
 
 hipError_t moe_group(const int* idx, int T, int E, int k, const void* x, int d, int rows, int n_tiles, int* counts,
-                     int* offsets, int* cursors, int* tile_expert, int* src_row, int* pos_of, void* xs, hipStream_t s) {
+                     int* offsets, int* cursors, int* tile_expert, int* src_row, int* dst_slot, int* pos_of, void* xs,
+                     hipStream_t s) {
   const int n = T * k;
   hipError_t e = zero_fill(counts, (size_t)E * sizeof(int), s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(moe_count_kernel, dim3(blocks(n, 256 * 8)), dim3(256), 0, s, idx, n, E, counts);
   hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(1024), 0, s, counts, E, offsets, cursors, tile_expert, n_tiles,
-                     src_row, rows);
+                     src_row, dst_slot, rows);
   hipLaunchKernelGGL(moe_scatter_kernel, dim3(blocks(n, 256 * 8)), dim3(256), 0, s, idx, n, k, E, offsets, cursors,
-                     src_row, pos_of);
+                     src_row, dst_slot, pos_of);
   if (!xs) return hipGetLastError();  // the GEMM reads x through src_row
   const int64_t units = (int64_t)rows * (d / 8);
   hipLaunchKernelGGL(moe_gather_kernel, dim3(blocks(units, 256)), dim3(256), 0, s, reinterpret_cast<const uint4*>(x),

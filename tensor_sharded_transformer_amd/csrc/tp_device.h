@@ -91,6 +91,7 @@ struct GemmParams {
   int64_t b_expert_stride;  //   ... whose B0/B1 start this many elements further per expert index
   const int* a_rows;        // tiled kernel, k-contiguous A only: the A row of each output row (-1: a zero
                             //   row), A0 pointing at row 0; A's bytes must stay below 2^31
+  const int* c_rows;        // tiled kernel, EPI_STORE: the C row each output row is stored to (-1: not stored)
 };
 
 // Calls f(integral_constant<int, I>) for I = 0 .. N-1, so array indices in
