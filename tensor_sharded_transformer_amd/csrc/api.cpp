@@ -265,7 +265,7 @@ tp_status linear_fp8(const char* who, const void* x, const void* wq, const float
 struct MoeLayout {
   int64_t rows = 0, n_tiles = 0;
   bool gather = false;  // x too large for the GEMM's 32-bit row offsets: copy the routed rows first
-  size_t counts = 0, offsets = 0, cursors = 0, tiles = 0, src = 0, dst = 0, pos = 0, xs = 0, hs = 0, zs = 0, total = 0;
+  size_t offsets = 0, cursors = 0, tiles = 0, src = 0, dst = 0, pos = 0, xs = 0, hs = 0, zs = 0, total = 0;
 };
 MoeLayout moe_layout(int64_t T, int64_t d, int64_t ff_i, int E, int k) {
   MoeLayout L;
@@ -278,7 +278,6 @@ MoeLayout moe_layout(int64_t T, int64_t d, int64_t ff_i, int E, int k) {
     o += tpk::align_up(bytes, 256);
     return at;
   };
-  L.counts = take((size_t)E * 4);
   L.offsets = take((size_t)(E + 1) * 4);
   L.cursors = take((size_t)E * 4);
   L.tiles = take((size_t)L.n_tiles * 4);
@@ -601,12 +600,11 @@ tp_status tp_moe_shard_fwd(const void* x, const int32_t* idx, const float* gate,
   if (ws_bytes < L.total)
     return fail(TP_ERR_WORKSPACE, "tp_moe_shard_fwd: workspace of %zu bytes < %zu needed", ws_bytes, L.total);
   char* base = reinterpret_cast<char*>(ws);
-  int* counts = reinterpret_cast<int*>(base + L.counts);
   int* tiles = reinterpret_cast<int*>(base + L.tiles);
   int* pos_of = reinterpret_cast<int*>(base + L.pos);
   int* src = reinterpret_cast<int*>(base + L.src);
   int* dst = reinterpret_cast<int*>(base + L.dst);
-  hipError_t e = tpk::moe_group(idx, (int)T, E, k, x, (int)d, (int)L.rows, (int)L.n_tiles, counts,
+  hipError_t e = tpk::moe_group(idx, (int)T, E, k, x, (int)d, (int)L.rows, (int)L.n_tiles,
                                 reinterpret_cast<int*>(base + L.offsets), reinterpret_cast<int*>(base + L.cursors),
                                 tiles, src, dst, pos_of, L.gather ? base + L.xs : nullptr, s);
   if (e != hipSuccess) return hip_status(e, "tp_moe_shard_fwd (grouping)");

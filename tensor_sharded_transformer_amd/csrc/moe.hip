@@ -13,11 +13,11 @@
 // Design:
 //  * Routing: one wave per token, k passes of a wave arg-max over the fp32
 //    logits (k <= 16, E <= 1024), exponentials relative to the largest.
-//  * Grouping, without a host round trip: per-expert counts (per-workgroup
-//    LDS histograms, one global atomic per workgroup and expert), one
-//    workgroup turns them into offsets with every expert's group padded to a
-//    whole 128-row tile and writes the tile -> expert table, then each routed
-//    (token, slot) takes a row in its expert's group.  Row order inside a
+//  * Grouping, without a host round trip: one workgroup counts the routed
+//    slots per expert in LDS and turns the counts into offsets with every
+//    expert's group padded to a whole 128-row tile (and the tile -> expert
+//    table), then each routed (token, slot) takes a row in its expert's group
+//    (per-workgroup LDS counts, one global atomic per workgroup and expert).  Row order inside a
 //    group does not affect any value (every output row is its own dot
 //    products), so the atomics leave results bitwise reproducible.
 //  * The grouped tiled GEMMs read each tile's expert weights from the tile
@@ -32,6 +32,8 @@
 
 namespace tpk {
 namespace {
+
+constexpr int SCATTER_PER = 512;  // routed slots per scatter workgroup
 
 // One wave per token: lane l holds logits l, l + 64, ... (a NaN logit ranks
 // as -inf); each of the k passes takes the wave's arg-max (larger value, then
@@ -91,41 +93,59 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict_
   }
 }
 
-// (expert indices outside [0, E) are skipped here and in the scatter: such a
-// slot contributes nothing)
-__global__ __launch_bounds__(256) void moe_count_kernel(const int* __restrict__ idx, int n, int E,
-                                                        int* __restrict__ counts) {
-  __shared__ int h[MOE_MAX_E];
-  for (int e = threadIdx.x; e < E; e += 256) h[e] = 0;
-  __syncthreads();
-  for (int i = blockIdx.x * 256 * 8 + threadIdx.x; i < min(n, (blockIdx.x + 1) * 256 * 8); i += 256) {
-    const int e = idx[i];
-    if (e >= 0 && e < E) atomicAdd(&h[e], 1);
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 256)
-    if (h[e]) atomicAdd(&counts[e], h[e]);
-}
-
-// One workgroup: padded group offsets, tile -> expert table, cleared cursors
-// and padding rows marked empty.
-__global__ __launch_bounds__(1024) void moe_plan_kernel(const int* __restrict__ counts, int E, int* __restrict__ offsets,
-                                                        int* __restrict__ cursors, int* __restrict__ tile_expert,
-                                                        int n_tiles, int* __restrict__ src_row,
-                                                        int* __restrict__ dst_slot, int rows) {
+// One workgroup plans the grouping: per-expert counts (an LDS histogram of
+// idx; indices outside [0, E) are skipped here and in the scatter, so such a
+// slot contributes nothing), every expert's group padded to whole tiles
+// (exclusive scan), the tile -> expert table, cleared cursors, and the padding
+// rows of each group marked empty (every other row of an active tile is
+// written by the scatter; tiles past the last group are never read).
+__global__ __launch_bounds__(1024) void moe_plan_kernel(const int* __restrict__ idx, int n, int E,
+                                                        int* __restrict__ offsets, int* __restrict__ cursors,
+                                                        int* __restrict__ tile_expert, int n_tiles,
+                                                        int* __restrict__ src_row, int* __restrict__ dst_slot) {
+  __shared__ int cnt[MOE_MAX_E];
   __shared__ int s_off[MOE_MAX_E + 1];
-  if (threadIdx.x == 0) {
-    int o = 0;
-    for (int e = 0; e < E; ++e) {
-      s_off[e] = o;
-      o += (counts[e] + MOE_TILE - 1) / MOE_TILE * MOE_TILE;
+  __shared__ int wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < E; e += 1024) cnt[e] = 0;
+  __syncthreads();
+  for (int i0 = 0; i0 < n; i0 += 1024 * 16) {  // 16 loads in flight per thread, then the LDS atomics
+    int v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int i = i0 + u * 1024 + tid;
+      v[u] = i < n ? idx[i] : -1;
     }
-    s_off[E] = o;
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (v[u] >= 0 && v[u] < E) atomicAdd(&cnt[v[u]], 1);
   }
   __syncthreads();
-  for (int e = threadIdx.x; e <= E; e += blockDim.x) offsets[e] = s_off[e];
-  for (int e = threadIdx.x; e < E; e += blockDim.x) cursors[e] = 0;
-  for (int tl = threadIdx.x; tl < n_tiles; tl += blockDim.x) {
+  // exclusive scan of the padded sizes, one expert per thread (E <= 1024)
+  const int c = tid < E ? cnt[tid] : 0;
+  const int padded = (c + MOE_TILE - 1) / MOE_TILE * MOE_TILE;
+  int incl = padded;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off);
+    if (lane >= off) incl += v;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += wsum[w];
+  const int start = before + incl - padded;
+  if (tid < E) {
+    s_off[tid] = start;
+    offsets[tid] = start;
+    cursors[tid] = 0;
+  }
+  if (tid == E - 1) {
+    s_off[E] = start + padded;
+    offsets[E] = start + padded;
+  }
+  __syncthreads();
+  for (int tl = tid; tl < n_tiles; tl += 1024) {
     const int r = tl * MOE_TILE;
     int ex = -1;
     if (r < s_off[E]) {  // the expert whose padded group holds row r (binary search)
@@ -139,13 +159,17 @@ __global__ __launch_bounds__(1024) void moe_plan_kernel(const int* __restrict__ 
     }
     tile_expert[tl] = ex;
   }
-  for (int r = threadIdx.x; r < rows; r += blockDim.x) {
-    src_row[r] = -1;
-    dst_slot[r] = -1;
+  // padding rows: each expert's last (padded - count) rows, one wave per expert
+  for (int e = wave; e < E; e += 16) {
+    const int first = s_off[e] + cnt[e];
+    for (int r = first + lane; r < s_off[e + 1]; r += 64) {
+      src_row[r] = -1;
+      dst_slot[r] = -1;
+    }
   }
 }
 
-// Each workgroup (2048 entries) counts its entries per expert in LDS,
+// Each workgroup (SCATTER_PER entries) counts its entries per expert in LDS,
 // reserves one block per expert with a single global atomic, then hands out
 // rows inside the block with LDS atomics.
 __global__ __launch_bounds__(256) void moe_scatter_kernel(const int* __restrict__ idx, int n, int k, int E,
@@ -156,7 +180,7 @@ __global__ __launch_bounds__(256) void moe_scatter_kernel(const int* __restrict_
   __shared__ int base[MOE_MAX_E];
   for (int e = threadIdx.x; e < E; e += 256) h[e] = 0;
   __syncthreads();
-  const int lo = blockIdx.x * 256 * 8, hi = min(n, lo + 256 * 8);
+  const int lo = blockIdx.x * SCATTER_PER, hi = min(n, lo + SCATTER_PER);
   for (int i = lo + threadIdx.x; i < hi; i += 256) {
     const int e = idx[i];
     if (e >= 0 && e < E) atomicAdd(&h[e], 1);
@@ -180,12 +204,15 @@ __global__ __launch_bounds__(256) void moe_scatter_kernel(const int* __restrict_
   }
 }
 
-// xs[r] = x[src_row[r]] (zero for padding rows); d % 8 == 0, 16-byte rows.
+// xs[r] = x[src_row[r]] (zero for padding rows) for the rows of the groups
+// (r < *used; later rows are never read); d % 8 == 0, 16-byte rows.
 __global__ __launch_bounds__(256) void moe_gather_kernel(const uint4* __restrict__ x, const int* __restrict__ src_row,
-                                                         int rows, int d8, uint4* __restrict__ xs) {
+                                                         const int* __restrict__ used, int rows, int d8,
+                                                         uint4* __restrict__ xs) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= (int64_t)rows * d8) return;
   const int r = (int)(i / d8), c = (int)(i % d8);
+  if (r >= *used) return;
   const int s = src_row[r];
   xs[i] = s >= 0 ? x[(int64_t)s * d8 + c] : make_uint4(0u, 0u, 0u, 0u);
 }
@@ -231,21 +258,17 @@ hipError_t moe_route(const float* logits, int T, int E, int k, int* idx, float* 
   return hipGetLastError();
 }
 
-hipError_t moe_group(const int* idx, int T, int E, int k, const void* x, int d, int rows, int n_tiles, int* counts,
-                     int* offsets, int* cursors, int* tile_expert, int* src_row, int* dst_slot, int* pos_of, void* xs,
-                     hipStream_t s) {
+hipError_t moe_group(const int* idx, int T, int E, int k, const void* x, int d, int rows, int n_tiles, int* offsets,
+                     int* cursors, int* tile_expert, int* src_row, int* dst_slot, int* pos_of, void* xs, hipStream_t s) {
   const int n = T * k;
-  hipError_t e = zero_fill(counts, (size_t)E * sizeof(int), s);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(moe_count_kernel, dim3(blocks(n, 256 * 8)), dim3(256), 0, s, idx, n, E, counts);
-  hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(1024), 0, s, counts, E, offsets, cursors, tile_expert, n_tiles,
-                     src_row, dst_slot, rows);
-  hipLaunchKernelGGL(moe_scatter_kernel, dim3(blocks(n, 256 * 8)), dim3(256), 0, s, idx, n, k, E, offsets, cursors,
+  hipLaunchKernelGGL(moe_plan_kernel, dim3(1), dim3(1024), 0, s, idx, n, E, offsets, cursors, tile_expert, n_tiles,
+                     src_row, dst_slot);
+  hipLaunchKernelGGL(moe_scatter_kernel, dim3(blocks(n, SCATTER_PER)), dim3(256), 0, s, idx, n, k, E, offsets, cursors,
                      src_row, dst_slot, pos_of);
   if (!xs) return hipGetLastError();  // the GEMM reads x through src_row
   const int64_t units = (int64_t)rows * (d / 8);
   hipLaunchKernelGGL(moe_gather_kernel, dim3(blocks(units, 256)), dim3(256), 0, s, reinterpret_cast<const uint4*>(x),
-                     src_row, rows, d / 8, reinterpret_cast<uint4*>(xs));
+                     src_row, offsets + E, rows, d / 8, reinterpret_cast<uint4*>(xs));
   return hipGetLastError();
 }
 

@@ -166,9 +166,8 @@ constexpr int MOE_MAX_K = 16;
 constexpr int MOE_TILE = 128;
 hipError_t moe_route(const float* logits, int T, int E, int k, int* idx, float* gate, hipStream_t s);
 // (xs == nullptr: no gathered copy of x, the GEMM reads x through src_row)
-hipError_t moe_group(const int* idx, int T, int E, int k, const void* x, int d, int rows, int n_tiles, int* counts,
-                     int* offsets, int* cursors, int* tile_expert, int* src_row, int* dst_slot, int* pos_of, void* xs,
-                     hipStream_t s);
+hipError_t moe_group(const int* idx, int T, int E, int k, const void* x, int d, int rows, int n_tiles, int* offsets,
+                     int* cursors, int* tile_expert, int* src_row, int* dst_slot, int* pos_of, void* xs, hipStream_t s);
 hipError_t moe_combine(const float* zs, const int* pos_of, const float* gate, int T, int k, int d, void* y,
                        bool out_f32, hipStream_t s);
 

@@ -952,3 +952,25 @@ def test_moe_x_of_2gib_takes_the_gathered_path():
     assert_close(y[rows], ref, BF16_TOL, "moe rows, gathered x")
     del ws, x
     torch.cuda.empty_cache()
+
+
+def test_moe_dropped_slots_contribute_nothing():
+    """Slots whose expert index lies outside [0, E) are skipped: the result
+    equals the block with those slots' gates set to zero."""
+    wl = W.MoeWorkload("moe_drop", T=150, d=128, ff=64, E=8, k=3, p=1, seed=62)
+    t = W.moe_rank_inputs(wl)
+    ridx, rgate = O.moe_route(t["logits"], wl.k)
+    bad = np.zeros_like(ridx, dtype=bool)
+    bad[::7, 1] = True
+    bad[3::11, 2] = True
+    idx_in = ridx.copy()
+    idx_in[::7, 1] = -1
+    idx_in[3::11, 2] = wl.E
+    idx = torch.from_numpy(idx_in.astype(np.int32)).cuda()
+    gate = torch.from_numpy(rgate.astype(np.float32)).cuda()
+    y = torch.full((wl.T, wl.d), 7.0, dtype=torch.float32, device="cuda")
+    ws = tp.new_workspace(tp.tp_moe_shard_fwd_workspace(wl.T, wl.d, wl.ff_i, wl.E, wl.k))
+    tp.tp_moe_shard_fwd(cuda(t["x"]), idx, gate, cuda(t["w1"]), cuda(t["w_up"]), cuda(t["w2"]), y, ws)
+    g_ref = np.where(bad, 0.0, gate.cpu().numpy().astype(np.float64))
+    ref = O.moe_shard_fwd(t["x"], np.where(bad, 0, ridx), g_ref, t["w1"], t["w_up"], t["w2"])
+    assert_close(y, ref, BF16_TOL, "moe with dropped slots")
