@@ -46,10 +46,12 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict_
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float* lg = logits + (int64_t)t * E;
+  const int per = (E + 63) / 64;  // register slots in use (uniform)
   float v[PER];
   uint32_t live = 0;  // bit q: value q of this lane is still a candidate
 #pragma unroll
   for (int q = 0; q < PER; ++q) {
+    if (q >= per) break;
     const int e = lane + 64 * q;
     const float x = e < E ? lg[e] : -INFINITY;
     v[q] = x != x ? -INFINITY : x;
@@ -61,11 +63,13 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict_
     float bv = -INFINITY;
     int be = NONE;
 #pragma unroll
-    for (int q = 0; q < PER; ++q)  // indices rise with q: strict > keeps the lower on ties
+    for (int q = 0; q < PER; ++q) {  // indices rise with q: strict > keeps the lower on ties
+      if (q >= per) break;
       if ((live >> q & 1u) && (be == NONE || v[q] > bv)) {
         bv = v[q];
         be = lane + 64 * q;
       }
+    }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
       const float ov = __shfl_xor(bv, off);
