@@ -123,6 +123,13 @@ def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
+def _dtypes(dtype, **named) -> None:
+    """Every given tensor must have `dtype` (the kernels read raw bytes)."""
+    for nm, t in named.items():
+        if t is not None and t.dtype != dtype:
+            raise TypeError(f"{nm} must be {dtype}, got {t.dtype}")
+
+
 def _shape(t: torch.Tensor, shape, name: str) -> None:
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
@@ -161,6 +168,7 @@ def tp_col_linear(x, w, w_up, bias, y, act: str = "none", ws: Optional[torch.Ten
     _shape(y, (T, N), "y")
     if w_up is not None:
         _shape(w_up, (K, N), "w_up")
+    _dtypes(x.dtype, w=w, w_up=w_up, bias=bias, y=y)
     ws_bytes = 0 if ws is None else ws.numel()
     _check(load().tp_col_linear(_ptr(x), _ptr(w), _ptr(w_up), _ptr(bias), _ptr(y), _ptr(ws), ws_bytes, T, K, N,
                                 _dt(x), ACT[act], _stream()))
@@ -175,6 +183,7 @@ def tp_act_inplace(h, up, act: str):
     T, N = h.shape
     if up is not None:
         _shape(up, (T, N), "up")
+    _dtypes(h.dtype, up=up)
     _check(load().tp_act_inplace(_ptr(h), _ptr(up), T, N, _dt(h), ACT[act], _stream()))
     return h
 
@@ -184,6 +193,7 @@ def tp_row_linear_partial(x_i, w_i, z_i, ws: Optional[torch.Tensor] = None):
     N = w_i.shape[1]
     _shape(w_i, (K, N), "w_i")
     _shape(z_i, (T, N), "z_i")
+    _dtypes(x_i.dtype, w_i=w_i)
     ws_bytes = 0 if ws is None else ws.numel()
     _check(load().tp_row_linear_partial(_ptr(x_i), _ptr(w_i), _ptr(z_i), _ptr(ws), ws_bytes, T, K, N, _dt(x_i),
                                         _dt(z_i), _stream()))
@@ -208,6 +218,7 @@ def tp_mlp_shard_fwd(x, w1_i, w_up_i, w2_i, y_i, act: str, ws: torch.Tensor, sav
         _shape(w_up_i, (d, ff_i), "w_up_i")
     if saved is not None:
         _shape(saved, (T, (2 if act == "swiglu" else 1) * ff_i), "saved")
+    _dtypes(x.dtype, w1_i=w1_i, w_up_i=w_up_i, w2_i=w2_i, saved=saved)
     _check(load().tp_mlp_shard_fwd(_ptr(x), _ptr(w1_i), _ptr(w_up_i), _ptr(w2_i), _ptr(y_i), _ptr(saved), _ptr(ws),
                                    ws.numel() if ws is not None else 0, T, d, ff_i, _dt(x), _dt(y_i), ACT[act],
                                    _stream()))
@@ -226,6 +237,8 @@ def tp_mlp_shard_bwd(x, w1_i, w_up_i, w2_i, saved, dy, dw1_i, dw_up_i, dw2_i, dx
         _shape(t, shp, nm)
     if dw_up_i is not None:
         _shape(dw_up_i, (d, ff_i), "dw_up_i")
+    _dtypes(x.dtype, w1_i=w1_i, w_up_i=w_up_i, w2_i=w2_i, saved=saved, dy=dy, dw1_i=dw1_i, dw_up_i=dw_up_i,
+            dw2_i=dw2_i, dx_i=dx_i)
     _check(load().tp_mlp_shard_bwd(_ptr(x), _ptr(w1_i), _ptr(w_up_i), _ptr(w2_i), _ptr(saved), _ptr(dy),
                                    _ptr(dw1_i), _ptr(dw_up_i), _ptr(dw2_i), _ptr(dx_i), _ptr(ws),
                                    ws.numel() if ws is not None else 0, T, d, ff_i, _dt(x), ACT[act], _stream()))
@@ -247,6 +260,7 @@ def tp_linear_shard_bwd(x, w, dy, dw, dx, ws: Optional[torch.Tensor] = None):
         _shape(dw, (K, N), "dw")
     if dx is not None:
         _shape(dx, (T, K), "dx")
+    _dtypes(dy.dtype, x=x, w=w, dw=dw, dx=dx)
     _check(load().tp_linear_shard_bwd(_ptr(x), _ptr(w), _ptr(dy), _ptr(dw), _ptr(dx), _ptr(ws),
                                       ws.numel() if ws is not None else 0, T, K, N, _dt(dy), _stream()))
 
@@ -257,6 +271,7 @@ def tp_gqa_attention_fwd(qkv, out, n_q: int, n_kv: int, head_dim: int, causal: b
     T = qkv.shape[0]
     _shape(qkv, (T, (n_q + 2 * n_kv) * head_dim), "qkv")
     _shape(out, (T, n_q * head_dim), "out")
+    _dtypes(torch.bfloat16, qkv=qkv, out=out)
     _check(load().tp_gqa_attention_fwd(_ptr(qkv), _ptr(out), T, n_q, n_kv, head_dim, int(bool(causal)), scale,
                                        _stream()))
     return out
@@ -300,6 +315,8 @@ def tp_mlp_shard_fwd_fp8(x, wq1_i, s1_i, wq_up_i, s_up_i, wq2_i, s2_i, y_i, act:
     if wq_up_i is not None:
         _fp8_codes(wq_up_i, "wq_up_i")
         _shape(wq_up_i, (d, ff_i), "wq_up_i")
+    _dtypes(torch.bfloat16, x=x)
+    _dtypes(torch.float32, s1_i=s1_i, s_up_i=s_up_i, s2_i=s2_i)
     _check(load().tp_mlp_shard_fwd_fp8(_ptr(x), _ptr(wq1_i), _ptr(s1_i), _ptr(wq_up_i), _ptr(s_up_i), _ptr(wq2_i),
                                        _ptr(s2_i), _ptr(y_i), _ptr(ws), ws.numel() if ws is not None else 0, T, d,
                                        ff_i, _dt(y_i), ACT[act], _stream()))
@@ -335,6 +352,7 @@ def tp_moe_shard_fwd(x, idx, gate, w1, w_up, w2, y_i, ws: torch.Tensor):
     _shape(y_i, (T, d), "y_i")
     if idx.dtype != torch.int32 or gate.dtype != torch.float32:
         raise TypeError("idx must be int32 and gate float32")
+    _dtypes(torch.bfloat16, x=x, w1=w1, w_up=w_up, w2=w2)
     _check(load().tp_moe_shard_fwd(_ptr(x), _ptr(idx), _ptr(gate), _ptr(w1), _ptr(w_up), _ptr(w2), _ptr(y_i),
                                    _ptr(ws), ws.numel() if ws is not None else 0, T, d, ff_i, E, k, _dt(y_i),
                                    _stream()))
@@ -354,6 +372,8 @@ def tp_col_linear_fp8(x, wq, scale, wq_up, scale_up, bias, y, act: str, ws: torc
     if wq_up is not None:
         _fp8_codes(wq_up, "wq_up")
         _shape(wq_up, (K, N), "wq_up")
+    _dtypes(torch.bfloat16, x=x, bias=bias, y=y)
+    _dtypes(torch.float32, scale=scale, scale_up=scale_up)
     _check(load().tp_col_linear_fp8(_ptr(x), _ptr(wq), _ptr(scale), _ptr(wq_up), _ptr(scale_up), _ptr(bias), _ptr(y),
                                     _ptr(ws), ws.numel() if ws is not None else 0, T, K, N, ACT[act], _stream()))
     return y
@@ -367,6 +387,8 @@ def tp_row_linear_partial_fp8(x_i, wq_i, scale_i, z_i, ws: torch.Tensor):
     _shape(wq_i, (K, N), "wq_i")
     _shape(scale_i, (N,), "scale_i")
     _shape(z_i, (T, N), "z_i")
+    _dtypes(torch.bfloat16, x_i=x_i)
+    _dtypes(torch.float32, scale_i=scale_i)
     _check(load().tp_row_linear_partial_fp8(_ptr(x_i), _ptr(wq_i), _ptr(scale_i), _ptr(z_i), _ptr(ws),
                                             ws.numel() if ws is not None else 0, T, K, N, _dt(z_i), _stream()))
     return z_i
@@ -376,6 +398,8 @@ def tp_partial_sum(zs: Sequence[torch.Tensor], bias, y):
     T, N = y.shape
     for z in zs:
         _shape(z, (T, N), "z")
+        _dtypes(zs[0].dtype, z=z)
+    _dtypes(zs[0].dtype if zs else y.dtype, bias=bias)
     arr = (c_p * len(zs))(*[_ptr(z) for z in zs])
     _check(load().tp_partial_sum(arr, len(zs), _ptr(bias), _ptr(y), T, N, _dt(zs[0]), _dt(y), _stream()))
     return y
@@ -394,6 +418,10 @@ def tp_rs_residual_rmsnorm(zs: Sequence[torch.Tensor], rank: int, bias, residual
     _shape(residual_out, (rows, N), "residual_out")
     _shape(y, (rows, N), "y")
     _shape(norm_w, (N,), "norm_w")
+    for z in zs:
+        _dtypes(zs[0].dtype, z=z)
+    _dtypes(zs[0].dtype, bias=bias)
+    _dtypes(y.dtype, residual_in=residual_in, residual_out=residual_out, norm_w=norm_w)
     arr = (c_p * p)(*[_ptr(z) for z in zs])
     _check(load().tp_rs_residual_rmsnorm(arr, p, rank, _ptr(bias), _ptr(residual_in), _ptr(norm_w), eps,
                                          _ptr(residual_out), _ptr(y), T, N, _dt(zs[0]), _dt(y), _stream()))

@@ -255,3 +255,19 @@ def test_moe_validation(lib):
 def test_status_strings(lib):
     for s in range(8):
         assert lib.tp_status_string(s)
+
+
+def test_binding_rejects_mixed_operand_dtypes():
+    """The kernels read raw bytes, so the binding refuses operands whose dtype
+    differs from the one the call declares (checked before any device call)."""
+    import torch
+    f32 = torch.zeros(4, 8, dtype=torch.float32)
+    bf = torch.zeros(8, 8, dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        B.tp_col_linear(f32, bf, None, None, torch.zeros(4, 8), "none")
+    with pytest.raises(TypeError):
+        B.tp_row_linear_partial(f32, bf, torch.zeros(4, 8))
+    with pytest.raises(TypeError):
+        B.tp_gqa_attention_fwd(torch.zeros(4, 3 * 128), torch.zeros(4, 128), 1, 1, 128, True, 0.1)
+    with pytest.raises(TypeError):
+        B.tp_partial_sum([torch.zeros(4, 8), torch.zeros(4, 8, dtype=torch.bfloat16)], None, torch.zeros(4, 8))
