@@ -609,11 +609,11 @@ tp_status tp_moe_shard_fwd(const void* x, const int32_t* idx, const float* gate,
                                 tiles, src, dst, pos_of, L.gather ? base + L.xs : nullptr, s);
   if (e != hipSuccess) return hip_status(e, "tp_moe_shard_fwd (grouping)");
 
-  // grouped gate/up GEMM with the SwiGLU epilogue, 128-row tiles, one expert
+  // grouped gate/up GEMM with the SwiGLU epilogue, MOE_TILE-row tiles, one expert
   // each, reading the routed rows of x through the row table
   GemmPlan plan;
   plan.kernel = tpk::KERNEL_TILED;
-  plan.tile = tpk::TILE_128x128;
+  plan.tile = tpk::TILE_256x256;  // BM == MOE_TILE
   plan.splitk = 1;
   GemmParams p1 = base_params();
   p1.A0 = L.gather ? base + L.xs : x;

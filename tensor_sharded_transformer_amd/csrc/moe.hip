@@ -15,11 +15,12 @@
 //    logits (k <= 16, E <= 1024), exponentials relative to the largest.
 //  * Grouping, without a host round trip: one workgroup counts the routed
 //    slots per expert in LDS and turns the counts into offsets with every
-//    expert's group padded to a whole 128-row tile (and the tile -> expert
+//    expert's group padded to whole MOE_TILE-row tiles (and the tile -> expert
 //    table), then each routed (token, slot) takes a row in its expert's group
-//    (per-workgroup LDS counts, one global atomic per workgroup and expert).  Row order inside a
-//    group does not affect any value (every output row is its own dot
-//    products), so the atomics leave results bitwise reproducible.
+//    (per-workgroup LDS counts, one global atomic per workgroup and
+//    expert).  Row order inside a group does not affect any value (every
+//    output row is its own dot products), so the atomics leave results
+//    bitwise reproducible.
 //  * The grouped tiled GEMMs read each tile's expert weights from the tile
 //    table (gate/up with the SwiGLU epilogue, then down to fp32 rows); the
 //    gate/up GEMM reads the routed rows of x through the row table (padding

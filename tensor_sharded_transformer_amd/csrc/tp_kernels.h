@@ -163,7 +163,7 @@ hipError_t pack_fp8_strips(const void* src, void* dst, int64_t K, int64_t N, hip
 // routed rows into 128-row tiles per expert, weighted combine.
 constexpr int MOE_MAX_E = 1024;
 constexpr int MOE_MAX_K = 16;
-constexpr int MOE_TILE = 128;
+constexpr int MOE_TILE = 256;  // rows per expert-group tile (the grouped GEMMs' BM)
 hipError_t moe_route(const float* logits, int T, int E, int k, int* idx, float* gate, hipStream_t s);
 // (xs == nullptr: no gathered copy of x, the GEMM reads x through src_row)
 hipError_t moe_group(const int* idx, int T, int E, int k, const void* x, int d, int rows, int n_tiles, int* offsets,
