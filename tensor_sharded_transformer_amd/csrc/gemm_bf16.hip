@@ -356,7 +356,8 @@ static hipError_t launch_shape(GemmParams p, const GemmPlan& plan, hipStream_t s
   p.splitk = plan.splitk;
   switch (plan.tile) {
     case TILE_256x256: return launch_cfg<256, 256, 2, 2, AKC, BKC, DUAL, EPI, OutT>(p, s);
-    case TILE_128x128: return launch_cfg<128, 128, 2, 2, AKC, BKC, DUAL, EPI, OutT>(p, s);
+    case TILE_128x128:
+    case TILE_128x128_W8: return launch_cfg<128, 128, 2, 2, AKC, BKC, DUAL, EPI, OutT>(p, s);
     case TILE_64x128: return launch_cfg<64, 128, 2, 2, AKC, BKC, DUAL, EPI, OutT>(p, s);
     default: return hipErrorInvalidValue;
   }
@@ -414,6 +415,11 @@ GemmPlan plan_gemm(int M, int N, int K, bool dual, bool fwd_layout, bool vec_ok,
   const int r128 = (tiles_for(128, 128) + CUS - 1) / CUS;
   plan.tile = TP_TILE_COST ? (r256 * 32 < r128 * 10 ? TILE_256x256 : TILE_128x128)
                            : (tiles_for(256, 256) >= CUS ? TILE_256x256 : TILE_128x128);
+  // A grid of fewer 128x128 tiles than CUs leaves each busy CU one
+  // workgroup: give it 8 waves so every SIMD has two to interleave (measured
+  // on the 224-tile shard-backward dh GEMM: 80 -> 68 us; a full 256-tile grid
+  // ran slightly slower with 8 waves, so it keeps 4).
+  if (plan.tile == TILE_128x128 && tiles_for(128, 128) < CUS) plan.tile = TILE_128x128_W8;
   plan.splitk = 1;
   return plan;
 }

@@ -454,7 +454,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(const GemmPar
   }
   // fp32 rows (partials): the same per-wave patch, 16-byte stores of 128-byte
   // row pieces, rows optionally remapped through c_rows.
-  if constexpr (std::is_same<OutT, float>::value && EPI == EPI_STORE && !DUAL) {
+  if constexpr (std::is_same<OutT, float>::value && EPI == EPI_STORE && !DUAL && NT / 64 * 32 * 144 <= STAGE) {
     if (!p.C2 && !p.cpk && p.N % 4 == 0 && p.ldc % 4 == 0 && ((uintptr_t)p.C & 15) == 0) {
       wait_loads_barrier<0>();
       constexpr int PITCH = 144;              // 128 + 16 bytes of padding
@@ -525,6 +525,7 @@ hipError_t launch_tile_shape(const GemmParams& p, int tile, hipStream_t s) {
       return launch_tile<256, 256, TP_TILE_WGM_256, TP_TILE_WGN_256, TP_TILE_STAGES_256, AKC, BKC, DUAL, EPI, OutT>(p, s);
     case TILE_128x128:
       return launch_tile<128, 128, TP_TILE_WGM_128, TP_TILE_WGN_128, TP_TILE_STAGES_128, AKC, BKC, DUAL, EPI, OutT>(p, s);
+    case TILE_128x128_W8: return launch_tile<128, 128, 4, 2, TP_TILE_STAGES_128, AKC, BKC, DUAL, EPI, OutT>(p, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -537,7 +538,7 @@ bool aligned16(const void* q) { return q == nullptr || ((uintptr_t)q & 15) == 0;
 // and either wholly inside or wholly outside the matrix.
 bool gemm_tile_supported(const GemmParams& p, const GemmPlan& plan, GemmKind kind) {
   if (plan.kernel != KERNEL_TILED || plan.splitk != 1) return false;
-  if (plan.tile != TILE_256x256 && plan.tile != TILE_128x128) return false;
+  if (plan.tile != TILE_256x256 && plan.tile != TILE_128x128 && plan.tile != TILE_128x128_W8) return false;
   if (!p.vecA || !p.vecB) return false;
   if (p.lda % 8 || p.ldb % 8 || p.K0 % 8 || p.K1 % 8) return false;
   if (p.lda > (1 << 21) || p.ldb > (1 << 21)) return false;  // per-lane offsets stay below 2^31

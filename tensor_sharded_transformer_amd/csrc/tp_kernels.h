@@ -100,7 +100,9 @@ size_t stream_lds_bytes(int M, int ksteps, bool dual);
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
-enum TileShape : int { TILE_256x256 = 0, TILE_128x128 = 1, TILE_64x128 = 2 };
+// TILE_128x128_W8: 128x128 tiles with 8 waves (4x2) instead of 4, for grids
+// of at most one tile per CU.
+enum TileShape : int { TILE_256x256 = 0, TILE_128x128 = 1, TILE_64x128 = 2, TILE_128x128_W8 = 3 };
 enum KernelKind : int { KERNEL_TILED = 0, KERNEL_STREAM = 1, KERNEL_DECODE = 2 };
 
 struct GemmPlan {
