@@ -974,3 +974,18 @@ def test_moe_dropped_slots_contribute_nothing():
     g_ref = np.where(bad, 0.0, gate.cpu().numpy().astype(np.float64))
     ref = O.moe_shard_fwd(t["x"], np.where(bad, 0, ridx), g_ref, t["w1"], t["w_up"], t["w2"])
     assert_close(y, ref, BF16_TOL, "moe with dropped slots")
+
+
+@pytest.mark.parametrize("T,d,ff_i,E,k", [(40, 64, 8, 1024, 16), (33, 128, 16, 1000, 16), (5, 64, 8, 65, 1)])
+def test_moe_at_the_expert_and_slot_limits(T, d, ff_i, E, k):
+    """E up to 1024 and k = 16: every register slot of the routing waves, the
+    planning scan across all 16 waves of its workgroup, more tiles than its
+    threads, and an E that is not a multiple of 64."""
+    wl = W.MoeWorkload("moe_limits", T=T, d=d, ff=ff_i, E=E, k=k, p=1, seed=63 + E)
+    t = W.moe_rank_inputs(wl)
+    idx, gate, y = moe_run(t, k, torch.float32)
+    ridx, rgate = O.moe_route(t["logits"], k)
+    assert torch.equal(idx.cpu().long(), torch.from_numpy(ridx)), "routing decisions"
+    np.testing.assert_allclose(gate.cpu().numpy(), rgate, rtol=1e-5, atol=1e-6)
+    ref = O.moe_shard_fwd(t["x"], ridx, rgate, t["w1"], t["w_up"], t["w2"])
+    assert_close(y, ref, BF16_TOL, "moe block at the limits")
