@@ -989,3 +989,42 @@ def test_moe_at_the_expert_and_slot_limits(T, d, ff_i, E, k):
     np.testing.assert_allclose(gate.cpu().numpy(), rgate, rtol=1e-5, atol=1e-6)
     ref = O.moe_shard_fwd(t["x"], ridx, rgate, t["w1"], t["w_up"], t["w2"])
     assert_close(y, ref, BF16_TOL, "moe block at the limits")
+
+
+def test_moe_graph_replay():
+    """Routing and the MoE block captured in one HIP graph: several replays,
+    with an eager MoE call on the graph's workspace between them, each
+    bit-identical to the eager result (the grouping state is rebuilt by every
+    call and nothing issues a memset)."""
+    wl = W.MoeWorkload("moe_graph", T=300, d=256, ff=64, E=16, k=4, p=1, seed=64)
+    t = W.moe_rank_inputs(wl)
+    other = W.moe_rank_inputs(W.MoeWorkload("moe_graph_other", T=300, d=256, ff=64, E=16, k=4, p=1, seed=65))
+    x, lg, w1, wu, w2 = (cuda(t[n]) for n in ("x", "logits", "w1", "w_up", "w2"))
+    x2, lg2 = cuda(other["x"]), cuda(other["logits"])
+    idx = torch.empty(wl.T, wl.k, dtype=torch.int32, device="cuda")
+    gate = torch.empty(wl.T, wl.k, dtype=torch.float32, device="cuda")
+    idx2, gate2 = torch.empty_like(idx), torch.empty_like(gate)
+    y = torch.empty(wl.T, wl.d, dtype=torch.float32, device="cuda")
+    y2 = torch.empty_like(y)
+    ws = tp.new_workspace(tp.tp_moe_shard_fwd_workspace(wl.T, wl.d, wl.ff_i, wl.E, wl.k))
+
+    def step():
+        tp.tp_moe_route(lg, wl.k, idx, gate)
+        tp.tp_moe_shard_fwd(x, idx, gate, w1, wu, w2, y, ws)
+
+    step()
+    torch.cuda.synchronize()
+    y_eager = y.clone()
+    ridx, rgate = O.moe_route(t["logits"], wl.k)
+    assert_close(y_eager, O.moe_shard_fwd(t["x"], ridx, rgate, t["w1"], t["w_up"], t["w2"]), BF16_TOL, "eager")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(4):
+        y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager), f"replay {r}"
+        tp.tp_moe_route(lg2, wl.k, idx2, gate2)
+        tp.tp_moe_shard_fwd(x2, idx2, gate2, w1, wu, w2, y2, ws)   # the graph's workspace, eagerly
+        torch.cuda.synchronize()
