@@ -257,7 +257,9 @@ tp_status tp_mlp_shard_fwd_fp8(const void* x, const void* wq1_i, const float* s1
  * round trip); ws (device) of ws_bytes >= tp_moe_shard_fwd_workspace(...),
  * same rules as tp_mlp_shard_fwd's.  Results do not depend on the order in
  * which the rows are grouped.  A slot whose idx lies outside [0, E) (a
- * dropped slot) contributes nothing. */
+ * dropped slot) contributes nothing.  Each routed row's down projection is
+ * kept in out_dtype (bf16 like h, or fp32) before the gate-weighted sum,
+ * which accumulates in fp32. */
 tp_status tp_moe_route(const float* logits, int64_t T, int E, int k, int32_t* idx, float* gate,
                        tp_stream stream);
 size_t tp_moe_shard_fwd_workspace(int64_t T, int64_t d, int64_t ff_i, int E, int k);

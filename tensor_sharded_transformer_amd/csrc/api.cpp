@@ -287,7 +287,7 @@ MoeLayout moe_layout(int64_t T, int64_t d, int64_t ff_i, int E, int k) {
   L.gather = T * d * 2 > INT32_MAX - 64;
   L.xs = take(L.gather ? (size_t)L.rows * d * 2 : 0);
   L.hs = take((size_t)L.rows * ff_i * 2);
-  L.zs = take((size_t)T * k * d * 4);  // down-projection rows in (token, slot) order
+  L.zs = take((size_t)T * k * d * 4);  // down-projection rows in (token, slot) order (fp32 or bf16)
   L.total = o;
   return L;
 }
@@ -635,7 +635,9 @@ tp_status tp_moe_shard_fwd(const void* x, const int32_t* idx, const float* gate,
     return fail(TP_ERR_UNSUPPORTED, "tp_moe_shard_fwd: no grouped kernel for these operands");
   e = tpk::gemm_tile(p1, plan, tpk::GK_FWD_SWIGLU, false, s);
   if (e != hipSuccess) return hip_status(e, "tp_moe_shard_fwd (gate/up GEMM)");
-  // grouped down GEMM to fp32 rows, each stored at its (token, slot) row
+  // grouped down GEMM, each row stored at its (token, slot) row: bf16 rows
+  // for a bf16 output (an intermediate, like h), fp32 rows for an fp32 one
+  const bool zs_f32 = out_dtype == TP_F32;
   GemmParams p2 = base_params();
   p2.A0 = base + L.hs;
   p2.lda = ff_i;
@@ -652,10 +654,9 @@ tp_status tp_moe_shard_fwd(const void* x, const int32_t* idx, const float* gate,
   p2.c_rows = dst;
   if (!tpk::gemm_tile_supported(p2, plan, tpk::GK_FWD_STORE))
     return fail(TP_ERR_UNSUPPORTED, "tp_moe_shard_fwd: no grouped kernel for these operands");
-  e = tpk::gemm_tile(p2, plan, tpk::GK_FWD_STORE, true, s);
+  e = tpk::gemm_tile(p2, plan, tpk::GK_FWD_STORE, zs_f32, s);
   if (e != hipSuccess) return hip_status(e, "tp_moe_shard_fwd (down GEMM)");
-  return hip_status(tpk::moe_combine(reinterpret_cast<const float*>(base + L.zs), pos_of, gate, (int)T, k, (int)d, y_i,
-                                     out_dtype == TP_F32, s),
+  return hip_status(tpk::moe_combine(base + L.zs, zs_f32, pos_of, gate, (int)T, k, (int)d, y_i, out_dtype == TP_F32, s),
                     "tp_moe_shard_fwd (combine)");
 }
 

@@ -413,13 +413,20 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(const GemmPar
   // goes through a per-wave LDS patch so the global stores are 16 bytes per
   // lane along rows (two per tile) instead of 16 two-byte stores.
   if constexpr (std::is_same<OutT, uint16_t>::value && (EPI == EPI_STORE || EPI == EPI_ACT || EPI == EPI_SWIGLU)) {
-    if (!p.C2 && !p.cpk && !p.c_rows && p.N % 8 == 0 && p.ldc % 8 == 0 && ((uintptr_t)p.C & 15) == 0) {
+    if (!p.C2 && !p.cpk && (!p.c_rows || EPI == EPI_STORE) && p.N % 8 == 0 && p.ldc % 8 == 0 &&
+        ((uintptr_t)p.C & 15) == 0) {
       wait_loads_barrier<0>();                // every stage is idle (masked tail loads included)
       constexpr int PITCH = 80;               // bytes per patch row: 64 + 16 of padding
       static_assert(NT / 64 * 32 * PITCH <= STAGE, "patches fit in stage 0");
       char* patch = st0 + wave * 32 * PITCH;
       static_for<0, TM>([&](auto ic) __attribute__((always_inline)) {
         constexpr int i = decltype(ic)::value;
+        int crow[2];                          // destination rows of this lane's two stores
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int m = m0 + wm * WM + i * 32 + q * 16 + (lane >> 2);
+          crow[q] = m >= p.M ? -1 : (p.c_rows ? p.c_rows[m] : m);
+        }
         static_for<0, TNO>([&](auto jc) __attribute__((always_inline)) {
           constexpr int j = decltype(jc)::value;
           const int ncol = n0 + wn * (DUAL ? WN / 2 : WN) + j * 32;
@@ -443,9 +450,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(const GemmPar
             const int row = q * 16 + (lane >> 2);
             const int cc = (lane & 3) * 8;
             const u32x4 v = *reinterpret_cast<const u32x4*>(patch + row * PITCH + cc * 2);
-            const int m = m0 + wm * WM + i * 32 + row;
-            if (m < p.M && ncol + cc < p.N)
-              *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.C) + (int64_t)m * p.ldc + ncol + cc) = v;
+            if (crow[q] >= 0 && ncol + cc < p.N)
+              *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.C) + (int64_t)crow[q] * p.ldc + ncol + cc) = v;
           });
         });
       });

@@ -26,8 +26,10 @@
 //    gate/up GEMM reads the routed rows of x through the row table (padding
 //    rows load as zeros; an x of 2 GiB or more is first gathered into the
 //    grouped order), and the down GEMM stores each row at its (token, slot)
-//    position (padding rows are not stored).  The combine adds each token's
-//    k contiguous rows in slot order with their gates.
+//    position (padding rows are not stored), rounded to bf16 when the block's
+//    output is bf16 (an intermediate, like h) and fp32 otherwise.  The
+//    combine adds each token's k contiguous rows in slot order with their
+//    gates, in fp32.
 #include "tp_kernels.h"
 #include "tp_device.h"
 
@@ -224,9 +226,16 @@ __global__ __launch_bounds__(256) void moe_gather_kernel(const uint4* __restrict
 
 // y[t, c] = sum_j gate[t, j] * zs[t k + j, c] in slot order (fp32), over
 // the slots that were routed (pos_of >= 0); four columns per thread
-// (d % 8 == 0).
-template <typename OutT>
-__global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ zs, const int* __restrict__ pos_of,
+// (d % 8 == 0).  zs holds fp32 or bf16 rows (ZT).
+__device__ __forceinline__ float4 load4(const float* z) { return *reinterpret_cast<const float4*>(z); }
+__device__ __forceinline__ float4 load4(const uint16_t* z) {
+  const uint2 w = *reinterpret_cast<const uint2*>(z);
+  return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
+                     __uint_as_float(w.y & 0xffff0000u));
+}
+
+template <typename ZT, typename OutT>
+__global__ __launch_bounds__(256) void moe_combine_kernel(const ZT* __restrict__ zs, const int* __restrict__ pos_of,
                                                           const float* __restrict__ gate, int T, int k, int d,
                                                           OutT* __restrict__ y) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -237,7 +246,7 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
   for (int j = 0; j < k; ++j) {
     if (pos_of[(int64_t)t * k + j] < 0) continue;
     const float g = gate[(int64_t)t * k + j];
-    const float4 z = *reinterpret_cast<const float4*>(zs + ((int64_t)t * k + j) * d + c);
+    const float4 z = load4(zs + ((int64_t)t * k + j) * d + c);
     s.x += g * z.x;
     s.y += g * z.y;
     s.z += g * z.z;
@@ -277,16 +286,23 @@ hipError_t moe_group(const int* idx, int T, int E, int k, const void* x, int d, 
   return hipGetLastError();
 }
 
-hipError_t moe_combine(const float* zs, const int* pos_of, const float* gate, int T, int k, int d, void* y,
-                       bool out_f32, hipStream_t s) {
+hipError_t moe_combine(const void* zs, bool zs_f32, const int* pos_of, const float* gate, int T, int k, int d,
+                       void* y, bool out_f32, hipStream_t s) {
   const int64_t n = (int64_t)T * (d / 4);
   if (n == 0) return hipSuccess;
-  if (out_f32)
-    hipLaunchKernelGGL(moe_combine_kernel<float>, dim3(blocks(n, 256)), dim3(256), 0, s, zs, pos_of, gate, T, k, d,
-                       reinterpret_cast<float*>(y));
+  const dim3 grid(blocks(n, 256));
+  if (zs_f32 && out_f32)
+    hipLaunchKernelGGL((moe_combine_kernel<float, float>), grid, dim3(256), 0, s, reinterpret_cast<const float*>(zs),
+                       pos_of, gate, T, k, d, reinterpret_cast<float*>(y));
+  else if (zs_f32)
+    hipLaunchKernelGGL((moe_combine_kernel<float, uint16_t>), grid, dim3(256), 0, s,
+                       reinterpret_cast<const float*>(zs), pos_of, gate, T, k, d, reinterpret_cast<uint16_t*>(y));
+  else if (out_f32)
+    hipLaunchKernelGGL((moe_combine_kernel<uint16_t, float>), grid, dim3(256), 0, s,
+                       reinterpret_cast<const uint16_t*>(zs), pos_of, gate, T, k, d, reinterpret_cast<float*>(y));
   else
-    hipLaunchKernelGGL(moe_combine_kernel<uint16_t>, dim3(blocks(n, 256)), dim3(256), 0, s, zs, pos_of, gate, T, k, d,
-                       reinterpret_cast<uint16_t*>(y));
+    hipLaunchKernelGGL((moe_combine_kernel<uint16_t, uint16_t>), grid, dim3(256), 0, s,
+                       reinterpret_cast<const uint16_t*>(zs), pos_of, gate, T, k, d, reinterpret_cast<uint16_t*>(y));
   return hipGetLastError();
 }
 

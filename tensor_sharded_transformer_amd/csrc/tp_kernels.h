@@ -170,8 +170,8 @@ hipError_t moe_route(const float* logits, int T, int E, int k, int* idx, float* 
 // (xs == nullptr: no gathered copy of x, the GEMM reads x through src_row)
 hipError_t moe_group(const int* idx, int T, int E, int k, const void* x, int d, int rows, int n_tiles, int* offsets,
                      int* cursors, int* tile_expert, int* src_row, int* dst_slot, int* pos_of, void* xs, hipStream_t s);
-hipError_t moe_combine(const float* zs, const int* pos_of, const float* gate, int T, int k, int d, void* y,
-                       bool out_f32, hipStream_t s);
+hipError_t moe_combine(const void* zs, bool zs_f32, const int* pos_of, const float* gate, int T, int k, int d,
+                       void* y, bool out_f32, hipStream_t s);
 
 // Local grouped-query attention over a rank's heads: qkv (T, (n_q + 2 n_kv)
 // * 128) bf16 rows [Q | K | V], out (T, n_q * 128) bf16; both 16-byte
