@@ -38,6 +38,22 @@ namespace {
 
 constexpr int SCATTER_PER = 512;  // routed slots per scatter workgroup
 
+// (bv, be) <- the better of itself and (ov, oe): larger value, then lower index.
+__device__ __forceinline__ void take(float& bv, int& be, float ov, int oe) {
+  if (ov > bv || (ov == bv && oe < be)) {
+    bv = ov;
+    be = oe;
+  }
+}
+
+// take() with the partner lane's pair read through a DPP permutation.
+template <int CTRL>
+__device__ __forceinline__ void dpp_take(float& bv, int& be) {
+  const float ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(bv), CTRL, 0xF, 0xF, false));
+  const int oe = __builtin_amdgcn_update_dpp(0, be, CTRL, 0xF, 0xF, false);
+  take(bv, be, ov, oe);
+}
+
 // One wave per token: lane l holds logits l, l + 64, ... (a NaN logit ranks
 // as -inf); each of the k passes takes the wave's arg-max (larger value, then
 // lower index) and removes it.
@@ -73,15 +89,16 @@ __global__ __launch_bounds__(256) void moe_route_kernel(const float* __restrict_
         be = lane + 64 * q;
       }
     }
+    // butterfly over the wave: every step pairs each lane with a partner
+    // whose group has not been merged yet, so all lanes end with the same
+    // (value, index); the first four steps are DPP lane permutations (xor 1
+    // and xor 2 inside quads, then the half-row and row mirrors)
+    dpp_take<0xB1>(bv, be);   // quad_perm [1, 0, 3, 2]
+    dpp_take<0x4E>(bv, be);   // quad_perm [2, 3, 0, 1]
+    dpp_take<0x141>(bv, be);  // row_half_mirror
+    dpp_take<0x140>(bv, be);  // row_mirror
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off);
-      const int oe = __shfl_xor(be, off);
-      if (ov > bv || (ov == bv && oe < be)) {
-        bv = ov;
-        be = oe;
-      }
-    }
+    for (int off = 16; off <= 32; off <<= 1) take(bv, be, __shfl_xor(bv, off), __shfl_xor(be, off));
     if (lane == j) {
       my_val = bv;
       my_sel = be;
