@@ -290,10 +290,10 @@ tp_status tp_partial_sum(const void* const* z, int p, const void* bias, void* y,
                          int64_t N, tp_dtype in_dtype, tp_dtype out_dtype, tp_stream stream);
 
 /* Sequence-parallel boundary, one rank's share: with sequence parallelism the
- * block's all-reduce becomes a reduce-scatter + all-gather ([KL] "With
- * Sequence Parallelism ... each AllReduce becomes a ReduceScatter +
- * AllGather"), and the summed output feeds the residual add and the following
- * normalization ([FFN] "One collective").  Rank `rank` owns rows
+ * block's all-reduce is replaced by a reduce-scatter followed by an
+ * all-gather of the same bytes ([KS] "Where the 320 comes from", the
+ * sequence-parallel paragraph), and the summed output feeds the residual add
+ * and the following normalization ([FFN] "One collective").  Rank `rank` owns rows
  * [rank*T/p, (rank+1)*T/p) of the T x N partials; for each owned row r (row
  * R = rank*T/p + r of the partials):
  *   s[r]            = residual_in[r] + sum_i z[i][R] (ascending i) + bias     (fp32)

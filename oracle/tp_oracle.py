@@ -18,6 +18,8 @@ Sources (the web pages this method is described on):
          bookkeeping), fifth paragraph (KV heads bound the TP width).
   [KS]   "Why Tensor Parallelism has to stay inside the scale-up domain" -
          "What is Tensor Parallel" (h=2, d_ff=3 worked example),
+         "Where the 320 comes from" (sequence parallelism: reduce-scatter
+         + all-gather in place of each all-reduce),
          "What happens if TP leaves the node" (6 x params x tokens).
   [FFN]  "How does tensor parallelism split a transformer feed-forward block's
          two matmuls across devices?" - "The shape of the block",
@@ -256,9 +258,10 @@ def partial_sum(zs: Sequence[np.ndarray], bias=None) -> np.ndarray:
 def rs_residual_rmsnorm(zs: Sequence[np.ndarray], rank: int, residual, norm_w, eps: float, bias=None):
     """One rank's share of the sequence-parallel block boundary.
 
-    [KL] sequence-parallelism paragraph (with sequence parallelism each
-    all-reduce becomes a reduce-scatter + all-gather: rank `rank` ends up
-    with the sum over its T/p contiguous rows only) and [FFN] "One
+    [KS] "Where the 320 comes from", sequence-parallel paragraph (with
+    sequence parallelism every all-reduce is split into a reduce-scatter and
+    an all-gather: after the reduce-scatter rank `rank` holds the sum over
+    its T/p contiguous rows only) and [FFN] "One
     collective" (the summed output goes to the residual add and the
     following normalization).  The normalization is read as RMSNorm with a
     learned scale (the pages name a Llama-style block but not the norm):
@@ -413,8 +416,12 @@ def linear_shard_bwd(x, w, dy) -> Dict[str, np.ndarray]:
 def moe_route(logits, k: int) -> Tuple[np.ndarray, np.ndarray]:
     """(idx (T, k) int, gate (T, k)) from router logits (T, E): the k largest
     softmax probabilities per row in descending order (equal logits: lower
-    expert index first), renormalised over the chosen k."""
+    expert index first), renormalised over the chosen k.  A NaN logit ranks
+    as -inf (a NaN has no place in the order; treating it as the least
+    likely expert keeps the ranking total), so it ties with -inf logits and
+    those ties also go to the lower index."""
     lg = to64(logits)
+    lg = np.where(np.isnan(lg), -np.inf, lg)
     T, E = lg.shape
     if not 1 <= k <= E:
         raise ValueError("k must be in 1..E")

@@ -163,6 +163,70 @@ def test_column_bias_slices():
                                    full[:, s:s + n], rtol=1e-13, atol=1e-13)
 
 
+# Hand values for the column-parallel bias (each shard adds its own slice of
+# the bias BEFORE the activation, so h_i stays a genuine slice of h):
+# x = [1, 2] through the worked example's A gives x A = [1, 2, 3]; with
+# b = [-2, -1, -4] the pre-activations are [-1, 1, -1].  Adding the bias after
+# the activation would give relu(x A) + b = [-1, 1, -1] instead of [0, 1, 0].
+# Phi(-1) = 0.158655253931457051 (standard normal CDF), so gelu(-1) = -Phi(-1)
+# and gelu(1) = 1 - Phi(-1).
+_PHI_M1 = 0.158655253931457051
+_BIAS_HAND = {"relu": [0.0, 1.0, 0.0],
+              "gelu": [-_PHI_M1, 1.0 - _PHI_M1, -_PHI_M1],
+              "none": [-1.0, 1.0, -1.0]}
+
+
+def _column_bias_pin_error():
+    """Largest deviation of the oracle's column-parallel linear (bf16-style and
+    fp8 weights) from the hand values above, shard by shard (TP = 3, one column
+    and one bias entry per shard)."""
+    tpo = O.tp_oracle
+    x = np.array([[1.0, 2.0]])
+    a = np.array([[1.0, 0.0, 1.0], [0.0, 1.0, 1.0]])
+    b = np.array([-2.0, -1.0, -4.0])
+    # fp8 weights: code 0x40 is 2.0; with a column scale of 0.5 it is 1.0 again
+    q = np.where(a > 0, 0x40, 0x00)
+    sc = np.full(3, 0.5)
+    err = 0.0
+    for act, want in _BIAS_HAND.items():
+        for i in range(3):
+            s, n = O.shard_range(3, 3, i)
+            got = tpo.col_linear(x, a[:, s:s + n], bias=b[s:s + n], act=act)
+            got8 = tpo.col_linear_fp8(x, q[:, s:s + n], sc[s:s + n], bias=b[s:s + n], act=act)
+            err = max(err, float(np.max(np.abs(got - want[i]))), float(np.max(np.abs(got8 - want[i]))))
+    return err
+
+
+def test_column_bias_hand_values():
+    assert _column_bias_pin_error() <= 1e-15
+
+
+def test_planted_bias_after_activation_is_caught(monkeypatch):
+    """Adding the column bias after the activation must fail the hand values."""
+    tpo = O.tp_oracle
+
+    def wrong(x, w, w_up=None, bias=None, act="none"):
+        h = tpo.act_apply(tpo.matmul(x, w), act)
+        return h + O.to64(bias)[None, :] if bias is not None else h
+
+    monkeypatch.setattr(tpo, "col_linear", wrong)
+    assert _column_bias_pin_error() > 0.5
+
+
+def test_planted_fp8_scale_after_bias_is_caught(monkeypatch):
+    """Scaling the fp8 column sums after the bias is added must fail too."""
+    tpo = O.tp_oracle
+
+    def wrong(x, wq, scale, wq_up=None, scale_up=None, bias=None, act="none"):
+        a = tpo.matmul(x, tpo.e4m3_decode(wq))
+        if bias is not None:
+            a = a + O.to64(bias)[None, :]
+        return tpo.act_apply(a * O.to64(scale)[None, :], act)
+
+    monkeypatch.setattr(tpo, "col_linear_fp8", wrong)
+    assert _column_bias_pin_error() > 0.1
+
+
 def test_row_then_column_needs_a_reduction_first():
     """Common failure: splitting the first matmul by rows yields partial sums,
     and the nonlinearity does not commute with the sum."""
@@ -567,6 +631,17 @@ def test_moe_route_hand_values():
     np.testing.assert_array_equal(idx, [[1, 2], [0, 1]])            # equal logits: lower index first
     np.testing.assert_allclose(gate, [[0.5, 0.5], [math.e ** 2 / (math.e ** 2 + 1), 1 / (math.e ** 2 + 1)]],
                                rtol=1e-14)
+
+
+def test_moe_route_nan_and_infinite_logits():
+    """A NaN logit ranks as -inf: below every finite logit, tied with -inf
+    (lower index first), and an expert picked at -inf gets gate exp(-inf) = 0."""
+    nan, inf = float("nan"), float("inf")
+    idx, gate = O.moe_route(np.array([[nan, 0.0, -inf, 1.0, nan],
+                                      [-inf, nan, 2.0, -inf, 2.0]]), 4)
+    np.testing.assert_array_equal(idx, [[3, 1, 0, 2], [2, 4, 0, 1]])
+    e = math.e
+    np.testing.assert_allclose(gate, [[e / (e + 1), 1 / (e + 1), 0.0, 0.0], [0.5, 0.5, 0.0, 0.0]], rtol=1e-14)
 
 
 def test_moe_route_all_experts_is_the_softmax():
