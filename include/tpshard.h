@@ -141,6 +141,28 @@ tp_status tp_mlp_shard_fwd(const void* x, const void* w1_i, const void* w_up_i, 
                            int64_t ff_i, tp_dtype dtype, tp_dtype out_dtype, tp_act act,
                            tp_stream stream);
 
+/* Bytes of the static device scratch behind tp_mlp_shard_fwd_noalloc (per GPU). */
+#define TP_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* tp_mlp_shard_fwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops
+ * and harnesses that forbid hipMalloc.  Same arguments (minus ws/ws_bytes),
+ * checks and results as tp_mlp_shard_fwd, computed by the same kernels; the
+ * scratch those kernels use (split-K arrival counters and partials, h, the
+ * packed activations) lives in a static device array of
+ * TP_NOALLOC_SCRATCH_BYTES (32 MiB) that every GPU the library runs on holds
+ * until the process ends.  Sizes whose tp_mlp_shard_fwd_workspace exceeds it
+ * return TP_ERR_WORKSPACE before any launch.  The first call on a device
+ * looks up the array's device address (with that device current) and clears
+ * its counter region with a fill kernel on `stream`; no call allocates (no
+ * hipMalloc, hipFree or allocating library routine).  Every call on a GPU
+ * shares that GPU's array and leaves its counters zero: calls that overlap on
+ * one GPU (other streams or threads) race, so the caller orders them. */
+tp_status tp_mlp_shard_fwd_noalloc(const void* x, const void* w1_i, const void* w_up_i,
+                                   const void* w2_i, void* y_i, void* saved, int64_t T, int64_t d,
+                                   int64_t ff_i, tp_dtype dtype, tp_dtype out_dtype, tp_act act,
+                                   tp_stream stream);
+
 /* Workspace (bytes) tp_mlp_shard_bwd needs (same zero-fill rule as forward). */
 size_t tp_mlp_shard_bwd_workspace(int64_t T, int64_t d, int64_t ff_i, tp_dtype dtype, tp_act act);
 

@@ -17,6 +17,7 @@ import torch
 from . import build as _build
 
 TP_BF16, TP_F32 = 0, 1
+NOALLOC_SCRATCH_BYTES = 32 << 20   # TP_NOALLOC_SCRATCH_BYTES in include/tpshard.h
 ACT = {"none": 0, "relu": 1, "gelu": 2, "swiglu": 3}
 STATUS = {0: "TP_OK", 1: "TP_ERR_NULL", 2: "TP_ERR_SHAPE", 3: "TP_ERR_DTYPE", 4: "TP_ERR_ACT",
           5: "TP_ERR_WORKSPACE", 6: "TP_ERR_UNSUPPORTED", 7: "TP_ERR_HIP"}
@@ -45,6 +46,8 @@ SIGNATURES = {
     "tp_mlp_shard_fwd_workspace": (c_sz, [c_i64, c_i64, c_i64, c_int, c_int]),
     "tp_mlp_shard_fwd": (c_int, [c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_sz, c_i64, c_i64, c_i64, c_int, c_int, c_int,
                                  c_p]),
+    "tp_mlp_shard_fwd_noalloc": (c_int, [c_p, c_p, c_p, c_p, c_p, c_p, c_i64, c_i64, c_i64, c_int, c_int, c_int,
+                                         c_p]),
     "tp_mlp_shard_bwd_workspace": (c_sz, [c_i64, c_i64, c_i64, c_int, c_int]),
     "tp_mlp_shard_bwd": (c_int, [c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_sz, c_i64, c_i64, c_i64,
                                  c_int, c_int, c_p]),
@@ -222,6 +225,23 @@ def tp_mlp_shard_fwd(x, w1_i, w_up_i, w2_i, y_i, act: str, ws: torch.Tensor, sav
     _check(load().tp_mlp_shard_fwd(_ptr(x), _ptr(w1_i), _ptr(w_up_i), _ptr(w2_i), _ptr(y_i), _ptr(saved), _ptr(ws),
                                    ws.numel() if ws is not None else 0, T, d, ff_i, _dt(x), _dt(y_i), ACT[act],
                                    _stream()))
+    return y_i
+
+
+def tp_mlp_shard_fwd_noalloc(x, w1_i, w_up_i, w2_i, y_i, act: str, saved=None):
+    """tp_mlp_shard_fwd with the library's static device scratch instead of a workspace."""
+    T, d = x.shape
+    ff_i = w1_i.shape[1]
+    _shape(w1_i, (d, ff_i), "w1_i")
+    _shape(w2_i, (ff_i, d), "w2_i")
+    _shape(y_i, (T, d), "y_i")
+    if w_up_i is not None:
+        _shape(w_up_i, (d, ff_i), "w_up_i")
+    if saved is not None:
+        _shape(saved, (T, (2 if act == "swiglu" else 1) * ff_i), "saved")
+    _dtypes(x.dtype, w1_i=w1_i, w_up_i=w_up_i, w2_i=w2_i, saved=saved)
+    _check(load().tp_mlp_shard_fwd_noalloc(_ptr(x), _ptr(w1_i), _ptr(w_up_i), _ptr(w2_i), _ptr(y_i), _ptr(saved),
+                                           T, d, ff_i, _dt(x), _dt(y_i), ACT[act], _stream()))
     return y_i
 
 
@@ -430,3 +450,4 @@ def tp_rs_residual_rmsnorm(zs: Sequence[torch.Tensor], rank: int, bias, residual
 
 def tp_workspace_init(ws: torch.Tensor):
     _check(load().tp_workspace_init(_ptr(ws), ws.numel(), _stream()))
+

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/tpshard.h"
@@ -721,31 +722,83 @@ size_t tp_mlp_shard_fwd_workspace(int64_t T, int64_t d, int64_t ff_i, tp_dtype d
   return a > b ? a : b;
 }
 
-tp_status tp_mlp_shard_fwd(const void* x, const void* w1_i, const void* w_up_i, const void* w2_i, void* y_i,
-                           void* saved, void* ws, size_t ws_bytes, int64_t T, int64_t d, int64_t ff_i, tp_dtype dtype,
-                           tp_dtype out_dtype, tp_act act, tp_stream stream) {
+}  // extern "C"
+
+namespace {
+
+// ---- allocation-free scratch ----------------------------------------------------------
+// The forward shard's scratch (split-K arrival counters and partials, h and the
+// packed activations) for callers that cannot allocate: a static device array
+// per GPU.  Host code never uses the array's name as an address (on the host it
+// is only a stand-in symbol); the device address is looked up once per device.
+constexpr size_t kNoAllocScratch = TP_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) char scratch[kNoAllocScratch];
+
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch: on the first call on a device, its address
+// (hipGetSymbolAddress with that device current) and a cleared counter region
+// (a fill kernel on `s`, ahead of the call's own launches on the same stream;
+// every call leaves the counters zero again).
+tp_status noalloc_scratch(const char* who, hipStream_t s, char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, who);
+  if (dev < 0 || dev >= kMaxDevices) return fail(TP_ERR_UNSUPPORTED, "%s: device %d out of range", who, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    e = tpk::zero_fill(ptr, CNT_RESERVE, s);
+    if (e != hipSuccess) return hip_status(e, who);
+    g_scratch_ptr[dev] = reinterpret_cast<char*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return TP_OK;
+}
+
+// The forward shard behind tp_mlp_shard_fwd (caller workspace) and
+// tp_mlp_shard_fwd_noalloc (static scratch; ws is ignored).
+tp_status mlp_shard_fwd_impl(const char* who, bool noalloc, const void* x, const void* w1_i, const void* w_up_i,
+                             const void* w2_i, void* y_i, void* saved, void* ws, size_t ws_bytes, int64_t T,
+                             int64_t d, int64_t ff_i, tp_dtype dtype, tp_dtype out_dtype, tp_act act,
+                             tp_stream stream) {
   tp_status st = check_common(dtype, act);
   if (st != TP_OK) return st;
   if (!valid_dtype(out_dtype) || (dtype == TP_F32 && out_dtype != TP_F32))
-    return fail(TP_ERR_DTYPE, "tp_mlp_shard_fwd: out_dtype must be f32 for f32 inputs, bf16 or f32 otherwise");
+    return fail(TP_ERR_DTYPE, "%s: out_dtype must be f32 for f32 inputs, bf16 or f32 otherwise", who);
   if (!dim_ok(T) || !dim_ok(d) || !dim_ok(ff_i) || !prod_ok(T, d) || !prod_ok(d, ff_i) || !prod_ok(T, 2 * ff_i))
-    return fail(TP_ERR_SHAPE, "tp_mlp_shard_fwd: sizes out of range");
+    return fail(TP_ERR_SHAPE, "%s: sizes out of range", who);
   const bool sw = act == TP_ACT_SWIGLU;
-  if (sw != (w_up_i != nullptr)) return fail(TP_ERR_ACT, "tp_mlp_shard_fwd: w_up_i must be given iff SWIGLU");
+  if (sw != (w_up_i != nullptr)) return fail(TP_ERR_ACT, "%s: w_up_i must be given iff SWIGLU", who);
   if (T == 0 || d == 0) return TP_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (ff_i == 0) {  // empty intermediate: the partial is zero (and saved is empty)
-    if (!y_i) return fail(TP_ERR_NULL, "tp_mlp_shard_fwd: null y_i");
+    if (!y_i) return fail(TP_ERR_NULL, "%s: null y_i", who);
     const size_t yb = (size_t)T * d * esize(out_dtype);
-    return hip_status(tpk::zero_fill(y_i, yb, reinterpret_cast<hipStream_t>(stream)), "tp_mlp_shard_fwd (ff_i=0)");
+    return hip_status(tpk::zero_fill(y_i, yb, s), who);
   }
-  if (!x || !w1_i || !w2_i || !y_i) return fail(TP_ERR_NULL, "tp_mlp_shard_fwd: null x, w1_i, w2_i or y_i");
+  if (!x || !w1_i || !w2_i || !y_i) return fail(TP_ERR_NULL, "%s: null x, w1_i, w2_i or y_i", who);
   const bool vec = aligned16(x) && aligned16(w1_i) && (!sw || aligned16(w_up_i)) && aligned16(w2_i) &&
                    d % 8 == 0 && ff_i % 8 == 0;
   const FwdLayout L = fwd_layout(T, d, ff_i, dtype, act, vec);
-  if (!ws) return fail(TP_ERR_WORKSPACE, "tp_mlp_shard_fwd: workspace required (%zu bytes)", L.total);
-  if (ws_bytes < L.total)
-    return fail(TP_ERR_WORKSPACE, "tp_mlp_shard_fwd: workspace of %zu bytes < %zu needed", ws_bytes, L.total);
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (noalloc) {
+    if (L.total > kNoAllocScratch)
+      return fail(TP_ERR_WORKSPACE, "%s: these sizes need %zu bytes of scratch; the static scratch holds %zu", who,
+                  L.total, kNoAllocScratch);
+    char* sp = nullptr;
+    st = noalloc_scratch(who, s, &sp);
+    if (st != TP_OK) return st;
+    ws = sp;
+    ws_bytes = kNoAllocScratch;
+  } else {
+    if (!ws) return fail(TP_ERR_WORKSPACE, "%s: workspace required (%zu bytes)", who, L.total);
+    if (ws_bytes < L.total)
+      return fail(TP_ERR_WORKSPACE, "%s: workspace of %zu bytes < %zu needed", who, ws_bytes, L.total);
+  }
   char* base = reinterpret_cast<char*>(ws);
   void* h = base + L.h_off;
 
@@ -790,9 +843,27 @@ tp_status tp_mlp_shard_fwd(const void* x, const void* w1_i, const void* w_up_i, 
   p2.apk_ready = L.fuse_pack ? 1 : 0;
 
   hipError_t e = run_gemm(dtype, p1, L.p1, sw ? tpk::GK_FWD_SWIGLU : tpk::GK_FWD_ACT, false, s);
-  if (e != hipSuccess) return hip_status(e, "tp_mlp_shard_fwd (column GEMM)");
+  if (e != hipSuccess) return hip_status(e, who);
   e = run_gemm(dtype, p2, L.p2, tpk::GK_FWD_STORE, out_dtype == TP_F32, s);
-  return hip_status(e, "tp_mlp_shard_fwd (row GEMM)");
+  return hip_status(e, who);
+}
+
+}  // namespace
+
+extern "C" {
+
+tp_status tp_mlp_shard_fwd(const void* x, const void* w1_i, const void* w_up_i, const void* w2_i, void* y_i,
+                           void* saved, void* ws, size_t ws_bytes, int64_t T, int64_t d, int64_t ff_i, tp_dtype dtype,
+                           tp_dtype out_dtype, tp_act act, tp_stream stream) {
+  return mlp_shard_fwd_impl("tp_mlp_shard_fwd", false, x, w1_i, w_up_i, w2_i, y_i, saved, ws, ws_bytes, T, d, ff_i,
+                            dtype, out_dtype, act, stream);
+}
+
+tp_status tp_mlp_shard_fwd_noalloc(const void* x, const void* w1_i, const void* w_up_i, const void* w2_i, void* y_i,
+                                   void* saved, int64_t T, int64_t d, int64_t ff_i, tp_dtype dtype,
+                                   tp_dtype out_dtype, tp_act act, tp_stream stream) {
+  return mlp_shard_fwd_impl("tp_mlp_shard_fwd_noalloc", true, x, w1_i, w_up_i, w2_i, y_i, saved, nullptr, 0, T, d,
+                            ff_i, dtype, out_dtype, act, stream);
 }
 
 // ---- MLP shard backward --------------------------------------------------------------

@@ -271,3 +271,17 @@ def test_binding_rejects_mixed_operand_dtypes():
         B.tp_gqa_attention_fwd(torch.zeros(4, 3 * 128), torch.zeros(4, 128), 1, 1, 128, True, 0.1)
     with pytest.raises(TypeError):
         B.tp_partial_sum([torch.zeros(4, 8), torch.zeros(4, 8, dtype=torch.bfloat16)], None, torch.zeros(4, 8))
+
+
+def test_mlp_shard_fwd_noalloc_rejects_sizes_beyond_its_scratch(lib):
+    """The allocation-free forward refuses shapes whose scratch exceeds its
+    static array, before it touches the device."""
+    need = tp.tp_mlp_shard_fwd_workspace(4096, 16384, 8192, tp.TP_BF16, "swiglu")
+    assert need > B.NOALLOC_SCRATCH_BYTES
+    f = lib.tp_mlp_shard_fwd_noalloc
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, None, 4096, 16384, 8192, 0, 0, 3, None) == WS
+    assert "static scratch" in lib.tp_last_error().decode()
+    # the other argument checks come first, as in tp_mlp_shard_fwd
+    assert f(FAKE, FAKE, None, FAKE, FAKE, None, 64, 64, 64, 0, 0, 3, None) == ACTE
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, None, 64, 64, 64, 1, 0, 3, None) == DTYPE
+
