@@ -2,16 +2,20 @@
 """Benchmark: one tensor-parallel rank's SwiGLU MLP shard on one MI355X.
 
 A step is one rank's shard forward of a 70B-class SwiGLU MLP at decode size
-(T=64 tokens, d=8192, ff_i=28672/8=3584, bf16): the column-parallel gate/up
-GEMM with the SwiGLU epilogue fused, then the row-parallel down GEMM writing
-the full-shape partial y_i.  Inputs are resident in HBM before timing starts;
-three distinct weight sets (528 MB) rotate so the 256 MB Infinity Cache
-cannot serve them.  The headline value is algorithmic bytes (weights + x +
-y_i) per second.
+(T=64 tokens, d=8192, ff_i=28672/8=3584, bf16): the activations rearranged
+into the matrix cores' operand order, the column-parallel gate/up GEMM with
+the SwiGLU epilogue fused, then the row-parallel down GEMM writing the
+full-shape partial y_i.  The weights are read in the packed layout they are
+rearranged into once, when a shard is loaded (tp_pack_weight; outside the
+timed region, like the fp8 strips); the same step on (in, out) row-major
+weights is a row.  Inputs are resident in HBM before timing starts; three
+distinct weight sets (528 MB) rotate so the 256 MB Infinity Cache cannot serve
+them.  The headline value is algorithmic bytes (weights + x + y_i) per second.
 
 The same JSON line carries:
-  roofline      the dominant kernel (the fused gate/up GEMM) timed alone with
-                HIP events on its stream: algorithmic bytes / launch time vs 8 TB/s;
+  roofline      the dominant kernel (the fused gate/up GEMM on packed weights)
+                launched alone on pre-packed activations and timed with HIP
+                events on its stream: algorithmic bytes / launch time vs 8 TB/s;
   rows          the other hot-path rows: prefill shard (T=4096), GQA
                 projections (T=4096 and 64), the shard backward (T=2048,
                 d=4096, ff_i=1792), the fp32 sum of partials and the
@@ -28,6 +32,7 @@ counters of the same profiling run.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -38,14 +43,21 @@ sys.path.insert(0, ROOT)
 
 METRIC = "per-rank sharded MLP TFLOP/s (prefill) & GB/s (decode), % of MFMA/HBM peak"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
-BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+BF16_PEAK_TFLOPS = 2516.6    # MI355X dense bf16 MFMA (256 CUs x 4096 flop/clk x 2.4 GHz)
+
+# HBM bytes per launch of the roofline kernel (the packed gate/up GEMM) from
+# rocprofv3 PMC (FETCH_SIZE + WRITE_SIZE, each scaled by what the same counter
+# reads for a plain copy of known size: run with --rows calib), keyed by the
+# sha256 of the kernel's source file when the counters were taken; reported
+# as null once that source has changed.
+TRAFFIC_GATE_UP = None
+TRAFFIC_SOURCE_SHA256 = None
+KERNEL_SOURCE = os.path.join(ROOT, "tensor_sharded_transformer_amd", "csrc", "gemm_packed.hip")
 
 
-# HBM bytes per launch of the fused gate/up decode kernel from rocprofv3 PMC
-# (FETCH_SIZE + WRITE_SIZE, each scaled by what the same counter reads for a
-# plain copy of known size: run with --rows calib); None once the kernel has
-# changed since the counters were taken.
-TRAFFIC_GATE_UP = 141_925_088
+def source_sha256(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
 
 
 def log(*a):
@@ -123,11 +135,14 @@ def main() -> int:
         del wt
     x = W.mlp_input(wl).to(dev)
     y = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
-    ws = tp.new_workspace(tp.tp_mlp_shard_fwd_workspace(T, d, ff_i, tp.TP_BF16, "swiglu"), dev)
+    # the packed layout of every weight set, made once (a weight-load-time step)
+    psets = [{k: tp.tp_pack_weight(v) for k, v in st.items()} for st in sets]
+    torch.cuda.synchronize()
+    ws = tp.new_workspace(tp.tp_mlp_shard_fwd_packed_workspace(T, d, ff_i, "swiglu"), dev)
 
     def step(i):
-        s = sets[i % R]
-        tp.tp_mlp_shard_fwd(x, s["w1"], s["w_up"], s["w2"], y, "swiglu", ws)
+        s = psets[i % R]
+        tp.tp_mlp_shard_fwd_packed(x, s["w1"], s["w_up"], s["w2"], y, "swiglu", ff_i, ws)
 
     for i in range(args.warmup):
         step(i)
@@ -147,27 +162,50 @@ def main() -> int:
     log(f"bench: decode shard {ms * 1e3:.1f} us/step -> {value:.0f} GB/s ({value / HBM_PEAK_GBS:.1%} of HBM); "
         f"wall {wall:.3f}s")
 
-    # ---------------- roofline: the fused gate/up GEMM alone ------------------------
+    # ---------------- roofline: the fused gate/up GEMM kernel alone -----------------
+    # one launch per call: the packed GEMM on activations packed beforehand
     h = torch.empty(T, ff_i, dtype=torch.bfloat16, device=dev)
-    ws_c = tp.new_workspace(tp.tp_col_linear_workspace(T, d, ff_i, tp.TP_BF16, "swiglu"), dev)
+    xp = tp.tp_pack_act(x)
+    ws_c = tp.new_workspace(tp.tp_linear_packed_workspace(T, d, ff_i, "swiglu"), dev)
 
     def gate_up(i):
-        s = sets[i % R]
-        tp.tp_col_linear(x, s["w1"], s["w_up"], None, h, "swiglu", ws_c)
+        s = psets[i % R]
+        tp.tp_linear_packed_gemm(xp, s["w1"], s["w_up"], None, h, "swiglu", d, ws_c)
 
     k_ms = time_gpu(gate_up, args.steps, args.warmup)
     k_bytes = (2 * d * ff_i + T * d + T * ff_i) * 2
     k_gbs = k_bytes / (k_ms * 1e-3) / 1e9
+    fresh = TRAFFIC_SOURCE_SHA256 is not None and source_sha256(KERNEL_SOURCE) == TRAFFIC_SOURCE_SHA256
     roofline = {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": TRAFFIC_GATE_UP,
-                "kernel": "gemm_decode_kernel (dual, SwiGLU epilogue): fused gate/up weight-streaming GEMM, with its activation-packing pass",
+                "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": TRAFFIC_GATE_UP if fresh else None,
+                "kernel": "packed_gemm_kernel<4, 2, true, 2, unsigned short>: fused gate/up weight-streaming "
+                          "GEMM with the SwiGLU epilogue, packed weights",
                 "algorithmic_bytes": k_bytes, "avg_launch_us": round(k_ms * 1e3, 2)}
     log(f"bench: gate/up GEMM {k_ms * 1e3:.1f} us -> {k_gbs:.0f} GB/s")
 
     rows = {}
-    want = set(["prefill", "gqa", "attn", "bwd", "fp8", "moe", "sum"]) if args.rows == "all" else (
+    want = set(["decode", "prefill", "gqa", "attn", "bwd", "fp8", "moe", "sum"]) if args.rows == "all" else (
         set() if args.rows == "none" else set(args.rows.split(",")))
     steps_r = max(10, args.steps // 2)
+
+    if "decode" in want:
+        # the down GEMM alone (packed h, packed W2) and the same step on row-major weights
+        hp = torch.empty(tp.tp_packed_act_bytes(T, ff_i), dtype=torch.uint8, device=dev)
+        tp.tp_pack_act(h, hp)
+        ws_d = tp.new_workspace(tp.tp_linear_packed_workspace(T, ff_i, d), dev)
+        t_ = time_gpu(lambda i: tp.tp_linear_packed_gemm(hp, psets[i % R]["w2"], None, None, y, "none", ff_i, ws_d),
+                      args.steps, 200)
+        b_ = (d * ff_i + T * ff_i + T * d) * 2
+        rows["decode_down_gemm_packed_T64"] = {"us": round(t_ * 1e3, 2), "GB/s": round(b_ / t_ / 1e6, 1),
+                                               "frac_hbm": round(b_ / t_ / 1e6 / HBM_PEAK_GBS, 4),
+                                               "algorithmic_bytes": b_}
+        ws_r = tp.new_workspace(tp.tp_mlp_shard_fwd_workspace(T, d, ff_i, tp.TP_BF16, "swiglu"), dev)
+        t_ = time_gpu(lambda i: tp.tp_mlp_shard_fwd(x, sets[i % R]["w1"], sets[i % R]["w_up"], sets[i % R]["w2"], y,
+                                                    "swiglu", ws_r), args.steps, 200)
+        rows["decode_shard_T64_rowmajor_weights"] = {"us": round(t_ * 1e3, 2),
+                                                     "GB/s": round(bytes_step / t_ / 1e6, 1),
+                                                     "frac_hbm": round(bytes_step / t_ / 1e6 / HBM_PEAK_GBS, 4)}
+        del hp, ws_d, ws_r
 
     if "calib" in want:
         src = torch.ones(8192, 7168, dtype=torch.bfloat16, device=dev)
@@ -304,6 +342,21 @@ def main() -> int:
             wso = tp.new_workspace(tp.tp_row_linear_partial_workspace(Tg, o_, h_, tp.TP_BF16), dev)
             tq = time_gpu(lambda i: tp.tp_col_linear(xg, wqkv[i % nset], None, None, qkv, "none", wsq), steps_r, 3)
             to = time_gpu(lambda i: tp.tp_row_linear_partial(ag, wo[i % nset], og, wso), steps_r, 3)
+            if Tg <= 64:
+                # decode size: the same projections on (in, out) row-major weights are
+                # rows of their own; the headline rows read packed weights
+                bq = (h_ * q_ + Tg * h_ + Tg * q_) * 2
+                bo = (o_ * h_ + Tg * o_ + Tg * h_) * 2
+                rows[f"gqa_qkv_T{Tg}_rowmajor_weights"] = {"us": round(tq * 1e3, 2), "GB/s": round(bq / tq / 1e6, 1)}
+                rows[f"gqa_oproj_T{Tg}_rowmajor_weights"] = {"us": round(to * 1e3, 2), "GB/s": round(bo / to / 1e6, 1)}
+                pq = [tp.tp_pack_weight(wqkv[j]) for j in range(nset)]
+                po = [tp.tp_pack_weight(wo[j]) for j in range(nset)]
+                wsq = tp.new_workspace(tp.tp_linear_packed_workspace(Tg, h_, q_), dev)
+                wso = tp.new_workspace(tp.tp_linear_packed_workspace(Tg, o_, h_), dev)
+                tq = time_gpu(lambda i: tp.tp_col_linear_packed(xg, pq[i % nset], None, None, qkv, "none", h_, q_, wsq),
+                              steps_r, 3)
+                to = time_gpu(lambda i: tp.tp_row_linear_partial_packed(ag, po[i % nset], og, h_, wso), steps_r, 3)
+                del pq, po
             if Tg > 64:
                 fq, fo = 2 * Tg * h_ * q_, 2 * Tg * o_ * h_
                 rows[f"gqa_qkv_T{Tg}"] = {"us": round(tq * 1e3, 1), "TFLOP/s": round(fq / tq / 1e9, 1),

@@ -302,6 +302,90 @@ tp_status tp_row_linear_partial_fp8(const void* x_i, const void* wq_i, const flo
                                     void* ws, size_t ws_bytes, int64_t T, int64_t K_i, int64_t N,
                                     tp_dtype out_dtype, tp_stream stream);
 
+/* ---- packed weights for decode-sized calls ---------------------------------
+ * At decode size a rank's GEMMs are bound by streaming the weight shard from
+ * HBM ([KL] fourth paragraph: one token costs the weight bytes over the HBM
+ * bandwidth).  These entry points read weights rearranged ONCE (e.g. when the
+ * shard is loaded) into the order the matrix cores consume them, so every
+ * workgroup owns 16 output columns over the whole K range and reads its
+ * operands straight into registers.  Layout of a packed (K, N) weight:
+ * 1024-byte chunks, one per (block b of 32 rows, strip s of 16 columns), in
+ * block-major order: byte 16*l + 2*j of chunk (s, b), at byte offset
+ * (b * ceil(N/16) + s) * 1024, holds W[32b + 8*(l/16) + j][16s + l%16] for
+ * l = 0..63, j = 0..7, zero outside K x N.  All activations and weights are
+ * bf16; T <= 64 (TP_ERR_SHAPE beyond: prefill-sized calls take the (in, out)
+ * row-major entry points above). */
+
+/* Bytes of a packed (K, N) weight. */
+size_t tp_packed_weight_bytes(int64_t K, int64_t N);
+
+/* w (K, N) bf16 row-major (device) -> w_packed (tp_packed_weight_bytes(K, N)
+ * bytes, device, 16-byte aligned), asynchronously on `stream`.  A pure
+ * rearrangement (bitwise).  Errors: TP_ERR_NULL, TP_ERR_SHAPE (negative
+ * sizes, unaligned w_packed), TP_ERR_HIP. */
+tp_status tp_pack_weight(const void* w, void* w_packed, int64_t K, int64_t N, tp_stream stream);
+
+/* Workspace (bytes, 16-byte aligned, zero-filled before first use like
+ * tp_mlp_shard_fwd_workspace's) of tp_col_linear_packed and
+ * tp_row_linear_partial_packed (act TP_ACT_NONE for the latter); 0 for T == 0
+ * or T > 64.  The workspace is required: it holds x rearranged into the
+ * matrix cores' operand order. */
+size_t tp_linear_packed_workspace(int64_t T, int64_t K, int64_t N, tp_act act);
+
+/* tp_col_linear with packed weights ([KL] Y_i = X W_i; [FFN] "First matmul,
+ * column-parallel", "The nonlinearity is free"): y (T, N_i) = act(x w + bias)
+ * or silu(x w) * (x w_up).  x (T, K) bf16 row-major, w_packed / w_up_packed
+ * packed (K, N_i) (w_up_packed iff SWIGLU), bias (N_i) bf16 or NULL (not with
+ * SWIGLU), y (T, N_i) bf16; all device.  Errors as tp_col_linear, plus
+ * TP_ERR_SHAPE for T > 64 and TP_ERR_WORKSPACE. */
+tp_status tp_col_linear_packed(const void* x, const void* w_packed, const void* w_up_packed,
+                               const void* bias, void* y, void* ws, size_t ws_bytes, int64_t T,
+                               int64_t K, int64_t N_i, tp_act act, tp_stream stream);
+
+/* tp_row_linear_partial with a packed weight ([KL] Z_i = X_i W_i; [FFN]
+ * "Second matmul, row-parallel"): z_i (T, N) = x_i w, never a bias.  x_i
+ * (T, K_i) bf16, w_packed packed (K_i, N), z_i (T, N) in out_dtype (bf16 or
+ * f32); all device. */
+tp_status tp_row_linear_partial_packed(const void* x_i, const void* w_packed, void* z_i, void* ws,
+                                       size_t ws_bytes, int64_t T, int64_t K_i, int64_t N,
+                                       tp_dtype out_dtype, tp_stream stream);
+
+/* Bytes of x (T, K) in the packed-activation order the packed GEMMs read:
+ * ceil(K/32) blocks of m chunks of 1024 bytes (m = 1, 2 or 4 for T <= 16,
+ * <= 32, <= 64); byte 16*l + 2*j of chunk (block b, tile i), at byte offset
+ * (b*m + i) * 1024, holds x[16i + l%16][32b + 8*(l/16) + j], zero outside
+ * T x K.  0 for T == 0 or T > 64. */
+size_t tp_packed_act_bytes(int64_t T, int64_t K);
+
+/* x (T, K) bf16 row-major -> x_packed (tp_packed_act_bytes(T, K) bytes,
+ * 16-byte aligned), all device; a pure rearrangement.  T <= 64. */
+tp_status tp_pack_act(const void* x, void* x_packed, int64_t T, int64_t K, tp_stream stream);
+
+/* The packed GEMM alone, on activations already in the packed order (from
+ * tp_pack_act, or written that way by a previous kernel): y (T, N) =
+ * act(x w + bias), silu(x w) * (x w_up) for SWIGLU, or x w for NONE without a
+ * bias (out_dtype bf16 or f32; f32 only for NONE).  One kernel launch.  ws as
+ * for tp_linear_packed_workspace(T, K, N, act). */
+tp_status tp_linear_packed_gemm(const void* x_packed, const void* w_packed, const void* w_up_packed,
+                                const void* bias, void* y, void* ws, size_t ws_bytes, int64_t T,
+                                int64_t K, int64_t N, tp_act act, tp_dtype out_dtype,
+                                tp_stream stream);
+
+/* Workspace (bytes) of tp_mlp_shard_fwd_packed (same rules as
+ * tp_linear_packed_workspace). */
+size_t tp_mlp_shard_fwd_packed_workspace(int64_t T, int64_t d, int64_t ff_i, tp_act act);
+
+/* tp_mlp_shard_fwd with packed weights ([FFN] "Column split, then row
+ * split"): y_i = act(x w1_i [, x w_up_i]) w2_i.  x (T, d) bf16, w1_packed and
+ * w_up_packed packed (d, ff_i), w2_packed packed (ff_i, d), y_i (T, d) in
+ * out_dtype; all device.  h_i stays in the workspace (bf16), written by the
+ * column GEMM's epilogue straight in the operand order the row GEMM reads.
+ * Inference only: no saved pre-activations. */
+tp_status tp_mlp_shard_fwd_packed(const void* x, const void* w1_packed, const void* w_up_packed,
+                                  const void* w2_packed, void* y_i, void* ws, size_t ws_bytes, int64_t T,
+                                  int64_t d, int64_t ff_i, tp_dtype out_dtype, tp_act act,
+                                  tp_stream stream);
+
 /* Sum of the p full-shape partials, then the bias once ([KL] Y = sum_i Z_i;
  * [FFN] "One collective"; [MLX] bias after the sum).  This is the one-GPU
  * stand-in for the group's all-reduce.  z (host array of p device pointers),

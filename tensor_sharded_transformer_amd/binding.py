@@ -65,6 +65,16 @@ SIGNATURES = {
                                      c_int, c_p]),
     "tp_col_linear_fp8": (c_int, [c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_sz, c_i64, c_i64, c_i64, c_int, c_p]),
     "tp_row_linear_partial_fp8": (c_int, [c_p, c_p, c_p, c_p, c_p, c_sz, c_i64, c_i64, c_i64, c_int, c_p]),
+    "tp_packed_weight_bytes": (c_sz, [c_i64, c_i64]),
+    "tp_pack_weight": (c_int, [c_p, c_p, c_i64, c_i64, c_p]),
+    "tp_linear_packed_workspace": (c_sz, [c_i64, c_i64, c_i64, c_int]),
+    "tp_col_linear_packed": (c_int, [c_p, c_p, c_p, c_p, c_p, c_p, c_sz, c_i64, c_i64, c_i64, c_int, c_p]),
+    "tp_row_linear_partial_packed": (c_int, [c_p, c_p, c_p, c_p, c_sz, c_i64, c_i64, c_i64, c_int, c_p]),
+    "tp_packed_act_bytes": (c_sz, [c_i64, c_i64]),
+    "tp_pack_act": (c_int, [c_p, c_p, c_i64, c_i64, c_p]),
+    "tp_linear_packed_gemm": (c_int, [c_p, c_p, c_p, c_p, c_p, c_p, c_sz, c_i64, c_i64, c_i64, c_int, c_int, c_p]),
+    "tp_mlp_shard_fwd_packed_workspace": (c_sz, [c_i64, c_i64, c_i64, c_int]),
+    "tp_mlp_shard_fwd_packed": (c_int, [c_p, c_p, c_p, c_p, c_p, c_p, c_sz, c_i64, c_i64, c_i64, c_int, c_int, c_p]),
     "tp_partial_sum": (c_int, [ctypes.POINTER(c_p), c_int, c_p, c_p, c_i64, c_i64, c_int, c_int, c_p]),
     "tp_rs_residual_rmsnorm": (c_int, [ctypes.POINTER(c_p), c_int, c_int, c_p, c_p, c_p, ctypes.c_float, c_p, c_p,
                                        c_i64, c_i64, c_int, c_int, c_p]),
@@ -451,3 +461,104 @@ def tp_rs_residual_rmsnorm(zs: Sequence[torch.Tensor], rank: int, bias, residual
 def tp_workspace_init(ws: torch.Tensor):
     _check(load().tp_workspace_init(_ptr(ws), ws.numel(), _stream()))
 
+
+# ---- packed weights (decode-sized calls) -------------------------------------------
+def tp_packed_weight_bytes(K: int, N: int) -> int:
+    return load().tp_packed_weight_bytes(K, N)
+
+
+def tp_pack_weight(w: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """(K, N) bf16 row-major -> the packed layout (a flat uint8 tensor of
+    tp_packed_weight_bytes(K, N) bytes); `out` may be given."""
+    K, N = w.shape
+    _dtypes(torch.bfloat16, w=w)
+    nbytes = tp_packed_weight_bytes(K, N)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
+    if out.numel() * out.element_size() < nbytes:
+        raise ValueError(f"out holds {out.numel() * out.element_size()} bytes < {nbytes}")
+    _check(load().tp_pack_weight(_ptr(w), _ptr(out), K, N, _stream()))
+    return out
+
+
+def tp_linear_packed_workspace(T: int, K: int, N: int, act: str = "none") -> int:
+    return load().tp_linear_packed_workspace(T, K, N, ACT[act])
+
+
+def _packed(t, K, N, name):
+    if t is not None and t.numel() * t.element_size() < tp_packed_weight_bytes(K, N):
+        raise ValueError(f"{name}: packed weight of {t.numel() * t.element_size()} bytes < "
+                         f"{tp_packed_weight_bytes(K, N)}")
+
+
+def tp_col_linear_packed(x, w_packed, w_up_packed, bias, y, act: str, K: int, N_i: int, ws: torch.Tensor):
+    T = x.shape[0]
+    _shape(x, (T, K), "x")
+    _shape(y, (T, N_i), "y")
+    _packed(w_packed, K, N_i, "w_packed")
+    _packed(w_up_packed, K, N_i, "w_up_packed")
+    if bias is not None:
+        _shape(bias, (N_i,), "bias")
+    _dtypes(torch.bfloat16, x=x, y=y, bias=bias)
+    _check(load().tp_col_linear_packed(_ptr(x), _ptr(w_packed), _ptr(w_up_packed), _ptr(bias), _ptr(y), _ptr(ws),
+                                       ws.numel() if ws is not None else 0, T, K, N_i, ACT[act], _stream()))
+    return y
+
+
+def tp_row_linear_partial_packed(x_i, w_packed, z_i, N: int, ws: torch.Tensor):
+    T, K_i = x_i.shape
+    _shape(z_i, (T, N), "z_i")
+    _packed(w_packed, K_i, N, "w_packed")
+    _dtypes(torch.bfloat16, x_i=x_i)
+    _check(load().tp_row_linear_partial_packed(_ptr(x_i), _ptr(w_packed), _ptr(z_i), _ptr(ws),
+                                               ws.numel() if ws is not None else 0, T, K_i, N, _dt(z_i), _stream()))
+    return z_i
+
+
+def tp_mlp_shard_fwd_packed_workspace(T: int, d: int, ff_i: int, act: str) -> int:
+    return load().tp_mlp_shard_fwd_packed_workspace(T, d, ff_i, ACT[act])
+
+
+def tp_mlp_shard_fwd_packed(x, w1_packed, w_up_packed, w2_packed, y_i, act: str, ff_i: int, ws: torch.Tensor):
+    T, d = x.shape
+    _shape(y_i, (T, d), "y_i")
+    _packed(w1_packed, d, ff_i, "w1_packed")
+    _packed(w_up_packed, d, ff_i, "w_up_packed")
+    _packed(w2_packed, ff_i, d, "w2_packed")
+    _dtypes(torch.bfloat16, x=x)
+    _check(load().tp_mlp_shard_fwd_packed(_ptr(x), _ptr(w1_packed), _ptr(w_up_packed), _ptr(w2_packed), _ptr(y_i),
+                                          _ptr(ws), ws.numel() if ws is not None else 0, T, d, ff_i, _dt(y_i),
+                                          ACT[act], _stream()))
+    return y_i
+
+
+def tp_packed_act_bytes(T: int, K: int) -> int:
+    return load().tp_packed_act_bytes(T, K)
+
+
+def tp_pack_act(x: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """x (T, K) bf16 -> the packed-activation bytes (flat uint8)."""
+    T, K = x.shape
+    _dtypes(torch.bfloat16, x=x)
+    nbytes = tp_packed_act_bytes(T, K)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    if out.numel() * out.element_size() < nbytes:
+        raise ValueError(f"out holds {out.numel() * out.element_size()} bytes < {nbytes}")
+    _check(load().tp_pack_act(_ptr(x), _ptr(out), T, K, _stream()))
+    return out
+
+
+def tp_linear_packed_gemm(x_packed, w_packed, w_up_packed, bias, y, act: str, K: int, ws: torch.Tensor):
+    T, N = y.shape
+    if x_packed.numel() * x_packed.element_size() < tp_packed_act_bytes(T, K):
+        raise ValueError("x_packed is smaller than the packed activations")
+    _packed(w_packed, K, N, "w_packed")
+    _packed(w_up_packed, K, N, "w_up_packed")
+    if bias is not None:
+        _shape(bias, (N,), "bias")
+        _dtypes(torch.bfloat16, bias=bias)
+    _check(load().tp_linear_packed_gemm(_ptr(x_packed), _ptr(w_packed), _ptr(w_up_packed), _ptr(bias), _ptr(y),
+                                        _ptr(ws), ws.numel() if ws is not None else 0, T, K, N, ACT[act], _dt(y),
+                                        _stream()))
+    return y

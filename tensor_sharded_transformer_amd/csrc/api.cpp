@@ -866,6 +866,260 @@ tp_status tp_mlp_shard_fwd_noalloc(const void* x, const void* w1_i, const void* 
                             ff_i, dtype, out_dtype, act, stream);
 }
 
+// ---- packed weights (decode-sized calls) ---------------------------------------------
+}  // extern "C"
+
+namespace {
+
+constexpr int64_t kPackedMaxT = 64;
+
+// Workspace of the packed-weight entry points:
+//   [ split-K counters (>= CNT_RESERVE, zero between calls) ][ packed x ][ packed h ][ split-K partials ]
+struct PackedLayout {
+  tpk::PackedPlan p1, p2;
+  size_t x_off = 0, h_off = 0, part_off = 0, total = 0;
+};
+
+size_t counter_region(size_t units) {
+  const size_t b = tpk::align_up(units * sizeof(int), 256);
+  return b > CNT_RESERVE ? b : CNT_RESERVE;
+}
+
+// One GEMM (p1 only; h_off == part_off): x (T, K) -> (T, N).
+PackedLayout packed_linear_layout(int64_t T, int64_t K, int64_t N, bool dual) {
+  PackedLayout L;
+  L.p1 = tpk::plan_packed((int)T, (int)N, (int)K, true);
+  L.x_off = counter_region(tpk::packed_units((int)T, (int)N, L.p1));
+  L.h_off = L.x_off + tpk::align_up(tpk::packed_act_bytes((int)T, (int)K), 256);
+  L.part_off = L.h_off;
+  L.total = L.part_off + tpk::align_up(tpk::packed_partial_bytes((int)T, (int)N, dual, L.p1), 256);
+  return L;
+}
+
+// The feed-forward shard: x (T, d) -> h (T, ff_i), packed -> y (T, d).
+PackedLayout packed_fwd_layout(int64_t T, int64_t d, int64_t ff_i, bool dual) {
+  PackedLayout L;
+  L.p1 = tpk::plan_packed((int)T, (int)ff_i, (int)d, true);
+  L.p2 = tpk::plan_packed((int)T, (int)d, (int)ff_i, true);
+  const size_t u1 = tpk::packed_units((int)T, (int)ff_i, L.p1), u2 = tpk::packed_units((int)T, (int)d, L.p2);
+  const size_t q1 = tpk::packed_partial_bytes((int)T, (int)ff_i, dual, L.p1);
+  const size_t q2 = tpk::packed_partial_bytes((int)T, (int)d, false, L.p2);
+  L.x_off = counter_region(u1 > u2 ? u1 : u2);
+  L.h_off = L.x_off + tpk::align_up(tpk::packed_act_bytes((int)T, (int)d), 256);
+  L.part_off = L.h_off + tpk::align_up(tpk::packed_act_bytes((int)T, (int)ff_i), 256);
+  L.total = L.part_off + tpk::align_up(q1 > q2 ? q1 : q2, 256);
+  return L;
+}
+
+tpk::PackedParams packed_params(const void* A, const void* B0, const void* B1, int64_t T, int64_t K, int64_t N,
+                                const tpk::PackedPlan& pl, char* ws, const PackedLayout& L) {
+  tpk::PackedParams p;
+  std::memset(&p, 0, sizeof p);
+  p.A = A;
+  p.B0 = B0;
+  p.B1 = B1;
+  p.M = (int)T;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.mt = tpk::packed_mt((int)T);
+  p.nkb = (int)((K + 31) / 32);
+  p.nstrips = (int)((N + 15) / 16);
+  p.splitk = pl.splitk;
+  p.counters = reinterpret_cast<int*>(ws);
+  p.partials = reinterpret_cast<float*>(ws + L.part_off);
+  return p;
+}
+
+tp_status packed_sizes_ok(const char* who, int64_t T, int64_t K, int64_t N) {
+  if (!dim_ok(T) || !dim_ok(K) || !dim_ok(N) || !prod_ok(T, K) || !prod_ok(K, N) || !prod_ok(T, N))
+    return fail(TP_ERR_SHAPE, "%s: sizes out of range", who);
+  if (T > kPackedMaxT) return fail(TP_ERR_SHAPE, "%s: packed weights serve decode sizes, T <= 64 (T=%lld)", who,
+                                   (long long)T);
+  return TP_OK;
+}
+
+tp_status packed_ws_ok(const char* who, const void* ws, size_t ws_bytes, size_t need) {
+  if (!ws) return fail(TP_ERR_WORKSPACE, "%s: workspace required (%zu bytes)", who, need);
+  if (ws_bytes < need) return fail(TP_ERR_WORKSPACE, "%s: workspace of %zu bytes < %zu needed", who, ws_bytes, need);
+  if (!aligned16(ws)) return fail(TP_ERR_WORKSPACE, "%s: workspace must be 16-byte aligned", who);
+  return TP_OK;
+}
+
+bool rows_vec16(const void* c, int64_t ld, size_t es) { return aligned16(c) && (ld * (int64_t)es) % 16 == 0; }
+
+}  // namespace
+
+extern "C" {
+
+size_t tp_packed_weight_bytes(int64_t K, int64_t N) {
+  if (!dim_ok(K) || !dim_ok(N)) return 0;
+  return tpk::packed_weight_bytes(K, N);
+}
+
+tp_status tp_pack_weight(const void* w, void* w_packed, int64_t K, int64_t N, tp_stream stream) {
+  if (!dim_ok(K) || !dim_ok(N) || !prod_ok(K, N)) return fail(TP_ERR_SHAPE, "tp_pack_weight: sizes out of range");
+  if (K == 0 || N == 0) return TP_OK;
+  if (!w || !w_packed) return fail(TP_ERR_NULL, "tp_pack_weight: null w or w_packed");
+  if (!aligned16(w_packed)) return fail(TP_ERR_SHAPE, "tp_pack_weight: w_packed must be 16-byte aligned");
+  const bool vec = aligned16(w) && N % 8 == 0;
+  return hip_status(tpk::pack_weight16(w, N, (int)K, (int)N, vec, w_packed, reinterpret_cast<hipStream_t>(stream)),
+                    "tp_pack_weight");
+}
+
+size_t tp_linear_packed_workspace(int64_t T, int64_t K, int64_t N, tp_act act) {
+  if (!valid_act(act) || !dim_ok(T) || !dim_ok(K) || !dim_ok(N) || T == 0 || T > kPackedMaxT) return 0;
+  return packed_linear_layout(T, K, N, act == TP_ACT_SWIGLU).total;
+}
+
+tp_status tp_col_linear_packed(const void* x, const void* w_packed, const void* w_up_packed, const void* bias,
+                               void* y, void* ws, size_t ws_bytes, int64_t T, int64_t K, int64_t N_i, tp_act act,
+                               tp_stream stream) {
+  const char* who = "tp_col_linear_packed";
+  if (!valid_act(act)) return fail(TP_ERR_ACT, "%s: unknown act %d", who, act);
+  tp_status st = packed_sizes_ok(who, T, K, N_i);
+  if (st != TP_OK) return st;
+  const bool sw = act == TP_ACT_SWIGLU;
+  if (sw && !w_up_packed) return fail(TP_ERR_ACT, "%s: SWIGLU needs w_up_packed", who);
+  if (!sw && w_up_packed) return fail(TP_ERR_ACT, "%s: w_up_packed is only used by SWIGLU", who);
+  if (sw && bias) return fail(TP_ERR_ACT, "%s: a bias is not defined for SWIGLU", who);
+  if (T == 0 || N_i == 0) return TP_OK;
+  if ((!x && K > 0) || (!w_packed && K > 0) || !y) return fail(TP_ERR_NULL, "%s: null x, w_packed or y", who);
+  if (!aligned16(w_packed) || (sw && !aligned16(w_up_packed)))
+    return fail(TP_ERR_SHAPE, "%s: packed weights must be 16-byte aligned", who);
+  const PackedLayout L = packed_linear_layout(T, K, N_i, sw);
+  st = packed_ws_ok(who, ws, ws_bytes, L.total);
+  if (st != TP_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* base = reinterpret_cast<char*>(ws);
+  hipError_t e = tpk::pack_act16(x, K, (int)T, (int)K, aligned16(x) && K % 8 == 0, base + L.x_off, s);
+  if (e != hipSuccess) return hip_status(e, who);
+  tpk::PackedParams p = packed_params(base + L.x_off, w_packed, sw ? w_up_packed : nullptr, T, K, N_i, L.p1, base, L);
+  p.C = y;
+  p.ldc = N_i;
+  p.vec_out = rows_vec16(y, N_i, 2);
+  p.bias = reinterpret_cast<const uint16_t*>(bias);
+  p.act = act;
+  return hip_status(tpk::gemm_packed(p, L.p1, sw ? tpk::GK_FWD_SWIGLU : tpk::GK_FWD_ACT, false, s), who);
+}
+
+tp_status tp_row_linear_partial_packed(const void* x_i, const void* w_packed, void* z_i, void* ws, size_t ws_bytes,
+                                       int64_t T, int64_t K_i, int64_t N, tp_dtype out_dtype, tp_stream stream) {
+  const char* who = "tp_row_linear_partial_packed";
+  if (!valid_dtype(out_dtype)) return fail(TP_ERR_DTYPE, "%s: unknown out_dtype", who);
+  tp_status st = packed_sizes_ok(who, T, K_i, N);
+  if (st != TP_OK) return st;
+  if (T == 0 || N == 0) return TP_OK;
+  if ((!x_i && K_i > 0) || (!w_packed && K_i > 0) || !z_i) return fail(TP_ERR_NULL, "%s: null x_i, w_packed or z_i", who);
+  if (!aligned16(w_packed)) return fail(TP_ERR_SHAPE, "%s: packed weights must be 16-byte aligned", who);
+  const PackedLayout L = packed_linear_layout(T, K_i, N, false);
+  st = packed_ws_ok(who, ws, ws_bytes, L.total);
+  if (st != TP_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* base = reinterpret_cast<char*>(ws);
+  hipError_t e = tpk::pack_act16(x_i, K_i, (int)T, (int)K_i, aligned16(x_i) && K_i % 8 == 0, base + L.x_off, s);
+  if (e != hipSuccess) return hip_status(e, who);
+  tpk::PackedParams p = packed_params(base + L.x_off, w_packed, nullptr, T, K_i, N, L.p1, base, L);
+  p.C = z_i;
+  p.ldc = N;
+  p.vec_out = rows_vec16(z_i, N, esize(out_dtype));
+  return hip_status(tpk::gemm_packed(p, L.p1, tpk::GK_FWD_STORE, out_dtype == TP_F32, s), who);
+}
+
+size_t tp_packed_act_bytes(int64_t T, int64_t K) {
+  if (!dim_ok(T) || !dim_ok(K) || T == 0 || T > kPackedMaxT) return 0;
+  return tpk::packed_act_bytes((int)T, (int)K);
+}
+
+tp_status tp_pack_act(const void* x, void* x_packed, int64_t T, int64_t K, tp_stream stream) {
+  const char* who = "tp_pack_act";
+  tp_status st = packed_sizes_ok(who, T, K, 0);
+  if (st != TP_OK) return st;
+  if (T == 0 || K == 0) return TP_OK;
+  if (!x || !x_packed) return fail(TP_ERR_NULL, "%s: null x or x_packed", who);
+  if (!aligned16(x_packed)) return fail(TP_ERR_SHAPE, "%s: x_packed must be 16-byte aligned", who);
+  return hip_status(tpk::pack_act16(x, K, (int)T, (int)K, aligned16(x) && K % 8 == 0, x_packed,
+                                    reinterpret_cast<hipStream_t>(stream)),
+                    who);
+}
+
+tp_status tp_linear_packed_gemm(const void* x_packed, const void* w_packed, const void* w_up_packed,
+                                const void* bias, void* y, void* ws, size_t ws_bytes, int64_t T, int64_t K,
+                                int64_t N, tp_act act, tp_dtype out_dtype, tp_stream stream) {
+  const char* who = "tp_linear_packed_gemm";
+  if (!valid_act(act)) return fail(TP_ERR_ACT, "%s: unknown act %d", who, act);
+  if (!valid_dtype(out_dtype)) return fail(TP_ERR_DTYPE, "%s: unknown out_dtype", who);
+  if (out_dtype == TP_F32 && act != TP_ACT_NONE)
+    return fail(TP_ERR_DTYPE, "%s: an f32 output is only written without an activation", who);
+  tp_status st = packed_sizes_ok(who, T, K, N);
+  if (st != TP_OK) return st;
+  const bool sw = act == TP_ACT_SWIGLU;
+  if (sw != (w_up_packed != nullptr)) return fail(TP_ERR_ACT, "%s: w_up_packed must be given iff SWIGLU", who);
+  if (sw && bias) return fail(TP_ERR_ACT, "%s: a bias is not defined for SWIGLU", who);
+  if (T == 0 || N == 0) return TP_OK;
+  if ((!x_packed && K > 0) || (!w_packed && K > 0) || !y)
+    return fail(TP_ERR_NULL, "%s: null x_packed, w_packed or y", who);
+  if (!aligned16(x_packed) || !aligned16(w_packed) || (sw && !aligned16(w_up_packed)))
+    return fail(TP_ERR_SHAPE, "%s: packed operands must be 16-byte aligned", who);
+  const PackedLayout L = packed_linear_layout(T, K, N, sw);
+  st = packed_ws_ok(who, ws, ws_bytes, L.total);
+  if (st != TP_OK) return st;
+  char* base = reinterpret_cast<char*>(ws);
+  tpk::PackedParams p = packed_params(x_packed, w_packed, sw ? w_up_packed : nullptr, T, K, N, L.p1, base, L);
+  p.C = y;
+  p.ldc = N;
+  p.vec_out = rows_vec16(y, N, esize(out_dtype));
+  p.bias = reinterpret_cast<const uint16_t*>(bias);
+  p.act = act;
+  const tpk::GemmKind kind = sw ? tpk::GK_FWD_SWIGLU : (act == TP_ACT_NONE && !bias ? tpk::GK_FWD_STORE : tpk::GK_FWD_ACT);
+  return hip_status(tpk::gemm_packed(p, L.p1, kind, out_dtype == TP_F32, reinterpret_cast<hipStream_t>(stream)), who);
+}
+
+size_t tp_mlp_shard_fwd_packed_workspace(int64_t T, int64_t d, int64_t ff_i, tp_act act) {
+  if (!valid_act(act) || !dim_ok(T) || !dim_ok(d) || !dim_ok(ff_i) || T == 0 || T > kPackedMaxT) return 0;
+  return packed_fwd_layout(T, d, ff_i, act == TP_ACT_SWIGLU).total;
+}
+
+tp_status tp_mlp_shard_fwd_packed(const void* x, const void* w1_packed, const void* w_up_packed,
+                                  const void* w2_packed, void* y_i, void* ws, size_t ws_bytes, int64_t T, int64_t d,
+                                  int64_t ff_i, tp_dtype out_dtype, tp_act act, tp_stream stream) {
+  const char* who = "tp_mlp_shard_fwd_packed";
+  if (!valid_act(act)) return fail(TP_ERR_ACT, "%s: unknown act %d", who, act);
+  if (!valid_dtype(out_dtype)) return fail(TP_ERR_DTYPE, "%s: unknown out_dtype", who);
+  tp_status st = packed_sizes_ok(who, T, d, ff_i);
+  if (st != TP_OK) return st;
+  const bool sw = act == TP_ACT_SWIGLU;
+  if (sw != (w_up_packed != nullptr)) return fail(TP_ERR_ACT, "%s: w_up_packed must be given iff SWIGLU", who);
+  if (T == 0 || d == 0) return TP_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (ff_i == 0) {  // empty intermediate: the partial is zero
+    if (!y_i) return fail(TP_ERR_NULL, "%s: null y_i", who);
+    return hip_status(tpk::zero_fill(y_i, (size_t)T * d * esize(out_dtype), s), who);
+  }
+  if (!x || !w1_packed || !w2_packed || !y_i) return fail(TP_ERR_NULL, "%s: null x, w1_packed, w2_packed or y_i", who);
+  if (!aligned16(w1_packed) || !aligned16(w2_packed) || (sw && !aligned16(w_up_packed)))
+    return fail(TP_ERR_SHAPE, "%s: packed weights must be 16-byte aligned", who);
+  const PackedLayout L = packed_fwd_layout(T, d, ff_i, sw);
+  st = packed_ws_ok(who, ws, ws_bytes, L.total);
+  if (st != TP_OK) return st;
+  char* base = reinterpret_cast<char*>(ws);
+  hipError_t e = tpk::pack_act16(x, d, (int)T, (int)d, aligned16(x) && d % 8 == 0, base + L.x_off, s);
+  if (e != hipSuccess) return hip_status(e, who);
+  // column GEMM: h = act(x W1_i [, x W_up_i]) straight into the row GEMM's packed activations
+  tpk::PackedParams p1 = packed_params(base + L.x_off, w1_packed, sw ? w_up_packed : nullptr, T, d, ff_i, L.p1,
+                                       base, L);
+  p1.cpk = base + L.h_off;
+  p1.cpk_mt = tpk::packed_mt((int)T);
+  p1.act = act;
+  e = tpk::gemm_packed(p1, L.p1, sw ? tpk::GK_FWD_SWIGLU : tpk::GK_FWD_ACT, false, s);
+  if (e != hipSuccess) return hip_status(e, who);
+  // row GEMM: the full-shape partial y_i = h W2_i
+  tpk::PackedParams p2 = packed_params(base + L.h_off, w2_packed, nullptr, T, ff_i, d, L.p2, base, L);
+  p2.C = y_i;
+  p2.ldc = d;
+  p2.vec_out = rows_vec16(y_i, d, esize(out_dtype));
+  return hip_status(tpk::gemm_packed(p2, L.p2, tpk::GK_FWD_STORE, out_dtype == TP_F32, s), who);
+}
+
 // ---- MLP shard backward --------------------------------------------------------------
 size_t tp_mlp_shard_bwd_workspace(int64_t T, int64_t d, int64_t ff_i, tp_dtype dtype, tp_act act) {
   if (!valid_dtype(dtype) || !valid_act(act) || !dim_ok(T) || !dim_ok(d) || !dim_ok(ff_i)) return 0;

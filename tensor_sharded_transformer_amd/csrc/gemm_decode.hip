@@ -149,7 +149,6 @@ __device__ __forceinline__ void tail_step(const GemmParams& p, int n0, int step,
 template <int MT, bool DUAL, bool F8, typename Ready>
 __device__ __forceinline__ void ring_loop(const GemmParams& p, int n0, int w_begin, int w_end, int rot_seed, int lane,
                                           char* my, f32x16 (&acc)[MT][DUAL ? 2 * NW : NW], Ready&& ready) {
-  constexpr int NF = DUAL ? 2 * NW : NW;
   const u32x4* apk = reinterpret_cast<const u32x4*>(p.apk);
   constexpr int RD = DEPTH;  // (fp8: 8 steps in flight measured no faster than 4)
   const int full_end = min(w_end, p.K0 / 16);  // steps whose weight rows all lie inside K

@@ -81,6 +81,15 @@
 #define TP_TILE_GROUP 8
 #endif
 
+// Packed-weight decode kernel: waves per workgroup and k-blocks of loads in
+// flight per wave.
+#ifndef TP_PACKED_KW
+#define TP_PACKED_KW 4
+#endif
+#ifndef TP_PACKED_DEPTH
+#define TP_PACKED_DEPTH 4
+#endif
+
 namespace tpk {
 
 constexpr int STREAM_NW = TP_STREAM_NW;
@@ -143,6 +152,44 @@ hipError_t gemm_decode(const GemmParams& p, const GemmPlan& plan, GemmKind kind,
 // The pipelined tiled kernel, for plans and operands it supports.
 bool gemm_tile_supported(const GemmParams& p, const GemmPlan& plan, GemmKind kind);
 hipError_t gemm_tile(const GemmParams& p, const GemmPlan& plan, GemmKind kind, bool out_f32, hipStream_t s);
+
+// Packed-weight decode GEMM (gemm_packed.hip): weights stored once in 1 KB
+// MFMA B-fragment chunks (16-column strips of 32-row k-blocks), activations
+// packed alike (32-column k-blocks of 16-row tiles), M <= 64.
+struct PackedParams {
+  const void* A;         // packed activations: nkb k-blocks x mt tiles
+  const void* B0;        // packed weights (nstrips strips x nkb k-blocks)
+  const void* B1;        // second packed weights (dual: gate and up), or null
+  int M, N, K;           // output rows and columns, contraction length
+  int mt;                // 16-row tiles of the packed activations
+  int nkb;               // 32-row k-blocks of both packed operands
+  int nstrips;           // 16-column strips of the weights
+  int splitk;            // workgroups along K per strip group
+  float* partials;       // split-K fp32 partial tiles
+  int* counters;         // split-K arrival counters (zero on entry, left zero)
+  void* C;               // row-major output (bf16 or f32)
+  int64_t ldc;
+  int vec_out;           // C allows 16-byte stores (aligned, ldc a multiple of 8)
+  void* cpk;             // if set: the bf16 output goes here in the packed-activation layout
+  int cpk_mt;            //   of a GEMM with this many 16-row tiles
+  const uint16_t* bias;  // per-column bias (EPI_ACT), may be null
+  int act;
+  int a_rowmajor;        // A is x (M, K) row-major with row pitch a_ld, read in fragment order
+  int64_t a_ld;          //   (16-byte aligned rows, K a multiple of 32)
+};
+struct PackedPlan {
+  int ns = 1;      // strips per workgroup
+  int splitk = 1;  // workgroups along K
+};
+int packed_mt(int M);
+PackedPlan plan_packed(int M, int N, int K, bool split_ok);
+size_t packed_act_bytes(int M, int K);
+size_t packed_units(int M, int N, const PackedPlan& pl);
+size_t packed_partial_bytes(int M, int N, bool dual, const PackedPlan& pl);
+inline size_t packed_weight_bytes(int64_t K, int64_t N) { return (size_t)((N + 15) / 16) * ((K + 31) / 32) * 1024; }
+hipError_t pack_act16(const void* x, int64_t lda, int M, int K, bool vec, void* out, hipStream_t s);
+hipError_t pack_weight16(const void* w, int64_t ldw, int K, int N, bool vec, void* out, hipStream_t s);
+hipError_t gemm_packed(const PackedParams& p, const PackedPlan& pl, GemmKind kind, bool out_f32, hipStream_t s);
 
 // fp32 (SIMT) GEMM with the same parameter block and epilogues.
 hipError_t gemm_f32(const GemmParams& p, GemmKind kind, hipStream_t s);

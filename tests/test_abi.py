@@ -285,3 +285,22 @@ def test_mlp_shard_fwd_noalloc_rejects_sizes_beyond_its_scratch(lib):
     assert f(FAKE, FAKE, None, FAKE, FAKE, None, 64, 64, 64, 0, 0, 3, None) == ACTE
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, None, 64, 64, 64, 1, 0, 3, None) == DTYPE
 
+
+def test_packed_entry_points_validation(lib):
+    """Packed-weight calls serve T <= 64 and check their arguments first."""
+    assert lib.tp_col_linear_packed(FAKE, FAKE, None, None, FAKE, FAKE, 1 << 20, 65, 64, 64, 0, None) == SHAPE
+    assert "T <= 64" in lib.tp_last_error().decode()
+    assert lib.tp_col_linear_packed(FAKE, FAKE, None, None, FAKE, FAKE, 1 << 20, 4, 64, 64, 3, None) == ACTE
+    assert lib.tp_col_linear_packed(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, 4, 64, 64, 3, None) == ACTE
+    assert lib.tp_col_linear_packed(FAKE, FAKE, None, None, FAKE, None, 0, 4, 64, 64, 0, None) == WS
+    assert lib.tp_col_linear_packed(FAKE, FAKE, None, None, FAKE, FAKE, 16, 4, 64, 64, 0, None) == WS
+    assert lib.tp_row_linear_partial_packed(FAKE, None, FAKE, FAKE, 1 << 20, 4, 64, 64, 0, None) == NULL
+    assert lib.tp_row_linear_partial_packed(FAKE, FAKE, FAKE, FAKE, 1 << 20, 4, 64, 64, 9, None) == DTYPE
+    assert lib.tp_mlp_shard_fwd_packed(FAKE, FAKE, None, FAKE, FAKE, FAKE, 1 << 20, 4, 64, 64, 0, 3, None) == ACTE
+    assert lib.tp_mlp_shard_fwd_packed(FAKE, FAKE, None, FAKE, FAKE, FAKE, 1 << 20, 100, 64, 64, 0, 1, None) == SHAPE
+    assert lib.tp_pack_weight(None, FAKE, 4, 4, None) == NULL
+    assert lib.tp_pack_weight(FAKE, ctypes.c_void_p(0x1008), 4, 4, None) == SHAPE
+    assert tp.tp_packed_weight_bytes(8192, 3584) == 224 * 256 * 1024
+    assert tp.tp_packed_weight_bytes(33, 17) == 2 * 2 * 1024
+    assert tp.tp_linear_packed_workspace(65, 64, 64) == 0
+    assert tp.tp_mlp_shard_fwd_packed_workspace(64, 8192, 3584, "swiglu") > 0

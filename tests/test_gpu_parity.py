@@ -1067,3 +1067,137 @@ def test_moe_graph_replay():
         tp.tp_moe_route(lg2, wl.k, idx2, gate2)
         tp.tp_moe_shard_fwd(x2, idx2, gate2, w1, wu, w2, y2, ws)   # the graph's workspace, eagerly
         torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# Packed weights (decode-sized calls): the layout is a pure rearrangement
+# (bitwise against the same permutation built on the CPU); the linears and the
+# feed-forward shard on packed weights against the oracle on ragged shapes
+# (T up to 64, K not a multiple of 32 or 8, N not a multiple of 16, an odd
+# number of 16-column strips) and at the 70B-class decode shape.
+# ---------------------------------------------------------------------------
+def packed_layout_cpu(w):
+    """w (K, N) -> the packed bytes: chunk (k-block b, strip s) in block-major
+    order, lane 16q + c, element j holds w[32b + 8q + j][16s + c] (zero padded)."""
+    K, N = w.shape
+    nkb, ns = (K + 31) // 32, (N + 15) // 16
+    wp = torch.zeros(nkb * 32, ns * 16, dtype=w.dtype)
+    wp[:K, :N] = w
+    t = wp.reshape(nkb, 4, 8, ns, 16).permute(0, 3, 1, 4, 2).contiguous()  # b, s, q, c, j
+    return t.reshape(-1).view(torch.uint8)
+
+
+def pk(w):
+    return tp.tp_pack_weight(cuda(w))
+
+
+@pytest.mark.parametrize("K,N", [(1, 1), (5, 17), (100, 131), (33, 48), (8192, 1280), (3584, 8192)])
+def test_pack_weight_is_the_fragment_permutation(K, N):
+    w = W.normal((K, N), 1.0, 91, K + N)
+    got = pk(w).cpu()
+    assert got.numel() == tp.tp_packed_weight_bytes(K, N)
+    assert torch.equal(got, packed_layout_cpu(w))
+
+
+@pytest.mark.parametrize("act", ["none", "relu", "gelu", "swiglu"])
+@pytest.mark.parametrize("T,K,N", [(1, 256, 48), (5, 1000, 200), (17, 100, 131), (33, 96, 16), (64, 520, 264)])
+def test_col_linear_packed_ragged(act, T, K, N):
+    seed = 3 * T + K + N
+    x = W.normal((T, K), 1.0, seed, 1)
+    w = W.normal((K, N), 0.05, seed, 2)
+    wu = W.normal((K, N), 0.05, seed, 3) if act == "swiglu" else None
+    b = W.normal((N,), 0.5, seed, 4) if act != "swiglu" else None
+    y = torch.full((T, N), 7.0, dtype=torch.bfloat16, device="cuda")
+    ws = tp.new_workspace(tp.tp_linear_packed_workspace(T, K, N, act))
+    tp.tp_col_linear_packed(cuda(x), pk(w), None if wu is None else pk(wu), None if b is None else cuda(b), y, act,
+                            K, N, ws)
+    ref = O.col_linear(O.to64(x), O.to64(w), None if wu is None else O.to64(wu), None if b is None else O.to64(b), act)
+    assert_close(y, ref, BF16_TOL, f"col_linear_packed {act}")
+
+
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+@pytest.mark.parametrize("T,K,N", [(1, 64, 16), (9, 333, 72), (40, 1024, 8192), (64, 3584, 136)])
+def test_row_linear_partial_packed(out, T, K, N):
+    seed = 5 * T + K + N
+    x = W.normal((T, K), 1.0, seed, 1)
+    w = W.normal((K, N), 0.05, seed, 2)
+    z = torch.full((T, N), 7.0, dtype=torch.bfloat16 if out == "bf16" else torch.float32, device="cuda")
+    ws = tp.new_workspace(tp.tp_linear_packed_workspace(T, K, N))
+    tp.tp_row_linear_partial_packed(cuda(x), pk(w), z, N, ws)
+    assert_close(z, O.row_linear_partial(O.to64(x), O.to64(w)), BF16_TOL, "row partial packed")
+
+
+def test_packed_split_k_qkv_decode_shape_is_deterministic():
+    """The rank's fused QKV projection at T=64 (1280 columns: 80 strips, so K
+    is split across workgroups): against the oracle, and bitwise run to run."""
+    wl = W.GQA_DECODE
+    t = W.gqa_unsharded(wl)
+    qb, ql, kb, kl = tp.tp_gqa_shard(wl.n_q, wl.n_kv, wl.head_dim, wl.p, 5)
+    wqkv = torch.cat([t["wq"][:, qb:qb + ql], t["wk"][:, kb:kb + kl], t["wv"][:, kb:kb + kl]], 1).contiguous()
+    x = cuda(t["x"])
+    wp = pk(wqkv)
+    ws = tp.new_workspace(tp.tp_linear_packed_workspace(wl.T, wl.h, 1280, "none"))
+    outs = []
+    for _ in range(2):
+        y = torch.empty(wl.T, 1280, dtype=torch.bfloat16, device="cuda")
+        outs.append(tp.tp_col_linear_packed(x, wp, None, None, y, "none", wl.h, 1280, ws))
+    assert_close(outs[0], O.matmul(O.to64(t["x"]), O.to64(wqkv)), BF16_TOL, "qkv packed")
+    assert torch.equal(outs[0], outs[1])
+
+
+@pytest.mark.parametrize("act,T,d,ff_i,out", [("swiglu", 37, 1000, 264, "bf16"), ("gelu", 5, 512, 48, "bf16"),
+                                               ("relu", 64, 256, 64, "f32"), ("none", 16, 136, 40, "bf16"),
+                                               ("swiglu", 64, 2056, 1024, "f32")])
+def test_mlp_shard_fwd_packed_ragged(act, T, d, ff_i, out):
+    seed = 11 * T + d + ff_i
+    x = W.normal((T, d), 1.0, seed, 1)
+    w1 = W.normal((d, ff_i), 0.05, seed, 2)
+    wu = W.normal((d, ff_i), 0.05, seed, 3) if act == "swiglu" else None
+    w2 = W.normal((ff_i, d), 0.05, seed, 4)
+    y = torch.full((T, d), 7.0, dtype=torch.bfloat16 if out == "bf16" else torch.float32, device="cuda")
+    ws = tp.new_workspace(tp.tp_mlp_shard_fwd_packed_workspace(T, d, ff_i, act))
+    # two calls on one workspace: nothing stale is read, the counters are left zero
+    for rep in range(2):
+        xr = x if rep == 0 else W.normal((T, d), 1.0, seed, 5)
+        tp.tp_mlp_shard_fwd_packed(cuda(xr), pk(w1), None if wu is None else pk(wu), pk(w2), y, act, ff_i, ws)
+        ref, _ = O.mlp_shard_fwd(O.to64(xr), O.to64(w1), None if wu is None else O.to64(wu), O.to64(w2), act)
+        assert_close(y, ref, BF16_TOL, f"packed shard {act} call {rep}")
+
+
+def test_mlp_shard_fwd_packed_decode_T64(rank0_weights):
+    """The 70B-class decode shard (T=64, d=8192, ff_i=3584) on packed weights,
+    every row, and bitwise run to run."""
+    w = W.DECODE
+    x = cuda(W.mlp_input(w))
+    wt = rank0_weights
+    w1p, wup, w2p = pk(wt["w1"]), pk(wt["w_up"]), pk(wt["w2"])
+    ws = tp.new_workspace(tp.tp_mlp_shard_fwd_packed_workspace(w.T, w.d, w.ff_i, "swiglu"))
+    ys = []
+    for _ in range(2):
+        y = torch.empty(w.T, w.d, dtype=torch.bfloat16, device="cuda")
+        ys.append(tp.tp_mlp_shard_fwd_packed(x, w1p, wup, w2p, y, "swiglu", w.ff_i, ws))
+    ref, _ = O.mlp_shard_fwd(O.to64(x), O.to64(wt["w1"]), O.to64(wt["w_up"]), O.to64(wt["w2"]), "swiglu")
+    _, rf, rm = O.within(ys[0], ref)
+    print(f"packed decode shard: rel_frob={rf:.3e} rel_max={rm:.3e}")
+    assert_close(ys[0], ref, BF16_TOL, "y_0 decode, packed weights")
+    assert torch.equal(ys[0], ys[1])
+
+
+@pytest.mark.parametrize("act,out", [("swiglu", "bf16"), ("none", "f32"), ("gelu", "bf16")])
+def test_linear_packed_gemm_on_prepacked_activations(act, out):
+    """tp_pack_act + tp_linear_packed_gemm give bitwise what the one-call
+    linears give (the same kernels run)."""
+    T, K, N = 48, 776, 392
+    x = cuda(W.normal((T, K), 1.0, 93, 1))
+    w = pk(W.normal((K, N), 0.05, 93, 2))
+    wu = pk(W.normal((K, N), 0.05, 93, 3)) if act == "swiglu" else None
+    xp = tp.tp_pack_act(x)
+    ws = tp.new_workspace(tp.tp_linear_packed_workspace(T, K, N, act))
+    odt = torch.bfloat16 if out == "bf16" else torch.float32
+    y = tp.tp_linear_packed_gemm(xp, w, wu, None, torch.empty(T, N, dtype=odt, device="cuda"), act, K, ws)
+    ref = torch.empty(T, N, dtype=odt, device="cuda")
+    if act == "none":
+        tp.tp_row_linear_partial_packed(x, w, ref, N, ws)
+    else:
+        tp.tp_col_linear_packed(x, w, wu, None, ref, act, K, N, ws)
+    assert torch.equal(y, ref)
