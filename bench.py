@@ -50,8 +50,8 @@ BF16_PEAK_TFLOPS = 2516.6    # MI355X dense bf16 MFMA (256 CUs x 4096 flop/clk x
 # reads for a plain copy of known size: run with --rows calib), keyed by the
 # sha256 of the kernel's source file when the counters were taken; reported
 # as null once that source has changed.
-TRAFFIC_GATE_UP = None
-TRAFFIC_SOURCE_SHA256 = None
+TRAFFIC_GATE_UP = 129_636_791
+TRAFFIC_SOURCE_SHA256 = "fcb7e7f2f481416adff7ec598fca9bf6936fd4afc4855e521dbe92d76aeaa2e1"
 KERNEL_SOURCE = os.path.join(ROOT, "tensor_sharded_transformer_amd", "csrc", "gemm_packed.hip")
 
 
