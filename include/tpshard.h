@@ -87,8 +87,11 @@ tp_status tp_col_linear(const void* x, const void* w, const void* w_up, const vo
                         tp_act act, tp_stream stream);
 
 /* Optional workspace (bytes) for tp_col_linear: with it, decode-sized calls
- * split K over more workgroups; ws may be NULL (then ws_bytes is ignored and
- * the call runs unsplit).  A non-NULL ws smaller than this is TP_ERR_WORKSPACE.
+ * (T <= 64) split K over more workgroups; ws may be NULL (then ws_bytes is
+ * ignored and the call runs unsplit: on a streaming kernel that keeps the
+ * activation slice in LDS when it fits, else on the register-staged tiled
+ * kernel; correct, but slower at decode sizes, since fewer workgroups share
+ * the weight stream).  A non-NULL ws smaller than this is TP_ERR_WORKSPACE.
  * Same zero-fill rule as tp_mlp_shard_fwd_workspace.  Returns 0 when no
  * workspace would be used. */
 size_t tp_col_linear_workspace(int64_t T, int64_t K, int64_t N_i, tp_dtype dtype, tp_act act);

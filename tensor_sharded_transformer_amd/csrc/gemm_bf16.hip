@@ -369,7 +369,7 @@ GemmPlan plan_gemm(int M, int N, int K, bool dual, bool fwd_layout, bool vec_ok,
   constexpr int CUS = 256;
   const int nsteps = (K + 15) / 16;
   const bool decode_shape = M <= STREAM_MAX_M && fwd_layout && vec_ok && N >= 8;
-  if (decode_shape && TP_DECODE && allow_split) {
+  if (decode_shape && allow_split) {
     // Decode-sized forward GEMM with a workspace: packed-activation weight
     // streaming.  Split K across workgroups (a power of two) until about one
     // workgroup per CU, keeping at least 8 k-steps per wave.
@@ -413,8 +413,7 @@ GemmPlan plan_gemm(int M, int N, int K, bool dual, bool fwd_layout, bool vec_ok,
   // runs at ~1.24 vs ~1.0 PFLOP/s, so it takes ~3.2x as long.
   const int r256 = (tiles_for(256, 256) + CUS - 1) / CUS;
   const int r128 = (tiles_for(128, 128) + CUS - 1) / CUS;
-  plan.tile = TP_TILE_COST ? (r256 * 32 < r128 * 10 ? TILE_256x256 : TILE_128x128)
-                           : (tiles_for(256, 256) >= CUS ? TILE_256x256 : TILE_128x128);
+  plan.tile = r256 * 32 < r128 * 10 ? TILE_256x256 : TILE_128x128;
   // A grid of fewer 128x128 tiles than CUs leaves each busy CU one
   // workgroup: give it 8 waves so every SIMD has two to interleave (measured
   // on the 224-tile shard-backward dh GEMM: 80 -> 68 us; a full 256-tile grid
@@ -434,7 +433,7 @@ void gemm_split_sizes(const GemmPlan& plan, int M, int N, int K, bool dual, size
     if (plan.splitk <= 1) return;
     const size_t tiles = decode_tiles(M, N);
     // split slots per tile: the plan's splits plus the slow-class strips' extra ones
-    *part_bytes = tiles * (plan.splitk + TP_DECODE_SLOW_EXTRA) * (dual ? 2 : 1) * 16 * 64 * sizeof(float);
+    *part_bytes = tiles * (plan.splitk + DECODE_SLOW_EXTRA) * (dual ? 2 : 1) * 16 * 64 * sizeof(float);
     *n_tiles = tiles;
     return;
   }
@@ -458,7 +457,7 @@ void gemm_split_sizes(const GemmPlan& plan, int M, int N, int K, bool dual, size
 hipError_t gemm_bf16(const GemmParams& p, const GemmPlan& plan, GemmKind kind, bool out_f32, hipStream_t s) {
   if (plan.kernel == KERNEL_STREAM) return gemm_stream(p, plan, kind, out_f32, s);
   if (plan.kernel == KERNEL_DECODE) return gemm_decode(p, plan, kind, out_f32, s);
-  if (TP_TILE_PIPE && gemm_tile_supported(p, plan, kind)) return gemm_tile(p, plan, kind, out_f32, s);
+  if (gemm_tile_supported(p, plan, kind)) return gemm_tile(p, plan, kind, out_f32, s);
   switch (kind) {
     case GK_FWD_STORE:
       return out_f32 ? launch_shape<true, false, false, EPI_STORE, float>(p, plan, s)

@@ -40,7 +40,7 @@ namespace {
 
 constexpr int KW = DECODE_KW;
 constexpr int NW = DECODE_NW;
-constexpr int DEPTH = TP_DECODE_DEPTH;
+constexpr int DEPTH = DECODE_DEPTH;
 
 // Packed A: fragment (step s, m-tile i) is 64 lanes x 16 bytes at
 // ((s * MT + i) * 64 + lane) * 16; lane l holds row 32i + l%32, k values
@@ -357,8 +357,8 @@ int decode_split(GemmParams& p, const GemmPlan& plan) {
   // only while the grid stays within one workgroup per CU, and for splits of
   // at most 4 (finer splits already keep the slow strips' tiles short)
   const bool extra = !p.b_fp8 && plan.splitk > 1 && plan.splitk <= 4 && ((b0 ^ b1) >> 7 & 7) == 0 && nslow > 0 &&
-                     nstrips * plan.splitk + nslow * TP_DECODE_SLOW_EXTRA <= 256;
-  p.slow_extra = extra ? TP_DECODE_SLOW_EXTRA : 0;
+                     nstrips * plan.splitk + nslow * DECODE_SLOW_EXTRA <= 256;
+  p.slow_extra = extra ? DECODE_SLOW_EXTRA : 0;
   p.splitk = plan.splitk + p.slow_extra;
   return nstrips * plan.splitk + (extra ? nslow * p.slow_extra : 0);
 }

@@ -49,8 +49,8 @@ namespace {
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int KW = TP_PACKED_KW;        // waves per workgroup
-constexpr int DEPTH = TP_PACKED_DEPTH;  // k-blocks of loads in flight per wave
+constexpr int KW = PACKED_KW;           // waves per workgroup
+constexpr int DEPTH = PACKED_DEPTH;     // k-blocks of loads in flight per wave
 constexpr int PATCH = 1280;             // bytes of a wave's store patch (16 fp32 rows of 80 bytes)
 
 // Fragments per wave that meet in LDS per reduction pass (at most two, so

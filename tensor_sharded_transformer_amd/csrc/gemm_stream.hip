@@ -165,7 +165,7 @@ size_t stream_lds_bytes(int M, int ksteps, bool dual) {
 
 template <int MT, bool DUAL, int EPI, typename OutT>
 static hipError_t launch_stream_mt(const GemmParams& p, const GemmPlan& plan, hipStream_t s) {
-  auto kern = gemm_stream_kernel<MT, STREAM_NW, DUAL, TP_STREAM_DEPTH, STREAM_CW, EPI, OutT>;
+  auto kern = gemm_stream_kernel<MT, STREAM_NW, DUAL, STREAM_DEPTH, STREAM_CW, EPI, OutT>;
   const int threads = 64 * STREAM_CW;
   const int nstrips = (p.N + STREAM_WCOLS - 1) / STREAM_WCOLS;
   const int nsteps = (p.K0 + 15) / 16;

@@ -10,16 +10,16 @@
 // Design (one workgroup of WGM x WGN waves = one BM x BN output tile):
 //  * v_mfma_f32_32x32x16_bf16; each wave owns a (BM/WGM) x (BN/WGN) block of
 //    32x32 accumulator tiles.
-//  * K advances in tiles of 32.  Operand tiles go from global memory straight
+//  * K advances in tiles of 64.  Operand tiles go from global memory straight
 //    into LDS (buffer_load_dwordx4 ... lds, no staging registers) through a
 //    ring of STAGES separate LDS arrays; the loads of tile kt+STAGES-1 are
 //    issued while tile kt feeds the MFMAs.  Because each stage is its own LDS
 //    object, the compiler orders a fragment read only after the loads into
 //    that stage, not after every load in flight.
 //  * Operands keep their memory layout in LDS.  A k-contiguous operand is a
-//    [rows][32] tile (64-byte rows) read as MFMA fragments with ds_read_b128;
+//    [rows][64] tile (128-byte rows) read as MFMA fragments with ds_read_b128;
 //    an m- or n-contiguous operand (the (in, out) weights, the transposed
-//    operands of the weight gradients) is a [32][cols] tile in sub-tiles of at
+//    operands of the weight gradients) is a [64][cols] tile in sub-tiles of at
 //    most 128 columns, read with ds_read_b64_tr_b16, which transposes 16-bit
 //    elements on the way out of LDS.  Both layouts XOR-swizzle 16-byte chunks
 //    (measured conflict-free on gfx950); the swizzle is applied on the global
@@ -41,7 +41,7 @@
 namespace tpk {
 namespace {
 
-constexpr int TBK = TP_TILE_BK;         // k per LDS stage (32 or 64)
+constexpr int TBK = TILE_BK;            // k per LDS stage
 constexpr int NSUB = TBK / 16;          // MFMA k-substeps per stage
 constexpr int KC_CHUNKS = TBK / 8;      // 16-byte chunks per k-contiguous row
 constexpr uint32_t OOB = 0x80000000u;   // buffer offset past the record bound
@@ -56,13 +56,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_at(const void* base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFFF, 0x00020000);
 }
 
-// Chunk swizzle of a k-contiguous [rows][TBK] tile: conflict-free
-// ds_read_b128 of 32 consecutive rows, one chunk each (both measured on
-// gfx950: 64-byte rows need the row bits 2-3, 128-byte rows bits 0-2 and 3).
-__device__ __forceinline__ int kc_swz(int row) {
-  if constexpr (TBK == 32) return ((row >> 2) ^ (row >> 3)) & 3;
-  else return (row ^ (row >> 3)) & 7;
-}
+// Chunk swizzle of a k-contiguous [rows][64] tile (128-byte rows):
+// conflict-free ds_read_b128 of 32 consecutive rows, one chunk each
+// (measured on gfx950: row bits 0-2 and 3).
+static_assert(TBK == 64, "the swizzles below are for 128-byte rows");
+__device__ __forceinline__ int kc_swz(int row) { return (row ^ (row >> 3)) & 7; }
 // Chunk swizzle of a [32][SW] sub-tile (SW = 128: 16 chunks per row,
 // SW = 64: 8): conflict-free ds_read_b64_tr_b16 of four k-rows x 32 columns.
 template <int SW>
@@ -269,7 +267,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(const GemmPar
   const int tiles_m = (p.M + BM - 1) / BM;
   const int tiles_n = (p.N + BNH - 1) / BNH;
   const int t = xcd_remap(blockIdx.x, gridDim.x);
-  constexpr int GROUP = TP_TILE_GROUP;
+  constexpr int GROUP = TILE_GROUP;
   const int per_group = GROUP * tiles_n;
   const int g = t / per_group;
   const int first_m = g * GROUP;
@@ -528,10 +526,10 @@ template <bool AKC, bool BKC, bool DUAL, int EPI, typename OutT>
 hipError_t launch_tile_shape(const GemmParams& p, int tile, hipStream_t s) {
   switch (tile) {
     case TILE_256x256:
-      return launch_tile<256, 256, TP_TILE_WGM_256, TP_TILE_WGN_256, TP_TILE_STAGES_256, AKC, BKC, DUAL, EPI, OutT>(p, s);
+      return launch_tile<256, 256, TILE_WGM_256, TILE_WGN_256, TILE_STAGES, AKC, BKC, DUAL, EPI, OutT>(p, s);
     case TILE_128x128:
-      return launch_tile<128, 128, TP_TILE_WGM_128, TP_TILE_WGN_128, TP_TILE_STAGES_128, AKC, BKC, DUAL, EPI, OutT>(p, s);
-    case TILE_128x128_W8: return launch_tile<128, 128, 4, 2, TP_TILE_STAGES_128, AKC, BKC, DUAL, EPI, OutT>(p, s);
+      return launch_tile<128, 128, TILE_WGM_128, TILE_WGN_128, TILE_STAGES, AKC, BKC, DUAL, EPI, OutT>(p, s);
+    case TILE_128x128_W8: return launch_tile<128, 128, 4, 2, TILE_STAGES, AKC, BKC, DUAL, EPI, OutT>(p, s);
     default: return hipErrorInvalidValue;
   }
 }

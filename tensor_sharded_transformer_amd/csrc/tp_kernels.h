@@ -6,102 +6,40 @@
 
 #include "tp_device.h"
 
-// Build-time tuning of the weight-streaming kernel: k-steps of weight loads
-// in flight per wave, 32-column fragments per wave, waves (column groups) per
-// workgroup.
-#ifndef TP_STREAM_DEPTH
-#define TP_STREAM_DEPTH 3
-#endif
-#ifndef TP_STREAM_NW
-#define TP_STREAM_NW 1
-#endif
-#ifndef TP_STREAM_CW
-#define TP_STREAM_CW 4
-#endif
-#ifndef TP_STREAM_TARGET_WGS
-#define TP_STREAM_TARGET_WGS 256
-#endif
-// Packed-activation decode kernel: waves per workgroup (each streams its own
-// K sub-range), 32-column fragments per weight matrix and workgroup, k-steps
-// of loads in flight per wave; TP_DECODE=0 keeps the LDS-slice kernel.
-#ifndef TP_DECODE
-#define TP_DECODE 1
-#endif
-#ifndef TP_DECODE_KW
-#define TP_DECODE_KW 4
-#endif
-#ifndef TP_DECODE_NW
-#define TP_DECODE_NW 2
-#endif
-#ifndef TP_DECODE_DEPTH
-#define TP_DECODE_DEPTH 4
-#endif
-// Extra K splits for the decode kernel's column strips of the slow
-// weight-address class (when split-K is on).
-#ifndef TP_DECODE_SLOW_EXTRA
-#define TP_DECODE_SLOW_EXTRA 4
-#endif
-
-// Pipelined tiled kernel (LDS-bound loads, four-stage ring) for the 256x256
-// and 128x128 tiles; TP_TILE_PIPE=0 keeps the register-staged two-stage
-// kernel for those tiles.
-#ifndef TP_TILE_BK
-#define TP_TILE_BK 64
-#endif
-#ifndef TP_TILE_STAGES_256
-#define TP_TILE_STAGES_256 2
-#endif
-#ifndef TP_TILE_STAGES_128
-#define TP_TILE_STAGES_128 2
-#endif
-#ifndef TP_TILE_PIPE
-#define TP_TILE_PIPE 1
-#endif
-// Wave grid of the 256x256 tile (waves along M x along N).
-#ifndef TP_TILE_WGM_256
-#define TP_TILE_WGM_256 2
-#endif
-#ifndef TP_TILE_WGN_256
-#define TP_TILE_WGN_256 4
-#endif
-// Wave grid of the 128x128 tile.
-#ifndef TP_TILE_WGM_128
-#define TP_TILE_WGM_128 2
-#endif
-#ifndef TP_TILE_WGN_128
-#define TP_TILE_WGN_128 2
-#endif
-// Tiled kernel: choose the tile size by estimated time (0: 256x256 whenever
-// it gives a full round).
-#ifndef TP_TILE_COST
-#define TP_TILE_COST 1
-#endif
-// M tiles per group of the tiled kernel's tile order (operand panel reuse in L2).
-#ifndef TP_TILE_GROUP
-#define TP_TILE_GROUP 8
-#endif
-
-// Packed-weight decode kernel: waves per workgroup and k-blocks of loads in
-// flight per wave.
-#ifndef TP_PACKED_KW
-#define TP_PACKED_KW 4
-#endif
-#ifndef TP_PACKED_DEPTH
-#define TP_PACKED_DEPTH 4
-#endif
-
 namespace tpk {
 
-constexpr int STREAM_NW = TP_STREAM_NW;
-constexpr int STREAM_CW = TP_STREAM_CW;
+// Weight-streaming kernel with the activation slice in LDS (decode-size calls
+// made without a workspace): k-steps of weight loads in flight per wave,
+// 32-column fragments per wave, waves (column groups) per workgroup.
+constexpr int STREAM_DEPTH = 3;
+constexpr int STREAM_NW = 1;
+constexpr int STREAM_CW = 4;
 constexpr int STREAM_WCOLS = 32 * STREAM_NW * STREAM_CW;  // output columns per workgroup
 constexpr int STREAM_TILES_PER_WG = STREAM_CW;            // split-K tiles per workgroup
-constexpr int DECODE_KW = TP_DECODE_KW;
-constexpr int DECODE_NW = TP_DECODE_NW;
-constexpr int DECODE_WCOLS = 32 * DECODE_NW;              // output columns per workgroup
 constexpr int STREAM_LDS_MAX = 160 * 1024;                // gfx950 LDS per workgroup
-constexpr int STREAM_MAX_M = 64;                          // tokens the streaming kernel serves
-constexpr int STREAM_TARGET_WGS = TP_STREAM_TARGET_WGS;   // K is split until about this many workgroups
+constexpr int STREAM_MAX_M = 64;                          // tokens the streaming kernels serve
+constexpr int STREAM_TARGET_WGS = 256;                    // K is split until about this many workgroups
+// Packed-activation decode kernel (row-major weights, a workspace given):
+// waves per workgroup (each streams its own K sub-range), 32-column fragments
+// per weight matrix and workgroup, k-steps of loads in flight per wave, and
+// the extra K splits of the column strips of the slow weight-address class.
+constexpr int DECODE_KW = 4;
+constexpr int DECODE_NW = 2;
+constexpr int DECODE_DEPTH = 4;
+constexpr int DECODE_SLOW_EXTRA = 4;
+constexpr int DECODE_WCOLS = 32 * DECODE_NW;              // output columns per workgroup
+// Pipelined tiled kernel: k per LDS stage, ring stages, wave grids (waves
+// along M x along N) of the 256x256 and 128x128 tiles, M tiles per group of
+// the tile order (operand panel reuse in L2).
+constexpr int TILE_BK = 64;
+constexpr int TILE_STAGES = 2;
+constexpr int TILE_WGM_256 = 2, TILE_WGN_256 = 4;
+constexpr int TILE_WGM_128 = 2, TILE_WGN_128 = 2;
+constexpr int TILE_GROUP = 8;
+// Packed-weight decode kernel: waves per workgroup, k-blocks of loads in
+// flight per wave.
+constexpr int PACKED_KW = 4;
+constexpr int PACKED_DEPTH = 4;
 
 // LDS bytes the streaming kernel needs for M rows and a K range of `ksteps`
 // 16-value steps.

@@ -1201,3 +1201,73 @@ def test_linear_packed_gemm_on_prepacked_activations(act, out):
     else:
         tp.tp_col_linear_packed(x, w, wu, None, ref, act, K, N, ws)
     assert torch.equal(y, ref)
+
+
+@pytest.mark.parametrize("act,K", [("swiglu", 2048), ("gelu", 1000), ("swiglu", 1000)])
+def test_decode_size_linears_without_a_workspace(act, K):
+    """Decode-size calls made without a workspace run unsplit (slower,
+    documented in the header): K=1000 on the streaming kernel with the
+    activation slice in LDS, K=2048 (slice too large) on the register-staged
+    tiled kernel; the results meet the oracle's tolerance either way."""
+    T, N = 40, 1000
+    x = W.normal((T, K), 1.0, 95, 1)
+    w = W.normal((K, N), 0.05, 95, 2)
+    wu = W.normal((K, N), 0.05, 95, 3) if act == "swiglu" else None
+    y = torch.full((T, N), 7.0, dtype=torch.bfloat16, device="cuda")
+    tp.tp_col_linear(cuda(x), cuda(w), None if wu is None else cuda(wu), None, y, act)
+    ref = O.col_linear(O.to64(x), O.to64(w), None if wu is None else O.to64(wu), None, act)
+    assert_close(y, ref, BF16_TOL, "col linear, no workspace")
+    z = torch.full((T, 1024), 7.0, dtype=torch.float32, device="cuda")
+    h = W.normal((T, N), 1.0, 95, 4)
+    w2 = W.normal((N, 1024), 0.05, 95, 5)
+    tp.tp_row_linear_partial(cuda(h), cuda(w2), z)
+    assert_close(z, O.row_linear_partial(O.to64(h), O.to64(w2)), BF16_TOL, "row partial, no workspace")
+
+
+def _at_offset(t, offset_bytes):
+    """A device copy of t whose data starts `offset_bytes` past a 4 KiB-aligned base."""
+    n = t.numel() * t.element_size()
+    buf = torch.empty(n + 8192, dtype=torch.uint8, device="cuda")
+    base = (-buf.data_ptr()) % 4096
+    view = buf[base + offset_bytes: base + offset_bytes + n].view(t.dtype).view(t.shape)
+    view.copy_(t.to("cuda"))
+    return view, buf
+
+
+def test_weight_address_class_changes_only_the_last_bits():
+    """The row-major decode kernel gives the column strips whose weight bytes
+    fall in one address class (bits 7-9 equal to 3) extra K splits, so the
+    summation order, and with it the rounding, follows the weight buffer's
+    address: the same inputs at two addresses of different classes agree to
+    fp32 rounding and both meet the oracle's tolerance, but need not be
+    bitwise equal.  The packed-weight path splits by shape only: its results
+    are bitwise independent of the address."""
+    T, d, ff = 64, 4096, 1792
+    x = W.normal((T, d), 1.0, 97, 1)
+    w1 = W.normal((d, ff), 0.02, 97, 2)
+    wu = W.normal((d, ff), 0.02, 97, 3)
+    w2 = W.normal((ff, d), 0.02, 97, 4)
+    ref, _ = O.mlp_shard_fwd(O.to64(x), O.to64(w1), O.to64(wu), O.to64(w2), "swiglu")
+    xs = cuda(x)
+    outs, outs_packed, keep = [], [], []
+    for off in (0, 3 * 128):   # weight pointer bits 7-9: class 0, then class 3
+        a1, b1 = _at_offset(w1, off)
+        au, bu = _at_offset(wu, off)
+        a2, b2 = _at_offset(w2, off)
+        keep += [b1, bu, b2]
+        assert (a1.data_ptr() >> 7) & 7 == off // 128
+        y = torch.empty(T, d, dtype=torch.bfloat16, device="cuda")
+        ws = tp.new_workspace(tp.tp_mlp_shard_fwd_workspace(T, d, ff, tp.TP_BF16, "swiglu"))
+        tp.tp_mlp_shard_fwd(xs, a1, au, a2, y, "swiglu", ws)
+        assert_close(y, ref, BF16_TOL, f"row-major weights at offset {off}")
+        outs.append(y)
+        pw = [_at_offset(tp.tp_pack_weight(a).cpu(), off) for a in (a1, au, a2)]
+        keep += [b for _, b in pw]
+        yp = torch.empty(T, d, dtype=torch.bfloat16, device="cuda")
+        wsp = tp.new_workspace(tp.tp_mlp_shard_fwd_packed_workspace(T, d, ff, "swiglu"))
+        tp.tp_mlp_shard_fwd_packed(xs, pw[0][0], pw[1][0], pw[2][0], yp, "swiglu", ff, wsp)
+        assert_close(yp, ref, BF16_TOL, f"packed weights at offset {off}")
+        outs_packed.append(yp)
+    _, rf, _ = O.within(outs[1], outs[0])
+    assert rf < 2e-3, rf           # bf16 outputs of two fp32 summation orders
+    assert torch.equal(outs_packed[0], outs_packed[1])
