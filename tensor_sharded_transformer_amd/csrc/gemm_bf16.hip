@@ -293,12 +293,11 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_bf16_kernel(const GemmPara
   if (interior) kloop(std::false_type{});
   else kloop(std::true_type{});
 
-  // ---- split-K (only the small-M tile splits K) ----------------------------
-  // Each wave's accumulators are one exchange tile; see splitk_exchange.
-  if constexpr (BM <= 64) {
-    if (p.splitk > 1) {
-      if (!splitk_exchange<TM * TN>(p, t * (NT / 64) + wave, split, lane, &acc[0][0])) return;
-    }
+  // ---- split-K ---------------------------------------------------------------
+  // Each wave's accumulators are one exchange tile; see splitk_exchange (the
+  // epilogue below has no barrier, so the waves may leave independently).
+  if (p.splitk > 1) {
+    if (!splitk_exchange<TM * TN>(p, t * (NT / 64) + wave, split, lane, &acc[0][0])) return;
   }
 
   // ---- epilogue -----------------------------------------------------------
@@ -414,12 +413,16 @@ GemmPlan plan_gemm(int M, int N, int K, bool dual, bool fwd_layout, bool vec_ok,
   const int r256 = (tiles_for(256, 256) + CUS - 1) / CUS;
   const int r128 = (tiles_for(128, 128) + CUS - 1) / CUS;
   plan.tile = r256 * 32 < r128 * 10 ? TILE_256x256 : TILE_128x128;
-  // A grid of fewer 128x128 tiles than CUs leaves each busy CU one
-  // workgroup: give it 8 waves so every SIMD has two to interleave (measured
-  // on the 224-tile shard-backward dh GEMM: 80 -> 68 us; a full 256-tile grid
-  // ran slightly slower with 8 waves, so it keeps 4).
-  if (plan.tile == TILE_128x128 && tiles_for(128, 128) < CUS) plan.tile = TILE_128x128_W8;
   plan.splitk = 1;
+  if (plan.tile == TILE_128x128 && tiles_for(128, 128) <= CUS) {
+    // At most one 128x128 tile per CU: with a workspace, split K in two so
+    // each CU runs two 4-wave workgroups (twice the loads in flight; the
+    // fp32 partial tiles meet in the workspace); without one, give the single
+    // workgroup 8 waves so every SIMD has two to interleave (measured on the
+    // 224-tile shard-backward dh GEMM: 80 -> 68 us).
+    if (allow_split && (K + 63) / 64 >= 32) plan.splitk = 2;
+    else if (tiles_for(128, 128) < CUS) plan.tile = TILE_128x128_W8;
+  }
   return plan;
 }
 
@@ -446,8 +449,10 @@ void gemm_split_sizes(const GemmPlan& plan, int M, int N, int K, bool dual, size
     *n_tiles = tiles;
     return;
   }
-  // only the 64x128 tile (4 waves) splits K; one exchange tile per wave
-  const int bm = 64, bn = 128, waves = 4;
+  // the 64x128 and 128x128 tiles (4 waves) split K: every split publishes
+  // its fp32 tile; one arrival counter per wave (the register-staged kernel
+  // takes a ticket per wave, the pipelined one per workgroup)
+  const int bm = plan.tile == TILE_64x128 ? 64 : 128, bn = 128, waves = 4;
   const int bnh = dual ? bn / 2 : bn;
   const size_t tiles = (size_t)((M + bm - 1) / bm) * ((N + bnh - 1) / bnh);
   *part_bytes = tiles * plan.splitk * (size_t)bm * bn * sizeof(float);

@@ -263,10 +263,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(const GemmPar
   const int wm = wave / WGN;
   const int wn = wave % WGN;
 
-  // ---- tile assignment (XCD-contiguous, M-grouped) -------------------------
+  // ---- tile and K-split assignment (XCD-contiguous, M-grouped) -------------
   const int tiles_m = (p.M + BM - 1) / BM;
   const int tiles_n = (p.N + BNH - 1) / BNH;
-  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int split = id / (tiles_m * tiles_n);
+  const int t = id - split * (tiles_m * tiles_n);
   constexpr int GROUP = TILE_GROUP;
   const int per_group = GROUP * tiles_n;
   const int g = t / per_group;
@@ -278,6 +280,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(const GemmPar
 
   const int nk0 = (p.K0 + TBK - 1) / TBK;
   const int nk = nk0 + (p.K1 + TBK - 1) / TBK;
+  // this split's k-tiles (both K segments counted together)
+  const int kt_begin = (int)((int64_t)nk * split / p.splitk);
+  const int kt_end = (int)((int64_t)nk * (split + 1) / p.splitk);
 
   // grouped mode: this M tile's expert selects the weights (a tile with no
   // routed rows has nothing to do; the whole workgroup leaves together)
@@ -306,7 +311,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(const GemmPar
   auto issue = [&](int kt, char* st) {
     const bool s1 = kt >= nk0;
     const int k0 = (s1 ? kt - nk0 : kt) * TBK;
-    const int kvalid = kt >= nk ? 0 : (s1 ? p.K1 : p.K0) - k0;
+    const int kvalid = kt >= kt_end ? 0 : (s1 ? p.K1 : p.K0) - k0;
     const uint16_t* a = reinterpret_cast<const uint16_t*>(s1 ? p.A1 : p.A0);
     const uint16_t* b0 = s1 ? gB1 : gB0;
     const uint16_t* b1 = gB1;
@@ -366,7 +371,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(const GemmPar
   // The loop is unrolled by STAGES so every stage array is a constant.
   static_for<0, STAGES - 1>([&](auto ic) __attribute__((always_inline)) {
     constexpr int i = decltype(ic)::value;
-    issue(i, stage(ic));
+    issue(kt_begin + i, stage(ic));
   });
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -379,11 +384,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(const GemmPar
   wait_loads_barrier<(STAGES - 2) * LPS>();
   constexpr int NMF = TM * TN;                                  // MFMAs per block
   constexpr int NRD = TM * (AKC ? 1 : 2) + TN * (BKC ? 1 : 2);  // LDS reads per block
-  const int nk_pad = (nk + STAGES - 1) / STAGES * STAGES;
+  const int nk_pad = (kt_end - kt_begin + STAGES - 1) / STAGES * STAGES;
   for (int kt0 = 0; kt0 < nk_pad; kt0 += STAGES) {
     static_for<0, STAGES>([&](auto uc) __attribute__((always_inline)) {
       constexpr int u = decltype(uc)::value;
-      const int kt = kt0 + u;
+      const int kt = kt_begin + kt0 + u;
       const char* cur = stage(uc);
       issue(kt + STAGES - 1, stage(std::integral_constant<int, u + STAGES - 1>{}));
       // block b: MFMAs of the substep before b (block 0: the previous tile's
@@ -399,6 +404,50 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(const GemmPar
     });
   }
   mma(1);
+
+  // ---- split-K ---------------------------------------------------------------
+  // Every wave publishes its accumulators ([split][acc][quarter][lane][4], 1 KB
+  // per wave instruction); the workgroup takes one arrival ticket for its
+  // tile, so all its waves either leave together or, in the last split to
+  // arrive, add the splits in split order and go on to the epilogue.
+  if (p.splitk > 1) {
+    constexpr int NACC = TM * TN;
+    constexpr uint32_t WAVE_BYTES = NACC * 16 * 64 * 4;
+    __shared__ int ticket;
+    const float* base = p.partials + ((int64_t)t * (NT / 64) + wave) * p.splitk * (WAVE_BYTES / 4);
+    const __amdgpu_buffer_rsrc_t r = splitk_rsrc(base, WAVE_BYTES * (uint32_t)p.splitk);
+    static_for<0, NACC>([&](auto ac) __attribute__((always_inline)) {
+      constexpr int a = decltype(ac)::value;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4v v = {acc[a / TN][a % TN][4 * q], acc[a / TN][a % TN][4 * q + 1], acc[a / TN][a % TN][4 * q + 2],
+                          acc[a / TN][a % TN][4 * q + 3]};
+        splitk_store(r, split * WAVE_BYTES + ((a * 4 + q) * 64 + lane) * 16, v);
+      }
+    });
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's partial stores are complete
+    __syncthreads();
+    if (tid == 0) ticket = __hip_atomic_fetch_add(&p.counters[t], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (ticket != p.splitk - 1) return;
+    static_for<0, NACC>([&](auto ac) __attribute__((always_inline)) {
+      constexpr int a = decltype(ac)::value;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a / TN][a % TN][e] = 0.0f;
+    });
+    for (int sp = 0; sp < p.splitk; ++sp) {
+      static_for<0, NACC>([&](auto ac) __attribute__((always_inline)) {
+        constexpr int a = decltype(ac)::value;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4v v = splitk_load(r, sp * WAVE_BYTES + ((a * 4 + q) * 64 + lane) * 16);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[a / TN][a % TN][4 * q + e] += v[e];
+        }
+      });
+    }
+    if (tid == 0) __hip_atomic_store(&p.counters[t], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 
   // ---- epilogue --------------------------------------------------------------
   // Accumulator register r of tile (i, j) is row 8(r/4) + 4(lane/32) + r%4,
@@ -450,6 +499,88 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(const GemmPar
             const u32x4 v = *reinterpret_cast<const u32x4*>(patch + row * PITCH + cc * 2);
             if (crow[q] >= 0 && ncol + cc < p.N)
               *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.C) + (int64_t)crow[q] * p.ldc + ncol + cc) = v;
+          });
+        });
+      });
+      return;
+    }
+  }
+  // Backward activation epilogues (dh times the activation's derivative, read
+  // from the saved pre-activations, plus the recomputed activation): the
+  // fp32 accumulators go through a per-wave LDS patch 16 rows at a time, so
+  // each lane owns 8 consecutive columns of one row and every side load and
+  // output store is 16 bytes (instead of five 2-byte accesses per element).
+  if constexpr (std::is_same<OutT, uint16_t>::value && !DUAL && (EPI == EPI_SWIGLU_BWD || EPI == EPI_ACT_BWD)) {
+    const bool two_sides = EPI == EPI_SWIGLU_BWD;
+    if (!p.c_rows && p.N % 8 == 0 && p.ldc % 8 == 0 && p.ldc3 % 8 == 0 && p.lds % 8 == 0 &&
+        (!two_sides || p.ldc2 % 8 == 0) &&
+        (((uintptr_t)p.C | (uintptr_t)p.C3 | (uintptr_t)p.S0 | (two_sides ? (uintptr_t)p.C2 | (uintptr_t)p.S1 : 0)) &
+         15) == 0) {
+      wait_loads_barrier<0>();
+      constexpr int PITCH = 144;              // 32 fp32 columns + 16 bytes of padding
+      static_assert(NT / 64 * 16 * PITCH <= STAGE, "patches fit in stage 0");
+      char* patch = st0 + wave * 16 * PITCH;
+      const int prow = lane >> 2;             // this lane's patch row
+      const int pcol = (lane & 3) * 8;        // and first of its 8 columns
+      static_for<0, TM>([&](auto ic) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
+        static_for<0, TN>([&](auto jc) __attribute__((always_inline)) {
+          constexpr int j = decltype(jc)::value;
+          const int n = n0 + wn * WN + j * 32 + pcol;
+          static_for<0, 2>([&](auto hc) __attribute__((always_inline)) {
+            constexpr int h = decltype(hc)::value;
+            // accumulator registers 8h .. 8h+7 are rows 16h .. 16h+15 of the fragment
+            static_for<0, 8>([&](auto rc) __attribute__((always_inline)) {
+              constexpr int r = 8 * h + decltype(rc)::value;
+              const int row = 8 * ((r >> 2) & 1) + 4 * (lane >> 5) + (r & 3);
+              *reinterpret_cast<float*>(patch + row * PITCH + (lane & 31) * 4) = acc[i][j][r];
+            });
+            // one wave's LDS operations complete in order: the reads see the writes
+            const u32x4 d0 = *reinterpret_cast<const u32x4*>(patch + prow * PITCH + pcol * 4);
+            const u32x4 d1 = *reinterpret_cast<const u32x4*>(patch + prow * PITCH + pcol * 4 + 16);
+            const int m = m0 + wm * WM + i * 32 + 16 * h + prow;
+            if (m < p.M && n < p.N) {
+              float dh[8];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                dh[e] = __uint_as_float(d0[e]);
+                dh[4 + e] = __uint_as_float(d1[e]);
+              }
+              const u32x4 sa = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.S0) + (int64_t)m * p.lds + n);
+              u32x4 sb = {0, 0, 0, 0};
+              if (two_sides) sb = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(p.S1) + (int64_t)m * p.lds + n);
+              u32x4 o0, o2, o3;
+#pragma unroll
+              for (int w = 0; w < 4; ++w) {
+                uint32_t r0 = 0, r2 = 0, r3 = 0;
+#pragma unroll
+                for (int hw = 0; hw < 2; ++hw) {
+                  const int e = 2 * w + hw;
+                  const float a = bf2f((uint16_t)(sa[w] >> (16 * hw)));
+                  float v0, v2 = 0.0f, v3;
+                  if constexpr (EPI == EPI_SWIGLU_BWD) {
+                    const float u = bf2f((uint16_t)(sb[w] >> (16 * hw)));
+                    const float s = sigmoidf_(a);
+                    const float sg = a * s;
+                    v0 = dh[e] * u * (s + sg * (1.0f - s));
+                    v2 = dh[e] * sg;
+                    v3 = sg * u;
+                  } else {
+                    v0 = dh[e] * act_grad(p.act, a);
+                    v3 = act_fwd(p.act, a);
+                  }
+                  r0 |= (uint32_t)f2bf(v0) << (16 * hw);
+                  r2 |= (uint32_t)f2bf(v2) << (16 * hw);
+                  r3 |= (uint32_t)f2bf(v3) << (16 * hw);
+                }
+                o0[w] = r0;
+                o2[w] = r2;
+                o3[w] = r3;
+              }
+              *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.C) + (int64_t)m * p.ldc + n) = o0;
+              if (two_sides) *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.C2) + (int64_t)m * p.ldc2 + n) = o2;
+              *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.C3) + (int64_t)m * p.ldc3 + n) = o3;
+            }
           });
         });
       });
@@ -516,7 +647,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(const GemmPar
 template <int BM, int BN, int WGM, int WGN, int STAGES, bool AKC, bool BKC, bool DUAL, int EPI, typename OutT>
 hipError_t launch_tile(const GemmParams& p, hipStream_t s) {
   constexpr int BNH = DUAL ? BN / 2 : BN;
-  const int grid = ((p.M + BM - 1) / BM) * ((p.N + BNH - 1) / BNH);
+  const int grid = ((p.M + BM - 1) / BM) * ((p.N + BNH - 1) / BNH) * p.splitk;
   hipLaunchKernelGGL((gemm_tile_kernel<BM, BN, WGM, WGN, STAGES, AKC, BKC, DUAL, EPI, OutT>), dim3(grid),
                      dim3(64 * WGM * WGN), 0, s, p);
   return hipGetLastError();
@@ -541,7 +672,8 @@ bool aligned16(const void* q) { return q == nullptr || ((uintptr_t)q & 15) == 0;
 // The pipelined kernel needs every 16-byte chunk it loads to be aligned
 // and either wholly inside or wholly outside the matrix.
 bool gemm_tile_supported(const GemmParams& p, const GemmPlan& plan, GemmKind kind) {
-  if (plan.kernel != KERNEL_TILED || plan.splitk != 1) return false;
+  if (plan.kernel != KERNEL_TILED) return false;
+  if (plan.splitk > 1 && (p.tile_expert || p.a_rows || p.c_rows)) return false;
   if (plan.tile != TILE_256x256 && plan.tile != TILE_128x128 && plan.tile != TILE_128x128_W8) return false;
   if (!p.vecA || !p.vecB) return false;
   if (p.lda % 8 || p.ldb % 8 || p.K0 % 8 || p.K1 % 8) return false;

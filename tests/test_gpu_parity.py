@@ -454,9 +454,12 @@ def test_gqa_projections(wl):
 # ---------------------------------------------------------------------------
 # Backward.
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("act", ["swiglu", "relu", "gelu", "none"])
-def test_backward_small_ragged(act):
-    w = W.MlpWorkload("bwd_small", T=70, d=136, ff=168, p=3, act=act, dtype="bf16", seed=31)
+@pytest.mark.parametrize("act,ff", [("swiglu", 168), ("relu", 168), ("gelu", 168), ("none", 168),
+                                    ("swiglu", 174), ("gelu", 174)])
+def test_backward_small_ragged(act, ff):
+    """ff = 168: 56 columns per shard (the dh epilogue's 16-byte path);
+    ff = 174: 58 (its element-wise path)."""
+    w = W.MlpWorkload("bwd_small", T=70, d=136, ff=ff, p=3, act=act, dtype="bf16", seed=31)
     t = W.mlp_unsharded(w, with_dy=True)
     x, dy = cuda(t["x"]), cuda(t["dy"])
     dxs = []
@@ -1271,3 +1274,24 @@ def test_weight_address_class_changes_only_the_last_bits():
     _, rf, _ = O.within(outs[1], outs[0])
     assert rf < 2e-3, rf           # bf16 outputs of two fp32 summation orders
     assert torch.equal(outs_packed[0], outs_packed[1])
+
+
+@pytest.mark.parametrize("K", [4096, 4095])
+def test_tiled_split_k_when_tiles_are_few(K):
+    """A GEMM with at most one 128x128 tile per CU and a long K is split in
+    two across workgroups (aligned operands: the pipelined kernel with one
+    arrival ticket per workgroup; K = 4095: the register-staged kernel with one
+    per wave); ragged N, bias + GELU epilogue, and bitwise run to run."""
+    T, N = 200, 520
+    x = W.normal((T, K), 1.0, 99, 1)
+    w = W.normal((K, N), 0.02, 99, 2)
+    b = W.normal((N,), 0.5, 99, 3)
+    ws = tp.new_workspace(tp.tp_col_linear_workspace(T, K, N, tp.TP_BF16, "gelu"))
+    assert ws is not None   # the split needs a workspace
+    outs = []
+    for _ in range(2):
+        y = torch.full((T, N), 7.0, dtype=torch.bfloat16, device="cuda")
+        outs.append(tp.tp_col_linear(cuda(x), cuda(w), None, cuda(b), y, "gelu", ws))
+    ref = O.col_linear(O.to64(x), O.to64(w), None, O.to64(b), "gelu")
+    assert_close(outs[0], ref, BF16_TOL, f"split-K tiled GEMM, K={K}")
+    assert torch.equal(outs[0], outs[1])
