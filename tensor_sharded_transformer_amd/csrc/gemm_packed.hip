@@ -201,17 +201,22 @@ __device__ __forceinline__ void store_tile(const PackedParams& p, int i, int gs,
 }
 
 template <int MT, int NS, bool DUAL, int EPI, typename OutT>
-__global__ __launch_bounds__(KW * 64) void packed_gemm_kernel(const PackedParams p) {
+__global__ __launch_bounds__(KW * 64) void packed_gemm_kernel(const PackedParams params) {
   constexpr int NB = DUAL ? 2 : 1;           // weight matrices
   constexpr int WF = NS * NB;                // weight fragments per k-block (all streamed by every wave)
   constexpr int PF = pass_frags<WF>();       // fragments per wave per reduction pass
   constexpr int NPASS = WF / PF;
   static_assert(WF % PF == 0 && PF % NB == 0, "passes hold whole strips");
   __shared__ __attribute__((aligned(16))) char smem[packed_lds_bytes<MT, PF>()];
-  // every parameter the main loop needs, requested in one batch
+  // Every parameter, requested in one batch at the start and held in SGPRs:
+  // a kernel argument first read after the main loop would be a scalar load
+  // queued behind the loop's memory traffic, on the launch's critical path.
+  PackedParams p = params;
   __asm__ volatile("" ::"s"(p.A), "s"(p.B0), "s"(p.B1), "s"(p.nkb), "s"(p.nstrips), "s"(p.splitk));
+  __asm__ volatile("" : "+s"(p.partials), "+s"(p.counters), "+s"(p.C), "+s"(p.ldc), "+s"(p.vec_out), "+s"(p.cpk),
+                   "+s"(p.cpk_mt), "+s"(p.M), "+s"(p.N), "+s"(p.bias), "+s"(p.act));
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ngroups = (p.nstrips + NS - 1) / NS;
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   const int split = id / ngroups;
@@ -239,16 +244,30 @@ __global__ __launch_bounds__(KW * 64) void packed_gemm_kernel(const PackedParams
     for (int j = 0; j < WF; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   if (n > 0) {
+    // The ring runs over q = n rounded up to whole rings of DEPTH k-blocks:
+    // the main loop always loads DEPTH k-blocks ahead and the last ring only
+    // drains, so no load is issued past the end (a step past n loads the
+    // last k-block again and is not accumulated; that happens only when
+    // DEPTH does not divide n).  Loads still in flight when the loop ends
+    // would hold up the reduction that follows.
     const int64_t kbs = (int64_t)p.nstrips * 64;  // u32x4 elements from one k-block to the next
+    const int q = (n + DEPTH - 1) / DEPTH * DEPTH;
     auto phys = [&](int it) { return w0 + min(it, n - 1); };
     KStep<MT, WF> ring[DEPTH];
     static_for<0, DEPTH>([&](auto d) { load_step<MT, WF>(ring[d], bp, ap, phys(d), kbs); });
-    for (int it = 0; it < n; it += DEPTH) {
+    for (int it = 0; it < q - DEPTH; it += DEPTH) {
       static_for<0, DEPTH>([&](auto d) {
-        if (it + (int)d < n) mma_step<MT, WF>(ring[d], acc);
+        mma_step<MT, WF>(ring[d], acc);  // it + d < q - DEPTH <= n - 1
         load_step<MT, WF>(ring[d], bp, ap, phys(it + DEPTH + (int)d), kbs);
+        // keep the ring order: without this the scheduler hoists all of an
+        // iteration's loads above its MFMAs into fresh registers and then
+        // waits for the whole previous ring at the top of the next iteration
+        __builtin_amdgcn_sched_barrier(0);
       });
     }
+    static_for<0, DEPTH>([&](auto d) {
+      if (q - DEPTH + (int)d < n) mma_step<MT, WF>(ring[d], acc);
+    });
   }
 
   // The waves' accumulators meet in LDS, a pass of PF fragments per wave at a

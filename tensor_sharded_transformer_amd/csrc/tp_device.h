@@ -33,7 +33,12 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 
 // Activations in fp32 (exact erf GELU; silu(g) = g * sigmoid(g)).
-__device__ __forceinline__ float sigmoidf_(float g) { return 1.0f / (1.0f + expf(-g)); }
+// 1 / (1 + e^-g) from the hardware 2^x and reciprocal (v_exp_f32, v_rcp_f32,
+// about 1 ulp each, far inside the bf16 rounding of every value it feeds);
+// g -> -inf gives 0, g -> +inf gives 1, NaN stays NaN.
+__device__ __forceinline__ float sigmoidf_(float g) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.44269504088896341f));
+}
 __device__ __forceinline__ float act_fwd(int act, float a) {
   if (act == ACT_RELU) return a > 0.0f ? a : 0.0f;
   if (act == ACT_GELU) return 0.5f * a * (1.0f + erff(a * 0.70710678118654752f));
