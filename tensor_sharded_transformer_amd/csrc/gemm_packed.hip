@@ -53,12 +53,13 @@ constexpr int KW = PACKED_KW;           // waves per workgroup
 constexpr int DEPTH = PACKED_DEPTH;     // k-blocks of loads in flight per wave
 constexpr int PATCH = 1280;             // bytes of a wave's store patch (16 fp32 rows of 80 bytes)
 
-// Fragments per wave that meet in LDS per reduction pass (at most two, so
-// the reduction area stays at 32 KiB per 4 waves; a strip's gate and up
-// fragments go together).
+// Fragments per wave that meet in LDS per reduction pass (at most four, so
+// the reduction area stays at 64 KiB per 4 waves; a strip's gate and up
+// fragments go together).  Each extra pass costs two barriers on the
+// launch's critical path.
 template <int WF>
 constexpr int pass_frags() {
-  return WF <= 2 ? WF : 2;
+  return WF <= 4 ? WF : 4;
 }
 template <int MT, int PF>
 constexpr int packed_lds_bytes() {
