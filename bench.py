@@ -242,32 +242,48 @@ def main() -> int:
 
     if "fp8" in want:
         # the decode shard step with fp8 (E4M3) weights and per-column scales:
-        # gate/up column-parallel GEMM + SwiGLU, then the down row-parallel partial
+        # gate/up column-parallel GEMM + SwiGLU, then the down row-parallel partial;
+        # codes packed once in MFMA fragment order (the row), and the same step on
+        # 64-column strip-major codes (a row of its own)
         R8 = 4   # 4 x 88 MB of weights rotate, more than the 256 MB Infinity Cache holds
         g8 = torch.Generator(device=dev)
-        sets8 = []
+        raw8 = []
         for r in range(R8):
             g8.manual_seed(100 + r)
             codes = lambda shp: (torch.randn(*shp, generator=g8, device=dev) * 64.0).clamp_(-448, 448).to(
                 torch.float8_e4m3fn).view(torch.uint8)
             sc = lambda n: (0.5 + torch.rand(n, generator=g8, device=dev)) * (0.02 / 64.0)
-            def strips(q):   # the strip-major order the fp8 linears read
-                return tp.tp_fp8_pack_strips(q, torch.empty_like(q))
-            sets8.append((strips(codes((d, ff_i))), sc(ff_i), strips(codes((d, ff_i))), sc(ff_i),
-                          strips(codes((ff_i, d))), sc(d)))
+            raw8.append((codes((d, ff_i)), sc(ff_i), codes((d, ff_i)), sc(ff_i), codes((ff_i, d)), sc(d)))
+        b8 = 3 * d * ff_i + (2 * ff_i + d) * 4 + 2 * T * d * 2
         y8 = torch.empty(T, d, dtype=torch.bfloat16, device=dev)
-        ws8 = tp.new_workspace(tp.tp_mlp_shard_fwd_fp8_workspace(T, d, ff_i, "swiglu"), dev)
+
+        sets8 = [(tp.tp_pack_weight_fp8(qg), sg, tp.tp_pack_weight_fp8(qu), su, tp.tp_pack_weight_fp8(qd), sd)
+                 for qg, sg, qu, su, qd, sd in raw8]
+        ws8 = tp.new_workspace(tp.tp_mlp_shard_fwd_packed_fp8_workspace(T, d, ff_i, "swiglu"), dev)
 
         def step8(i):
             qg, sg, qu, su, qd, sd = sets8[i % R8]
-            tp.tp_mlp_shard_fwd_fp8(x, qg, sg, qu, su, qd, sd, y8, "swiglu", ws8)
+            tp.tp_mlp_shard_fwd_packed_fp8(x, qg, sg, qu, su, qd, sd, y8, "swiglu", ff_i, ws8)
 
         t_ = time_gpu(step8, steps_r, 3)
-        b8 = 3 * d * ff_i + (2 * ff_i + d) * 4 + 2 * T * d * 2
         rows["decode_fp8_weights_shard_T64"] = {"us": round(t_ * 1e3, 2), "GB/s": round(b8 / t_ / 1e6, 1),
                                                 "frac_hbm": round(b8 / t_ / 1e6 / HBM_PEAK_GBS, 4),
                                                 "algorithmic_bytes": b8}
-        del sets8, y8, ws8
+        del sets8, ws8
+
+        def strips(q):   # the strip-major order the strip-major fp8 linears read
+            return tp.tp_fp8_pack_strips(q, torch.empty_like(q))
+        sets8 = [(strips(qg), sg, strips(qu), su, strips(qd), sd) for qg, sg, qu, su, qd, sd in raw8]
+        ws8 = tp.new_workspace(tp.tp_mlp_shard_fwd_fp8_workspace(T, d, ff_i, "swiglu"), dev)
+
+        def step8s(i):
+            qg, sg, qu, su, qd, sd = sets8[i % R8]
+            tp.tp_mlp_shard_fwd_fp8(x, qg, sg, qu, su, qd, sd, y8, "swiglu", ws8)
+
+        t_ = time_gpu(step8s, steps_r, 3)
+        rows["decode_fp8_weights_shard_T64_stripmajor"] = {"us": round(t_ * 1e3, 2), "GB/s": round(b8 / t_ / 1e6, 1),
+                                                           "frac_hbm": round(b8 / t_ / 1e6 / HBM_PEAK_GBS, 4)}
+        del sets8, y8, ws8, raw8
 
     if "sum" in want:
         parts = [torch.randn(T, d, device=dev).to(torch.bfloat16) for _ in range(8)]

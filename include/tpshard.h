@@ -389,6 +389,63 @@ tp_status tp_mlp_shard_fwd_packed(const void* x, const void* w1_packed, const vo
                                   int64_t d, int64_t ff_i, tp_dtype out_dtype, tp_act act,
                                   tp_stream stream);
 
+/* ---- packed fp8 weights for decode-sized calls ----------------------------
+ * The fp8 linears above ([MLX] the quantized equivalent of the sharded
+ * linear: W[k, n] = e4m3(code(k, n)) * scale[n], OCP e4m3 codes, one fp32
+ * scale per output column, bf16 activations, fp32 sums, the scale applied to
+ * each column's sum) on codes packed once like the bf16 packed weights, at
+ * one byte per weight.  Layout of packed (K, N) codes: 1024-byte chunks, one
+ * per (pair p of 64 rows, strip s of 16 columns), pair-major: byte
+ * 16*l + 8*h + j of chunk (s, p), at byte offset (p * ceil(N/16) + s) * 1024,
+ * holds code[64p + 32h + 8*(l/16) + j][16s + l%16] for l = 0..63, h = 0..1,
+ * j = 0..7, zero outside K x N.  T <= 64 (TP_ERR_SHAPE beyond). */
+
+/* Bytes of packed (K, N) fp8 codes. */
+size_t tp_packed_fp8_weight_bytes(int64_t K, int64_t N);
+
+/* codes (K, N) row-major bytes (device) -> w_packed (tp_packed_fp8_weight_bytes
+ * (K, N) bytes, device, 16-byte aligned), asynchronously on `stream`.  A pure
+ * rearrangement.  Errors: TP_ERR_NULL, TP_ERR_SHAPE, TP_ERR_HIP. */
+tp_status tp_pack_weight_fp8(const void* codes, void* w_packed, int64_t K, int64_t N, tp_stream stream);
+
+/* Workspace (bytes; rules of tp_linear_packed_workspace) of
+ * tp_col_linear_packed_fp8 and tp_row_linear_partial_packed_fp8 (act
+ * TP_ACT_NONE for the latter); 0 for T == 0 or T > 64. */
+size_t tp_linear_packed_fp8_workspace(int64_t T, int64_t K, int64_t N, tp_act act);
+
+/* tp_col_linear_fp8 on packed codes: y (T, N_i) = act(x W + bias) or
+ * silu(x W) * (x W_up), W = e4m3(wq) * scale (wq_up_packed and scale_up iff
+ * SWIGLU; no bias then).  x (T, K) bf16 row-major, scale / scale_up (N_i)
+ * fp32, bias (N_i) bf16 or NULL, y (T, N_i) bf16; all device; any K and N_i.
+ * Errors as tp_col_linear_packed. */
+tp_status tp_col_linear_packed_fp8(const void* x, const void* wq_packed, const float* scale,
+                                   const void* wq_up_packed, const float* scale_up, const void* bias,
+                                   void* y, void* ws, size_t ws_bytes, int64_t T, int64_t K, int64_t N_i,
+                                   tp_act act, tp_stream stream);
+
+/* tp_row_linear_partial_fp8 on packed codes: z_i (T, N) = x_i W_i, W_i =
+ * e4m3(wq) * scale_i, out_dtype bf16 or f32.  Errors as
+ * tp_row_linear_partial_packed. */
+tp_status tp_row_linear_partial_packed_fp8(const void* x_i, const void* wq_packed, const float* scale_i,
+                                           void* z_i, void* ws, size_t ws_bytes, int64_t T, int64_t K_i,
+                                           int64_t N, tp_dtype out_dtype, tp_stream stream);
+
+/* Workspace (bytes) of tp_mlp_shard_fwd_packed_fp8; 0 for T == 0, T > 64 or
+ * ff_i not a multiple of 64. */
+size_t tp_mlp_shard_fwd_packed_fp8_workspace(int64_t T, int64_t d, int64_t ff_i, tp_act act);
+
+/* tp_mlp_shard_fwd_fp8 on packed codes ([FFN] "Column split, then row split"
+ * with fp8 weights): y_i = act(x W1_i [, x W_up_i]) W2_i.  wq1_packed and
+ * wq_up_packed packed (d, ff_i) codes with scales s1_i, s_up_i (ff_i),
+ * wq2_packed packed (ff_i, d) codes with s2_i (d); ff_i a multiple of 64
+ * (TP_ERR_UNSUPPORTED otherwise).  h_i stays in the workspace (bf16), in the
+ * row GEMM's operand order.  Other rules as tp_mlp_shard_fwd_packed. */
+tp_status tp_mlp_shard_fwd_packed_fp8(const void* x, const void* wq1_packed, const float* s1_i,
+                                      const void* wq_up_packed, const float* s_up_i, const void* wq2_packed,
+                                      const float* s2_i, void* y_i, void* ws, size_t ws_bytes, int64_t T,
+                                      int64_t d, int64_t ff_i, tp_dtype out_dtype, tp_act act,
+                                      tp_stream stream);
+
 /* Sum of the p full-shape partials, then the bias once ([KL] Y = sum_i Z_i;
  * [FFN] "One collective"; [MLX] bias after the sum).  This is the one-GPU
  * stand-in for the group's all-reduce.  z (host array of p device pointers),

@@ -75,6 +75,15 @@ SIGNATURES = {
     "tp_linear_packed_gemm": (c_int, [c_p, c_p, c_p, c_p, c_p, c_p, c_sz, c_i64, c_i64, c_i64, c_int, c_int, c_p]),
     "tp_mlp_shard_fwd_packed_workspace": (c_sz, [c_i64, c_i64, c_i64, c_int]),
     "tp_mlp_shard_fwd_packed": (c_int, [c_p, c_p, c_p, c_p, c_p, c_p, c_sz, c_i64, c_i64, c_i64, c_int, c_int, c_p]),
+    "tp_packed_fp8_weight_bytes": (c_sz, [c_i64, c_i64]),
+    "tp_pack_weight_fp8": (c_int, [c_p, c_p, c_i64, c_i64, c_p]),
+    "tp_linear_packed_fp8_workspace": (c_sz, [c_i64, c_i64, c_i64, c_int]),
+    "tp_col_linear_packed_fp8": (c_int, [c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_sz, c_i64, c_i64, c_i64, c_int,
+                                         c_p]),
+    "tp_row_linear_partial_packed_fp8": (c_int, [c_p, c_p, c_p, c_p, c_p, c_sz, c_i64, c_i64, c_i64, c_int, c_p]),
+    "tp_mlp_shard_fwd_packed_fp8_workspace": (c_sz, [c_i64, c_i64, c_i64, c_int]),
+    "tp_mlp_shard_fwd_packed_fp8": (c_int, [c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_p, c_sz, c_i64, c_i64, c_i64,
+                                            c_int, c_int, c_p]),
     "tp_partial_sum": (c_int, [ctypes.POINTER(c_p), c_int, c_p, c_p, c_i64, c_i64, c_int, c_int, c_p]),
     "tp_rs_residual_rmsnorm": (c_int, [ctypes.POINTER(c_p), c_int, c_int, c_p, c_p, c_p, ctypes.c_float, c_p, c_p,
                                        c_i64, c_i64, c_int, c_int, c_p]),
@@ -529,6 +538,92 @@ def tp_mlp_shard_fwd_packed(x, w1_packed, w_up_packed, w2_packed, y_i, act: str,
     _check(load().tp_mlp_shard_fwd_packed(_ptr(x), _ptr(w1_packed), _ptr(w_up_packed), _ptr(w2_packed), _ptr(y_i),
                                           _ptr(ws), ws.numel() if ws is not None else 0, T, d, ff_i, _dt(y_i),
                                           ACT[act], _stream()))
+    return y_i
+
+
+# ---- packed fp8 weights -----------------------------------------------------------
+def tp_packed_fp8_weight_bytes(K: int, N: int) -> int:
+    return load().tp_packed_fp8_weight_bytes(K, N)
+
+
+def tp_pack_weight_fp8(codes: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """(K, N) row-major e4m3 codes -> the packed fp8 layout (a flat uint8 tensor
+    of tp_packed_fp8_weight_bytes(K, N) bytes); `out` may be given."""
+    K, N = codes.shape
+    _fp8_codes(codes, "codes")
+    nbytes = tp_packed_fp8_weight_bytes(K, N)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=codes.device)
+    if out.numel() * out.element_size() < nbytes:
+        raise ValueError(f"out holds {out.numel() * out.element_size()} bytes < {nbytes}")
+    _check(load().tp_pack_weight_fp8(_ptr(codes), _ptr(out), K, N, _stream()))
+    return out
+
+
+def _packed8(t, K, N, name):
+    if t is not None and t.numel() * t.element_size() < tp_packed_fp8_weight_bytes(K, N):
+        raise ValueError(f"{name}: packed fp8 weight of {t.numel() * t.element_size()} bytes < "
+                         f"{tp_packed_fp8_weight_bytes(K, N)}")
+
+
+def tp_linear_packed_fp8_workspace(T: int, K: int, N: int, act: str = "none") -> int:
+    return load().tp_linear_packed_fp8_workspace(T, K, N, ACT[act])
+
+
+def tp_col_linear_packed_fp8(x, wq_packed, scale, wq_up_packed, scale_up, bias, y, act: str, K: int, N_i: int,
+                             ws: torch.Tensor):
+    T = x.shape[0]
+    _shape(x, (T, K), "x")
+    _shape(y, (T, N_i), "y")
+    _packed8(wq_packed, K, N_i, "wq_packed")
+    _packed8(wq_up_packed, K, N_i, "wq_up_packed")
+    _shape(scale, (N_i,), "scale")
+    if scale_up is not None:
+        _shape(scale_up, (N_i,), "scale_up")
+    if bias is not None:
+        _shape(bias, (N_i,), "bias")
+    _dtypes(torch.bfloat16, x=x, y=y, bias=bias)
+    _dtypes(torch.float32, scale=scale, scale_up=scale_up)
+    _check(load().tp_col_linear_packed_fp8(_ptr(x), _ptr(wq_packed), _ptr(scale), _ptr(wq_up_packed), _ptr(scale_up),
+                                           _ptr(bias), _ptr(y), _ptr(ws), ws.numel() if ws is not None else 0, T, K,
+                                           N_i, ACT[act], _stream()))
+    return y
+
+
+def tp_row_linear_partial_packed_fp8(x_i, wq_packed, scale_i, z_i, N: int, ws: torch.Tensor):
+    T, K_i = x_i.shape
+    _shape(z_i, (T, N), "z_i")
+    _packed8(wq_packed, K_i, N, "wq_packed")
+    _shape(scale_i, (N,), "scale_i")
+    _dtypes(torch.bfloat16, x_i=x_i)
+    _dtypes(torch.float32, scale_i=scale_i)
+    _check(load().tp_row_linear_partial_packed_fp8(_ptr(x_i), _ptr(wq_packed), _ptr(scale_i), _ptr(z_i), _ptr(ws),
+                                                   ws.numel() if ws is not None else 0, T, K_i, N, _dt(z_i),
+                                                   _stream()))
+    return z_i
+
+
+def tp_mlp_shard_fwd_packed_fp8_workspace(T: int, d: int, ff_i: int, act: str) -> int:
+    return load().tp_mlp_shard_fwd_packed_fp8_workspace(T, d, ff_i, ACT[act])
+
+
+def tp_mlp_shard_fwd_packed_fp8(x, wq1_packed, s1_i, wq_up_packed, s_up_i, wq2_packed, s2_i, y_i, act: str, ff_i: int,
+                                ws: torch.Tensor):
+    T, d = x.shape
+    _shape(y_i, (T, d), "y_i")
+    _packed8(wq1_packed, d, ff_i, "wq1_packed")
+    _packed8(wq_up_packed, d, ff_i, "wq_up_packed")
+    _packed8(wq2_packed, ff_i, d, "wq2_packed")
+    _shape(s1_i, (ff_i,), "s1_i")
+    _shape(s2_i, (d,), "s2_i")
+    if s_up_i is not None:
+        _shape(s_up_i, (ff_i,), "s_up_i")
+    _dtypes(torch.bfloat16, x=x)
+    _dtypes(torch.float32, s1_i=s1_i, s_up_i=s_up_i, s2_i=s2_i)
+    _check(load().tp_mlp_shard_fwd_packed_fp8(_ptr(x), _ptr(wq1_packed), _ptr(s1_i), _ptr(wq_up_packed),
+                                              _ptr(s_up_i), _ptr(wq2_packed), _ptr(s2_i), _ptr(y_i), _ptr(ws),
+                                              ws.numel() if ws is not None else 0, T, d, ff_i, _dt(y_i), ACT[act],
+                                              _stream()))
     return y_i
 
 

@@ -1120,6 +1120,191 @@ tp_status tp_mlp_shard_fwd_packed(const void* x, const void* w1_packed, const vo
   return hip_status(tpk::gemm_packed(p2, L.p2, tpk::GK_FWD_STORE, out_dtype == TP_F32, s), who);
 }
 
+// ---- packed fp8 weights (decode-sized calls) -----------------------------------------
+}  // extern "C"
+
+namespace {
+
+// Workspace of the packed fp8 entry points: the bf16 packed layout, with the
+// packed activations padded to whole 64-row k-pairs (zeros past K).
+int64_t kpair_pad(int64_t K) { return (K + 63) / 64 * 64; }
+
+PackedLayout packed8_linear_layout(int64_t T, int64_t K, int64_t N, bool dual) {
+  PackedLayout L;
+  const int64_t Kp = kpair_pad(K);
+  L.p1 = tpk::plan_packed((int)T, (int)N, (int)Kp, true, true);
+  L.x_off = counter_region(tpk::packed_units((int)T, (int)N, L.p1));
+  L.h_off = L.x_off + tpk::align_up(tpk::packed_act_bytes((int)T, (int)Kp), 256);
+  L.part_off = L.h_off;
+  L.total = L.part_off + tpk::align_up(tpk::packed_partial_bytes((int)T, (int)N, dual, L.p1), 256);
+  return L;
+}
+
+// The feed-forward shard (ff_i a multiple of 64, so h fills whole k-pairs).
+PackedLayout packed8_fwd_layout(int64_t T, int64_t d, int64_t ff_i, bool dual) {
+  PackedLayout L;
+  const int64_t dp = kpair_pad(d);
+  L.p1 = tpk::plan_packed((int)T, (int)ff_i, (int)dp, true, true);
+  L.p2 = tpk::plan_packed((int)T, (int)d, (int)ff_i, true, true);
+  const size_t u1 = tpk::packed_units((int)T, (int)ff_i, L.p1), u2 = tpk::packed_units((int)T, (int)d, L.p2);
+  const size_t q1 = tpk::packed_partial_bytes((int)T, (int)ff_i, dual, L.p1);
+  const size_t q2 = tpk::packed_partial_bytes((int)T, (int)d, false, L.p2);
+  L.x_off = counter_region(u1 > u2 ? u1 : u2);
+  L.h_off = L.x_off + tpk::align_up(tpk::packed_act_bytes((int)T, (int)dp), 256);
+  L.part_off = L.h_off + tpk::align_up(tpk::packed_act_bytes((int)T, (int)ff_i), 256);
+  L.total = L.part_off + tpk::align_up(q1 > q2 ? q1 : q2, 256);
+  return L;
+}
+
+tpk::PackedParams packed8_params(const void* A, const void* B0, const float* sc0, const void* B1, const float* sc1,
+                                 int64_t T, int64_t K, int64_t N, const tpk::PackedPlan& pl, char* ws,
+                                 const PackedLayout& L) {
+  tpk::PackedParams p = packed_params(A, B0, B1, T, K, N, pl, ws, L);
+  p.nkb = (int)(kpair_pad(K) / 32);
+  p.bscale0 = sc0;
+  p.bscale1 = sc1;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t tp_packed_fp8_weight_bytes(int64_t K, int64_t N) {
+  if (!dim_ok(K) || !dim_ok(N)) return 0;
+  return tpk::packed_fp8_weight_bytes(K, N);
+}
+
+tp_status tp_pack_weight_fp8(const void* codes, void* w_packed, int64_t K, int64_t N, tp_stream stream) {
+  const char* who = "tp_pack_weight_fp8";
+  if (!dim_ok(K) || !dim_ok(N) || !prod_ok(K, N)) return fail(TP_ERR_SHAPE, "%s: sizes out of range", who);
+  if (K == 0 || N == 0) return TP_OK;
+  if (!codes || !w_packed) return fail(TP_ERR_NULL, "%s: null codes or w_packed", who);
+  if (!aligned16(w_packed)) return fail(TP_ERR_SHAPE, "%s: w_packed must be 16-byte aligned", who);
+  const bool vec = aligned16(codes) && N % 16 == 0;
+  return hip_status(tpk::pack_weight8(codes, N, (int)K, (int)N, vec, w_packed, reinterpret_cast<hipStream_t>(stream)),
+                    who);
+}
+
+size_t tp_linear_packed_fp8_workspace(int64_t T, int64_t K, int64_t N, tp_act act) {
+  if (!valid_act(act) || !dim_ok(T) || !dim_ok(K) || !dim_ok(N) || T == 0 || T > kPackedMaxT) return 0;
+  return packed8_linear_layout(T, K, N, act == TP_ACT_SWIGLU).total;
+}
+
+tp_status tp_col_linear_packed_fp8(const void* x, const void* wq_packed, const float* scale, const void* wq_up_packed,
+                                   const float* scale_up, const void* bias, void* y, void* ws, size_t ws_bytes,
+                                   int64_t T, int64_t K, int64_t N_i, tp_act act, tp_stream stream) {
+  const char* who = "tp_col_linear_packed_fp8";
+  if (!valid_act(act)) return fail(TP_ERR_ACT, "%s: unknown act %d", who, act);
+  tp_status st = packed_sizes_ok(who, T, K, N_i);
+  if (st != TP_OK) return st;
+  const bool sw = act == TP_ACT_SWIGLU;
+  if (sw != (wq_up_packed != nullptr) || sw != (scale_up != nullptr))
+    return fail(TP_ERR_ACT, "%s: wq_up_packed and scale_up must be given iff SWIGLU", who);
+  if (sw && bias) return fail(TP_ERR_ACT, "%s: a bias is not defined for SWIGLU", who);
+  if (T == 0 || N_i == 0) return TP_OK;
+  if ((!x && K > 0) || (!wq_packed && K > 0) || !scale || !y)
+    return fail(TP_ERR_NULL, "%s: null x, wq_packed, scale or y", who);
+  if (!aligned16(wq_packed) || (sw && !aligned16(wq_up_packed)))
+    return fail(TP_ERR_SHAPE, "%s: packed weights must be 16-byte aligned", who);
+  const PackedLayout L = packed8_linear_layout(T, K, N_i, sw);
+  st = packed_ws_ok(who, ws, ws_bytes, L.total);
+  if (st != TP_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* base = reinterpret_cast<char*>(ws);
+  const int nkb = (int)(kpair_pad(K) / 32);
+  hipError_t e = tpk::pack_act16(x, K, (int)T, (int)K, aligned16(x) && K % 8 == 0, base + L.x_off, s, nkb);
+  if (e != hipSuccess) return hip_status(e, who);
+  tpk::PackedParams p = packed8_params(base + L.x_off, wq_packed, scale, sw ? wq_up_packed : nullptr,
+                                       sw ? scale_up : nullptr, T, K, N_i, L.p1, base, L);
+  p.C = y;
+  p.ldc = N_i;
+  p.vec_out = rows_vec16(y, N_i, 2);
+  p.bias = reinterpret_cast<const uint16_t*>(bias);
+  p.act = act;
+  const tpk::GemmKind kind = sw ? tpk::GK_FWD_SWIGLU : tpk::GK_FWD_ACT;
+  return hip_status(tpk::gemm_packed(p, L.p1, kind, false, s, true), who);
+}
+
+tp_status tp_row_linear_partial_packed_fp8(const void* x_i, const void* wq_packed, const float* scale_i, void* z_i,
+                                           void* ws, size_t ws_bytes, int64_t T, int64_t K_i, int64_t N,
+                                           tp_dtype out_dtype, tp_stream stream) {
+  const char* who = "tp_row_linear_partial_packed_fp8";
+  if (!valid_dtype(out_dtype)) return fail(TP_ERR_DTYPE, "%s: unknown out_dtype", who);
+  tp_status st = packed_sizes_ok(who, T, K_i, N);
+  if (st != TP_OK) return st;
+  if (T == 0 || N == 0) return TP_OK;
+  if ((!x_i && K_i > 0) || (!wq_packed && K_i > 0) || !scale_i || !z_i)
+    return fail(TP_ERR_NULL, "%s: null x_i, wq_packed, scale_i or z_i", who);
+  if (!aligned16(wq_packed)) return fail(TP_ERR_SHAPE, "%s: packed weights must be 16-byte aligned", who);
+  const PackedLayout L = packed8_linear_layout(T, K_i, N, false);
+  st = packed_ws_ok(who, ws, ws_bytes, L.total);
+  if (st != TP_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* base = reinterpret_cast<char*>(ws);
+  const int nkb = (int)(kpair_pad(K_i) / 32);
+  hipError_t e = tpk::pack_act16(x_i, K_i, (int)T, (int)K_i, aligned16(x_i) && K_i % 8 == 0, base + L.x_off, s, nkb);
+  if (e != hipSuccess) return hip_status(e, who);
+  tpk::PackedParams p = packed8_params(base + L.x_off, wq_packed, scale_i, nullptr, nullptr, T, K_i, N, L.p1, base, L);
+  p.C = z_i;
+  p.ldc = N;
+  p.vec_out = rows_vec16(z_i, N, esize(out_dtype));
+  return hip_status(tpk::gemm_packed(p, L.p1, tpk::GK_FWD_STORE, out_dtype == TP_F32, s, true), who);
+}
+
+size_t tp_mlp_shard_fwd_packed_fp8_workspace(int64_t T, int64_t d, int64_t ff_i, tp_act act) {
+  if (!valid_act(act) || !dim_ok(T) || !dim_ok(d) || !dim_ok(ff_i) || T == 0 || T > kPackedMaxT || ff_i % 64 != 0)
+    return 0;
+  return packed8_fwd_layout(T, d, ff_i, act == TP_ACT_SWIGLU).total;
+}
+
+tp_status tp_mlp_shard_fwd_packed_fp8(const void* x, const void* wq1_packed, const float* s1_i,
+                                      const void* wq_up_packed, const float* s_up_i, const void* wq2_packed,
+                                      const float* s2_i, void* y_i, void* ws, size_t ws_bytes, int64_t T, int64_t d,
+                                      int64_t ff_i, tp_dtype out_dtype, tp_act act, tp_stream stream) {
+  const char* who = "tp_mlp_shard_fwd_packed_fp8";
+  if (!valid_act(act)) return fail(TP_ERR_ACT, "%s: unknown act %d", who, act);
+  if (!valid_dtype(out_dtype)) return fail(TP_ERR_DTYPE, "%s: unknown out_dtype", who);
+  tp_status st = packed_sizes_ok(who, T, d, ff_i);
+  if (st != TP_OK) return st;
+  if (ff_i % 64 != 0) return fail(TP_ERR_UNSUPPORTED, "%s: ff_i must be a multiple of 64 (ff_i=%lld)", who,
+                                  (long long)ff_i);
+  const bool sw = act == TP_ACT_SWIGLU;
+  if (sw != (wq_up_packed != nullptr) || sw != (s_up_i != nullptr))
+    return fail(TP_ERR_ACT, "%s: wq_up_packed and s_up_i must be given iff SWIGLU", who);
+  if (T == 0 || d == 0) return TP_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (ff_i == 0) {  // empty intermediate: the partial is zero
+    if (!y_i) return fail(TP_ERR_NULL, "%s: null y_i", who);
+    return hip_status(tpk::zero_fill(y_i, (size_t)T * d * esize(out_dtype), s), who);
+  }
+  if (!x || !wq1_packed || !s1_i || !wq2_packed || !s2_i || !y_i)
+    return fail(TP_ERR_NULL, "%s: null x, wq1_packed, s1_i, wq2_packed, s2_i or y_i", who);
+  if (!aligned16(wq1_packed) || !aligned16(wq2_packed) || (sw && !aligned16(wq_up_packed)))
+    return fail(TP_ERR_SHAPE, "%s: packed weights must be 16-byte aligned", who);
+  const PackedLayout L = packed8_fwd_layout(T, d, ff_i, sw);
+  st = packed_ws_ok(who, ws, ws_bytes, L.total);
+  if (st != TP_OK) return st;
+  char* base = reinterpret_cast<char*>(ws);
+  const int nkb = (int)(kpair_pad(d) / 32);
+  hipError_t e = tpk::pack_act16(x, d, (int)T, (int)d, aligned16(x) && d % 8 == 0, base + L.x_off, s, nkb);
+  if (e != hipSuccess) return hip_status(e, who);
+  // column GEMM: h = act(x W1_i [, x W_up_i]) straight into the row GEMM's packed activations
+  tpk::PackedParams p1 = packed8_params(base + L.x_off, wq1_packed, s1_i, sw ? wq_up_packed : nullptr,
+                                        sw ? s_up_i : nullptr, T, d, ff_i, L.p1, base, L);
+  p1.cpk = base + L.h_off;
+  p1.cpk_mt = tpk::packed_mt((int)T);
+  p1.act = act;
+  e = tpk::gemm_packed(p1, L.p1, sw ? tpk::GK_FWD_SWIGLU : tpk::GK_FWD_ACT, false, s, true);
+  if (e != hipSuccess) return hip_status(e, who);
+  // row GEMM: the full-shape partial y_i = h W2_i
+  tpk::PackedParams p2 = packed8_params(base + L.h_off, wq2_packed, s2_i, nullptr, nullptr, T, ff_i, d, L.p2, base, L);
+  p2.C = y_i;
+  p2.ldc = d;
+  p2.vec_out = rows_vec16(y_i, d, esize(out_dtype));
+  return hip_status(tpk::gemm_packed(p2, L.p2, tpk::GK_FWD_STORE, out_dtype == TP_F32, s, true), who);
+}
+
 // ---- MLP shard backward --------------------------------------------------------------
 size_t tp_mlp_shard_bwd_workspace(int64_t T, int64_t d, int64_t ff_i, tp_dtype dtype, tp_act act) {
   if (!valid_dtype(dtype) || !valid_act(act) || !dim_ok(T) || !dim_ok(d) || !dim_ok(ff_i)) return 0;

@@ -39,6 +39,14 @@
 // arrive adds the splits in split order.  Each output tile then goes through
 // an LDS patch so the stores are 16 bytes per lane.  Every sum has a fixed
 // order, so results are bitwise reproducible.
+//
+// fp8 weights (OCP e4m3 codes, one fp32 scale per output column) use the
+// same scheme at half the bytes: a chunk covers a 64-row k-pair of a strip,
+// lane l's 16 bytes being the codes of k-block 2p (bytes 0..7) and 2p + 1
+// (bytes 8..15) at rows 8(l/16) + j, column l%16 -- one load feeds two MFMAs
+// once the codes are widened to bf16 in registers (exact: every e4m3 value is
+// a bf16 value).  A ring step is then a k-pair, with twice the activation
+// chunks; the scales multiply the finished sums in the epilogue.
 #include <type_traits>
 
 #include "tp_kernels.h"
@@ -80,6 +88,38 @@ __device__ __forceinline__ void load_step(KStep<MT, NF>& r, const u32x4* const (
   for (int f = 0; f < NF; ++f) r.b[f] = bp[f][kb * kb_stride];
 #pragma unroll
   for (int i = 0; i < MT; ++i) r.a[i] = ap[((int64_t)kb * MT + i) * 64];
+}
+
+// Four fp8 codes -> four bf16 values in two words, low code first.
+__device__ __forceinline__ void e4m3x4_to_bf16(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  typedef float f32x2_ __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_ __attribute__((ext_vector_type(2)));
+  const f32x2_ a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const f32x2_ b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(a, bf16x2_));
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(b, bf16x2_));
+}
+
+// One k-pair of fp8 weights: r.a holds the MT tiles of k-block 2p, then of 2p + 1.
+template <int MT, int NF>
+__device__ __forceinline__ void mma_step_f8(const KStep<2 * MT, NF>& r, f32x4 (&acc)[MT][NF]) {
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    u32x4 b[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint32_t w0, w1, w2, w3;
+      e4m3x4_to_bf16(r.b[f][2 * h], w0, w1);
+      e4m3x4_to_bf16(r.b[f][2 * h + 1], w2, w3);
+      b[h] = u32x4{w0, w1, w2, w3};
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+        acc[i][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r.a[h * MT + i]),
+                                                           __builtin_bit_cast(bf16x8, b[h]), acc[i][f], 0, 0, 0);
+  }
 }
 
 template <int MT, int NF>
@@ -201,8 +241,9 @@ __device__ __forceinline__ void store_tile(const PackedParams& p, int i, int gs,
   }
 }
 
-template <int MT, int NS, bool DUAL, int EPI, typename OutT>
+template <int MT, int NS, bool DUAL, int EPI, typename OutT, bool F8>
 __global__ __launch_bounds__(KW * 64) void packed_gemm_kernel(const PackedParams params) {
+  constexpr int AT = F8 ? 2 * MT : MT;       // activation chunks per ring step (fp8: a k-pair)
   constexpr int NB = DUAL ? 2 : 1;           // weight matrices
   constexpr int WF = NS * NB;                // weight fragments per k-block (all streamed by every wave)
   constexpr int PF = pass_frags<WF>();       // fragments per wave per reduction pass
@@ -216,6 +257,7 @@ __global__ __launch_bounds__(KW * 64) void packed_gemm_kernel(const PackedParams
   __asm__ volatile("" ::"s"(p.A), "s"(p.B0), "s"(p.B1), "s"(p.nkb), "s"(p.nstrips), "s"(p.splitk));
   __asm__ volatile("" : "+s"(p.partials), "+s"(p.counters), "+s"(p.C), "+s"(p.ldc), "+s"(p.vec_out), "+s"(p.cpk),
                    "+s"(p.cpk_mt), "+s"(p.M), "+s"(p.N), "+s"(p.bias), "+s"(p.act));
+  if constexpr (F8) __asm__ volatile("" : "+s"(p.bscale0), "+s"(p.bscale1));
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ngroups = (p.nstrips + NS - 1) / NS;
@@ -223,9 +265,10 @@ __global__ __launch_bounds__(KW * 64) void packed_gemm_kernel(const PackedParams
   const int split = id / ngroups;
   const int group = id - split * ngroups;
 
-  // this wave's k-blocks: its share of the split's range
-  const int s0 = (int)((int64_t)p.nkb * split / p.splitk);
-  const int s1 = (int)((int64_t)p.nkb * (split + 1) / p.splitk);
+  // this wave's ring steps (k-blocks; fp8: k-pairs): its share of the split's range
+  const int nks = F8 ? p.nkb / 2 : p.nkb;
+  const int s0 = (int)((int64_t)nks * split / p.splitk);
+  const int s1 = (int)((int64_t)nks * (split + 1) / p.splitk);
   const int w0 = s0 + (s1 - s0) * wave / KW;
   const int n = s0 + (s1 - s0) * (wave + 1) / KW - w0;
 
@@ -254,12 +297,16 @@ __global__ __launch_bounds__(KW * 64) void packed_gemm_kernel(const PackedParams
     const int64_t kbs = (int64_t)p.nstrips * 64;  // u32x4 elements from one k-block to the next
     const int q = (n + DEPTH - 1) / DEPTH * DEPTH;
     auto phys = [&](int it) { return w0 + min(it, n - 1); };
-    KStep<MT, WF> ring[DEPTH];
-    static_for<0, DEPTH>([&](auto d) { load_step<MT, WF>(ring[d], bp, ap, phys(d), kbs); });
+    KStep<AT, WF> ring[DEPTH];
+    auto mma = [&](const KStep<AT, WF>& r) __attribute__((always_inline)) {
+      if constexpr (F8) mma_step_f8<MT, WF>(r, acc);
+      else mma_step<MT, WF>(r, acc);
+    };
+    static_for<0, DEPTH>([&](auto d) { load_step<AT, WF>(ring[d], bp, ap, phys(d), kbs); });
     for (int it = 0; it < q - DEPTH; it += DEPTH) {
       static_for<0, DEPTH>([&](auto d) {
-        mma_step<MT, WF>(ring[d], acc);  // it + d < q - DEPTH <= n - 1
-        load_step<MT, WF>(ring[d], bp, ap, phys(it + DEPTH + (int)d), kbs);
+        mma(ring[d]);  // it + d < q - DEPTH <= n - 1
+        load_step<AT, WF>(ring[d], bp, ap, phys(it + DEPTH + (int)d), kbs);
         // keep the ring order: without this the scheduler hoists all of an
         // iteration's loads above its MFMAs into fresh registers and then
         // waits for the whole previous ring at the top of the next iteration
@@ -267,7 +314,7 @@ __global__ __launch_bounds__(KW * 64) void packed_gemm_kernel(const PackedParams
       });
     }
     static_for<0, DEPTH>([&](auto d) {
-      if (q - DEPTH + (int)d < n) mma_step<MT, WF>(ring[d], acc);
+      if (q - DEPTH + (int)d < n) mma(ring[d]);
     });
   }
 
@@ -316,9 +363,17 @@ __global__ __launch_bounds__(KW * 64) void packed_gemm_kernel(const PackedParams
     const int i = u / NS, s = u % NS;
     const int gs = group * NS + s;
     if (u >= MT * NS || gs >= p.nstrips) continue;
+    const int col = gs * 16 + (lane & 15);
+    float sc0 = 1.0f, sc1 = 1.0f;  // fp8 column scales (columns past N are not stored)
+    if constexpr (F8) {
+      if (col < p.N) {
+        sc0 = p.bscale0[col];
+        if constexpr (DUAL) sc1 = p.bscale1[col];
+      }
+    }
     float out[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) out[j] = epi_value<EPI>(p, gs * 16 + (lane & 15), v[k][0][j], v[k][NB - 1][j]);
+    for (int j = 0; j < 4; ++j) out[j] = epi_value<EPI>(p, col, v[k][0][j] * sc0, v[k][NB - 1][j] * sc1);
     store_tile<EPI, OutT>(p, i, gs, lane, patch, out);
   }
 }
@@ -347,6 +402,44 @@ __global__ __launch_bounds__(256) void pack_act16_kernel(const uint16_t* __restr
     }
   }
   out[gid] = v;
+}
+
+// fp8 codes (K, N) row-major -> packed k-pair chunks.  A workgroup reads a
+// 64 x 64 block (one k-pair of four strips) into LDS with 16-byte row
+// pieces, then each lane gathers its 16 codes (8 rows of each k-block of the
+// pair, one column); codes outside K x N are zero.
+__global__ __launch_bounds__(256) void pack_weight8_kernel(const uint8_t* __restrict__ w, int64_t ldw, int K, int N,
+                                                           int nstrips, int vec, u32x4* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[64][64 + 16];
+  const int kp = blockIdx.x;       // k-pair
+  const int sg = blockIdx.y * 4;   // first strip of the four
+  const int t = threadIdx.x;
+  {
+    const int r = t >> 2, c16 = (t & 3) * 16;  // row r, columns c16 .. c16+15 of the block
+    const int k = kp * 64 + r, n = sg * 16 + c16;
+    u32x4 q = {0u, 0u, 0u, 0u};
+    if (k < K && vec && n + 16 <= N) {
+      q = *reinterpret_cast<const u32x4*>(w + (int64_t)k * ldw + n);
+    } else {
+      uint8_t v[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) v[e] = (k < K && n + e < N) ? w[(int64_t)k * ldw + n + e] : (uint8_t)0;
+      __builtin_memcpy(&q, v, 16);
+    }
+    *reinterpret_cast<u32x4*>(&tile[r][c16]) = q;
+  }
+  __syncthreads();
+  const int s = t >> 6, lane = t & 63;
+  if (sg + s >= nstrips) return;
+  const int col = 16 * s + (lane & 15), r0 = 8 * (lane >> 4);
+  uint8_t o[16];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[8 * h + j] = tile[32 * h + r0 + j][col];
+  u32x4 v;
+  __builtin_memcpy(&v, o, 16);
+  out[((int64_t)kp * nstrips + sg + s) * 64 + lane] = v;
 }
 
 // Weights (K, N) row-major -> packed chunks.  A workgroup rearranges a 32 x 64
@@ -383,28 +476,29 @@ __global__ __launch_bounds__(256) void pack_weight16_kernel(const uint16_t* __re
   out[((int64_t)b * nstrips + sg + s) * 64 + lane] = u32x4{q[0], q[1], q[2], q[3]};
 }
 
-template <int MT, int NS, bool DUAL, int EPI, typename OutT>
+template <int MT, int NS, bool DUAL, int EPI, typename OutT, bool F8>
 hipError_t launch_ns(const PackedParams& p, hipStream_t s) {
   const int ngroups = (p.nstrips + NS - 1) / NS;
-  hipLaunchKernelGGL((packed_gemm_kernel<MT, NS, DUAL, EPI, OutT>), dim3(ngroups * p.splitk), dim3(KW * 64), 0, s, p);
+  hipLaunchKernelGGL((packed_gemm_kernel<MT, NS, DUAL, EPI, OutT, F8>), dim3(ngroups * p.splitk), dim3(KW * 64), 0, s,
+                     p);
   return hipGetLastError();
 }
 
-template <bool DUAL, int EPI, typename OutT>
+template <bool DUAL, int EPI, typename OutT, bool F8>
 hipError_t launch_packed(const PackedParams& p, int ns, hipStream_t s) {
   const int mt = p.mt;
   if (ns == 1) {
-    if (mt == 1) return launch_ns<1, 1, DUAL, EPI, OutT>(p, s);
-    if (mt == 2) return launch_ns<2, 1, DUAL, EPI, OutT>(p, s);
-    if (mt == 4) return launch_ns<4, 1, DUAL, EPI, OutT>(p, s);
+    if (mt == 1) return launch_ns<1, 1, DUAL, EPI, OutT, F8>(p, s);
+    if (mt == 2) return launch_ns<2, 1, DUAL, EPI, OutT, F8>(p, s);
+    if (mt == 4) return launch_ns<4, 1, DUAL, EPI, OutT, F8>(p, s);
   } else if (ns == 2) {
-    if (mt == 1) return launch_ns<1, 2, DUAL, EPI, OutT>(p, s);
-    if (mt == 2) return launch_ns<2, 2, DUAL, EPI, OutT>(p, s);
-    if (mt == 4) return launch_ns<4, 2, DUAL, EPI, OutT>(p, s);
+    if (mt == 1) return launch_ns<1, 2, DUAL, EPI, OutT, F8>(p, s);
+    if (mt == 2) return launch_ns<2, 2, DUAL, EPI, OutT, F8>(p, s);
+    if (mt == 4) return launch_ns<4, 2, DUAL, EPI, OutT, F8>(p, s);
   } else if (ns == 4) {
-    if (mt == 1) return launch_ns<1, 4, DUAL, EPI, OutT>(p, s);
-    if (mt == 2) return launch_ns<2, 4, DUAL, EPI, OutT>(p, s);
-    if (mt == 4) return launch_ns<4, 4, DUAL, EPI, OutT>(p, s);
+    if (mt == 1) return launch_ns<1, 4, DUAL, EPI, OutT, F8>(p, s);
+    if (mt == 2) return launch_ns<2, 4, DUAL, EPI, OutT, F8>(p, s);
+    if (mt == 4) return launch_ns<4, 4, DUAL, EPI, OutT, F8>(p, s);
   }
   return hipErrorInvalidValue;
 }
@@ -413,14 +507,21 @@ hipError_t launch_packed(const PackedParams& p, int ns, hipStream_t s) {
 
 int packed_mt(int M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
 
-PackedPlan plan_packed(int M, int N, int K, bool split_ok) {
+PackedPlan plan_packed(int M, int N, int K, bool split_ok, bool f8) {
   PackedPlan pl;
   const int nstrips = (N + 15) / 16;
-  const int nkb = (K + 31) / 32;
+  const int nkb = f8 ? (K + 63) / 64 : (K + 31) / 32;  // ring steps along K
   // two strips per workgroup once there are enough strips for 64 groups
   // (fewer activation bytes per weight byte), then K split across
   // workgroups until the grid fills the CUs
+#ifndef NS8_GU
+#define NS8_GU 2
+#endif
+#ifndef NS8_DOWN
+#define NS8_DOWN 2
+#endif
   pl.ns = nstrips >= 128 ? 2 : 1;
+  if (f8) pl.ns = nstrips >= 512 ? NS8_DOWN : nstrips >= 128 ? NS8_GU : 1;
   const int ngroups = (nstrips + pl.ns - 1) / pl.ns;
   pl.splitk = 1;
   if (split_ok) {
@@ -448,8 +549,16 @@ size_t packed_partial_bytes(int M, int N, bool dual, const PackedPlan& pl) {
   return packed_units(M, N, pl) * pl.splitk * uw * (dual ? 2 : 1) * 1024;
 }
 
-hipError_t pack_act16(const void* x, int64_t lda, int M, int K, bool vec, void* out, hipStream_t s) {
-  const int nkb = (K + 31) / 32, mt = packed_mt(M);
+hipError_t pack_weight8(const void* w, int64_t ldw, int K, int N, bool vec, void* out, hipStream_t s) {
+  const int nkp = (K + 63) / 64, nstrips = (N + 15) / 16;
+  if (nkp == 0 || nstrips == 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_weight8_kernel, dim3(nkp, (nstrips + 3) / 4), dim3(256), 0, s,
+                     reinterpret_cast<const uint8_t*>(w), ldw, K, N, nstrips, vec ? 1 : 0, reinterpret_cast<u32x4*>(out));
+  return hipGetLastError();
+}
+
+hipError_t pack_act16(const void* x, int64_t lda, int M, int K, bool vec, void* out, hipStream_t s, int nkb_out) {
+  const int nkb = nkb_out > (K + 31) / 32 ? nkb_out : (K + 31) / 32, mt = packed_mt(M);
   const int n = nkb * mt * 64;
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(pack_act16_kernel, dim3((n + 255) / 256), dim3(256), 0, s,
@@ -467,15 +576,25 @@ hipError_t pack_weight16(const void* w, int64_t ldw, int K, int N, bool vec, voi
   return hipGetLastError();
 }
 
-hipError_t gemm_packed(const PackedParams& p, const PackedPlan& pl, GemmKind kind, bool out_f32, hipStream_t s) {
+template <bool F8>
+hipError_t gemm_packed_kind(const PackedParams& p, const PackedPlan& pl, GemmKind kind, bool out_f32, hipStream_t s) {
   switch (kind) {
     case GK_FWD_STORE:
-      return out_f32 ? launch_packed<false, EPI_STORE, float>(p, pl.ns, s)
-                     : launch_packed<false, EPI_STORE, uint16_t>(p, pl.ns, s);
-    case GK_FWD_ACT: return launch_packed<false, EPI_ACT, uint16_t>(p, pl.ns, s);
-    case GK_FWD_SWIGLU: return launch_packed<true, EPI_SWIGLU, uint16_t>(p, pl.ns, s);
+      return out_f32 ? launch_packed<false, EPI_STORE, float, F8>(p, pl.ns, s)
+                     : launch_packed<false, EPI_STORE, uint16_t, F8>(p, pl.ns, s);
+    case GK_FWD_ACT: return launch_packed<false, EPI_ACT, uint16_t, F8>(p, pl.ns, s);
+    case GK_FWD_SWIGLU: return launch_packed<true, EPI_SWIGLU, uint16_t, F8>(p, pl.ns, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t gemm_packed(const PackedParams& p, const PackedPlan& pl, GemmKind kind, bool out_f32, hipStream_t s,
+                       bool f8) {
+  if (f8) {
+    if (p.nkb % 2 != 0 || !p.bscale0 || (kind == GK_FWD_SWIGLU && !p.bscale1)) return hipErrorInvalidValue;
+    return gemm_packed_kind<true>(p, pl, kind, out_f32, s);
+  }
+  return gemm_packed_kind<false>(p, pl, kind, out_f32, s);
 }
 
 }  // namespace tpk

@@ -92,11 +92,12 @@ bool gemm_tile_supported(const GemmParams& p, const GemmPlan& plan, GemmKind kin
 hipError_t gemm_tile(const GemmParams& p, const GemmPlan& plan, GemmKind kind, bool out_f32, hipStream_t s);
 
 // Packed-weight decode GEMM (gemm_packed.hip): weights stored once in 1 KB
-// MFMA B-fragment chunks (16-column strips of 32-row k-blocks), activations
-// packed alike (32-column k-blocks of 16-row tiles), M <= 64.
+// MFMA B-fragment chunks (16-column strips of 32-row k-blocks; fp8 codes: of
+// 64-row k-pairs), activations packed alike (32-column k-blocks of 16-row
+// tiles), M <= 64.
 struct PackedParams {
-  const void* A;         // packed activations: nkb k-blocks x mt tiles
-  const void* B0;        // packed weights (nstrips strips x nkb k-blocks)
+  const void* A;         // packed activations: nkb k-blocks x mt tiles (fp8 weights: nkb even)
+  const void* B0;        // packed weights (nstrips strips x nkb k-blocks, or nkb / 2 k-pairs of fp8 codes)
   const void* B1;        // second packed weights (dual: gate and up), or null
   int M, N, K;           // output rows and columns, contraction length
   int mt;                // 16-row tiles of the packed activations
@@ -112,22 +113,27 @@ struct PackedParams {
   int cpk_mt;            //   of a GEMM with this many 16-row tiles
   const uint16_t* bias;  // per-column bias (EPI_ACT), may be null
   int act;
-  int a_rowmajor;        // A is x (M, K) row-major with row pitch a_ld, read in fragment order
-  int64_t a_ld;          //   (16-byte aligned rows, K a multiple of 32)
+  const float* bscale0;  // fp8 weights: per-column scales of B0 / B1, applied to the sums
+  const float* bscale1;
 };
 struct PackedPlan {
   int ns = 1;      // strips per workgroup
   int splitk = 1;  // workgroups along K
 };
 int packed_mt(int M);
-PackedPlan plan_packed(int M, int N, int K, bool split_ok);
+PackedPlan plan_packed(int M, int N, int K, bool split_ok, bool f8 = false);
 size_t packed_act_bytes(int M, int K);
 size_t packed_units(int M, int N, const PackedPlan& pl);
 size_t packed_partial_bytes(int M, int N, bool dual, const PackedPlan& pl);
 inline size_t packed_weight_bytes(int64_t K, int64_t N) { return (size_t)((N + 15) / 16) * ((K + 31) / 32) * 1024; }
-hipError_t pack_act16(const void* x, int64_t lda, int M, int K, bool vec, void* out, hipStream_t s);
+inline size_t packed_fp8_weight_bytes(int64_t K, int64_t N) { return (size_t)((N + 15) / 16) * ((K + 63) / 64) * 1024; }
+// nkb: k-blocks to write (at least (K + 31) / 32; those past K are zeros)
+hipError_t pack_act16(const void* x, int64_t lda, int M, int K, bool vec, void* out, hipStream_t s, int nkb = 0);
 hipError_t pack_weight16(const void* w, int64_t ldw, int K, int N, bool vec, void* out, hipStream_t s);
-hipError_t gemm_packed(const PackedParams& p, const PackedPlan& pl, GemmKind kind, bool out_f32, hipStream_t s);
+hipError_t pack_weight8(const void* w, int64_t ldw, int K, int N, bool vec, void* out, hipStream_t s);
+// f8: B0/B1 hold packed fp8 codes (p.nkb even, p.bscale0/1 set)
+hipError_t gemm_packed(const PackedParams& p, const PackedPlan& pl, GemmKind kind, bool out_f32, hipStream_t s,
+                       bool f8 = false);
 
 // fp32 (SIMT) GEMM with the same parameter block and epilogues.
 hipError_t gemm_f32(const GemmParams& p, GemmKind kind, hipStream_t s);

@@ -304,3 +304,28 @@ def test_packed_entry_points_validation(lib):
     assert tp.tp_packed_weight_bytes(33, 17) == 2 * 2 * 1024
     assert tp.tp_linear_packed_workspace(65, 64, 64) == 0
     assert tp.tp_mlp_shard_fwd_packed_workspace(64, 8192, 3584, "swiglu") > 0
+
+
+def test_packed_fp8_entry_points_validation(lib):
+    """Packed fp8 calls: T <= 64, scales required, up weights iff SWIGLU, the
+    fused shard needs ff_i % 64 == 0; sizes of the packed codes."""
+    f = lib.tp_col_linear_packed_fp8
+    assert f(FAKE, FAKE, FAKE, None, None, None, FAKE, FAKE, 1 << 20, 65, 64, 64, 0, None) == SHAPE
+    assert f(FAKE, FAKE, FAKE, None, None, None, FAKE, FAKE, 1 << 20, 4, 64, 64, 3, None) == ACTE   # SWIGLU, no up
+    assert f(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, 1 << 20, 4, 64, 64, 3, None) == ACTE   # up, no scale_up
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 1 << 20, 4, 64, 64, 0, None) == ACTE   # up without SWIGLU
+    assert f(FAKE, FAKE, None, None, None, None, FAKE, FAKE, 1 << 20, 4, 64, 64, 0, None) == NULL   # no scale
+    assert f(FAKE, FAKE, FAKE, None, None, None, FAKE, None, 0, 4, 64, 64, 0, None) == WS
+    g = lib.tp_row_linear_partial_packed_fp8
+    assert g(FAKE, FAKE, None, FAKE, FAKE, 1 << 20, 4, 64, 64, 0, None) == NULL
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, 4, 64, 64, 9, None) == DTYPE
+    m = lib.tp_mlp_shard_fwd_packed_fp8
+    assert m(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 24, 4, 64, 96, 0, 3, None) == 6   # ff_i % 64
+    assert m(FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, 1 << 24, 4, 64, 64, 0, 3, None) == ACTE
+    assert lib.tp_pack_weight_fp8(None, FAKE, 4, 4, None) == NULL
+    assert lib.tp_pack_weight_fp8(FAKE, ctypes.c_void_p(0x1008), 4, 4, None) == SHAPE
+    assert tp.tp_packed_fp8_weight_bytes(8192, 3584) == 224 * 128 * 1024
+    assert tp.tp_packed_fp8_weight_bytes(65, 17) == 2 * 2 * 1024
+    assert tp.tp_linear_packed_fp8_workspace(65, 64, 64) == 0
+    assert tp.tp_mlp_shard_fwd_packed_fp8_workspace(64, 8192, 3552, "swiglu") == 0
+    assert tp.tp_mlp_shard_fwd_packed_fp8_workspace(64, 8192, 3584, "swiglu") > 0

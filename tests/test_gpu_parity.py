@@ -772,6 +772,97 @@ def test_fp8_mlp_shard_fwd(T, act):
     assert torch.equal(y, y2)
 
 
+# ---------------------------------------------------------------------------
+# fp8 (E4M3) weights packed in MFMA fragment order (k-pairs of 16-column strips).
+# ---------------------------------------------------------------------------
+def packed8(q):
+    """Device copy of (K, N) row-major codes in the packed fp8 layout."""
+    return tp.tp_pack_weight_fp8(cuda(q))
+
+
+def packed8_layout_cpu(q):
+    """The packed fp8 layout written out: chunk (pair p, strip s), lane l, byte
+    8h + j holds code[64p + 32h + 8(l // 16) + j, 16s + l % 16], zero padded."""
+    K, N = q.shape
+    nkp, ns = (K + 63) // 64, (N + 15) // 16
+    qp = torch.zeros(nkp * 64, ns * 16, dtype=torch.uint8)
+    qp[:K, :N] = q
+    return qp.reshape(nkp, 2, 4, 8, ns, 16).permute(0, 4, 2, 5, 1, 3).reshape(-1)
+
+
+@pytest.mark.parametrize("K,N", [(1, 16), (5, 40), (130, 24), (1000, 3584), (64, 4096)])
+def test_pack_weight_fp8_is_the_fragment_permutation(K, N):
+    q = torch.randint(0, 256, (K, N), dtype=torch.uint8, generator=torch.Generator().manual_seed(7 * K + N))
+    assert torch.equal(packed8(q).cpu(), packed8_layout_cpu(q))
+
+
+@pytest.mark.parametrize("T,K,N", [(1, 1000, 256), (40, 4096, 1088), (64, 1000, 3584), (33, 2056, 520),
+                                   (64, 8192, 1280)])
+@pytest.mark.parametrize("act", ["none", "relu", "gelu", "swiglu"])
+def test_fp8_col_linear_packed(T, K, N, act):
+    """Ragged K (not whole k-pairs) and N (not whole strips), every activation,
+    every finite code with both signs and the subnormals at N = 256."""
+    x = W.normal((T, K), 1.0, 85, 1)
+    q = W.e4m3_codes((K, N), 85, 2)
+    if N == 256:
+        allc = torch.tensor([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=torch.uint8)
+        q[:2] = allc.repeat(4)[: 2 * N].view(2, N)
+    sc = W.column_scales(N, 85, 3)
+    qu = W.e4m3_codes((K, N), 85, 4) if act == "swiglu" else None
+    su = W.column_scales(N, 85, 5) if act == "swiglu" else None
+    bias = W.normal((N,), 0.1, 85, 6) if act in ("relu", "gelu") else None
+    y = torch.full((T, N), 7.0, dtype=torch.bfloat16, device="cuda")
+    ws = tp.new_workspace(tp.tp_linear_packed_fp8_workspace(T, K, N, act))
+    tp.tp_col_linear_packed_fp8(cuda(x), packed8(q), cuda(sc), None if qu is None else packed8(qu),
+                                None if su is None else cuda(su), None if bias is None else cuda(bias), y, act, K, N,
+                                ws)
+    assert_close(y, O.col_linear_fp8(x, q, sc, qu, su, bias, act), BF16_TOL, f"packed fp8 col linear {act}")
+
+
+@pytest.mark.parametrize("out_dt", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("T,K,N", [(64, 3584, 8192), (7, 1000, 1000), (1, 33, 24)])
+def test_fp8_row_linear_partial_packed(T, K, N, out_dt):
+    x = W.normal((T, K), 1.0, 86, 1)
+    q = W.e4m3_codes((K, N), 86, 2)
+    sc = W.column_scales(N, 86, 3)
+    z = torch.full((T, N), 7.0, dtype=out_dt, device="cuda")
+    ws = tp.new_workspace(tp.tp_linear_packed_fp8_workspace(T, K, N, "none"))
+    qp = packed8(q)
+    tp.tp_row_linear_partial_packed_fp8(cuda(x), qp, cuda(sc), z, N, ws)
+    assert_close(z, O.row_linear_partial_fp8(x, q, sc), BF16_TOL, "packed fp8 row partial")
+    again = torch.empty_like(z)
+    tp.tp_row_linear_partial_packed_fp8(cuda(x), qp, cuda(sc), again, N, ws)
+    assert torch.equal(z, again)
+
+
+@pytest.mark.parametrize("T,act", [(64, "swiglu"), (1, "swiglu"), (40, "gelu"), (33, "relu")])
+def test_fp8_mlp_shard_fwd_packed(T, act):
+    """The 70B-class shard at decode size on packed fp8 codes (h handed to the
+    row GEMM in operand order) against the fp64 chain, and bitwise against the
+    two separate packed fp8 linears."""
+    d, ff_i = 8192, 3584
+    x = W.normal((T, d), 1.0, 87, 1)
+    q1, qd = W.e4m3_codes((d, ff_i), 87, 2), W.e4m3_codes((ff_i, d), 87, 4)
+    qu = W.e4m3_codes((d, ff_i), 87, 3) if act == "swiglu" else None
+    s1, sd = W.column_scales(ff_i, 87, 5), W.column_scales(d, 87, 7)
+    su = W.column_scales(ff_i, 87, 6) if act == "swiglu" else None
+    p1, pu, p2 = packed8(q1), None if qu is None else packed8(qu), packed8(qd)
+    c1, cu, c2 = cuda(s1), None if su is None else cuda(su), cuda(sd)
+    y = torch.empty(T, d, dtype=torch.bfloat16, device="cuda")
+    ws = tp.new_workspace(tp.tp_mlp_shard_fwd_packed_fp8_workspace(T, d, ff_i, act))
+    tp.tp_mlp_shard_fwd_packed_fp8(cuda(x), p1, c1, pu, cu, p2, c2, y, act, ff_i, ws)
+    h64 = O.col_linear_fp8(x, q1, s1, qu, su, None, act)
+    assert_close(y, O.row_linear_partial_fp8(h64, qd, sd), BF16_TOL, f"packed fp8 shard {act}")
+    h = torch.empty(T, ff_i, dtype=torch.bfloat16, device="cuda")
+    y2 = torch.empty_like(y)
+    ws2 = tp.new_workspace(max(tp.tp_linear_packed_fp8_workspace(T, d, ff_i, act),
+                               tp.tp_linear_packed_fp8_workspace(T, ff_i, d)))
+    tp.tp_col_linear_packed_fp8(cuda(x), p1, c1, pu, cu, None, h, act, d, ff_i, ws2)
+    assert_close(h, h64, BF16_TOL, f"packed fp8 h {act}")
+    tp.tp_row_linear_partial_packed_fp8(h, p2, c2, y2, d, ws2)
+    assert torch.equal(y, y2)
+
+
 def test_one_workspace_serves_every_entry_point():
     """One zero-initialised workspace reused across entry points and shapes in
     sequence gives bitwise the results each call gives with a fresh one (the
