@@ -70,11 +70,15 @@ def time_gpu(fn, steps: int, warmup: int, repeats: int = 3, warm_s: float = 0.05
     at least `warm_s` seconds of untimed calls (the clocks settle under load),
     then the best of `repeats` timed runs of `steps` calls."""
     import torch
-    for i in range(warmup):
+    # one call counter throughout: a timed run resumes the rotation over
+    # weight sets where the previous calls left it, so it never starts on a
+    # set still held in the Infinity Cache
+    i = 0
+    for _ in range(warmup):
         fn(i)
+        i += 1
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    i = 0
     while time.perf_counter() - t0 < warm_s:
         for _ in range(8):
             fn(i)
@@ -86,8 +90,9 @@ def time_gpu(fn, steps: int, warmup: int, repeats: int = 3, warm_s: float = 0.05
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
         start.record(s)
-        for i in range(steps):
+        for _ in range(steps):
             fn(i)
+            i += 1
         end.record(s)
         torch.cuda.synchronize()
         best = min(best, start.elapsed_time(end) / steps)
@@ -151,7 +156,7 @@ def main() -> int:
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     ev0.record()
-    for i in range(args.steps):
+    for i in range(args.warmup, args.warmup + args.steps):   # the rotation continues from the warmup
         step(i)
     ev1.record()
     torch.cuda.synchronize()
@@ -193,7 +198,10 @@ def main() -> int:
         hp = torch.empty(tp.tp_packed_act_bytes(T, ff_i), dtype=torch.uint8, device=dev)
         tp.tp_pack_act(h, hp)
         ws_d = tp.new_workspace(tp.tp_linear_packed_workspace(T, ff_i, d), dev)
-        t_ = time_gpu(lambda i: tp.tp_linear_packed_gemm(hp, psets[i % R]["w2"], None, None, y, "none", ff_i, ws_d),
+        # alone, three W2 sets (176 MB) would sit in the 256 MB Infinity Cache:
+        # rotate six distinct buffers (352 MB) so the GEMM streams from HBM
+        w2s = [psets[r]["w2"] for r in range(R)] + [psets[r]["w2"].clone() for r in range(R)]
+        t_ = time_gpu(lambda i: tp.tp_linear_packed_gemm(hp, w2s[i % len(w2s)], None, None, y, "none", ff_i, ws_d),
                       args.steps, 200)
         b_ = (d * ff_i + T * ff_i + T * d) * 2
         rows["decode_down_gemm_packed_T64"] = {"us": round(t_ * 1e3, 2), "GB/s": round(b_ / t_ / 1e6, 1),
@@ -205,7 +213,7 @@ def main() -> int:
         rows["decode_shard_T64_rowmajor_weights"] = {"us": round(t_ * 1e3, 2),
                                                      "GB/s": round(bytes_step / t_ / 1e6, 1),
                                                      "frac_hbm": round(bytes_step / t_ / 1e6 / HBM_PEAK_GBS, 4)}
-        del hp, ws_d, ws_r
+        del hp, ws_d, ws_r, w2s
 
     if "calib" in want:
         src = torch.ones(8192, 7168, dtype=torch.bfloat16, device=dev)
@@ -286,36 +294,42 @@ def main() -> int:
         del sets8, y8, ws8, raw8
 
     if "sum" in want:
+        # every sum row rotates more partials than the 256 MB Infinity Cache holds
+        NS_ = 40   # 40 x 8 MB at decode size
         parts = [torch.randn(T, d, device=dev).to(torch.bfloat16) for _ in range(8)]
+        pbuf = [[t.clone() for t in parts] for _ in range(NS_)]
         yf = torch.empty(T, d, dtype=torch.float32, device=dev)
-        # a few-microsecond kernel: call the C ABI with a prepared pointer array
+        # a few-microsecond kernel: call the C ABI with prepared pointer arrays
         # so host-side argument marshalling does not leave the GPU idle
         import ctypes
         lib = tp.load()
-        parr = (ctypes.c_void_p * 8)(*[t.data_ptr() for t in parts])
+        parrs = [(ctypes.c_void_p * 8)(*[t.data_ptr() for t in ps_]) for ps_ in pbuf]
         stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
         yptr = ctypes.c_void_p(yf.data_ptr())
-        t_ = time_gpu(lambda i: lib.tp_partial_sum(parr, 8, None, yptr, T, d, tp.TP_BF16, tp.TP_F32, stream), steps_r, 5)
+        t_ = time_gpu(lambda i: lib.tp_partial_sum(parrs[i % NS_], 8, None, yptr, T, d, tp.TP_BF16, tp.TP_F32, stream),
+                      steps_r, 5)
+        del pbuf, parrs
         b_ = (8 * T * d * 2 + T * d * 4)
         rows["sum_partials_decode_p8"] = {"us": round(t_ * 1e3, 2), "GB/s": round(b_ / t_ / 1e6, 1),
                                           "frac_hbm": round(b_ / t_ / 1e6 / HBM_PEAK_GBS, 4)}
         T5, d5 = W.BACKWARD.T, W.BACKWARD.d
-        parts = [torch.randn(T5, d5, device=dev).to(torch.bfloat16) for _ in range(8)]
+        parts = [[torch.randn(T5, d5, device=dev).to(torch.bfloat16) for _ in range(8)] for _ in range(3)]
         yf = torch.empty(T5, d5, dtype=torch.float32, device=dev)
-        t_ = time_gpu(lambda i: tp.tp_partial_sum(parts, None, yf), steps_r, 5)
+        t_ = time_gpu(lambda i: tp.tp_partial_sum(parts[i % 3], None, yf), steps_r, 5)
         b_ = (8 * T5 * d5 * 2 + T5 * d5 * 4)
         rows["sum_partials_dx_p8_T2048"] = {"us": round(t_ * 1e3, 2), "GB/s": round(b_ / t_ / 1e6, 1),
                                             "frac_hbm": round(b_ / t_ / 1e6 / HBM_PEAK_GBS, 4)}
         del parts
-        # sequence-parallel boundary at prefill size: rank 3's 512 rows of 8 partials
-        # (4096 x 8192 bf16) + residual, then RMSNorm
+        # sequence-parallel boundary at prefill size: one rank's 512 rows of 8
+        # partials (4096 x 8192 bf16) + residual, then RMSNorm; the rank rotates
+        # over all 8 so the partials read (8 x 67 MB) exceed the Infinity Cache
         Ts, ps = W.PREFILL.T, 8
         parts = [torch.randn(Ts, d, device=dev).to(torch.bfloat16) for _ in range(ps)]
         res = torch.randn(Ts // ps, d, device=dev).to(torch.bfloat16)
         nw = torch.randn(d, device=dev).to(torch.bfloat16)
         r_out = torch.empty_like(res)
         yn = torch.empty_like(res)
-        t_ = time_gpu(lambda i: tp.tp_rs_residual_rmsnorm(parts, 3, None, res, nw, 1e-5, r_out, yn), steps_r, 5)
+        t_ = time_gpu(lambda i: tp.tp_rs_residual_rmsnorm(parts, i % ps, None, res, nw, 1e-5, r_out, yn), steps_r, 5)
         b_ = (ps * (Ts // ps) * d + 3 * (Ts // ps) * d + d) * 2
         rows["sp_rs_residual_rmsnorm_T4096_p8"] = {"us": round(t_ * 1e3, 2), "GB/s": round(b_ / t_ / 1e6, 1),
                                                    "frac_hbm": round(b_ / t_ / 1e6 / HBM_PEAK_GBS, 4)}

@@ -513,15 +513,10 @@ PackedPlan plan_packed(int M, int N, int K, bool split_ok, bool f8) {
   const int nkb = f8 ? (K + 63) / 64 : (K + 31) / 32;  // ring steps along K
   // two strips per workgroup once there are enough strips for 64 groups
   // (fewer activation bytes per weight byte), then K split across
-  // workgroups until the grid fills the CUs
-#ifndef NS8_GU
-#define NS8_GU 2
-#endif
-#ifndef NS8_DOWN
-#define NS8_DOWN 2
-#endif
+  // workgroups until the grid fills the CUs.  (Four strips with twice the
+  // K splits measured slower for bf16 and for fp8 codes alike: the larger
+  // split-K exchange costs more than the activation loads it saves.)
   pl.ns = nstrips >= 128 ? 2 : 1;
-  if (f8) pl.ns = nstrips >= 512 ? NS8_DOWN : nstrips >= 128 ? NS8_GU : 1;
   const int ngroups = (nstrips + pl.ns - 1) / pl.ns;
   pl.splitk = 1;
   if (split_ok) {
