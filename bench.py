@@ -48,16 +48,20 @@ BF16_PEAK_TFLOPS = 2516.6    # MI355X dense bf16 MFMA (256 CUs x 4096 flop/clk x
 # HBM bytes per launch of the roofline kernel (the packed gate/up GEMM) from
 # rocprofv3 PMC (FETCH_SIZE + WRITE_SIZE, each scaled by what the same counter
 # reads for a plain copy of known size: run with --rows calib), keyed by the
-# sha256 of the kernel's source file when the counters were taken; reported
+# sha256 of the kernel's source files when the counters were taken; reported
 # as null once that source has changed.
-TRAFFIC_GATE_UP = 129_636_791
-TRAFFIC_SOURCE_SHA256 = "fcb7e7f2f481416adff7ec598fca9bf6936fd4afc4855e521dbe92d76aeaa2e1"
-KERNEL_SOURCE = os.path.join(ROOT, "tensor_sharded_transformer_amd", "csrc", "gemm_packed.hip")
+TRAFFIC_GATE_UP = 129_610_172
+TRAFFIC_SOURCE_SHA256 = "8e406fa2741883332f9055aef70e891cc8560e7d084ea0dc02de10ec0fa6f1af"
+KERNEL_SOURCES = [os.path.join(ROOT, "tensor_sharded_transformer_amd", "csrc", f)
+                  for f in ("gemm_packed.hip", "tp_device.h", "tp_kernels.h")]
 
 
-def source_sha256(path: str) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def source_sha256(paths) -> str:
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def log(*a):
@@ -180,10 +184,10 @@ def main() -> int:
     k_ms = time_gpu(gate_up, args.steps, args.warmup)
     k_bytes = (2 * d * ff_i + T * d + T * ff_i) * 2
     k_gbs = k_bytes / (k_ms * 1e-3) / 1e9
-    fresh = TRAFFIC_SOURCE_SHA256 is not None and source_sha256(KERNEL_SOURCE) == TRAFFIC_SOURCE_SHA256
+    fresh = TRAFFIC_SOURCE_SHA256 is not None and source_sha256(KERNEL_SOURCES) == TRAFFIC_SOURCE_SHA256
     roofline = {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": TRAFFIC_GATE_UP if fresh else None,
-                "kernel": "packed_gemm_kernel<4, 2, true, 2, unsigned short>: fused gate/up weight-streaming "
+                "kernel": "packed_gemm_kernel<4, 2, true, 2, unsigned short, false>: fused gate/up weight-streaming "
                           "GEMM with the SwiGLU epilogue, packed weights",
                 "algorithmic_bytes": k_bytes, "avg_launch_us": round(k_ms * 1e3, 2)}
     log(f"bench: gate/up GEMM {k_ms * 1e3:.1f} us -> {k_gbs:.0f} GB/s")
