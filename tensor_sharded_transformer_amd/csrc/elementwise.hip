@@ -102,20 +102,41 @@ __global__ __launch_bounds__(256) void partial_sum_kernel(const SumArgs a, int p
       float acc[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-      for (int i = 0; i < p; ++i) {
+      // the partials in batches of 8: a batch's loads are all issued before
+      // the first is added (one memory round trip per batch, not per
+      // partial), then added in ascending i
+      for (int i0 = 0; i0 < p; i0 += 8) {
+        const int nb = p - i0 < 8 ? p - i0 : 8;
         if constexpr (IN_BF16) {
-          const uint4 w = reinterpret_cast<const uint4*>(a.z[i])[v];
-          const uint32_t* ww = reinterpret_cast<const uint32_t*>(&w);
+          uint4 w[8];  // unconditional loads (straight-line code); slots past p re-read partial i0
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            acc[2 * q] += bf2f((uint16_t)(ww[q] & 0xffffu));
-            acc[2 * q + 1] += bf2f((uint16_t)(ww[q] >> 16));
+          for (int b = 0; b < 8; ++b) w[b] = reinterpret_cast<const uint4*>(a.z[i0 + (b < nb ? b : 0)])[v];
+#pragma unroll
+          for (int b = 0; b < 8; ++b) {
+            if (b < nb) {
+              const uint32_t ww[4] = {w[b].x, w[b].y, w[b].z, w[b].w};
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                acc[2 * q] += bf2f((uint16_t)(ww[q] & 0xffffu));
+                acc[2 * q + 1] += bf2f((uint16_t)(ww[q] >> 16));
+              }
+            }
           }
         } else {
-          const float4 w0 = reinterpret_cast<const float4*>(a.z[i])[2 * v];
-          const float4 w1 = reinterpret_cast<const float4*>(a.z[i])[2 * v + 1];
-          acc[0] += w0.x; acc[1] += w0.y; acc[2] += w0.z; acc[3] += w0.w;
-          acc[4] += w1.x; acc[5] += w1.y; acc[6] += w1.z; acc[7] += w1.w;
+          float4 w0[8], w1[8];
+#pragma unroll
+          for (int b = 0; b < 8; ++b) {
+            const float4* z = reinterpret_cast<const float4*>(a.z[i0 + (b < nb ? b : 0)]);
+            w0[b] = z[2 * v];
+            w1[b] = z[2 * v + 1];
+          }
+#pragma unroll
+          for (int b = 0; b < 8; ++b) {
+            if (b < nb) {
+              acc[0] += w0[b].x; acc[1] += w0[b].y; acc[2] += w0[b].z; acc[3] += w0[b].w;
+              acc[4] += w1[b].x; acc[5] += w1[b].y; acc[6] += w1[b].z; acc[7] += w1[b].w;
+            }
+          }
         }
       }
       if (bias) {
