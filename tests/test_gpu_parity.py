@@ -1221,6 +1221,38 @@ def test_row_linear_partial_packed(out, T, K, N):
     assert_close(z, O.row_linear_partial(O.to64(x), O.to64(w)), BF16_TOL, "row partial packed")
 
 
+def test_gqa_projections_packed_decode_T64_all_ranks():
+    """The decode GQA projections on packed weights, as the bench times them
+    (70B-class, T=64): QKV of ranks 0 and 7 (all 64 rows) against the oracle,
+    and the eight ranks' packed o_proj partials summed against the unsharded
+    product (and rank 0's partial alone)."""
+    wl = W.GQA_DECODE
+    t = W.gqa_unsharded(wl)
+    x = cuda(t["x"])
+    x64 = O.to64(t["x"])
+    wsq = tp.new_workspace(tp.tp_linear_packed_workspace(wl.T, wl.h, 1280, "none"))
+    parts = []
+    for i in range(wl.p):
+        qb, ql, kb, kl = tp.tp_gqa_shard(wl.n_q, wl.n_kv, wl.head_dim, wl.p, i)
+        if i in (0, wl.p - 1):
+            wqkv = torch.cat([t["wq"][:, qb:qb + ql], t["wk"][:, kb:kb + kl], t["wv"][:, kb:kb + kl]], 1).contiguous()
+            qkv = torch.full((wl.T, 1280), 7.0, dtype=torch.bfloat16, device="cuda")
+            tp.tp_col_linear_packed(x, pk(wqkv), None, None, qkv, "none", wl.h, 1280, wsq)
+            ref = O.matmul(x64, O.gqa_local_qkv_weight(t["wq"], t["wk"], t["wv"], wl.n_q, wl.n_kv, wl.head_dim,
+                                                       wl.p, i))
+            assert_close(qkv, ref, BF16_TOL, f"packed qkv rank {i}")
+        a_i = cuda(t["attn"][:, qb:qb + ql])
+        wso = tp.new_workspace(tp.tp_linear_packed_workspace(wl.T, ql, wl.h))
+        o_i = torch.full((wl.T, wl.h), 7.0, dtype=torch.bfloat16, device="cuda")
+        tp.tp_row_linear_partial_packed(a_i, pk(t["wo"][qb:qb + ql, :].contiguous()), o_i, wl.h, wso)
+        parts.append(o_i)
+    y = torch.empty(wl.T, wl.h, dtype=torch.float32, device="cuda")
+    tp.tp_partial_sum(parts, None, y)
+    assert_close(y, O.matmul(O.to64(t["attn"]), O.to64(t["wo"])), BF16_TOL, "sum of packed o_proj partials")
+    ref0 = O.matmul(O.to64(t["attn"][:, :1024]), O.to64(t["wo"][:1024]))
+    assert_close(parts[0], ref0, BF16_TOL, "packed o_proj partial rank 0")
+
+
 def test_packed_split_k_qkv_decode_shape_is_deterministic():
     """The rank's fused QKV projection at T=64 (1280 columns: 80 strips, so K
     is split across workgroups): against the oracle, and bitwise run to run."""
