@@ -1253,6 +1253,32 @@ def test_gqa_projections_packed_decode_T64_all_ranks():
     assert_close(parts[0], ref0, BF16_TOL, "packed o_proj partial rank 0")
 
 
+def packed_act_layout_cpu(x):
+    """The packed activation layout written out: chunk (k-block b, 16-row tile
+    i), lane l holds x[16i + l % 16, 32b + 8(l // 16) + j], j = 0..7, zero
+    padded to whole tiles and k-blocks."""
+    T, K = x.shape
+    mt = 1 if T <= 16 else (2 if T <= 32 else 4)
+    nkb = (K + 31) // 32
+    xp = torch.zeros(mt * 16, nkb * 32, dtype=x.dtype)
+    xp[:T, :K] = x
+    return xp.reshape(mt, 16, nkb, 4, 8).permute(2, 0, 3, 1, 4).reshape(-1)
+
+
+@pytest.mark.parametrize("T,K,offset", [(64, 8192, 0), (33, 1000, 0), (16, 72, 0), (17, 3584, 0), (5, 1003, 0),
+                                        (64, 1024, 1)])
+def test_pack_act_is_the_fragment_permutation(T, K, offset):
+    """Whole and ragged tiles (T = 16, 17, 33, 64, 5), ragged k-blocks (K = 1000,
+    1003) and rows 2 bytes off 16-byte alignment (the element-wise load path)."""
+    x = W.normal((T, K), 1.0, 41 + T + K, 1)
+    buf = torch.empty(T * K + offset, dtype=torch.bfloat16, device="cuda")
+    xd = buf[offset:].view(T, K)     # contiguous; offset 1 leaves the rows 2 bytes off 16-byte alignment
+    xd.copy_(cuda(x))
+    want = packed_act_layout_cpu(x)
+    got = tp.tp_pack_act(xd)
+    assert torch.equal(got.view(torch.bfloat16).cpu()[: want.numel()], want)
+
+
 def test_packed_split_k_qkv_decode_shape_is_deterministic():
     """The rank's fused QKV projection at T=64 (1280 columns: 80 strips, so K
     is split across workgroups): against the oracle, and bitwise run to run."""
