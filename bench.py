@@ -51,7 +51,7 @@ BF16_PEAK_TFLOPS = 2516.6    # MI355X dense bf16 MFMA (256 CUs x 4096 flop/clk x
 # sha256 of the kernel's source files when the counters were taken; reported
 # as null once that source has changed.
 TRAFFIC_GATE_UP = 129_610_172
-TRAFFIC_SOURCE_SHA256 = "8e406fa2741883332f9055aef70e891cc8560e7d084ea0dc02de10ec0fa6f1af"
+TRAFFIC_SOURCE_SHA256 = "61aefca1dc08f9a819bc00cf2b572c30c693c15f29df4d836bcbb9c0256eb323"
 KERNEL_SOURCES = [os.path.join(ROOT, "tensor_sharded_transformer_amd", "csrc", f)
                   for f in ("gemm_packed.hip", "tp_device.h", "tp_kernels.h")]
 

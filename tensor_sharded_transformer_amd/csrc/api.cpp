@@ -655,7 +655,10 @@ tp_status tp_moe_shard_fwd(const void* x, const int32_t* idx, const float* gate,
   p2.c_rows = dst;
   if (!tpk::gemm_tile_supported(p2, plan, tpk::GK_FWD_STORE))
     return fail(TP_ERR_UNSUPPORTED, "tp_moe_shard_fwd: no grouped kernel for these operands");
-  e = tpk::gemm_tile(p2, plan, tpk::GK_FWD_STORE, zs_f32, s);
+  // a short contraction (ff_i <= 128) with bf16 rows: one workgroup per row
+  // tile walks all of d with its rows of h held in LDS
+  if (!zs_f32 && tpk::gemm_walk_supported(p2, T * k)) e = tpk::gemm_walk(p2, s);
+  else e = tpk::gemm_tile(p2, plan, tpk::GK_FWD_STORE, zs_f32, s);
   if (e != hipSuccess) return hip_status(e, "tp_moe_shard_fwd (down GEMM)");
   return hip_status(tpk::moe_combine(base + L.zs, zs_f32, pos_of, gate, (int)T, k, (int)d, y_i, out_dtype == TP_F32, s),
                     "tp_moe_shard_fwd (combine)");

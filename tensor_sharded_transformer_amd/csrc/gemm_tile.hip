@@ -163,6 +163,21 @@ struct OpTile {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(src_of(c) ? r1 : r0, dst, 16, off, 0, 0, 0);
     }
   }
+
+  // The same k-tile through registers (single source): fetch loads this
+  // thread's chunks (masked ones read as zeros), put writes them to the LDS
+  // slots issue() would fill.
+  __device__ __forceinline__ void fetch(const void* base, int kvalid, u32x4 (&r)[NL]) const {
+    static_assert(!DUAL, "one source");
+    const __amdgpu_buffer_rsrc_t rs = rsrc_at(base);
+#pragma unroll
+    for (int c = 0; c < NL; ++c)
+      r[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, kidx[c] < kvalid ? voff[c] : OOB, 0, 0));
+  }
+  __device__ __forceinline__ void put(char* lds, int tid, const u32x4 (&r)[NL]) const {
+#pragma unroll
+    for (int c = 0; c < NL; ++c) *reinterpret_cast<u32x4*>(lds + (c * NT + tid) * 16) = r[c];
+  }
 };
 
 // Lane-constant part of the LDS byte offset of an MFMA fragment whose 32
@@ -214,6 +229,7 @@ __device__ __forceinline__ void wait_loads_barrier() {
   else if constexpr (N == 12) __asm__ volatile("s_waitcnt vmcnt(12)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   else if constexpr (N == 32) __asm__ volatile("s_waitcnt vmcnt(32)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   else if constexpr (N == 48) __asm__ volatile("s_waitcnt vmcnt(48)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 63) __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // LDS only
   else static_assert(N == 0, "add the vmcnt value here");
 }
 
@@ -644,6 +660,201 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(const GemmPar
   });
 }
 
+// Column walk for a short contraction (K <= NKT * 64) with a bf16 output:
+// the grouped down GEMM of the MoE block, whose K is one rank's slice of an
+// expert's hidden size.  There a BM x BN tile does only BM * BN * K * 2
+// flops per BM * BN * 2 bytes it stores, so a workgroup per tile pays its
+// start-up (operand loads, pipeline fill) for very little work.  Here one
+// workgroup owns a BM-row tile and walks every BN-column tile of N: the A rows
+// (all of K) are loaded into LDS once, and per column tile only B is loaded,
+// the MFMAs run over the k-substeps that hold data, and the tile is stored
+// through a per-wave LDS patch as 16-byte row pieces.  The next column tile's
+// B is loaded into registers while the current tile's MFMAs run and written
+// to LDS after them, and the stores drain while the next tile computes
+// (buffer stores: a masked lane gets an out-of-range offset instead of a
+// branch).
+// Grouped mode and row tables as in gemm_tile_kernel (tile_expert, a_rows,
+// c_rows).
+// NS: 16-value k-substeps run per column tile (K0 <= 16 * NS; substeps past K0
+// read zeros).
+template <int BM, int BN, int WGM, int WGN, int NS>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_walk_kernel(const GemmParams p) {
+  constexpr int NT = 64 * WGM * WGN;
+  constexpr int WM = BM / WGM, WN = BN / WGN;
+  constexpr int TM = WM / 32, TN = WN / 32;
+  constexpr int NKT = (NS + NSUB - 1) / NSUB;  // k-tiles of 64 held in LDS
+  static_assert(NS >= 2 && NS % 2 == 0 && NKT <= 2, "two to eight substeps, an even number");
+  using TA = OpTile<BM, true, false, NT>;
+  using TB = OpTile<BN, false, false, NT>;
+  constexpr int PITCH = 80;                   // bytes per patch row: 64 + 16 of padding
+  constexpr int NRD = TM + TN * 2;            // LDS fragment reads per substep
+  __shared__ __attribute__((aligned(1024))) char sa0[TA::BYTES];
+  __shared__ __attribute__((aligned(1024))) char sa1[NKT > 1 ? TA::BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) char sb0[TB::BYTES];
+  __shared__ __attribute__((aligned(1024))) char sb1[NKT > 1 ? TB::BYTES : 16];
+  __shared__ __attribute__((aligned(16))) char patches[NT / 64 * 32 * PITCH];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WGN;
+  const int wn = wave % WGN;
+  const int mt = xcd_remap(blockIdx.x, gridDim.x);
+  const int m0 = mt * BM;
+  const uint16_t* gB = reinterpret_cast<const uint16_t*>(p.B0);
+  if (p.tile_expert) {
+    const int ex = p.tile_expert[mt];
+    if (ex < 0) return;
+    gB += ex * p.b_expert_stride;
+  }
+
+  TA ta;
+  TB tb;
+  if (p.a_rows) ta.setup_rows(tid, m0, p.M, p.lda, p.a_rows);
+  else ta.setup(tid, m0, p.M, p.lda);
+  auto issue_a = [&](int kt, char* st) {
+    const int kvalid = p.K0 - kt * TBK;
+    const uint16_t* a = reinterpret_cast<const uint16_t*>(p.A0);
+    if (kvalid > 0) a += (p.a_rows ? 0 : (int64_t)m0 * p.lda) + kt * TBK;
+    ta.issue(a, a, kvalid, st, wave);
+  };
+  auto issue_b = [&](int kt, int n0, char* st) {
+    const int kvalid = p.K0 - kt * TBK;
+    const uint16_t* b = gB;
+    if (kvalid > 0) b += (int64_t)kt * TBK * p.ldb + n0;
+    tb.issue(b, b, kvalid, st, wave);
+  };
+
+  int ao0[TM], ao1[TM], bo0[TN], bo1[TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) frag_offsets<BM, true, false>(wm * WM + i * 32, lane, &ao0[i], &ao1[i]);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) frag_offsets<BN, false, false>(wn * WN + j * 32, lane, &bo0[j], &bo1[j]);
+
+  // byte offsets of the destination rows of this lane's two stores per
+  // 32-row fragment (the same for every column tile; below 2^31, which the
+  // host checks); OOB: not stored
+  uint32_t crow[TM][2];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int m = m0 + wm * WM + i * 32 + q * 16 + (lane >> 2);
+      const int r = m >= p.M ? -1 : (p.c_rows ? p.c_rows[m] : m);
+      crow[i][q] = r < 0 ? OOB : (uint32_t)r * (uint32_t)(p.ldc * 2);
+    }
+  const __amdgpu_buffer_rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(p.C, 0, 0x7FFFFFFF, 0x00020000);
+  char* patch = patches + wave * 32 * PITCH;
+
+  tb.setup(tid, 0, p.N, p.ldb);
+  issue_a(0, sa0);
+  if constexpr (NKT > 1) issue_a(1, sa1);
+  issue_b(0, 0, sb0);
+  if constexpr (NKT > 1) issue_b(1, 0, sb1);
+  wait_loads_barrier<0>();
+  // the same wait, visible to the compiler: with the LDS-bound loads known to
+  // be complete it puts no wait for them before the loop's fragment reads
+  // (one that would also wait for the stores queued behind them)
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+
+  const int tiles_n = (p.N + BN - 1) / BN;
+  f32x16 acc[TM][TN];
+  bf16x8 af[2][TM];
+  bf16x8 bf[2][TN];
+  u32x4 breg[NKT][TB::NL];  // the next column tile's B, in flight during this tile's MFMAs
+  for (int tn = 0; tn < tiles_n; ++tn) {
+    const int n0 = tn * BN;
+    const bool more = tn + 1 < tiles_n;
+    if (more) {
+      tb.setup(tid, n0 + BN, p.N, p.ldb);
+      static_for<0, NKT>([&](auto kc) __attribute__((always_inline)) {
+        constexpr int kt = decltype(kc)::value;
+        const int kvalid = p.K0 - kt * TBK;
+        const uint16_t* b = gB;
+        if (kvalid > 0) b += (int64_t)kt * TBK * p.ldb + n0 + BN;
+        tb.fetch(b, kvalid, breg[kt]);
+      });
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    // substep s reads its fragments while the MFMAs of substep s - 1 run
+    static_for<0, NS>([&](auto sc) __attribute__((always_inline)) {
+      constexpr int st = decltype(sc)::value;
+      constexpr int buf = st & 1;
+      const char* sa = st / NSUB == 0 ? sa0 : sa1;
+      const char* sb = st / NSUB == 0 ? sb0 : sb1;
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[buf][i] = read_frag<BM, true, false>(sa, ao0[i], ao1[i], st % NSUB);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bf[buf][j] = read_frag<BN, false, false>(sb, bo0[j], bo1[j], st % NSUB);
+      if constexpr (st > 0) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf ^ 1][i], bf[buf ^ 1][j], acc[i][j], 0, 0, 0);
+        interleave<TM * TN, NRD, 0, 0>();
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    constexpr int lb = (NS - 1) & 1;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[lb][i], bf[lb][j], acc[i][j], 0, 0, 0);
+
+    // every wave has read this tile's B: put the next one in its place
+    wait_loads_barrier<63>();
+    if (more) {
+      tb.put(sb0, tid, breg[0]);
+      if constexpr (NKT > 1) tb.put(sb1, tid, breg[NKT - 1]);
+    }
+
+    // epilogue: accumulator register r of fragment (i, j) is row
+    // 8(r/4) + 4(lane/32) + r%4, column lane%32; through the patch each lane
+    // stores 16 bytes of one row (8 columns)
+    static_for<0, TM>([&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      static_for<0, TN>([&](auto jc) __attribute__((always_inline)) {
+        constexpr int j = decltype(jc)::value;
+        const int ncol = n0 + wn * WN + j * 32;
+        // registers r and r + 1 (r even) are neighbouring rows: one conversion
+        // for the pair, then a 2-byte write each
+        static_for<0, 8>([&](auto rc) __attribute__((always_inline)) {
+          constexpr int r = 2 * decltype(rc)::value;
+          const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const uint32_t two = f2bf2(acc[i][j][r], acc[i][j][r + 1]);
+          *reinterpret_cast<uint16_t*>(patch + row * PITCH + (lane & 31) * 2) = (uint16_t)two;
+          *reinterpret_cast<uint16_t*>(patch + (row + 1) * PITCH + (lane & 31) * 2) = (uint16_t)(two >> 16);
+        });
+        // one wave's LDS operations complete in order: the reads see the writes
+        static_for<0, 2>([&](auto qc) __attribute__((always_inline)) {
+          constexpr int q = decltype(qc)::value;
+          const int row = q * 16 + (lane >> 2);
+          const int cc = (lane & 3) * 8;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(patch + row * PITCH + cc * 2);
+          const uint32_t off = crow[i][q] == OOB || ncol + cc >= p.N ? OOB : crow[i][q] + (uint32_t)(ncol + cc) * 2;
+          __builtin_amdgcn_raw_buffer_store_b128(v, cr, off, 0, 0);
+        });
+      });
+    });
+    // the next tile's B is in LDS for every wave (the stores keep draining)
+    wait_loads_barrier<63>();
+  }
+}
+
+template <int BM, int BN, int WGM, int WGN, int NS>
+hipError_t launch_walk(const GemmParams& p, hipStream_t s) {
+  const int grid = (p.M + BM - 1) / BM;
+  hipLaunchKernelGGL((gemm_walk_kernel<BM, BN, WGM, WGN, NS>), dim3(grid), dim3(64 * WGM * WGN), 0, s, p);
+  return hipGetLastError();
+}
+
 template <int BM, int BN, int WGM, int WGN, int STAGES, bool AKC, bool BKC, bool DUAL, int EPI, typename OutT>
 hipError_t launch_tile(const GemmParams& p, hipStream_t s) {
   constexpr int BNH = DUAL ? BN / 2 : BN;
@@ -686,6 +897,26 @@ bool gemm_tile_supported(const GemmParams& p, const GemmPlan& plan, GemmKind kin
   if (p.c_rows && (kind != GK_FWD_STORE || p.C2 || p.cpk)) return false;
   if (!bkc && p.N % 8) return false;
   return true;
+}
+
+// The column walk: a forward store GEMM (A k-contiguous, B (K, N)
+// n-contiguous) with a bf16 output, K <= 128, every stored byte offset below
+// 2^31 (c_max_row: the largest output row plus one).
+bool gemm_walk_supported(const GemmParams& p, int64_t c_max_row) {
+  GemmPlan plan;
+  plan.kernel = KERNEL_TILED;
+  plan.tile = TILE_256x256;
+  if (!gemm_tile_supported(p, plan, GK_FWD_STORE)) return false;
+  if (p.A1 || p.K1 || p.B1 || p.C2 || p.cpk || p.K0 < 1 || p.K0 > 2 * TBK) return false;
+  if (p.ldc % 8 || p.ldc < p.N || ((uintptr_t)p.C & 15)) return false;
+  return c_max_row * p.ldc * 2 < (int64_t)OOB - 64;
+}
+
+hipError_t gemm_walk(const GemmParams& p, hipStream_t s) {
+  if (p.K0 <= 32) return launch_walk<256, 256, TILE_WGM_256, TILE_WGN_256, 2>(p, s);
+  if (p.K0 <= 64) return launch_walk<256, 256, TILE_WGM_256, TILE_WGN_256, 4>(p, s);
+  if (p.K0 <= 96) return launch_walk<256, 256, TILE_WGM_256, TILE_WGN_256, 6>(p, s);
+  return launch_walk<256, 256, TILE_WGM_256, TILE_WGN_256, 8>(p, s);
 }
 
 hipError_t gemm_tile(const GemmParams& p, const GemmPlan& plan, GemmKind kind, bool out_f32, hipStream_t s) {

@@ -31,6 +31,13 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
   return (uint16_t)(u >> 16);
 }
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+// Two floats to two bf16 (lo in bits 0-15) with the hardware conversion
+// (v_cvt_pk_bf16_f32: round to nearest even, one instruction for the pair).
+__device__ __forceinline__ uint32_t f2bf2(float lo, float hi) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
+}
 
 // Activations in fp32 (exact erf GELU; silu(g) = g * sigmoid(g)).
 // 1 / (1 + e^-g) from the hardware 2^x and reciprocal (v_exp_f32, v_rcp_f32,

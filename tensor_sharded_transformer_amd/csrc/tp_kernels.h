@@ -90,6 +90,11 @@ hipError_t gemm_decode(const GemmParams& p, const GemmPlan& plan, GemmKind kind,
 // The pipelined tiled kernel, for plans and operands it supports.
 bool gemm_tile_supported(const GemmParams& p, const GemmPlan& plan, GemmKind kind);
 hipError_t gemm_tile(const GemmParams& p, const GemmPlan& plan, GemmKind kind, bool out_f32, hipStream_t s);
+// Column walk of the tiled kernel (one workgroup per 256-row tile walks every
+// column tile; A held in LDS): forward store GEMMs with K <= 128 and a bf16
+// output whose stored byte offsets (rows below c_max_row) stay below 2^31.
+bool gemm_walk_supported(const GemmParams& p, int64_t c_max_row);
+hipError_t gemm_walk(const GemmParams& p, hipStream_t s);
 
 // Packed-weight decode GEMM (gemm_packed.hip): weights stored once in 1 KB
 // MFMA B-fragment chunks (16-column strips of 32-row k-blocks; fp8 codes: of

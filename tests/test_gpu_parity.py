@@ -997,7 +997,7 @@ def moe_run(t, k, out_dt=torch.bfloat16):
 
 
 @pytest.mark.parametrize("T,d,ff_i,E,k", [(1, 64, 32, 4, 2), (77, 256, 96, 16, 4), (300, 512, 200, 8, 8),
-                                         (513, 128, 64, 64, 1)])
+                                         (513, 128, 64, 64, 1), (200, 640, 120, 8, 2), (64, 384, 40, 4, 3)])
 def test_moe_small(T, d, ff_i, E, k):
     wl = W.MoeWorkload("moe_small", T=T, d=d, ff=ff_i, E=E, k=k, p=1, seed=40 + T)
     t = W.moe_rank_inputs(wl)
