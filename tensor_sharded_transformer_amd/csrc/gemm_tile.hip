@@ -498,14 +498,20 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(const GemmPar
           if constexpr (EPI == EPI_ACT) {
             if (p.bias && n < p.N) bias = bf2f(reinterpret_cast<const uint16_t*>(p.bias)[n]);
           }
-          static_for<0, 16>([&](auto rc) __attribute__((always_inline)) {
+          auto value = [&](auto rc) __attribute__((always_inline)) {
             constexpr int r = decltype(rc)::value;
-            float v;
-            if constexpr (EPI == EPI_STORE) v = acc[i][j][r];
-            else if constexpr (EPI == EPI_ACT) v = act_fwd(p.act, acc[i][j][r] + bias);
-            else v = acc[i][j][r] * sigmoidf_(acc[i][j][r]) * acc[i][j + TNO][r];
+            if constexpr (EPI == EPI_STORE) return acc[i][j][r];
+            else if constexpr (EPI == EPI_ACT) return act_fwd(p.act, acc[i][j][r] + bias);
+            else return acc[i][j][r] * sigmoidf_(acc[i][j][r]) * acc[i][j + TNO][r];
+          };
+          // registers r and r + 1 (r even) are neighbouring rows: one
+          // conversion for the pair, then a 2-byte write each
+          static_for<0, 8>([&](auto rc) __attribute__((always_inline)) {
+            constexpr int r = 2 * decltype(rc)::value;
             const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            *reinterpret_cast<uint16_t*>(patch + row * PITCH + (lane & 31) * 2) = f2bf(v);
+            const uint32_t two = f2bf2(value(std::integral_constant<int, r>{}), value(std::integral_constant<int, r + 1>{}));
+            *reinterpret_cast<uint16_t*>(patch + row * PITCH + (lane & 31) * 2) = (uint16_t)two;
+            *reinterpret_cast<uint16_t*>(patch + (row + 1) * PITCH + (lane & 31) * 2) = (uint16_t)(two >> 16);
           });
           // one wave's LDS operations complete in order: the reads see the writes
           static_for<0, 2>([&](auto qc) __attribute__((always_inline)) {
@@ -568,30 +574,27 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_tile_kernel(const GemmPar
               u32x4 o0, o2, o3;
 #pragma unroll
               for (int w = 0; w < 4; ++w) {
-                uint32_t r0 = 0, r2 = 0, r3 = 0;
+                float v0[2], v2[2] = {0.0f, 0.0f}, v3[2];
 #pragma unroll
                 for (int hw = 0; hw < 2; ++hw) {
                   const int e = 2 * w + hw;
                   const float a = bf2f((uint16_t)(sa[w] >> (16 * hw)));
-                  float v0, v2 = 0.0f, v3;
                   if constexpr (EPI == EPI_SWIGLU_BWD) {
                     const float u = bf2f((uint16_t)(sb[w] >> (16 * hw)));
                     const float s = sigmoidf_(a);
                     const float sg = a * s;
-                    v0 = dh[e] * u * (s + sg * (1.0f - s));
-                    v2 = dh[e] * sg;
-                    v3 = sg * u;
+                    v0[hw] = dh[e] * u * (s + sg * (1.0f - s));
+                    v2[hw] = dh[e] * sg;
+                    v3[hw] = sg * u;
                   } else {
-                    v0 = dh[e] * act_grad(p.act, a);
-                    v3 = act_fwd(p.act, a);
+                    v0[hw] = dh[e] * act_grad(p.act, a);
+                    v3[hw] = act_fwd(p.act, a);
                   }
-                  r0 |= (uint32_t)f2bf(v0) << (16 * hw);
-                  r2 |= (uint32_t)f2bf(v2) << (16 * hw);
-                  r3 |= (uint32_t)f2bf(v3) << (16 * hw);
                 }
-                o0[w] = r0;
-                o2[w] = r2;
-                o3[w] = r3;
+                // neighbouring columns: one conversion per pair
+                o0[w] = f2bf2(v0[0], v0[1]);
+                o2[w] = f2bf2(v2[0], v2[1]);
+                o3[w] = f2bf2(v3[0], v3[1]);
               }
               *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.C) + (int64_t)m * p.ldc + n) = o0;
               if (two_sides) *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.C2) + (int64_t)m * p.ldc2 + n) = o2;
