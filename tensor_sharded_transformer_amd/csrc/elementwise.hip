@@ -47,7 +47,7 @@ __global__ __launch_bounds__(256) void act_bf16_kernel(uint16_t* h, const uint16
         a0 = act_fwd(act, a0);
         a1 = act_fwd(act, a1);
       }
-      hw[q] = (uint32_t)f2bf(a0) | ((uint32_t)f2bf(a1) << 16);
+      hw[q] = f2bf2(a0, a1);
     }
     reinterpret_cast<uint4*>(h)[v] = hv;
   }
@@ -149,10 +149,10 @@ __global__ __launch_bounds__(256) void partial_sum_kernel(const SumArgs a, int p
       }
       if constexpr (OUT_BF16) {
         uint4 o;
-        o.x = (uint32_t)f2bf(acc[0]) | ((uint32_t)f2bf(acc[1]) << 16);
-        o.y = (uint32_t)f2bf(acc[2]) | ((uint32_t)f2bf(acc[3]) << 16);
-        o.z = (uint32_t)f2bf(acc[4]) | ((uint32_t)f2bf(acc[5]) << 16);
-        o.w = (uint32_t)f2bf(acc[6]) | ((uint32_t)f2bf(acc[7]) << 16);
+        o.x = f2bf2(acc[0], acc[1]);
+        o.y = f2bf2(acc[2], acc[3]);
+        o.z = f2bf2(acc[4], acc[5]);
+        o.w = f2bf2(acc[6], acc[7]);
         reinterpret_cast<uint4*>(y)[v] = o;
       } else {
         reinterpret_cast<float4*>(y)[2 * v] = make_float4(acc[0], acc[1], acc[2], acc[3]);
@@ -236,10 +236,10 @@ template <typename T>
 __device__ __forceinline__ void st8(void* p, int64_t i, const float (&v)[8]) {
   if constexpr (std::is_same<T, uint16_t>::value) {
     uint4 o;
-    o.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-    o.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
-    o.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
-    o.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
+    o.x = f2bf2(v[0], v[1]);
+    o.y = f2bf2(v[2], v[3]);
+    o.z = f2bf2(v[4], v[5]);
+    o.w = f2bf2(v[6], v[7]);
     *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p) + i) = o;
   } else {
     *reinterpret_cast<float4*>(reinterpret_cast<float*>(p) + i) = make_float4(v[0], v[1], v[2], v[3]);

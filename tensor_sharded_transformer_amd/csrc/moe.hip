@@ -273,8 +273,8 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const ZT* __restrict__
     *reinterpret_cast<float4*>(y + (int64_t)t * d + c) = s;
   } else {
     uint2 o;
-    o.x = (uint32_t)f2bf(s.x) | ((uint32_t)f2bf(s.y) << 16);
-    o.y = (uint32_t)f2bf(s.z) | ((uint32_t)f2bf(s.w) << 16);
+    o.x = f2bf2(s.x, s.y);
+    o.y = f2bf2(s.z, s.w);
     *reinterpret_cast<uint2*>(y + (int64_t)t * d + c) = o;
   }
 }
