@@ -23,6 +23,9 @@ The same JSON line carries:
                 residual, then RMSNorm);
   cpu_baseline  the fp64 oracle computing the same decode step on the host.
 
+Rows named context_* time something that is not this library (the vendor
+GEMM, torch.matmul on hipBLASLt, on the prefill shapes) for comparison.
+
     python bench.py [--steps K] [--warmup W] [--rows all|none|prefill,gqa,bwd,sum,calib]
 
 --rows calib adds a plain device-to-device copy of 117,440,512 bytes (five
@@ -360,7 +363,19 @@ def main() -> int:
         fl = 2 * Tp * d * ff_i
         rows["prefill_down_gemm"] = {"us": round(t_ * 1e3, 1), "TFLOP/s": round(fl / t_ / 1e9, 1),
                                      "frac_mfma": round(fl / t_ / 1e9 / BF16_PEAK_TFLOPS, 4)}
-        del xp, yp, wsp, hp
+        # context, not this library: the vendor GEMM (torch.matmul -> hipBLASLt)
+        # on the same two shapes, without the activation epilogue
+        wcat = torch.cat([sets[0]["w1"], sets[0]["w_up"]], dim=1)
+        zc = torch.empty(Tp, 2 * ff_i, dtype=torch.bfloat16, device=dev)
+        t_ = time_gpu(lambda i: torch.matmul(xp, wcat, out=zc), steps_r, 3)
+        fl = 2 * 2 * Tp * d * ff_i
+        rows["context_vendor_matmul_4096x8192x7168"] = {"us": round(t_ * 1e3, 1), "TFLOP/s": round(fl / t_ / 1e9, 1),
+                                                        "frac_mfma": round(fl / t_ / 1e9 / BF16_PEAK_TFLOPS, 4)}
+        t_ = time_gpu(lambda i: torch.matmul(hp, sets[0]["w2"], out=yp), steps_r, 3)
+        fl = 2 * Tp * d * ff_i
+        rows["context_vendor_matmul_4096x3584x8192"] = {"us": round(t_ * 1e3, 1), "TFLOP/s": round(fl / t_ / 1e9, 1),
+                                                        "frac_mfma": round(fl / t_ / 1e9 / BF16_PEAK_TFLOPS, 4)}
+        del xp, yp, wsp, hp, wcat, zc
 
     if "gqa" in want:
         h_, q_, o_ = 8192, 1280, 1024
