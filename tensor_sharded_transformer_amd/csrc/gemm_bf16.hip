@@ -407,12 +407,16 @@ GemmPlan plan_gemm(int M, int N, int K, bool dual, bool fwd_layout, bool vec_ok,
     plan.splitk = allow_split ? split : 1;
     return plan;
   }
-  // Tile size by estimated time: rounds of 256 CUs times the time of one tile.
-  // A 256x256 tile (8 waves) has 4x the work of a 128x128 one (4 waves) and
-  // runs at ~1.24 vs ~1.0 PFLOP/s, so it takes ~3.2x as long.
+  // Tile size by estimated time: rounds of 256 CUs times the time of one
+  // round.  A round of 256x256 tiles (8 waves) has 4x the work of a round of
+  // 128x128 ones (4 waves) and measures ~2.2x as long at K ~ 4096 (107 vs
+  // 48 us: the small tiles load twice the bytes per flop through the shared
+  // L2-to-CU path), so 256x256 wins once it needs fewer than 1/2.2 of the
+  // rounds (attention-projection backward dW_qkv, 640 -> 160 tiles: 121 ->
+  // ~100 us).
   const int r256 = (tiles_for(256, 256) + CUS - 1) / CUS;
   const int r128 = (tiles_for(128, 128) + CUS - 1) / CUS;
-  plan.tile = r256 * 32 < r128 * 10 ? TILE_256x256 : TILE_128x128;
+  plan.tile = r256 * 22 < r128 * 10 ? TILE_256x256 : TILE_128x128;
   plan.splitk = 1;
   if (plan.tile == TILE_128x128 && tiles_for(128, 128) <= CUS) {
     // At most one 128x128 tile per CU: with a workspace, split K in two so
