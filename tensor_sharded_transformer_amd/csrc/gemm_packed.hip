@@ -22,7 +22,11 @@
 //    b * mt + i, lane l holding X[16i + l%16][32b + 8(l/16) + j] (the A
 //    operand); rows >= M and k >= K are zero.  A packing pass writes it (x is
 //    small and every workgroup reads all of it from L2); the SwiGLU epilogue
-//    of the column GEMM writes h straight into it for the row GEMM.
+//    of the column GEMM writes h straight into it for the row GEMM.  For a
+//    short contraction (K <= 1024, a multiple of 32) the packing launch costs
+//    more than it saves, and the fragments are read from row-major x
+//    instead (16 bytes of one row per lane; two k-blocks share each 128-byte
+//    line of a row).
 //
 // A workgroup owns NS strips (NS * 16 output columns, gate and up together in
 // dual mode) and a K range.  Its KW waves each stream a contiguous share of
@@ -88,6 +92,19 @@ __device__ __forceinline__ void load_step(KStep<MT, NF>& r, const u32x4* const (
   for (int f = 0; f < NF; ++f) r.b[f] = bp[f][kb * kb_stride];
 #pragma unroll
   for (int i = 0; i < MT; ++i) r.a[i] = ap[((int64_t)kb * MT + i) * 64];
+}
+
+// The same with the activation fragments read from row-major x: lane l of
+// tile i holds row 16 i + l % 16, columns 32 kb + 8 (l / 16) .. + 7 (16
+// bytes); rows past M (row_ok false) hold zeros.
+template <int MT, int NF>
+__device__ __forceinline__ void load_step_rm(KStep<MT, NF>& r, const u32x4* const (&bp)[NF], const uint16_t* xl,
+                                             int64_t lda16, const bool (&row_ok)[MT], int kb, int64_t kb_stride) {
+#pragma unroll
+  for (int f = 0; f < NF; ++f) r.b[f] = bp[f][kb * kb_stride];
+#pragma unroll
+  for (int i = 0; i < MT; ++i)
+    r.a[i] = row_ok[i] ? *reinterpret_cast<const u32x4*>(xl + i * lda16 + kb * 32) : u32x4{0u, 0u, 0u, 0u};
 }
 
 // Four fp8 codes -> four bf16 values in two words, low code first.
@@ -241,7 +258,7 @@ __device__ __forceinline__ void store_tile(const PackedParams& p, int i, int gs,
   }
 }
 
-template <int MT, int NS, bool DUAL, int EPI, typename OutT, bool F8>
+template <int MT, int NS, bool DUAL, int EPI, typename OutT, bool F8, bool RM>
 __global__ __launch_bounds__(KW * 64) void packed_gemm_kernel(const PackedParams params) {
   constexpr int AT = F8 ? 2 * MT : MT;       // activation chunks per ring step (fp8: a k-pair)
   constexpr int NB = DUAL ? 2 : 1;           // weight matrices
@@ -280,6 +297,16 @@ __global__ __launch_bounds__(KW * 64) void packed_gemm_kernel(const PackedParams
     bp[j] = reinterpret_cast<const u32x4*>(m ? p.B1 : p.B0) + (int64_t)strip * 64 + lane;
   }
   const u32x4* ap = reinterpret_cast<const u32x4*>(p.A) + lane;
+  // row-major activations (RM): this lane's row and k offset, and which of its rows exist
+  const uint16_t* xl = nullptr;
+  int64_t lda16 = 0;
+  bool row_ok[MT];
+  if constexpr (RM) {
+    xl = p.xrm + (int64_t)(lane & 15) * p.xlda + (lane >> 4) * 8;
+    lda16 = 16 * p.xlda;
+#pragma unroll
+    for (int i = 0; i < MT; ++i) row_ok[i] = 16 * i + (lane & 15) < p.M;
+  }
 
   f32x4 acc[MT][WF];
 #pragma unroll
@@ -302,11 +329,15 @@ __global__ __launch_bounds__(KW * 64) void packed_gemm_kernel(const PackedParams
       if constexpr (F8) mma_step_f8<MT, WF>(r, acc);
       else mma_step<MT, WF>(r, acc);
     };
-    static_for<0, DEPTH>([&](auto d) { load_step<AT, WF>(ring[d], bp, ap, phys(d), kbs); });
+    static_for<0, DEPTH>([&](auto d) {
+      if constexpr (RM) load_step_rm<AT, WF>(ring[d], bp, xl, lda16, row_ok, phys(d), kbs);
+      else load_step<AT, WF>(ring[d], bp, ap, phys(d), kbs);
+    });
     for (int it = 0; it < q - DEPTH; it += DEPTH) {
       static_for<0, DEPTH>([&](auto d) {
         mma(ring[d]);  // it + d < q - DEPTH <= n - 1
-        load_step<AT, WF>(ring[d], bp, ap, phys(it + DEPTH + (int)d), kbs);
+        if constexpr (RM) load_step_rm<AT, WF>(ring[d], bp, xl, lda16, row_ok, phys(it + DEPTH + (int)d), kbs);
+        else load_step<AT, WF>(ring[d], bp, ap, phys(it + DEPTH + (int)d), kbs);
         // keep the ring order: without this the scheduler hoists all of an
         // iteration's loads above its MFMAs into fresh registers and then
         // waits for the whole previous ring at the top of the next iteration
@@ -479,8 +510,16 @@ __global__ __launch_bounds__(256) void pack_weight16_kernel(const uint16_t* __re
 template <int MT, int NS, bool DUAL, int EPI, typename OutT, bool F8>
 hipError_t launch_ns(const PackedParams& p, hipStream_t s) {
   const int ngroups = (p.nstrips + NS - 1) / NS;
-  hipLaunchKernelGGL((packed_gemm_kernel<MT, NS, DUAL, EPI, OutT, F8>), dim3(ngroups * p.splitk), dim3(KW * 64), 0, s,
-                     p);
+  if constexpr (!F8) {
+    if (p.xrm) {
+      hipLaunchKernelGGL((packed_gemm_kernel<MT, NS, DUAL, EPI, OutT, F8, true>), dim3(ngroups * p.splitk),
+                         dim3(KW * 64), 0, s, p);
+      return hipGetLastError();
+    }
+  }
+  if (p.xrm) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((packed_gemm_kernel<MT, NS, DUAL, EPI, OutT, F8, false>), dim3(ngroups * p.splitk),
+                     dim3(KW * 64), 0, s, p);
   return hipGetLastError();
 }
 

@@ -1355,6 +1355,33 @@ def test_linear_packed_gemm_on_prepacked_activations(act, out):
     assert torch.equal(y, ref)
 
 
+@pytest.mark.parametrize("T,K,act", [(64, 1024, "none"), (37, 1024, "swiglu"), (1, 32, "gelu"), (17, 544, "none"),
+                                     (64, 992, "relu")])
+def test_packed_linears_reading_row_major_x(T, K, act):
+    """Short contractions (K <= 1024, a multiple of 32) read the activation
+    fragments straight from row-major x (rows past T as zeros) instead of a
+    packed copy: against the oracle, and bitwise against the same GEMM on x
+    packed beforehand (only the source of the fragments differs)."""
+    N = 520
+    seed = 7 * T + K
+    x = W.normal((T, K), 1.0, seed, 1)
+    w = W.normal((K, N), 0.05, seed, 2)
+    wu = W.normal((K, N), 0.05, seed, 3) if act == "swiglu" else None
+    wp, wup = pk(w), None if wu is None else pk(wu)
+    ws = tp.new_workspace(tp.tp_linear_packed_workspace(T, K, N, act))
+    y = torch.full((T, N), 7.0, dtype=torch.bfloat16, device="cuda")
+    if act == "none":
+        tp.tp_row_linear_partial_packed(cuda(x), wp, y, N, ws)
+        ref = O.row_linear_partial(O.to64(x), O.to64(w))
+    else:
+        tp.tp_col_linear_packed(cuda(x), wp, wup, None, y, act, K, N, ws)
+        ref = O.col_linear(O.to64(x), O.to64(w), None if wu is None else O.to64(wu), None, act)
+    assert_close(y, ref, BF16_TOL, f"row-major x, T={T} K={K} {act}")
+    via_packed = tp.tp_linear_packed_gemm(tp.tp_pack_act(cuda(x)), wp, wup, None,
+                                          torch.empty(T, N, dtype=torch.bfloat16, device="cuda"), act, K, ws)
+    assert torch.equal(y, via_packed)
+
+
 @pytest.mark.parametrize("act,K", [("swiglu", 2048), ("gelu", 1000), ("swiglu", 1000)])
 def test_decode_size_linears_without_a_workspace(act, K):
     """Decode-size calls made without a workspace run unsplit (slower,
