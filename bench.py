@@ -53,8 +53,8 @@ BF16_PEAK_TFLOPS = 2516.6    # MI355X dense bf16 MFMA (256 CUs x 4096 flop/clk x
 # reads for a plain copy of known size: run with --rows calib), keyed by the
 # sha256 of the kernel's source files when the counters were taken; reported
 # as null once that source has changed.
-TRAFFIC_GATE_UP = 129_610_172
-TRAFFIC_SOURCE_SHA256 = "61aefca1dc08f9a819bc00cf2b572c30c693c15f29df4d836bcbb9c0256eb323"
+TRAFFIC_GATE_UP = 129_616_315
+TRAFFIC_SOURCE_SHA256 = "0d826771634274c11ca439e83bd5ab13eef4031593f8513caff9dceca33efad8"
 KERNEL_SOURCES = [os.path.join(ROOT, "tensor_sharded_transformer_amd", "csrc", f)
                   for f in ("gemm_packed.hip", "tp_device.h", "tp_kernels.h")]
 
