@@ -54,7 +54,7 @@ BF16_PEAK_TFLOPS = 2516.6    # MI355X dense bf16 MFMA (256 CUs x 4096 flop/clk x
 # sha256 of the kernel's source files when the counters were taken; reported
 # as null once that source has changed.
 TRAFFIC_GATE_UP = 129_616_315
-TRAFFIC_SOURCE_SHA256 = "0d826771634274c11ca439e83bd5ab13eef4031593f8513caff9dceca33efad8"
+TRAFFIC_SOURCE_SHA256 = "98f22b54ea77debe6ce0452e40cf43fb3a8a14f011047b79f28003945ca201a6"
 KERNEL_SOURCES = [os.path.join(ROOT, "tensor_sharded_transformer_amd", "csrc", f)
                   for f in ("gemm_packed.hip", "tp_device.h", "tp_kernels.h")]
 

@@ -933,12 +933,19 @@ tpk::PackedParams packed_params(const void* A, const void* B0, const void* B1, i
   return p;
 }
 
-// Short contractions read the activations straight from row-major x (bf16):
-// the packing launch measured slower there (o_proj at T=64, K=1024: 11.5 ->
-// 9.3 us without it), longer ones slower without it (QKV, K=8192: 15.2 ->
-// 18.1 us), because each row-major fragment load touches 16 half lines.
-bool rowmajor_x(tpk::PackedParams& p, const void* x, int64_t K) {
-  if (K > 1024 || K % 32 != 0 || !aligned16(x)) return false;
+// Launches that read few activation bytes in all take them straight from
+// row-major x (bf16 weights): every workgroup reads its K range of x, so a
+// launch reads (strip groups) x K x 32 x mt bytes of fragments, and a
+// row-major fragment load touches 16 half lines where a packed one touches 8
+// full ones.  Measured at T=64 (packing launch -> row-major reads): o_proj
+// K=1024 N=8192 11.5 -> 9.3 us (34 MB of fragments), K=2048 N=2048 12.2 ->
+// 9.6 us (17 MB), K=4096 N=1280 12.3 -> 11.8 us (42 MB); slower from 67 MB
+// on (K=2048 N=8192 14.3 -> 15.6 us, QKV K=8192 N=1280 15.2 -> 18.1 us, the
+// decode gate/up), where the packing launch stays.
+bool rowmajor_x(tpk::PackedParams& p, const tpk::PackedPlan& pl, const void* x, int64_t K) {
+  if (K % 32 != 0 || !aligned16(x)) return false;
+  const int64_t groups = (p.nstrips + pl.ns - 1) / pl.ns;
+  if (groups * K * 32 * p.mt > ((int64_t)48 << 20)) return false;
   p.xrm = reinterpret_cast<const uint16_t*>(x);
   p.xlda = K;
   return true;
@@ -1006,7 +1013,7 @@ tp_status tp_col_linear_packed(const void* x, const void* w_packed, const void* 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* base = reinterpret_cast<char*>(ws);
   tpk::PackedParams p = packed_params(base + L.x_off, w_packed, sw ? w_up_packed : nullptr, T, K, N_i, L.p1, base, L);
-  if (!rowmajor_x(p, x, K)) {
+  if (!rowmajor_x(p, L.p1, x, K)) {
     const hipError_t e = tpk::pack_act16(x, K, (int)T, (int)K, aligned16(x) && K % 8 == 0, base + L.x_off, s);
     if (e != hipSuccess) return hip_status(e, who);
   }
@@ -1033,7 +1040,7 @@ tp_status tp_row_linear_partial_packed(const void* x_i, const void* w_packed, vo
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* base = reinterpret_cast<char*>(ws);
   tpk::PackedParams p = packed_params(base + L.x_off, w_packed, nullptr, T, K_i, N, L.p1, base, L);
-  if (!rowmajor_x(p, x_i, K_i)) {
+  if (!rowmajor_x(p, L.p1, x_i, K_i)) {
     const hipError_t e = tpk::pack_act16(x_i, K_i, (int)T, (int)K_i, aligned16(x_i) && K_i % 8 == 0, base + L.x_off, s);
     if (e != hipSuccess) return hip_status(e, who);
   }
@@ -1124,7 +1131,7 @@ tp_status tp_mlp_shard_fwd_packed(const void* x, const void* w1_packed, const vo
   tpk::PackedParams p1 = packed_params(base + L.x_off, w1_packed, sw ? w_up_packed : nullptr, T, d, ff_i, L.p1,
                                        base, L);
   hipError_t e = hipSuccess;
-  if (!rowmajor_x(p1, x, d)) {
+  if (!rowmajor_x(p1, L.p1, x, d)) {
     e = tpk::pack_act16(x, d, (int)T, (int)d, aligned16(x) && d % 8 == 0, base + L.x_off, s);
     if (e != hipSuccess) return hip_status(e, who);
   }

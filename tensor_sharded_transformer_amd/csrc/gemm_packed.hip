@@ -22,11 +22,11 @@
 //    b * mt + i, lane l holding X[16i + l%16][32b + 8(l/16) + j] (the A
 //    operand); rows >= M and k >= K are zero.  A packing pass writes it (x is
 //    small and every workgroup reads all of it from L2); the SwiGLU epilogue
-//    of the column GEMM writes h straight into it for the row GEMM.  For a
-//    short contraction (K <= 1024, a multiple of 32) the packing launch costs
-//    more than it saves, and the fragments are read from row-major x
-//    instead (16 bytes of one row per lane; two k-blocks share each 128-byte
-//    line of a row).
+//    of the column GEMM writes h straight into it for the row GEMM.  When a
+//    launch reads few activation bytes in all (K a multiple of 32), the
+//    packing launch costs more than it saves, and the fragments are read
+//    from row-major x instead (16 bytes of one row per lane; two k-blocks
+//    share each 128-byte line of a row).
 //
 // A workgroup owns NS strips (NS * 16 output columns, gate and up together in
 // dual mode) and a K range.  Its KW waves each stream a contiguous share of

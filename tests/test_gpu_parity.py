@@ -1356,12 +1356,13 @@ def test_linear_packed_gemm_on_prepacked_activations(act, out):
 
 
 @pytest.mark.parametrize("T,K,act", [(64, 1024, "none"), (37, 1024, "swiglu"), (1, 32, "gelu"), (17, 544, "none"),
-                                     (64, 992, "relu")])
+                                     (64, 992, "relu"), (48, 4096, "swiglu")])
 def test_packed_linears_reading_row_major_x(T, K, act):
-    """Short contractions (K <= 1024, a multiple of 32) read the activation
-    fragments straight from row-major x (rows past T as zeros) instead of a
-    packed copy: against the oracle, and bitwise against the same GEMM on x
-    packed beforehand (only the source of the fragments differs)."""
+    """Launches that read few activation bytes in all (here N = 520: 33
+    strip groups; K a multiple of 32) take the activation fragments straight
+    from row-major x (rows past T as zeros) instead of a packed copy: against
+    the oracle, and bitwise against the same GEMM on x packed beforehand (only
+    the source of the fragments differs)."""
     N = 520
     seed = 7 * T + K
     x = W.normal((T, K), 1.0, seed, 1)
