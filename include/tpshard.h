@@ -332,7 +332,12 @@ tp_status tp_pack_weight(const void* w, void* w_packed, int64_t K, int64_t N, tp
  * tp_mlp_shard_fwd_workspace's) of tp_col_linear_packed and
  * tp_row_linear_partial_packed (act TP_ACT_NONE for the latter); 0 for T == 0
  * or T > 64.  The workspace is required: it holds x rearranged into the
- * matrix cores' operand order. */
+ * matrix cores' operand order (a launch of its own) and the split-K
+ * partials.  Calls whose GEMM reads few activation bytes in all (K a
+ * multiple of 32, x 16-byte aligned, at most 48 MiB of operand fragments:
+ * ceil(N/16 / strips per workgroup) * K * 32 * ceil(T/16 rounded to 1, 2,
+ * 4) bytes) read x in place instead and skip that launch; the results are
+ * bitwise the same either way. */
 size_t tp_linear_packed_workspace(int64_t T, int64_t K, int64_t N, tp_act act);
 
 /* tp_col_linear with packed weights ([KL] Y_i = X W_i; [FFN] "First matmul,
