@@ -53,8 +53,8 @@ BF16_PEAK_TFLOPS = 2516.6    # MI355X dense bf16 MFMA (256 CUs x 4096 flop/clk x
 # reads for a plain copy of known size: run with --rows calib), keyed by the
 # sha256 of the kernel's source files when the counters were taken; reported
 # as null once that source has changed.
-TRAFFIC_GATE_UP = 129_616_315
-TRAFFIC_SOURCE_SHA256 = "98f22b54ea77debe6ce0452e40cf43fb3a8a14f011047b79f28003945ca201a6"
+TRAFFIC_GATE_UP = 129_610_172
+TRAFFIC_SOURCE_SHA256 = "7cfeb7dc3e19bc7b226295410bd38fe815c18232ccf243a56eae6084b398e8ce"
 KERNEL_SOURCES = [os.path.join(ROOT, "tensor_sharded_transformer_amd", "csrc", f)
                   for f in ("gemm_packed.hip", "tp_device.h", "tp_kernels.h")]
 

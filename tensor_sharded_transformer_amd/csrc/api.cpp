@@ -942,8 +942,8 @@ tpk::PackedParams packed_params(const void* A, const void* B0, const void* B1, i
 // 9.6 us (17 MB), K=4096 N=1280 12.3 -> 11.8 us (42 MB); slower from 67 MB
 // on (K=2048 N=8192 14.3 -> 15.6 us, QKV K=8192 N=1280 15.2 -> 18.1 us, the
 // decode gate/up), where the packing launch stays.
-bool rowmajor_x(tpk::PackedParams& p, const tpk::PackedPlan& pl, const void* x, int64_t K) {
-  if (K % 32 != 0 || !aligned16(x)) return false;
+bool rowmajor_x(tpk::PackedParams& p, const tpk::PackedPlan& pl, const void* x, int64_t K, bool f8 = false) {
+  if (K % (f8 ? 64 : 32) != 0 || !aligned16(x)) return false;  // fp8: whole k-pairs
   const int64_t groups = (p.nstrips + pl.ns - 1) / pl.ns;
   if (groups * K * 32 * p.mt > ((int64_t)48 << 20)) return false;
   p.xrm = reinterpret_cast<const uint16_t*>(x);
@@ -1241,10 +1241,12 @@ tp_status tp_col_linear_packed_fp8(const void* x, const void* wq_packed, const f
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* base = reinterpret_cast<char*>(ws);
   const int nkb = (int)(kpair_pad(K) / 32);
-  hipError_t e = tpk::pack_act16(x, K, (int)T, (int)K, aligned16(x) && K % 8 == 0, base + L.x_off, s, nkb);
-  if (e != hipSuccess) return hip_status(e, who);
   tpk::PackedParams p = packed8_params(base + L.x_off, wq_packed, scale, sw ? wq_up_packed : nullptr,
                                        sw ? scale_up : nullptr, T, K, N_i, L.p1, base, L);
+  if (!rowmajor_x(p, L.p1, x, K, true)) {
+    const hipError_t e = tpk::pack_act16(x, K, (int)T, (int)K, aligned16(x) && K % 8 == 0, base + L.x_off, s, nkb);
+    if (e != hipSuccess) return hip_status(e, who);
+  }
   p.C = y;
   p.ldc = N_i;
   p.vec_out = rows_vec16(y, N_i, 2);
@@ -1271,9 +1273,12 @@ tp_status tp_row_linear_partial_packed_fp8(const void* x_i, const void* wq_packe
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* base = reinterpret_cast<char*>(ws);
   const int nkb = (int)(kpair_pad(K_i) / 32);
-  hipError_t e = tpk::pack_act16(x_i, K_i, (int)T, (int)K_i, aligned16(x_i) && K_i % 8 == 0, base + L.x_off, s, nkb);
-  if (e != hipSuccess) return hip_status(e, who);
   tpk::PackedParams p = packed8_params(base + L.x_off, wq_packed, scale_i, nullptr, nullptr, T, K_i, N, L.p1, base, L);
+  if (!rowmajor_x(p, L.p1, x_i, K_i, true)) {
+    const hipError_t e =
+        tpk::pack_act16(x_i, K_i, (int)T, (int)K_i, aligned16(x_i) && K_i % 8 == 0, base + L.x_off, s, nkb);
+    if (e != hipSuccess) return hip_status(e, who);
+  }
   p.C = z_i;
   p.ldc = N;
   p.vec_out = rows_vec16(z_i, N, esize(out_dtype));
@@ -1315,11 +1320,14 @@ tp_status tp_mlp_shard_fwd_packed_fp8(const void* x, const void* wq1_packed, con
   if (st != TP_OK) return st;
   char* base = reinterpret_cast<char*>(ws);
   const int nkb = (int)(kpair_pad(d) / 32);
-  hipError_t e = tpk::pack_act16(x, d, (int)T, (int)d, aligned16(x) && d % 8 == 0, base + L.x_off, s, nkb);
-  if (e != hipSuccess) return hip_status(e, who);
   // column GEMM: h = act(x W1_i [, x W_up_i]) straight into the row GEMM's packed activations
   tpk::PackedParams p1 = packed8_params(base + L.x_off, wq1_packed, s1_i, sw ? wq_up_packed : nullptr,
                                         sw ? s_up_i : nullptr, T, d, ff_i, L.p1, base, L);
+  hipError_t e = hipSuccess;
+  if (!rowmajor_x(p1, L.p1, x, d, true)) {
+    e = tpk::pack_act16(x, d, (int)T, (int)d, aligned16(x) && d % 8 == 0, base + L.x_off, s, nkb);
+    if (e != hipSuccess) return hip_status(e, who);
+  }
   p1.cpk = base + L.h_off;
   p1.cpk_mt = tpk::packed_mt((int)T);
   p1.act = act;

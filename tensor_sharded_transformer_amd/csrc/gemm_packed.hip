@@ -95,16 +95,22 @@ __device__ __forceinline__ void load_step(KStep<MT, NF>& r, const u32x4* const (
 }
 
 // The same with the activation fragments read from row-major x: lane l of
-// tile i holds row 16 i + l % 16, columns 32 kb + 8 (l / 16) .. + 7 (16
-// bytes); rows past M (row_ok false) hold zeros.
-template <int MT, int NF>
-__device__ __forceinline__ void load_step_rm(KStep<MT, NF>& r, const u32x4* const (&bp)[NF], const uint16_t* xl,
-                                             int64_t lda16, const bool (&row_ok)[MT], int kb, int64_t kb_stride) {
+// tile i holds row 16 i + l % 16, columns 32 b + 8 (l / 16) .. + 7 (16 bytes)
+// of k-block b (ring step kb; with fp8 codes a ring step is the k-pair 2 kb,
+// 2 kb + 1, tiles of k-block 2 kb first); rows past M (row_ok false) hold
+// zeros.
+template <int MT, int NF, bool F8>
+__device__ __forceinline__ void load_step_rm(KStep<F8 ? 2 * MT : MT, NF>& r, const u32x4* const (&bp)[NF],
+                                             const uint16_t* xl, int64_t lda16, const bool (&row_ok)[MT], int kb,
+                                             int64_t kb_stride) {
+  constexpr int AT = F8 ? 2 * MT : MT;
 #pragma unroll
   for (int f = 0; f < NF; ++f) r.b[f] = bp[f][kb * kb_stride];
 #pragma unroll
-  for (int i = 0; i < MT; ++i)
-    r.a[i] = row_ok[i] ? *reinterpret_cast<const u32x4*>(xl + i * lda16 + kb * 32) : u32x4{0u, 0u, 0u, 0u};
+  for (int c = 0; c < AT; ++c) {
+    const int i = c % MT, b = (F8 ? 2 * kb : kb) + c / MT;
+    r.a[c] = row_ok[i] ? *reinterpret_cast<const u32x4*>(xl + i * lda16 + b * 32) : u32x4{0u, 0u, 0u, 0u};
+  }
 }
 
 // Four fp8 codes -> four bf16 values in two words, low code first.
@@ -330,13 +336,13 @@ __global__ __launch_bounds__(KW * 64) void packed_gemm_kernel(const PackedParams
       else mma_step<MT, WF>(r, acc);
     };
     static_for<0, DEPTH>([&](auto d) {
-      if constexpr (RM) load_step_rm<AT, WF>(ring[d], bp, xl, lda16, row_ok, phys(d), kbs);
+      if constexpr (RM) load_step_rm<MT, WF, F8>(ring[d], bp, xl, lda16, row_ok, phys(d), kbs);
       else load_step<AT, WF>(ring[d], bp, ap, phys(d), kbs);
     });
     for (int it = 0; it < q - DEPTH; it += DEPTH) {
       static_for<0, DEPTH>([&](auto d) {
         mma(ring[d]);  // it + d < q - DEPTH <= n - 1
-        if constexpr (RM) load_step_rm<AT, WF>(ring[d], bp, xl, lda16, row_ok, phys(it + DEPTH + (int)d), kbs);
+        if constexpr (RM) load_step_rm<MT, WF, F8>(ring[d], bp, xl, lda16, row_ok, phys(it + DEPTH + (int)d), kbs);
         else load_step<AT, WF>(ring[d], bp, ap, phys(it + DEPTH + (int)d), kbs);
         // keep the ring order: without this the scheduler hoists all of an
         // iteration's loads above its MFMAs into fresh registers and then
@@ -510,14 +516,11 @@ __global__ __launch_bounds__(256) void pack_weight16_kernel(const uint16_t* __re
 template <int MT, int NS, bool DUAL, int EPI, typename OutT, bool F8>
 hipError_t launch_ns(const PackedParams& p, hipStream_t s) {
   const int ngroups = (p.nstrips + NS - 1) / NS;
-  if constexpr (!F8) {
-    if (p.xrm) {
-      hipLaunchKernelGGL((packed_gemm_kernel<MT, NS, DUAL, EPI, OutT, F8, true>), dim3(ngroups * p.splitk),
-                         dim3(KW * 64), 0, s, p);
-      return hipGetLastError();
-    }
+  if (p.xrm) {
+    hipLaunchKernelGGL((packed_gemm_kernel<MT, NS, DUAL, EPI, OutT, F8, true>), dim3(ngroups * p.splitk),
+                       dim3(KW * 64), 0, s, p);
+    return hipGetLastError();
   }
-  if (p.xrm) return hipErrorInvalidValue;
   hipLaunchKernelGGL((packed_gemm_kernel<MT, NS, DUAL, EPI, OutT, F8, false>), dim3(ngroups * p.splitk),
                      dim3(KW * 64), 0, s, p);
   return hipGetLastError();

@@ -120,9 +120,10 @@ struct PackedParams {
   int act;
   const float* bscale0;  // fp8 weights: per-column scales of B0 / B1, applied to the sums
   const float* bscale1;
-  // bf16 weights only: if set, the activation fragments are read straight
-  // from row-major x (M, K) with rows of xlda elements (K a multiple of 32,
-  // x and its rows 16-byte aligned; rows past M read as zeros) instead of A
+  // If set, the activation fragments are read straight from row-major x
+  // (M, K) with rows of xlda elements (K a multiple of 32, of 64 with fp8
+  // codes; x and its rows 16-byte aligned; rows past M read as zeros)
+  // instead of A
   const uint16_t* xrm;
   int64_t xlda;
 };

@@ -1383,6 +1383,39 @@ def test_packed_linears_reading_row_major_x(T, K, act):
     assert torch.equal(y, via_packed)
 
 
+@pytest.mark.parametrize("T,K,act", [(64, 1024, "none"), (37, 1024, "swiglu"), (1, 64, "gelu"), (33, 4096, "none")])
+def test_packed_fp8_linears_reading_row_major_x(T, K, act):
+    """The packed fp8 linears take their bf16 activation fragments straight
+    from row-major x when K is a multiple of 64 and the launch reads few
+    activation bytes: against the oracle, and bitwise against the same call
+    on an unaligned copy of x (which takes the packing launch)."""
+    N = 520
+    seed = 5 * T + K
+    x = W.normal((T, K), 1.0, seed, 1)
+    q = W.e4m3_codes((K, N), seed, 2)
+    sc = W.column_scales(N, seed, 3)
+    qu = W.e4m3_codes((K, N), seed, 4) if act == "swiglu" else None
+    su = W.column_scales(N, seed, 5) if act == "swiglu" else None
+    qp, qup = packed8(q), None if qu is None else packed8(qu)
+    c, cu = cuda(sc), None if su is None else cuda(su)
+    ws = tp.new_workspace(tp.tp_linear_packed_fp8_workspace(T, K, N, act))
+    xa = cuda(x)
+    buf = torch.empty(T * K + 1, dtype=torch.bfloat16, device="cuda")
+    xu = buf[1:].view(T, K)      # 2 bytes past a 16-byte boundary: packed by a launch of its own
+    xu.copy_(xa)
+    outs = []
+    for xin in (xa, xu):
+        y = torch.full((T, N), 7.0, dtype=torch.bfloat16, device="cuda")
+        if act == "none":
+            tp.tp_row_linear_partial_packed_fp8(xin, qp, c, y, N, ws)
+        else:
+            tp.tp_col_linear_packed_fp8(xin, qp, c, qup, cu, None, y, act, K, N, ws)
+        outs.append(y)
+    ref = (O.row_linear_partial_fp8(x, q, sc) if act == "none" else O.col_linear_fp8(x, q, sc, qu, su, None, act))
+    assert_close(outs[0], ref, BF16_TOL, f"fp8 row-major x, T={T} K={K} {act}")
+    assert torch.equal(outs[0], outs[1])
+
+
 @pytest.mark.parametrize("act,K", [("swiglu", 2048), ("gelu", 1000), ("swiglu", 1000)])
 def test_decode_size_linears_without_a_workspace(act, K):
     """Decode-size calls made without a workspace run unsplit (slower,
