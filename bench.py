@@ -190,7 +190,7 @@ def main() -> int:
     fresh = TRAFFIC_SOURCE_SHA256 is not None and source_sha256(KERNEL_SOURCES) == TRAFFIC_SOURCE_SHA256
     roofline = {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": TRAFFIC_GATE_UP if fresh else None,
-                "kernel": "packed_gemm_kernel<4, 2, true, 2, unsigned short, false>: fused gate/up weight-streaming "
+                "kernel": "packed_gemm_kernel<4, 2, true, 2, unsigned short, false, false>: fused gate/up weight-streaming "
                           "GEMM with the SwiGLU epilogue, packed weights",
                 "algorithmic_bytes": k_bytes, "avg_launch_us": round(k_ms * 1e3, 2)}
     log(f"bench: gate/up GEMM {k_ms * 1e3:.1f} us -> {k_gbs:.0f} GB/s")
