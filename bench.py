@@ -53,8 +53,8 @@ BF16_PEAK_TFLOPS = 2516.6    # MI355X dense bf16 MFMA (256 CUs x 4096 flop/clk x
 # reads for a plain copy of known size: run with --rows calib), keyed by the
 # sha256 of the kernel's source files when the counters were taken; reported
 # as null once that source has changed.
-TRAFFIC_GATE_UP = 129_610_172
-TRAFFIC_SOURCE_SHA256 = "7cfeb7dc3e19bc7b226295410bd38fe815c18232ccf243a56eae6084b398e8ce"
+TRAFFIC_GATE_UP = 129_627_585
+TRAFFIC_SOURCE_SHA256 = "1acda0a0d13ae7d149c2187ced402430966a79a66047042833b05c7c0c92eebc"
 KERNEL_SOURCES = [os.path.join(ROOT, "tensor_sharded_transformer_amd", "csrc", f)
                   for f in ("gemm_packed.hip", "tp_device.h", "tp_kernels.h")]
 
@@ -190,7 +190,7 @@ def main() -> int:
     fresh = TRAFFIC_SOURCE_SHA256 is not None and source_sha256(KERNEL_SOURCES) == TRAFFIC_SOURCE_SHA256
     roofline = {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": TRAFFIC_GATE_UP if fresh else None,
-                "kernel": "packed_gemm_kernel<4, 2, true, 2, unsigned short, false, false>: fused gate/up weight-streaming "
+                "kernel": "packed_gemm_kernel<4, 2, true, 2, unsigned short, false, false, 8>: fused gate/up weight-streaming "
                           "GEMM with the SwiGLU epilogue, packed weights",
                 "algorithmic_bytes": k_bytes, "avg_launch_us": round(k_ms * 1e3, 2)}
     log(f"bench: gate/up GEMM {k_ms * 1e3:.1f} us -> {k_gbs:.0f} GB/s")

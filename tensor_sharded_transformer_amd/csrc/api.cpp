@@ -891,7 +891,7 @@ size_t counter_region(size_t units) {
 // One GEMM (p1 only; h_off == part_off): x (T, K) -> (T, N).
 PackedLayout packed_linear_layout(int64_t T, int64_t K, int64_t N, bool dual) {
   PackedLayout L;
-  L.p1 = tpk::plan_packed((int)T, (int)N, (int)K, true);
+  L.p1 = tpk::plan_packed((int)T, (int)N, (int)K, true, false, dual);
   L.x_off = counter_region(tpk::packed_units((int)T, (int)N, L.p1));
   L.h_off = L.x_off + tpk::align_up(tpk::packed_act_bytes((int)T, (int)K), 256);
   L.part_off = L.h_off;
@@ -902,7 +902,7 @@ PackedLayout packed_linear_layout(int64_t T, int64_t K, int64_t N, bool dual) {
 // The feed-forward shard: x (T, d) -> h (T, ff_i), packed -> y (T, d).
 PackedLayout packed_fwd_layout(int64_t T, int64_t d, int64_t ff_i, bool dual) {
   PackedLayout L;
-  L.p1 = tpk::plan_packed((int)T, (int)ff_i, (int)d, true);
+  L.p1 = tpk::plan_packed((int)T, (int)ff_i, (int)d, true, false, dual);
   L.p2 = tpk::plan_packed((int)T, (int)d, (int)ff_i, true);
   const size_t u1 = tpk::packed_units((int)T, (int)ff_i, L.p1), u2 = tpk::packed_units((int)T, (int)d, L.p2);
   const size_t q1 = tpk::packed_partial_bytes((int)T, (int)ff_i, dual, L.p1);
@@ -1160,7 +1160,7 @@ int64_t kpair_pad(int64_t K) { return (K + 63) / 64 * 64; }
 PackedLayout packed8_linear_layout(int64_t T, int64_t K, int64_t N, bool dual) {
   PackedLayout L;
   const int64_t Kp = kpair_pad(K);
-  L.p1 = tpk::plan_packed((int)T, (int)N, (int)Kp, true, true);
+  L.p1 = tpk::plan_packed((int)T, (int)N, (int)Kp, true, true, dual);
   L.x_off = counter_region(tpk::packed_units((int)T, (int)N, L.p1));
   L.h_off = L.x_off + tpk::align_up(tpk::packed_act_bytes((int)T, (int)Kp), 256);
   L.part_off = L.h_off;
@@ -1172,7 +1172,7 @@ PackedLayout packed8_linear_layout(int64_t T, int64_t K, int64_t N, bool dual) {
 PackedLayout packed8_fwd_layout(int64_t T, int64_t d, int64_t ff_i, bool dual) {
   PackedLayout L;
   const int64_t dp = kpair_pad(d);
-  L.p1 = tpk::plan_packed((int)T, (int)ff_i, (int)dp, true, true);
+  L.p1 = tpk::plan_packed((int)T, (int)ff_i, (int)dp, true, true, dual);
   L.p2 = tpk::plan_packed((int)T, (int)d, (int)ff_i, true, true);
   const size_t u1 = tpk::packed_units((int)T, (int)ff_i, L.p1), u2 = tpk::packed_units((int)T, (int)d, L.p2);
   const size_t q1 = tpk::packed_partial_bytes((int)T, (int)ff_i, dual, L.p1);

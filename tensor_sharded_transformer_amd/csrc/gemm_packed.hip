@@ -61,7 +61,6 @@ namespace {
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int KW = PACKED_KW;           // waves per workgroup
 constexpr int DEPTH = PACKED_DEPTH;     // k-blocks of loads in flight per wave
 constexpr int PATCH = 1280;             // bytes of a wave's store patch (16 fp32 rows of 80 bytes)
 
@@ -73,7 +72,7 @@ template <int WF>
 constexpr int pass_frags() {
   return WF <= 4 ? WF : 4;
 }
-template <int MT, int PF>
+template <int MT, int PF, int KW>
 constexpr int packed_lds_bytes() {
   return KW * MT * PF * 1024 + KW * PATCH;  // cross-wave reduction (one pass) + per-wave store patch
 }
@@ -264,7 +263,7 @@ __device__ __forceinline__ void store_tile(const PackedParams& p, int i, int gs,
   }
 }
 
-template <int MT, int NS, bool DUAL, int EPI, typename OutT, bool F8, bool RM>
+template <int MT, int NS, bool DUAL, int EPI, typename OutT, bool F8, bool RM, int KW>
 __global__ __launch_bounds__(KW * 64) void packed_gemm_kernel(const PackedParams params) {
   constexpr int AT = F8 ? 2 * MT : MT;       // activation chunks per ring step (fp8: a k-pair)
   constexpr int NB = DUAL ? 2 : 1;           // weight matrices
@@ -272,7 +271,7 @@ __global__ __launch_bounds__(KW * 64) void packed_gemm_kernel(const PackedParams
   constexpr int PF = pass_frags<WF>();       // fragments per wave per reduction pass
   constexpr int NPASS = WF / PF;
   static_assert(WF % PF == 0 && PF % NB == 0, "passes hold whole strips");
-  __shared__ __attribute__((aligned(16))) char smem[packed_lds_bytes<MT, PF>()];
+  __shared__ __attribute__((aligned(16))) char smem[packed_lds_bytes<MT, PF, KW>()];
   // Every parameter, requested in one batch at the start and held in SGPRs:
   // a kernel argument first read after the main loop would be a scalar load
   // queued behind the loop's memory traffic, on the launch's critical path.
@@ -513,44 +512,56 @@ __global__ __launch_bounds__(256) void pack_weight16_kernel(const uint16_t* __re
   out[((int64_t)b * nstrips + sg + s) * 64 + lane] = u32x4{q[0], q[1], q[2], q[3]};
 }
 
-template <int MT, int NS, bool DUAL, int EPI, typename OutT, bool F8>
+template <int MT, int NS, bool DUAL, int EPI, typename OutT, bool F8, int KW>
 hipError_t launch_ns(const PackedParams& p, hipStream_t s) {
   const int ngroups = (p.nstrips + NS - 1) / NS;
   if (p.xrm) {
-    hipLaunchKernelGGL((packed_gemm_kernel<MT, NS, DUAL, EPI, OutT, F8, true>), dim3(ngroups * p.splitk),
+    hipLaunchKernelGGL((packed_gemm_kernel<MT, NS, DUAL, EPI, OutT, F8, true, KW>), dim3(ngroups * p.splitk),
                        dim3(KW * 64), 0, s, p);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((packed_gemm_kernel<MT, NS, DUAL, EPI, OutT, F8, false>), dim3(ngroups * p.splitk),
+  hipLaunchKernelGGL((packed_gemm_kernel<MT, NS, DUAL, EPI, OutT, F8, false, KW>), dim3(ngroups * p.splitk),
                      dim3(KW * 64), 0, s, p);
   return hipGetLastError();
 }
 
-template <bool DUAL, int EPI, typename OutT, bool F8>
-hipError_t launch_packed(const PackedParams& p, int ns, hipStream_t s) {
+template <bool DUAL, int EPI, typename OutT, bool F8, int KW>
+hipError_t launch_packed_kw(const PackedParams& p, int ns, hipStream_t s) {
   const int mt = p.mt;
   if (ns == 1) {
-    if (mt == 1) return launch_ns<1, 1, DUAL, EPI, OutT, F8>(p, s);
-    if (mt == 2) return launch_ns<2, 1, DUAL, EPI, OutT, F8>(p, s);
-    if (mt == 4) return launch_ns<4, 1, DUAL, EPI, OutT, F8>(p, s);
+    if (mt == 1) return launch_ns<1, 1, DUAL, EPI, OutT, F8, KW>(p, s);
+    if (mt == 2) return launch_ns<2, 1, DUAL, EPI, OutT, F8, KW>(p, s);
+    if (mt == 4) return launch_ns<4, 1, DUAL, EPI, OutT, F8, KW>(p, s);
   } else if (ns == 2) {
-    if (mt == 1) return launch_ns<1, 2, DUAL, EPI, OutT, F8>(p, s);
-    if (mt == 2) return launch_ns<2, 2, DUAL, EPI, OutT, F8>(p, s);
-    if (mt == 4) return launch_ns<4, 2, DUAL, EPI, OutT, F8>(p, s);
+    if (mt == 1) return launch_ns<1, 2, DUAL, EPI, OutT, F8, KW>(p, s);
+    if (mt == 2) return launch_ns<2, 2, DUAL, EPI, OutT, F8, KW>(p, s);
+    if (mt == 4) return launch_ns<4, 2, DUAL, EPI, OutT, F8, KW>(p, s);
   } else if (ns == 4) {
-    if (mt == 1) return launch_ns<1, 4, DUAL, EPI, OutT, F8>(p, s);
-    if (mt == 2) return launch_ns<2, 4, DUAL, EPI, OutT, F8>(p, s);
-    if (mt == 4) return launch_ns<4, 4, DUAL, EPI, OutT, F8>(p, s);
+    if (mt == 1) return launch_ns<1, 4, DUAL, EPI, OutT, F8, KW>(p, s);
+    if (mt == 2) return launch_ns<2, 4, DUAL, EPI, OutT, F8, KW>(p, s);
+    if (mt == 4) return launch_ns<4, 4, DUAL, EPI, OutT, F8, KW>(p, s);
   }
   return hipErrorInvalidValue;
+}
+
+// The plan's waves per workgroup: PACKED_KW_DUAL for the bf16 dual
+// (gate/up) launches, PACKED_KW for every other.
+template <bool DUAL, int EPI, typename OutT, bool F8>
+hipError_t launch_packed(const PackedParams& p, int ns, int kw, hipStream_t s) {
+  if constexpr (DUAL && !F8) {
+    if (kw == PACKED_KW_DUAL) return launch_packed_kw<DUAL, EPI, OutT, F8, PACKED_KW_DUAL>(p, ns, s);
+  }
+  if (kw != PACKED_KW) return hipErrorInvalidValue;
+  return launch_packed_kw<DUAL, EPI, OutT, F8, PACKED_KW>(p, ns, s);
 }
 
 }  // namespace
 
 int packed_mt(int M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
 
-PackedPlan plan_packed(int M, int N, int K, bool split_ok, bool f8) {
+PackedPlan plan_packed(int M, int N, int K, bool split_ok, bool f8, bool dual) {
   PackedPlan pl;
+  pl.kw = dual && !f8 ? PACKED_KW_DUAL : PACKED_KW;
   const int nstrips = (N + 15) / 16;
   const int nkb = f8 ? (K + 63) / 64 : (K + 31) / 32;  // ring steps along K
   // two strips per workgroup once there are enough strips for 64 groups
@@ -564,7 +575,7 @@ PackedPlan plan_packed(int M, int N, int K, bool split_ok, bool f8) {
   if (split_ok) {
     // split K while the grid stays within one workgroup per CU and every
     // wave keeps at least two k-blocks
-    while (ngroups * (pl.splitk + 1) <= 256 && nkb / (pl.splitk + 1) >= 2 * KW) ++pl.splitk;
+    while (ngroups * (pl.splitk + 1) <= 256 && nkb / (pl.splitk + 1) >= 2 * pl.kw) ++pl.splitk;
   }
   (void)M;
   return pl;
@@ -577,12 +588,12 @@ size_t packed_units(int M, int N, const PackedPlan& pl) {
   const int nstrips = (N + 15) / 16;
   const int ngroups = (nstrips + pl.ns - 1) / pl.ns;
   (void)M;
-  return (size_t)ngroups * KW;
+  return (size_t)ngroups * pl.kw;
 }
 
 size_t packed_partial_bytes(int M, int N, bool dual, const PackedPlan& pl) {
   if (pl.splitk <= 1) return 0;
-  const int uw = (packed_mt(M) * pl.ns + KW - 1) / KW;  // output units per wave
+  const int uw = (packed_mt(M) * pl.ns + pl.kw - 1) / pl.kw;  // output units per wave
   return packed_units(M, N, pl) * pl.splitk * uw * (dual ? 2 : 1) * 1024;
 }
 
@@ -617,10 +628,10 @@ template <bool F8>
 hipError_t gemm_packed_kind(const PackedParams& p, const PackedPlan& pl, GemmKind kind, bool out_f32, hipStream_t s) {
   switch (kind) {
     case GK_FWD_STORE:
-      return out_f32 ? launch_packed<false, EPI_STORE, float, F8>(p, pl.ns, s)
-                     : launch_packed<false, EPI_STORE, uint16_t, F8>(p, pl.ns, s);
-    case GK_FWD_ACT: return launch_packed<false, EPI_ACT, uint16_t, F8>(p, pl.ns, s);
-    case GK_FWD_SWIGLU: return launch_packed<true, EPI_SWIGLU, uint16_t, F8>(p, pl.ns, s);
+      return out_f32 ? launch_packed<false, EPI_STORE, float, F8>(p, pl.ns, pl.kw, s)
+                     : launch_packed<false, EPI_STORE, uint16_t, F8>(p, pl.ns, pl.kw, s);
+    case GK_FWD_ACT: return launch_packed<false, EPI_ACT, uint16_t, F8>(p, pl.ns, pl.kw, s);
+    case GK_FWD_SWIGLU: return launch_packed<true, EPI_SWIGLU, uint16_t, F8>(p, pl.ns, pl.kw, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -40,6 +40,10 @@ constexpr int TILE_GROUP = 8;
 // flight per wave.
 constexpr int PACKED_KW = 4;
 constexpr int PACKED_DEPTH = 4;
+// waves per workgroup of the bf16 dual (gate/up) launches: 8 streams the
+// fused gate/up GEMM 28.4 -> 27.7 us at T=64 (down, QKV and the fp8 launches
+// measured slower with 8)
+constexpr int PACKED_KW_DUAL = 8;
 
 // LDS bytes the streaming kernel needs for M rows and a K range of `ksteps`
 // 16-value steps.
@@ -128,11 +132,12 @@ struct PackedParams {
   int64_t xlda;
 };
 struct PackedPlan {
-  int ns = 1;      // strips per workgroup
-  int splitk = 1;  // workgroups along K
+  int ns = 1;              // strips per workgroup
+  int splitk = 1;          // workgroups along K
+  int kw = PACKED_KW;      // waves per workgroup
 };
 int packed_mt(int M);
-PackedPlan plan_packed(int M, int N, int K, bool split_ok, bool f8 = false);
+PackedPlan plan_packed(int M, int N, int K, bool split_ok, bool f8 = false, bool dual = false);
 size_t packed_act_bytes(int M, int K);
 size_t packed_units(int M, int N, const PackedPlan& pl);
 size_t packed_partial_bytes(int M, int N, bool dual, const PackedPlan& pl);
