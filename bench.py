@@ -13,9 +13,10 @@ distinct weight sets (528 MB) rotate so the 256 MB Infinity Cache cannot serve
 them.  The headline value is algorithmic bytes (weights + x + y_i) per second.
 
 The same JSON line carries:
-  roofline      the dominant kernel (the fused gate/up GEMM on packed weights)
-                launched alone on pre-packed activations and timed with HIP
-                events on its stream: algorithmic bytes / launch time vs 8 TB/s;
+  roofline      the dominant kernel (the fused gate/up GEMM on packed weights,
+                reading row-major x as the step does) launched alone and timed
+                with HIP events on its stream: algorithmic bytes / launch time
+                vs 8 TB/s;
   rows          the other hot-path rows: prefill shard (T=4096), GQA
                 projections (T=4096 and 64), the shard backward (T=2048,
                 d=4096, ff_i=1792), the fp32 sum of partials and the
@@ -53,8 +54,8 @@ BF16_PEAK_TFLOPS = 2516.6    # MI355X dense bf16 MFMA (256 CUs x 4096 flop/clk x
 # reads for a plain copy of known size: run with --rows calib), keyed by the
 # sha256 of the kernel's source files when the counters were taken; reported
 # as null once that source has changed.
-TRAFFIC_GATE_UP = 129_627_585
-TRAFFIC_SOURCE_SHA256 = "1acda0a0d13ae7d149c2187ced402430966a79a66047042833b05c7c0c92eebc"
+TRAFFIC_GATE_UP = 129_663_418
+TRAFFIC_SOURCE_SHA256 = "d145813d46bdafd384cfb0c8b9887c538bfb6f2f52d8122b8ef3239af9e6332b"
 KERNEL_SOURCES = [os.path.join(ROOT, "tensor_sharded_transformer_amd", "csrc", f)
                   for f in ("gemm_packed.hip", "tp_device.h", "tp_kernels.h")]
 
@@ -175,14 +176,13 @@ def main() -> int:
         f"wall {wall:.3f}s")
 
     # ---------------- roofline: the fused gate/up GEMM kernel alone -----------------
-    # one launch per call: the packed GEMM on activations packed beforehand
+    # one launch per call: the packed GEMM reading row-major x, as in the step
     h = torch.empty(T, ff_i, dtype=torch.bfloat16, device=dev)
-    xp = tp.tp_pack_act(x)
     ws_c = tp.new_workspace(tp.tp_linear_packed_workspace(T, d, ff_i, "swiglu"), dev)
 
     def gate_up(i):
         s = psets[i % R]
-        tp.tp_linear_packed_gemm(xp, s["w1"], s["w_up"], None, h, "swiglu", d, ws_c)
+        tp.tp_col_linear_packed(x, s["w1"], s["w_up"], None, h, "swiglu", d, ff_i, ws_c)
 
     k_ms = time_gpu(gate_up, args.steps, args.warmup)
     k_bytes = (2 * d * ff_i + T * d + T * ff_i) * 2
@@ -190,8 +190,8 @@ def main() -> int:
     fresh = TRAFFIC_SOURCE_SHA256 is not None and source_sha256(KERNEL_SOURCES) == TRAFFIC_SOURCE_SHA256
     roofline = {"bound": "hbm", "achieved": round(k_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(k_gbs / HBM_PEAK_GBS, 4), "traffic": TRAFFIC_GATE_UP if fresh else None,
-                "kernel": "packed_gemm_kernel<4, 2, true, 2, unsigned short, false, false, 8>: fused gate/up weight-streaming "
-                          "GEMM with the SwiGLU epilogue, packed weights",
+                "kernel": "packed_gemm_kernel<4, 2, true, 2, unsigned short, false, 2, 8>: fused gate/up weight-streaming "
+                          "GEMM with the SwiGLU epilogue, packed weights, row-major x staged through LDS",
                 "algorithmic_bytes": k_bytes, "avg_launch_us": round(k_ms * 1e3, 2)}
     log(f"bench: gate/up GEMM {k_ms * 1e3:.1f} us -> {k_gbs:.0f} GB/s")
 

@@ -942,10 +942,21 @@ tpk::PackedParams packed_params(const void* A, const void* B0, const void* B1, i
 // 9.6 us (17 MB), K=4096 N=1280 12.3 -> 11.8 us (42 MB); slower from 67 MB
 // on (K=2048 N=8192 14.3 -> 15.6 us, QKV K=8192 N=1280 15.2 -> 18.1 us, the
 // decode gate/up), where the packing launch stays.
+//
+// Larger launches on bf16 weights with K a multiple of 64 and at least two
+// weight fragments per k-block load x in whole 128-byte lines (8 rows x 64
+// columns per load, the same lines per byte as the packed copy) and turn them
+// into fragments through LDS, with no packing launch either: the decode shard
+// step at T=64 49.7 -> 45.6 us.  With one weight fragment per k-block (QKV at
+// T=64: 80 single strips) the staging costs more than the packing launch
+// (15.2 -> 16.2 us), and the launch keeps it.
 bool rowmajor_x(tpk::PackedParams& p, const tpk::PackedPlan& pl, const void* x, int64_t K, bool f8 = false) {
   if (K % (f8 ? 64 : 32) != 0 || !aligned16(x)) return false;  // fp8: whole k-pairs
   const int64_t groups = (p.nstrips + pl.ns - 1) / pl.ns;
-  if (groups * K * 32 * p.mt > ((int64_t)48 << 20)) return false;
+  if (groups * K * 32 * p.mt > ((int64_t)48 << 20)) {
+    if (f8 || K % 64 != 0 || pl.ns * (p.B1 ? 2 : 1) < 2) return false;
+    p.xstage = 1;
+  }
   p.xrm = reinterpret_cast<const uint16_t*>(x);
   p.xlda = K;
   return true;

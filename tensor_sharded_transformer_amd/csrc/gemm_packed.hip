@@ -26,7 +26,10 @@
 //    launch reads few activation bytes in all (K a multiple of 32), the
 //    packing launch costs more than it saves, and the fragments are read
 //    from row-major x instead (16 bytes of one row per lane; two k-blocks
-//    share each 128-byte line of a row).
+//    share each 128-byte line of a row).  Larger launches with two or more
+//    weight fragments per k-block load row-major x in whole lines (8 rows x
+//    64 columns per load) and turn them into the same fragments through the
+//    wave's LDS slot, a 64-row k-pair per ring step.
 //
 // A workgroup owns NS strips (NS * 16 output columns, gate and up together in
 // dual mode) and a K range.  Its KW waves each stream a contiguous share of
@@ -72,9 +75,16 @@ template <int WF>
 constexpr int pass_frags() {
   return WF <= 4 ? WF : 4;
 }
-template <int MT, int PF, int KW>
+// Per wave: its reduction slot (one pass of PF fragments per tile), which
+// during the main loop also holds the wave's x staging (XM_STAGED: the 16-row
+// tiles of one 64-row k-pair, MT x 2 KB).
+template <int MT, int PF, int XM>
+constexpr int packed_slot_bytes() {
+  return XM == 2 && PF < 2 ? MT * 2048 : MT * PF * 1024;
+}
+template <int MT, int PF, int KW, int XM>
 constexpr int packed_lds_bytes() {
-  return KW * MT * PF * 1024 + KW * PATCH;  // cross-wave reduction (one pass) + per-wave store patch
+  return KW * packed_slot_bytes<MT, PF, XM>() + KW * PATCH;  // cross-wave reduction (one pass) + per-wave store patch
 }
 
 // One k-block of one wave: NF weight fragments and MT activation fragments.
@@ -109,6 +119,55 @@ __device__ __forceinline__ void load_step_rm(KStep<F8 ? 2 * MT : MT, NF>& r, con
   for (int c = 0; c < AT; ++c) {
     const int i = c % MT, b = (F8 ? 2 * kb : kb) + c / MT;
     r.a[c] = row_ok[i] ? *reinterpret_cast<const u32x4*>(xl + i * lda16 + b * 32) : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// One k-pair (k-blocks 2 kp, 2 kp + 1) with the activations as whole 128-byte
+// lines of row-major x: load c brings rows 8 c .. 8 c + 7 (lane l: row
+// 8 c + l / 8, columns 64 kp + 8 (l % 8) .. + 7), rows past M as zeros;
+// weights r.b[h * NF + f] for k-block 2 kp + h.
+template <int MT, int NF>
+__device__ __forceinline__ void load_pair_x(KStep<2 * MT, 2 * NF>& r, const u32x4* const (&bp)[NF],
+                                            const uint16_t* xs, int64_t lda8, const bool (&line_ok)[2 * MT], int kp,
+                                            int64_t kb_stride) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int f = 0; f < NF; ++f) r.b[h * NF + f] = bp[f][(int64_t)(2 * kp + h) * kb_stride];
+#pragma unroll
+  for (int c = 0; c < 2 * MT; ++c)
+    r.a[c] = line_ok[c] ? *reinterpret_cast<const u32x4*>(xs + c * lda8 + kp * 64) : u32x4{0u, 0u, 0u, 0u};
+}
+
+// The staged k-pair through the wave's LDS slot: the lines go in with row R's
+// eight 16-byte pieces rotated by R % 8 (piece q of row R at R * 128 +
+// 16 (q ^ R % 8)), so that both the line writes and the fragment reads of
+// eight consecutive rows hit eight different bank groups; the fragments read
+// back are exactly the packed-activation chunks (lane l: row 16 i + l % 16,
+// columns 32 h + 8 (l / 16) .. + 7 of the pair).
+template <int MT, int NF>
+__device__ __forceinline__ void mma_pair_staged(const KStep<2 * MT, 2 * NF>& r, char* stg, int lane,
+                                                f32x4 (&acc)[MT][NF]) {
+#pragma unroll
+  for (int c = 0; c < 2 * MT; ++c) {
+    const int row = 8 * c + (lane >> 3);
+    *reinterpret_cast<u32x4*>(stg + row * 128 + (((lane & 7) ^ (lane >> 3)) << 4)) = r.a[c];
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    u32x4 af[MT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const int row = 16 * i + (lane & 15);
+      af[i] = *reinterpret_cast<const u32x4*>(stg + row * 128 + (((4 * h + (lane >> 4)) ^ (lane & 7)) << 4));
+    }
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+        acc[i][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[i]),
+                                                           __builtin_bit_cast(bf16x8, r.b[h * NF + f]), acc[i][f], 0,
+                                                           0, 0);
   }
 }
 
@@ -263,15 +322,22 @@ __device__ __forceinline__ void store_tile(const PackedParams& p, int i, int gs,
   }
 }
 
-template <int MT, int NS, bool DUAL, int EPI, typename OutT, bool F8, bool RM, int KW>
+// XM: where the activation fragments come from: 0 the packed copy (A), 1
+// row-major x read straight into the fragments (16 half lines per load), 2
+// row-major x in whole lines staged through LDS (bf16 weights, k-pairs).
+template <int MT, int NS, bool DUAL, int EPI, typename OutT, bool F8, int XM, int KW>
 __global__ __launch_bounds__(KW * 64) void packed_gemm_kernel(const PackedParams params) {
+  constexpr bool RM = XM == 1;
+  constexpr bool ST = XM == 2;
+  static_assert(!(ST && F8), "staged row-major activations serve bf16 weights");
   constexpr int AT = F8 ? 2 * MT : MT;       // activation chunks per ring step (fp8: a k-pair)
   constexpr int NB = DUAL ? 2 : 1;           // weight matrices
   constexpr int WF = NS * NB;                // weight fragments per k-block (all streamed by every wave)
   constexpr int PF = pass_frags<WF>();       // fragments per wave per reduction pass
   constexpr int NPASS = WF / PF;
   static_assert(WF % PF == 0 && PF % NB == 0, "passes hold whole strips");
-  __shared__ __attribute__((aligned(16))) char smem[packed_lds_bytes<MT, PF, KW>()];
+  constexpr int SLOT = packed_slot_bytes<MT, PF, XM>();
+  __shared__ __attribute__((aligned(16))) char smem[packed_lds_bytes<MT, PF, KW, XM>()];
   // Every parameter, requested in one batch at the start and held in SGPRs:
   // a kernel argument first read after the main loop would be a scalar load
   // queued behind the loop's memory traffic, on the launch's critical path.
@@ -288,7 +354,7 @@ __global__ __launch_bounds__(KW * 64) void packed_gemm_kernel(const PackedParams
   const int group = id - split * ngroups;
 
   // this wave's ring steps (k-blocks; fp8: k-pairs): its share of the split's range
-  const int nks = F8 ? p.nkb / 2 : p.nkb;
+  const int nks = F8 || ST ? p.nkb / 2 : p.nkb;
   const int s0 = (int)((int64_t)nks * split / p.splitk);
   const int s1 = (int)((int64_t)nks * (split + 1) / p.splitk);
   const int w0 = s0 + (s1 - s0) * wave / KW;
@@ -312,6 +378,18 @@ __global__ __launch_bounds__(KW * 64) void packed_gemm_kernel(const PackedParams
 #pragma unroll
     for (int i = 0; i < MT; ++i) row_ok[i] = 16 * i + (lane & 15) < p.M;
   }
+  // staged row-major activations (ST): this lane's line piece, which of its
+  // lines exist, and the wave's staging area (its own reduction slot)
+  const uint16_t* xs = nullptr;
+  int64_t lda8 = 0;
+  bool line_ok[2 * MT];
+  char* stg = smem + wave * SLOT;
+  if constexpr (ST) {
+    xs = p.xrm + (int64_t)(lane >> 3) * p.xlda + (lane & 7) * 8;
+    lda8 = 8 * p.xlda;
+#pragma unroll
+    for (int c = 0; c < 2 * MT; ++c) line_ok[c] = 8 * c + (lane >> 3) < p.M;
+  }
 
   f32x4 acc[MT][WF];
 #pragma unroll
@@ -319,7 +397,25 @@ __global__ __launch_bounds__(KW * 64) void packed_gemm_kernel(const PackedParams
 #pragma unroll
     for (int j = 0; j < WF; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  if (n > 0) {
+  if (ST && n > 0) {
+    // The same ring over k-pairs, DEPTH / 2 of them in flight (DEPTH k-blocks).
+    constexpr int DP = DEPTH / 2;
+    const int64_t kbs = (int64_t)p.nstrips * 64;
+    const int q = (n + DP - 1) / DP * DP;
+    auto phys = [&](int it) { return w0 + min(it, n - 1); };
+    KStep<2 * MT, 2 * WF> ring[DP];
+    static_for<0, DP>([&](auto d) { load_pair_x<MT, WF>(ring[d], bp, xs, lda8, line_ok, phys(d), kbs); });
+    for (int it = 0; it < q - DP; it += DP) {
+      static_for<0, DP>([&](auto d) {
+        mma_pair_staged<MT, WF>(ring[d], stg, lane, acc);
+        load_pair_x<MT, WF>(ring[d], bp, xs, lda8, line_ok, phys(it + DP + (int)d), kbs);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    }
+    static_for<0, DP>([&](auto d) {
+      if (q - DP + (int)d < n) mma_pair_staged<MT, WF>(ring[d], stg, lane, acc);
+    });
+  } else if (!ST && n > 0) {
     // The ring runs over q = n rounded up to whole rings of DEPTH k-blocks:
     // the main loop always loads DEPTH k-blocks ahead and the last ring only
     // drains, so no load is issued past the end (a step past n loads the
@@ -358,9 +454,10 @@ __global__ __launch_bounds__(KW * 64) void packed_gemm_kernel(const PackedParams
   // time (red[wave][tile][fragment of the pass][lane][4]); wave w owns the
   // output units (16-row tile i, strip s) u = w, w + KW, ... and sums them over
   // the K ranges in order.
-  float* red = reinterpret_cast<float*>(smem);
-  auto red_at = [&](int w, int i, int j) { return red + (((w * MT + i) * PF + j) * 64 + lane) * 4; };
-  char* patch = smem + KW * MT * PF * 1024 + wave * PATCH;
+  auto red_at = [&](int w, int i, int j) {
+    return reinterpret_cast<float*>(smem + w * SLOT) + ((i * PF + j) * 64 + lane) * 4;
+  };
+  char* patch = smem + KW * SLOT + wave * PATCH;
   constexpr int SPP = PF / NB;                       // strips reduced per pass
   constexpr int UW = (MT * NS + KW - 1) / KW;        // units per wave
   f32x4 v[UW][NB];
@@ -515,12 +612,20 @@ __global__ __launch_bounds__(256) void pack_weight16_kernel(const uint16_t* __re
 template <int MT, int NS, bool DUAL, int EPI, typename OutT, bool F8, int KW>
 hipError_t launch_ns(const PackedParams& p, hipStream_t s) {
   const int ngroups = (p.nstrips + NS - 1) / NS;
+  if constexpr (!F8) {
+    if (p.xrm && p.xstage) {
+      hipLaunchKernelGGL((packed_gemm_kernel<MT, NS, DUAL, EPI, OutT, F8, 2, KW>), dim3(ngroups * p.splitk),
+                         dim3(KW * 64), 0, s, p);
+      return hipGetLastError();
+    }
+  }
+  if (p.xstage) return hipErrorInvalidValue;
   if (p.xrm) {
-    hipLaunchKernelGGL((packed_gemm_kernel<MT, NS, DUAL, EPI, OutT, F8, true, KW>), dim3(ngroups * p.splitk),
+    hipLaunchKernelGGL((packed_gemm_kernel<MT, NS, DUAL, EPI, OutT, F8, 1, KW>), dim3(ngroups * p.splitk),
                        dim3(KW * 64), 0, s, p);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((packed_gemm_kernel<MT, NS, DUAL, EPI, OutT, F8, false, KW>), dim3(ngroups * p.splitk),
+  hipLaunchKernelGGL((packed_gemm_kernel<MT, NS, DUAL, EPI, OutT, F8, 0, KW>), dim3(ngroups * p.splitk),
                      dim3(KW * 64), 0, s, p);
   return hipGetLastError();
 }

@@ -130,6 +130,9 @@ struct PackedParams {
   // instead of A
   const uint16_t* xrm;
   int64_t xlda;
+  // With xrm (bf16 weights, K a multiple of 64, rows 16-byte aligned): load
+  // x in whole 128-byte lines and pass it through LDS into the fragments
+  int xstage;
 };
 struct PackedPlan {
   int ns = 1;              // strips per workgroup

@@ -1383,6 +1383,42 @@ def test_packed_linears_reading_row_major_x(T, K, act):
     assert torch.equal(y, via_packed)
 
 
+@pytest.mark.parametrize("T,K,N,act,same_cuts", [(64, 8192, 3584, "swiglu", True), (37, 8192, 3584, "none", True),
+                                                 (1, 8192, 8192, "gelu", True), (17, 4096, 8192, "relu", True),
+                                                 (48, 3584, 8192, "none", True), (64, 8192, 1280, "none", False)])
+def test_packed_linears_staging_row_major_x(T, K, N, act, same_cuts):
+    """Launches that read many activation bytes (more than 48 MiB of
+    fragments in all; K a multiple of 64, bf16 weights) load row-major x in
+    whole 128-byte lines and turn them into fragments through LDS, with no
+    packing launch: against the oracle, and against the same GEMM on x packed
+    beforehand. The fragments are the same values, but the staged launch cuts
+    K into whole 64-row k-pairs: where the packed launch's K splits and wave
+    ranges fall on the same k-blocks (every shape here but K=8192, N=1280,
+    whose 3 splits of 256 k-blocks cut at 85 and 170 against 84 and 170) the
+    two agree bit for bit; otherwise their fp32 sums differ in order only."""
+    seed = 11 * T + K + N
+    x = W.normal((T, K), 1.0, seed, 1)
+    w = W.normal((K, N), 0.02, seed, 2)
+    wu = W.normal((K, N), 0.02, seed, 3) if act == "swiglu" else None
+    wp, wup = pk(w), None if wu is None else pk(wu)
+    ws = tp.new_workspace(tp.tp_linear_packed_workspace(T, K, N, act))
+    y = torch.full((T, N), 7.0, dtype=torch.bfloat16, device="cuda")
+    if act == "none":
+        tp.tp_row_linear_partial_packed(cuda(x), wp, y, N, ws)
+        ref = O.row_linear_partial(O.to64(x), O.to64(w))
+    else:
+        tp.tp_col_linear_packed(cuda(x), wp, wup, None, y, act, K, N, ws)
+        ref = O.col_linear(O.to64(x), O.to64(w), None if wu is None else O.to64(wu), None, act)
+    assert_close(y, ref, BF16_TOL, f"staged row-major x, T={T} K={K} N={N} {act}")
+    via_packed = tp.tp_linear_packed_gemm(tp.tp_pack_act(cuda(x)), wp, wup, None,
+                                          torch.empty(T, N, dtype=torch.bfloat16, device="cuda"), act, K, ws)
+    if same_cuts:
+        assert torch.equal(y, via_packed)
+    else:   # one bf16 rounding apart at most
+        d = (y.float() - via_packed.float()).abs()
+        assert (d <= 2.0 ** -7 * via_packed.float().abs() + 1e-4).all()
+
+
 @pytest.mark.parametrize("T,K,act", [(64, 1024, "none"), (37, 1024, "swiglu"), (1, 64, "gelu"), (33, 4096, "none")])
 def test_packed_fp8_linears_reading_row_major_x(T, K, act):
     """The packed fp8 linears take their bf16 activation fragments straight
