@@ -1385,7 +1385,8 @@ def test_packed_linears_reading_row_major_x(T, K, act):
 
 @pytest.mark.parametrize("T,K,N,act,same_cuts", [(64, 8192, 3584, "swiglu", True), (37, 8192, 3584, "none", True),
                                                  (1, 8192, 8192, "gelu", True), (17, 4096, 8192, "relu", True),
-                                                 (48, 3584, 8192, "none", True), (64, 8192, 1280, "none", False)])
+                                                 (48, 3584, 8192, "none", True), (64, 8192, 1280, "none", False),
+                                                 (64, 64, 200000, "none", False)])
 def test_packed_linears_staging_row_major_x(T, K, N, act, same_cuts):
     """Launches that read many activation bytes (more than 48 MiB of
     fragments in all; K a multiple of 64, bf16 weights) load row-major x in
@@ -1395,7 +1396,10 @@ def test_packed_linears_staging_row_major_x(T, K, N, act, same_cuts):
     K into whole 64-row k-pairs: where the packed launch's K splits and wave
     ranges fall on the same k-blocks (every shape here but K=8192, N=1280,
     whose 3 splits of 256 k-blocks cut at 85 and 170 against 84 and 170) the
-    two agree bit for bit; otherwise their fp32 sums differ in order only."""
+    two agree bit for bit; otherwise their fp32 sums differ in order only.
+    K=64, N=200000: one k-pair for four waves (three stream nothing) over
+    6250 workgroups; the packed launch spreads its two k-blocks over two
+    waves, so there too only the order of the sums differs."""
     seed = 11 * T + K + N
     x = W.normal((T, K), 1.0, seed, 1)
     w = W.normal((K, N), 0.02, seed, 2)
