@@ -55,7 +55,7 @@ BF16_PEAK_TFLOPS = 2516.6    # MI355X dense bf16 MFMA (256 CUs x 4096 flop/clk x
 # sha256 of the kernel's source files when the counters were taken; reported
 # as null once that source has changed.
 TRAFFIC_GATE_UP = 129_663_418
-TRAFFIC_SOURCE_SHA256 = "d145813d46bdafd384cfb0c8b9887c538bfb6f2f52d8122b8ef3239af9e6332b"
+TRAFFIC_SOURCE_SHA256 = "642d2cc9f301f10093845a4163d3d9c80585ba8392914460f01361e8f0fb94f3"
 KERNEL_SOURCES = [os.path.join(ROOT, "tensor_sharded_transformer_amd", "csrc", f)
                   for f in ("gemm_packed.hip", "tp_device.h", "tp_kernels.h")]
 

@@ -339,10 +339,12 @@ tp_status tp_pack_weight(const void* w, void* w_packed, int64_t K, int64_t N, tp
  * 4) bytes) read x in place instead and skip that launch; the results are
  * bitwise the same either way.  Larger calls on these bf16 weights with K a
  * multiple of 64, x 16-byte aligned and at least two weight fragments per
- * k-block (SWIGLU, or more than 2032 columns) skip it too: they load x in
+ * k-block (SWIGLU, or more than 1008 columns, which such a call then
+ * streams two 16-column strips per workgroup) skip it too: they load x in
  * whole 128-byte lines and rearrange it on chip; their fp32 sums run over
- * whole 64-row k-pairs, so where the packed launch would split K inside a
- * pair the results can differ from it by one bf16 rounding. */
+ * whole 64-row k-pairs and their own K splits, so where the packed launch
+ * would cut K elsewhere the results can differ from it by one bf16
+ * rounding. */
 size_t tp_linear_packed_workspace(int64_t T, int64_t K, int64_t N, tp_act act);
 
 /* tp_col_linear with packed weights ([KL] Y_i = X W_i; [FFN] "First matmul,

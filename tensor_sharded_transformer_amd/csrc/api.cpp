@@ -1,6 +1,7 @@
 // C ABI of the tpshard library: argument checks on the host, workspace
 // layout, and dispatch to the HIP kernels.  Every check happens before the
 // first launch, so a rejected call has no side effect.
+#include <algorithm>
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -880,6 +881,7 @@ constexpr int64_t kPackedMaxT = 64;
 //   [ split-K counters (>= CNT_RESERVE, zero between calls) ][ packed x ][ packed h ][ split-K partials ]
 struct PackedLayout {
   tpk::PackedPlan p1, p2;
+  tpk::PackedPlan p1s;  // p1 for a call that stages row-major x (regions sized for both)
   size_t x_off = 0, h_off = 0, part_off = 0, total = 0;
 };
 
@@ -892,10 +894,14 @@ size_t counter_region(size_t units) {
 PackedLayout packed_linear_layout(int64_t T, int64_t K, int64_t N, bool dual) {
   PackedLayout L;
   L.p1 = tpk::plan_packed((int)T, (int)N, (int)K, true, false, dual);
-  L.x_off = counter_region(tpk::packed_units((int)T, (int)N, L.p1));
+  L.p1s = tpk::plan_packed((int)T, (int)N, (int)K, true, false, dual, true);
+  const size_t u = std::max(tpk::packed_units((int)T, (int)N, L.p1), tpk::packed_units((int)T, (int)N, L.p1s));
+  const size_t q = std::max(tpk::packed_partial_bytes((int)T, (int)N, dual, L.p1),
+                            tpk::packed_partial_bytes((int)T, (int)N, dual, L.p1s));
+  L.x_off = counter_region(u);
   L.h_off = L.x_off + tpk::align_up(tpk::packed_act_bytes((int)T, (int)K), 256);
   L.part_off = L.h_off;
-  L.total = L.part_off + tpk::align_up(tpk::packed_partial_bytes((int)T, (int)N, dual, L.p1), 256);
+  L.total = L.part_off + tpk::align_up(q, 256);
   return L;
 }
 
@@ -903,9 +909,12 @@ PackedLayout packed_linear_layout(int64_t T, int64_t K, int64_t N, bool dual) {
 PackedLayout packed_fwd_layout(int64_t T, int64_t d, int64_t ff_i, bool dual) {
   PackedLayout L;
   L.p1 = tpk::plan_packed((int)T, (int)ff_i, (int)d, true, false, dual);
+  L.p1s = tpk::plan_packed((int)T, (int)ff_i, (int)d, true, false, dual, true);
   L.p2 = tpk::plan_packed((int)T, (int)d, (int)ff_i, true);
-  const size_t u1 = tpk::packed_units((int)T, (int)ff_i, L.p1), u2 = tpk::packed_units((int)T, (int)d, L.p2);
-  const size_t q1 = tpk::packed_partial_bytes((int)T, (int)ff_i, dual, L.p1);
+  const size_t u1 = std::max(tpk::packed_units((int)T, (int)ff_i, L.p1), tpk::packed_units((int)T, (int)ff_i, L.p1s)),
+               u2 = tpk::packed_units((int)T, (int)d, L.p2);
+  const size_t q1 = std::max(tpk::packed_partial_bytes((int)T, (int)ff_i, dual, L.p1),
+                             tpk::packed_partial_bytes((int)T, (int)ff_i, dual, L.p1s));
   const size_t q2 = tpk::packed_partial_bytes((int)T, (int)d, false, L.p2);
   L.x_off = counter_region(u1 > u2 ? u1 : u2);
   L.h_off = L.x_off + tpk::align_up(tpk::packed_act_bytes((int)T, (int)d), 256);
@@ -943,23 +952,30 @@ tpk::PackedParams packed_params(const void* A, const void* B0, const void* B1, i
 // on (K=2048 N=8192 14.3 -> 15.6 us, QKV K=8192 N=1280 15.2 -> 18.1 us, the
 // decode gate/up), where the packing launch stays.
 //
-// Larger launches on bf16 weights with K a multiple of 64 and at least two
-// weight fragments per k-block load x in whole 128-byte lines (8 rows x 64
-// columns per load, the same lines per byte as the packed copy) and turn them
-// into fragments through LDS, with no packing launch either: the decode shard
-// step at T=64 49.7 -> 45.6 us.  With one weight fragment per k-block (QKV at
-// T=64: 80 single strips) the staging costs more than the packing launch
-// (15.2 -> 16.2 us), and the launch keeps it.
-bool rowmajor_x(tpk::PackedParams& p, const tpk::PackedPlan& pl, const void* x, int64_t K, bool f8 = false) {
-  if (K % (f8 ? 64 : 32) != 0 || !aligned16(x)) return false;  // fp8: whole k-pairs
-  const int64_t groups = (p.nstrips + pl.ns - 1) / pl.ns;
+// Larger launches on bf16 weights with K a multiple of 64 load x in whole
+// 128-byte lines (8 rows x 64 columns per load, the same lines per byte as
+// the packed copy) and turn them into fragments through LDS, with no packing
+// launch either: the decode shard step at T=64 49.7 -> 45.6 us.  They run the
+// staged plan (L.p1s: two strips per workgroup from 64 strips on, so QKV at
+// T=64 runs 40 groups x 6 K splits, 15.25 -> 14.3 us); one weight fragment
+// per k-block (fewer than 64 strips, no gate/up pair) keeps the packing
+// launch, where the staging costs more than it saves (QKV with one strip per
+// workgroup: 15.2 -> 16.2 us).
+//
+// Returns the plan the launch runs and sets p.xrm (and p.xstage) where x is
+// read in place; otherwise the caller packs x first.
+const tpk::PackedPlan& x_source(tpk::PackedParams& p, const PackedLayout& L, const void* x, int64_t K,
+                                bool f8 = false) {
+  if (K % (f8 ? 64 : 32) != 0 || !aligned16(x)) return L.p1;  // fp8: whole k-pairs
+  const int64_t groups = (p.nstrips + L.p1.ns - 1) / L.p1.ns;
   if (groups * K * 32 * p.mt > ((int64_t)48 << 20)) {
-    if (f8 || K % 64 != 0 || pl.ns * (p.B1 ? 2 : 1) < 2) return false;
+    if (f8 || K % 64 != 0 || L.p1s.ns * (p.B1 ? 2 : 1) < 2) return L.p1;
     p.xstage = 1;
+    p.splitk = L.p1s.splitk;
   }
   p.xrm = reinterpret_cast<const uint16_t*>(x);
   p.xlda = K;
-  return true;
+  return p.xstage ? L.p1s : L.p1;
 }
 
 tp_status packed_sizes_ok(const char* who, int64_t T, int64_t K, int64_t N) {
@@ -1024,7 +1040,8 @@ tp_status tp_col_linear_packed(const void* x, const void* w_packed, const void* 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* base = reinterpret_cast<char*>(ws);
   tpk::PackedParams p = packed_params(base + L.x_off, w_packed, sw ? w_up_packed : nullptr, T, K, N_i, L.p1, base, L);
-  if (!rowmajor_x(p, L.p1, x, K)) {
+  const tpk::PackedPlan& pl = x_source(p, L, x, K);
+  if (!p.xrm) {
     const hipError_t e = tpk::pack_act16(x, K, (int)T, (int)K, aligned16(x) && K % 8 == 0, base + L.x_off, s);
     if (e != hipSuccess) return hip_status(e, who);
   }
@@ -1033,7 +1050,7 @@ tp_status tp_col_linear_packed(const void* x, const void* w_packed, const void* 
   p.vec_out = rows_vec16(y, N_i, 2);
   p.bias = reinterpret_cast<const uint16_t*>(bias);
   p.act = act;
-  return hip_status(tpk::gemm_packed(p, L.p1, sw ? tpk::GK_FWD_SWIGLU : tpk::GK_FWD_ACT, false, s), who);
+  return hip_status(tpk::gemm_packed(p, pl, sw ? tpk::GK_FWD_SWIGLU : tpk::GK_FWD_ACT, false, s), who);
 }
 
 tp_status tp_row_linear_partial_packed(const void* x_i, const void* w_packed, void* z_i, void* ws, size_t ws_bytes,
@@ -1051,14 +1068,15 @@ tp_status tp_row_linear_partial_packed(const void* x_i, const void* w_packed, vo
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* base = reinterpret_cast<char*>(ws);
   tpk::PackedParams p = packed_params(base + L.x_off, w_packed, nullptr, T, K_i, N, L.p1, base, L);
-  if (!rowmajor_x(p, L.p1, x_i, K_i)) {
+  const tpk::PackedPlan& pl = x_source(p, L, x_i, K_i);
+  if (!p.xrm) {
     const hipError_t e = tpk::pack_act16(x_i, K_i, (int)T, (int)K_i, aligned16(x_i) && K_i % 8 == 0, base + L.x_off, s);
     if (e != hipSuccess) return hip_status(e, who);
   }
   p.C = z_i;
   p.ldc = N;
   p.vec_out = rows_vec16(z_i, N, esize(out_dtype));
-  return hip_status(tpk::gemm_packed(p, L.p1, tpk::GK_FWD_STORE, out_dtype == TP_F32, s), who);
+  return hip_status(tpk::gemm_packed(p, pl, tpk::GK_FWD_STORE, out_dtype == TP_F32, s), who);
 }
 
 size_t tp_packed_act_bytes(int64_t T, int64_t K) {
@@ -1142,14 +1160,15 @@ tp_status tp_mlp_shard_fwd_packed(const void* x, const void* w1_packed, const vo
   tpk::PackedParams p1 = packed_params(base + L.x_off, w1_packed, sw ? w_up_packed : nullptr, T, d, ff_i, L.p1,
                                        base, L);
   hipError_t e = hipSuccess;
-  if (!rowmajor_x(p1, L.p1, x, d)) {
+  const tpk::PackedPlan& pl1 = x_source(p1, L, x, d);
+  if (!p1.xrm) {
     e = tpk::pack_act16(x, d, (int)T, (int)d, aligned16(x) && d % 8 == 0, base + L.x_off, s);
     if (e != hipSuccess) return hip_status(e, who);
   }
   p1.cpk = base + L.h_off;
   p1.cpk_mt = tpk::packed_mt((int)T);
   p1.act = act;
-  e = tpk::gemm_packed(p1, L.p1, sw ? tpk::GK_FWD_SWIGLU : tpk::GK_FWD_ACT, false, s);
+  e = tpk::gemm_packed(p1, pl1, sw ? tpk::GK_FWD_SWIGLU : tpk::GK_FWD_ACT, false, s);
   if (e != hipSuccess) return hip_status(e, who);
   // row GEMM: the full-shape partial y_i = h W2_i
   tpk::PackedParams p2 = packed_params(base + L.h_off, w2_packed, nullptr, T, ff_i, d, L.p2, base, L);
@@ -1172,6 +1191,7 @@ PackedLayout packed8_linear_layout(int64_t T, int64_t K, int64_t N, bool dual) {
   PackedLayout L;
   const int64_t Kp = kpair_pad(K);
   L.p1 = tpk::plan_packed((int)T, (int)N, (int)Kp, true, true, dual);
+  L.p1s = L.p1;
   L.x_off = counter_region(tpk::packed_units((int)T, (int)N, L.p1));
   L.h_off = L.x_off + tpk::align_up(tpk::packed_act_bytes((int)T, (int)Kp), 256);
   L.part_off = L.h_off;
@@ -1184,6 +1204,7 @@ PackedLayout packed8_fwd_layout(int64_t T, int64_t d, int64_t ff_i, bool dual) {
   PackedLayout L;
   const int64_t dp = kpair_pad(d);
   L.p1 = tpk::plan_packed((int)T, (int)ff_i, (int)dp, true, true, dual);
+  L.p1s = L.p1;
   L.p2 = tpk::plan_packed((int)T, (int)d, (int)ff_i, true, true);
   const size_t u1 = tpk::packed_units((int)T, (int)ff_i, L.p1), u2 = tpk::packed_units((int)T, (int)d, L.p2);
   const size_t q1 = tpk::packed_partial_bytes((int)T, (int)ff_i, dual, L.p1);
@@ -1254,7 +1275,8 @@ tp_status tp_col_linear_packed_fp8(const void* x, const void* wq_packed, const f
   const int nkb = (int)(kpair_pad(K) / 32);
   tpk::PackedParams p = packed8_params(base + L.x_off, wq_packed, scale, sw ? wq_up_packed : nullptr,
                                        sw ? scale_up : nullptr, T, K, N_i, L.p1, base, L);
-  if (!rowmajor_x(p, L.p1, x, K, true)) {
+  x_source(p, L, x, K, true);  // fp8 codes: L.p1
+  if (!p.xrm) {
     const hipError_t e = tpk::pack_act16(x, K, (int)T, (int)K, aligned16(x) && K % 8 == 0, base + L.x_off, s, nkb);
     if (e != hipSuccess) return hip_status(e, who);
   }
@@ -1285,7 +1307,8 @@ tp_status tp_row_linear_partial_packed_fp8(const void* x_i, const void* wq_packe
   char* base = reinterpret_cast<char*>(ws);
   const int nkb = (int)(kpair_pad(K_i) / 32);
   tpk::PackedParams p = packed8_params(base + L.x_off, wq_packed, scale_i, nullptr, nullptr, T, K_i, N, L.p1, base, L);
-  if (!rowmajor_x(p, L.p1, x_i, K_i, true)) {
+  x_source(p, L, x_i, K_i, true);  // fp8 codes: L.p1
+  if (!p.xrm) {
     const hipError_t e =
         tpk::pack_act16(x_i, K_i, (int)T, (int)K_i, aligned16(x_i) && K_i % 8 == 0, base + L.x_off, s, nkb);
     if (e != hipSuccess) return hip_status(e, who);
@@ -1335,7 +1358,8 @@ tp_status tp_mlp_shard_fwd_packed_fp8(const void* x, const void* wq1_packed, con
   tpk::PackedParams p1 = packed8_params(base + L.x_off, wq1_packed, s1_i, sw ? wq_up_packed : nullptr,
                                         sw ? s_up_i : nullptr, T, d, ff_i, L.p1, base, L);
   hipError_t e = hipSuccess;
-  if (!rowmajor_x(p1, L.p1, x, d, true)) {
+  x_source(p1, L, x, d, true);  // fp8 codes: L.p1
+  if (!p1.xrm) {
     e = tpk::pack_act16(x, d, (int)T, (int)d, aligned16(x) && d % 8 == 0, base + L.x_off, s, nkb);
     if (e != hipSuccess) return hip_status(e, who);
   }

@@ -664,7 +664,7 @@ hipError_t launch_packed(const PackedParams& p, int ns, int kw, hipStream_t s) {
 
 int packed_mt(int M) { return M <= 16 ? 1 : (M <= 32 ? 2 : 4); }
 
-PackedPlan plan_packed(int M, int N, int K, bool split_ok, bool f8, bool dual) {
+PackedPlan plan_packed(int M, int N, int K, bool split_ok, bool f8, bool dual, bool staged) {
   PackedPlan pl;
   pl.kw = dual && !f8 ? PACKED_KW_DUAL : PACKED_KW;
   const int nstrips = (N + 15) / 16;
@@ -674,7 +674,10 @@ PackedPlan plan_packed(int M, int N, int K, bool split_ok, bool f8, bool dual) {
   // workgroups until the grid fills the CUs.  (Four strips with twice the
   // K splits measured slower for bf16 and for fp8 codes alike: the larger
   // split-K exchange costs more than the activation loads it saves.)
-  pl.ns = nstrips >= 128 ? 2 : 1;
+  // (A launch staging row-major x takes two strips from 64 strips on: QKV at
+  // T=64, 80 strips, 40 groups x 6 K splits, 14.3 against 15.25 us with one
+  // strip per workgroup and its packing launch.)
+  pl.ns = nstrips >= 128 || (staged && nstrips >= 64) ? 2 : 1;
   const int ngroups = (nstrips + pl.ns - 1) / pl.ns;
   pl.splitk = 1;
   if (split_ok) {

@@ -140,7 +140,10 @@ struct PackedPlan {
   int kw = PACKED_KW;      // waves per workgroup
 };
 int packed_mt(int M);
-PackedPlan plan_packed(int M, int N, int K, bool split_ok, bool f8 = false, bool dual = false);
+// staged: the plan of a launch that stages row-major x through LDS (two
+// strips per workgroup from 64 strips on, so that every such launch has at
+// least two weight fragments per k-block)
+PackedPlan plan_packed(int M, int N, int K, bool split_ok, bool f8 = false, bool dual = false, bool staged = false);
 size_t packed_act_bytes(int M, int K);
 size_t packed_units(int M, int N, const PackedPlan& pl);
 size_t packed_partial_bytes(int M, int N, bool dual, const PackedPlan& pl);

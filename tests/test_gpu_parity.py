@@ -1393,10 +1393,11 @@ def test_packed_linears_staging_row_major_x(T, K, N, act, same_cuts):
     whole 128-byte lines and turn them into fragments through LDS, with no
     packing launch: against the oracle, and against the same GEMM on x packed
     beforehand. The fragments are the same values, but the staged launch cuts
-    K into whole 64-row k-pairs: where the packed launch's K splits and wave
-    ranges fall on the same k-blocks (every shape here but K=8192, N=1280,
-    whose 3 splits of 256 k-blocks cut at 85 and 170 against 84 and 170) the
-    two agree bit for bit; otherwise their fp32 sums differ in order only.
+    K into whole 64-row k-pairs, and from 64 strips on it runs two strips per
+    workgroup: where both launches cut K at the same k-blocks (every shape
+    here but K=8192, N=1280, whose 80 strips run as 40 pairs x 6 K splits
+    staged against 80 single strips x 3 splits packed) the two agree bit for
+    bit; otherwise their fp32 sums differ in order only.
     K=64, N=200000: one k-pair for four waves (three stream nothing) over
     6250 workgroups; the packed launch spreads its two k-blocks over two
     waves, so there too only the order of the sums differs."""
